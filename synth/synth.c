@@ -1,0 +1,355 @@
+/*
+ * Seeded synthetic inputs for the routed-expert FFN path.
+ *
+ * This module is shared by the CPU oracle and by the GPU tests/bench. It holds
+ * no arithmetic of the method itself (no routing, no dequantization, no FFN):
+ * it draws random numbers and writes them out, including the *encoding* of
+ * float weights into the record byte layout described below (the decoders on
+ * both sides are written independently from that description).
+ *
+ * Random numbers: SplitMix64 (Steele, Lea & Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014), used counter-based: the j-th
+ * draw of a stream is mix64(key + (j + 1) * GAMMA), where the key is derived
+ * from (seed, tag, a, b).  Any record or row can therefore be regenerated on
+ * its own.
+ *
+ * Approximate normal draws: the sum of the four 16-bit fields of one 64-bit
+ * draw (Irwin-Hall, n = 4), centred and scaled to unit variance.
+ *
+ * Record layout (one record = every tensor of one (layer, expert)):
+ *   gate payload [I x H] | up payload [I x H] | down payload [H x I] |
+ *   gate scales | up scales | down scales
+ * The tensor order follows the expert record of the NVMe streaming page
+ * ("엔진", item 1).  Each matrix (N output rows, Kd input columns, N % 64 == 0,
+ * Kd % 32 == 0) is cut into 1 KiB payload blocks of 64 rows x 32 columns,
+ * ordered block = kb * (N / 64) + nb with kb = k / 32, nb = n / 64.  Inside a
+ * block, element (n, k) sits at byte (q * 16 + r) * 16 + t * 4 + i / 2 with
+ * t = (n % 64) / 16, r = n % 16, q = (k % 32) / 8, i = k % 8; even i in the
+ * low nibble.  Each payload block has a 128-byte scale block at the same
+ * index: int4 -> bf16 scale of (n, k / 32) at (r * 4 + t) * 2; NVFP4 -> e4m3
+ * scale of (n, k / 16) at (((k % 32) / 16) * 16 + r) * 4 + t.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define GAMMA 0x9E3779B97F4A7C15ULL
+
+static inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+uint64_t synth_key(uint64_t seed, uint64_t tag, uint64_t a, uint64_t b) {
+  uint64_t k = mix64(seed ^ mix64(tag + GAMMA));
+  k = mix64(k ^ mix64(a + 2 * GAMMA));
+  k = mix64(k ^ mix64(b + 3 * GAMMA));
+  return k;
+}
+
+static inline uint64_t draw(uint64_t key, uint64_t j) { return mix64(key + (j + 1) * GAMMA); }
+
+static const double IH4_MEAN = 131070.0; /* 4 * 65535 / 2 */
+
+static inline double approx_normal(uint64_t r) {
+  const double inv_sd = 1.0 / sqrt(4.0 * (65536.0 * 65536.0 - 1.0) / 12.0); /* folded at compile time */
+  double s = (double)(r & 0xFFFF) + (double)((r >> 16) & 0xFFFF) + (double)((r >> 32) & 0xFFFF) +
+             (double)(r >> 48);
+  return (s - IH4_MEAN) * inv_sd;
+}
+
+static inline double uniform01(uint64_t r) { return ((double)(r >> 11) + 0.5) * (1.0 / 9007199254740992.0); }
+
+static inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint32_t bias = 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)((u + bias) >> 16);
+}
+
+static inline float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* ---------------------------------------------------------------- plain tensors */
+
+void synth_normal_f32(uint64_t seed, uint64_t tag, uint64_t a, uint64_t b, int64_t n, double scale,
+                      float* out) {
+  uint64_t key = synth_key(seed, tag, a, b);
+  for (int64_t j = 0; j < n; ++j) out[j] = (float)(scale * approx_normal(draw(key, (uint64_t)j)));
+}
+
+void synth_normal_bf16(uint64_t seed, uint64_t tag, uint64_t a, uint64_t b, int64_t n, double scale,
+                       uint16_t* out) {
+  uint64_t key = synth_key(seed, tag, a, b);
+  for (int64_t j = 0; j < n; ++j)
+    out[j] = f32_to_bf16_rne((float)(scale * approx_normal(draw(key, (uint64_t)j))));
+}
+
+void synth_uniform_f64(uint64_t seed, uint64_t tag, uint64_t a, uint64_t b, int64_t n, double* out) {
+  uint64_t key = synth_key(seed, tag, a, b);
+  for (int64_t j = 0; j < n; ++j) out[j] = uniform01(draw(key, (uint64_t)j));
+}
+
+/* ---------------------------------------------------------------- encoders */
+
+/* e4m3 (OCP E4M3FN) value of a code: bias 7, subnormals, S.1111.111 is NaN. */
+static double e4m3_value(int code) {
+  int e = (code >> 3) & 15, m = code & 7;
+  double v = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return (code & 0x80) ? -v : v;
+}
+
+/* nearest positive e4m3 code (0x00..0x7E), ties to the even code; clamps to 448. */
+static uint8_t e4m3_encode_pos(double v) {
+  if (!(v > 0.0)) return 0;
+  if (v >= 448.0) return 0x7E;
+  int lo = 0, hi = 0x7E; /* value is monotone in the code over 0..0x7E */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (e4m3_value(mid) <= v) lo = mid; else hi = mid;
+  }
+  double dl = v - e4m3_value(lo), dh = e4m3_value(hi) - v;
+  if (dl < dh) return (uint8_t)lo;
+  if (dh < dl) return (uint8_t)hi;
+  return (uint8_t)((lo & 1) ? hi : lo);
+}
+
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* nearest e2m1 code for v (sign kept, magnitude clamped to 6), ties to the even code. */
+static uint8_t e2m1_encode(double v) {
+  double a = fabs(v);
+  int best = 0;
+  if (a >= 6.0) best = 7;
+  else {
+    for (int c = 0; c < 7; ++c) {
+      if (a >= E2M1_MAG[c] && a <= E2M1_MAG[c + 1]) {
+        double dl = a - E2M1_MAG[c], dh = E2M1_MAG[c + 1] - a;
+        best = (dl < dh) ? c : (dh < dl) ? c + 1 : ((c & 1) ? c + 1 : c);
+        break;
+      }
+    }
+  }
+  return (uint8_t)(best | ((v < 0.0) ? 8 : 0));
+}
+
+/* ---------------------------------------------------------------- record layout (writer side) */
+
+static inline int64_t payload_off(int64_t N, int64_t n, int64_t k) {
+  int64_t kb = k / 32, nb = n / 64;
+  int64_t blk = kb * (N / 64) + nb;
+  int64_t t = (n % 64) / 16, r = n % 16, q = (k % 32) / 8, i = k % 8;
+  return blk * 1024 + (q * 16 + r) * 16 + t * 4 + i / 2;
+}
+
+static inline void put_nibble(uint8_t* base, int64_t N, int64_t n, int64_t k, uint8_t code) {
+  int64_t off = payload_off(N, n, k);
+  if (k % 2 == 0) base[off] = (uint8_t)((base[off] & 0xF0) | (code & 15));
+  else base[off] = (uint8_t)((base[off] & 0x0F) | ((code & 15) << 4));
+}
+
+static inline int64_t scale_block_off(int64_t N, int64_t n, int64_t k) {
+  return ((k / 32) * (N / 64) + n / 64) * 128;
+}
+
+int64_t synth_record_bytes(int64_t H, int64_t I) { return 3 * H * I / 2 + 3 * H * I / 16; }
+
+enum { FMT_INT4_G32_BF16 = 0, FMT_NVFP4_G16_E4M3 = 1 };
+enum { TAG_WEIGHT = 1 };
+
+/* float weights of matrix m (0 gate [I,H], 1 up [I,H], 2 down [H,I]) of expert (l, e). */
+void synth_weights_f32(uint64_t seed, int64_t E, int64_t l, int64_t e, int m, int64_t H, int64_t I,
+                       double sigma, float* out) {
+  int64_t N = (m == 2) ? H : I, Kd = (m == 2) ? I : H;
+  synth_normal_f32(seed, TAG_WEIGHT, (uint64_t)(l * E + e), (uint64_t)m, N * Kd, sigma, out);
+}
+
+/* Encode one matrix (row-major floats w[N][Kd]) into payload + scale bytes. */
+static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_t* pay, uint8_t* sc,
+                          float* tensor_scale) {
+  if (fmt == FMT_INT4_G32_BF16) {
+    for (int64_t n = 0; n < N; ++n) {
+      for (int64_t g = 0; g < Kd / 32; ++g) {
+        const float* wg = w + n * Kd + g * 32;
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)wg[i]));
+        uint16_t sbits = f32_to_bf16_rne((float)(amax / 7.0));
+        double s = (double)bf16_to_f32(sbits);
+        if (!(s > 0.0)) { sbits = 0x3F80; s = 1.0; } /* all-zero group: codes 8 -> 0.0 */
+        int64_t so = scale_block_off(N, n, g * 32) + ((n % 16) * 4 + (n % 64) / 16) * 2;
+        memcpy(sc + so, &sbits, 2);
+        for (int i = 0; i < 32; ++i) {
+          double qd = nearbyint((double)wg[i] / s); /* round-half-even (default FP mode) */
+          if (qd < -8) qd = -8;
+          if (qd > 7) qd = 7;
+          put_nibble(pay, N, n, g * 32 + i, (uint8_t)((int)qd + 8));
+        }
+      }
+    }
+    *tensor_scale = 1.0f;
+  } else {
+    double amax = 0.0;
+    for (int64_t j = 0; j < N * Kd; ++j) amax = fmax(amax, fabs((double)w[j]));
+    float ts = (float)(amax / (6.0 * 448.0));
+    if (!(ts > 0.0f)) ts = 1.0f;
+    *tensor_scale = ts;
+    for (int64_t n = 0; n < N; ++n) {
+      for (int64_t g = 0; g < Kd / 16; ++g) {
+        const float* wg = w + n * Kd + g * 16;
+        double bmax = 0.0;
+        for (int i = 0; i < 16; ++i) bmax = fmax(bmax, fabs((double)wg[i]));
+        uint8_t sb = e4m3_encode_pos(bmax / (6.0 * (double)ts));
+        double sv = e4m3_value(sb) * (double)ts;
+        int64_t k0 = g * 16;
+        int64_t so = scale_block_off(N, n, k0) + (((k0 % 32) / 16) * 16 + (n % 16)) * 4 + (n % 64) / 16;
+        sc[so] = sb;
+        for (int i = 0; i < 16; ++i) {
+          uint8_t c = (sv > 0.0) ? e2m1_encode((double)wg[i] / sv) : 0;
+          put_nibble(pay, N, n, k0 + i, c);
+        }
+      }
+    }
+  }
+}
+
+/* Write the record of expert (l, e) into rec (synth_record_bytes bytes); ts3 gets the
+ * three tensor scales (1.0 for int4). scratch must hold max(I*H) floats. */
+void synth_record(uint64_t seed, int64_t E, int64_t l, int64_t e, int64_t H, int64_t I, int fmt,
+                  double sigma, uint8_t* rec, float* ts3, float* scratch) {
+  int64_t pay_m = H * I / 2, sc_m = H * I / 16;
+  memset(rec, 0, (size_t)synth_record_bytes(H, I));
+  for (int m = 0; m < 3; ++m) {
+    int64_t N = (m == 2) ? H : I, Kd = (m == 2) ? I : H;
+    synth_weights_f32(seed, E, l, e, m, H, I, sigma, scratch);
+    encode_matrix(scratch, N, Kd, fmt, rec + m * pay_m, rec + 3 * pay_m + m * sc_m, &ts3[m]);
+  }
+}
+
+typedef struct {
+  uint64_t seed;
+  int64_t E, H, I, first, count, R;
+  int fmt;
+  double sigma;
+  uint8_t* pool;
+  float* ts;
+  int64_t next; /* shared work counter */
+  pthread_mutex_t mu;
+} fill_job;
+
+static void* fill_worker(void* arg) {
+  fill_job* J = (fill_job*)arg;
+  float* scratch = (float*)malloc(sizeof(float) * (size_t)(J->H * J->I));
+  if (!scratch) return (void*)1;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int64_t i = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (i >= J->count) break;
+    int64_t flat = J->first + i;
+    int64_t l = flat / J->E, e = flat % J->E;
+    synth_record(J->seed, J->E, l, e, J->H, J->I, J->fmt, J->sigma, J->pool + i * J->R,
+                 J->ts + 3 * i, scratch);
+  }
+  free(scratch);
+  return NULL;
+}
+
+/* Fill `count` consecutive records starting at flat id `first` (= layer * E + expert). */
+int synth_fill_records(uint64_t seed, int64_t E, int64_t H, int64_t I, int fmt, double sigma,
+                       int64_t first, int64_t count, uint8_t* pool, float* ts, int nthreads) {
+  if (H % 64 || I % 64 || nthreads < 1) return -1;
+  fill_job J;
+  J.seed = seed; J.E = E; J.H = H; J.I = I; J.first = first; J.count = count;
+  J.R = synth_record_bytes(H, I); J.fmt = fmt; J.sigma = sigma; J.pool = pool; J.ts = ts; J.next = 0;
+  pthread_mutex_init(&J.mu, NULL);
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  int started = 0, rc = 0;
+  for (int t = 0; t < nthreads; ++t)
+    if (pthread_create(&th[t], NULL, fill_worker, &J) == 0) started++;
+  if (started == 0) rc = -2;
+  for (int t = 0; t < started; ++t) {
+    void* ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret) rc = -3;
+  }
+  pthread_mutex_destroy(&J.mu);
+  return rc;
+}
+
+/* ---------------------------------------------------------------- routing traces */
+
+enum { TAG_PERM = 11, TAG_GUMBEL = 12, TAG_SPEC = 13 };
+
+/* Popularity of layer l: a seeded permutation pi (Fisher-Yates), p[pi[i]] ~ 1/(i+1)^s. */
+void synth_zipf_logp(uint64_t seed, int64_t l, int64_t E, double s, double* logp) {
+  int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!perm) return;
+  for (int64_t i = 0; i < E; ++i) perm[i] = (int32_t)i;
+  uint64_t key = synth_key(seed, TAG_PERM, (uint64_t)l, 0);
+  for (int64_t i = E - 1; i > 0; --i) {
+    int64_t j = (int64_t)(uniform01(draw(key, (uint64_t)i)) * (double)(i + 1));
+    if (j > i) j = i;
+    int32_t t = perm[i]; perm[i] = perm[j]; perm[j] = t;
+  }
+  double z = 0.0;
+  for (int64_t i = 0; i < E; ++i) z += pow((double)(i + 1), -s);
+  for (int64_t i = 0; i < E; ++i) logp[perm[i]] = -s * log((double)(i + 1)) - log(z);
+  free(perm);
+}
+
+/* Trace logits of layer l for tokens [t0, t0 + n): logp + Gumbel; the top-K of each row is a
+ * draw of K experts without replacement, proportional to p (Gumbel-top-k). out[n][E], fp32. */
+void synth_trace_logits(uint64_t seed, int64_t l, int64_t E, double s, int64_t t0, int64_t n,
+                        float* out) {
+  double* logp = (double*)malloc(sizeof(double) * (size_t)E);
+  if (!logp) return;
+  synth_zipf_logp(seed, l, E, s, logp);
+  for (int64_t t = 0; t < n; ++t) {
+    uint64_t key = synth_key(seed, TAG_GUMBEL, (uint64_t)l, (uint64_t)(t0 + t));
+    for (int64_t e = 0; e < E; ++e) {
+      double u = uniform01(draw(key, (uint64_t)e));
+      out[t * E + e] = (float)(logp[e] - log(-log(u)));
+    }
+  }
+  free(logp);
+}
+
+/* Predicted ids for a speculative request: each id of the true set `truth[K]` is kept with
+ * probability keep; every dropped one is replaced by a fresh draw from p (rejection of ids
+ * already in the true set or already chosen).  out[K]. */
+void synth_spec_ids(uint64_t seed, int64_t l, int64_t E, double s, int64_t t, const int32_t* truth,
+                    int K, double keep, int32_t* out) {
+  double* logp = (double*)malloc(sizeof(double) * (size_t)E);
+  double* cdf = (double*)malloc(sizeof(double) * (size_t)E);
+  if (!logp || !cdf) { free(logp); free(cdf); return; }
+  synth_zipf_logp(seed, l, E, s, logp);
+  double acc = 0.0;
+  for (int64_t e = 0; e < E; ++e) { acc += exp(logp[e]); cdf[e] = acc; }
+  uint64_t key = synth_key(seed, TAG_SPEC, (uint64_t)l, (uint64_t)t);
+  uint64_t j = 0;
+  for (int k = 0; k < K; ++k) out[k] = -1;
+  for (int k = 0; k < K; ++k)
+    if (uniform01(draw(key, j++)) < keep) out[k] = truth[k];
+  for (int k = 0; k < K; ++k) {
+    if (out[k] >= 0) continue;
+    for (int tries = 0; tries < 100000; ++tries) {
+      double u = uniform01(draw(key, j++)) * acc;
+      int64_t lo = 0, hi = E - 1;
+      while (lo < hi) { int64_t mid = (lo + hi) / 2; if (cdf[mid] < u) lo = mid + 1; else hi = mid; }
+      int32_t c = (int32_t)lo;
+      int dup = 0;
+      for (int q = 0; q < K; ++q) if (truth[q] == c || out[q] == c) dup = 1;
+      if (!dup) { out[k] = c; break; }
+    }
+  }
+  free(logp);
+  free(cdf);
+}
