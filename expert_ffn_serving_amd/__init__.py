@@ -1,0 +1,266 @@
+"""Python binding of libeff (routed-expert FFN over an HBM slot cache, MI355X).
+
+Argument marshalling only: every step runs in the HIP library (libeff.so, built
+in-tree by ``expert_ffn_serving_amd.build``).  torch is imported first so that
+the process has exactly one HIP runtime (torch's), which libeff then binds to.
+Device arguments are torch tensors on the GPU; streams are torch.cuda.Stream
+objects (or None for the current stream).  Errors raise EffError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch  # noqa: F401  (loads the HIP runtime libeff binds to)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libeff.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "eff.h")
+
+INT4_G32_BF16 = 0
+NVFP4_G16_E4M3 = 1
+SPECULATIVE = 1
+
+EFF_OK, EFF_EINVAL, EFF_ENOMEM, EFF_EHIP, EFF_ECAPTURE, EFF_ESTATE, EFF_EDEVICE = 0, -1, -2, -3, -4, -5, -6
+
+
+class EffError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("libeff error %d: %s" % (code, msg))
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("wformat", ctypes.c_int32),
+                ("num_slots", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("max_prefill_tokens", ctypes.c_int32), ("fetch_frac_q16", ctypes.c_uint32),
+                ("host_threads", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int64), ("hits", ctypes.c_int64), ("fetched", ctypes.c_int64),
+                ("host", ctypes.c_int64), ("spec_fetched", ctypes.c_int64), ("bytes_fetched", ctypes.c_int64),
+                ("qstar_hist", ctypes.c_int64 * 17)]
+
+
+_lib = None
+VP, I32, U32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_int64
+
+
+def lib():
+    """Load libeff.so; fails loudly when the HIP library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libeff.so is not built (run: python -m expert_ffn_serving_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "eff_last_error": (ctypes.c_char_p, []),
+            "eff_record_bytes": (I64, [VP]),
+            "eff_create": (I32, [VP, VP, VP, VP]),
+            "eff_destroy": (I32, [VP]),
+            "eff_host_alloc": (I32, [ctypes.c_size_t, VP]),
+            "eff_host_free": (I32, [VP]),
+            "eff_route": (I32, [VP, VP, VP, I32, VP, VP, VP]),
+            "eff_route_logits": (I32, [VP, VP, I32, VP, VP, VP]),
+            "eff_ensure_experts": (I32, [VP, I32, VP, I32, U32, VP]),
+            "eff_split_misses": (I32, [VP, VP, VP, VP, VP]),
+            "eff_qstar": (I64, [I64, U32]),
+            "eff_qstar_batch": (I32, [VP, VP, VP, I32, VP]),
+            "eff_copy_missing": (I32, [VP, VP, VP]),
+            "eff_expert_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP, VP]),
+            "eff_host_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP]),
+            "eff_combine": (I32, [VP, VP, VP, VP, VP, I32, VP, VP]),
+            "eff_decode_layer": (I32, [VP, I32, VP, VP, VP, I32, VP, VP, VP, VP]),
+            "eff_last_layer_info": (I32, [VP, VP, VP, VP, VP, VP]),
+            "eff_prefill_stream_layer": (I32, [VP, I32, VP]),
+            "eff_expert_ffn_prefill_layer": (I32, [VP, I32, VP, VP, VP, I32, VP, VP]),
+            "eff_snapshot_tables": (I32, [VP, VP, VP, VP, VP, VP]),
+            "eff_get_stats": (I32, [VP, VP]),
+            "eff_slot_ptr": (I32, [VP, I32, VP]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_functions():
+    """Names of the functions include/eff.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(eff_\w+)\s*\(", text, re.M)))
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise EffError(rc, lib().eff_last_error().decode())
+
+
+def _p(t) -> int:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _s(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+_hip = None
+
+
+def _memcpy_d2h(dst: int, src: int, nbytes: int):
+    """hipMemcpy device -> host through the HIP runtime torch loaded (the one libeff uses)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so.7")
+        _hip.hipMemcpy.restype = ctypes.c_int
+        _hip.hipMemcpy.argtypes = [VP, VP, ctypes.c_size_t, ctypes.c_int]
+    rc = _hip.hipMemcpy(dst, src, nbytes, 2)  # hipMemcpyDeviceToHost
+    if rc != 0:
+        raise EffError(EFF_EHIP, "hipMemcpy failed: %d" % rc)
+
+
+def qstar(m: int, f: int) -> int:
+    return int(lib().eff_qstar(m, f))
+
+
+def qstar_batch(m, f, q, stream=None):
+    _check(lib().eff_qstar_batch(_p(m), _p(f), _p(q), m.numel(), _s(stream)))
+
+
+def host_alloc(nbytes: int) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().eff_host_alloc(nbytes, ctypes.byref(out)))
+    return out.value
+
+
+def host_free(ptr: int):
+    _check(lib().eff_host_free(ptr))
+
+
+def make_config(L, E, K, H, I, wformat, S, max_tokens, max_prefill_tokens=0, f_q16=65536, host_threads=0):
+    return Config(L, E, K, H, I, wformat, S, max_tokens, max_prefill_tokens, f_q16, host_threads, 0)
+
+
+def record_bytes(cfg: Config) -> int:
+    return int(lib().eff_record_bytes(ctypes.byref(cfg)))
+
+
+class Engine:
+    """One libeff engine.  host_pool: address of L*E*R bytes of pinned host memory (kept
+    alive by the caller); tensor_scales: numpy float32 [L*E*3] or None (int4)."""
+
+    def __init__(self, cfg: Config, host_pool: int, tensor_scales=None):
+        self.cfg = cfg
+        self._ts = None if tensor_scales is None else tensor_scales.astype("float32").copy()
+        h = ctypes.c_void_p()
+        _check(lib().eff_create(ctypes.byref(cfg), host_pool,
+                                None if self._ts is None else self._ts.ctypes.data, ctypes.byref(h)))
+        self.h = h.value
+
+    def close(self):
+        if self.h:
+            _check(lib().eff_destroy(self.h))
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- decode primitives
+    def route(self, x, w_router, ids, w, stream=None):
+        _check(lib().eff_route(self.h, _p(x), _p(w_router), x.shape[0], _p(ids), _p(w), _s(stream)))
+
+    def route_logits(self, logits, ids, w, stream=None):
+        _check(lib().eff_route_logits(self.h, _p(logits), logits.shape[0], _p(ids), _p(w), _s(stream)))
+
+    def ensure_experts(self, layer, ids, flags=0, stream=None):
+        _check(lib().eff_ensure_experts(self.h, layer, _p(ids), ids.numel(), flags, _s(stream)))
+
+    def split_misses(self, ids, cpu_ids, counts, stream=None):
+        _check(lib().eff_split_misses(self.h, _p(ids), _p(cpu_ids), _p(counts), _s(stream)))
+
+    def copy_missing(self, compute=None, side=None):
+        _check(lib().eff_copy_missing(self.h, _s(compute), _s(side) if side is not None else _s(compute)))
+
+    def expert_ffn_decode(self, layer, x, slots, y, stream=None):
+        _check(lib().eff_expert_ffn_decode(self.h, layer, _p(x), _p(slots), x.shape[0], _p(y), _s(stream)))
+
+    def host_ffn_decode(self, layer, x_host, cpu_ids_host, y_host):
+        """numpy arrays: x uint16 [B,H], cpu_ids int32 [B*K], y float32 [B,K,H]."""
+        _check(lib().eff_host_ffn_decode(self.h, layer, x_host.ctypes.data, cpu_ids_host.ctypes.data,
+                                         x_host.shape[0], y_host.ctypes.data))
+
+    def combine(self, y_gpu, y_host, slots, w, out, stream=None):
+        _check(lib().eff_combine(self.h, _p(y_gpu), _p(y_host), _p(slots), _p(w), out.shape[0], _p(out),
+                                 _s(stream)))
+
+    def decode_layer(self, layer, x, out, w_router=None, logits=None, spec_ids=None, compute=None, side=None):
+        _check(lib().eff_decode_layer(self.h, layer, _p(x), _p(w_router), _p(logits), x.shape[0], _p(spec_ids),
+                                      _p(out), _s(compute), _s(side) if side is not None else _s(compute)))
+
+    def last_layer_arrays(self, B: int) -> dict:
+        """Host copies of the last eff_decode_layer's ids, slots, host ids (int32 [B*K]) and counts [6]."""
+        import numpy as np
+        ids, _, slots, cpu, counts = self.last_layer_info()
+        n = B * self.cfg.top_k
+        torch.cuda.synchronize()
+        out = {}
+        for name, ptr, cnt in (("ids", ids, n), ("slots", slots, n), ("cpu", cpu, n), ("counts", counts, 6)):
+            host = np.empty(cnt, np.int32)
+            _memcpy_d2h(host.ctypes.data, ptr, cnt * 4)
+            out[name] = host
+        return out
+
+    def last_layer_info(self):
+        """Device addresses (ids, w, slots, cpu_ids, counts) of the last eff_decode_layer."""
+        vals = [ctypes.c_void_p() for _ in range(5)]
+        _check(lib().eff_last_layer_info(self.h, *[ctypes.byref(v) for v in vals]))
+        return [v.value for v in vals]
+
+    # -- prefill
+    def prefill_stream_layer(self, layer, side=None):
+        _check(lib().eff_prefill_stream_layer(self.h, layer, _s(side)))
+
+    def expert_ffn_prefill_layer(self, layer, x, ids, w, out, stream=None):
+        _check(lib().eff_expert_ffn_prefill_layer(self.h, layer, _p(x), _p(ids), _p(w), x.shape[0], _p(out),
+                                                  _s(stream)))
+
+    # -- diagnostics
+    def snapshot_tables(self):
+        import numpy as np
+        c = self.cfg
+        table = np.empty(c.num_layers * c.num_experts, np.int32)
+        owner = np.empty(max(1, c.num_slots), np.int32)
+        usage = np.empty(max(1, c.num_slots), np.int64)
+        recency = np.empty(c.num_layers * c.num_experts, np.int64)
+        clock = np.empty(2, np.int64)
+        _check(lib().eff_snapshot_tables(self.h, table.ctypes.data, owner.ctypes.data, usage.ctypes.data,
+                                         recency.ctypes.data, clock.ctypes.data))
+        return dict(table=table, owner=owner[:c.num_slots], usage=usage[:c.num_slots], recency=recency,
+                    step=int(clock[0]), last_real=int(clock[1]))
+
+    def stats(self) -> dict:
+        st = Stats()
+        _check(lib().eff_get_stats(self.h, ctypes.byref(st)))
+        return dict(calls=st.calls, hits=st.hits, fetched=st.fetched, host=st.host,
+                    spec_fetched=st.spec_fetched, bytes_fetched=st.bytes_fetched,
+                    qstar_hist=list(st.qstar_hist))
+
+    def slot_ptr(self, slot: int) -> int:
+        out = ctypes.c_void_p()
+        _check(lib().eff_slot_ptr(self.h, slot, ctypes.byref(out)))
+        return out.value

@@ -1,0 +1,189 @@
+// Internal declarations shared by the libeff translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <condition_variable>
+#include <cstdint>
+#include <functional>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/eff.h"
+
+namespace eff {
+
+constexpr int kMaxTokens = 32;        // decode batch bound
+constexpr int kMaxTopK = 32;
+constexpr int kMaxEntries = kMaxTokens * kMaxTopK;  // entries of one decode call
+constexpr int kMaxSlots = 16384;      // single-workgroup victim sort (keys in LDS)
+constexpr int kMaxExperts = 4096;
+
+// Error reporting -----------------------------------------------------------------------------
+void set_error(const std::string& msg);
+int fail(int code, const std::string& msg);
+#define EFF_HIP_TRY(expr)                                                                  \
+  do {                                                                                     \
+    hipError_t _e = (expr);                                                                \
+    if (_e != hipSuccess)                                                                  \
+      return ::eff::fail(EFF_EHIP, std::string(#expr) + ": " + hipGetErrorString(_e));     \
+  } while (0)
+
+// Pending ensure (device-resident) ----------------------------------------------------------------
+struct Pending {
+  int32_t valid;       // 1 while an ensure waits for its split
+  int32_t layer;
+  int32_t n;           // entries
+  int32_t spec;        // speculative call
+  int64_t s;           // step of the call
+  int64_t floor_;      // victims need usage < floor_
+  int32_t nuniq, nmiss;
+  int32_t ids[kMaxEntries];    // routed expert ids of the call
+  int32_t uniq[kMaxEntries];   // unique ids ascending
+  int32_t miss[kMaxEntries];   // unique missing ids ascending
+};
+
+// Fetch list written by the split kernel (device memory and a host-mapped mirror) ----------------
+struct FetchList {
+  int32_t count;
+  int32_t err;         // device error word of the ensure/split pair (bit 1: bad id, bit 2: no pending)
+  int32_t flat[kMaxEntries];
+  int32_t slot[kMaxEntries];
+};
+
+// Plan of one decode expert-FFN call: distinct GPU slots and their entries ----------------------
+struct DecodePlan {
+  int32_t nu;
+  int32_t uslot[kMaxEntries];
+  int32_t ucount[kMaxEntries];
+  int32_t uentry[kMaxEntries][kMaxTokens];  // entry p = t*K + k
+};
+
+// Device stats counters (int64) ----------------------------------------------------------------
+enum { ST_CALLS, ST_HITS, ST_FETCHED, ST_HOST, ST_SPEC_FETCHED, ST_HIST0, ST_COUNT = ST_HIST0 + 17 };
+
+// Host thread pool for the host executor --------------------------------------------------------
+class ThreadPool {
+ public:
+  explicit ThreadPool(int n);
+  ~ThreadPool();
+  // run fn(i) for i in [0, n) on the pool and the calling thread; returns when all are done
+  void parallel_for(int n, const std::function<void(int)>& fn);
+  int size() const { return (int)workers_.size() + 1; }
+
+ private:
+  void loop();
+  std::vector<std::thread> workers_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_cv_;
+  const std::function<void(int)>* fn_ = nullptr;
+  int n_ = 0;
+  std::atomic<int> next_{0};
+  int active_ = 0;
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+};
+
+}  // namespace eff
+
+struct eff_engine {
+  eff_config cfg;
+  int64_t R = 0;              // record bytes
+  const uint8_t* pool = nullptr;
+  int device = 0;
+
+  // slot arena and tables (device)
+  uint8_t* d_arena = nullptr;
+  int32_t* d_table = nullptr;
+  int32_t* d_owner = nullptr;
+  int64_t* d_usage = nullptr;
+  int64_t* d_recency = nullptr;
+  int64_t* d_clock = nullptr;     // {step, last_real}
+  float* d_ts = nullptr;          // [L*E*3]
+  eff::Pending* d_pending = nullptr;
+  eff::FetchList* d_fetch = nullptr;   // [2]: real, speculative
+  eff::FetchList* h_fetch = nullptr;   // host-mapped mirror [2] (host view)
+  eff::FetchList* h_fetch_dev = nullptr;  // the same memory as seen by kernels
+  int32_t* d_err = nullptr;            // device error word
+  int64_t* d_stats = nullptr;
+  bool pending_host = false;           // host-side mirror of Pending::valid
+  bool spec_pending_call = false;      // the pending ensure is speculative
+  bool spec_split_pending = false;     // a speculative split's fetches not yet copied
+  bool real_split_pending = false;
+
+  // decode scratch
+  eff::DecodePlan* d_plan = nullptr;
+  float* d_a = nullptr;           // [maxU][I][maxB] fp32 SwiGLU activations
+  float* d_part = nullptr;        // gate/up partial sums for split-k
+  int32_t* d_counters = nullptr;  // last-block counters
+  int ksplit = 1;
+  int maxU = 0;
+
+  // orchestrator buffers (device)
+  int32_t* d_ids = nullptr;
+  float* d_w = nullptr;
+  int32_t* d_slots = nullptr;
+  int32_t* d_cpu = nullptr;
+  int32_t* d_counts = nullptr;    // [6]
+  int32_t* d_spec_ids = nullptr;
+  int32_t* d_spec_cpu = nullptr;
+  float* d_logits = nullptr;      // [maxT or maxB][E]
+  float* d_ygpu = nullptr;        // [maxB*K*H]
+  float* d_yhost = nullptr;       // [maxB*K*H]
+  // pinned host staging
+  uint16_t* h_x = nullptr;        // [maxB*H]
+  int32_t* h_cpu = nullptr;       // [maxB*K]
+  float* h_yhost = nullptr;       // [maxB*K*H]
+
+  // prefill scratch
+  int32_t* d_pf_count = nullptr;  // [E+1] per-expert counts / offsets
+  int32_t* d_pf_rows = nullptr;   // [T*K] sorted entries (t*K+k)
+  uint16_t* d_pf_a = nullptr;     // [T*K][I] fp16 SwiGLU activations
+  float* d_pf_y = nullptr;        // [T*K][H] fp32 expert outputs
+  int32_t* d_pf_meta = nullptr;   // misc
+  hipEvent_t ev_copy = nullptr, ev_spec = nullptr, ev_pf[2] = {nullptr, nullptr};
+  bool pf_streamed[2] = {false, false};
+  int pf_layer[2] = {-1, -1};
+
+  std::vector<float> h_ts;        // host copy of the tensor scales (host executor)
+  int32_t* h_err = nullptr;       // host-mapped mirror of the device error word
+  hipEvent_t ev_pf_done[2] = {nullptr, nullptr};
+  bool pf_done_recorded[2] = {false, false};
+  int32_t* d_pf_slot_of = nullptr;  // [E] slot per expert (fallback prefill)
+  int32_t* d_pf_experts = nullptr;  // [E] expert list of a fallback group
+  int32_t* h_pf_ids = nullptr;      // pinned [T*K]
+  int32_t* h_pf_meta = nullptr;     // pinned [2E]
+  eff::ThreadPool* pool_threads = nullptr;
+  int64_t host_bytes_fetched = 0;
+  int64_t host_spec_fetched = 0;
+};
+
+// Kernel launchers (implemented in the .hip files) -------------------------------------------------
+namespace eff {
+hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, int B, int E, int H, float* logits,
+                               hipStream_t s);
+hipError_t launch_topk(const float* logits, int B, int E, int K, int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_ensure(eff_engine* e, int layer, int32_t* ids, int n, int spec, hipStream_t s);
+hipError_t launch_split(eff_engine* e, int32_t* ids, int32_t* cpu_ids, int32_t* counts, int which,
+                        hipStream_t s);
+hipError_t launch_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, int n, hipStream_t s);
+hipError_t launch_prefill_install(eff_engine* e, int layer, hipStream_t s);
+hipError_t launch_fallback_install(eff_engine* e, int layer, const int32_t* experts, int n,
+                                   hipStream_t s);
+hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
+                             float* y, hipStream_t s);
+hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
+                          int B, int K, int H, uint16_t* out, hipStream_t s);
+hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int32_t* ids,
+                          const float* w, int T, uint16_t* out, const int32_t* slot_of_expert,
+                          int slot_base, bool combine, hipStream_t s);
+hipError_t split_kernel_setup(int S);
+hipError_t decode_kernels_setup(int fmt, int maxB, int I);
+int decode_nt(int maxB);
+int64_t qstar_host(int64_t m, int64_t f);
+// host executor
+void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_ids, int B, float* y);
+}  // namespace eff

@@ -1,0 +1,535 @@
+// libeff host side: engine lifecycle, the C ABI entry points, the eager decode-layer
+// orchestration and prefill streaming.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "eff_internal.h"
+
+namespace eff {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+static bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+static int validate(const eff_config* c, std::string* why) {
+  auto bad = [&](const char* m) {
+    *why = m;
+    return EFF_EINVAL;
+  };
+  if (!c) return bad("config is NULL");
+  if (c->num_layers < 1) return bad("num_layers must be >= 1");
+  if (c->num_experts < 1 || c->num_experts > kMaxExperts) return bad("num_experts must be in [1, 4096]");
+  if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->num_experts) return bad("top_k must be in [1, min(32, E)]");
+  if (c->hidden < 64 || c->hidden % 64) return bad("hidden must be a positive multiple of 64");
+  if (c->inter < 64 || c->inter % 64 || c->inter > 4096) return bad("inter must be a multiple of 64 in [64, 4096]");
+  if (c->wformat != EFF_WFMT_INT4_G32_BF16 && c->wformat != EFF_WFMT_NVFP4_G16_E4M3) return bad("unknown wformat");
+  if (c->num_slots < 0 || c->num_slots > kMaxSlots) return bad("num_slots must be in [0, 16384]");
+  if (c->max_tokens < 1 || c->max_tokens > kMaxTokens) return bad("max_tokens must be in [1, 32]");
+  if (c->max_prefill_tokens < 0) return bad("max_prefill_tokens must be >= 0");
+  if (c->fetch_frac_q16 > 65536u) return bad("fetch_frac_q16 must be in [0, 65536]");
+  if (c->host_threads < 0 || c->host_threads > 256) return bad("host_threads must be in [0, 256]");
+  if ((int64_t)c->num_layers * c->num_experts > (int64_t)1 << 30) return bad("L*E too large");
+  return EFF_OK;
+}
+
+static int64_t record_bytes(const eff_config* c) {
+  return 3 * (int64_t)c->hidden * c->inter / 2 + 3 * (int64_t)c->hidden * c->inter / 16;
+}
+
+template <typename T>
+static hipError_t dalloc(T** p, size_t count) {
+  return hipMalloc((void**)p, std::max<size_t>(1, count) * sizeof(T));
+}
+
+static void release(eff_engine* e) {
+  if (!e) return;
+  void* dev[] = {e->d_arena, e->d_table, e->d_owner, e->d_usage, e->d_recency, e->d_clock, e->d_ts,
+                 e->d_pending, e->d_fetch, e->d_err, e->d_stats, e->d_plan, e->d_a, e->d_part,
+                 e->d_counters, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, e->d_spec_ids,
+                 e->d_spec_cpu, e->d_logits, e->d_ygpu, e->d_yhost, e->d_pf_count, e->d_pf_rows,
+                 e->d_pf_a, e->d_pf_y, e->d_pf_meta, e->d_pf_slot_of, e->d_pf_experts};
+  for (void* p : dev)
+    if (p) (void)hipFree(p);
+  void* host[] = {e->h_fetch, e->h_x, e->h_cpu, e->h_yhost, e->h_pf_ids, e->h_pf_meta};
+  for (void* p : host)
+    if (p) (void)hipHostFree(p);
+  hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0], e->ev_pf_done[1]};
+  for (hipEvent_t v : evs)
+    if (v) (void)hipEventDestroy(v);
+  delete e->pool_threads;
+  delete e;
+}
+
+static int alloc_all(eff_engine* e) {
+  const eff_config& c = e->cfg;
+  const int64_t L = c.num_layers, E = c.num_experts, S = c.num_slots, H = c.hidden, I = c.inter;
+  const int64_t K = c.top_k, B = c.max_tokens, T = c.max_prefill_tokens;
+  EFF_HIP_TRY(dalloc(&e->d_arena, (size_t)(S * e->R)));
+  EFF_HIP_TRY(dalloc(&e->d_table, L * E));
+  EFF_HIP_TRY(dalloc(&e->d_owner, S));
+  EFF_HIP_TRY(dalloc(&e->d_usage, S));
+  EFF_HIP_TRY(dalloc(&e->d_recency, L * E));
+  EFF_HIP_TRY(dalloc(&e->d_clock, 2));
+  EFF_HIP_TRY(dalloc(&e->d_ts, L * E * 3));
+  EFF_HIP_TRY(dalloc(&e->d_pending, 1));
+  EFF_HIP_TRY(dalloc(&e->d_fetch, 2));
+  EFF_HIP_TRY(dalloc(&e->d_err, 1));
+  EFF_HIP_TRY(dalloc(&e->d_stats, ST_COUNT));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_fetch, 2 * sizeof(FetchList), hipHostMallocMapped));
+  EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_fetch_dev, e->h_fetch, 0));
+  // decode scratch
+  e->maxU = (int)std::min<int64_t>(B * K, E);
+  const int NB = (int)(I / 64), KB = (int)(H / 32);
+  // split-k for the gate/up pass: enough workgroups to cover the chip at batch 1
+  int ks = 1;
+  while (ks * 2 <= KB && KB % (ks * 2) == 0 && (int64_t)e->maxU * NB * ks < 1024 && ks < 16) ks *= 2;
+  e->ksplit = ks;
+  EFF_HIP_TRY(dalloc(&e->d_plan, 1));
+  EFF_HIP_TRY(dalloc(&e->d_a, (size_t)e->maxU * B * I));
+  EFF_HIP_TRY(dalloc(&e->d_part, (size_t)e->maxU * NB * ks * 2 * 64 * B));
+  EFF_HIP_TRY(dalloc(&e->d_counters, (size_t)e->maxU * NB));
+  // orchestrator
+  EFF_HIP_TRY(dalloc(&e->d_ids, B * K));
+  EFF_HIP_TRY(dalloc(&e->d_w, B * K));
+  EFF_HIP_TRY(dalloc(&e->d_slots, B * K));
+  EFF_HIP_TRY(dalloc(&e->d_cpu, B * K));
+  EFF_HIP_TRY(dalloc(&e->d_counts, 6));
+  EFF_HIP_TRY(dalloc(&e->d_spec_ids, B * K));
+  EFF_HIP_TRY(dalloc(&e->d_spec_cpu, B * K));
+  EFF_HIP_TRY(dalloc(&e->d_logits, std::max(B, T) * E));
+  EFF_HIP_TRY(dalloc(&e->d_ygpu, B * K * H));
+  EFF_HIP_TRY(dalloc(&e->d_yhost, B * K * H));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_x, (size_t)(B * H) * 2, 0));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_cpu, (size_t)(B * K) * 4, 0));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_yhost, (size_t)(B * K * H) * 4, 0));
+  // prefill
+  if (T > 0) {
+    EFF_HIP_TRY(dalloc(&e->d_pf_count, E + 1));
+    EFF_HIP_TRY(dalloc(&e->d_pf_rows, T * K));
+    EFF_HIP_TRY(dalloc(&e->d_pf_a, (size_t)(T * K * I)));
+    EFF_HIP_TRY(dalloc(&e->d_pf_y, (size_t)(T * K * H)));
+    EFF_HIP_TRY(dalloc(&e->d_pf_slot_of, E));
+    EFF_HIP_TRY(dalloc(&e->d_pf_experts, E));
+    EFF_HIP_TRY(hipHostMalloc((void**)&e->h_pf_ids, (size_t)(T * K) * 4, 0));
+    EFF_HIP_TRY(hipHostMalloc((void**)&e->h_pf_meta, (size_t)(2 * E) * 4, 0));
+  }
+  EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_copy, hipEventDisableTiming));
+  EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_spec, hipEventDisableTiming));
+  for (int b = 0; b < 2; ++b) {
+    EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_pf[b], hipEventDisableTiming));
+    EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_pf_done[b], hipEventDisableTiming));
+  }
+  // initial state: empty cache
+  EFF_HIP_TRY(hipMemset(e->d_table, 0xFF, (size_t)(L * E) * 4));
+  EFF_HIP_TRY(hipMemset(e->d_owner, 0xFF, (size_t)std::max<int64_t>(1, S) * 4));
+  EFF_HIP_TRY(hipMemset(e->d_usage, 0xFF, (size_t)std::max<int64_t>(1, S) * 8));
+  EFF_HIP_TRY(hipMemset(e->d_recency, 0xFF, (size_t)(L * E) * 8));
+  EFF_HIP_TRY(hipMemset(e->d_clock, 0, 16));
+  EFF_HIP_TRY(hipMemset(e->d_pending, 0, sizeof(Pending)));
+  EFF_HIP_TRY(hipMemset(e->d_err, 0, 4));
+  EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
+  EFF_HIP_TRY(hipMemset(e->d_counters, 0, (size_t)e->maxU * NB * 4));
+  std::memset(e->h_fetch, 0, 2 * sizeof(FetchList));
+  EFF_HIP_TRY(split_kernel_setup((int)S));
+  EFF_HIP_TRY(decode_kernels_setup(c.wformat, (int)B, (int)I));
+  EFF_HIP_TRY(hipDeviceSynchronize());
+  return EFF_OK;
+}
+
+static int check_engine(eff_engine* e) {
+  if (!e) return fail(EFF_EINVAL, "engine is NULL");
+  return EFF_OK;
+}
+
+static int read_device_error(eff_engine* e) {
+  for (int w = 0; w < 2; ++w) {
+    const int err = e->h_fetch[w].err;
+    if (err) {
+      e->h_fetch[w].err = 0;
+      return fail(EFF_EDEVICE, (err & 1) ? "an expert id was outside [0, E) (entries skipped)"
+                                         : "split ran without a pending ensure");
+    }
+  }
+  return EFF_OK;
+}
+
+}  // namespace eff
+
+using namespace eff;
+
+extern "C" {
+
+const char* eff_last_error(void) { return g_last_error.c_str(); }
+
+int64_t eff_record_bytes(const eff_config* cfg) {
+  std::string why;
+  if (validate(cfg, &why) != EFF_OK) return 0;
+  return record_bytes(cfg);
+}
+
+int eff_host_alloc(size_t bytes, void** out) {
+  if (!out || bytes == 0) return fail(EFF_EINVAL, "eff_host_alloc: bad arguments");
+  hipError_t err = hipHostMalloc(out, bytes, hipHostMallocMapped | hipHostMallocPortable);
+  if (err != hipSuccess) return fail(EFF_ENOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(err));
+  return EFF_OK;
+}
+
+int eff_host_free(void* p) {
+  if (!p) return EFF_OK;
+  EFF_HIP_TRY(hipHostFree(p));
+  return EFF_OK;
+}
+
+int eff_create(const eff_config* cfg, const void* host_pool, const float* tensor_scales, eff_engine** out) {
+  std::string why;
+  if (!out) return fail(EFF_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (validate(cfg, &why) != EFF_OK) return fail(EFF_EINVAL, why);
+  if (!host_pool) return fail(EFF_EINVAL, "host_pool is NULL");
+  if (cfg->wformat == EFF_WFMT_NVFP4_G16_E4M3 && !tensor_scales)
+    return fail(EFF_EINVAL, "NVFP4 needs tensor_scales");
+  const int64_t R = record_bytes(cfg);
+  // the pool must be pinned host memory covering L*E records
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host_pool) != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(EFF_EINVAL, "host_pool is not pinned host memory (use hipHostMalloc / eff_host_alloc)");
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(EFF_EHIP, "no HIP device");
+  size_t free_b = 0, total_b = 0;
+  if (hipMemGetInfo(&free_b, &total_b) == hipSuccess &&
+      (uint64_t)cfg->num_slots * (uint64_t)R > (uint64_t)free_b)
+    return fail(EFF_ENOMEM, "slot arena does not fit in free device memory");
+  eff_engine* e = new (std::nothrow) eff_engine();
+  if (!e) return fail(EFF_ENOMEM, "engine allocation failed");
+  e->cfg = *cfg;
+  e->R = R;
+  e->pool = (const uint8_t*)host_pool;
+  e->device = dev;
+  int rc = alloc_all(e);
+  if (rc != EFF_OK) {
+    std::string msg = g_last_error;
+    release(e);
+    return fail(rc == EFF_EHIP ? EFF_ENOMEM : rc, msg);
+  }
+  const size_t nts = (size_t)cfg->num_layers * cfg->num_experts * 3;
+  e->h_ts.assign(nts, 1.0f);
+  if (tensor_scales) std::memcpy(e->h_ts.data(), tensor_scales, nts * sizeof(float));
+  if (hipMemcpy(e->d_ts, e->h_ts.data(), nts * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+    release(e);
+    return fail(EFF_EHIP, "copying tensor scales failed");
+  }
+  int nth = cfg->host_threads;
+  if (nth == 0) nth = (int)std::max(1u, std::thread::hardware_concurrency());
+  e->pool_threads = new (std::nothrow) ThreadPool(nth);
+  if (!e->pool_threads) {
+    release(e);
+    return fail(EFF_ENOMEM, "thread pool");
+  }
+  *out = e;
+  return EFF_OK;
+}
+
+int eff_destroy(eff_engine* e) {
+  if (!e) return EFF_OK;
+  (void)hipDeviceSynchronize();
+  release(e);
+  return EFF_OK;
+}
+
+int eff_route(eff_engine* e, const void* x, const void* w_router, int B, int32_t* ids, float* w,
+              eff_stream_t stream) {
+  if (int rc = check_engine(e)) return rc;
+  const int maxB = std::max(e->cfg.max_tokens, e->cfg.max_prefill_tokens);
+  if (!x || !w_router || !ids || !w || B < 1 || B > maxB) return fail(EFF_EINVAL, "eff_route: bad arguments");
+  hipStream_t s = (hipStream_t)stream;
+  EFF_HIP_TRY(launch_route_logits((const uint16_t*)x, (const uint16_t*)w_router, B, e->cfg.num_experts,
+                                  e->cfg.hidden, e->d_logits, s));
+  EFF_HIP_TRY(launch_topk(e->d_logits, B, e->cfg.num_experts, e->cfg.top_k, ids, w, s));
+  return EFF_OK;
+}
+
+int eff_route_logits(eff_engine* e, const float* logits, int B, int32_t* ids, float* w, eff_stream_t stream) {
+  if (int rc = check_engine(e)) return rc;
+  const int maxB = std::max(e->cfg.max_tokens, e->cfg.max_prefill_tokens);
+  if (!logits || !ids || !w || B < 1 || B > maxB) return fail(EFF_EINVAL, "eff_route_logits: bad arguments");
+  EFF_HIP_TRY(launch_topk(logits, B, e->cfg.num_experts, e->cfg.top_k, ids, w, (hipStream_t)stream));
+  return EFF_OK;
+}
+
+int eff_ensure_experts(eff_engine* e, int layer, int32_t* ids_inout, int n, uint32_t flags, eff_stream_t stream) {
+  if (int rc = check_engine(e)) return rc;
+  if (!ids_inout || layer < 0 || layer >= e->cfg.num_layers || n < 1 || n > e->cfg.max_tokens * e->cfg.top_k)
+    return fail(EFF_EINVAL, "eff_ensure_experts: bad arguments");
+  if (flags & ~(uint32_t)EFF_SPECULATIVE) return fail(EFF_EINVAL, "eff_ensure_experts: unknown flags");
+  if (e->pending_host) return fail(EFF_ESTATE, "an ensure is already pending its split");
+  EFF_HIP_TRY(launch_ensure(e, layer, ids_inout, n, (flags & EFF_SPECULATIVE) ? 1 : 0, (hipStream_t)stream));
+  e->pending_host = true;
+  e->spec_pending_call = (flags & EFF_SPECULATIVE) != 0;
+  return EFF_OK;
+}
+
+int eff_split_misses(eff_engine* e, int32_t* ids_inout, int32_t* cpu_ids, int32_t* counts, eff_stream_t stream) {
+  if (int rc = check_engine(e)) return rc;
+  if (!ids_inout) return fail(EFF_EINVAL, "eff_split_misses: ids is NULL");
+  if (!e->pending_host) return fail(EFF_ESTATE, "split without a pending ensure");
+  EFF_HIP_TRY(launch_split(e, ids_inout, cpu_ids, counts, 0, (hipStream_t)stream));
+  e->pending_host = false;
+  if (e->spec_pending_call) e->spec_split_pending = true;
+  else e->real_split_pending = true;
+  return EFF_OK;
+}
+
+int64_t eff_qstar(int64_t m, uint32_t f) {
+  if (m < 0 || m > ((int64_t)1 << 40) || f > 65536u) return -1;
+  return qstar_host(m, f);
+}
+
+int eff_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, int n, eff_stream_t stream) {
+  if ((!m || !f || !q) && n > 0) return fail(EFF_EINVAL, "eff_qstar_batch: NULL pointer");
+  if (n < 0) return fail(EFF_EINVAL, "eff_qstar_batch: n < 0");
+  EFF_HIP_TRY(launch_qstar_batch(m, f, q, n, (hipStream_t)stream));
+  return EFF_OK;
+}
+
+static int issue_copies(eff_engine* e, int which, hipStream_t side) {
+  const FetchList& fl = e->h_fetch[which];
+  for (int i = 0; i < fl.count; ++i) {
+    const int64_t flat = fl.flat[i], slot = fl.slot[i];
+    EFF_HIP_TRY(hipMemcpyAsync(e->d_arena + slot * e->R, e->pool + flat * e->R, (size_t)e->R,
+                               hipMemcpyHostToDevice, side));
+  }
+  if (which == 0) e->host_bytes_fetched += (int64_t)fl.count * e->R;
+  else e->host_spec_fetched += fl.count;
+  return EFF_OK;
+}
+
+int eff_copy_missing(eff_engine* e, eff_stream_t compute, eff_stream_t side) {
+  if (int rc = check_engine(e)) return rc;
+  hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
+  if (capturing(cs) || capturing(ss)) return fail(EFF_ECAPTURE, "eff_copy_missing waits on the host");
+  EFF_HIP_TRY(hipStreamSynchronize(cs));
+  if (int rc = read_device_error(e)) return rc;
+  if (e->real_split_pending) {
+    if (int rc = issue_copies(e, 0, ss)) return rc;
+    e->real_split_pending = false;
+  }
+  if (e->spec_split_pending) {
+    if (int rc = issue_copies(e, 1, ss)) return rc;
+    e->spec_split_pending = false;
+  }
+  // compute waits for every copy issued so far (the side stream is in order, so this also
+  // covers speculative copies issued one layer earlier that this layer now hits)
+  EFF_HIP_TRY(hipEventRecord(e->ev_copy, ss));
+  EFF_HIP_TRY(hipStreamWaitEvent(cs, e->ev_copy, 0));
+  return EFF_OK;
+}
+
+int eff_expert_ffn_decode(eff_engine* e, int layer, const void* x, const int32_t* slots, int B, float* y,
+                          eff_stream_t stream) {
+  if (int rc = check_engine(e)) return rc;
+  if (!x || !slots || !y || B < 1 || B > e->cfg.max_tokens || layer < 0 || layer >= e->cfg.num_layers)
+    return fail(EFF_EINVAL, "eff_expert_ffn_decode: bad arguments");
+  EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, slots, B, y, (hipStream_t)stream));
+  return EFF_OK;
+}
+
+int eff_host_ffn_decode(eff_engine* e, int layer, const void* x_host, const int32_t* cpu_ids_host, int B,
+                        float* y_host) {
+  if (int rc = check_engine(e)) return rc;
+  if (!x_host || !cpu_ids_host || !y_host || B < 1 || B > e->cfg.max_tokens || layer < 0 ||
+      layer >= e->cfg.num_layers)
+    return fail(EFF_EINVAL, "eff_host_ffn_decode: bad arguments");
+  host_ffn(e, layer, (const uint16_t*)x_host, cpu_ids_host, B, y_host);
+  return EFF_OK;
+}
+
+int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const int32_t* slots, const float* w,
+                int B, void* out, eff_stream_t stream) {
+  if (int rc = check_engine(e)) return rc;
+  if (!y_gpu || !slots || !w || !out || B < 1 || B > std::max(e->cfg.max_tokens, e->cfg.max_prefill_tokens))
+    return fail(EFF_EINVAL, "eff_combine: bad arguments");
+  EFF_HIP_TRY(launch_combine(y_gpu, y_host ? y_host : y_gpu, slots, w, B, e->cfg.top_k, e->cfg.hidden,
+                             (uint16_t*)out, (hipStream_t)stream));
+  return EFF_OK;
+}
+
+int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_router, const float* logits, int B,
+                     const int32_t* spec_ids, void* out, eff_stream_t compute, eff_stream_t side) {
+  if (int rc = check_engine(e)) return rc;
+  const eff_config& c = e->cfg;
+  if (!x || !out || (!w_router && !logits) || B < 1 || B > c.max_tokens || layer < 0 || layer >= c.num_layers)
+    return fail(EFF_EINVAL, "eff_decode_layer: bad arguments");
+  hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
+  if (capturing(cs) || capturing(ss)) return fail(EFF_ECAPTURE, "eff_decode_layer waits on the host");
+  const int K = c.top_k, n = B * K;
+  if (w_router) {
+    EFF_HIP_TRY(launch_route_logits((const uint16_t*)x, (const uint16_t*)w_router, B, c.num_experts, c.hidden,
+                                    e->d_logits, cs));
+    EFF_HIP_TRY(launch_topk(e->d_logits, B, c.num_experts, K, e->d_ids, e->d_w, cs));
+  } else {
+    EFF_HIP_TRY(launch_topk(logits, B, c.num_experts, K, e->d_ids, e->d_w, cs));
+  }
+  EFF_HIP_TRY(hipMemcpyAsync(e->d_slots, e->d_ids, (size_t)n * 4, hipMemcpyDeviceToDevice, cs));
+  if (int rc = eff_ensure_experts(e, layer, e->d_slots, n, 0, compute)) return rc;
+  if (int rc = eff_split_misses(e, e->d_slots, e->d_cpu, e->d_counts, compute)) return rc;
+  const bool spec = spec_ids && layer + 1 < c.num_layers;
+  if (spec) {
+    EFF_HIP_TRY(hipMemcpyAsync(e->d_spec_ids, spec_ids, (size_t)n * 4, hipMemcpyDeviceToDevice, cs));
+    if (int rc = eff_ensure_experts(e, layer + 1, e->d_spec_ids, n, EFF_SPECULATIVE, compute)) return rc;
+    if (int rc = eff_split_misses(e, e->d_spec_ids, e->d_spec_cpu, e->d_counts + 3, compute)) return rc;
+  }
+  // host ids and x for the host share come back with the same wait
+  EFF_HIP_TRY(hipMemcpyAsync(e->h_cpu, e->d_cpu, (size_t)n * 4, hipMemcpyDeviceToHost, cs));
+  EFF_HIP_TRY(hipMemcpyAsync(e->h_x, x, (size_t)B * c.hidden * 2, hipMemcpyDeviceToHost, cs));
+  if (int rc = eff_copy_missing(e, compute, side)) return rc;  // waits once on the host
+  EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs));
+  bool any_host = false;
+  for (int p = 0; p < n; ++p) any_host |= e->h_cpu[p] >= 0;
+  if (any_host) {
+    host_ffn(e, layer, e->h_x, e->h_cpu, B, e->h_yhost);  // overlaps the GPU expert kernels
+    EFF_HIP_TRY(hipMemcpyAsync(e->d_yhost, e->h_yhost, (size_t)n * c.hidden * 4, hipMemcpyHostToDevice, cs));
+  }
+  EFF_HIP_TRY(launch_combine(e->d_ygpu, e->d_yhost, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs));
+  return EFF_OK;
+}
+
+int eff_last_layer_info(eff_engine* e, const int32_t** ids, const float** w, const int32_t** slots,
+                        const int32_t** cpu_ids, const int32_t** counts) {
+  if (int rc = check_engine(e)) return rc;
+  if (ids) *ids = e->d_ids;
+  if (w) *w = e->d_w;
+  if (slots) *slots = e->d_slots;
+  if (cpu_ids) *cpu_ids = e->d_cpu;
+  if (counts) *counts = e->d_counts;
+  return EFF_OK;
+}
+
+int eff_prefill_stream_layer(eff_engine* e, int layer, eff_stream_t side) {
+  if (int rc = check_engine(e)) return rc;
+  const eff_config& c = e->cfg;
+  if (layer < 0 || layer >= c.num_layers) return fail(EFF_EINVAL, "eff_prefill_stream_layer: bad layer");
+  if (c.num_slots < 2 * c.num_experts) return fail(EFF_EINVAL, "double buffering needs S >= 2E");
+  hipStream_t ss = (hipStream_t)side;
+  const int b = layer % 2;
+  // the buffer is free once the layer that used it last has finished computing
+  if (e->pf_done_recorded[b]) EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_pf_done[b], 0));
+  EFF_HIP_TRY(launch_prefill_install(e, layer, ss));
+  const int64_t E = c.num_experts;
+  EFF_HIP_TRY(hipMemcpyAsync(e->d_arena + (int64_t)b * E * e->R, e->pool + (int64_t)layer * E * e->R,
+                             (size_t)(E * e->R), hipMemcpyHostToDevice, ss));
+  EFF_HIP_TRY(hipEventRecord(e->ev_pf[b], ss));
+  e->pf_layer[b] = layer;
+  e->pf_streamed[b] = true;
+  return EFF_OK;
+}
+
+int eff_expert_ffn_prefill_layer(eff_engine* e, int layer, const void* x, const int32_t* ids, const float* w,
+                                 int T, void* out, eff_stream_t stream) {
+  if (int rc = check_engine(e)) return rc;
+  const eff_config& c = e->cfg;
+  if (!x || !ids || !w || !out || T < 1 || T > c.max_prefill_tokens || layer < 0 || layer >= c.num_layers)
+    return fail(EFF_EINVAL, "eff_expert_ffn_prefill_layer: bad arguments");
+  hipStream_t cs = (hipStream_t)stream;
+  const int E = c.num_experts, K = c.top_k;
+  if (c.num_slots >= 2 * E) {
+    const int b = layer % 2;
+    if (!e->pf_streamed[b] || e->pf_layer[b] != layer)
+      return fail(EFF_ESTATE, "layer was not streamed (call eff_prefill_stream_layer first)");
+    EFF_HIP_TRY(hipStreamWaitEvent(cs, e->ev_pf[b], 0));
+    EFF_HIP_TRY(launch_prefill(e, layer, (const uint16_t*)x, ids, w, T, (uint16_t*)out, nullptr, b * E, true, cs));
+    EFF_HIP_TRY(hipEventRecord(e->ev_pf_done[b], cs));
+    e->pf_done_recorded[b] = true;
+    e->pf_streamed[b] = false;
+    return EFF_OK;
+  }
+  // on-demand fallback: routed experts ascending, in groups of min(S, E), copy then compute
+  if (capturing(cs)) return fail(EFF_ECAPTURE, "the prefill fallback waits on the host");
+  if (c.num_slots < 1) return fail(EFF_EINVAL, "prefill needs at least one slot");
+  EFF_HIP_TRY(hipMemcpyAsync(e->h_pf_ids, ids, (size_t)T * K * 4, hipMemcpyDeviceToHost, cs));
+  EFF_HIP_TRY(hipStreamSynchronize(cs));
+  std::vector<char> used(E, 0);
+  for (int p = 0; p < T * K; ++p)
+    if (e->h_pf_ids[p] >= 0 && e->h_pf_ids[p] < E) used[e->h_pf_ids[p]] = 1;
+  std::vector<int> routed;
+  for (int x2 = 0; x2 < E; ++x2)
+    if (used[x2]) routed.push_back(x2);
+  const int G = std::min(c.num_slots, E);
+  for (size_t g0 = 0; g0 < routed.size(); g0 += G) {
+    const int n = (int)std::min<size_t>(G, routed.size() - g0);
+    int32_t* slot_of = e->h_pf_meta;
+    int32_t* experts = e->h_pf_meta + E;
+    for (int x2 = 0; x2 < E; ++x2) slot_of[x2] = -1;
+    for (int i = 0; i < n; ++i) {
+      experts[i] = routed[g0 + i];
+      slot_of[routed[g0 + i]] = i;
+    }
+    EFF_HIP_TRY(hipMemcpyAsync(e->d_pf_slot_of, slot_of, (size_t)E * 4, hipMemcpyHostToDevice, cs));
+    EFF_HIP_TRY(hipMemcpyAsync(e->d_pf_experts, experts, (size_t)n * 4, hipMemcpyHostToDevice, cs));
+    EFF_HIP_TRY(launch_fallback_install(e, layer, e->d_pf_experts, n, cs));
+    for (int i = 0; i < n; ++i)
+      EFF_HIP_TRY(hipMemcpyAsync(e->d_arena + (int64_t)i * e->R,
+                                 e->pool + ((int64_t)layer * E + routed[g0 + i]) * e->R, (size_t)e->R,
+                                 hipMemcpyHostToDevice, cs));
+    EFF_HIP_TRY(launch_prefill(e, layer, (const uint16_t*)x, ids, w, T, (uint16_t*)out, e->d_pf_slot_of, -1,
+                               false, cs));
+    // staging buffers are reused by the next group
+    EFF_HIP_TRY(hipStreamSynchronize(cs));
+  }
+  EFF_HIP_TRY(launch_combine(e->d_pf_y, nullptr, nullptr, w, T, K, c.hidden, (uint16_t*)out, cs));
+  return EFF_OK;
+}
+
+int eff_snapshot_tables(eff_engine* e, int32_t* table, int32_t* owner, int64_t* usage, int64_t* recency,
+                        int64_t* clock) {
+  if (int rc = check_engine(e)) return rc;
+  EFF_HIP_TRY(hipDeviceSynchronize());
+  const eff_config& c = e->cfg;
+  const size_t LE = (size_t)c.num_layers * c.num_experts, S = (size_t)c.num_slots;
+  if (table) EFF_HIP_TRY(hipMemcpy(table, e->d_table, LE * 4, hipMemcpyDeviceToHost));
+  if (owner && S) EFF_HIP_TRY(hipMemcpy(owner, e->d_owner, S * 4, hipMemcpyDeviceToHost));
+  if (usage && S) EFF_HIP_TRY(hipMemcpy(usage, e->d_usage, S * 8, hipMemcpyDeviceToHost));
+  if (recency) EFF_HIP_TRY(hipMemcpy(recency, e->d_recency, LE * 8, hipMemcpyDeviceToHost));
+  if (clock) EFF_HIP_TRY(hipMemcpy(clock, e->d_clock, 16, hipMemcpyDeviceToHost));
+  return read_device_error(e);
+}
+
+int eff_get_stats(eff_engine* e, eff_stats* out) {
+  if (int rc = check_engine(e)) return rc;
+  if (!out) return fail(EFF_EINVAL, "eff_get_stats: out is NULL");
+  int64_t st[ST_COUNT];
+  EFF_HIP_TRY(hipDeviceSynchronize());
+  EFF_HIP_TRY(hipMemcpy(st, e->d_stats, sizeof(st), hipMemcpyDeviceToHost));
+  std::memset(out, 0, sizeof(*out));
+  out->calls = st[ST_CALLS];
+  out->hits = st[ST_HITS];
+  out->fetched = st[ST_FETCHED];
+  out->host = st[ST_HOST];
+  out->spec_fetched = st[ST_SPEC_FETCHED];
+  out->bytes_fetched = e->host_bytes_fetched;
+  for (int i = 0; i < 17; ++i) out->qstar_hist[i] = st[ST_HIST0 + i];
+  return EFF_OK;
+}
+
+int eff_slot_ptr(eff_engine* e, int slot, const void** out) {
+  if (int rc = check_engine(e)) return rc;
+  if (!out || slot < 0 || slot >= e->cfg.num_slots) return fail(EFF_EINVAL, "eff_slot_ptr: bad slot");
+  *out = e->d_arena + (int64_t)slot * e->R;
+  return EFF_OK;
+}
+
+}  // extern "C"

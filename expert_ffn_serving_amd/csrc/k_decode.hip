@@ -1,0 +1,504 @@
+// Decode expert FFN: y = W_d (silu(W_g x) * (W_u x)) per GPU-owned (token, k) entry,
+// straight from the slot bytes, with weights dequantized in registers.
+//
+// The step is bound by HBM bandwidth: every routed expert's weights are read in
+// full per step ([FT-blog] §三.2).  Each distinct slot's record is read once for
+// all tokens routed to it.  Work is split three ways:
+//   k_plan      distinct GPU slots of the call and their entries (one workgroup)
+//   k_gateup    gate and up rows of one 64-row block over a slice of H, both
+//               matrices at once; the last slice to finish (per-block counter)
+//               adds the slices in fixed order and applies SwiGLU
+//   k_down      one 64-row block of the down matrix over all of I
+//   k_combine   out[t] = sum over k of w[t,k] * y[t,k] (fixed k order), bf16 RNE
+// Every reduction has a fixed order (no float atomics): results are bitwise
+// reproducible from run to run.
+//
+// Register dequantization:
+//   int4   nibble u -> bf16(128 + u) by OR-ing it under 0x4300; a 2-wide bf16 dot
+//          then gives sum (128+u) x, and sum (u-8) x = that - 136 * sum x.  In the
+//          down projection the activations are fp16 and the base is fp16(1024+u).
+//   e2m1   v_cvt_scalef32_pk_{bf16,f16}_fp4 with scale 1.0 (the instruction uses
+//          only the exponent of its scale operand, so the e4m3 block scale is
+//          applied afterwards in fp32); e4m3 via v_cvt_f32_fp8 (OCP E4M3FN).
+#include "eff_internal.h"
+
+namespace eff {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWG = 256;  // 4 waves
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         c, false);
+}
+__device__ inline float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+template <int SEL>
+__device__ inline uint32_t fp4_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+template <int SEL>
+__device__ inline uint32_t fp4_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+}
+
+__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------- plan
+__global__ void __launch_bounds__(256)
+k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, DecodePlan* plan) {
+  __shared__ int32_t s_sl[kMaxEntries];
+  __shared__ int32_t s_first[kMaxEntries];
+  __shared__ int s_nu;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_nu = 0;
+  for (int p = tid; p < n; p += blockDim.x) {
+    const int v = slots[p];
+    s_sl[p] = (v >= 0 && v < S) ? v : -1;  // slots outside the arena are never read
+  }
+  __syncthreads();
+  for (int p = tid; p < n; p += blockDim.x) {
+    int v = s_sl[p], first = v >= 0;
+    for (int q = 0; q < p && first; ++q) first = s_sl[q] != v;
+    s_first[p] = first;
+  }
+  __syncthreads();
+  for (int p = tid; p < n; p += blockDim.x) {
+    if (!s_first[p]) continue;
+    int v = s_sl[p], rank = 0, cnt = 0;
+    for (int q = 0; q < n; ++q) rank += s_first[q] && s_sl[q] < v;
+    if (rank >= maxU) continue;  // more distinct slots than a layer has experts: not computed
+    for (int q = 0; q < n && cnt < maxB; ++q)  // a slot appears at most once per token
+      if (s_sl[q] == v) plan->uentry[rank][cnt++] = q;
+    plan->uslot[rank] = v;
+    plan->ucount[rank] = cnt;
+    atomicAdd(&s_nu, 1);
+  }
+  __syncthreads();
+  if (tid == 0) plan->nu = min(s_nu, maxU);
+}
+
+// ---------------------------------------------------------------------------- gate / up
+// grid: maxU * (I/64) * ksplit workgroups of 256 threads.  Lane (q = lane/16, r = lane%16)
+// of a 1 KiB block holds rows 16t + r (t = 0..3), inputs 8q..8q+7 of the block's 32.
+template <int FMT, int NT>
+__global__ void __launch_bounds__(kWG)
+k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
+         const int32_t* __restrict__ owner, const DecodePlan* __restrict__ plan,
+         const uint16_t* __restrict__ x, int H, int I, int K, int ksplit, int maxB,
+         float* __restrict__ part, int32_t* __restrict__ counters, float* __restrict__ a_out) {
+  __shared__ float s_red[4][2][64][NT];
+  __shared__ int s_last;
+  const int NB = I / 64, KB = H / 32, kbs = KB / ksplit;
+  const int wg = blockIdx.x;
+  const int sp = wg % ksplit, nb = (wg / ksplit) % NB, u = wg / (ksplit * NB);
+  if (u >= plan->nu) return;
+  const int slot = plan->uslot[u], cnt = plan->ucount[u];
+  const uint8_t* rec = arena + (int64_t)slot * R;
+  const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
+  const uint8_t* gp = rec;
+  const uint8_t* up = rec + pay;
+  const uint8_t* gs = rec + 3 * pay;
+  const uint8_t* us = rec + 3 * pay + sca;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
+  float tsg = 1.f, tsu = 1.f;
+  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
+    const int fl = owner[slot];
+    tsg = ts[(int64_t)fl * 3 + 0];
+    tsu = ts[(int64_t)fl * 3 + 1];
+  }
+  for (int c0 = 0; c0 < cnt; c0 += NT) {
+    const int nt = min(NT, cnt - c0);
+    int tok[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) tok[j] = (j < nt) ? plan->uentry[u][c0 + j] / K : 0;
+    float acc[2][4][NT];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[m][t][j] = 0.f;
+
+    for (int kb = sp * kbs + wave; kb < (sp + 1) * kbs; kb += 4) {
+      const int64_t blk = (int64_t)kb * NB + nb;
+      const uint4 wg4 = *reinterpret_cast<const uint4*>(gp + blk * 1024 + lane * 16);
+      const uint4 wu4 = *reinterpret_cast<const uint4*>(up + blk * 1024 + lane * 16);
+      float sg[4], su[4];
+      if (FMT == EFF_WFMT_INT4_G32_BF16) {
+        const uint2 a = *reinterpret_cast<const uint2*>(gs + blk * 128 + r * 8);
+        const uint2 b = *reinterpret_cast<const uint2*>(us + blk * 128 + r * 8);
+        sg[0] = bf16_lo(a.x); sg[1] = bf16_hi(a.x); sg[2] = bf16_lo(a.y); sg[3] = bf16_hi(a.y);
+        su[0] = bf16_lo(b.x); su[1] = bf16_hi(b.x); su[2] = bf16_lo(b.y); su[3] = bf16_hi(b.y);
+      } else {
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(gs + blk * 128 + ((q >> 1) * 16 + r) * 4);
+        const uint32_t b = *reinterpret_cast<const uint32_t*>(us + blk * 128 + ((q >> 1) * 16 + r) * 4);
+        sg[0] = __builtin_amdgcn_cvt_f32_fp8(a, 0); sg[1] = __builtin_amdgcn_cvt_f32_fp8(a, 1);
+        sg[2] = __builtin_amdgcn_cvt_f32_fp8(a, 2); sg[3] = __builtin_amdgcn_cvt_f32_fp8(a, 3);
+        su[0] = __builtin_amdgcn_cvt_f32_fp8(b, 0); su[1] = __builtin_amdgcn_cvt_f32_fp8(b, 1);
+        su[2] = __builtin_amdgcn_cvt_f32_fp8(b, 2); su[3] = __builtin_amdgcn_cvt_f32_fp8(b, 3);
+      }
+      uint32_t xw[NT][4];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if (j < nt) {
+          const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)tok[j] * H + kb * 32 + q * 8);
+          if (FMT == EFF_WFMT_INT4_G32_BF16) {
+            // pairs (x0,x4), (x1,x5), (x2,x6), (x3,x7) to meet the nibble pairs below
+            xw[j][0] = (v.x & 0xFFFFu) | (v.z << 16);
+            xw[j][1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
+            xw[j][2] = (v.y & 0xFFFFu) | (v.w << 16);
+            xw[j][3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+          } else {
+            xw[j][0] = v.x; xw[j][1] = v.y; xw[j][2] = v.z; xw[j][3] = v.w;
+          }
+        } else {
+          xw[j][0] = xw[j][1] = xw[j][2] = xw[j][3] = 0u;
+        }
+      }
+      const uint32_t wdw[2][4] = {{wg4.x, wg4.y, wg4.z, wg4.w}, {wu4.x, wu4.y, wu4.z, wu4.w}};
+      if (FMT == EFF_WFMT_INT4_G32_BF16) {
+        float xs[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          xs[j] = dot2_bf16(xw[j][3], 0x3F803F80u,
+                            dot2_bf16(xw[j][2], 0x3F803F80u,
+                                      dot2_bf16(xw[j][1], 0x3F803F80u, dot2_bf16(xw[j][0], 0x3F803F80u, 0.f))));
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t d = wdw[m][t];
+            const uint32_t p0 = (d & 0x000F000Fu) | 0x43004300u;
+            const uint32_t p1 = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
+            const uint32_t p2 = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
+            const uint32_t p3 = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
+            const float sc = m ? su[t] : sg[t];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              float raw = dot2_bf16(p3, xw[j][3], dot2_bf16(p2, xw[j][2],
+                                    dot2_bf16(p1, xw[j][1], dot2_bf16(p0, xw[j][0], 0.f))));
+              acc[m][t][j] = fmaf(sc, fmaf(-136.f, xs[j], raw), acc[m][t][j]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t d = wdw[m][t];
+            const uint32_t p0 = fp4_to_bf16x2<0>(d), p1 = fp4_to_bf16x2<1>(d);
+            const uint32_t p2 = fp4_to_bf16x2<2>(d), p3 = fp4_to_bf16x2<3>(d);
+            const float sc = m ? su[t] : sg[t];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              float raw = dot2_bf16(p3, xw[j][3], dot2_bf16(p2, xw[j][2],
+                                    dot2_bf16(p1, xw[j][1], dot2_bf16(p0, xw[j][0], 0.f))));
+              acc[m][t][j] = fmaf(sc, raw, acc[m][t][j]);
+            }
+          }
+        }
+      }
+    }
+    // reduce over q (lanes r, r+16, r+32, r+48), then over the 4 waves in order
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          float v = acc[m][t][j];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          acc[m][t][j] = v;
+        }
+    if (lane < 16) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) s_red[wave][m][t * 16 + r][j] = acc[m][t][j];
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * 64 * nt; i += kWG) {
+      const int m = i / (64 * nt), row = (i / nt) % 64, j = i % nt;
+      float v = s_red[0][m][row][j] + s_red[1][m][row][j];
+      v += s_red[2][m][row][j];
+      v += s_red[3][m][row][j];
+      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= m ? tsu : tsg;
+      // partial of split sp: part[((u*NB + nb)*ksplit + sp)][m][row][token]
+      part[((((int64_t)u * NB + nb) * ksplit + sp) * 2 + m) * 64 * maxB + row * maxB + c0 + j] = v;
+    }
+    __syncthreads();
+  }
+  // the last split of this (u, nb) to finish adds the splits in order and applies SwiGLU
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = atomicAdd(&counters[u * NB + nb], 1);
+    s_last = (prev == ksplit - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int i = tid; i < 64 * cnt; i += kWG) {
+    const int row = i / cnt, j = i % cnt;
+    float g = 0.f, v = 0.f;
+    for (int s2 = 0; s2 < ksplit; ++s2) {
+      const int64_t b = (((int64_t)u * NB + nb) * ksplit + s2) * 2;
+      g += __builtin_nontemporal_load(&part[(b + 0) * 64 * maxB + row * maxB + j]);
+      v += __builtin_nontemporal_load(&part[(b + 1) * 64 * maxB + row * maxB + j]);
+    }
+    a_out[((int64_t)u * maxB + j) * I + nb * 64 + row] = silu(g) * v;
+  }
+  if (tid == 0) counters[u * NB + nb] = 0;
+}
+
+// ---------------------------------------------------------------------------- down
+// grid: maxU * (H/64) workgroups.  The SwiGLU activations of the slot's tokens are staged
+// in LDS as fp16, each token scaled by a power of two so that its largest value fits.
+template <int FMT, int NT>
+__global__ void __launch_bounds__(kWG)
+k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
+       const int32_t* __restrict__ owner, const DecodePlan* __restrict__ plan,
+       const float* __restrict__ a_in, int H, int I, int maxB, float* __restrict__ y) {
+  extern __shared__ uint32_t s_a[];          // [NT][I/2] fp16 pairs, int4 order permuted per 8
+  __shared__ float s_asum[NT][512];          // int4: sum of each 8-group (I/8 <= 512)
+  __shared__ float s_red[4][64][NT];
+  __shared__ float s_scale[NT];
+  __shared__ float s_amax[NT][4];
+  const int NBH = H / 64, KB = I / 32;
+  const int u = blockIdx.x / NBH, nb = blockIdx.x % NBH;
+  if (u >= plan->nu) return;
+  const int slot = plan->uslot[u], cnt = plan->ucount[u];
+  const uint8_t* rec = arena + (int64_t)slot * R;
+  const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
+  const uint8_t* dp = rec + 2 * pay;
+  const uint8_t* ds = rec + 3 * pay + 2 * sca;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
+  float tsd = 1.f;
+  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsd = ts[(int64_t)owner[slot] * 3 + 2];
+
+  for (int c0 = 0; c0 < cnt; c0 += NT) {
+    const int nt = min(NT, cnt - c0);
+    // per-token power-of-two scale: |a| * 2^-e < 2^15
+    for (int j = 0; j < nt; ++j) {
+      const float* aj = a_in + ((int64_t)u * maxB + c0 + j) * I;
+      float mx = 0.f;
+      for (int k = tid; k < I; k += kWG) mx = fmaxf(mx, fabsf(aj[k]));
+      for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if (lane == 0) s_amax[j][wave] = mx;
+    }
+    __syncthreads();
+    if (tid < nt) {
+      float mx = fmaxf(fmaxf(s_amax[tid][0], s_amax[tid][1]), fmaxf(s_amax[tid][2], s_amax[tid][3]));
+      int e = 0;
+      if (mx > 0.f) {
+        frexpf(mx, &e);        // mx = f * 2^e, f in [0.5, 1)
+        e = e > 15 ? e - 15 : 0;
+      }
+      s_scale[tid] = ldexpf(1.f, e);
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * (I / 8); i += kWG) {
+      const int j = i / (I / 8), g = i % (I / 8);
+      const float* src = a_in + ((int64_t)u * maxB + c0 + j) * I + g * 8;
+      const float inv = 1.f / s_scale[j];
+      _Float16 h[8];
+      float sum = 0.f;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        h[z] = (_Float16)(src[z] * inv);
+        sum += (float)h[z];
+      }
+      uint32_t* dst = s_a + j * (I / 2) + g * 4;
+      if (FMT == EFF_WFMT_INT4_G32_BF16) {
+#pragma unroll
+        for (int z = 0; z < 4; ++z)
+          dst[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[z]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, h[z + 4]) << 16);
+        s_asum[j][g] = sum;
+      } else {
+#pragma unroll
+        for (int z = 0; z < 4; ++z)
+          dst[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * z]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * z + 1]) << 16);
+      }
+    }
+    __syncthreads();
+    float acc[4][NT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[t][j] = 0.f;
+    for (int kb = wave; kb < KB; kb += 4) {
+      const int64_t blk = (int64_t)kb * NBH + nb;
+      const uint4 w4 = *reinterpret_cast<const uint4*>(dp + blk * 1024 + lane * 16);
+      float sd[4];
+      if (FMT == EFF_WFMT_INT4_G32_BF16) {
+        const uint2 a = *reinterpret_cast<const uint2*>(ds + blk * 128 + r * 8);
+        sd[0] = bf16_lo(a.x); sd[1] = bf16_hi(a.x); sd[2] = bf16_lo(a.y); sd[3] = bf16_hi(a.y);
+      } else {
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(ds + blk * 128 + ((q >> 1) * 16 + r) * 4);
+        sd[0] = __builtin_amdgcn_cvt_f32_fp8(a, 0); sd[1] = __builtin_amdgcn_cvt_f32_fp8(a, 1);
+        sd[2] = __builtin_amdgcn_cvt_f32_fp8(a, 2); sd[3] = __builtin_amdgcn_cvt_f32_fp8(a, 3);
+      }
+      const uint32_t wdw[4] = {w4.x, w4.y, w4.z, w4.w};
+      uint32_t av[NT][4];
+      float asum[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if (j < nt) {
+          const uint4 v = *reinterpret_cast<const uint4*>(s_a + j * (I / 2) + (kb * 4 + q) * 4);
+          av[j][0] = v.x; av[j][1] = v.y; av[j][2] = v.z; av[j][3] = v.w;
+          asum[j] = (FMT == EFF_WFMT_INT4_G32_BF16) ? s_asum[j][kb * 4 + q] : 0.f;
+        } else {
+          av[j][0] = av[j][1] = av[j][2] = av[j][3] = 0u;
+          asum[j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t d = wdw[t];
+        uint32_t p0, p1, p2, p3;
+        if (FMT == EFF_WFMT_INT4_G32_BF16) {
+          p0 = (d & 0x000F000Fu) | 0x64006400u;
+          p1 = ((d >> 4) & 0x000F000Fu) | 0x64006400u;
+          p2 = ((d >> 8) & 0x000F000Fu) | 0x64006400u;
+          p3 = ((d >> 12) & 0x000F000Fu) | 0x64006400u;
+        } else {
+          p0 = fp4_to_f16x2<0>(d); p1 = fp4_to_f16x2<1>(d);
+          p2 = fp4_to_f16x2<2>(d); p3 = fp4_to_f16x2<3>(d);
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          float raw = dot2_f16(p3, av[j][3], dot2_f16(p2, av[j][2], dot2_f16(p1, av[j][1],
+                               dot2_f16(p0, av[j][0], 0.f))));
+          if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-1032.f, asum[j], raw);
+          acc[t][j] = fmaf(sd[t], raw, acc[t][j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        float v = acc[t][j];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[t][j] = v;
+      }
+    if (lane < 16) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) s_red[wave][t * 16 + r][j] = acc[t][j];
+    }
+    __syncthreads();
+    for (int i = tid; i < 64 * nt; i += kWG) {
+      const int row = i / nt, j = i % nt;
+      float v = s_red[0][row][j] + s_red[1][row][j];
+      v += s_red[2][row][j];
+      v += s_red[3][row][j];
+      v = v * s_scale[j] * tsd;
+      const int p = plan->uentry[u][c0 + j];
+      y[(int64_t)p * H + nb * 64 + row] = v;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------- combine
+__global__ void __launch_bounds__(256)
+k_combine(const float* __restrict__ yg, const float* __restrict__ yh, const int32_t* __restrict__ slots,
+          const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const int p = t * K + k;
+    const float* src = (slots == nullptr || slots[p] >= 0) ? yg : yh;
+    acc = fmaf(w[p], src[(int64_t)p * H + h], acc);
+  }
+  uint32_t b = __float_as_uint(acc);
+  b += 0x7FFFu + ((b >> 16) & 1u);  // round to nearest even
+  out[(int64_t)t * H + h] = (uint16_t)(b >> 16);
+}
+
+template <int FMT, int NT>
+hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, hipStream_t s) {
+  const eff_config& c = e->cfg;
+  const int H = c.hidden, I = c.inter;
+  dim3 g1(e->maxU * (I / 64) * e->ksplit);
+  hipLaunchKernelGGL((k_gateup<FMT, NT>), g1, dim3(kWG), 0, s, e->d_arena, e->R, e->d_ts, e->d_owner,
+                     e->d_plan, x, H, I, c.top_k, e->ksplit, c.max_tokens, e->d_part, e->d_counters,
+                     e->d_a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dim3 g2(e->maxU * (H / 64));
+  size_t lds = (size_t)NT * (I / 2) * sizeof(uint32_t);
+  hipLaunchKernelGGL((k_down<FMT, NT>), g2, dim3(kWG), lds, s, e->d_arena, e->R, e->d_ts, e->d_owner,
+                     e->d_plan, e->d_a, H, I, c.max_tokens, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_nt(int maxB) { return maxB >= 8 ? 8 : maxB >= 4 ? 4 : maxB >= 2 ? 2 : 1; }
+
+hipError_t decode_kernels_setup(int fmt, int maxB, int I) {
+  // allow up to NT * I * 2 bytes of dynamic LDS for the down kernel
+  const int NT = decode_nt(maxB);
+  const int lds = NT * (I / 2) * 4;
+  hipError_t err = hipSuccess;
+#define SETUP(F, N)                                                                                    \
+  if (fmt == F && NT == N)                                                                              \
+    err = hipFuncSetAttribute((const void*)k_down<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  SETUP(EFF_WFMT_INT4_G32_BF16, 1) SETUP(EFF_WFMT_INT4_G32_BF16, 2) SETUP(EFF_WFMT_INT4_G32_BF16, 4)
+  SETUP(EFF_WFMT_INT4_G32_BF16, 8) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 1) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 2)
+  SETUP(EFF_WFMT_NVFP4_G16_E4M3, 4) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 8)
+#undef SETUP
+  return err;
+}
+
+hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
+                             float* y, hipStream_t s) {
+  (void)layer;
+  const int n = B * e->cfg.top_k;
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, s, slots, n, e->cfg.num_slots, e->maxU, e->cfg.max_tokens,
+                     e->d_plan);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int NT = decode_nt(e->cfg.max_tokens);
+  const bool fp4 = e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3;
+  switch (NT) {
+    case 1: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 1>(e, x, y, s)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 1>(e, x, y, s);
+    case 2: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 2>(e, x, y, s)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 2>(e, x, y, s);
+    case 4: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 4>(e, x, y, s)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 4>(e, x, y, s);
+    default: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 8>(e, x, y, s)
+                        : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 8>(e, x, y, s);
+  }
+}
+
+hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
+                          int B, int K, int H, uint16_t* out, hipStream_t s) {
+  dim3 g((H + 255) / 256, B);
+  hipLaunchKernelGGL(k_combine, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace eff

@@ -1,0 +1,208 @@
+/*
+ * libeff — routed-expert FFN over an HBM slot cache, for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Device pointers are caller-owned HIP
+ * device memory; streams are hipStream_t passed as void* (NULL = the default
+ * stream).  Every call returns EFF_OK (0) or a negative EFF_E* code and never
+ * aborts; eff_last_error() gives a thread-local message for the last failure.
+ * Calls that take a stream only enqueue work (no allocation, no host wait)
+ * unless stated otherwise.  An engine is single-threaded: do not call into one
+ * engine from two threads at once.
+ *
+ * Sources (cited by page title and section):
+ *   [FT-deep]  "FreeToken 딥다이브 — 게이밍 PC 한 대로 284B 모델을 돌리는 엔진"
+ *   [FT-blog]  "FreeToken:让消费级电脑跑起 284B MoE，一次把整机当成推理集群的系统设计"
+ *   [NVMe-8GB] "NVMe에서 전문가(experts)를 스트리밍하여 8GB GPU에서 133GB MoE 모델 구동하기 (11 토큰/초)"
+ *   [Edge0]    "SSD 가중치층으로 35B MoE를 라우팅 예측으로 24GB 데스크톱에서 서빙한다"
+ *
+ * Expert records.  The full pool of L*E records lives in pinned host memory and
+ * is the source of truth; HBM holds only S slots of one record each, addressed
+ * by the flat id layer*E + expert ([FT-blog] §四, §七 item 3; [FT-deep] §4 ⑤).
+ * Record = gate[I,H] | up[I,H] | down[H,I] payloads, then their scales in the
+ * same order ([NVMe-8GB] "엔진" item 1).  Each matrix (N rows = outputs, Kd
+ * columns = inputs) is stored as 1 KiB blocks of 64 rows x 32 inputs, block
+ * index kb*(N/64)+nb (kb = k/32, nb = n/64); inside a block element (n, k) is
+ * at byte (q*16 + r)*16 + t*4 + i/2 with t=(n%64)/16, r=n%16, q=(k%32)/8,
+ * i=k%8, even i in the low nibble.  Each block has a 128-byte scale block at
+ * the same index: INT4_G32_BF16 stores the bf16 scale of (n, k/32) at byte
+ * (r*4+t)*2 and values are (u-8)*scale; NVFP4_G16_E4M3 stores the e4m3 scale
+ * of (n, k/16) at byte (((k%32)/16)*16 + r)*4 + t and values are
+ * e2m1(code)*e4m3(scale)*tensor_scale, with one fp32 tensor scale per matrix
+ * kept resident in the engine (tensor_scales[(layer*E+expert)*3 + m]).
+ * Record size R = 3*H*I/2 + 3*H*I/16 bytes in both formats.
+ */
+#ifndef EFF_H
+#define EFF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct eff_engine eff_engine;
+typedef void* eff_stream_t; /* hipStream_t */
+
+enum {
+  EFF_OK = 0,
+  EFF_EINVAL = -1,   /* bad argument; nothing was changed */
+  EFF_ENOMEM = -2,   /* device or host allocation failed; nothing was changed */
+  EFF_EHIP = -3,     /* a HIP runtime call failed (message has hipGetErrorString) */
+  EFF_ECAPTURE = -4, /* the call must wait on the host and the stream is being captured */
+  EFF_ESTATE = -5,   /* call out of order (e.g. split without a pending ensure) */
+  EFF_EDEVICE = -6   /* a kernel reported bad input (e.g. an expert id >= E); see message */
+};
+
+enum { EFF_WFMT_INT4_G32_BF16 = 0, EFF_WFMT_NVFP4_G16_E4M3 = 1 };
+
+/* eff_ensure_experts flags */
+enum { EFF_SPECULATIVE = 1u };
+
+typedef struct eff_config {
+  int32_t num_layers;         /* L */
+  int32_t num_experts;        /* E, <= 4096 */
+  int32_t top_k;              /* K, <= 32 */
+  int32_t hidden;             /* H, multiple of 64 */
+  int32_t inter;              /* I, multiple of 64 */
+  int32_t wformat;            /* EFF_WFMT_* */
+  int32_t num_slots;          /* S, 0 <= S <= 16384 */
+  int32_t max_tokens;         /* decode batch bound B, 1..32 */
+  int32_t max_prefill_tokens; /* prefill chunk bound T (0: no prefill) */
+  uint32_t fetch_frac_q16;    /* f = B_P/B_H * 65536, 0..65536 */
+  int32_t host_threads;       /* threads of the host executor (0: hardware concurrency) */
+  uint32_t flags;             /* reserved, 0 */
+} eff_config;
+
+/* Record size R for the config's (H, I, format); 0 if the config is invalid. */
+int64_t eff_record_bytes(const eff_config* cfg);
+
+/* Creates an engine.  Validates everything before allocating (a rejected config
+ * changes nothing, [FT-deep] §4 design pattern ⑦).  host_pool: L*E*R bytes of
+ * pinned host memory (hipHostMalloc), caller-owned, read-only to the library,
+ * alive until eff_destroy.  tensor_scales: L*E*3 floats (NVFP4; may be NULL
+ * for INT4), copied.  Allocates S*R bytes of HBM for the slots plus tables.
+ * Errors: EFF_EINVAL, EFF_ENOMEM, EFF_EHIP. */
+int eff_create(const eff_config* cfg, const void* host_pool, const float* tensor_scales,
+               eff_engine** out);
+int eff_destroy(eff_engine* e);
+const char* eff_last_error(void);
+
+/* Pinned host memory helpers (hipHostMalloc / hipHostFree) for pools and staging. */
+int eff_host_alloc(size_t bytes, void** out);
+int eff_host_free(void* p);
+
+/* Router ([FT-deep] §2; [FT-blog] §二).  x: bf16 [B,H]; w_router: bf16 [E,H];
+ * ids: int32 [B,K] out, ordered by (logit desc, id asc); w: fp32 [B,K] out,
+ * softmax over the K selected logits.  Logits are fp32 sums in a fixed order:
+ * 64 lanes, lane l adds j = 64*V*c + V*l + i (c outer, i inner; V the largest
+ * of 8,4,2,1 dividing H/64), then lanes fold pairwise (l, l+o) for o =
+ * 32,16,...,1.  B <= max_tokens (decode) or <= max_prefill_tokens. */
+int eff_route(eff_engine* e, const void* x, const void* w_router, int B, int32_t* ids, float* w,
+              eff_stream_t stream);
+/* Same top-k/softmax from precomputed fp32 logits [B,E] (routing traces). */
+int eff_route_logits(eff_engine* e, const float* logits, int B, int32_t* ids, float* w,
+                     eff_stream_t stream);
+
+/* ensure ([FT-deep] §4 ③ "ensure_experts_hybrid", §4 ⑤; [FT-blog] §六):
+ * ids_inout: n = B*K device int32 expert ids of `layer`, rewritten in place to
+ * the resident slot or -1.  Stamps hits as used at this step; keeps the call
+ * pending for eff_split_misses.  flags: EFF_SPECULATIVE for a fetch-only
+ * request made one layer early ([NVMe-8GB] "시간이 실제로 소요되는 부분").
+ * An id outside [0,E) is reported as EFF_EDEVICE by the next host-waiting call. */
+int eff_ensure_experts(eff_engine* e, int layer, int32_t* ids_inout, int n, uint32_t flags,
+                       eff_stream_t stream);
+
+/* split ([FT-deep] §4 ② q*, ⑤ recency; [FT-blog] §六): q = q*(m, f) of the m
+ * unique misses; misses ranked by (recency desc, id asc) take the q' =
+ * min(q, #victims) least recently used slots (usage asc, slot asc) whose
+ * usage is below the call's floor.  Rewrites ids_inout to slot-or--1, writes
+ * cpu_ids (the expert id where the host computes, -1 elsewhere; all -1 for a
+ * speculative call) and counts = {m, q', host}.  The fetch list is kept in the
+ * engine for eff_copy_missing.  Errors: EFF_ESTATE without a pending ensure. */
+int eff_split_misses(eff_engine* e, int32_t* ids_inout, int32_t* cpu_ids, int32_t* counts,
+                     eff_stream_t stream);
+
+/* q* itself: argmin over F in [0,m] of max(F*(65536-f), (m-F)*f), lowest F on
+ * ties ([FT-deep] §4 ②).  Host version returns q (or -1 for bad input); the
+ * batch version evaluates n pairs on the device. */
+int64_t eff_qstar(int64_t m, uint32_t f);
+int eff_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, int n, eff_stream_t stream);
+
+/* copy ([FT-deep] §4 ③ copy_missing): waits on the host for `compute` to reach
+ * the last split, then enqueues one hipMemcpyAsync per fetched record (host
+ * pool -> slot) on `side` and makes `compute` wait for them.  Also issues the
+ * fetches of a speculative split made after it.  EFF_ECAPTURE under capture. */
+int eff_copy_missing(eff_engine* e, eff_stream_t compute, eff_stream_t side);
+
+/* GPU expert compute ([FT-deep] §4 ③ _expert_gemm; [Edge0] "어떻게 동작하나"):
+ * for every entry p = t*K+k with slots[p] >= 0, y[p,:] = W_d (silu(W_g x_t) *
+ * (W_u x_t)) with the record in that slot; each distinct slot's weights are
+ * read once for all its tokens.  x: bf16 [B,H]; y: fp32 [B,K,H]; entries with
+ * slots[p] < 0 are not written. */
+int eff_expert_ffn_decode(eff_engine* e, int layer, const void* x, const int32_t* slots, int B,
+                          float* y, eff_stream_t stream);
+
+/* Host share ([FT-deep] §4 ③ decode_submit/decode_sync; [FT-blog] §三.2): the
+ * same expert FFN on the host, from the pinned pool, for entries with
+ * cpu_ids[p] >= 0.  Synchronous; all pointers are host memory.  y_host fp32
+ * [B,K,H]; other entries are not written. */
+int eff_host_ffn_decode(eff_engine* e, int layer, const void* x_host, const int32_t* cpu_ids_host,
+                        int B, float* y_host);
+
+/* Merge ([FT-deep] §4 ③ "gpu_routed + cpu_routed"): out[t,:] = bf16_rne(sum over
+ * k ascending of w[t,k] * (slots[t,k] >= 0 ? y_gpu : y_host)[t,k,:]).  y_host
+ * is device memory (may be NULL if no entry has slot < 0). */
+int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const int32_t* slots,
+                const float* w, int B, void* out, eff_stream_t stream);
+
+/* One decode MoE layer end to end, eager: route (from x and w_router, or from
+ * logits if w_router is NULL) -> ensure -> split -> [speculative ensure/split
+ * of layer+1 on spec_ids if not NULL] -> copies on `side` -> GPU expert FFN ->
+ * host share -> combine into out (bf16 [B,H]).  Waits on the host once (to
+ * read the fetch list and the host ids).  ids/w/slots/cpu_ids/counts of the
+ * call can be read back with eff_last_layer_info. */
+int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_router,
+                     const float* logits, int B, const int32_t* spec_ids, void* out,
+                     eff_stream_t compute, eff_stream_t side);
+/* Device pointers of the engine-owned buffers used by eff_decode_layer:
+ * ids int32 [B*K] (routed expert ids), w fp32 [B*K], slots int32 [B*K],
+ * cpu_ids int32 [B*K], counts int32 [3] (+3 for the speculative split). */
+int eff_last_layer_info(eff_engine* e, const int32_t** ids, const float** w, const int32_t** slots,
+                        const int32_t** cpu_ids, const int32_t** counts);
+
+/* Prefill streaming ([FT-deep] §4 ①; [FT-blog] §五): installs layer's E
+ * experts into buffer layer%2 (slots (layer%2)*E + e) and enqueues the E
+ * record copies on `side`, then records an event that the next
+ * eff_expert_ffn_prefill_layer of this layer waits on.  EFF_EINVAL if S < 2E
+ * (the layer then runs through the fallback inside the prefill call). */
+int eff_prefill_stream_layer(eff_engine* e, int layer, eff_stream_t side);
+
+/* Whole-layer prefill ([FT-deep] §4 ①; [NVMe-8GB] "엔진" item 5): x bf16 [T,H],
+ * ids int32 [T,K] (expert ids from eff_route), w fp32 [T,K] -> out bf16 [T,H].
+ * Groups the (t,k) pairs by expert and runs a grouped GEMM per expert on the
+ * slot buffer of layer%2, then the weighted combine.  With S < 2E it loads the
+ * routed experts on demand in groups of min(S,E) (waits on the host). */
+int eff_expert_ffn_prefill_layer(eff_engine* e, int layer, const void* x, const int32_t* ids,
+                                 const float* w, int T, void* out, eff_stream_t stream);
+
+/* Diagnostics (wait on the host; EFF_ECAPTURE under capture).  Any pointer may
+ * be NULL.  table int32 [L*E], owner int32 [S], usage int64 [S], recency int64
+ * [L*E], clock int64 [2] = {step, last_real}. */
+int eff_snapshot_tables(eff_engine* e, int32_t* table, int32_t* owner, int64_t* usage,
+                        int64_t* recency, int64_t* clock);
+
+typedef struct eff_stats {
+  int64_t calls, hits, fetched, host, spec_fetched; /* unique experts, summed over calls */
+  int64_t bytes_fetched;
+  int64_t qstar_hist[17]; /* q' counts 0..15, 16+ */
+} eff_stats;
+int eff_get_stats(eff_engine* e, eff_stats* out);
+
+/* Device pointer of slot s (for tests: slot bytes must equal the host record). */
+int eff_slot_ptr(eff_engine* e, int slot, const void** out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EFF_H */

@@ -1,0 +1,181 @@
+"""GPU parity of the integer control path against the oracle, bit for bit:
+q* (every f for m <= 64), router ids, and whole ensure/split call sequences
+(slots, host ids, counts, fetch lists, final tables), including speculative
+calls, S = 0, tiny caches and calls large enough for the sorted victim path."""
+import random
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import synth  # noqa: E402
+from oracle.policy import SlotCache  # noqa: E402
+from oracle.qstar import Q16  # noqa: E402
+from oracle.router import logits_fixed_order, topk_softmax  # noqa: E402
+from tests.helpers import PinnedPool, make_engine  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def eff():
+    import expert_ffn_serving_amd as e
+    assert torch.cuda.is_available()
+    return e
+
+
+def brute_all_f(m):
+    F = np.arange(m + 1, dtype=np.int64)[:, None]
+    f = np.arange(Q16 + 1, dtype=np.int64)[None, :]
+    return np.argmin(np.maximum(F * (Q16 - f), (m - F) * f), axis=0)
+
+
+def test_qstar_batch_every_f(eff):
+    ms = np.repeat(np.arange(65, dtype=np.int32), Q16 + 1)
+    fs = np.tile(np.arange(Q16 + 1, dtype=np.uint32), 65)
+    m_d = torch.from_numpy(ms).cuda()
+    f_d = torch.from_numpy(fs.view(np.int32)).cuda()
+    q_d = torch.empty_like(m_d)
+    eff.qstar_batch(m_d, f_d, q_d)
+    got = q_d.cpu().numpy().reshape(65, Q16 + 1)
+    for m in range(65):
+        assert np.array_equal(got[m], brute_all_f(m)), m
+    # large m, random f
+    rng = np.random.default_rng(1)
+    m2 = rng.integers(0, 4097, 20000).astype(np.int32)
+    f2 = rng.integers(0, Q16 + 1, 20000).astype(np.uint32)
+    q2 = torch.empty(20000, dtype=torch.int32, device="cuda")
+    eff.qstar_batch(torch.from_numpy(m2).cuda(), torch.from_numpy(f2.view(np.int32)).cuda(), q2)
+    from oracle.qstar import qstar_bruteforce
+    got2 = q2.cpu().numpy()
+    for i in range(0, 20000, 97):
+        assert got2[i] == qstar_bruteforce(int(m2[i]), int(f2[i]))
+
+
+@pytest.mark.parametrize("H,E,K,B", [(64, 8, 2, 1), (2048, 256, 8, 1), (2560, 512, 10, 16), (4096, 256, 6, 4),
+                                     (4096, 256, 6, 77), (2048, 64, 8, 33)])
+def test_route_ids_bit_exact(eff, H, E, K, B):
+    pool = PinnedPool(eff, 5, 1, 1, 64, 64, synth.FMT_INT4)   # engine needs a pool; routing does not read it
+    cfg = eff.make_config(1, E, K, H, 64, 0, 0, min(B, 32), max(B, 1), 65536, 2)
+    eng = eff.Engine(cfg, pool.ptr)
+    try:
+        x = synth.activations(7, 0, 0, B, H)
+        wr = synth.router_weights(7, 0, E, H)
+        ids = torch.empty((B, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((B, K), dtype=torch.float32, device="cuda")
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        wd = torch.from_numpy(wr.view(np.int16)).cuda()
+        eng.route(xd, wd, ids, w)
+        torch.cuda.synchronize()
+        rid, rw = topk_softmax(logits_fixed_order(x, wr), K)
+        assert np.array_equal(ids.cpu().numpy(), rid)
+        assert np.allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+    finally:
+        eng.close()
+        pool.free()
+
+
+def test_route_logits_traces_and_ties(eff):
+    pool = PinnedPool(eff, 5, 1, 1, 64, 64, synth.FMT_INT4)
+    E, K, B = 512, 10, 16
+    cfg = eff.make_config(1, E, K, 64, 64, 0, 0, B, 0, 65536, 2)
+    eng = eff.Engine(cfg, pool.ptr)
+    try:
+        lg = synth.trace_logits(3, 0, E, 1.2, 0, B)
+        lg[0, :] = 0.0            # all tied: ids 0..K-1
+        lg[1, 7] = lg[1, 9] = lg[1, 300] = 50.0
+        ids = torch.empty((B, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((B, K), dtype=torch.float32, device="cuda")
+        eng.route_logits(torch.from_numpy(lg).cuda(), ids, w)
+        torch.cuda.synchronize()
+        rid, rw = topk_softmax(lg, K)
+        got = ids.cpu().numpy()
+        assert np.array_equal(got, rid)
+        assert list(got[0]) == list(range(K)) and list(got[1][:3]) == [7, 9, 300]
+        assert np.allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+    finally:
+        eng.close()
+        pool.free()
+
+
+def run_sequence(eff, L, E, K, S, f, calls, maxB):
+    """calls: list of (layer, ids list, speculative).  Compares every call and the final tables."""
+    pool = PinnedPool(eff, 9, L, E, 64, 64, synth.FMT_INT4)
+    eng = make_engine(eff, pool, K, S, maxB, f)
+    orc = SlotCache(L, E, S, f)
+    try:
+        for i, (layer, ids, spec) in enumerate(calls):
+            n = len(ids)
+            d_ids = torch.tensor(ids, dtype=torch.int32, device="cuda")
+            cpu = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+            counts = torch.zeros(3, dtype=torch.int32, device="cuda")
+            eng.ensure_experts(layer, d_ids, eff.SPECULATIVE if spec else 0)
+            ens = d_ids.cpu().numpy().copy()
+            eng.split_misses(d_ids, cpu, counts)
+            eng.copy_missing()
+            torch.cuda.synchronize()
+            o_ens = orc.ensure(layer, ids, speculative=spec)
+            r = orc.split()
+            assert list(ens) == o_ens, ("ensure", i)
+            assert list(d_ids.cpu().numpy()) == r.slots, ("slots", i)
+            assert list(cpu.cpu().numpy()) == r.cpu_ids, ("cpu_ids", i)
+            assert list(counts.cpu().numpy()) == [r.m, r.q, r.host], ("counts", i)
+        snap = eng.snapshot_tables()
+        assert list(snap["table"]) == orc.table
+        assert list(snap["owner"]) == orc.owner
+        assert list(snap["usage"]) == orc.usage
+        assert list(snap["recency"]) == orc.recency
+        assert (snap["step"], snap["last_real"]) == (orc.step, orc.last_real)
+        st = eng.stats()
+        return st
+    finally:
+        eng.close()
+        pool.free()
+
+
+@pytest.mark.parametrize("S", [0, 1, 4, 16])
+@pytest.mark.parametrize("f", [0, 1, 16384, 32768, 49152, 65535, 65536])
+def test_sequences_tiny(eff, S, f):
+    rng = random.Random(S * 100003 + f)
+    L, E, K = 2, 8, 2
+    calls = [(rng.randrange(L), rng.sample(range(E), K), False) for _ in range(60)]
+    run_sequence(eff, L, E, K, S, f, calls, 1)
+
+
+def test_sequences_batched_speculative(eff):
+    rng = random.Random(3)
+    L, E, K, B = 4, 64, 10, 16
+    calls = []
+    for step in range(40):
+        layer = step % L
+        ids = [e for _ in range(B) for e in rng.sample(range(E), K)]
+        calls.append((layer, ids, False))
+        if layer + 1 < L:
+            calls.append((layer + 1, [e for _ in range(B) for e in rng.sample(range(E), K)], True))
+    for S, f in [(40, 65535), (100, 45875), (200, 26214), (0, 65536)]:
+        run_sequence(eff, L, E, K, S, f, calls, B)
+
+
+def test_sequences_many_fetches_sorted_path(eff):
+    # > 16 fetches per call exercise the sorted victim selection
+    rng = random.Random(4)
+    L, E, K, B = 3, 256, 8, 32
+    calls = [(s % L, [e for _ in range(B) for e in rng.sample(range(E), K)], False) for s in range(18)]
+    run_sequence(eff, L, E, K, 700, 65536, calls, B)
+    run_sequence(eff, L, E, K, 5000, 65536, calls, B)
+
+
+def test_bad_id_reported(eff):
+    pool = PinnedPool(eff, 9, 1, 8, 64, 64, synth.FMT_INT4)
+    eng = make_engine(eff, pool, 2, 4, 1, 65536)
+    try:
+        d_ids = torch.tensor([3, 9], dtype=torch.int32, device="cuda")
+        eng.ensure_experts(0, d_ids)
+        eng.split_misses(d_ids, torch.empty(2, dtype=torch.int32, device="cuda"),
+                         torch.empty(3, dtype=torch.int32, device="cuda"))
+        with pytest.raises(eff.EffError) as ei:
+            eng.copy_missing()
+        assert ei.value.code == eff.EFF_EDEVICE
+    finally:
+        eng.close()
+        pool.free()

@@ -1,0 +1,155 @@
+"""GPU parity of decode layers against the oracle.
+
+Per call: routing ids, slots, host ids and counts bit for bit; expert outputs y
+and the combined bf16 output within rel-L2 <= 5e-3 and max-abs <= 2e-2.  Covers
+both weight formats, batch 1 and ragged batches (tokens per expert up to 16,
+more than one token chunk), every f of the tiny sweep, all-host (S = 0) and
+all-GPU partitions, speculative requests, and cache-size invariance on the GPU
+(bit-identical outputs for every S >= B*K when f = 65536)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import synth  # noqa: E402
+from synth.configs import TINY  # noqa: E402
+from tests.helpers import PinnedPool, assert_close_bf16, make_engine, oracle_engine, rel_l2  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def eff():
+    import expert_ffn_serving_amd as e
+    assert torch.cuda.is_available()
+    return e
+
+
+def dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def run_decode(eff, pool, K, S, f, B, tokens, router=True, zipf=1.1, spec_keep=-1.0, seed=11,
+               compare_y=True):
+    """Decode `tokens` steps through all layers on the GPU (eff_decode_layer) and the oracle."""
+    L, E, H = pool.L, pool.E, pool.H
+    eng = make_engine(eff, pool, K, S, B, f)
+    orc = oracle_engine(pool, K, S, f)
+    side = torch.cuda.Stream()
+    outs = []
+    try:
+        wrs = [synth.router_weights(seed, l, E, H) for l in range(L)]
+        wrs_d = [dev_bf16(w) for w in wrs]
+        for t in range(tokens):
+            for l in range(L):
+                x = synth.activations(seed, l, t * B, B, H)
+                xd = dev_bf16(x)
+                out = torch.empty((B, H), dtype=torch.int16, device="cuda")
+                spec_ids = None
+                spec_np = None
+                if router:
+                    lg = None
+                else:
+                    lg = synth.trace_logits(seed, l, E, zipf, t * B, B)
+                if spec_keep >= 0 and l + 1 < L:
+                    nxt = synth.trace_logits(seed, l + 1, E, zipf, t * B, B)
+                    truth = synth.gumbel_topk_sets(nxt, K)
+                    spec_np = np.stack([synth.spec_ids(seed, l + 1, E, zipf, t * B + b, truth[b], spec_keep)
+                                        for b in range(B)])
+                    spec_ids = torch.from_numpy(spec_np.reshape(-1)).cuda()
+                eng.decode_layer(l, xd, out, w_router=wrs_d[l] if router else None,
+                                 logits=None if router else torch.from_numpy(lg).cuda(), spec_ids=spec_ids,
+                                 side=side)
+                torch.cuda.synchronize()
+                got = eng.last_layer_arrays(B)
+                r = orc.decode_layer(l, x, logits=lg, router_bits=wrs[l] if router else None, spec_next=spec_np)
+                assert np.array_equal(got["ids"], r["ids"].reshape(-1)), ("ids", t, l)
+                assert list(got["slots"]) == r["slots"], ("slots", t, l)
+                assert list(got["cpu"]) == r["cpu_ids"], ("cpu", t, l)
+                assert list(got["counts"][:3]) == [r["m"], r["q"], r["host"]], ("counts", t, l)
+                if r["spec"] is not None:
+                    assert list(got["counts"][3:5]) == [r["spec"].m, r["spec"].q], ("spec counts", t, l)
+                o = out.cpu().numpy().view(np.uint16)
+                assert_close_bf16(o, r["out_bits"], what="out t=%d l=%d" % (t, l))
+                outs.append(o.copy())
+        snap = eng.snapshot_tables()
+        assert list(snap["table"]) == orc.cache.table
+        assert list(snap["usage"]) == orc.cache.usage
+        return np.stack(outs), eng.stats()
+    finally:
+        eng.close()
+
+
+@pytest.fixture(scope="module")
+def tiny_pool(eff):
+    p = PinnedPool(eff, TINY.seed, TINY.L, TINY.E, TINY.H, TINY.I, TINY.fmt)
+    yield p
+    p.free()
+
+
+@pytest.mark.parametrize("f", list(TINY.f_sweep))
+def test_tiny_decode_every_f(eff, tiny_pool, f):
+    outs, st = run_decode(eff, tiny_pool, TINY.K, TINY.S, f, 1, 16, seed=TINY.seed)
+    assert outs.shape[0] == 16 * TINY.L
+
+
+def test_tiny_all_host_and_invariance(eff, tiny_pool):
+    ref, _ = run_decode(eff, tiny_pool, TINY.K, 16, 65536, 1, 12, seed=TINY.seed)
+    same, _ = run_decode(eff, tiny_pool, TINY.K, 4, 65536, 1, 12, seed=TINY.seed)
+    assert np.array_equal(ref, same)        # S >= B*K with f = 65536: all on the GPU, bit-identical
+    host, st = run_decode(eff, tiny_pool, TINY.K, 0, 65536, 1, 12, seed=TINY.seed)
+    assert st["fetched"] == 0 and st["host"] > 0
+    assert_close_bf16(host, ref, what="all-host vs all-GPU")
+
+
+@pytest.mark.parametrize("fmt,H,I,E,K,B,S,f", [
+    (synth.FMT_INT4, 2048, 512, 16, 8, 1, 24, 26214),
+    (synth.FMT_INT4, 2048, 512, 16, 8, 3, 40, 45875),
+    (synth.FMT_NVFP4, 4096, 2048, 12, 6, 1, 8, 45875),
+    (synth.FMT_NVFP4, 4096, 2048, 12, 6, 4, 20, 65535),
+    (synth.FMT_NVFP4, 2560, 640, 24, 10, 16, 60, 65535),
+])
+def test_decode_shapes(eff, fmt, H, I, E, K, B, S, f):
+    pool = PinnedPool(eff, 21, 2, E, H, I, fmt)
+    try:
+        run_decode(eff, pool, K, S, f, B, 3, router=False, zipf=1.1, seed=21)
+    finally:
+        pool.free()
+
+
+def test_decode_speculative(eff):
+    pool = PinnedPool(eff, 22, 3, 32, 2560, 640, synth.FMT_NVFP4)
+    try:
+        _, st = run_decode(eff, pool, 10, 40, 65535, 2, 4, router=False, zipf=1.2, spec_keep=0.65, seed=22)
+        assert st["spec_fetched"] > 0
+    finally:
+        pool.free()
+
+
+@pytest.mark.parametrize("fmt,H,I", [(synth.FMT_INT4, 2048, 512), (synth.FMT_NVFP4, 4096, 2048),
+                                     (synth.FMT_NVFP4, 2560, 640), (synth.FMT_INT4, 64, 128)])
+def test_expert_ffn_outputs(eff, fmt, H, I):
+    """eff_expert_ffn_decode alone: y of every GPU entry against the oracle's fp64 y."""
+    from oracle.cffn import expert_ffn_batch
+    E, K, B = 8, 4, 5
+    pool = PinnedPool(eff, 23, 1, E, H, I, fmt)
+    eng = make_engine(eff, pool, K, E, B, 65536)
+    try:
+        ids = np.array([[0, 1, 2, 3], [1, 2, 3, 4], [2, 5, 6, 7], [0, 1, 6, 3], [7, 6, 5, 4]], np.int32)
+        d = torch.from_numpy(ids.reshape(-1).copy()).cuda()
+        eng.ensure_experts(0, d)
+        eng.split_misses(d, torch.empty_like(d), torch.empty(3, dtype=torch.int32, device="cuda"))
+        eng.copy_missing()
+        x = synth.activations(23, 0, 0, B, H)
+        y = torch.full((B, K, H), 7.0, dtype=torch.float32, device="cuda")
+        eng.expert_ffn_decode(0, dev_bf16(x), d, y)
+        torch.cuda.synchronize()
+        yg = y.cpu().numpy()
+        xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        jobs = [(pool.record(int(ids[b, k])), pool.tensor_scales(int(ids[b, k])), xf[b:b + 1])
+                for b in range(B) for k in range(K)]
+        refs = expert_ffn_batch(jobs, fmt, H, I, nthreads=16)
+        for j, (b, k) in enumerate([(b, k) for b in range(B) for k in range(K)]):
+            assert rel_l2(yg[b, k], refs[j][0]) < 2e-3, (b, k)
+    finally:
+        eng.close()
+        pool.free()
