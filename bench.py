@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert FFN step over an HBM slot cache on one MI355X.
+
+Default workload (one JSON line on stdout, progress on stderr):
+  decode, 35B-A3B shape: 40 layers x 256 experts, top-8, hidden 2048, expert
+  intermediate 512, int4-g32 weights, 5120 HBM slots (50 %), f = 26214, batch 1,
+  Zipf(1.1) routing trace.  A step is one token through all 40 layers: route,
+  ensure, split (q*), fetch copies, GPU expert FFN, host share, combine.
+  value = tokens/s over `--steps` steps after `--warmup` untimed steps.
+
+Extra fields:
+  roofline      the decode expert-FFN kernels (gate/up + down), algorithmic bytes per
+                launch over their average duration (HIP events on their stream,
+                measured in a separate pass of --profile-steps steps)
+  prefill       whole-layer prefill on the DeepSeek-V4-Flash shape (2048 tokens, 256
+                experts, top-6, 4096 x 2048 NVFP4); MoE TFLOP/s of the grouped GEMM
+  cpu_baseline  the CPU oracle on a bounded sample of the same decode trace
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
+METRIC = "decode expert-FFN tok/s + HBM GB/s (% peak); prefill MoE TFLOP/s (% MFMA)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fill_pool(eff, synth, seed, L, E, H, I, fmt, nthreads):
+    import numpy as np
+    R = synth.record_bytes(H, I)
+    ptr = eff.host_alloc(L * E * R)
+    ts = np.empty(L * E * 3, np.float32)
+    t0 = time.time()
+    synth.fill_records(seed, E, H, I, fmt, 0, L * E, ptr, ts, nthreads)
+    log("  pool %.2f GB filled in %.1f s" % (L * E * R / 1e9, time.time() - t0))
+    return ptr, ts, R
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "expert_ffn_serving_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_sources, n_launch_units):
+    """HBM bytes per launch from committed PMC summaries, when they match the current sources."""
+    path = os.path.join(ROOT, "profiles", "decode_ffn_traffic_35b_a3b.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_sha") != src_hash(*kernel_sources):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------- decode
+def run_decode(eff, torch, synth, W, steps, warmup, profile_steps, threads):
+    import numpy as np
+    log("decode %s: L=%d E=%d K=%d H=%d I=%d S=%d f=%d" % (W.name, W.L, W.E, W.K, W.H, W.I, W.S, W.f_q16))
+    ptr, ts, R = fill_pool(eff, synth, W.seed, W.L, W.E, W.H, W.I, W.fmt, threads)
+    B = W.batches[0]
+    cfg = eff.make_config(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, B, 0, W.f_q16, threads)
+    eng = eff.Engine(cfg, ptr, ts if W.fmt == synth.FMT_NVFP4 else None)
+    n_tok = warmup + steps + profile_steps
+    t0 = time.time()
+    # inputs resident in HBM before timing: x [L, n_tok*B, H] bf16 and trace logits [L, n_tok*B, E]
+    X = torch.empty((W.L, n_tok * B, W.H), dtype=torch.int16, device="cuda")
+    LG = torch.empty((W.L, n_tok * B, W.E), dtype=torch.float32, device="cuda")
+    for l in range(W.L):
+        X[l].copy_(torch.from_numpy(synth.activations(W.seed, l, 0, n_tok * B, W.H).view(np.int16)))
+        LG[l].copy_(torch.from_numpy(synth.trace_logits(W.seed, l, W.E, W.zipf_s, 0, n_tok * B)))
+    out = torch.empty((B, W.H), dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    log("  inputs generated in %.1f s" % (time.time() - t0))
+    L_ = eff.lib()
+    h = eng.h
+    cs = torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    ss = side.cuda_stream
+    xs, ls = X.stride(1) * 2, LG.stride(1) * 4
+    xb, lb = X.data_ptr(), LG.data_ptr()
+    xl, ll = X.stride(0) * 2, LG.stride(0) * 4
+    op = out.data_ptr()
+
+    def step(t):
+        for l in range(W.L):
+            rc = L_.eff_decode_layer(h, l, xb + l * xl + t * B * xs, None, lb + l * ll + t * B * ls, B, None, op,
+                                     cs, ss)
+            if rc:
+                raise eff.EffError(rc, L_.eff_last_error().decode())
+
+    t0 = time.time()
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    log("  warmup %d steps in %.1f s" % (warmup, time.time() - t0))
+    eng.reset_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warmup, warmup + steps):
+        step(t)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = eng.stats()
+    calls = W.L * steps
+    log("  timed %d steps: %.3f s -> %.1f tok/s; per layer-call hit %.2f fetch %.2f host %.2f" % (
+        steps, dt, steps * B / dt, st["hits"] / calls, st["fetched"] / calls, st["host"] / calls))
+    # profiled pass: the same path with the expert kernels bracketed by HIP events
+    eng.reset_stats()
+    eng.set_flags(eff.CFG_TIMING)
+    for t in range(warmup + steps, n_tok):
+        step(t)
+    torch.cuda.synchronize()
+    sp = eng.stats()
+    eng.set_flags(0)
+    n_launch = sp["launches"][eff.T_DECODE_GATEUP]
+    g_ms, d_ms = sp["kernel_ms"][eff.T_DECODE_GATEUP], sp["kernel_ms"][eff.T_DECODE_DOWN]
+    gpu_unique = sp["hits"] + sp["fetched"]               # distinct GPU experts over the pass
+    # algorithmic bytes: every GPU expert's record once, x read, y written per GPU entry (B = 1)
+    total_bytes = gpu_unique * R + n_launch * B * W.H * 2 + gpu_unique * W.H * 4
+    achieved = total_bytes / ((g_ms + d_ms) * 1e-3) / 1e9 if g_ms + d_ms > 0 else 0.0
+    per_launch = total_bytes / max(1, n_launch)
+    src = ("k_decode.hip",)
+    traffic = traffic_from_profile(src, n_launch)
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+        "kernel": "expert_ffn_decode = k_gateup + k_down (one launch pair per layer)",
+        "algorithmic_bytes_per_launch": int(per_launch),
+        "avg_launch_us": round((g_ms + d_ms) * 1e3 / max(1, n_launch), 2),
+        "avg_gateup_us": round(g_ms * 1e3 / max(1, n_launch), 2),
+        "avg_down_us": round(d_ms * 1e3 / max(1, n_launch), 2),
+        "gpu_experts_per_launch": round(gpu_unique / max(1, n_launch), 3),
+        "launches": n_launch, "source_sha": src_hash(*src),
+    }
+    kernel_tok_s = profile_steps * B / ((g_ms + d_ms) * 1e-3) if g_ms + d_ms > 0 else 0.0
+    detail = {
+        "per_layer_call": {k: round(st[k] / calls, 3) for k in ("hits", "fetched", "host")},
+        "bytes_fetched_per_token": int(st["bytes_fetched"] / steps),
+        "kernel_only_tok_s": round(kernel_tok_s, 1),
+        "profile_steps": profile_steps,
+    }
+    eng.close()
+    del X, LG
+    return dict(value=steps * B / dt, ms=dt * 1e3 / steps, roofline=roofline, detail=detail,
+                pool=(ptr, ts, R), B=B)
+
+
+# ------------------------------------------------------------------------------------- prefill
+def run_prefill(eff, torch, synth, W, layers, threads):
+    import numpy as np
+    T = W.prefill_T
+    log("prefill %s: T=%d E=%d K=%d H=%d I=%d (%d layers streamed)" % (W.name, T, W.E, W.K, W.H, W.I, layers))
+    ptr, ts, R = fill_pool(eff, synth, W.seed, layers, W.E, W.H, W.I, W.fmt, threads)
+    cfg = eff.make_config(layers, W.E, W.K, W.H, W.I, W.fmt, W.S, 1, T, W.f_q16, threads, eff.CFG_TIMING)
+    eng = eff.Engine(cfg, ptr, ts)
+    X = [torch.from_numpy(synth.activations(W.seed, l, 0, T, W.H, tag=synth.TAG_PREFILL_X).view(np.int16)).cuda()
+         for l in range(layers)]
+    WR = [torch.from_numpy(synth.router_weights(W.seed, l, W.E, W.H).view(np.int16)).cuda() for l in range(layers)]
+    ids = torch.empty((T, W.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, W.K), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, W.H), dtype=torch.int16, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    eng.reset_stats()
+    t0 = time.perf_counter()
+    eng.prefill_stream_layer(0, side)
+    for l in range(layers):
+        if l + 1 < layers:
+            eng.prefill_stream_layer(l + 1, side)
+        eng.route(X[l], WR[l], ids, w)
+        eng.expert_ffn_prefill_layer(l, X[l], ids, w, out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = eng.stats()
+    g_ms = st["kernel_ms"][eff.T_PREFILL_GATEUP]
+    d_ms = st["kernel_ms"][eff.T_PREFILL_DOWN]
+    n = st["launches"][eff.T_PREFILL_GATEUP]
+    flops = 2.0 * T * W.K * 3 * W.H * W.I           # per layer
+    tflops = flops * n / ((g_ms + d_ms) * 1e-3) / 1e12
+    wbytes = W.E * R
+    res = {
+        "workload": W.name, "tokens": T, "layers_timed": n, "pool_layers": layers,
+        "gflop_per_layer": round(flops / 1e9, 1),
+        "tflops": round(tflops, 1), "peak_tflops": MFMA_PEAK_TFLOPS, "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+        "gemm_ms_per_layer": round((g_ms + d_ms) / max(1, n), 3),
+        "gateup_ms_per_layer": round(g_ms / max(1, n), 3), "down_ms_per_layer": round(d_ms / max(1, n), 3),
+        "weight_GBps": round(wbytes * n / ((g_ms + d_ms) * 1e-3) / 1e9, 1),
+        "wall_ms_per_layer_with_streaming": round(wall * 1e3 / layers, 2),
+        "stream_GBps": round(wbytes * layers / wall / 1e9, 1),
+        "source_sha": src_hash("k_prefill.hip"),
+    }
+    log("  prefill: %.1f TFLOP/s (%.1f%% of MFMA peak), GEMM %.3f ms/layer, wall %.1f ms/layer" % (
+        tflops, 100 * tflops / MFMA_PEAK_TFLOPS, (g_ms + d_ms) / max(1, n), wall * 1e3 / layers))
+    eng.close()
+    eff.host_free(ptr)
+    return res
+
+
+# ------------------------------------------------------------------------------------- CPU oracle
+def cpu_baseline(synth, W, pool, tokens, threads):
+    """The oracle as it stands, on `tokens` decode steps of the same trace (cold cache)."""
+    import ctypes
+
+    import numpy as np
+
+    from oracle.engine import OracleEngine
+    ptr, ts, R = pool
+
+    def rec(flat):
+        return np.frombuffer((ctypes.c_uint8 * R).from_address(ptr + flat * R), np.uint8)
+
+    eng = OracleEngine(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, W.f_q16, rec, lambda f: ts[3 * f:3 * f + 3],
+                       use_c=True, nthreads=threads)
+    lg = [synth.trace_logits(W.seed, l, W.E, W.zipf_s, 0, tokens) for l in range(W.L)]
+    xs = [synth.activations(W.seed, l, 0, tokens, W.H) for l in range(W.L)]
+    t0 = time.perf_counter()
+    for t in range(tokens):
+        for l in range(W.L):
+            eng.decode_layer(l, xs[l][t:t + 1], logits=lg[l][t:t + 1])
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": "%d tokens x %d layers of the %s trace from a cold cache; fp64 C evaluator on %d threads "
+                      "plus single-threaded NumPy routing/policy" % (tokens, W.L, W.name, threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=1024)
+    ap.add_argument("--profile-steps", type=int, default=64)
+    ap.add_argument("--prefill-layers", type=int, default=4)
+    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import expert_ffn_serving_amd as eff
+    import synth
+    from synth.configs import A3B, DSV4_PREFILL
+
+    eff.lib()   # fails loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    dec = run_decode(eff, torch, synth, A3B, args.steps, args.warmup, args.profile_steps, args.threads)
+    cpu = None
+    if not args.skip_cpu:
+        t0 = time.time()
+        cpu = cpu_baseline(synth, A3B, dec["pool"], args.cpu_tokens, args.threads)
+        log("  cpu oracle: %.3f tok/s (%.1f s)" % (cpu["value"], time.time() - t0))
+    eff.host_free(dec["pool"][0])
+    pre = None
+    if not args.skip_prefill:
+        pre = run_prefill(eff, torch, synth, DSV4_PREFILL, args.prefill_layers, args.threads)
+    line = {
+        "metric": METRIC, "value": round(dec["value"], 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dec["ms"], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded generator; random-init int4 experts)",
+        "config": {"workload": A3B.name, "layers": A3B.L, "experts": A3B.E, "top_k": A3B.K, "hidden": A3B.H,
+                   "inter": A3B.I, "weights": "int4-g32-bf16", "slots": A3B.S, "fetch_frac_q16": A3B.f_q16,
+                   "batch": dec["B"], "routing": "zipf(%.1f) trace" % A3B.zipf_s, "parallelism": "single-gpu"},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "decode_detail": dec["detail"],
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,6 +21,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "eff.h")
 INT4_G32_BF16 = 0
 NVFP4_G16_E4M3 = 1
 SPECULATIVE = 1
+CFG_TIMING = 1
+T_DECODE_GATEUP, T_DECODE_DOWN, T_PREFILL_GATEUP, T_PREFILL_DOWN = 0, 1, 2, 3
 
 EFF_OK, EFF_EINVAL, EFF_ENOMEM, EFF_EHIP, EFF_ECAPTURE, EFF_ESTATE, EFF_EDEVICE = 0, -1, -2, -3, -4, -5, -6
 
@@ -42,7 +44,8 @@ class Config(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64), ("hits", ctypes.c_int64), ("fetched", ctypes.c_int64),
                 ("host", ctypes.c_int64), ("spec_fetched", ctypes.c_int64), ("bytes_fetched", ctypes.c_int64),
-                ("qstar_hist", ctypes.c_int64 * 17)]
+                ("qstar_hist", ctypes.c_int64 * 17), ("launches", ctypes.c_int64 * 4),
+                ("kernel_ms", ctypes.c_double * 4)]
 
 
 _lib = None
@@ -79,6 +82,8 @@ def lib():
             "eff_expert_ffn_prefill_layer": (I32, [VP, I32, VP, VP, VP, I32, VP, VP]),
             "eff_snapshot_tables": (I32, [VP, VP, VP, VP, VP, VP]),
             "eff_get_stats": (I32, [VP, VP]),
+            "eff_reset_stats": (I32, [VP]),
+            "eff_set_flags": (I32, [VP, U32]),
             "eff_slot_ptr": (I32, [VP, I32, VP]),
         }
         for name, (res, args) in sig.items():
@@ -91,8 +96,8 @@ def lib():
 
 def declared_functions():
     """Names of the functions include/eff.h declares."""
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(eff_\w+)\s*\(", text, re.M)))
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(eff_\w+)\s*\([^;{]*?\)\s*;", text, re.S)))
 
 
 def _check(rc: int):
@@ -149,8 +154,9 @@ def host_free(ptr: int):
     _check(lib().eff_host_free(ptr))
 
 
-def make_config(L, E, K, H, I, wformat, S, max_tokens, max_prefill_tokens=0, f_q16=65536, host_threads=0):
-    return Config(L, E, K, H, I, wformat, S, max_tokens, max_prefill_tokens, f_q16, host_threads, 0)
+def make_config(L, E, K, H, I, wformat, S, max_tokens, max_prefill_tokens=0, f_q16=65536, host_threads=0,
+                flags=0):
+    return Config(L, E, K, H, I, wformat, S, max_tokens, max_prefill_tokens, f_q16, host_threads, flags)
 
 
 def record_bytes(cfg: Config) -> int:
@@ -258,7 +264,14 @@ class Engine:
         _check(lib().eff_get_stats(self.h, ctypes.byref(st)))
         return dict(calls=st.calls, hits=st.hits, fetched=st.fetched, host=st.host,
                     spec_fetched=st.spec_fetched, bytes_fetched=st.bytes_fetched,
-                    qstar_hist=list(st.qstar_hist))
+                    qstar_hist=list(st.qstar_hist), launches=list(st.launches), kernel_ms=list(st.kernel_ms))
+
+    def reset_stats(self):
+        _check(lib().eff_reset_stats(self.h))
+
+    def set_flags(self, flags: int):
+        _check(lib().eff_set_flags(self.h, flags))
+        self.cfg.flags = flags
 
     def slot_ptr(self, slot: int) -> int:
         out = ctypes.c_void_p()

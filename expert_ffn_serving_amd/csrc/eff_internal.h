@@ -116,10 +116,7 @@ struct eff_engine {
 
   // decode scratch
   eff::DecodePlan* d_plan = nullptr;
-  float* d_a = nullptr;           // [maxU][I][maxB] fp32 SwiGLU activations
-  float* d_part = nullptr;        // gate/up partial sums for split-k
-  int32_t* d_counters = nullptr;  // last-block counters
-  int ksplit = 1;
+  float* d_a = nullptr;           // [maxU][maxB][I] fp32 SwiGLU activations
   int maxU = 0;
 
   // orchestrator buffers (device)
@@ -157,6 +154,12 @@ struct eff_engine {
   int32_t* h_pf_ids = nullptr;      // pinned [T*K]
   int32_t* h_pf_meta = nullptr;     // pinned [2E]
   eff::ThreadPool* pool_threads = nullptr;
+  // kernel timing (EFF_CFG_TIMING): event triples (before, middle, after) per call
+  struct TimedCall { int kind; hipEvent_t ev[3]; };
+  std::vector<TimedCall> timed;     // recorded, not yet resolved
+  std::vector<hipEvent_t> free_events;
+  int64_t t_launches[4] = {0, 0, 0, 0};
+  double t_ms[4] = {0, 0, 0, 0};
   int64_t host_bytes_fetched = 0;
   int64_t host_spec_fetched = 0;
 };
@@ -175,6 +178,9 @@ hipError_t launch_fallback_install(eff_engine* e, int layer, const int32_t* expe
                                    hipStream_t s);
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
                              float* y, hipStream_t s);
+// timing hooks: returns the call's event slot (or -1 when timing is off); mark(i) records event i
+int timing_begin(eff_engine* e, int kind, hipStream_t s);
+void timing_mark(eff_engine* e, int slot, int i, hipStream_t s);
 hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
                           int B, int K, int H, uint16_t* out, hipStream_t s);
 hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int32_t* ids,

@@ -41,6 +41,7 @@ static int validate(const eff_config* c, std::string* why) {
   if (c->max_prefill_tokens < 0) return bad("max_prefill_tokens must be >= 0");
   if (c->fetch_frac_q16 > 65536u) return bad("fetch_frac_q16 must be in [0, 65536]");
   if (c->host_threads < 0 || c->host_threads > 256) return bad("host_threads must be in [0, 256]");
+  if (c->flags & ~(uint32_t)EFF_CFG_TIMING) return bad("unknown config flags");
   if ((int64_t)c->num_layers * c->num_experts > (int64_t)1 << 30) return bad("L*E too large");
   return EFF_OK;
 }
@@ -57,8 +58,7 @@ static hipError_t dalloc(T** p, size_t count) {
 static void release(eff_engine* e) {
   if (!e) return;
   void* dev[] = {e->d_arena, e->d_table, e->d_owner, e->d_usage, e->d_recency, e->d_clock, e->d_ts,
-                 e->d_pending, e->d_fetch, e->d_err, e->d_stats, e->d_plan, e->d_a, e->d_part,
-                 e->d_counters, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, e->d_spec_ids,
+                 e->d_pending, e->d_fetch, e->d_err, e->d_stats, e->d_plan, e->d_a, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, e->d_spec_ids,
                  e->d_spec_cpu, e->d_logits, e->d_ygpu, e->d_yhost, e->d_pf_count, e->d_pf_rows,
                  e->d_pf_a, e->d_pf_y, e->d_pf_meta, e->d_pf_slot_of, e->d_pf_experts};
   for (void* p : dev)
@@ -69,6 +69,10 @@ static void release(eff_engine* e) {
   hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0], e->ev_pf_done[1]};
   for (hipEvent_t v : evs)
     if (v) (void)hipEventDestroy(v);
+  for (auto& tc : e->timed)
+    for (hipEvent_t v : tc.ev)
+      if (v) (void)hipEventDestroy(v);
+  for (hipEvent_t v : e->free_events) (void)hipEventDestroy(v);
   delete e->pool_threads;
   delete e;
 }
@@ -92,15 +96,8 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_fetch_dev, e->h_fetch, 0));
   // decode scratch
   e->maxU = (int)std::min<int64_t>(B * K, E);
-  const int NB = (int)(I / 64), KB = (int)(H / 32);
-  // split-k for the gate/up pass: enough workgroups to cover the chip at batch 1
-  int ks = 1;
-  while (ks * 2 <= KB && KB % (ks * 2) == 0 && (int64_t)e->maxU * NB * ks < 1024 && ks < 16) ks *= 2;
-  e->ksplit = ks;
   EFF_HIP_TRY(dalloc(&e->d_plan, 1));
   EFF_HIP_TRY(dalloc(&e->d_a, (size_t)e->maxU * B * I));
-  EFF_HIP_TRY(dalloc(&e->d_part, (size_t)e->maxU * NB * ks * 2 * 64 * B));
-  EFF_HIP_TRY(dalloc(&e->d_counters, (size_t)e->maxU * NB));
   // orchestrator
   EFF_HIP_TRY(dalloc(&e->d_ids, B * K));
   EFF_HIP_TRY(dalloc(&e->d_w, B * K));
@@ -141,12 +138,59 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipMemset(e->d_pending, 0, sizeof(Pending)));
   EFF_HIP_TRY(hipMemset(e->d_err, 0, 4));
   EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
-  EFF_HIP_TRY(hipMemset(e->d_counters, 0, (size_t)e->maxU * NB * 4));
   std::memset(e->h_fetch, 0, 2 * sizeof(FetchList));
   EFF_HIP_TRY(split_kernel_setup((int)S));
   EFF_HIP_TRY(decode_kernels_setup(c.wformat, (int)B, (int)I));
   EFF_HIP_TRY(hipDeviceSynchronize());
   return EFF_OK;
+}
+
+// ---------------------------------------------------------------------------------- timing
+static hipEvent_t take_event(eff_engine* e) {
+  if (!e->free_events.empty()) {
+    hipEvent_t ev = e->free_events.back();
+    e->free_events.pop_back();
+    return ev;
+  }
+  hipEvent_t ev = nullptr;
+  if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+  return ev;
+}
+
+// Adds the durations of every recorded call (waits for them) and recycles the events.
+static void resolve_timing(eff_engine* e) {
+  for (auto& tc : e->timed) {
+    bool ok = tc.ev[0] && tc.ev[1] && tc.ev[2] && hipEventSynchronize(tc.ev[2]) == hipSuccess;
+    float a = 0.f, b = 0.f;
+    if (ok && hipEventElapsedTime(&a, tc.ev[0], tc.ev[1]) == hipSuccess &&
+        hipEventElapsedTime(&b, tc.ev[1], tc.ev[2]) == hipSuccess) {
+      e->t_ms[tc.kind] += a;
+      e->t_ms[tc.kind + 1] += b;
+      e->t_launches[tc.kind] += 1;
+      e->t_launches[tc.kind + 1] += 1;
+    }
+    for (hipEvent_t ev : tc.ev)
+      if (ev) e->free_events.push_back(ev);
+  }
+  e->timed.clear();
+}
+
+int timing_begin(eff_engine* e, int kind, hipStream_t s) {
+  if (!(e->cfg.flags & EFF_CFG_TIMING)) return -1;
+  if (e->timed.size() >= 4096) resolve_timing(e);  // bounded number of live events
+  eff_engine::TimedCall tc;
+  tc.kind = kind;
+  for (int i = 0; i < 3; ++i) tc.ev[i] = take_event(e);
+  e->timed.push_back(tc);
+  const int slot = (int)e->timed.size() - 1;
+  timing_mark(e, slot, 0, s);
+  return slot;
+}
+
+void timing_mark(eff_engine* e, int slot, int i, hipStream_t s) {
+  if (slot < 0 || slot >= (int)e->timed.size()) return;
+  hipEvent_t ev = e->timed[slot].ev[i];
+  if (ev) (void)hipEventRecord(ev, s);
 }
 
 static int check_engine(eff_engine* e) {
@@ -522,6 +566,32 @@ int eff_get_stats(eff_engine* e, eff_stats* out) {
   out->spec_fetched = st[ST_SPEC_FETCHED];
   out->bytes_fetched = e->host_bytes_fetched;
   for (int i = 0; i < 17; ++i) out->qstar_hist[i] = st[ST_HIST0 + i];
+  resolve_timing(e);
+  for (int i = 0; i < 4; ++i) {
+    out->launches[i] = e->t_launches[i];
+    out->kernel_ms[i] = e->t_ms[i];
+  }
+  return EFF_OK;
+}
+
+int eff_set_flags(eff_engine* e, uint32_t flags) {
+  if (int rc = check_engine(e)) return rc;
+  if (flags & ~(uint32_t)EFF_CFG_TIMING) return fail(EFF_EINVAL, "unknown config flags");
+  e->cfg.flags = flags;
+  return EFF_OK;
+}
+
+int eff_reset_stats(eff_engine* e) {
+  if (int rc = check_engine(e)) return rc;
+  EFF_HIP_TRY(hipDeviceSynchronize());
+  resolve_timing(e);
+  for (int i = 0; i < 4; ++i) {
+    e->t_launches[i] = 0;
+    e->t_ms[i] = 0.0;
+  }
+  e->host_bytes_fetched = 0;
+  e->host_spec_fetched = 0;
+  EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
   return EFF_OK;
 }
 

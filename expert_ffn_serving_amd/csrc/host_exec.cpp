@@ -52,8 +52,8 @@ void block_dot(const uint8_t* pay, const uint8_t* sca, int64_t blk, int fmt, con
   float w[8];
   for (int q = 0; q < 4; ++q) {
     for (int r = 0; r < 16; ++r) {
-      const uint8_t* lanep = pb + (q * 16 + r) * 16;
       for (int t = 0; t < 4; ++t) {
+        const uint8_t* lanep = pb + t * 256 + (q * 16 + r) * 4;
         const int row = t * 16 + r;
         float s;
         if (fmt == EFF_WFMT_INT4_G32_BF16) {
@@ -61,14 +61,14 @@ void block_dot(const uint8_t* pay, const uint8_t* sca, int64_t blk, int fmt, con
           std::memcpy(&sbits, sb + (r * 4 + t) * 2, 2);
           s = bf16f(sbits);
           for (int i = 0; i < 8; ++i) {
-            const uint8_t byte = lanep[t * 4 + i / 2];
+            const uint8_t byte = lanep[i / 2];
             const int u = (i & 1) ? (byte >> 4) : (byte & 15);
             w[i] = (float)(u - 8);
           }
         } else {
           s = T.e4m3[sb[((q >> 1) * 16 + r) * 4 + t]];
           for (int i = 0; i < 8; ++i) {
-            const uint8_t byte = lanep[t * 4 + i / 2];
+            const uint8_t byte = lanep[i / 2];
             w[i] = T.e2m1[(i & 1) ? (byte >> 4) : (byte & 15)];
           }
         }

@@ -5,10 +5,12 @@
 // full per step ([FT-blog] §三.2).  Each distinct slot's record is read once for
 // all tokens routed to it.  Work is split three ways:
 //   k_plan      distinct GPU slots of the call and their entries (one workgroup)
-//   k_gateup    gate and up rows of one 64-row block over a slice of H, both
-//               matrices at once; the last slice to finish (per-block counter)
-//               adds the slices in fixed order and applies SwiGLU
-//   k_down      one 64-row block of the down matrix over all of I
+//   k_gateup    gate and up rows of one 16-row slice over all of H, both matrices
+//               at once, reduced inside the workgroup, SwiGLU applied
+//   k_down      one 16-row slice of the down matrix over all of I
+// No workgroup depends on another inside a kernel, so no device-scope fence is
+// needed (on this multi-die part such a fence writes back and invalidates a whole
+// L2 per wave).
 //   k_combine   out[t] = sum over k of w[t,k] * y[t,k] (fixed k order), bf16 RNE
 // Every reduction has a fixed order (no float atomics): results are bitwise
 // reproducible from run to run.
@@ -87,28 +89,36 @@ k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, Deco
 }
 
 // ---------------------------------------------------------------------------- gate / up
-// grid: maxU * (I/64) * ksplit workgroups of 256 threads.  Lane (q = lane/16, r = lane%16)
-// of a 1 KiB block holds rows 16t + r (t = 0..3), inputs 8q..8q+7 of the block's 32.
+// grid: maxU * (I/16) workgroups of 256 threads, one per (distinct slot, 16-row slice of I).
+// The 4 waves split the 32-input blocks of H; lane (q = lane/16, r = lane%16) holds row r of
+// the slice, inputs 8q..8q+7 of each block (4 bytes of gate, 4 of up).  Everything reduces
+// inside the workgroup, so no workgroup ever waits for another.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
 k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
          const int32_t* __restrict__ owner, const DecodePlan* __restrict__ plan,
-         const uint16_t* __restrict__ x, int H, int I, int K, int ksplit, int maxB,
-         float* __restrict__ part, int32_t* __restrict__ counters, float* __restrict__ a_out) {
-  __shared__ float s_red[4][2][64][NT];
-  __shared__ int s_last;
-  const int NB = I / 64, KB = H / 32, kbs = KB / ksplit;
-  const int wg = blockIdx.x;
-  const int sp = wg % ksplit, nb = (wg / ksplit) % NB, u = wg / (ksplit * NB);
+         const uint16_t* __restrict__ x, int H, int I, int K, int maxB, float* __restrict__ a_out) {
+  constexpr int UNR = NT >= 4 ? 2 : (NT == 2 ? 4 : 8);  // blocks in flight per wave
+  __shared__ float s_red[4][2][16][NT];
+  const int NS = I / 16, NB = I / 64, KB = H / 32;
+  const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
   if (u >= plan->nu) return;
+  const int nb = sl >> 2, t = sl & 3;
   const int slot = plan->uslot[u], cnt = plan->ucount[u];
   const uint8_t* rec = arena + (int64_t)slot * R;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const uint8_t* gp = rec;
-  const uint8_t* up = rec + pay;
-  const uint8_t* gs = rec + 3 * pay;
-  const uint8_t* us = rec + 3 * pay + sca;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
+  const uint8_t* gp = rec + t * 256 + lane * 4;
+  const uint8_t* up = rec + pay + t * 256 + lane * 4;
+  const uint8_t* gs;
+  const uint8_t* us;
+  if (FMT == EFF_WFMT_INT4_G32_BF16) {
+    gs = rec + 3 * pay + r * 8 + t * 2;
+    us = rec + 3 * pay + sca + r * 8 + t * 2;
+  } else {
+    gs = rec + 3 * pay + ((q >> 1) * 16 + r) * 4 + t;
+    us = rec + 3 * pay + sca + ((q >> 1) * 16 + r) * 4 + t;
+  }
   float tsg = 1.f, tsu = 1.f;
   if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
     const int fl = owner[slot];
@@ -120,91 +130,74 @@ k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__
     int tok[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) tok[j] = (j < nt) ? plan->uentry[u][c0 + j] / K : 0;
-    float acc[2][4][NT];
+    float acc[2][NT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int j = 0; j < NT; ++j) acc[0][j] = acc[1][j] = 0.f;
+    for (int kb0 = wave; kb0 < KB; kb0 += 4 * UNR) {
+      // issue every load of UNR blocks first
+      uint32_t wdw[UNR][2];
+      float sc[UNR][2];
+      uint4 xv[UNR][NT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[m][t][j] = 0.f;
-
-    for (int kb = sp * kbs + wave; kb < (sp + 1) * kbs; kb += 4) {
-      const int64_t blk = (int64_t)kb * NB + nb;
-      const uint4 wg4 = *reinterpret_cast<const uint4*>(gp + blk * 1024 + lane * 16);
-      const uint4 wu4 = *reinterpret_cast<const uint4*>(up + blk * 1024 + lane * 16);
-      float sg[4], su[4];
-      if (FMT == EFF_WFMT_INT4_G32_BF16) {
-        const uint2 a = *reinterpret_cast<const uint2*>(gs + blk * 128 + r * 8);
-        const uint2 b = *reinterpret_cast<const uint2*>(us + blk * 128 + r * 8);
-        sg[0] = bf16_lo(a.x); sg[1] = bf16_hi(a.x); sg[2] = bf16_lo(a.y); sg[3] = bf16_hi(a.y);
-        su[0] = bf16_lo(b.x); su[1] = bf16_hi(b.x); su[2] = bf16_lo(b.y); su[3] = bf16_hi(b.y);
-      } else {
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(gs + blk * 128 + ((q >> 1) * 16 + r) * 4);
-        const uint32_t b = *reinterpret_cast<const uint32_t*>(us + blk * 128 + ((q >> 1) * 16 + r) * 4);
-        sg[0] = __builtin_amdgcn_cvt_f32_fp8(a, 0); sg[1] = __builtin_amdgcn_cvt_f32_fp8(a, 1);
-        sg[2] = __builtin_amdgcn_cvt_f32_fp8(a, 2); sg[3] = __builtin_amdgcn_cvt_f32_fp8(a, 3);
-        su[0] = __builtin_amdgcn_cvt_f32_fp8(b, 0); su[1] = __builtin_amdgcn_cvt_f32_fp8(b, 1);
-        su[2] = __builtin_amdgcn_cvt_f32_fp8(b, 2); su[3] = __builtin_amdgcn_cvt_f32_fp8(b, 3);
-      }
-      uint32_t xw[NT][4];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        if (j < nt) {
-          const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)tok[j] * H + kb * 32 + q * 8);
+      for (int z = 0; z < UNR; ++z) {
+        const int kb = kb0 + 4 * z;
+        if (kb < KB) {
+          const int64_t blk = (int64_t)kb * NB + nb;
+          wdw[z][0] = *reinterpret_cast<const uint32_t*>(gp + blk * 1024);
+          wdw[z][1] = *reinterpret_cast<const uint32_t*>(up + blk * 1024);
           if (FMT == EFF_WFMT_INT4_G32_BF16) {
-            // pairs (x0,x4), (x1,x5), (x2,x6), (x3,x7) to meet the nibble pairs below
-            xw[j][0] = (v.x & 0xFFFFu) | (v.z << 16);
-            xw[j][1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
-            xw[j][2] = (v.y & 0xFFFFu) | (v.w << 16);
-            xw[j][3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+            sc[z][0] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(gs + blk * 128) << 16);
+            sc[z][1] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(us + blk * 128) << 16);
           } else {
-            xw[j][0] = v.x; xw[j][1] = v.y; xw[j][2] = v.z; xw[j][3] = v.w;
+            sc[z][0] = __builtin_amdgcn_cvt_f32_fp8((uint32_t)gs[blk * 128], 0);
+            sc[z][1] = __builtin_amdgcn_cvt_f32_fp8((uint32_t)us[blk * 128], 0);
           }
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            xv[z][j] = (j < nt) ? *reinterpret_cast<const uint4*>(x + (int64_t)tok[j] * H + kb * 32 + q * 8)
+                                : make_uint4(0u, 0u, 0u, 0u);
         } else {
-          xw[j][0] = xw[j][1] = xw[j][2] = xw[j][3] = 0u;
+          wdw[z][0] = wdw[z][1] = 0u;
+          sc[z][0] = sc[z][1] = 0.f;
+#pragma unroll
+          for (int j = 0; j < NT; ++j) xv[z][j] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
-      const uint32_t wdw[2][4] = {{wg4.x, wg4.y, wg4.z, wg4.w}, {wu4.x, wu4.y, wu4.z, wu4.w}};
-      if (FMT == EFF_WFMT_INT4_G32_BF16) {
-        float xs[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          xs[j] = dot2_bf16(xw[j][3], 0x3F803F80u,
-                            dot2_bf16(xw[j][2], 0x3F803F80u,
-                                      dot2_bf16(xw[j][1], 0x3F803F80u, dot2_bf16(xw[j][0], 0x3F803F80u, 0.f))));
+      for (int z = 0; z < UNR; ++z) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t d = wdw[m][t];
-            const uint32_t p0 = (d & 0x000F000Fu) | 0x43004300u;
-            const uint32_t p1 = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
-            const uint32_t p2 = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
-            const uint32_t p3 = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
-            const float sc = m ? su[t] : sg[t];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-              float raw = dot2_bf16(p3, xw[j][3], dot2_bf16(p2, xw[j][2],
-                                    dot2_bf16(p1, xw[j][1], dot2_bf16(p0, xw[j][0], 0.f))));
-              acc[m][t][j] = fmaf(sc, fmaf(-136.f, xs[j], raw), acc[m][t][j]);
-            }
+        for (int j = 0; j < NT; ++j) {
+          const uint4 v = xv[z][j];
+          uint32_t xw[4];
+          if (FMT == EFF_WFMT_INT4_G32_BF16) {
+            // pairs (x0,x4), (x1,x5), (x2,x6), (x3,x7) meet the nibble pairs below
+            xw[0] = (v.x & 0xFFFFu) | (v.z << 16);
+            xw[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
+            xw[2] = (v.y & 0xFFFFu) | (v.w << 16);
+            xw[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+          } else {
+            xw[0] = v.x; xw[1] = v.y; xw[2] = v.z; xw[3] = v.w;
           }
-        }
-      } else {
+          float xs = 0.f;
+          if (FMT == EFF_WFMT_INT4_G32_BF16)
+            xs = dot2_bf16(xw[3], 0x3F803F80u, dot2_bf16(xw[2], 0x3F803F80u,
+                           dot2_bf16(xw[1], 0x3F803F80u, dot2_bf16(xw[0], 0x3F803F80u, 0.f))));
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t d = wdw[m][t];
-            const uint32_t p0 = fp4_to_bf16x2<0>(d), p1 = fp4_to_bf16x2<1>(d);
-            const uint32_t p2 = fp4_to_bf16x2<2>(d), p3 = fp4_to_bf16x2<3>(d);
-            const float sc = m ? su[t] : sg[t];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-              float raw = dot2_bf16(p3, xw[j][3], dot2_bf16(p2, xw[j][2],
-                                    dot2_bf16(p1, xw[j][1], dot2_bf16(p0, xw[j][0], 0.f))));
-              acc[m][t][j] = fmaf(sc, raw, acc[m][t][j]);
+          for (int m = 0; m < 2; ++m) {
+            const uint32_t d = wdw[z][m];
+            uint32_t p0, p1, p2, p3;
+            if (FMT == EFF_WFMT_INT4_G32_BF16) {
+              p0 = (d & 0x000F000Fu) | 0x43004300u;
+              p1 = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
+              p2 = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
+              p3 = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
+            } else {
+              p0 = fp4_to_bf16x2<0>(d); p1 = fp4_to_bf16x2<1>(d);
+              p2 = fp4_to_bf16x2<2>(d); p3 = fp4_to_bf16x2<3>(d);
             }
+            float raw = dot2_bf16(p3, xw[3], dot2_bf16(p2, xw[2], dot2_bf16(p1, xw[1], dot2_bf16(p0, xw[0], 0.f))));
+            if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-136.f, xs, raw);
+            acc[m][j] = fmaf(sc[z][m], raw, acc[m][j]);
           }
         }
       }
@@ -213,79 +206,61 @@ k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          float v = acc[m][t][j];
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 32);
-          acc[m][t][j] = v;
-        }
+      for (int j = 0; j < NT; ++j) {
+        float v = acc[m][j];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[m][j] = v;
+      }
     if (lane < 16) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int j = 0; j < NT; ++j) s_red[wave][m][t * 16 + r][j] = acc[m][t][j];
+        for (int j = 0; j < NT; ++j) s_red[wave][m][r][j] = acc[m][j];
     }
     __syncthreads();
-    for (int i = tid; i < 2 * 64 * nt; i += kWG) {
-      const int m = i / (64 * nt), row = (i / nt) % 64, j = i % nt;
-      float v = s_red[0][m][row][j] + s_red[1][m][row][j];
-      v += s_red[2][m][row][j];
-      v += s_red[3][m][row][j];
-      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= m ? tsu : tsg;
-      // partial of split sp: part[((u*NB + nb)*ksplit + sp)][m][row][token]
-      part[((((int64_t)u * NB + nb) * ksplit + sp) * 2 + m) * 64 * maxB + row * maxB + c0 + j] = v;
+    if (tid < 16 * nt) {
+      const int row = tid / nt, j = tid % nt;
+      float g = s_red[0][0][row][j] + s_red[1][0][row][j];
+      g += s_red[2][0][row][j];
+      g += s_red[3][0][row][j];
+      float v = s_red[0][1][row][j] + s_red[1][1][row][j];
+      v += s_red[2][1][row][j];
+      v += s_red[3][1][row][j];
+      g *= tsg;
+      v *= tsu;
+      a_out[((int64_t)u * maxB + c0 + j) * I + sl * 16 + row] = silu(g) * v;
     }
     __syncthreads();
   }
-  // the last split of this (u, nb) to finish adds the splits in order and applies SwiGLU
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&counters[u * NB + nb], 1);
-    s_last = (prev == ksplit - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int i = tid; i < 64 * cnt; i += kWG) {
-    const int row = i / cnt, j = i % cnt;
-    float g = 0.f, v = 0.f;
-    for (int s2 = 0; s2 < ksplit; ++s2) {
-      const int64_t b = (((int64_t)u * NB + nb) * ksplit + s2) * 2;
-      g += __builtin_nontemporal_load(&part[(b + 0) * 64 * maxB + row * maxB + j]);
-      v += __builtin_nontemporal_load(&part[(b + 1) * 64 * maxB + row * maxB + j]);
-    }
-    a_out[((int64_t)u * maxB + j) * I + nb * 64 + row] = silu(g) * v;
-  }
-  if (tid == 0) counters[u * NB + nb] = 0;
 }
 
 // ---------------------------------------------------------------------------- down
-// grid: maxU * (H/64) workgroups.  The SwiGLU activations of the slot's tokens are staged
-// in LDS as fp16, each token scaled by a power of two so that its largest value fits.
+// grid: maxU * (H/16) workgroups, one per (distinct slot, 16-row slice of H).  The SwiGLU
+// activations of the slot's tokens are staged in LDS as fp16, each token scaled by a power of
+// two so that its largest value fits.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
 k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
        const int32_t* __restrict__ owner, const DecodePlan* __restrict__ plan,
        const float* __restrict__ a_in, int H, int I, int maxB, float* __restrict__ y) {
-  extern __shared__ uint32_t s_a[];          // [NT][I/2] fp16 pairs, int4 order permuted per 8
+  extern __shared__ uint4 s_a4[];            // [NT][I/8] groups of 8 fp16 (int4 order permuted)
   __shared__ float s_asum[NT][512];          // int4: sum of each 8-group (I/8 <= 512)
-  __shared__ float s_red[4][64][NT];
+  __shared__ float s_red[4][16][NT];
   __shared__ float s_scale[NT];
   __shared__ float s_amax[NT][4];
-  const int NBH = H / 64, KB = I / 32;
-  const int u = blockIdx.x / NBH, nb = blockIdx.x % NBH;
+  constexpr int UNR = NT >= 4 ? 2 : 4;
+  const int NS = H / 16, NBH = H / 64, KB = I / 32;
+  const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
   if (u >= plan->nu) return;
+  const int nb = sl >> 2, t = sl & 3;
   const int slot = plan->uslot[u], cnt = plan->ucount[u];
   const uint8_t* rec = arena + (int64_t)slot * R;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const uint8_t* dp = rec + 2 * pay;
-  const uint8_t* ds = rec + 3 * pay + 2 * sca;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
+  const uint8_t* dp = rec + 2 * pay + t * 256 + lane * 4;
+  const uint8_t* ds = (FMT == EFF_WFMT_INT4_G32_BF16) ? rec + 3 * pay + 2 * sca + r * 8 + t * 2
+                                                      : rec + 3 * pay + 2 * sca + ((q >> 1) * 16 + r) * 4 + t;
   float tsd = 1.f;
   if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsd = ts[(int64_t)owner[slot] * 3 + 2];
 
@@ -321,55 +296,46 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
         h[z] = (_Float16)(src[z] * inv);
         sum += (float)h[z];
       }
-      uint32_t* dst = s_a + j * (I / 2) + g * 4;
+      uint32_t o[4];
       if (FMT == EFF_WFMT_INT4_G32_BF16) {
 #pragma unroll
         for (int z = 0; z < 4; ++z)
-          dst[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[z]) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, h[z + 4]) << 16);
+          o[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[z]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[z + 4]) << 16);
         s_asum[j][g] = sum;
       } else {
 #pragma unroll
         for (int z = 0; z < 4; ++z)
-          dst[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * z]) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * z + 1]) << 16);
+          o[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * z]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * z + 1]) << 16);
       }
+      s_a4[j * (I / 8) + g] = make_uint4(o[0], o[1], o[2], o[3]);
     }
     __syncthreads();
-    float acc[4][NT];
+    float acc[NT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int j = 0; j < NT; ++j) acc[j] = 0.f;
+    for (int kb0 = wave; kb0 < KB; kb0 += 4 * UNR) {
+      uint32_t wdw[UNR];
+      float sd[UNR];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[t][j] = 0.f;
-    for (int kb = wave; kb < KB; kb += 4) {
-      const int64_t blk = (int64_t)kb * NBH + nb;
-      const uint4 w4 = *reinterpret_cast<const uint4*>(dp + blk * 1024 + lane * 16);
-      float sd[4];
-      if (FMT == EFF_WFMT_INT4_G32_BF16) {
-        const uint2 a = *reinterpret_cast<const uint2*>(ds + blk * 128 + r * 8);
-        sd[0] = bf16_lo(a.x); sd[1] = bf16_hi(a.x); sd[2] = bf16_lo(a.y); sd[3] = bf16_hi(a.y);
-      } else {
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(ds + blk * 128 + ((q >> 1) * 16 + r) * 4);
-        sd[0] = __builtin_amdgcn_cvt_f32_fp8(a, 0); sd[1] = __builtin_amdgcn_cvt_f32_fp8(a, 1);
-        sd[2] = __builtin_amdgcn_cvt_f32_fp8(a, 2); sd[3] = __builtin_amdgcn_cvt_f32_fp8(a, 3);
-      }
-      const uint32_t wdw[4] = {w4.x, w4.y, w4.z, w4.w};
-      uint32_t av[NT][4];
-      float asum[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        if (j < nt) {
-          const uint4 v = *reinterpret_cast<const uint4*>(s_a + j * (I / 2) + (kb * 4 + q) * 4);
-          av[j][0] = v.x; av[j][1] = v.y; av[j][2] = v.z; av[j][3] = v.w;
-          asum[j] = (FMT == EFF_WFMT_INT4_G32_BF16) ? s_asum[j][kb * 4 + q] : 0.f;
+      for (int z = 0; z < UNR; ++z) {
+        const int kb = kb0 + 4 * z;
+        if (kb < KB) {
+          const int64_t blk = (int64_t)kb * NBH + nb;
+          wdw[z] = *reinterpret_cast<const uint32_t*>(dp + blk * 1024);
+          sd[z] = (FMT == EFF_WFMT_INT4_G32_BF16)
+                      ? __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(ds + blk * 128) << 16)
+                      : __builtin_amdgcn_cvt_f32_fp8((uint32_t)ds[blk * 128], 0);
         } else {
-          av[j][0] = av[j][1] = av[j][2] = av[j][3] = 0u;
-          asum[j] = 0.f;
+          wdw[z] = 0u;
+          sd[z] = 0.f;
         }
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t d = wdw[t];
+      for (int z = 0; z < UNR; ++z) {
+        const int kb = kb0 + 4 * z;
+        if (kb >= KB) break;
+        const uint32_t d = wdw[z];
         uint32_t p0, p1, p2, p3;
         if (FMT == EFF_WFMT_INT4_G32_BF16) {
           p0 = (d & 0x000F000Fu) | 0x64006400u;
@@ -382,37 +348,35 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          float raw = dot2_f16(p3, av[j][3], dot2_f16(p2, av[j][2], dot2_f16(p1, av[j][1],
-                               dot2_f16(p0, av[j][0], 0.f))));
-          if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-1032.f, asum[j], raw);
-          acc[t][j] = fmaf(sd[t], raw, acc[t][j]);
+          if (j < nt) {
+            const uint4 av = s_a4[j * (I / 8) + kb * 4 + q];
+            float raw = dot2_f16(p3, av.w, dot2_f16(p2, av.z, dot2_f16(p1, av.y, dot2_f16(p0, av.x, 0.f))));
+            if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-1032.f, s_asum[j][kb * 4 + q], raw);
+            acc[j] = fmaf(sd[z], raw, acc[j]);
+          }
         }
       }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        float v = acc[t][j];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[t][j] = v;
-      }
+    for (int j = 0; j < NT; ++j) {
+      float v = acc[j];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[j] = v;
+    }
     if (lane < 16) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) s_red[wave][t * 16 + r][j] = acc[t][j];
+      for (int j = 0; j < NT; ++j) s_red[wave][r][j] = acc[j];
     }
     __syncthreads();
-    for (int i = tid; i < 64 * nt; i += kWG) {
-      const int row = i / nt, j = i % nt;
+    if (tid < 16 * nt) {
+      const int row = tid / nt, j = tid % nt;
       float v = s_red[0][row][j] + s_red[1][row][j];
       v += s_red[2][row][j];
       v += s_red[3][row][j];
       v = v * s_scale[j] * tsd;
       const int p = plan->uentry[u][c0 + j];
-      y[(int64_t)p * H + nb * 64 + row] = v;
+      y[(int64_t)p * H + sl * 16 + row] = v;
     }
     __syncthreads();
   }
@@ -440,17 +404,18 @@ template <int FMT, int NT>
 hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, hipStream_t s) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
-  dim3 g1(e->maxU * (I / 64) * e->ksplit);
-  hipLaunchKernelGGL((k_gateup<FMT, NT>), g1, dim3(kWG), 0, s, e->d_arena, e->R, e->d_ts, e->d_owner,
-                     e->d_plan, x, H, I, c.top_k, e->ksplit, c.max_tokens, e->d_part, e->d_counters,
-                     e->d_a);
+  const int ts = timing_begin(e, EFF_T_DECODE_GATEUP, s);
+  hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(e->maxU * (I / 16)), dim3(kWG), 0, s, e->d_arena, e->R, e->d_ts,
+                     e->d_owner, e->d_plan, x, H, I, c.top_k, c.max_tokens, e->d_a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dim3 g2(e->maxU * (H / 64));
-  size_t lds = (size_t)NT * (I / 2) * sizeof(uint32_t);
-  hipLaunchKernelGGL((k_down<FMT, NT>), g2, dim3(kWG), lds, s, e->d_arena, e->R, e->d_ts, e->d_owner,
-                     e->d_plan, e->d_a, H, I, c.max_tokens, y);
-  return hipGetLastError();
+  timing_mark(e, ts, 1, s);
+  size_t lds = (size_t)NT * (I / 8) * sizeof(uint4);
+  hipLaunchKernelGGL((k_down<FMT, NT>), dim3(e->maxU * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->R, e->d_ts,
+                     e->d_owner, e->d_plan, e->d_a, H, I, c.max_tokens, y);
+  err = hipGetLastError();
+  timing_mark(e, ts, 2, s);
+  return err;
 }
 
 }  // namespace
@@ -460,7 +425,7 @@ int decode_nt(int maxB) { return maxB >= 8 ? 8 : maxB >= 4 ? 4 : maxB >= 2 ? 2 :
 hipError_t decode_kernels_setup(int fmt, int maxB, int I) {
   // allow up to NT * I * 2 bytes of dynamic LDS for the down kernel
   const int NT = decode_nt(maxB);
-  const int lds = NT * (I / 2) * 4;
+  const int lds = NT * (I / 8) * 16;
   hipError_t err = hipSuccess;
 #define SETUP(F, N)                                                                                    \
   if (fmt == F && NT == N)                                                                              \

@@ -13,7 +13,8 @@
 //
 // Weights stay 4-bit in HBM and are dequantized in registers straight into the
 // MFMA B operand: a lane's 4 bytes for rows 16t+r, inputs 8q..8q+7 of a record
-// block are exactly the B fragment of lane 16q+r for n-subtile t.  NVFP4:
+// block (slice t, offset (16q+r)*4) are exactly the B fragment of lane 16q+r for
+// n-subtile t.  NVFP4:
 // e2m1 -> fp16 with v_cvt_scalef32_pk_f16_fp4, times the e4m3 block scale with
 // a packed fp16 multiply (e2m1 * e4m3 has at most 6 significant bits and lies
 // in [2^-10, 2688], so it is exact in fp16); the fp32 tensor scale is applied
@@ -188,6 +189,13 @@ __device__ inline void stage_tile(uint32_t* s_tile, const void* src, int ld, con
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// The 4 bytes of this lane in each 16-row slice t of a 1 KiB payload block (slice t holds
+// rows 16t..16t+15 as 256 contiguous bytes): .x = t0, .y = t1, .z = t2, .w = t3.
+__device__ inline uint4 load_block(const uint8_t* blk, int lane) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(blk + lane * 4);
+  return make_uint4(p[0], p[64], p[128], p[192]);
+}
+
 // grid: E * (I / 256); 4 waves, wave w owns row block nb = j*4 + w of gate and up
 template <int FMT>
 __global__ void __launch_bounds__(256)
@@ -228,8 +236,8 @@ k_pf_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restric
     uint32_t sn[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     if (active) {
       const int64_t blk = (int64_t)0 * NB + nb;
-      wn[0] = *reinterpret_cast<const uint4*>(rec + blk * 1024 + lane * 16);
-      wn[1] = *reinterpret_cast<const uint4*>(rec + pay + blk * 1024 + lane * 16);
+      wn[0] = load_block(rec + blk * 1024, lane);
+      wn[1] = load_block(rec + pay + blk * 1024, lane);
       load_scales<FMT>(rec + 3 * pay + blk * 128, q, r, sn[0]);
       load_scales<FMT>(rec + 3 * pay + sca + blk * 128, q, r, sn[1]);
     }
@@ -242,8 +250,8 @@ k_pf_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restric
         for (int t = 0; t < 4; ++t) sc[m][t] = sn[m][t];
       if (active && kb + 1 < KB) {  // prefetch the next k block
         const int64_t blk = (int64_t)(kb + 1) * NB + nb;
-        wn[0] = *reinterpret_cast<const uint4*>(rec + blk * 1024 + lane * 16);
-        wn[1] = *reinterpret_cast<const uint4*>(rec + pay + blk * 1024 + lane * 16);
+        wn[0] = load_block(rec + blk * 1024, lane);
+        wn[1] = load_block(rec + pay + blk * 1024, lane);
         load_scales<FMT>(rec + 3 * pay + blk * 128, q, r, sn[0]);
         load_scales<FMT>(rec + 3 * pay + sca + blk * 128, q, r, sn[1]);
       }
@@ -320,7 +328,7 @@ k_pf_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
     uint4 wn = make_uint4(0u, 0u, 0u, 0u);
     uint32_t sn[4] = {0u, 0u, 0u, 0u};
     if (active) {
-      wn = *reinterpret_cast<const uint4*>(dp + (int64_t)nb * 1024 + lane * 16);
+      wn = load_block(dp + (int64_t)nb * 1024, lane);
       load_scales<FMT>(ds + (int64_t)nb * 128, q, r, sn);
     }
     for (int kb = 0; kb < KB; ++kb) {
@@ -328,7 +336,7 @@ k_pf_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
       uint32_t sc[4] = {sn[0], sn[1], sn[2], sn[3]};
       if (active && kb + 1 < KB) {
         const int64_t blk = (int64_t)(kb + 1) * NB + nb;
-        wn = *reinterpret_cast<const uint4*>(dp + blk * 1024 + lane * 16);
+        wn = load_block(dp + blk * 1024, lane);
         load_scales<FMT>(ds + blk * 128, q, r, sn);
       }
       __syncthreads();
@@ -380,6 +388,7 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
   const bool fp4 = c.wformat == EFF_WFMT_NVFP4_G16_E4M3;
   const int nbx1 = ((E + 7) / 8) * 8 * ((I / 64 + 3) / 4);
   const int nbx2 = ((E + 7) / 8) * 8 * ((H / 64 + 3) / 4);
+  const int ts = timing_begin(e, EFF_T_PREFILL_GATEUP, s);
   if (fp4)
     hipLaunchKernelGGL(k_pf_gateup<EFF_WFMT_NVFP4_G16_E4M3>, dim3(nbx1), dim3(256), 0, s, e->d_arena, e->R,
                        e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, x, E, H, I,
@@ -389,6 +398,7 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
                        e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, x, E, H, I,
                        K, e->d_pf_a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  timing_mark(e, ts, 1, s);
   if (fp4)
     hipLaunchKernelGGL(k_pf_down<EFF_WFMT_NVFP4_G16_E4M3>, dim3(nbx2), dim3(256), 0, s, e->d_arena, e->R,
                        e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, e->d_pf_a,
@@ -398,6 +408,7 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
                        e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, e->d_pf_a,
                        E, H, I, e->d_pf_y);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  timing_mark(e, ts, 2, s);
   if (!combine) return hipSuccess;
   return launch_combine(e->d_pf_y, nullptr, nullptr, w, T, K, H, out, s);
 }

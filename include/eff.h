@@ -22,8 +22,8 @@
  * same order ([NVMe-8GB] "엔진" item 1).  Each matrix (N rows = outputs, Kd
  * columns = inputs) is stored as 1 KiB blocks of 64 rows x 32 inputs, block
  * index kb*(N/64)+nb (kb = k/32, nb = n/64); inside a block element (n, k) is
- * at byte (q*16 + r)*16 + t*4 + i/2 with t=(n%64)/16, r=n%16, q=(k%32)/8,
- * i=k%8, even i in the low nibble.  Each block has a 128-byte scale block at
+ * at byte t*256 + (q*16 + r)*4 + i/2 with t=(n%64)/16, r=n%16, q=(k%32)/8,
+ * i=k%8, even i in the low nibble (each 16-row slice is 256 contiguous bytes).  Each block has a 128-byte scale block at
  * the same index: INT4_G32_BF16 stores the bf16 scale of (n, k/32) at byte
  * (r*4+t)*2 and values are (u-8)*scale; NVFP4_G16_E4M3 stores the e4m3 scale
  * of (n, k/16) at byte (((k%32)/16)*16 + r)*4 + t and values are
@@ -59,6 +59,12 @@ enum { EFF_WFMT_INT4_G32_BF16 = 0, EFF_WFMT_NVFP4_G16_E4M3 = 1 };
 /* eff_ensure_experts flags */
 enum { EFF_SPECULATIVE = 1u };
 
+/* eff_config.flags */
+enum {
+  EFF_CFG_TIMING = 1u /* bracket the expert kernels with HIP events on their stream; the
+                         durations are summed into eff_stats (adds two event records per call) */
+};
+
 typedef struct eff_config {
   int32_t num_layers;         /* L */
   int32_t num_experts;        /* E, <= 4096 */
@@ -71,7 +77,7 @@ typedef struct eff_config {
   int32_t max_prefill_tokens; /* prefill chunk bound T (0: no prefill) */
   uint32_t fetch_frac_q16;    /* f = B_P/B_H * 65536, 0..65536 */
   int32_t host_threads;       /* threads of the host executor (0: hardware concurrency) */
-  uint32_t flags;             /* reserved, 0 */
+  uint32_t flags;             /* EFF_CFG_* bits */
 } eff_config;
 
 /* Record size R for the config's (H, I, format); 0 if the config is invalid. */
@@ -192,12 +198,22 @@ int eff_expert_ffn_prefill_layer(eff_engine* e, int layer, const void* x, const 
 int eff_snapshot_tables(eff_engine* e, int32_t* table, int32_t* owner, int64_t* usage,
                         int64_t* recency, int64_t* clock);
 
+/* Kernel timing slots of eff_stats (filled with EFF_CFG_TIMING). */
+enum { EFF_T_DECODE_GATEUP = 0, EFF_T_DECODE_DOWN = 1, EFF_T_PREFILL_GATEUP = 2, EFF_T_PREFILL_DOWN = 3 };
+
 typedef struct eff_stats {
   int64_t calls, hits, fetched, host, spec_fetched; /* unique experts, summed over calls */
   int64_t bytes_fetched;
   int64_t qstar_hist[17]; /* q' counts 0..15, 16+ */
+  int64_t launches[4];    /* timed launches per EFF_T_* slot */
+  double kernel_ms[4];    /* summed durations per EFF_T_* slot (HIP events) */
 } eff_stats;
+/* Changes eff_config.flags of a live engine (EFF_CFG_* bits); EFF_EINVAL for unknown bits. */
+int eff_set_flags(eff_engine* e, uint32_t flags);
+
+/* Waits for the device; counters since eff_create (or the last eff_reset_stats). */
 int eff_get_stats(eff_engine* e, eff_stats* out);
+int eff_reset_stats(eff_engine* e);
 
 /* Device pointer of slot s (for tests: slot bytes must equal the host record). */
 int eff_slot_ptr(eff_engine* e, int slot, const void** out);

@@ -45,7 +45,7 @@ static void decode_row(const uint8_t* rec, int fmt, int64_t H, int64_t I, int m,
   for (int64_t k = 0; k < Kd; ++k) {
     int64_t kb = k / 32, nb = n / 64, blk = kb * (N / 64) + nb;
     int64_t t = (n % 64) / 16, r = n % 16, q = (k % 32) / 8, i = k % 8;
-    int64_t off = blk * 1024 + (q * 16 + r) * 16 + t * 4 + i / 2;
+    int64_t off = blk * 1024 + t * 256 + (q * 16 + r) * 4 + i / 2;
     int code = (i % 2 == 0) ? (pay[off] & 15) : (pay[off] >> 4);
     int64_t sbase = blk * 128;
     if (fmt == 0) {

@@ -16,7 +16,7 @@ Record byte layout (the layout the library is written against; restated here
 independently of the writer): a matrix of N output rows by Kd inputs is cut
 into payload blocks of 64 rows x 32 inputs (1 KiB), block index
 kb * (N/64) + nb for kb = k // 32, nb = n // 64.  Inside the block element
-(n, k) is at byte (q*16 + r)*16 + t*4 + i//2, t = (n%64)//16, r = n%16,
+(n, k) is at byte t*256 + (q*16 + r)*4 + i//2, t = (n%64)//16, r = n%16,
 q = (k%32)//8, i = k%8, even i in the low nibble.  Scale block b is 128 bytes
 at the same index: int4 keeps the bf16 of (n, k//32) at byte (r*4 + t)*2;
 NVFP4 keeps the e4m3 of (n, k//16) at byte (((k%32)//16)*16 + r)*4 + t.
@@ -89,7 +89,7 @@ def payload_index(N: int, n: np.ndarray, k: np.ndarray):
     kb, nb = k // 32, n // 64
     blk = kb * (N // 64) + nb
     t, r, q, i = (n % 64) // 16, n % 16, (k % 32) // 8, k % 8
-    return blk * 1024 + (q * 16 + r) * 16 + t * 4 + i // 2, (i % 2) * 4
+    return blk * 1024 + t * 256 + (q * 16 + r) * 4 + i // 2, (i % 2) * 4
 
 
 def scale_index(fmt: int, N: int, n: np.ndarray, k: np.ndarray) -> np.ndarray:

@@ -31,7 +31,8 @@ def build(force: bool = False) -> str:
     """Compile libsynth.so with gcc (plain C, no GPU code)."""
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         tmp = _SO + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O3", "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", "-O3", "-mavx2", "-mfma", "-ffp-contract=off", "-fno-math-errno", "-fPIC",
+                               "-shared", "-pthread", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _SO)
     return _SO
 

@@ -23,9 +23,9 @@
  * ("엔진", item 1).  Each matrix (N output rows, Kd input columns, N % 64 == 0,
  * Kd % 32 == 0) is cut into 1 KiB payload blocks of 64 rows x 32 columns,
  * ordered block = kb * (N / 64) + nb with kb = k / 32, nb = n / 64.  Inside a
- * block, element (n, k) sits at byte (q * 16 + r) * 16 + t * 4 + i / 2 with
+ * block, element (n, k) sits at byte t * 256 + (q * 16 + r) * 4 + i / 2 with
  * t = (n % 64) / 16, r = n % 16, q = (k % 32) / 8, i = k % 8; even i in the
- * low nibble.  Each payload block has a 128-byte scale block at the same
+ * low nibble (each 16-row slice t is a contiguous 256 bytes).  Each payload block has a 128-byte scale block at the same
  * index: int4 -> bf16 scale of (n, k / 32) at (r * 4 + t) * 2; NVFP4 -> e4m3
  * scale of (n, k / 16) at (((k % 32) / 16) * 16 + r) * 4 + t.
  */
@@ -106,54 +106,33 @@ static double e4m3_value(int code) {
   return (code & 0x80) ? -v : v;
 }
 
-/* nearest positive e4m3 code (0x00..0x7E), ties to the even code; clamps to 448. */
+/* nearest positive e4m3 code (0x00..0x7E), ties to the even code; clamps to 448.
+ * Within a binade 2^e * (1 + m/8) the nearest m is rint of the scaled mantissa (ties to even
+ * m, i.e. the even code); m = 8 carries into the next binade; below 2^-6 the codes are the
+ * subnormals m * 2^-9 with the same spacing. */
 static uint8_t e4m3_encode_pos(double v) {
   if (!(v > 0.0)) return 0;
   if (v >= 448.0) return 0x7E;
-  int lo = 0, hi = 0x7E; /* value is monotone in the code over 0..0x7E */
-  while (hi - lo > 1) {
-    int mid = (lo + hi) / 2;
-    if (e4m3_value(mid) <= v) lo = mid; else hi = mid;
-  }
-  double dl = v - e4m3_value(lo), dh = e4m3_value(hi) - v;
-  if (dl < dh) return (uint8_t)lo;
-  if (dh < dl) return (uint8_t)hi;
-  return (uint8_t)((lo & 1) ? hi : lo);
+  if (v < 0.015625) return (uint8_t)rint(v * 512.0); /* 0..8; 8 is 2^-6, code 0x08 */
+  int ex;
+  double f = frexp(v, &ex);                           /* v = f * 2^ex, f in [0.5, 1) */
+  int e = ex - 1;
+  int m = (int)rint((2.0 * f - 1.0) * 8.0);
+  if (m == 8) { m = 0; e += 1; }
+  int code = ((e + 7) << 3) | m;
+  return (uint8_t)(code > 0x7E ? 0x7E : code);
 }
 
-static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
-
-/* nearest e2m1 code for v (sign kept, magnitude clamped to 6), ties to the even code. */
-static uint8_t e2m1_encode(double v) {
+/* nearest e2m1 code for v (sign kept, magnitude clamped to 6), ties to the even code.
+ * Magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; midpoints .25 .75 1.25 1.75 2.5 3.5 5 go to the even
+ * code of the two (codes 0, 2, 2, 4, 4, 6, 6). */
+static inline uint8_t e2m1_encode(double v) {
   double a = fabs(v);
-  int best = 0;
-  if (a >= 6.0) best = 7;
-  else {
-    for (int c = 0; c < 7; ++c) {
-      if (a >= E2M1_MAG[c] && a <= E2M1_MAG[c + 1]) {
-        double dl = a - E2M1_MAG[c], dh = E2M1_MAG[c + 1] - a;
-        best = (dl < dh) ? c : (dh < dl) ? c + 1 : ((c & 1) ? c + 1 : c);
-        break;
-      }
-    }
-  }
-  return (uint8_t)(best | ((v < 0.0) ? 8 : 0));
+  int c = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0);
+  return (uint8_t)(c | ((v < 0.0) ? 8 : 0));
 }
 
 /* ---------------------------------------------------------------- record layout (writer side) */
-
-static inline int64_t payload_off(int64_t N, int64_t n, int64_t k) {
-  int64_t kb = k / 32, nb = n / 64;
-  int64_t blk = kb * (N / 64) + nb;
-  int64_t t = (n % 64) / 16, r = n % 16, q = (k % 32) / 8, i = k % 8;
-  return blk * 1024 + (q * 16 + r) * 16 + t * 4 + i / 2;
-}
-
-static inline void put_nibble(uint8_t* base, int64_t N, int64_t n, int64_t k, uint8_t code) {
-  int64_t off = payload_off(N, n, k);
-  if (k % 2 == 0) base[off] = (uint8_t)((base[off] & 0xF0) | (code & 15));
-  else base[off] = (uint8_t)((base[off] & 0x0F) | ((code & 15) << 4));
-}
 
 static inline int64_t scale_block_off(int64_t N, int64_t n, int64_t k) {
   return ((k / 32) * (N / 64) + n / 64) * 128;
@@ -171,12 +150,25 @@ void synth_weights_f32(uint64_t seed, int64_t E, int64_t l, int64_t e, int m, in
   synth_normal_f32(seed, TAG_WEIGHT, (uint64_t)(l * E + e), (uint64_t)m, N * Kd, sigma, out);
 }
 
+/* Store the 32 codes of inputs 32*kb .. 32*kb+31 of row n (one chunk) into the payload. */
+static inline void put_chunk(uint8_t* pay, int64_t N, int64_t n, int64_t kb, const uint8_t* codes) {
+  int64_t blk = kb * (N / 64) + n / 64;
+  int64_t t = (n % 64) / 16, r = n % 16;
+  for (int q = 0; q < 4; ++q) {
+    uint8_t* dst = pay + blk * 1024 + t * 256 + (q * 16 + r) * 4;
+    for (int j = 0; j < 4; ++j)
+      dst[j] = (uint8_t)((codes[q * 8 + 2 * j] & 15) | ((codes[q * 8 + 2 * j + 1] & 15) << 4));
+  }
+}
+
 /* Encode one matrix (row-major floats w[N][Kd]) into payload + scale bytes. */
 static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_t* pay, uint8_t* sc,
                           float* tensor_scale) {
+  uint8_t codes[32];
+  /* chunks are visited in the payload's own order (input block outer, row inner) */
   if (fmt == FMT_INT4_G32_BF16) {
-    for (int64_t n = 0; n < N; ++n) {
-      for (int64_t g = 0; g < Kd / 32; ++g) {
+    for (int64_t g = 0; g < Kd / 32; ++g) {
+      for (int64_t n = 0; n < N; ++n) {
         const float* wg = w + n * Kd + g * 32;
         double amax = 0.0;
         for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)wg[i]));
@@ -185,12 +177,14 @@ static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_
         if (!(s > 0.0)) { sbits = 0x3F80; s = 1.0; } /* all-zero group: codes 8 -> 0.0 */
         int64_t so = scale_block_off(N, n, g * 32) + ((n % 16) * 4 + (n % 64) / 16) * 2;
         memcpy(sc + so, &sbits, 2);
+        const double inv = 1.0 / s;
         for (int i = 0; i < 32; ++i) {
-          double qd = nearbyint((double)wg[i] / s); /* round-half-even (default FP mode) */
+          double qd = nearbyint((double)wg[i] * inv); /* round-half-even (default FP mode) */
           if (qd < -8) qd = -8;
           if (qd > 7) qd = 7;
-          put_nibble(pay, N, n, g * 32 + i, (uint8_t)((int)qd + 8));
+          codes[i] = (uint8_t)((int)qd + 8);
         }
+        put_chunk(pay, N, n, g, codes);
       }
     }
     *tensor_scale = 1.0f;
@@ -200,20 +194,25 @@ static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_
     float ts = (float)(amax / (6.0 * 448.0));
     if (!(ts > 0.0f)) ts = 1.0f;
     *tensor_scale = ts;
-    for (int64_t n = 0; n < N; ++n) {
-      for (int64_t g = 0; g < Kd / 16; ++g) {
-        const float* wg = w + n * Kd + g * 16;
-        double bmax = 0.0;
-        for (int i = 0; i < 16; ++i) bmax = fmax(bmax, fabs((double)wg[i]));
-        uint8_t sb = e4m3_encode_pos(bmax / (6.0 * (double)ts));
-        double sv = e4m3_value(sb) * (double)ts;
-        int64_t k0 = g * 16;
-        int64_t so = scale_block_off(N, n, k0) + (((k0 % 32) / 16) * 16 + (n % 16)) * 4 + (n % 64) / 16;
-        sc[so] = sb;
-        for (int i = 0; i < 16; ++i) {
-          uint8_t c = (sv > 0.0) ? e2m1_encode((double)wg[i] / sv) : 0;
-          put_nibble(pay, N, n, k0 + i, c);
+    for (int64_t g = 0; g < Kd / 32; ++g) {
+      for (int64_t n = 0; n < N; ++n) {
+        for (int h = 0; h < 2; ++h) {
+          const float* wg = w + n * Kd + g * 32 + h * 16;
+          double bmax = 0.0;
+          for (int i = 0; i < 16; ++i) bmax = fmax(bmax, fabs((double)wg[i]));
+          uint8_t sb = e4m3_encode_pos(bmax / (6.0 * (double)ts));
+          double sv = e4m3_value(sb) * (double)ts;
+          int64_t k0 = g * 32 + h * 16;
+          int64_t so = scale_block_off(N, n, k0) + (((k0 % 32) / 16) * 16 + (n % 16)) * 4 + (n % 64) / 16;
+          sc[so] = sb;
+          if (sv > 0.0) {
+            const double inv = 1.0 / sv;
+            for (int i = 0; i < 16; ++i) codes[h * 16 + i] = e2m1_encode((double)wg[i] * inv);
+          } else {
+            for (int i = 0; i < 16; ++i) codes[h * 16 + i] = 0;
+          }
         }
+        put_chunk(pay, N, n, g, codes);
       }
     }
   }
@@ -224,7 +223,6 @@ static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_
 void synth_record(uint64_t seed, int64_t E, int64_t l, int64_t e, int64_t H, int64_t I, int fmt,
                   double sigma, uint8_t* rec, float* ts3, float* scratch) {
   int64_t pay_m = H * I / 2, sc_m = H * I / 16;
-  memset(rec, 0, (size_t)synth_record_bytes(H, I));
   for (int m = 0; m < 3; ++m) {
     int64_t N = (m == 2) ? H : I, Kd = (m == 2) ? I : H;
     synth_weights_f32(seed, E, l, e, m, H, I, sigma, scratch);

@@ -143,7 +143,7 @@ def test_negative_control_transposed_block_fails():
     off, sh = F.payload_index(N, n, k)
     # swap the roles of t (row group) and q (column group) inside each block
     t, r, q, i = (n % 64) // 16, n % 16, (k % 32) // 8, k % 8
-    off_bad = (off - ((q * 16 + r) * 16 + t * 4)) + (t * 16 + r) * 16 + q * 4
+    off_bad = (off - (t * 256 + (q * 16 + r) * 4)) + q * 256 + (t * 16 + r) * 4
     codes = (rec[off_bad].astype(np.int64) >> sh) & 15
     assert not np.array_equal(codes, (rec[off].astype(np.int64) >> sh) & 15)
 
