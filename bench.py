@@ -129,27 +129,34 @@ def run_decode(eff, torch, synth, W, steps, warmup, profile_steps, threads):
     eng.set_flags(0)
     n_launch = sp["launches"][eff.T_DECODE_GATEUP]
     g_ms, d_ms = sp["kernel_ms"][eff.T_DECODE_GATEUP], sp["kernel_ms"][eff.T_DECODE_DOWN]
-    gpu_unique = sp["hits"] + sp["fetched"]               # distinct GPU experts over the pass
-    # algorithmic bytes: every GPU expert's record once, x read, y written per GPU entry (B = 1)
-    total_bytes = gpu_unique * R + n_launch * B * W.H * 2 + gpu_unique * W.H * 4
-    achieved = total_bytes / ((g_ms + d_ms) * 1e-3) / 1e9 if g_ms + d_ms > 0 else 0.0
-    per_launch = total_bytes / max(1, n_launch)
+    gpu_unique = sp["hits"] + sp["fetched"]               # distinct GPU experts over the pass (= entries, B = 1)
+    mat_bytes = W.H * W.I // 2 + W.H * W.I // 16           # one matrix: payload + scales
+    # algorithmic bytes of k_gateup: gate and up of every GPU expert once, x read, SwiGLU output written
+    gu_bytes = gpu_unique * 2 * mat_bytes + n_launch * B * W.H * 2 + gpu_unique * W.I * 4
+    # k_down: down of every GPU expert once, SwiGLU output read, y written
+    dn_bytes = gpu_unique * mat_bytes + gpu_unique * W.I * 4 + gpu_unique * W.H * 4
+    gu_gbps = gu_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else 0.0
+    dn_gbps = dn_bytes / (d_ms * 1e-3) / 1e9 if d_ms > 0 else 0.0
     src = ("k_decode.hip",)
     traffic = traffic_from_profile(src, n_launch)
     roofline = {
-        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-        "kernel": "expert_ffn_decode = k_gateup + k_down (one launch pair per layer)",
-        "algorithmic_bytes_per_launch": int(per_launch),
-        "avg_launch_us": round((g_ms + d_ms) * 1e3 / max(1, n_launch), 2),
-        "avg_gateup_us": round(g_ms * 1e3 / max(1, n_launch), 2),
-        "avg_down_us": round(d_ms * 1e3 / max(1, n_launch), 2),
+        "bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+        "kernel": "k_gateup (decode gate+up GEMV with SwiGLU, one launch per layer)",
+        "algorithmic_bytes_per_launch": int(gu_bytes / max(1, n_launch)),
+        "avg_launch_us": round(g_ms * 1e3 / max(1, n_launch), 2),
         "gpu_experts_per_launch": round(gpu_unique / max(1, n_launch), 3),
         "launches": n_launch, "source_sha": src_hash(*src),
+        "down": {"kernel": "k_down", "achieved": round(dn_gbps, 1), "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
+                 "algorithmic_bytes_per_launch": int(dn_bytes / max(1, n_launch)),
+                 "avg_launch_us": round(d_ms * 1e3 / max(1, n_launch), 2)},
     }
     kernel_tok_s = profile_steps * B / ((g_ms + d_ms) * 1e-3) if g_ms + d_ms > 0 else 0.0
     detail = {
         "per_layer_call": {k: round(st[k] / calls, 3) for k in ("hits", "fetched", "host")},
+        "host_executor_us_per_layer": round(st["host_ms"] * 1e3 / calls, 2),
+        "control_wait_us_per_layer": round(st["wait_ms"] * 1e3 / calls, 2),
+        "layers_with_host_share": round(st["host_calls"] / calls, 3),
         "bytes_fetched_per_token": int(st["bytes_fetched"] / steps),
         "kernel_only_tok_s": round(kernel_tok_s, 1),
         "profile_steps": profile_steps,

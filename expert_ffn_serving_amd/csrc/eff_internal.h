@@ -55,17 +55,29 @@ struct FetchList {
 };
 
 // Plan of one decode expert-FFN call: distinct GPU slots and their entries ----------------------
+// One distinct slot: everything a decode workgroup needs comes from one record.  Units at
+// index >= nu have count 0 (so a kernel never needs nu before its own unit).
+struct DecodeUnit {
+  int32_t slot;
+  int32_t count;
+  int32_t flat;                  // layer * E + expert held by the slot (tensor scales)
+  int32_t pad;
+  int32_t entry[kMaxTokens];     // entry p = t*K + k, ascending
+};
 struct DecodePlan {
   int32_t nu;
-  int32_t uslot[kMaxEntries];
-  int32_t ucount[kMaxEntries];
-  int32_t uentry[kMaxEntries][kMaxTokens];  // entry p = t*K + k
+  int32_t pad[3];
+  DecodeUnit unit[kMaxEntries];
 };
 
 // Device stats counters (int64) ----------------------------------------------------------------
 enum { ST_CALLS, ST_HITS, ST_FETCHED, ST_HOST, ST_SPEC_FETCHED, ST_HIST0, ST_COUNT = ST_HIST0 + 17 };
 
 // Host thread pool for the host executor --------------------------------------------------------
+// Workers spin on the job generation for a couple of milliseconds after each job (decode calls
+// come every few hundred microseconds), then sleep on a condition variable.  A task index is
+// claimed by compare-and-swap on (generation << 32 | index), so a worker that wakes late can
+// never run a task of a finished or newer job.
 class ThreadPool {
  public:
   explicit ThreadPool(int n);
@@ -76,15 +88,17 @@ class ThreadPool {
 
  private:
   void loop();
+  void run_tasks(uint64_t g, const std::function<void(int)>* fn, int n);
   std::vector<std::thread> workers_;
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<uint64_t> next_{0};
+  std::atomic<int> done_{0};
+  std::atomic<const std::function<void(int)>*> fn_{nullptr};
+  std::atomic<int> n_{0};
+  std::atomic<bool> stop_{false};
+  std::atomic<int> sleepers_{0};
   std::mutex mu_;
-  std::condition_variable cv_, done_cv_;
-  const std::function<void(int)>* fn_ = nullptr;
-  int n_ = 0;
-  std::atomic<int> next_{0};
-  int active_ = 0;
-  uint64_t gen_ = 0;
-  bool stop_ = false;
+  std::condition_variable cv_;
 };
 
 }  // namespace eff
@@ -131,8 +145,10 @@ struct eff_engine {
   float* d_ygpu = nullptr;        // [maxB*K*H]
   float* d_yhost = nullptr;       // [maxB*K*H]
   // pinned host staging
-  uint16_t* h_x = nullptr;        // [maxB*H]
-  int32_t* h_cpu = nullptr;       // [maxB*K]
+  uint16_t* h_x = nullptr;        // [maxB*H] host-mapped
+  int32_t* h_cpu = nullptr;       // [maxB*K] host-mapped
+  uint16_t* h_x_dev = nullptr;    // device views of the two above
+  int32_t* h_cpu_dev = nullptr;
   float* h_yhost = nullptr;       // [maxB*K*H]
 
   // prefill scratch
@@ -154,8 +170,11 @@ struct eff_engine {
   int32_t* h_pf_ids = nullptr;      // pinned [T*K]
   int32_t* h_pf_meta = nullptr;     // pinned [2E]
   eff::ThreadPool* pool_threads = nullptr;
-  // kernel timing (EFF_CFG_TIMING): event triples (before, middle, after) per call
-  struct TimedCall { int kind; hipEvent_t ev[3]; };
+  // kernel timing (EFF_CFG_TIMING): events (start, end) of each of two kernels per call
+  struct TimedCall { int kind; hipEvent_t ev[4]; };
+  double host_ms = 0.0;           // wall time in the host executor
+  double wait_ms = 0.0;           // wall time waiting for the device in the decode path
+  int64_t host_calls = 0;
   std::vector<TimedCall> timed;     // recorded, not yet resolved
   std::vector<hipEvent_t> free_events;
   int64_t t_launches[4] = {0, 0, 0, 0};
@@ -177,7 +196,10 @@ hipError_t launch_prefill_install(eff_engine* e, int layer, hipStream_t s);
 hipError_t launch_fallback_install(eff_engine* e, int layer, const int32_t* experts, int n,
                                    hipStream_t s);
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
-                             float* y, hipStream_t s);
+                             float* y, hipStream_t s, bool plan_ready = false);
+hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s);
+hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
+                          const int32_t* spec_ids, hipStream_t s);
 // timing hooks: returns the call's event slot (or -1 when timing is off); mark(i) records event i
 int timing_begin(eff_engine* e, int kind, hipStream_t s);
 void timing_mark(eff_engine* e, int slot, int i, hipStream_t s);

@@ -1,6 +1,7 @@
 // libeff host side: engine lifecycle, the C ABI entry points, the eager decode-layer
 // orchestration and prefill streaming.
 #include <algorithm>
+#include <chrono>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -97,6 +98,7 @@ static int alloc_all(eff_engine* e) {
   // decode scratch
   e->maxU = (int)std::min<int64_t>(B * K, E);
   EFF_HIP_TRY(dalloc(&e->d_plan, 1));
+  EFF_HIP_TRY(hipMemset(e->d_plan, 0, sizeof(eff::DecodePlan)));  // every unit starts empty
   EFF_HIP_TRY(dalloc(&e->d_a, (size_t)e->maxU * B * I));
   // orchestrator
   EFF_HIP_TRY(dalloc(&e->d_ids, B * K));
@@ -109,8 +111,10 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(dalloc(&e->d_logits, std::max(B, T) * E));
   EFF_HIP_TRY(dalloc(&e->d_ygpu, B * K * H));
   EFF_HIP_TRY(dalloc(&e->d_yhost, B * K * H));
-  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_x, (size_t)(B * H) * 2, 0));
-  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_cpu, (size_t)(B * K) * 4, 0));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_x, (size_t)(B * H) * 2, hipHostMallocMapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_cpu, (size_t)(B * K) * 4, hipHostMallocMapped));
+  EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_x_dev, e->h_x, 0));
+  EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_cpu_dev, e->h_cpu, 0));
   EFF_HIP_TRY(hipHostMalloc((void**)&e->h_yhost, (size_t)(B * K * H) * 4, 0));
   // prefill
   if (T > 0) {
@@ -160,10 +164,10 @@ static hipEvent_t take_event(eff_engine* e) {
 // Adds the durations of every recorded call (waits for them) and recycles the events.
 static void resolve_timing(eff_engine* e) {
   for (auto& tc : e->timed) {
-    bool ok = tc.ev[0] && tc.ev[1] && tc.ev[2] && hipEventSynchronize(tc.ev[2]) == hipSuccess;
+    bool ok = tc.ev[0] && tc.ev[1] && tc.ev[2] && tc.ev[3] && hipEventSynchronize(tc.ev[3]) == hipSuccess;
     float a = 0.f, b = 0.f;
     if (ok && hipEventElapsedTime(&a, tc.ev[0], tc.ev[1]) == hipSuccess &&
-        hipEventElapsedTime(&b, tc.ev[1], tc.ev[2]) == hipSuccess) {
+        hipEventElapsedTime(&b, tc.ev[2], tc.ev[3]) == hipSuccess) {
       e->t_ms[tc.kind] += a;
       e->t_ms[tc.kind + 1] += b;
       e->t_launches[tc.kind] += 1;
@@ -180,7 +184,7 @@ int timing_begin(eff_engine* e, int kind, hipStream_t s) {
   if (e->timed.size() >= 4096) resolve_timing(e);  // bounded number of live events
   eff_engine::TimedCall tc;
   tc.kind = kind;
-  for (int i = 0; i < 3; ++i) tc.ev[i] = take_event(e);
+  for (int i = 0; i < 4; ++i) tc.ev[i] = take_event(e);
   e->timed.push_back(tc);
   const int slot = (int)e->timed.size() - 1;
   timing_mark(e, slot, 0, s);
@@ -362,11 +366,10 @@ static int issue_copies(eff_engine* e, int which, hipStream_t side) {
   return EFF_OK;
 }
 
-int eff_copy_missing(eff_engine* e, eff_stream_t compute, eff_stream_t side) {
-  if (int rc = check_engine(e)) return rc;
-  hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
-  if (capturing(cs) || capturing(ss)) return fail(EFF_ECAPTURE, "eff_copy_missing waits on the host");
-  EFF_HIP_TRY(hipStreamSynchronize(cs));
+// Issues the pending fetches (real, then speculative) on `side` and makes `compute` wait for
+// every copy issued so far (the side stream is in order, so this also covers speculative copies
+// issued one layer earlier that this layer now hits).  The host must have waited for the split.
+static int issue_pending_copies(eff_engine* e, hipStream_t cs, hipStream_t ss) {
   if (int rc = read_device_error(e)) return rc;
   if (e->real_split_pending) {
     if (int rc = issue_copies(e, 0, ss)) return rc;
@@ -376,11 +379,21 @@ int eff_copy_missing(eff_engine* e, eff_stream_t compute, eff_stream_t side) {
     if (int rc = issue_copies(e, 1, ss)) return rc;
     e->spec_split_pending = false;
   }
-  // compute waits for every copy issued so far (the side stream is in order, so this also
-  // covers speculative copies issued one layer earlier that this layer now hits)
   EFF_HIP_TRY(hipEventRecord(e->ev_copy, ss));
   EFF_HIP_TRY(hipStreamWaitEvent(cs, e->ev_copy, 0));
   return EFF_OK;
+}
+
+static double now_ms() {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+int eff_copy_missing(eff_engine* e, eff_stream_t compute, eff_stream_t side) {
+  if (int rc = check_engine(e)) return rc;
+  hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
+  if (capturing(cs) || capturing(ss)) return fail(EFF_ECAPTURE, "eff_copy_missing waits on the host");
+  EFF_HIP_TRY(hipStreamSynchronize(cs));
+  return issue_pending_copies(e, cs, ss);
 }
 
 int eff_expert_ffn_decode(eff_engine* e, int layer, const void* x, const int32_t* slots, int B, float* y,
@@ -418,34 +431,34 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   const eff_config& c = e->cfg;
   if (!x || !out || (!w_router && !logits) || B < 1 || B > c.max_tokens || layer < 0 || layer >= c.num_layers)
     return fail(EFF_EINVAL, "eff_decode_layer: bad arguments");
+  if (e->pending_host) return fail(EFF_ESTATE, "an ensure is pending its split");
   hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
   if (capturing(cs) || capturing(ss)) return fail(EFF_ECAPTURE, "eff_decode_layer waits on the host");
   const int K = c.top_k, n = B * K;
+  const float* lg = logits;
   if (w_router) {
     EFF_HIP_TRY(launch_route_logits((const uint16_t*)x, (const uint16_t*)w_router, B, c.num_experts, c.hidden,
                                     e->d_logits, cs));
-    EFF_HIP_TRY(launch_topk(e->d_logits, B, c.num_experts, K, e->d_ids, e->d_w, cs));
-  } else {
-    EFF_HIP_TRY(launch_topk(logits, B, c.num_experts, K, e->d_ids, e->d_w, cs));
+    lg = e->d_logits;
   }
-  EFF_HIP_TRY(hipMemcpyAsync(e->d_slots, e->d_ids, (size_t)n * 4, hipMemcpyDeviceToDevice, cs));
-  if (int rc = eff_ensure_experts(e, layer, e->d_slots, n, 0, compute)) return rc;
-  if (int rc = eff_split_misses(e, e->d_slots, e->d_cpu, e->d_counts, compute)) return rc;
+  // top-K, ensure, split, the speculative request and the decode plan in one workgroup; the
+  // fetch list, host ids and x land in host-mapped memory
   const bool spec = spec_ids && layer + 1 < c.num_layers;
-  if (spec) {
-    EFF_HIP_TRY(hipMemcpyAsync(e->d_spec_ids, spec_ids, (size_t)n * 4, hipMemcpyDeviceToDevice, cs));
-    if (int rc = eff_ensure_experts(e, layer + 1, e->d_spec_ids, n, EFF_SPECULATIVE, compute)) return rc;
-    if (int rc = eff_split_misses(e, e->d_spec_ids, e->d_spec_cpu, e->d_counts + 3, compute)) return rc;
-  }
-  // host ids and x for the host share come back with the same wait
-  EFF_HIP_TRY(hipMemcpyAsync(e->h_cpu, e->d_cpu, (size_t)n * 4, hipMemcpyDeviceToHost, cs));
-  EFF_HIP_TRY(hipMemcpyAsync(e->h_x, x, (size_t)B * c.hidden * 2, hipMemcpyDeviceToHost, cs));
-  if (int rc = eff_copy_missing(e, compute, side)) return rc;  // waits once on the host
-  EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs));
+  EFF_HIP_TRY(launch_control(e, layer, lg, B, (const uint16_t*)x, spec ? spec_ids : nullptr, cs));
+  e->real_split_pending = true;
+  if (spec) e->spec_split_pending = true;
+  const double t0 = now_ms();
+  EFF_HIP_TRY(hipStreamSynchronize(cs));  // the one wait of the layer
+  e->wait_ms += now_ms() - t0;
+  if (int rc = issue_pending_copies(e, cs, ss)) return rc;
+  EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true));
   bool any_host = false;
   for (int p = 0; p < n; ++p) any_host |= e->h_cpu[p] >= 0;
   if (any_host) {
+    const double t1 = now_ms();
     host_ffn(e, layer, e->h_x, e->h_cpu, B, e->h_yhost);  // overlaps the GPU expert kernels
+    e->host_ms += now_ms() - t1;
+    e->host_calls += 1;
     EFF_HIP_TRY(hipMemcpyAsync(e->d_yhost, e->h_yhost, (size_t)n * c.hidden * 4, hipMemcpyHostToDevice, cs));
   }
   EFF_HIP_TRY(launch_combine(e->d_ygpu, e->d_yhost, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs));
@@ -571,6 +584,9 @@ int eff_get_stats(eff_engine* e, eff_stats* out) {
     out->launches[i] = e->t_launches[i];
     out->kernel_ms[i] = e->t_ms[i];
   }
+  out->host_ms = e->host_ms;
+  out->wait_ms = e->wait_ms;
+  out->host_calls = e->host_calls;
   return EFF_OK;
 }
 
@@ -591,6 +607,8 @@ int eff_reset_stats(eff_engine* e) {
   }
   e->host_bytes_fetched = 0;
   e->host_spec_fetched = 0;
+  e->host_ms = e->wait_ms = 0.0;
+  e->host_calls = 0;
   EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
   return EFF_OK;
 }

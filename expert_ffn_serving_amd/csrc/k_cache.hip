@@ -25,30 +25,56 @@ __device__ __host__ inline int64_t qstar_dev(int64_t m, int64_t f) {
   return best < m ? best : m;
 }
 
-__global__ void __launch_bounds__(kThreads)
-k_ensure(int layer, int E, int32_t* __restrict__ ids, int n, int spec, const int32_t* __restrict__ table,
-         int64_t* __restrict__ usage, int64_t* __restrict__ clock, Pending* __restrict__ pd,
-         int32_t* __restrict__ err) {
-  __shared__ int32_t s_id[kMaxEntries];
-  __shared__ int32_t s_slot[kMaxEntries];
-  __shared__ int32_t s_first[kMaxEntries];
+struct CacheState {
+  int E, S;
+  uint32_t f;
+  int32_t* table;
+  int32_t* owner;
+  int64_t* usage;
+  int64_t* recency;
+  int64_t* clock;
+  Pending* pd;
+  FetchList* fl_dev;
+  FetchList* fl_host;  // host-mapped mirror (device view)
+  int64_t* stats;
+  int32_t* err;
+  int sort_pow2;
+};
+
+// LDS the control bodies need besides the dynamic key buffer.
+struct SplitLds {
+  int32_t ranked[kMaxEntries];
+  int32_t victim[kMaxEntries];
+  int32_t mid[kMaxEntries];
+  int64_t mrec[kMaxEntries];
+  uint64_t red[kThreads / 64];
+  int nv;
+};
+
+// ensure: dedup, residency, hits stamped at this step, ids rewritten to slot-or--1, call kept
+// pending.  scratch: 3 * kMaxEntries int32 of LDS (free outside this body).
+__device__ void ensure_body(const CacheState& c, int layer, int32_t* __restrict__ ids, int n, int spec,
+                            int32_t* scratch) {
+  int32_t* s_id = scratch;
+  int32_t* s_slot = scratch + kMaxEntries;
+  int32_t* s_first = scratch + 2 * kMaxEntries;
   __shared__ int64_t s_step, s_floor;
   __shared__ int s_nu, s_nm;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, E = c.E;
   if (tid == 0) {
-    s_step = clock[0] + 1;
-    s_floor = spec ? clock[1] : s_step;
+    s_step = c.clock[0] + 1;
+    s_floor = spec ? c.clock[1] : s_step;
     s_nu = 0;
     s_nm = 0;
   }
   for (int p = tid; p < n; p += kThreads) {
     int v = ids[p];
     if (v < 0 || v >= E) {
-      atomicOr(err, 1);
+      atomicOr(c.err, 1);
       v = -1;
     }
     s_id[p] = v;
-    s_slot[p] = (v >= 0) ? table[(int64_t)layer * E + v] : -1;
+    s_slot[p] = (v >= 0) ? c.table[(int64_t)layer * E + v] : -1;
   }
   __syncthreads();
   for (int p = tid; p < n; p += kThreads) {
@@ -68,31 +94,32 @@ k_ensure(int layer, int E, int32_t* __restrict__ ids, int n, int spec, const int
       ru += (o < id);
       rm += (o < id) && (s_slot[q] < 0);
     }
-    pd->uniq[ru] = id;
+    c.pd->uniq[ru] = id;
     if (miss) {
-      pd->miss[rm] = id;
+      c.pd->miss[rm] = id;
       atomicAdd(&s_nm, 1);
     } else {
-      usage[s_slot[p]] = s;  // hit: stamped as used now
+      c.usage[s_slot[p]] = s;  // hit: stamped as used now
     }
     atomicAdd(&s_nu, 1);
   }
   for (int p = tid; p < n; p += kThreads) {
-    pd->ids[p] = s_id[p];
+    c.pd->ids[p] = s_id[p];
     ids[p] = s_slot[p];
   }
   __syncthreads();
   if (tid == 0) {
-    clock[0] = s;
-    pd->valid = 1;
-    pd->layer = layer;
-    pd->n = n;
-    pd->spec = spec;
-    pd->s = s;
-    pd->floor_ = s_floor;
-    pd->nuniq = s_nu;
-    pd->nmiss = s_nm;
+    c.clock[0] = s;
+    c.pd->valid = 1;
+    c.pd->layer = layer;
+    c.pd->n = n;
+    c.pd->spec = spec;
+    c.pd->s = s;
+    c.pd->floor_ = s_floor;
+    c.pd->nuniq = s_nu;
+    c.pd->nmiss = s_nm;
   }
+  __syncthreads();
 }
 
 // Block-wide min of a 64-bit key; every thread gets the result.
@@ -110,109 +137,105 @@ __device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* s_red) {
   return r;
 }
 
-__global__ void __launch_bounds__(kThreads)
-k_split(int E, int S, uint32_t f, int32_t* __restrict__ ids_out, int32_t* __restrict__ cpu_out,
-        int32_t* __restrict__ counts, int32_t* __restrict__ table, int32_t* __restrict__ owner,
-        int64_t* __restrict__ usage, int64_t* __restrict__ recency, int64_t* __restrict__ clock,
-        Pending* __restrict__ pd, FetchList* __restrict__ fl_dev, FetchList* __restrict__ fl_host,
-        int64_t* __restrict__ stats, int32_t* __restrict__ err, int sort_pow2) {
-  extern __shared__ uint64_t s_key[];  // [sort_pow2] victim keys (usage+1) << 14 | slot
-  __shared__ int32_t s_ranked[kMaxEntries];
-  __shared__ int32_t s_victim[kMaxEntries];
-  __shared__ int32_t s_mid[kMaxEntries];
-  __shared__ int64_t s_mrec[kMaxEntries];
-  __shared__ uint64_t s_red[kThreads / 64];
-  __shared__ int s_nv;
+// split: q*, recency ranking, LRU victims, installs, the -1 partition, recency and counts.
+// cpu_host (may be null): a host-mapped copy of cpu_ids.  s_key: sort_pow2 uint64 of LDS.
+__device__ void split_body(const CacheState& c, int32_t* __restrict__ ids_out, int32_t* __restrict__ cpu_out,
+                           int32_t* __restrict__ cpu_host, int32_t* __restrict__ counts, SplitLds& L,
+                           uint64_t* s_key) {
   const int tid = threadIdx.x;
+  Pending* pd = c.pd;
   if (!pd->valid) {
-    if (tid == 0) atomicOr(err, 2);
+    if (tid == 0) atomicOr(c.err, 2);
     return;
   }
+  const int E = c.E, S = c.S;
   const int layer = pd->layer, n = pd->n, spec = pd->spec, m = pd->nmiss, nu = pd->nuniq;
   const int64_t s = pd->s, floor_ = pd->floor_;
   const int64_t base = (int64_t)layer * E;
-  const int q = (int)qstar_dev(m, f);
+  const int q = (int)qstar_dev(m, c.f);
 
-  // Misses ranked by (recency desc, id asc) ([FT-deep] §4 ⑤: prefer recently active experts).
-  for (int i = tid; i < m; i += kThreads) {
-    int e = pd->miss[i];
-    s_mid[i] = e;
-    s_mrec[i] = recency[base + e];
-  }
-  __syncthreads();
-  for (int i = tid; i < m; i += kThreads) {
-    int e = s_mid[i];
-    int64_t r = s_mrec[i];
-    int rank = 0;
-    for (int j = 0; j < m; ++j) {
-      int o = s_mid[j];
-      int64_t ro = s_mrec[j];
-      rank += (ro > r) || (ro == r && o < e);
+  int qq = 0;
+  if (q > 0) {
+    // Misses ranked by (recency desc, id asc) ([FT-deep] §4 ⑤: prefer recently active experts).
+    for (int i = tid; i < m; i += kThreads) {
+      int e = pd->miss[i];
+      L.mid[i] = e;
+      L.mrec[i] = c.recency[base + e];
     }
-    s_ranked[rank] = e;
-  }
-  // Victim keys: slots with usage below the floor, ordered by (usage, slot).
-  if (tid == 0) s_nv = 0;
-  __syncthreads();
-  int local_nv = 0;
-  for (int v = tid; v < sort_pow2; v += kThreads) {
-    uint64_t key = kInfKey;
-    if (v < S) {
-      int64_t u = usage[v];
-      if (u < floor_) {
-        key = ((uint64_t)(u + 1) << 14) | (uint64_t)v;
-        ++local_nv;
+    if (tid == 0) L.nv = 0;
+    __syncthreads();
+    for (int i = tid; i < m; i += kThreads) {
+      int e = L.mid[i];
+      int64_t r = L.mrec[i];
+      int rank = 0;
+      for (int j = 0; j < m; ++j) {
+        int o = L.mid[j];
+        int64_t ro = L.mrec[j];
+        rank += (ro > r) || (ro == r && o < e);
       }
+      L.ranked[rank] = e;
     }
-    s_key[v] = key;
-  }
-  if (local_nv) atomicAdd(&s_nv, local_nv);
-  __syncthreads();
-  const int qq = min(q, s_nv);
-  if (qq > 0 && qq <= 16) {
-    // few fetches: qq rounds of block-wide argmin
-    for (int i = 0; i < qq; ++i) {
-      uint64_t lm = kInfKey;
-      for (int v = tid; v < S; v += kThreads) lm = s_key[v] < lm ? s_key[v] : lm;
-      uint64_t g = block_min_u64(lm, s_red);
-      int v = (int)(g & 0x3FFF);
-      if (tid == 0) {
-        s_victim[i] = v;
-        s_key[v] = kInfKey;
+    // Victim keys: slots with usage below the floor, ordered by (usage, slot).
+    int local_nv = 0;
+    for (int v = tid; v < c.sort_pow2; v += kThreads) {
+      uint64_t key = kInfKey;
+      if (v < S) {
+        int64_t u = c.usage[v];
+        if (u < floor_) {
+          key = ((uint64_t)(u + 1) << 14) | (uint64_t)v;
+          ++local_nv;
+        }
       }
-      __syncthreads();
+      s_key[v] = key;
     }
-  } else if (qq > 16) {
-    // many fetches: bitonic sort of all keys (ascending)
-    for (int k = 2; k <= sort_pow2; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < sort_pow2; i += kThreads) {
-          int ixj = i ^ j;
-          if (ixj > i) {
-            uint64_t a = s_key[i], b = s_key[ixj];
-            bool up = (i & k) == 0;
-            if ((a > b) == up) {
-              s_key[i] = b;
-              s_key[ixj] = a;
-            }
-          }
+    if (local_nv) atomicAdd(&L.nv, local_nv);
+    __syncthreads();
+    qq = min(q, L.nv);
+    if (qq > 0 && qq <= 16) {
+      // few fetches: qq rounds of block-wide argmin
+      for (int i = 0; i < qq; ++i) {
+        uint64_t lm = kInfKey;
+        for (int v = tid; v < S; v += kThreads) lm = s_key[v] < lm ? s_key[v] : lm;
+        uint64_t g = block_min_u64(lm, L.red);
+        int v = (int)(g & 0x3FFF);
+        if (tid == 0) {
+          L.victim[i] = v;
+          s_key[v] = kInfKey;
         }
         __syncthreads();
       }
+    } else if (qq > 16) {
+      // many fetches: bitonic sort of all keys (ascending)
+      for (int k = 2; k <= c.sort_pow2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          for (int i = tid; i < c.sort_pow2; i += kThreads) {
+            int ixj = i ^ j;
+            if (ixj > i) {
+              uint64_t a = s_key[i], b = s_key[ixj];
+              bool up = (i & k) == 0;
+              if ((a > b) == up) {
+                s_key[i] = b;
+                s_key[ixj] = a;
+              }
+            }
+          }
+          __syncthreads();
+        }
+      }
+      for (int i = tid; i < qq; i += kThreads) L.victim[i] = (int)(s_key[i] & 0x3FFF);
+      __syncthreads();
     }
-    for (int i = tid; i < qq; i += kThreads) s_victim[i] = (int)(s_key[i] & 0x3FFF);
-    __syncthreads();
   }
   // Installs: i-th ranked miss -> i-th oldest victim.
-  FetchList* fl = fl_dev + (spec ? 1 : 0);
-  FetchList* flh = fl_host + (spec ? 1 : 0);
+  FetchList* fl = c.fl_dev + (spec ? 1 : 0);
+  FetchList* flh = c.fl_host + (spec ? 1 : 0);
   for (int i = tid; i < qq; i += kThreads) {
-    int v = s_victim[i], e = s_ranked[i];
-    int old = owner[v];
-    if (old >= 0) table[old] = -1;
-    owner[v] = (int32_t)(base + e);
-    table[base + e] = v;
-    usage[v] = s;
+    int v = L.victim[i], e = L.ranked[i];
+    int old = c.owner[v];
+    if (old >= 0) c.table[old] = -1;
+    c.owner[v] = (int32_t)(base + e);
+    c.table[base + e] = v;
+    c.usage[v] = s;
     fl->flat[i] = (int32_t)(base + e);
     fl->slot[i] = v;
     flh->flat[i] = (int32_t)(base + e);
@@ -222,15 +245,17 @@ k_split(int E, int S, uint32_t f, int32_t* __restrict__ ids_out, int32_t* __rest
   // The -1 partition ([FT-deep] §4 ③): GPU owns entries with a slot, the host the rest.
   for (int p = tid; p < n; p += kThreads) {
     int id = pd->ids[p];
-    int slot = (id >= 0) ? table[base + id] : -1;
+    int slot = (id >= 0) ? c.table[base + id] : -1;
     ids_out[p] = slot;
-    if (cpu_out) cpu_out[p] = (!spec && slot < 0 && id >= 0) ? id : -1;
+    const int cpu = (!spec && slot < 0 && id >= 0) ? id : -1;
+    if (cpu_out) cpu_out[p] = cpu;
+    if (cpu_host) cpu_host[p] = cpu;
   }
   if (!spec)
-    for (int u = tid; u < nu; u += kThreads) recency[base + pd->uniq[u]] = s;
+    for (int u = tid; u < nu; u += kThreads) c.recency[base + pd->uniq[u]] = s;
   __syncthreads();
   if (tid == 0) {
-    if (!spec) clock[1] = s;
+    if (!spec) c.clock[1] = s;
     if (counts) {
       counts[0] = m;
       counts[1] = qq;
@@ -238,20 +263,167 @@ k_split(int E, int S, uint32_t f, int32_t* __restrict__ ids_out, int32_t* __rest
     }
     fl->count = qq;
     flh->count = qq;
-    fl->err = *err;
-    flh->err = *err;
-    *err = 0;
+    fl->err = *c.err;
+    flh->err = *c.err;
+    *c.err = 0;
     pd->valid = 0;
-    stats[ST_CALLS] += 1;
+    c.stats[ST_CALLS] += 1;
     if (spec) {
-      stats[ST_SPEC_FETCHED] += qq;
+      c.stats[ST_SPEC_FETCHED] += qq;
     } else {
-      stats[ST_HITS] += nu - m;
-      stats[ST_FETCHED] += qq;
-      stats[ST_HOST] += m - qq;
-      stats[ST_HIST0 + (qq < 16 ? qq : 16)] += 1;
+      c.stats[ST_HITS] += nu - m;
+      c.stats[ST_FETCHED] += qq;
+      c.stats[ST_HOST] += m - qq;
+      c.stats[ST_HIST0 + (qq < 16 ? qq : 16)] += 1;
     }
   }
+  __syncthreads();
+}
+
+__device__ inline bool better(float a, int ia, float b, int ib) { return a > b || (a == b && ia < ib); }
+
+// top-K of one logits row by (logit desc, id asc) and the softmax of the K selected, by one wave.
+// sel: kMaxTopK floats of LDS for this wave.
+__device__ void wave_topk(const float* __restrict__ row, int E, int K, int32_t* __restrict__ ids,
+                          float* __restrict__ w, float* sel) {
+  const int lane = threadIdx.x & 63;
+  uint64_t taken = 0;  // element lane + 64*j is taken when bit j is set
+  for (int k = 0; k < K; ++k) {
+    float bv = 0.f;
+    int bi = 0x7FFFFFFF;
+    int j = 0;
+    for (int e = lane; e < E; e += 64, ++j) {
+      if ((taken >> j) & 1) continue;
+      const float v = row[e];
+      if (bi == 0x7FFFFFFF || better(v, e, bv, bi)) {
+        bv = v;
+        bi = e;
+      }
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
+    if (lane == 0) {
+      sel[k] = bv;
+      ids[k] = bi;
+    }
+  }
+  if (lane == 0) {
+    // softmax over the K selected logits, relative to the largest
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += expf(sel[k] - sel[0]);
+    for (int k = 0; k < K; ++k) w[k] = expf(sel[k] - sel[0]) / sum;
+  }
+}
+
+// decode plan (distinct GPU slots and their entries), by one workgroup; scratch: 2*kMaxEntries.
+__device__ void plan_body(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB,
+                          const int32_t* __restrict__ owner, DecodePlan* plan, int32_t* scratch) {
+  int32_t* s_sl = scratch;
+  int32_t* s_first = scratch + kMaxEntries;
+  __shared__ int s_nu;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_nu = 0;
+  for (int p = tid; p < n; p += blockDim.x) {
+    const int v = slots[p];
+    s_sl[p] = (v >= 0 && v < S) ? v : -1;  // slots outside the arena are never read
+  }
+  __syncthreads();
+  for (int p = tid; p < n; p += blockDim.x) {
+    int v = s_sl[p], first = v >= 0;
+    for (int q = 0; q < p && first; ++q) first = s_sl[q] != v;
+    s_first[p] = first;
+  }
+  __syncthreads();
+  for (int p = tid; p < n; p += blockDim.x) {
+    if (!s_first[p]) continue;
+    int v = s_sl[p], rank = 0, cnt = 0;
+    for (int q = 0; q < n; ++q) rank += s_first[q] && s_sl[q] < v;
+    if (rank >= maxU) continue;  // more distinct slots than a layer has experts: not computed
+    DecodeUnit& un = plan->unit[rank];
+    for (int q = 0; q < n && cnt < maxB; ++q)  // a slot appears at most once per token
+      if (s_sl[q] == v) un.entry[cnt++] = q;
+    un.slot = v;
+    un.count = cnt;
+    un.flat = owner[v];
+    atomicAdd(&s_nu, 1);
+  }
+  __syncthreads();
+  const int nu = min(s_nu, maxU);
+  for (int u = nu + tid; u < maxU; u += blockDim.x) {
+    plan->unit[u].count = 0;
+    plan->unit[u].slot = 0;
+    plan->unit[u].flat = 0;
+  }
+  if (tid == 0) plan->nu = nu;
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_ensure(CacheState c, int layer, int32_t* __restrict__ ids, int n, int spec) {
+  __shared__ int32_t scratch[3 * kMaxEntries];
+  ensure_body(c, layer, ids, n, spec, scratch);
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_split(CacheState c, int32_t* __restrict__ ids_out, int32_t* __restrict__ cpu_out, int32_t* __restrict__ counts) {
+  extern __shared__ uint64_t s_key[];
+  __shared__ SplitLds L;
+  split_body(c, ids_out, cpu_out, nullptr, counts, L, s_key);
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_topk(const float* __restrict__ logits, int B, int E, int K, int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ float s_sel[kThreads / 64][kMaxTopK];
+  const int wave = threadIdx.x >> 6;
+  for (int t = blockIdx.x * (kThreads / 64) + wave; t < B; t += gridDim.x * (kThreads / 64))
+    wave_topk(logits + (int64_t)t * E, E, K, ids + (int64_t)t * K, w + (int64_t)t * K, s_sel[wave]);
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, const int32_t* __restrict__ owner,
+       DecodePlan* plan) {
+  __shared__ int32_t scratch[2 * kMaxEntries];
+  plan_body(slots, n, S, maxU, maxB, owner, plan, scratch);
+}
+
+// One decode layer's control path in one workgroup: top-K of the B logits rows, ensure, split,
+// (speculative ensure + split of the next layer), the decode plan, and the host's inputs
+// (host ids and x) written to host-mapped memory.
+__global__ void __launch_bounds__(kThreads)
+k_control(CacheState c, const float* __restrict__ logits, int B, int K, int layer, int32_t* __restrict__ ids,
+          float* __restrict__ w, int32_t* __restrict__ slots, int32_t* __restrict__ cpu, int32_t* __restrict__ counts,
+          const int32_t* __restrict__ spec_ids, int32_t* __restrict__ spec_slots, int32_t* __restrict__ cpu_host,
+          const uint16_t* __restrict__ x, uint16_t* __restrict__ x_host, int H, int maxU, int maxB,
+          DecodePlan* plan) {
+  extern __shared__ uint64_t s_key[];  // victim keys; also scratch for ensure and plan
+  __shared__ SplitLds L;
+  __shared__ float s_sel[kThreads / 64][kMaxTopK];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int n = B * K;
+  for (int t = wave; t < B; t += kThreads / 64)
+    wave_topk(logits + (int64_t)t * c.E, c.E, K, ids + (int64_t)t * K, w + (int64_t)t * K, s_sel[wave]);
+  __syncthreads();
+  for (int p = tid; p < n; p += kThreads) slots[p] = ids[p];
+  // the host's copy of x travels while the control path runs (16 bytes per thread)
+  for (int i = tid; i < B * H / 8; i += kThreads)
+    reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
+  __syncthreads();
+  ensure_body(c, layer, slots, n, 0, reinterpret_cast<int32_t*>(s_key));
+  split_body(c, slots, cpu, cpu_host, counts, L, s_key);
+  if (spec_ids) {
+    for (int p = tid; p < n; p += kThreads) spec_slots[p] = spec_ids[p];
+    __syncthreads();
+    ensure_body(c, layer + 1, spec_slots, n, 1, reinterpret_cast<int32_t*>(s_key));
+    split_body(c, spec_slots, nullptr, nullptr, counts + 3, L, s_key);
+  }
+  plan_body(slots, n, c.S, maxU, maxB, c.owner, plan, reinterpret_cast<int32_t*>(s_key));
 }
 
 __global__ void k_qstar_batch(const int32_t* __restrict__ m, const uint32_t* __restrict__ f,
@@ -326,33 +498,80 @@ k_install(int layer, int E, int mode, const int32_t* __restrict__ experts, int n
 
 }  // namespace
 
-hipError_t launch_ensure(eff_engine* e, int layer, int32_t* ids, int n, int spec, hipStream_t s) {
-  hipLaunchKernelGGL(k_ensure, dim3(1), dim3(kThreads), 0, s, layer, e->cfg.num_experts, ids, n, spec,
-                     e->d_table, e->d_usage, e->d_clock, e->d_pending, e->d_err);
-  return hipGetLastError();
-}
-
 static int sort_pow2_of(int S) {
   int p = 1024;
   while (p < S) p <<= 1;
   return p;
 }
 
+static CacheState state_of(eff_engine* e) {
+  CacheState c;
+  c.E = e->cfg.num_experts;
+  c.S = e->cfg.num_slots;
+  c.f = e->cfg.fetch_frac_q16;
+  c.table = e->d_table;
+  c.owner = e->d_owner;
+  c.usage = e->d_usage;
+  c.recency = e->d_recency;
+  c.clock = e->d_clock;
+  c.pd = e->d_pending;
+  c.fl_dev = e->d_fetch;
+  c.fl_host = e->h_fetch_dev;
+  c.stats = e->d_stats;
+  c.err = e->d_err;
+  c.sort_pow2 = sort_pow2_of(c.S);
+  return c;
+}
+
+static size_t control_lds(int S) {
+  const size_t keys = (size_t)sort_pow2_of(S) * sizeof(uint64_t);
+  const size_t scratch = (size_t)3 * kMaxEntries * sizeof(int32_t);
+  return keys > scratch ? keys : scratch;
+}
+
+hipError_t launch_ensure(eff_engine* e, int layer, int32_t* ids, int n, int spec, hipStream_t s) {
+  hipLaunchKernelGGL(k_ensure, dim3(1), dim3(kThreads), 0, s, state_of(e), layer, ids, n, spec);
+  return hipGetLastError();
+}
+
 hipError_t launch_split(eff_engine* e, int32_t* ids, int32_t* cpu_ids, int32_t* counts, int which,
                         hipStream_t s) {
   (void)which;
-  int P = sort_pow2_of(e->cfg.num_slots);
-  hipLaunchKernelGGL(k_split, dim3(1), dim3(kThreads), (size_t)P * sizeof(uint64_t), s,
-                     e->cfg.num_experts, e->cfg.num_slots, e->cfg.fetch_frac_q16, ids, cpu_ids, counts,
-                     e->d_table, e->d_owner, e->d_usage, e->d_recency, e->d_clock, e->d_pending,
-                     e->d_fetch, e->h_fetch_dev, e->d_stats, e->d_err, P);
+  const CacheState c = state_of(e);
+  hipLaunchKernelGGL(k_split, dim3(1), dim3(kThreads), (size_t)c.sort_pow2 * sizeof(uint64_t), s, c, ids, cpu_ids,
+                     counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int B, int E, int K, int32_t* ids, float* w, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  const int per = kThreads / 64;
+  hipLaunchKernelGGL(k_topk, dim3((B + per - 1) / per), dim3(kThreads), 0, s, logits, B, E, K, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kThreads), 0, s, slots, n, e->cfg.num_slots, e->maxU,
+                     e->cfg.max_tokens, e->d_owner, e->d_plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
+                          const int32_t* spec_ids, hipStream_t s) {
+  const eff_config& cf = e->cfg;
+  hipLaunchKernelGGL(k_control, dim3(1), dim3(kThreads), control_lds(cf.num_slots), s, state_of(e), logits, B,
+                     cf.top_k, layer, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, spec_ids,
+                     e->d_spec_ids, e->h_cpu_dev, x, e->h_x_dev, cf.hidden, e->maxU, cf.max_tokens, e->d_plan);
   return hipGetLastError();
 }
 
 hipError_t split_kernel_setup(int S) {
-  int P = sort_pow2_of(S);
-  return hipFuncSetAttribute((const void*)k_split, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)(P * sizeof(uint64_t)));
+  const int P = sort_pow2_of(S);
+  hipError_t err = hipFuncSetAttribute((const void*)k_split, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(P * sizeof(uint64_t)));
+  if (err != hipSuccess) return err;
+  return hipFuncSetAttribute((const void*)k_control, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)control_lds(S));
 }
 
 hipError_t launch_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, int n, hipStream_t s) {

@@ -4,7 +4,8 @@
 // The step is bound by HBM bandwidth: every routed expert's weights are read in
 // full per step ([FT-blog] §三.2).  Each distinct slot's record is read once for
 // all tokens routed to it.  Work is split three ways:
-//   k_plan      distinct GPU slots of the call and their entries (one workgroup)
+//   (plan)      distinct GPU slots of the call and their entries, one record per slot,
+//               made by the control kernels (k_plan or the fused k_control)
 //   k_gateup    gate and up rows of one 16-row slice over all of H, both matrices
 //               at once, reduced inside the workgroup, SwiGLU applied
 //   k_down      one 16-row slice of the down matrix over all of I
@@ -54,153 +55,127 @@ __device__ inline uint32_t fp4_to_f16x2(uint32_t w) {
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// ---------------------------------------------------------------------------- plan
-__global__ void __launch_bounds__(256)
-k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, DecodePlan* plan) {
-  __shared__ int32_t s_sl[kMaxEntries];
-  __shared__ int32_t s_first[kMaxEntries];
-  __shared__ int s_nu;
-  const int tid = threadIdx.x;
-  if (tid == 0) s_nu = 0;
-  for (int p = tid; p < n; p += blockDim.x) {
-    const int v = slots[p];
-    s_sl[p] = (v >= 0 && v < S) ? v : -1;  // slots outside the arena are never read
-  }
-  __syncthreads();
-  for (int p = tid; p < n; p += blockDim.x) {
-    int v = s_sl[p], first = v >= 0;
-    for (int q = 0; q < p && first; ++q) first = s_sl[q] != v;
-    s_first[p] = first;
-  }
-  __syncthreads();
-  for (int p = tid; p < n; p += blockDim.x) {
-    if (!s_first[p]) continue;
-    int v = s_sl[p], rank = 0, cnt = 0;
-    for (int q = 0; q < n; ++q) rank += s_first[q] && s_sl[q] < v;
-    if (rank >= maxU) continue;  // more distinct slots than a layer has experts: not computed
-    for (int q = 0; q < n && cnt < maxB; ++q)  // a slot appears at most once per token
-      if (s_sl[q] == v) plan->uentry[rank][cnt++] = q;
-    plan->uslot[rank] = v;
-    plan->ucount[rank] = cnt;
-    atomicAdd(&s_nu, 1);
-  }
-  __syncthreads();
-  if (tid == 0) plan->nu = min(s_nu, maxU);
+// ---------------------------------------------------------------------------- gate / up
+// A matrix is stored as 16-row x 32-input tiles, row slices outer: the 16 rows of slice sl are
+// one contiguous run of (Kd/32) tiles of 256 payload bytes (and 32 scale bytes).  Lane
+// (q = lane/16, r = lane%16) reads the dword at byte lane*4 of a tile: row r, inputs 8q..8q+7.
+
+// per-lane scale offset inside a tile's 32 scale bytes
+template <int FMT>
+__device__ inline uint32_t scale_lane_off(int q, int r) {
+  return FMT == EFF_WFMT_INT4_G32_BF16 ? (uint32_t)r * 2u : (uint32_t)((q >> 1) * 16 + r);
+}
+template <int FMT>
+__device__ inline float load_scale(const uint8_t* p) {
+  if (FMT == EFF_WFMT_INT4_G32_BF16) return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
+  return __builtin_amdgcn_cvt_f32_fp8((uint32_t)*p, 0);
 }
 
-// ---------------------------------------------------------------------------- gate / up
-// grid: maxU * (I/16) workgroups of 256 threads, one per (distinct slot, 16-row slice of I).
-// The 4 waves split the 32-input blocks of H; lane (q = lane/16, r = lane%16) holds row r of
-// the slice, inputs 8q..8q+7 of each block (4 bytes of gate, 4 of up).  Everything reduces
-// inside the workgroup, so no workgroup ever waits for another.
+// 8 bf16 activations -> the 4 pairs that meet the weight pairs of one dword
+template <int FMT>
+__device__ inline void x_pairs(const uint4 v, uint32_t* xw) {
+  if (FMT == EFF_WFMT_INT4_G32_BF16) {
+    // pairs (x0,x4), (x1,x5), (x2,x6), (x3,x7) meet the nibble pairs (e0,e4) ...
+    xw[0] = (v.x & 0xFFFFu) | (v.z << 16);
+    xw[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    xw[2] = (v.y & 0xFFFFu) | (v.w << 16);
+    xw[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+  } else {
+    xw[0] = v.x; xw[1] = v.y; xw[2] = v.z; xw[3] = v.w;
+  }
+}
+
+// sum over the 8 inputs of one dword of weights against the paired activations (unscaled)
+template <int FMT>
+__device__ inline float dword_dot_bf16(uint32_t d, const uint32_t* xw, float xs) {
+  uint32_t p0, p1, p2, p3;
+  if (FMT == EFF_WFMT_INT4_G32_BF16) {
+    p0 = (d & 0x000F000Fu) | 0x43004300u;
+    p1 = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
+    p2 = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
+    p3 = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
+  } else {
+    p0 = fp4_to_bf16x2<0>(d); p1 = fp4_to_bf16x2<1>(d);
+    p2 = fp4_to_bf16x2<2>(d); p3 = fp4_to_bf16x2<3>(d);
+  }
+  float raw = dot2_bf16(p3, xw[3], dot2_bf16(p2, xw[2], dot2_bf16(p1, xw[1], dot2_bf16(p0, xw[0], 0.f))));
+  if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-136.f, xs, raw);
+  return raw;
+}
+
+template <int FMT, int NT>
+__device__ inline void gateup_tile(uint32_t wg, uint32_t wu, float sg, float su, const uint4* xv,
+                                   float (&acc)[2][NT]) {
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    uint32_t xw[4];
+    x_pairs<FMT>(xv[j], xw);
+    float xs = 0.f;
+    if (FMT == EFF_WFMT_INT4_G32_BF16)
+      xs = dot2_bf16(xw[3], 0x3F803F80u, dot2_bf16(xw[2], 0x3F803F80u,
+                     dot2_bf16(xw[1], 0x3F803F80u, dot2_bf16(xw[0], 0x3F803F80u, 0.f))));
+    acc[0][j] = fmaf(sg, dword_dot_bf16<FMT>(wg, xw, xs), acc[0][j]);
+    acc[1][j] = fmaf(su, dword_dot_bf16<FMT>(wu, xw, xs), acc[1][j]);
+  }
+}
+
+// grid: maxU * (I/16) workgroups of 256 threads, one per (plan unit, 16-row slice of I).  Wave w
+// takes tiles w, w+4, ... of the slice (the 4 waves together sweep 1 KiB runs), gate and up at
+// once; everything reduces inside the workgroup, so no workgroup ever waits for another.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
 k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
-         const int32_t* __restrict__ owner, const DecodePlan* __restrict__ plan,
-         const uint16_t* __restrict__ x, int H, int I, int K, int maxB, float* __restrict__ a_out) {
-  constexpr int UNR = NT >= 4 ? 2 : (NT == 2 ? 4 : 8);  // blocks in flight per wave
+         const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H, int I, int K,
+         int maxB, float* __restrict__ a_out) {
+  constexpr int UNR = NT >= 4 ? 2 : (NT == 2 ? 4 : 8);  // tiles in flight per wave
   __shared__ float s_red[4][2][16][NT];
-  const int NS = I / 16, NB = I / 64, KB = H / 32;
+  const int NS = I / 16, KB = H / 32;
   const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
-  if (u >= plan->nu) return;
-  const int nb = sl >> 2, t = sl & 3;
-  const int slot = plan->uslot[u], cnt = plan->ucount[u];
-  const uint8_t* rec = arena + (int64_t)slot * R;
+  const DecodeUnit* un = &plan->unit[u];
+  const int cnt = un->count;
+  if (cnt <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
-  const uint8_t* gp = rec + t * 256 + lane * 4;
-  const uint8_t* up = rec + pay + t * 256 + lane * 4;
-  const uint8_t* gs;
-  const uint8_t* us;
-  if (FMT == EFF_WFMT_INT4_G32_BF16) {
-    gs = rec + 3 * pay + r * 8 + t * 2;
-    us = rec + 3 * pay + sca + r * 8 + t * 2;
-  } else {
-    gs = rec + 3 * pay + ((q >> 1) * 16 + r) * 4 + t;
-    us = rec + 3 * pay + sca + ((q >> 1) * 16 + r) * 4 + t;
-  }
-  float tsg = 1.f, tsu = 1.f;
-  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
-    const int fl = owner[slot];
-    tsg = ts[(int64_t)fl * 3 + 0];
-    tsu = ts[(int64_t)fl * 3 + 1];
-  }
+  const uint8_t* rec = arena + (int64_t)un->slot * R;
+  const uint8_t* gp = rec + (int64_t)sl * KB * 256 + lane * 4;
+  const uint8_t* up = gp + pay;
+  const uint8_t* gs = rec + 3 * pay + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
+  const uint8_t* us = gs + sca;
+  const uint16_t* xq = x + q * 8;
   for (int c0 = 0; c0 < cnt; c0 += NT) {
     const int nt = min(NT, cnt - c0);
-    int tok[NT];
+    const uint16_t* xt[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) tok[j] = (j < nt) ? plan->uentry[u][c0 + j] / K : 0;
+    for (int j = 0; j < NT; ++j) xt[j] = xq + (int64_t)((j < nt) ? un->entry[c0 + j] / K : 0) * H;
     float acc[2][NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[0][j] = acc[1][j] = 0.f;
-    for (int kb0 = wave; kb0 < KB; kb0 += 4 * UNR) {
-      // issue every load of UNR blocks first
-      uint32_t wdw[UNR][2];
-      float sc[UNR][2];
+    int kb = wave;
+    for (; kb + 4 * (UNR - 1) < KB; kb += 4 * UNR) {  // full rounds: every load first
+      uint32_t wg[UNR], wu[UNR];
+      float sg[UNR], su[UNR];
       uint4 xv[UNR][NT];
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
-        const int kb = kb0 + 4 * z;
-        if (kb < KB) {
-          const int64_t blk = (int64_t)kb * NB + nb;
-          wdw[z][0] = *reinterpret_cast<const uint32_t*>(gp + blk * 1024);
-          wdw[z][1] = *reinterpret_cast<const uint32_t*>(up + blk * 1024);
-          if (FMT == EFF_WFMT_INT4_G32_BF16) {
-            sc[z][0] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(gs + blk * 128) << 16);
-            sc[z][1] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(us + blk * 128) << 16);
-          } else {
-            sc[z][0] = __builtin_amdgcn_cvt_f32_fp8((uint32_t)gs[blk * 128], 0);
-            sc[z][1] = __builtin_amdgcn_cvt_f32_fp8((uint32_t)us[blk * 128], 0);
-          }
+        const int k = kb + 4 * z;
+        wg[z] = *reinterpret_cast<const uint32_t*>(gp + k * 256);
+        wu[z] = *reinterpret_cast<const uint32_t*>(up + k * 256);
+        sg[z] = load_scale<FMT>(gs + k * 32);
+        su[z] = load_scale<FMT>(us + k * 32);
 #pragma unroll
-          for (int j = 0; j < NT; ++j)
-            xv[z][j] = (j < nt) ? *reinterpret_cast<const uint4*>(x + (int64_t)tok[j] * H + kb * 32 + q * 8)
-                                : make_uint4(0u, 0u, 0u, 0u);
-        } else {
-          wdw[z][0] = wdw[z][1] = 0u;
-          sc[z][0] = sc[z][1] = 0.f;
-#pragma unroll
-          for (int j = 0; j < NT; ++j) xv[z][j] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int j = 0; j < NT; ++j) xv[z][j] = *reinterpret_cast<const uint4*>(xt[j] + k * 32);
       }
 #pragma unroll
-      for (int z = 0; z < UNR; ++z) {
+      for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], sg[z], su[z], xv[z], acc);
+    }
+    for (; kb < KB; kb += 4) {  // tail
+      uint4 xv[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const uint4 v = xv[z][j];
-          uint32_t xw[4];
-          if (FMT == EFF_WFMT_INT4_G32_BF16) {
-            // pairs (x0,x4), (x1,x5), (x2,x6), (x3,x7) meet the nibble pairs below
-            xw[0] = (v.x & 0xFFFFu) | (v.z << 16);
-            xw[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
-            xw[2] = (v.y & 0xFFFFu) | (v.w << 16);
-            xw[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
-          } else {
-            xw[0] = v.x; xw[1] = v.y; xw[2] = v.z; xw[3] = v.w;
-          }
-          float xs = 0.f;
-          if (FMT == EFF_WFMT_INT4_G32_BF16)
-            xs = dot2_bf16(xw[3], 0x3F803F80u, dot2_bf16(xw[2], 0x3F803F80u,
-                           dot2_bf16(xw[1], 0x3F803F80u, dot2_bf16(xw[0], 0x3F803F80u, 0.f))));
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const uint32_t d = wdw[z][m];
-            uint32_t p0, p1, p2, p3;
-            if (FMT == EFF_WFMT_INT4_G32_BF16) {
-              p0 = (d & 0x000F000Fu) | 0x43004300u;
-              p1 = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
-              p2 = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
-              p3 = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
-            } else {
-              p0 = fp4_to_bf16x2<0>(d); p1 = fp4_to_bf16x2<1>(d);
-              p2 = fp4_to_bf16x2<2>(d); p3 = fp4_to_bf16x2<3>(d);
-            }
-            float raw = dot2_bf16(p3, xw[3], dot2_bf16(p2, xw[2], dot2_bf16(p1, xw[1], dot2_bf16(p0, xw[0], 0.f))));
-            if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-136.f, xs, raw);
-            acc[m][j] = fmaf(sc[z][m], raw, acc[m][j]);
-          }
-        }
-      }
+      for (int j = 0; j < NT; ++j) xv[j] = *reinterpret_cast<const uint4*>(xt[j] + kb * 32);
+      gateup_tile<FMT, NT>(*reinterpret_cast<const uint32_t*>(gp + kb * 256),
+                           *reinterpret_cast<const uint32_t*>(up + kb * 256), load_scale<FMT>(gs + kb * 32),
+                           load_scale<FMT>(us + kb * 32), xv, acc);
     }
     // reduce over q (lanes r, r+16, r+32, r+48), then over the 4 waves in order
 #pragma unroll
@@ -227,8 +202,10 @@ k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__
       float v = s_red[0][1][row][j] + s_red[1][1][row][j];
       v += s_red[2][1][row][j];
       v += s_red[3][1][row][j];
-      g *= tsg;
-      v *= tsu;
+      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
+        g *= ts[(int64_t)un->flat * 3 + 0];
+        v *= ts[(int64_t)un->flat * 3 + 1];
+      }
       a_out[((int64_t)u * maxB + c0 + j) * I + sl * 16 + row] = silu(g) * v;
     }
     __syncthreads();
@@ -236,36 +213,67 @@ k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------- down
-// grid: maxU * (H/16) workgroups, one per (distinct slot, 16-row slice of H).  The SwiGLU
-// activations of the slot's tokens are staged in LDS as fp16, each token scaled by a power of
+template <int FMT, int NT>
+__device__ inline void down_tile(uint32_t d, float sd, const uint4* s_a4, const float (*s_asum)[512], int kb,
+                                 int q, int nt, int I8, float (&acc)[NT]) {
+  uint32_t p0, p1, p2, p3;
+  if (FMT == EFF_WFMT_INT4_G32_BF16) {
+    p0 = (d & 0x000F000Fu) | 0x64006400u;
+    p1 = ((d >> 4) & 0x000F000Fu) | 0x64006400u;
+    p2 = ((d >> 8) & 0x000F000Fu) | 0x64006400u;
+    p3 = ((d >> 12) & 0x000F000Fu) | 0x64006400u;
+  } else {
+    p0 = fp4_to_f16x2<0>(d); p1 = fp4_to_f16x2<1>(d);
+    p2 = fp4_to_f16x2<2>(d); p3 = fp4_to_f16x2<3>(d);
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if (j < nt) {
+      const uint4 av = s_a4[j * I8 + kb * 4 + q];
+      float raw = dot2_f16(p3, av.w, dot2_f16(p2, av.z, dot2_f16(p1, av.y, dot2_f16(p0, av.x, 0.f))));
+      if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-1032.f, s_asum[j][kb * 4 + q], raw);
+      acc[j] = fmaf(sd, raw, acc[j]);
+    }
+  }
+}
+
+// grid: maxU * (H/16) workgroups, one per (plan unit, 16-row slice of H).  The SwiGLU
+// activations of the unit's tokens are staged in LDS as fp16, each token scaled by a power of
 // two so that its largest value fits.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
 k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
-       const int32_t* __restrict__ owner, const DecodePlan* __restrict__ plan,
-       const float* __restrict__ a_in, int H, int I, int maxB, float* __restrict__ y) {
+       const DecodePlan* __restrict__ plan, const float* __restrict__ a_in, int H, int I, int maxB,
+       float* __restrict__ y) {
   extern __shared__ uint4 s_a4[];            // [NT][I/8] groups of 8 fp16 (int4 order permuted)
   __shared__ float s_asum[NT][512];          // int4: sum of each 8-group (I/8 <= 512)
   __shared__ float s_red[4][16][NT];
   __shared__ float s_scale[NT];
   __shared__ float s_amax[NT][4];
   constexpr int UNR = NT >= 4 ? 2 : 4;
-  const int NS = H / 16, NBH = H / 64, KB = I / 32;
+  const int NS = H / 16, KB = I / 32, I8 = I / 8;
   const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
-  if (u >= plan->nu) return;
-  const int nb = sl >> 2, t = sl & 3;
-  const int slot = plan->uslot[u], cnt = plan->ucount[u];
-  const uint8_t* rec = arena + (int64_t)slot * R;
+  const DecodeUnit* un = &plan->unit[u];
+  const int cnt = un->count;
+  if (cnt <= 0) return;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
-  const uint8_t* dp = rec + 2 * pay + t * 256 + lane * 4;
-  const uint8_t* ds = (FMT == EFF_WFMT_INT4_G32_BF16) ? rec + 3 * pay + 2 * sca + r * 8 + t * 2
-                                                      : rec + 3 * pay + 2 * sca + ((q >> 1) * 16 + r) * 4 + t;
-  float tsd = 1.f;
-  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsd = ts[(int64_t)owner[slot] * 3 + 2];
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint8_t* rec = arena + (int64_t)un->slot * R;
+  const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 4;
+  const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
 
   for (int c0 = 0; c0 < cnt; c0 += NT) {
     const int nt = min(NT, cnt - c0);
+    // the weights do not depend on the activations: start their loads first
+    uint32_t wd[UNR];
+    float sd[UNR];
+#pragma unroll
+    for (int z = 0; z < UNR; ++z) {
+      const int k = wave + 4 * z;
+      wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
+      sd[z] = k < KB ? load_scale<FMT>(ds + k * 32) : 0.f;
+    }
     // per-token power-of-two scale: |a| * 2^-e < 2^15
     for (int j = 0; j < nt; ++j) {
       const float* aj = a_in + ((int64_t)u * maxB + c0 + j) * I;
@@ -285,8 +293,8 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
       s_scale[tid] = ldexpf(1.f, e);
     }
     __syncthreads();
-    for (int i = tid; i < nt * (I / 8); i += kWG) {
-      const int j = i / (I / 8), g = i % (I / 8);
+    for (int i = tid; i < nt * I8; i += kWG) {
+      const int j = i / I8, g = i % I8;
       const float* src = a_in + ((int64_t)u * maxB + c0 + j) * I + g * 8;
       const float inv = 1.f / s_scale[j];
       _Float16 h[8];
@@ -308,54 +316,25 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
           o[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * z]) |
                  ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * z + 1]) << 16);
       }
-      s_a4[j * (I / 8) + g] = make_uint4(o[0], o[1], o[2], o[3]);
+      s_a4[j * I8 + g] = make_uint4(o[0], o[1], o[2], o[3]);
     }
     __syncthreads();
     float acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = 0.f;
-    for (int kb0 = wave; kb0 < KB; kb0 += 4 * UNR) {
-      uint32_t wdw[UNR];
-      float sd[UNR];
+#pragma unroll
+    for (int z = 0; z < UNR; ++z)
+      if (wave + 4 * z < KB) down_tile<FMT, NT>(wd[z], sd[z], s_a4, s_asum, wave + 4 * z, q, nt, I8, acc);
+    for (int kb0 = wave + 4 * UNR; kb0 < KB; kb0 += 4 * UNR) {
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
-        const int kb = kb0 + 4 * z;
-        if (kb < KB) {
-          const int64_t blk = (int64_t)kb * NBH + nb;
-          wdw[z] = *reinterpret_cast<const uint32_t*>(dp + blk * 1024);
-          sd[z] = (FMT == EFF_WFMT_INT4_G32_BF16)
-                      ? __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(ds + blk * 128) << 16)
-                      : __builtin_amdgcn_cvt_f32_fp8((uint32_t)ds[blk * 128], 0);
-        } else {
-          wdw[z] = 0u;
-          sd[z] = 0.f;
-        }
+        const int k = kb0 + 4 * z;
+        wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
+        sd[z] = k < KB ? load_scale<FMT>(ds + k * 32) : 0.f;
       }
 #pragma unroll
-      for (int z = 0; z < UNR; ++z) {
-        const int kb = kb0 + 4 * z;
-        if (kb >= KB) break;
-        const uint32_t d = wdw[z];
-        uint32_t p0, p1, p2, p3;
-        if (FMT == EFF_WFMT_INT4_G32_BF16) {
-          p0 = (d & 0x000F000Fu) | 0x64006400u;
-          p1 = ((d >> 4) & 0x000F000Fu) | 0x64006400u;
-          p2 = ((d >> 8) & 0x000F000Fu) | 0x64006400u;
-          p3 = ((d >> 12) & 0x000F000Fu) | 0x64006400u;
-        } else {
-          p0 = fp4_to_f16x2<0>(d); p1 = fp4_to_f16x2<1>(d);
-          p2 = fp4_to_f16x2<2>(d); p3 = fp4_to_f16x2<3>(d);
-        }
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          if (j < nt) {
-            const uint4 av = s_a4[j * (I / 8) + kb * 4 + q];
-            float raw = dot2_f16(p3, av.w, dot2_f16(p2, av.z, dot2_f16(p1, av.y, dot2_f16(p0, av.x, 0.f))));
-            if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-1032.f, s_asum[j][kb * 4 + q], raw);
-            acc[j] = fmaf(sd[z], raw, acc[j]);
-          }
-        }
-      }
+      for (int z = 0; z < UNR; ++z)
+        if (kb0 + 4 * z < KB) down_tile<FMT, NT>(wd[z], sd[z], s_a4, s_asum, kb0 + 4 * z, q, nt, I8, acc);
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -374,8 +353,9 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
       float v = s_red[0][row][j] + s_red[1][row][j];
       v += s_red[2][row][j];
       v += s_red[3][row][j];
-      v = v * s_scale[j] * tsd;
-      const int p = plan->uentry[u][c0 + j];
+      v = v * s_scale[j];
+      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= ts[(int64_t)un->flat * 3 + 2];
+      const int p = un->entry[c0 + j];
       y[(int64_t)p * H + sl * 16 + row] = v;
     }
     __syncthreads();
@@ -406,15 +386,16 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, hipStream_t 
   const int H = c.hidden, I = c.inter;
   const int ts = timing_begin(e, EFF_T_DECODE_GATEUP, s);
   hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(e->maxU * (I / 16)), dim3(kWG), 0, s, e->d_arena, e->R, e->d_ts,
-                     e->d_owner, e->d_plan, x, H, I, c.top_k, c.max_tokens, e->d_a);
+                     e->d_plan, x, H, I, c.top_k, c.max_tokens, e->d_a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
+  timing_mark(e, ts, 2, s);
   size_t lds = (size_t)NT * (I / 8) * sizeof(uint4);
   hipLaunchKernelGGL((k_down<FMT, NT>), dim3(e->maxU * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->R, e->d_ts,
-                     e->d_owner, e->d_plan, e->d_a, H, I, c.max_tokens, y);
+                     e->d_plan, e->d_a, H, I, c.max_tokens, y);
   err = hipGetLastError();
-  timing_mark(e, ts, 2, s);
+  timing_mark(e, ts, 3, s);
   return err;
 }
 
@@ -438,13 +419,12 @@ hipError_t decode_kernels_setup(int fmt, int maxB, int I) {
 }
 
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
-                             float* y, hipStream_t s) {
+                             float* y, hipStream_t s, bool plan_ready) {
   (void)layer;
-  const int n = B * e->cfg.top_k;
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, s, slots, n, e->cfg.num_slots, e->maxU, e->cfg.max_tokens,
-                     e->d_plan);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (!plan_ready) {
+    hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s);
+    if (err != hipSuccess) return err;
+  }
   const int NT = decode_nt(e->cfg.max_tokens);
   const bool fp4 = e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3;
   switch (NT) {

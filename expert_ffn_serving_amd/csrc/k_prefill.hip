@@ -12,9 +12,8 @@
 //   k_combine     (shared with decode) out[t] = sum_k w[t,k] y[t,k]
 //
 // Weights stay 4-bit in HBM and are dequantized in registers straight into the
-// MFMA B operand: a lane's 4 bytes for rows 16t+r, inputs 8q..8q+7 of a record
-// block (slice t, offset (16q+r)*4) are exactly the B fragment of lane 16q+r for
-// n-subtile t.  NVFP4:
+// MFMA B operand: the 4 bytes at offset (16q+r)*4 of a 16-row x 32-input tile
+// (row r, inputs 8q..8q+7) are exactly the B fragment of lane 16q+r.  NVFP4:
 // e2m1 -> fp16 with v_cvt_scalef32_pk_f16_fp4, times the e4m3 block scale with
 // a packed fp16 multiply (e2m1 * e4m3 has at most 6 significant bits and lies
 // in [2^-10, 2688], so it is exact in fp16); the fp32 tensor scale is applied
@@ -128,20 +127,20 @@ __device__ inline f16x8_t dequant8(uint32_t d, uint32_t s2) {
   return __builtin_bit_cast(f16x8_t, u4);
 }
 
-// 4 scales of one lane (rows 16t + r, t = 0..3) as fp16 pairs
+// 4 scales of one lane for the tiles of 4 consecutive row slices (tiles tstride apart, scale
+// areas tstride/8 apart) as fp16 pairs
 template <int FMT>
-__device__ inline void load_scales(const uint8_t* sblk, int q, int r, uint32_t* s2) {
-  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
-    const uint32_t a = *reinterpret_cast<const uint32_t*>(sblk + ((q >> 1) * 16 + r) * 4);
-    float f0 = __builtin_amdgcn_cvt_f32_fp8(a, 0), f1 = __builtin_amdgcn_cvt_f32_fp8(a, 1);
-    float f2 = __builtin_amdgcn_cvt_f32_fp8(a, 2), f3 = __builtin_amdgcn_cvt_f32_fp8(a, 3);
-    s2[0] = pk_f16(f0, f0); s2[1] = pk_f16(f1, f1); s2[2] = pk_f16(f2, f2); s2[3] = pk_f16(f3, f3);
-  } else {
-    const uint2 a = *reinterpret_cast<const uint2*>(sblk + r * 8);
-    float f0 = __uint_as_float(a.x << 16), f1 = __uint_as_float(a.x & 0xFFFF0000u);
-    float f2 = __uint_as_float(a.y << 16), f3 = __uint_as_float(a.y & 0xFFFF0000u);
-    s2[0] = pk_f16(f0, f0); s2[1] = pk_f16(f1, f1); s2[2] = pk_f16(f2, f2); s2[3] = pk_f16(f3, f3);
+__device__ inline void load_scales(const uint8_t* sp, int64_t sstride, uint32_t* s2) {
+  float f[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (FMT == EFF_WFMT_NVFP4_G16_E4M3)
+      f[t] = __builtin_amdgcn_cvt_f32_fp8((uint32_t)sp[t * sstride], 0);
+    else
+      f[t] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(sp + t * sstride) << 16);
   }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) s2[t] = pk_f16(f[t], f[t]);
 }
 
 // Stage a 64 x 32 activation tile into LDS as fp16 (row-major, 64 B per row).  src_bf16: rows
@@ -189,11 +188,11 @@ __device__ inline void stage_tile(uint32_t* s_tile, const void* src, int ld, con
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// The 4 bytes of this lane in each 16-row slice t of a 1 KiB payload block (slice t holds
-// rows 16t..16t+15 as 256 contiguous bytes): .x = t0, .y = t1, .z = t2, .w = t3.
-__device__ inline uint4 load_block(const uint8_t* blk, int lane) {
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(blk + lane * 4);
-  return make_uint4(p[0], p[64], p[128], p[192]);
+// The 4 bytes of this lane in the same k tile of 4 consecutive row slices (tstride bytes apart).
+__device__ inline uint4 load_block(const uint8_t* p, int64_t tstride) {
+  return make_uint4(*reinterpret_cast<const uint32_t*>(p), *reinterpret_cast<const uint32_t*>(p + tstride),
+                    *reinterpret_cast<const uint32_t*>(p + 2 * tstride),
+                    *reinterpret_cast<const uint32_t*>(p + 3 * tstride));
 }
 
 // grid: E * (I / 256); 4 waves, wave w owns row block nb = j*4 + w of gate and up
@@ -217,6 +216,11 @@ k_pf_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
   const int nb = j * 4 + wave;
   const bool active = nb < NB;  // waves past the last row block only help stage tiles
+  // this wave's 64 rows are row slices 4nb..4nb+3: tiles KB*256 bytes apart, k tiles 256 apart
+  const int64_t tstride = (int64_t)KB * 256, sstride = (int64_t)KB * 32;
+  const uint8_t* gp = rec + (int64_t)nb * 4 * tstride + lane * 4;
+  const uint8_t* gs = rec + 3 * pay + (int64_t)nb * 4 * sstride +
+                      (FMT == EFF_WFMT_INT4_G32_BF16 ? r * 2 : (q >> 1) * 16 + r);
   float tsg = 1.f, tsu = 1.f;
   if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
     const int fl = owner[slot];
@@ -235,11 +239,10 @@ k_pf_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restric
     uint4 wn[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
     uint32_t sn[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     if (active) {
-      const int64_t blk = (int64_t)0 * NB + nb;
-      wn[0] = load_block(rec + blk * 1024, lane);
-      wn[1] = load_block(rec + pay + blk * 1024, lane);
-      load_scales<FMT>(rec + 3 * pay + blk * 128, q, r, sn[0]);
-      load_scales<FMT>(rec + 3 * pay + sca + blk * 128, q, r, sn[1]);
+      wn[0] = load_block(gp, tstride);
+      wn[1] = load_block(gp + pay, tstride);
+      load_scales<FMT>(gs, sstride, sn[0]);
+      load_scales<FMT>(gs + sca, sstride, sn[1]);
     }
     for (int kb = 0; kb < KB; ++kb) {
       const uint4 wc[2] = {wn[0], wn[1]};
@@ -248,12 +251,11 @@ k_pf_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restric
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int t = 0; t < 4; ++t) sc[m][t] = sn[m][t];
-      if (active && kb + 1 < KB) {  // prefetch the next k block
-        const int64_t blk = (int64_t)(kb + 1) * NB + nb;
-        wn[0] = load_block(rec + blk * 1024, lane);
-        wn[1] = load_block(rec + pay + blk * 1024, lane);
-        load_scales<FMT>(rec + 3 * pay + blk * 128, q, r, sn[0]);
-        load_scales<FMT>(rec + 3 * pay + sca + blk * 128, q, r, sn[1]);
+      if (active && kb + 1 < KB) {  // prefetch the next k tile
+        wn[0] = load_block(gp + (kb + 1) * 256, tstride);
+        wn[1] = load_block(gp + pay + (kb + 1) * 256, tstride);
+        load_scales<FMT>(gs + (kb + 1) * 32, sstride, sn[0]);
+        load_scales<FMT>(gs + sca + (kb + 1) * 32, sstride, sn[1]);
       }
       __syncthreads();
       stage_tile<FMT, true>(s_tile, x, H, rows, off, m0, mt, K, kb * 32);
@@ -310,12 +312,14 @@ k_pf_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   const int slot = slot_base >= 0 ? slot_base + e : slot_of[e];
   const uint8_t* rec = arena + (int64_t)slot * R;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const uint8_t* dp = rec + 2 * pay;
-  const uint8_t* ds = rec + 3 * pay + 2 * sca;
   const int NB = H / 64, KB = I / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
   const int nb = j * 4 + wave;
   const bool active = nb < NB;
+  const int64_t tstride = (int64_t)KB * 256, sstride = (int64_t)KB * 32;
+  const uint8_t* dp = rec + 2 * pay + (int64_t)nb * 4 * tstride + lane * 4;
+  const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)nb * 4 * sstride +
+                      (FMT == EFF_WFMT_INT4_G32_BF16 ? r * 2 : (q >> 1) * 16 + r);
   float tsd = 1.f;
   if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsd = ts[(int64_t)owner[slot] * 3 + 2];
   for (int m0 = 0; m0 < ne; m0 += kMT) {
@@ -328,16 +332,15 @@ k_pf_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
     uint4 wn = make_uint4(0u, 0u, 0u, 0u);
     uint32_t sn[4] = {0u, 0u, 0u, 0u};
     if (active) {
-      wn = load_block(dp + (int64_t)nb * 1024, lane);
-      load_scales<FMT>(ds + (int64_t)nb * 128, q, r, sn);
+      wn = load_block(dp, tstride);
+      load_scales<FMT>(ds, sstride, sn);
     }
     for (int kb = 0; kb < KB; ++kb) {
       const uint4 wc = wn;
       uint32_t sc[4] = {sn[0], sn[1], sn[2], sn[3]};
       if (active && kb + 1 < KB) {
-        const int64_t blk = (int64_t)(kb + 1) * NB + nb;
-        wn = load_block(dp + blk * 1024, lane);
-        load_scales<FMT>(ds + blk * 128, q, r, sn);
+        wn = load_block(dp + (kb + 1) * 256, tstride);
+        load_scales<FMT>(ds + (kb + 1) * 32, sstride, sn);
       }
       __syncthreads();
       stage_tile<FMT, false>(s_tile, a_in, I, rows, off, m0, mt, 0, kb * 32);
@@ -399,6 +402,7 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
                        K, e->d_pf_a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
+  timing_mark(e, ts, 2, s);
   if (fp4)
     hipLaunchKernelGGL(k_pf_down<EFF_WFMT_NVFP4_G16_E4M3>, dim3(nbx2), dim3(256), 0, s, e->d_arena, e->R,
                        e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, e->d_pf_a,
@@ -408,7 +412,7 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
                        e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, e->d_pf_a,
                        E, H, I, e->d_pf_y);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  timing_mark(e, ts, 2, s);
+  timing_mark(e, ts, 3, s);
   if (!combine) return hipSuccess;
   return launch_combine(e->d_pf_y, nullptr, nullptr, w, T, K, H, out, s);
 }

@@ -1,4 +1,4 @@
-// Router: fp32 logits in a fixed summation order, then top-K and softmax over the K.
+// Router logits: fp32 sums in a fixed order (top-K and softmax are in k_cache.hip).
 //
 // Routing is computed exactly and the model is left untouched ([FT-deep] §2);
 // the router runs on the GPU ahead of the hit/miss split ([FT-blog] §二).  The
@@ -51,122 +51,72 @@ __device__ inline void unpack<1>(const uint16_t& v, float* o) {
   o[0] = __uint_as_float((uint32_t)v << 16);
 }
 
-// grid: (ceil(E / (4*EPW)), ceil(B / TB)); wave w handles experts bx*4*EPW + w*EPW + [0, EPW)
-// for the tokens of tile by.
-template <int V, int EPW>
+// grid: (ceil(E / (4*EE)), ceil(B / TT)).  Wave w of workgroup (bx, by) computes the logits of
+// tokens by*TT .. +TT-1 against experts (bx*4 + w)*EE .. +EE-1; every (token, expert) sum keeps
+// the fixed lane order, the tile only shares the loads.
+template <int V, int TT, int EE>
 __global__ void __launch_bounds__(256)
-k_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int B, int E, int H, int TB,
+k_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int B, int E, int H,
          float* __restrict__ logits) {
   typedef typename Vec<V>::T VT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = (blockIdx.x * 4 + wave) * EPW;
+  const int e0 = (blockIdx.x * 4 + wave) * EE;
   if (e0 >= E) return;
-  const int t0 = blockIdx.y * TB, t1 = min(B, t0 + TB);
+  const int t0 = blockIdx.y * TT;
   const int rounds = H / (64 * V);
-  for (int t = t0; t < t1; ++t) {
-    float acc[EPW];
+  float acc[TT][EE];
 #pragma unroll
-    for (int q = 0; q < EPW; ++q) acc[q] = 0.f;
-    for (int c = 0; c < rounds; ++c) {
-      const int j0 = 64 * V * c + V * lane;
-      float xv[V];
-      unpack<V>(*reinterpret_cast<const VT*>(x + (int64_t)t * H + j0), xv);
+  for (int a = 0; a < TT; ++a)
 #pragma unroll
-      for (int q = 0; q < EPW; ++q) {
-        if (e0 + q < E) {
-          float wv[V];
-          unpack<V>(*reinterpret_cast<const VT*>(wr + (int64_t)(e0 + q) * H + j0), wv);
+    for (int b = 0; b < EE; ++b) acc[a][b] = 0.f;
+  for (int c = 0; c < rounds; ++c) {
+    const int j0 = 64 * V * c + V * lane;
+    float xv[TT][V];
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[q] = fmaf(xv[i], wv[i], acc[q]);
-        }
+    for (int a = 0; a < TT; ++a) {
+      if (t0 + a < B) {
+        unpack<V>(*reinterpret_cast<const VT*>(x + (int64_t)(t0 + a) * H + j0), xv[a]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) xv[a][i] = 0.f;
       }
     }
 #pragma unroll
-    for (int q = 0; q < EPW; ++q) {
-      float v = acc[q];
+    for (int b = 0; b < EE; ++b) {
+      if (e0 + b < E) {
+        float wv[V];
+        unpack<V>(*reinterpret_cast<const VT*>(wr + (int64_t)(e0 + b) * H + j0), wv);
+#pragma unroll
+        for (int a = 0; a < TT; ++a)
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[a][b] = fmaf(xv[a][i], wv[i], acc[a][b]);
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < TT; ++a)
+#pragma unroll
+    for (int b = 0; b < EE; ++b) {
+      float v = acc[a][b];
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o);
-      if (lane == 0 && e0 + q < E) logits[(int64_t)t * E + e0 + q] = v;
+      if (lane == 0 && t0 + a < B && e0 + b < E) logits[(int64_t)(t0 + a) * E + e0 + b] = v;
     }
-  }
 }
 
-__device__ inline bool better(float a, int ia, float b, int ib) { return a > b || (a == b && ia < ib); }
-
-// one workgroup per token: K rounds of block argmax over E logits by (logit desc, id asc)
-__global__ void __launch_bounds__(256)
-k_topk(const float* __restrict__ logits, int E, int K, int32_t* __restrict__ ids, float* __restrict__ w) {
-  extern __shared__ float s_l[];            // [E]
-  __shared__ int32_t s_taken[kMaxExperts / 32];
-  __shared__ float s_bv[4];
-  __shared__ int s_bi[4];
-  __shared__ float s_sel[kMaxTopK];
-  __shared__ int s_selid[kMaxTopK];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += blockDim.x) s_l[e] = logits[(int64_t)t * E + e];
-  for (int i = tid; i < (E + 31) / 32; i += blockDim.x) s_taken[i] = 0;
-  __syncthreads();
-  for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-    for (int e = tid; e < E; e += blockDim.x) {
-      if ((s_taken[e >> 5] >> (e & 31)) & 1) continue;
-      float v = s_l[e];
-      if (bi == 0x7FFFFFFF || better(v, e, bv, bi)) {
-        bv = v;
-        bi = e;
-      }
-    }
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o);
-      int oi = __shfl_xor(bi, o);
-      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lane == 0) {
-      s_bv[wave] = bv;
-      s_bi[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float v = s_bv[0];
-      int i = s_bi[0];
-      for (int q = 1; q < 4; ++q)
-        if (s_bi[q] != 0x7FFFFFFF && (i == 0x7FFFFFFF || better(s_bv[q], s_bi[q], v, i))) {
-          v = s_bv[q];
-          i = s_bi[q];
-        }
-      s_sel[k] = v;
-      s_selid[k] = i;
-      s_taken[i >> 5] |= 1 << (i & 31);
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    // softmax over the K selected logits, relative to the largest
-    float sum = 0.f;
-    for (int k = 0; k < K; ++k) sum += expf(s_sel[k] - s_sel[0]);
-    for (int k = 0; k < K; ++k) {
-      ids[(int64_t)t * K + k] = s_selid[k];
-      w[(int64_t)t * K + k] = expf(s_sel[k] - s_sel[0]) / sum;
-    }
-  }
+template <int V, int TT, int EE>
+hipError_t launch_logits_t(const uint16_t* x, const uint16_t* wr, int B, int E, int H, float* lg, hipStream_t s) {
+  dim3 g((E + 4 * EE - 1) / (4 * EE), (B + TT - 1) / TT);
+  hipLaunchKernelGGL((k_logits<V, TT, EE>), g, dim3(256), 0, s, x, wr, B, E, H, lg);
+  return hipGetLastError();
 }
 
 template <int V>
 hipError_t launch_logits_v(const uint16_t* x, const uint16_t* wr, int B, int E, int H, float* lg,
                            hipStream_t s) {
-  if (B <= 32) {
-    dim3 g((E + 3) / 4, 1);
-    hipLaunchKernelGGL((k_logits<V, 1>), g, dim3(256), 0, s, x, wr, B, E, H, B, lg);
-  } else {
-    const int TB = 64;
-    dim3 g((E + 15) / 16, (B + TB - 1) / TB);
-    hipLaunchKernelGGL((k_logits<V, 4>), g, dim3(256), 0, s, x, wr, B, E, H, TB, lg);
-  }
-  return hipGetLastError();
+  if (B <= 2) return launch_logits_t<V, 1, 1>(x, wr, B, E, H, lg, s);
+  if (B <= 32) return launch_logits_t<V, 4, 2>(x, wr, B, E, H, lg, s);
+  return launch_logits_t<V, 8, 4>(x, wr, B, E, H, lg, s);
 }
 
 }  // namespace
@@ -177,12 +127,6 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, int B, int
   if (H % 256 == 0) return launch_logits_v<4>(x, wr, B, E, H, logits, s);
   if (H % 128 == 0) return launch_logits_v<2>(x, wr, B, E, H, logits, s);
   return launch_logits_v<1>(x, wr, B, E, H, logits, s);
-}
-
-hipError_t launch_topk(const float* logits, int B, int E, int K, int32_t* ids, float* w, hipStream_t s) {
-  if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk, dim3(B), dim3(256), (size_t)E * sizeof(float), s, logits, E, K, ids, w);
-  return hipGetLastError();
 }
 
 }  // namespace eff

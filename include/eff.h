@@ -20,13 +20,14 @@
  * by the flat id layer*E + expert ([FT-blog] §四, §七 item 3; [FT-deep] §4 ⑤).
  * Record = gate[I,H] | up[I,H] | down[H,I] payloads, then their scales in the
  * same order ([NVMe-8GB] "엔진" item 1).  Each matrix (N rows = outputs, Kd
- * columns = inputs) is stored as 1 KiB blocks of 64 rows x 32 inputs, block
- * index kb*(N/64)+nb (kb = k/32, nb = n/64); inside a block element (n, k) is
- * at byte t*256 + (q*16 + r)*4 + i/2 with t=(n%64)/16, r=n%16, q=(k%32)/8,
- * i=k%8, even i in the low nibble (each 16-row slice is 256 contiguous bytes).  Each block has a 128-byte scale block at
- * the same index: INT4_G32_BF16 stores the bf16 scale of (n, k/32) at byte
- * (r*4+t)*2 and values are (u-8)*scale; NVFP4_G16_E4M3 stores the e4m3 scale
- * of (n, k/16) at byte (((k%32)/16)*16 + r)*4 + t and values are
+ * columns = inputs; N % 16 == 0, Kd % 32 == 0) is stored as tiles of 16 rows x
+ * 32 inputs, tile index (n/16)*(Kd/32) + k/32: the 16 rows of a row slice are one
+ * contiguous run.  A tile's 256 payload bytes hold element (n, k) at byte
+ * (q*16 + r)*4 + i/2 with r=n%16, q=(k%32)/8, i=k%8, even i in the low nibble.
+ * Each tile has 32 scale bytes at the same index in the scale area:
+ * INT4_G32_BF16 stores the bf16 scale of (n, k/32) at byte r*2 and values are
+ * (u-8)*scale; NVFP4_G16_E4M3 stores the e4m3 scale of (n, k/16) at byte
+ * ((k%32)/16)*16 + r and values are
  * e2m1(code)*e4m3(scale)*tensor_scale, with one fp32 tensor scale per matrix
  * kept resident in the engine (tensor_scales[(layer*E+expert)*3 + m]).
  * Record size R = 3*H*I/2 + 3*H*I/16 bytes in both formats.
@@ -165,8 +166,10 @@ int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const in
 /* One decode MoE layer end to end, eager: route (from x and w_router, or from
  * logits if w_router is NULL) -> ensure -> split -> [speculative ensure/split
  * of layer+1 on spec_ids if not NULL] -> copies on `side` -> GPU expert FFN ->
- * host share -> combine into out (bf16 [B,H]).  Waits on the host once (to
- * read the fetch list and the host ids).  ids/w/slots/cpu_ids/counts of the
+ * host share -> combine into out (bf16 [B,H]).  top-K, ensure, split and the
+ * speculative request run as one single-workgroup kernel with the same
+ * semantics as the separate calls.  Waits on the host once (to read the
+ * fetch list, the host ids and x from host-mapped memory).  ids/w/slots/cpu_ids/counts of the
  * call can be read back with eff_last_layer_info. */
 int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_router,
                      const float* logits, int B, const int32_t* spec_ids, void* out,
@@ -207,6 +210,9 @@ typedef struct eff_stats {
   int64_t qstar_hist[17]; /* q' counts 0..15, 16+ */
   int64_t launches[4];    /* timed launches per EFF_T_* slot */
   double kernel_ms[4];    /* summed durations per EFF_T_* slot (HIP events) */
+  double host_ms;         /* eff_decode_layer: wall time in the host executor */
+  double wait_ms;         /* eff_decode_layer: wall time waiting for the control kernel */
+  int64_t host_calls;     /* eff_decode_layer calls with a host share */
 } eff_stats;
 /* Changes eff_config.flags of a live engine (EFF_CFG_* bits); EFF_EINVAL for unknown bits. */
 int eff_set_flags(eff_engine* e, uint32_t flags);

@@ -7,7 +7,7 @@
  *
  * Formats: int4 value (u - 8) * bf16 scale per 32 inputs; NVFP4 value
  * e2m1(c) * e4m3(s) * tensor scale, e4m3 per 16 inputs.  Layout: see
- * oracle/formats.py (64 x 32 payload blocks, block = kb * (N / 64) + nb).
+ * oracle/formats.py (16 x 32 tiles, tile = (n / 16) * (Kd / 32) + k / 32).
  */
 #include <math.h>
 #include <pthread.h>
@@ -42,18 +42,18 @@ static void decode_row(const uint8_t* rec, int fmt, int64_t H, int64_t I, int m,
   int64_t N = (m == 2) ? H : I, Kd = (m == 2) ? I : H;
   const uint8_t* pay = rec + m * (H * I / 2);
   const uint8_t* sca = rec + 3 * (H * I / 2) + m * (H * I / 16);
+  (void)N;
   for (int64_t k = 0; k < Kd; ++k) {
-    int64_t kb = k / 32, nb = n / 64, blk = kb * (N / 64) + nb;
-    int64_t t = (n % 64) / 16, r = n % 16, q = (k % 32) / 8, i = k % 8;
-    int64_t off = blk * 1024 + t * 256 + (q * 16 + r) * 4 + i / 2;
+    int64_t tile = (n / 16) * (Kd / 32) + k / 32;
+    int64_t r = n % 16, q = (k % 32) / 8, i = k % 8;
+    int64_t off = tile * 256 + (q * 16 + r) * 4 + i / 2;
     int code = (i % 2 == 0) ? (pay[off] & 15) : (pay[off] >> 4);
-    int64_t sbase = blk * 128;
     if (fmt == 0) {
-      int64_t so = sbase + (r * 4 + t) * 2;
+      int64_t so = tile * 32 + r * 2;
       uint16_t sb = (uint16_t)(sca[so] | (sca[so + 1] << 8));
       out[k] = (double)(code - 8) * bf16(sb);
     } else {
-      int64_t so = sbase + (((k % 32) / 16) * 16 + r) * 4 + t;
+      int64_t so = tile * 32 + ((k % 32) / 16) * 16 + r;
       out[k] = e2m1(code) * e4m3(sca[so]) * ts;
     }
   }

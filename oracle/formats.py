@@ -14,14 +14,13 @@ down_scale ([NVMe-8GB] "엔진" item 1).  The bit-level definitions used here:
 
 Record byte layout (the layout the library is written against; restated here
 independently of the writer): a matrix of N output rows by Kd inputs is cut
-into payload blocks of 64 rows x 32 inputs (1 KiB), block index
-kb * (N/64) + nb for kb = k // 32, nb = n // 64.  Inside the block element
-(n, k) is at byte t*256 + (q*16 + r)*4 + i//2, t = (n%64)//16, r = n%16,
-q = (k%32)//8, i = k%8, even i in the low nibble.  Scale block b is 128 bytes
-at the same index: int4 keeps the bf16 of (n, k//32) at byte (r*4 + t)*2;
-NVFP4 keeps the e4m3 of (n, k//16) at byte (((k%32)//16)*16 + r)*4 + t.
-Record = gate[I,H] | up[I,H] | down[H,I] payloads, then their scales in the
-same order.
+into tiles of 16 rows x 32 inputs, tile index (n // 16) * (Kd // 32) + k // 32
+(row slices outer, inputs inner).  A tile's 256 payload bytes hold element
+(n, k) at byte (q*16 + r)*4 + i//2 with r = n%16, q = (k%32)//8, i = k%8, even
+i in the low nibble.  Each tile has 32 scale bytes at the same index in the
+scale area: int4 keeps the bf16 of (n, k//32) at byte r*2; NVFP4 keeps the
+e4m3 of (n, k//16) at byte ((k%32)//16)*16 + r.  Record = gate[I,H] | up[I,H] |
+down[H,I] payloads, then their scales in the same order.
 """
 from __future__ import annotations
 
@@ -84,21 +83,22 @@ def matrix_shape(m: int, H: int, I: int):
     return (H, I) if m == 2 else (I, H)
 
 
-def payload_index(N: int, n: np.ndarray, k: np.ndarray):
+def tile_index(Kd: int, n: np.ndarray, k: np.ndarray) -> np.ndarray:
+    return (n // 16) * (Kd // 32) + k // 32
+
+
+def payload_index(Kd: int, n: np.ndarray, k: np.ndarray):
     """(byte offset within the matrix payload, nibble shift 0|4) of elements (n, k)."""
-    kb, nb = k // 32, n // 64
-    blk = kb * (N // 64) + nb
-    t, r, q, i = (n % 64) // 16, n % 16, (k % 32) // 8, k % 8
-    return blk * 1024 + t * 256 + (q * 16 + r) * 4 + i // 2, (i % 2) * 4
+    r, q, i = n % 16, (k % 32) // 8, k % 8
+    return tile_index(Kd, n, k) * 256 + (q * 16 + r) * 4 + i // 2, (i % 2) * 4
 
 
-def scale_index(fmt: int, N: int, n: np.ndarray, k: np.ndarray) -> np.ndarray:
+def scale_index(fmt: int, Kd: int, n: np.ndarray, k: np.ndarray) -> np.ndarray:
     """Byte offset within the matrix scale area of the scale that covers (n, k)."""
-    base = ((k // 32) * (N // 64) + n // 64) * 128
-    t, r = (n % 64) // 16, n % 16
+    base = tile_index(Kd, n, k) * 32
     if fmt == INT4:
-        return base + (r * 4 + t) * 2
-    return base + (((k % 32) // 16) * 16 + r) * 4 + t
+        return base + (n % 16) * 2
+    return base + ((k % 32) // 16) * 16 + n % 16
 
 
 def dequant_matrix(rec: np.ndarray, fmt: int, H: int, I: int, m: int, ts: float = 1.0) -> np.ndarray:
@@ -109,9 +109,9 @@ def dequant_matrix(rec: np.ndarray, fmt: int, H: int, I: int, m: int, ts: float 
     pay = rec[m * (H * I // 2):(m + 1) * (H * I // 2)]
     sca = rec[3 * (H * I // 2) + m * (H * I // 16): 3 * (H * I // 2) + (m + 1) * (H * I // 16)]
     n, k = np.meshgrid(np.arange(N, dtype=np.int64), np.arange(Kd, dtype=np.int64), indexing="ij")
-    off, sh = payload_index(N, n, k)
+    off, sh = payload_index(Kd, n, k)
     code = (pay[off].astype(np.int64) >> sh) & 15
-    so = scale_index(fmt, N, n, k)
+    so = scale_index(fmt, Kd, n, k)
     if fmt == INT4:
         sbits = sca[so].astype(np.uint16) | (sca[so + 1].astype(np.uint16) << 8)
         return int4_value(code).astype(np.float64) * bf16_bits_to_f64(sbits)

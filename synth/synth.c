@@ -20,14 +20,13 @@
  *   gate payload [I x H] | up payload [I x H] | down payload [H x I] |
  *   gate scales | up scales | down scales
  * The tensor order follows the expert record of the NVMe streaming page
- * ("엔진", item 1).  Each matrix (N output rows, Kd input columns, N % 64 == 0,
- * Kd % 32 == 0) is cut into 1 KiB payload blocks of 64 rows x 32 columns,
- * ordered block = kb * (N / 64) + nb with kb = k / 32, nb = n / 64.  Inside a
- * block, element (n, k) sits at byte t * 256 + (q * 16 + r) * 4 + i / 2 with
- * t = (n % 64) / 16, r = n % 16, q = (k % 32) / 8, i = k % 8; even i in the
- * low nibble (each 16-row slice t is a contiguous 256 bytes).  Each payload block has a 128-byte scale block at the same
- * index: int4 -> bf16 scale of (n, k / 32) at (r * 4 + t) * 2; NVFP4 -> e4m3
- * scale of (n, k / 16) at (((k % 32) / 16) * 16 + r) * 4 + t.
+ * ("엔진", item 1).  Each matrix (N output rows, Kd input columns, N % 16 == 0,
+ * Kd % 32 == 0) is cut into tiles of 16 rows x 32 inputs, tile index
+ * (n / 16) * (Kd / 32) + k / 32 (row slices outer, inputs inner).  A tile's 256
+ * payload bytes hold element (n, k) at byte (q * 16 + r) * 4 + i / 2 with
+ * r = n % 16, q = (k % 32) / 8, i = k % 8, even i in the low nibble.  Its 32
+ * scale bytes (scale area, same tile index): int4 -> bf16 scale of (n, k / 32)
+ * at r * 2; NVFP4 -> e4m3 scale of (n, k / 16) at ((k % 32) / 16) * 16 + r.
  */
 #include <math.h>
 #include <pthread.h>
@@ -134,8 +133,8 @@ static inline uint8_t e2m1_encode(double v) {
 
 /* ---------------------------------------------------------------- record layout (writer side) */
 
-static inline int64_t scale_block_off(int64_t N, int64_t n, int64_t k) {
-  return ((k / 32) * (N / 64) + n / 64) * 128;
+static inline int64_t scale_tile_off(int64_t Kd, int64_t n, int64_t k) {
+  return ((n / 16) * (Kd / 32) + k / 32) * 32;
 }
 
 int64_t synth_record_bytes(int64_t H, int64_t I) { return 3 * H * I / 2 + 3 * H * I / 16; }
@@ -151,11 +150,11 @@ void synth_weights_f32(uint64_t seed, int64_t E, int64_t l, int64_t e, int m, in
 }
 
 /* Store the 32 codes of inputs 32*kb .. 32*kb+31 of row n (one chunk) into the payload. */
-static inline void put_chunk(uint8_t* pay, int64_t N, int64_t n, int64_t kb, const uint8_t* codes) {
-  int64_t blk = kb * (N / 64) + n / 64;
-  int64_t t = (n % 64) / 16, r = n % 16;
+static inline void put_chunk(uint8_t* pay, int64_t Kd, int64_t n, int64_t kb, const uint8_t* codes) {
+  int64_t tile = (n / 16) * (Kd / 32) + kb;
+  int64_t r = n % 16;
   for (int q = 0; q < 4; ++q) {
-    uint8_t* dst = pay + blk * 1024 + t * 256 + (q * 16 + r) * 4;
+    uint8_t* dst = pay + tile * 256 + (q * 16 + r) * 4;
     for (int j = 0; j < 4; ++j)
       dst[j] = (uint8_t)((codes[q * 8 + 2 * j] & 15) | ((codes[q * 8 + 2 * j + 1] & 15) << 4));
   }
@@ -175,7 +174,7 @@ static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_
         uint16_t sbits = f32_to_bf16_rne((float)(amax / 7.0));
         double s = (double)bf16_to_f32(sbits);
         if (!(s > 0.0)) { sbits = 0x3F80; s = 1.0; } /* all-zero group: codes 8 -> 0.0 */
-        int64_t so = scale_block_off(N, n, g * 32) + ((n % 16) * 4 + (n % 64) / 16) * 2;
+        int64_t so = scale_tile_off(Kd, n, g * 32) + (n % 16) * 2;
         memcpy(sc + so, &sbits, 2);
         const double inv = 1.0 / s;
         for (int i = 0; i < 32; ++i) {
@@ -184,7 +183,7 @@ static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_
           if (qd > 7) qd = 7;
           codes[i] = (uint8_t)((int)qd + 8);
         }
-        put_chunk(pay, N, n, g, codes);
+        put_chunk(pay, Kd, n, g, codes);
       }
     }
     *tensor_scale = 1.0f;
@@ -203,7 +202,7 @@ static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_
           uint8_t sb = e4m3_encode_pos(bmax / (6.0 * (double)ts));
           double sv = e4m3_value(sb) * (double)ts;
           int64_t k0 = g * 32 + h * 16;
-          int64_t so = scale_block_off(N, n, k0) + (((k0 % 32) / 16) * 16 + (n % 16)) * 4 + (n % 64) / 16;
+          int64_t so = scale_tile_off(Kd, n, k0) + ((k0 % 32) / 16) * 16 + (n % 16);
           sc[so] = sb;
           if (sv > 0.0) {
             const double inv = 1.0 / sv;
@@ -212,7 +211,7 @@ static void encode_matrix(const float* w, int64_t N, int64_t Kd, int fmt, uint8_
             for (int i = 0; i < 16; ++i) codes[h * 16 + i] = 0;
           }
         }
-        put_chunk(pay, N, n, g, codes);
+        put_chunk(pay, Kd, n, g, codes);
       }
     }
   }
@@ -262,7 +261,7 @@ static void* fill_worker(void* arg) {
 /* Fill `count` consecutive records starting at flat id `first` (= layer * E + expert). */
 int synth_fill_records(uint64_t seed, int64_t E, int64_t H, int64_t I, int fmt, double sigma,
                        int64_t first, int64_t count, uint8_t* pool, float* ts, int nthreads) {
-  if (H % 64 || I % 64 || nthreads < 1) return -1;
+  if (H % 64 || I % 64 || nthreads < 1) return -1; /* 32 | inputs, 16 | rows, and the library's 64 */
   fill_job J;
   J.seed = seed; J.E = E; J.H = H; J.I = I; J.first = first; J.count = count;
   J.R = synth_record_bytes(H, I); J.fmt = fmt; J.sigma = sigma; J.pool = pool; J.ts = ts; J.next = 0;

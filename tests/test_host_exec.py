@@ -1,0 +1,53 @@
+"""The library's host executor (the host share of a decode step) against the oracle, on the
+CPU: entries with a host id get y = W_d(silu(W_g x) * W_u x) from the pool, others untouched.
+Built from the library's own host_exec.cpp with a small shim (no GPU needed)."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import cffn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = [os.path.join(ROOT, "expert_ffn_serving_amd", "csrc", "host_exec.cpp"),
+       os.path.join(ROOT, "tests", "native", "host_exec_shim.cpp")]
+
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    so = str(tmp_path_factory.mktemp("shim") / "libhostshim.so")
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    subprocess.check_call([hipcc, "-O2", "-std=c++17", "-mavx2", "-mfma", "-fPIC", "-shared", "-o", so] + SRC)
+    lib = ctypes.CDLL(so)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.shim_host_ffn.argtypes = [i, i, i, i, i, i, vp, vp, i, vp, vp, i, vp, i]
+    return lib
+
+
+@pytest.mark.parametrize("fmt,H,I,E,K,B", [(synth.FMT_INT4, 64, 128, 8, 2, 3), (synth.FMT_INT4, 256, 128, 8, 4, 5),
+                                           (synth.FMT_NVFP4, 128, 192, 8, 3, 4), (synth.FMT_NVFP4, 320, 128, 6, 2, 2)])
+def test_host_executor_matches_oracle(shim, fmt, H, I, E, K, B):
+    L, layer = 2, 1
+    pool, ts = synth.pool_numpy(41, L, E, H, I, fmt)
+    x = synth.activations(41, layer, 0, B, H)
+    rng = np.random.default_rng(fmt * 100 + H)
+    ids = np.stack([rng.choice(E, K, replace=False) for _ in range(B)]).astype(np.int32)
+    cpu = ids.reshape(-1).copy()
+    cpu[rng.random(cpu.size) < 0.3] = -1            # those entries belong to the GPU
+    y = np.full((B, K, H), 7.0, np.float32)
+    shim.shim_host_ffn(L, E, K, H, I, fmt, pool.ctypes.data, ts.ctypes.data, layer, x.ctypes.data, cpu.ctypes.data,
+                       B, y.ctypes.data, 4)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for p, e in enumerate(cpu):
+        b, k = divmod(p, K)
+        if e < 0:
+            assert np.all(y[b, k] == 7.0)      # GPU-owned entries are not written
+            continue
+        ref = cffn.expert_ffn_batch([(pool[layer * E + e], ts[layer * E + e], xf[b:b + 1])], fmt, H, I, 1)[0][0]
+        err = np.linalg.norm(y[b, k] - ref) / np.linalg.norm(ref)
+        assert err < 1e-5, (p, e, err)

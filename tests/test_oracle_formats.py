@@ -133,24 +133,27 @@ def test_negative_control_swapped_nibbles_fails(fmt):
     assert np.linalg.norm(w - wq_bad) / np.linalg.norm(w) > 0.5
 
 
-def test_negative_control_transposed_block_fails():
-    """Reading rows and columns of a 64x32 block the other way round must fail the round trip."""
+def test_negative_control_transposed_tiles_fail():
+    """Reading the tiles inputs-outer (instead of row slices outer) must fail the round trip."""
     H, I = 64, 128
     rec, ts, outs = _roundtrip(F.INT4, H, I)
-    w, wq = outs[0]
+    w = outs[0][0]
     N, Kd = w.shape
     n, k = np.meshgrid(np.arange(N), np.arange(Kd), indexing="ij")
-    off, sh = F.payload_index(N, n, k)
-    # swap the roles of t (row group) and q (column group) inside each block
-    t, r, q, i = (n % 64) // 16, n % 16, (k % 32) // 8, k % 8
-    off_bad = (off - (t * 256 + (q * 16 + r) * 4)) + q * 256 + (t * 16 + r) * 4
-    codes = (rec[off_bad].astype(np.int64) >> sh) & 15
-    assert not np.array_equal(codes, (rec[off].astype(np.int64) >> sh) & 15)
+    _, sh = F.payload_index(Kd, n, k)
+    r, q, i = n % 16, (k % 32) // 8, k % 8
+    off_bad = ((k // 32) * (N // 16) + n // 16) * 256 + (q * 16 + r) * 4 + i // 2
+    codes_bad = (rec[off_bad].astype(np.int64) >> sh) & 15
+    sca = rec[3 * H * I // 2:]
+    so = F.scale_index(F.INT4, Kd, n, k)
+    s = F.bf16_bits_to_f64(sca[so].astype(np.uint16) | (sca[so + 1].astype(np.uint16) << 8))
+    bad = F.int4_value(codes_bad) * s
+    assert np.linalg.norm(bad - w) / np.linalg.norm(w) > 0.5
 
 
 def test_layout_is_a_bijection():
     for (N, Kd) in [(128, 64), (64, 128), (640, 2560)]:
         n, k = np.meshgrid(np.arange(N), np.arange(Kd), indexing="ij")
-        off, sh = F.payload_index(N, n, k)
+        off, sh = F.payload_index(Kd, n, k)
         lin = off * 2 + sh // 4
         assert np.array_equal(np.sort(lin.reshape(-1)), np.arange(N * Kd))
