@@ -18,7 +18,7 @@ namespace eff {
 
 constexpr int kMaxTokens = 32;        // decode batch bound
 constexpr int kMaxTopK = 32;
-constexpr int kMaxEntries = kMaxTokens * kMaxTopK;  // entries of one decode call
+constexpr int kMaxEntries = 512;     // entries (B*K) of one decode call
 constexpr int kMaxSlots = 16384;      // single-workgroup victim sort (keys in LDS)
 constexpr int kMaxExperts = 4096;
 
@@ -42,6 +42,7 @@ struct Pending {
   int64_t floor_;      // victims need usage < floor_
   int32_t nuniq, nmiss;
   int32_t ids[kMaxEntries];    // routed expert ids of the call
+  int32_t slot[kMaxEntries];   // slot of each entry after the ensure (hits), else -1
   int32_t uniq[kMaxEntries];   // unique ids ascending
   int32_t miss[kMaxEntries];   // unique missing ids ascending
 };
@@ -149,6 +150,9 @@ struct eff_engine {
   int32_t* h_cpu = nullptr;       // [maxB*K] host-mapped
   uint16_t* h_x_dev = nullptr;    // device views of the two above
   int32_t* h_cpu_dev = nullptr;
+  uint64_t* h_ready = nullptr;    // host-mapped word the control kernel sets to the call's sequence number
+  uint64_t* h_ready_dev = nullptr;
+  uint64_t ready_seq = 0;
   float* h_yhost = nullptr;       // [maxB*K*H]
 
   // prefill scratch
@@ -199,7 +203,7 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
                              float* y, hipStream_t s, bool plan_ready = false);
 hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s);
 hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
-                          const int32_t* spec_ids, hipStream_t s);
+                          const int32_t* spec_ids, uint64_t seq, hipStream_t s);
 // timing hooks: returns the call's event slot (or -1 when timing is off); mark(i) records event i
 int timing_begin(eff_engine* e, int kind, hipStream_t s);
 void timing_mark(eff_engine* e, int slot, int i, hipStream_t s);
@@ -208,7 +212,7 @@ hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* 
 hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int32_t* ids,
                           const float* w, int T, uint16_t* out, const int32_t* slot_of_expert,
                           int slot_base, bool combine, hipStream_t s);
-hipError_t split_kernel_setup(int S);
+hipError_t split_kernel_setup(int S, int E);
 hipError_t decode_kernels_setup(int fmt, int maxB, int I);
 int decode_nt(int maxB);
 int64_t qstar_host(int64_t m, int64_t f);

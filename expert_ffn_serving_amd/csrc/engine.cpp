@@ -1,5 +1,7 @@
 // libeff host side: engine lifecycle, the C ABI entry points, the eager decode-layer
 // orchestration and prefill streaming.
+#include <immintrin.h>
+
 #include <algorithm>
 #include <chrono>
 #include <cstdio>
@@ -39,6 +41,7 @@ static int validate(const eff_config* c, std::string* why) {
   if (c->wformat != EFF_WFMT_INT4_G32_BF16 && c->wformat != EFF_WFMT_NVFP4_G16_E4M3) return bad("unknown wformat");
   if (c->num_slots < 0 || c->num_slots > kMaxSlots) return bad("num_slots must be in [0, 16384]");
   if (c->max_tokens < 1 || c->max_tokens > kMaxTokens) return bad("max_tokens must be in [1, 32]");
+  if (c->max_tokens * c->top_k > kMaxEntries) return bad("max_tokens * top_k must be <= 512");
   if (c->max_prefill_tokens < 0) return bad("max_prefill_tokens must be >= 0");
   if (c->fetch_frac_q16 > 65536u) return bad("fetch_frac_q16 must be in [0, 65536]");
   if (c->host_threads < 0 || c->host_threads > 256) return bad("host_threads must be in [0, 256]");
@@ -64,7 +67,7 @@ static void release(eff_engine* e) {
                  e->d_pf_a, e->d_pf_y, e->d_pf_meta, e->d_pf_slot_of, e->d_pf_experts};
   for (void* p : dev)
     if (p) (void)hipFree(p);
-  void* host[] = {e->h_fetch, e->h_x, e->h_cpu, e->h_yhost, e->h_pf_ids, e->h_pf_meta};
+  void* host[] = {e->h_fetch, e->h_x, e->h_cpu, e->h_ready, e->h_yhost, e->h_pf_ids, e->h_pf_meta};
   for (void* p : host)
     if (p) (void)hipHostFree(p);
   hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0], e->ev_pf_done[1]};
@@ -93,7 +96,9 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(dalloc(&e->d_fetch, 2));
   EFF_HIP_TRY(dalloc(&e->d_err, 1));
   EFF_HIP_TRY(dalloc(&e->d_stats, ST_COUNT));
-  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_fetch, 2 * sizeof(FetchList), hipHostMallocMapped));
+  // host-mapped control words are coherent (fine-grained): the host reads them while kernels run
+  const unsigned mapped = hipHostMallocMapped | hipHostMallocCoherent;
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_fetch, 2 * sizeof(FetchList), mapped));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_fetch_dev, e->h_fetch, 0));
   // decode scratch
   e->maxU = (int)std::min<int64_t>(B * K, E);
@@ -111,10 +116,13 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(dalloc(&e->d_logits, std::max(B, T) * E));
   EFF_HIP_TRY(dalloc(&e->d_ygpu, B * K * H));
   EFF_HIP_TRY(dalloc(&e->d_yhost, B * K * H));
-  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_x, (size_t)(B * H) * 2, hipHostMallocMapped));
-  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_cpu, (size_t)(B * K) * 4, hipHostMallocMapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_x, (size_t)(B * H) * 2, mapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_cpu, (size_t)(B * K) * 4, mapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_ready, 64, mapped));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_x_dev, e->h_x, 0));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_cpu_dev, e->h_cpu, 0));
+  EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_ready_dev, e->h_ready, 0));
+  *reinterpret_cast<volatile uint64_t*>(e->h_ready) = 0;
   EFF_HIP_TRY(hipHostMalloc((void**)&e->h_yhost, (size_t)(B * K * H) * 4, 0));
   // prefill
   if (T > 0) {
@@ -143,7 +151,7 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipMemset(e->d_err, 0, 4));
   EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
   std::memset(e->h_fetch, 0, 2 * sizeof(FetchList));
-  EFF_HIP_TRY(split_kernel_setup((int)S));
+  EFF_HIP_TRY(split_kernel_setup((int)S, (int)E));
   EFF_HIP_TRY(decode_kernels_setup(c.wformat, (int)B, (int)I));
   EFF_HIP_TRY(hipDeviceSynchronize());
   return EFF_OK;
@@ -425,6 +433,27 @@ int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const in
   return EFF_OK;
 }
 
+// Wait until the control kernel has published call `seq` (host ids, fetch list, x) to host-mapped
+// memory.  Spins on the ready word; checks the stream now and then so that a failed launch or a
+// kernel fault ends the wait with an error instead of a hang.
+static int wait_ready(eff_engine* e, uint64_t seq, hipStream_t cs) {
+  volatile uint64_t* ready = e->h_ready;
+  for (uint64_t spin = 1;; ++spin) {
+    if (*ready == seq) break;
+    if ((spin & 1023) == 0) {
+      const hipError_t q = hipStreamQuery(cs);
+      if (q == hipSuccess) {  // the stream drained: the word must be there now
+        if (*ready == seq) break;
+        return fail(EFF_EHIP, "control kernel finished without publishing its call");
+      }
+      if (q != hipErrorNotReady) return fail(EFF_EHIP, std::string("control kernel: ") + hipGetErrorString(q));
+    }
+    _mm_pause();
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  return EFF_OK;
+}
+
 int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_router, const float* logits, int B,
                      const int32_t* spec_ids, void* out, eff_stream_t compute, eff_stream_t side) {
   if (int rc = check_engine(e)) return rc;
@@ -444,11 +473,12 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   // top-K, ensure, split, the speculative request and the decode plan in one workgroup; the
   // fetch list, host ids and x land in host-mapped memory
   const bool spec = spec_ids && layer + 1 < c.num_layers;
-  EFF_HIP_TRY(launch_control(e, layer, lg, B, (const uint16_t*)x, spec ? spec_ids : nullptr, cs));
+  const uint64_t seq = ++e->ready_seq;
+  EFF_HIP_TRY(launch_control(e, layer, lg, B, (const uint16_t*)x, spec ? spec_ids : nullptr, seq, cs));
   e->real_split_pending = true;
   if (spec) e->spec_split_pending = true;
   const double t0 = now_ms();
-  EFF_HIP_TRY(hipStreamSynchronize(cs));  // the one wait of the layer
+  if (int rc = wait_ready(e, seq, cs)) return rc;  // the one wait of the layer
   e->wait_ms += now_ms() - t0;
   if (int rc = issue_pending_copies(e, cs, ss)) return rc;
   EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true));

@@ -5,6 +5,8 @@
 // computes q, picks victims and rewrites ids to a slot or the host marker;
 // [FT-deep] §4 design pattern ② explains why: the miss count exists only on the
 // device while the decode step is captured).
+#include <algorithm>
+
 #include "eff_internal.h"
 
 namespace eff {
@@ -41,85 +43,91 @@ struct CacheState {
   int sort_pow2;
 };
 
-// LDS the control bodies need besides the dynamic key buffer.
-struct SplitLds {
-  int32_t ranked[kMaxEntries];
-  int32_t victim[kMaxEntries];
-  int32_t mid[kMaxEntries];
-  int64_t mrec[kMaxEntries];
+// Barrier for data exchanged through LDS only: waits for this wave's LDS accesses, not for its
+// global stores (those are committed together at the end of a call and need no barrier).
+__device__ inline void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One ensure + split call, kept in LDS.  The call reads the slot state from device memory and
+// writes every change in one commit at the end.
+struct CallLds {
+  int32_t id[kMaxEntries];      // expert id of each entry (-1: invalid)
+  int32_t hit[kMaxEntries];     // slot the ensure found (resident), else -1
+  int32_t slot[kMaxEntries];    // the partition after the split
+  int32_t first[kMaxEntries];   // entry is the first with its id
+  int32_t uniq[kMaxEntries];    // unique valid ids, ascending
+  int32_t miss[kMaxEntries];    // unique missing ids, ascending
+  int32_t ranked[kMaxEntries];  // misses by (recency desc, id asc)
+  int32_t victim[kMaxEntries];  // victims by (usage, slot)
+  int32_t vold[kMaxEntries];    // previous owner of each victim
+  int64_t mrec[kMaxEntries];    // recency of each miss
   uint64_t red[kThreads / 64];
-  int nv;
+  int64_t s, floor_;
+  int layer, n, spec, nu, nm, nv, qq, err;
 };
 
-// ensure: dedup, residency, hits stamped at this step, ids rewritten to slot-or--1, call kept
-// pending.  scratch: 3 * kMaxEntries int32 of LDS (free outside this body).
-__device__ void ensure_body(const CacheState& c, int layer, int32_t* __restrict__ ids, int n, int spec,
-                            int32_t* scratch) {
-  int32_t* s_id = scratch;
-  int32_t* s_slot = scratch + kMaxEntries;
-  int32_t* s_first = scratch + 2 * kMaxEntries;
-  __shared__ int64_t s_step, s_floor;
-  __shared__ int s_nu, s_nm;
+__device__ inline void stat_add(int64_t* p, int64_t v) {
+  atomicAdd(reinterpret_cast<unsigned long long*>(p), (unsigned long long)v);
+}
+
+// first[p]: entry p is the first one with its (valid) id.
+__device__ inline void mark_first(CallLds& C, int n) {
+  for (int p = threadIdx.x; p < n; p += kThreads) {
+    const int id = C.id[p];
+    int f = id >= 0;
+    for (int q = 0; q < p && f; ++q) f = C.id[q] != id;
+    C.first[p] = f;
+  }
+}
+
+// ensure: dedup and residency ([FT-deep] §4 ⑤; [FT-blog] §六).  In: C.id[0..n).  Out, in LDS:
+// C.hit, C.first, C.uniq, C.miss, step and floor.  Reads the table; writes nothing to memory.
+__device__ void ensure_body(const CacheState& c, int layer, int n, int spec, CallLds& C) {
   const int tid = threadIdx.x, E = c.E;
   if (tid == 0) {
-    s_step = c.clock[0] + 1;
-    s_floor = spec ? c.clock[1] : s_step;
-    s_nu = 0;
-    s_nm = 0;
+    const int64_t s = c.clock[0] + 1;
+    C.s = s;
+    C.floor_ = spec ? c.clock[1] : s;
+    C.nu = 0;
+    C.nm = 0;
+    C.layer = layer;
+    C.n = n;
+    C.spec = spec;
+    C.err = 0;
   }
   for (int p = tid; p < n; p += kThreads) {
-    int v = ids[p];
+    int v = C.id[p];
     if (v < 0 || v >= E) {
-      atomicOr(c.err, 1);
+      atomicOr(&C.err, 1);
       v = -1;
+      C.id[p] = -1;
     }
-    s_id[p] = v;
-    s_slot[p] = (v >= 0) ? c.table[(int64_t)layer * E + v] : -1;
+    C.hit[p] = (v >= 0) ? c.table[(int64_t)layer * E + v] : -1;
   }
-  __syncthreads();
+  lds_sync();
+  mark_first(C, n);
+  lds_sync();
   for (int p = tid; p < n; p += kThreads) {
-    int id = s_id[p], first = id >= 0;
-    for (int q = 0; q < p && first; ++q) first = (s_id[q] != id);
-    s_first[p] = first;
-  }
-  __syncthreads();
-  const int64_t s = s_step;
-  for (int p = tid; p < n; p += kThreads) {
-    if (!s_first[p]) continue;
-    int id = s_id[p], ru = 0, rm = 0;
-    bool miss = s_slot[p] < 0;
+    if (!C.first[p]) continue;
+    const int id = C.id[p];
+    int ru = 0, rm = 0;
     for (int q = 0; q < n; ++q) {
-      if (!s_first[q]) continue;
-      int o = s_id[q];
-      ru += (o < id);
-      rm += (o < id) && (s_slot[q] < 0);
+      if (!C.first[q]) continue;
+      const int o = C.id[q];
+      ru += o < id;
+      rm += (o < id) && (C.hit[q] < 0);
     }
-    c.pd->uniq[ru] = id;
-    if (miss) {
-      c.pd->miss[rm] = id;
-      atomicAdd(&s_nm, 1);
-    } else {
-      c.usage[s_slot[p]] = s;  // hit: stamped as used now
+    C.uniq[ru] = id;
+    if (C.hit[p] < 0) {
+      C.miss[rm] = id;
+      atomicAdd(&C.nm, 1);
     }
-    atomicAdd(&s_nu, 1);
+    atomicAdd(&C.nu, 1);
   }
-  for (int p = tid; p < n; p += kThreads) {
-    c.pd->ids[p] = s_id[p];
-    ids[p] = s_slot[p];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    c.clock[0] = s;
-    c.pd->valid = 1;
-    c.pd->layer = layer;
-    c.pd->n = n;
-    c.pd->spec = spec;
-    c.pd->s = s;
-    c.pd->floor_ = s_floor;
-    c.pd->nuniq = s_nu;
-    c.pd->nmiss = s_nm;
-  }
-  __syncthreads();
+  lds_sync();
 }
 
 // Block-wide min of a 64-bit key; every thread gets the result.
@@ -130,217 +138,368 @@ __device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* s_red) {
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) s_red[wave] = v;
-  __syncthreads();
+  lds_sync();
   uint64_t r = s_red[0];
   for (int i = 1; i < kThreads / 64; ++i) r = s_red[i] < r ? s_red[i] : r;
-  __syncthreads();
+  lds_sync();
   return r;
 }
 
-// split: q*, recency ranking, LRU victims, installs, the -1 partition, recency and counts.
-// cpu_host (may be null): a host-mapped copy of cpu_ids.  s_key: sort_pow2 uint64 of LDS.
-__device__ void split_body(const CacheState& c, int32_t* __restrict__ ids_out, int32_t* __restrict__ cpu_out,
-                           int32_t* __restrict__ cpu_host, int32_t* __restrict__ counts, SplitLds& L,
-                           uint64_t* s_key) {
+// split: q*, recency ranking, LRU victims and the -1 partition, computed in LDS (C.victim,
+// C.ranked, C.vold, C.qq, C.slot).  Reads recency, usage and owner; writes nothing to memory.
+// The call's hit slots are never victims (their stamp of this step is committed later).
+// s_key: sort_pow2 uint64 of LDS.
+__device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key) {
   const int tid = threadIdx.x;
-  Pending* pd = c.pd;
-  if (!pd->valid) {
-    if (tid == 0) atomicOr(c.err, 2);
-    return;
-  }
   const int E = c.E, S = c.S;
-  const int layer = pd->layer, n = pd->n, spec = pd->spec, m = pd->nmiss, nu = pd->nuniq;
-  const int64_t s = pd->s, floor_ = pd->floor_;
-  const int64_t base = (int64_t)layer * E;
+  const int n = C.n, m = C.nm;
+  const int64_t floor_ = C.floor_;
+  const int64_t base = (int64_t)C.layer * E;
   const int q = (int)qstar_dev(m, c.f);
-
   int qq = 0;
   if (q > 0) {
-    // Misses ranked by (recency desc, id asc) ([FT-deep] §4 ⑤: prefer recently active experts).
-    for (int i = tid; i < m; i += kThreads) {
-      int e = pd->miss[i];
-      L.mid[i] = e;
-      L.mrec[i] = c.recency[base + e];
-    }
-    if (tid == 0) L.nv = 0;
-    __syncthreads();
-    for (int i = tid; i < m; i += kThreads) {
-      int e = L.mid[i];
-      int64_t r = L.mrec[i];
-      int rank = 0;
-      for (int j = 0; j < m; ++j) {
-        int o = L.mid[j];
-        int64_t ro = L.mrec[j];
-        rank += (ro > r) || (ro == r && o < e);
-      }
-      L.ranked[rank] = e;
-    }
-    // Victim keys: slots with usage below the floor, ordered by (usage, slot).
+    if (tid == 0) C.nv = 0;
+    lds_sync();
+    // the misses' recency and the victim keys, loaded together
+    for (int i = tid; i < m; i += kThreads) C.mrec[i] = c.recency[base + C.miss[i]];
     int local_nv = 0;
     for (int v = tid; v < c.sort_pow2; v += kThreads) {
       uint64_t key = kInfKey;
       if (v < S) {
-        int64_t u = c.usage[v];
-        if (u < floor_) {
+        const int64_t u = c.usage[v];
+        if (u < floor_) {  // slots with usage below the floor, ordered by (usage, slot)
           key = ((uint64_t)(u + 1) << 14) | (uint64_t)v;
           ++local_nv;
         }
       }
       s_key[v] = key;
     }
-    if (local_nv) atomicAdd(&L.nv, local_nv);
-    __syncthreads();
-    qq = min(q, L.nv);
+    if (local_nv) atomicAdd(&C.nv, local_nv);
+    lds_sync();
+    for (int p = tid; p < n; p += kThreads) {
+      const int v = C.hit[p];
+      if (C.first[p] && v >= 0 && v < S && s_key[v] != kInfKey) {
+        s_key[v] = kInfKey;
+        atomicSub(&C.nv, 1);
+      }
+    }
+    // Misses ranked by (recency desc, id asc) ([FT-deep] §4 ⑤: prefer recently active experts).
+    for (int i = tid; i < m; i += kThreads) {
+      const int e = C.miss[i];
+      const int64_t r = C.mrec[i];
+      int rank = 0;
+      for (int j = 0; j < m; ++j) {
+        const int o = C.miss[j];
+        const int64_t ro = C.mrec[j];
+        rank += (ro > r) || (ro == r && o < e);
+      }
+      C.ranked[rank] = e;
+    }
+    lds_sync();
+    qq = min(q, C.nv);
     if (qq > 0 && qq <= 16) {
       // few fetches: qq rounds of block-wide argmin
       for (int i = 0; i < qq; ++i) {
         uint64_t lm = kInfKey;
         for (int v = tid; v < S; v += kThreads) lm = s_key[v] < lm ? s_key[v] : lm;
-        uint64_t g = block_min_u64(lm, L.red);
-        int v = (int)(g & 0x3FFF);
+        const uint64_t g = block_min_u64(lm, C.red);
+        const int v = (int)(g & 0x3FFF);
         if (tid == 0) {
-          L.victim[i] = v;
+          C.victim[i] = v;
           s_key[v] = kInfKey;
         }
-        __syncthreads();
+        lds_sync();
       }
     } else if (qq > 16) {
       // many fetches: bitonic sort of all keys (ascending)
       for (int k = 2; k <= c.sort_pow2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
           for (int i = tid; i < c.sort_pow2; i += kThreads) {
-            int ixj = i ^ j;
+            const int ixj = i ^ j;
             if (ixj > i) {
-              uint64_t a = s_key[i], b = s_key[ixj];
-              bool up = (i & k) == 0;
+              const uint64_t a = s_key[i], b = s_key[ixj];
+              const bool up = (i & k) == 0;
               if ((a > b) == up) {
                 s_key[i] = b;
                 s_key[ixj] = a;
               }
             }
           }
-          __syncthreads();
+          lds_sync();
         }
       }
-      for (int i = tid; i < qq; i += kThreads) L.victim[i] = (int)(s_key[i] & 0x3FFF);
-      __syncthreads();
+      for (int i = tid; i < qq; i += kThreads) C.victim[i] = (int)(s_key[i] & 0x3FFF);
+      lds_sync();
     }
+    for (int i = tid; i < qq; i += kThreads) C.vold[i] = c.owner[C.victim[i]];
   }
-  // Installs: i-th ranked miss -> i-th oldest victim.
+  // The -1 partition ([FT-deep] §4 ③): i-th ranked miss -> i-th victim; hits keep their slot.
+  for (int p = tid; p < n; p += kThreads) {
+    const int id = C.id[p];
+    int slot = C.hit[p];
+    if (slot < 0 && id >= 0)
+      for (int i = 0; i < qq; ++i)
+        if (C.ranked[i] == id) {
+          slot = C.victim[i];
+          break;
+        }
+    C.slot[p] = slot;
+  }
+  if (tid == 0) C.qq = qq;
+  lds_sync();
+}
+
+// Commit a call: hit stamps (when stamp_hits), installs, the fetch list, outputs, recency,
+// clocks, counts and stats.  Host-mapped outputs (cpu_host, the fetch list mirror) are written
+// by wave 0 only, so that one wave's system fence publishes them.  All arrays may be null.
+__device__ void commit_body(const CacheState& c, const CallLds& C, bool stamp_hits, int32_t* __restrict__ slots_out,
+                            int32_t* __restrict__ cpu_out, int32_t* __restrict__ cpu_host,
+                            int32_t* __restrict__ counts) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = C.n, spec = C.spec, m = C.nm, nu = C.nu, qq = C.qq;
+  const int64_t s = C.s, base = (int64_t)C.layer * c.E;
   FetchList* fl = c.fl_dev + (spec ? 1 : 0);
   FetchList* flh = c.fl_host + (spec ? 1 : 0);
+  if (stamp_hits)
+    for (int p = tid; p < n; p += kThreads)
+      if (C.first[p] && C.hit[p] >= 0) c.usage[C.hit[p]] = s;  // hit: stamped as used now
   for (int i = tid; i < qq; i += kThreads) {
-    int v = L.victim[i], e = L.ranked[i];
-    int old = c.owner[v];
+    const int v = C.victim[i], e = C.ranked[i], old = C.vold[i];
     if (old >= 0) c.table[old] = -1;
     c.owner[v] = (int32_t)(base + e);
     c.table[base + e] = v;
     c.usage[v] = s;
     fl->flat[i] = (int32_t)(base + e);
     fl->slot[i] = v;
-    flh->flat[i] = (int32_t)(base + e);
-    flh->slot[i] = v;
   }
-  __syncthreads();
-  // The -1 partition ([FT-deep] §4 ③): GPU owns entries with a slot, the host the rest.
   for (int p = tid; p < n; p += kThreads) {
-    int id = pd->ids[p];
-    int slot = (id >= 0) ? c.table[base + id] : -1;
-    ids_out[p] = slot;
-    const int cpu = (!spec && slot < 0 && id >= 0) ? id : -1;
-    if (cpu_out) cpu_out[p] = cpu;
-    if (cpu_host) cpu_host[p] = cpu;
+    const int slot = C.slot[p], id = C.id[p];
+    if (slots_out) slots_out[p] = slot;
+    if (cpu_out) cpu_out[p] = (!spec && slot < 0 && id >= 0) ? id : -1;
   }
   if (!spec)
-    for (int u = tid; u < nu; u += kThreads) c.recency[base + pd->uniq[u]] = s;
-  __syncthreads();
+    for (int u = tid; u < nu; u += kThreads) c.recency[base + C.uniq[u]] = s;
+  if (wave == 0) {
+    for (int i = lane; i < qq; i += 64) {
+      flh->flat[i] = (int32_t)(base + C.ranked[i]);
+      flh->slot[i] = C.victim[i];
+    }
+    if (cpu_host)
+      for (int p = lane; p < n; p += 64) {
+        const int slot = C.slot[p], id = C.id[p];
+        cpu_host[p] = (!spec && slot < 0 && id >= 0) ? id : -1;
+      }
+  }
   if (tid == 0) {
+    c.clock[0] = s;
     if (!spec) c.clock[1] = s;
     if (counts) {
       counts[0] = m;
       counts[1] = qq;
       counts[2] = spec ? 0 : m - qq;
     }
+    const int err = C.err | atomicExch(c.err, 0);
     fl->count = qq;
     flh->count = qq;
-    fl->err = *c.err;
-    flh->err = *c.err;
-    *c.err = 0;
-    pd->valid = 0;
-    c.stats[ST_CALLS] += 1;
+    fl->err = err;
+    flh->err = err;
+    c.pd->valid = 0;
+    stat_add(&c.stats[ST_CALLS], 1);
     if (spec) {
-      c.stats[ST_SPEC_FETCHED] += qq;
+      stat_add(&c.stats[ST_SPEC_FETCHED], qq);
     } else {
-      c.stats[ST_HITS] += nu - m;
-      c.stats[ST_FETCHED] += qq;
-      c.stats[ST_HOST] += m - qq;
-      c.stats[ST_HIST0 + (qq < 16 ? qq : 16)] += 1;
+      stat_add(&c.stats[ST_HITS], nu - m);
+      stat_add(&c.stats[ST_FETCHED], qq);
+      stat_add(&c.stats[ST_HOST], m - qq);
+      stat_add(&c.stats[ST_HIST0 + (qq < 16 ? qq : 16)], 1);
     }
   }
-  __syncthreads();
 }
 
-__device__ inline bool better(float a, int ia, float b, int ib) { return a > b || (a == b && ia < ib); }
+// The call, kept in device memory between a separate ensure and split.
+__device__ void store_pending(const CacheState& c, const CallLds& C) {
+  const int tid = threadIdx.x;
+  Pending* pd = c.pd;
+  for (int p = tid; p < C.n; p += kThreads) {
+    pd->ids[p] = C.id[p];
+    pd->slot[p] = C.hit[p];
+  }
+  for (int u = tid; u < C.nu; u += kThreads) pd->uniq[u] = C.uniq[u];
+  for (int u = tid; u < C.nm; u += kThreads) pd->miss[u] = C.miss[u];
+  if (tid == 0) {
+    pd->valid = 1;
+    pd->layer = C.layer;
+    pd->n = C.n;
+    pd->spec = C.spec;
+    pd->s = C.s;
+    pd->floor_ = C.floor_;
+    pd->nuniq = C.nu;
+    pd->nmiss = C.nm;
+    if (C.err) atomicOr(c.err, C.err);
+  }
+}
 
-// top-K of one logits row by (logit desc, id asc) and the softmax of the K selected, by one wave.
-// sel: kMaxTopK floats of LDS for this wave.
+// Returns false (and flags the error) when no ensure is pending.
+__device__ bool load_pending(const CacheState& c, CallLds& C) {
+  const int tid = threadIdx.x;
+  const Pending* pd = c.pd;
+  __shared__ int s_ok;
+  if (tid == 0) {
+    s_ok = pd->valid;
+    C.layer = pd->layer;
+    C.n = pd->n;
+    C.spec = pd->spec;
+    C.s = pd->s;
+    C.floor_ = pd->floor_;
+    C.nu = pd->nuniq;
+    C.nm = pd->nmiss;
+    C.err = 0;
+  }
+  lds_sync();
+  if (!s_ok) {
+    if (tid == 0) atomicOr(c.err, 2);
+    return false;
+  }
+  for (int p = tid; p < C.n; p += kThreads) {
+    C.id[p] = pd->ids[p];
+    C.hit[p] = pd->slot[p];
+  }
+  for (int u = tid; u < C.nu; u += kThreads) C.uniq[u] = pd->uniq[u];
+  for (int u = tid; u < C.nm; u += kThreads) C.miss[u] = pd->miss[u];
+  lds_sync();
+  mark_first(C, C.n);
+  lds_sync();
+  return true;
+}
+
+// Whole-wave reductions on DPP row operations (no LDS crossbar): the result is read from lane 63
+// and is the same on every lane.  Lanes outside a DPP source row contribute the identity.
+template <bool MAX>
+__device__ inline uint32_t wave_reduce_u32(uint32_t v) {
+  constexpr int kId = MAX ? 0 : -1;
+#define EFF_DPP_STEP(ctrl, rmask)                                                              \
+  {                                                                                            \
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, ctrl, rmask, 0xF, false); \
+    v = MAX ? (o > v ? o : v) : (o < v ? o : v);                                               \
+  }
+  EFF_DPP_STEP(0xB1, 0xF)   // quad_perm [1,0,3,2]
+  EFF_DPP_STEP(0x4E, 0xF)   // quad_perm [2,3,0,1]
+  EFF_DPP_STEP(0x124, 0xF)  // row_ror:4
+  EFF_DPP_STEP(0x128, 0xF)  // row_ror:8  (every lane of a row holds the row's result)
+  EFF_DPP_STEP(0x142, 0xA)  // row_bcast:15 into rows 1, 3
+  EFF_DPP_STEP(0x143, 0xC)  // row_bcast:31 into rows 2, 3
+#undef EFF_DPP_STEP
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ inline float wave_sum_f32(float v) {
+#define EFF_DPP_ADD(ctrl, rmask) \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xF, false));
+  EFF_DPP_ADD(0xB1, 0xF)
+  EFF_DPP_ADD(0x4E, 0xF)
+  EFF_DPP_ADD(0x124, 0xF)
+  EFF_DPP_ADD(0x128, 0xF)
+  EFF_DPP_ADD(0x142, 0xA)
+  EFF_DPP_ADD(0x143, 0xC)
+#undef EFF_DPP_ADD
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Order-preserving key of a float (larger value -> larger key; -0 is taken as +0).
+__device__ inline uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// top-K of one logits row by (logit desc, id asc) and the softmax of the K selected, by one
+// wave.  Lane l holds experts l, l+64, ... (E <= 64*NJ) as order keys in registers; each of the
+// K rounds takes the wave's largest key, then the lowest id holding it.  NJ = 0: E up to 4096,
+// the row is re-read from memory in each round.  lds_ids (may be null) receives the ids too.
+// Logits must not be NaN.
+template <int NJ>
 __device__ void wave_topk(const float* __restrict__ row, int E, int K, int32_t* __restrict__ ids,
-                          float* __restrict__ w, float* sel) {
+                          float* __restrict__ w, int32_t* lds_ids) {
   const int lane = threadIdx.x & 63;
+  uint32_t key[NJ > 0 ? NJ : 1];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? order_key(row[e]) : 0u;
+  }
   uint64_t taken = 0;  // element lane + 64*j is taken when bit j is set
+  float mysel = 0.f;   // lane k keeps the k-th selected logit
+  int myid = 0;
   for (int k = 0; k < K; ++k) {
-    float bv = 0.f;
-    int bi = 0x7FFFFFFF;
-    int j = 0;
-    for (int e = lane; e < E; e += 64, ++j) {
-      if ((taken >> j) & 1) continue;
-      const float v = row[e];
-      if (bi == 0x7FFFFFFF || better(v, e, bv, bi)) {
-        bv = v;
-        bi = e;
+    uint32_t best = 0u;
+    int bj = -1;
+    if (NJ > 0) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bool ok = !((taken >> j) & 1) && key[j] > best;
+        best = ok ? key[j] : best;
+        bj = ok ? j : bj;
+      }
+    } else {
+      int j = 0;
+      for (int e = lane; e < E; e += 64, ++j) {
+        const uint32_t kj = order_key(row[e]);
+        const bool ok = !((taken >> j) & 1) && kj > best;
+        best = ok ? kj : best;
+        bj = ok ? j : bj;
       }
     }
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
-    if (lane == 0) {
-      sel[k] = bv;
-      ids[k] = bi;
+    const uint32_t m = wave_reduce_u32<true>(best);
+    const uint32_t cand = (bj >= 0 && best == m) ? (uint32_t)(bj * 64 + lane) : 0xFFFFFFFFu;
+    const int id = (int)wave_reduce_u32<false>(cand);
+    if ((id & 63) == lane) taken |= 1ull << (id >> 6);
+    if (lane == k) {
+      mysel = key_value(m);
+      myid = id;
     }
   }
-  if (lane == 0) {
-    // softmax over the K selected logits, relative to the largest
-    float sum = 0.f;
-    for (int k = 0; k < K; ++k) sum += expf(sel[k] - sel[0]);
-    for (int k = 0; k < K; ++k) w[k] = expf(sel[k] - sel[0]) / sum;
+  // softmax over the K selected logits, relative to the largest (lane 0's)
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mysel), 0));
+  const float ex = lane < K ? expf(mysel - top) : 0.f;
+  const float sum = wave_sum_f32(ex);
+  if (lane < K) {
+    ids[lane] = myid;
+    w[lane] = ex / sum;
+    if (lds_ids) lds_ids[lane] = myid;
   }
 }
 
-// decode plan (distinct GPU slots and their entries), by one workgroup; scratch: 2*kMaxEntries.
-__device__ void plan_body(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB,
-                          const int32_t* __restrict__ owner, DecodePlan* plan, int32_t* scratch) {
+__device__ inline void topk_row(const float* row, int E, int K, int32_t* ids, float* w, int32_t* lds_ids) {
+  if (E <= 256) wave_topk<4>(row, E, K, ids, w, lds_ids);
+  else if (E <= 512) wave_topk<8>(row, E, K, ids, w, lds_ids);
+  else if (E <= 1024) wave_topk<16>(row, E, K, ids, w, lds_ids);
+  else wave_topk<0>(row, E, K, ids, w, lds_ids);
+}
+
+// Decode plan (distinct GPU slots and their entries) by one workgroup, from the entries' slots
+// in LDS.  flat id of a unit: base + lds_id[p] when ids are known, else owner[slot].
+// scratch: 2*kMaxEntries int32 of LDS.
+__device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, int64_t base,
+                          const int32_t* __restrict__ owner, int n, int S, int maxU, int maxB, DecodePlan* plan,
+                          int32_t* scratch) {
   int32_t* s_sl = scratch;
   int32_t* s_first = scratch + kMaxEntries;
   __shared__ int s_nu;
   const int tid = threadIdx.x;
   if (tid == 0) s_nu = 0;
   for (int p = tid; p < n; p += blockDim.x) {
-    const int v = slots[p];
+    const int v = lds_slot[p];
     s_sl[p] = (v >= 0 && v < S) ? v : -1;  // slots outside the arena are never read
   }
-  __syncthreads();
+  lds_sync();
   for (int p = tid; p < n; p += blockDim.x) {
     int v = s_sl[p], first = v >= 0;
     for (int q = 0; q < p && first; ++q) first = s_sl[q] != v;
     s_first[p] = first;
   }
-  __syncthreads();
+  lds_sync();
   for (int p = tid; p < n; p += blockDim.x) {
     if (!s_first[p]) continue;
     int v = s_sl[p], rank = 0, cnt = 0;
@@ -351,10 +510,10 @@ __device__ void plan_body(const int32_t* __restrict__ slots, int n, int S, int m
       if (s_sl[q] == v) un.entry[cnt++] = q;
     un.slot = v;
     un.count = cnt;
-    un.flat = owner[v];
+    un.flat = lds_id ? (int32_t)(base + lds_id[p]) : owner[v];
     atomicAdd(&s_nu, 1);
   }
-  __syncthreads();
+  lds_sync();
   const int nu = min(s_nu, maxU);
   for (int u = nu + tid; u < maxU; u += blockDim.x) {
     plan->unit[u].count = 0;
@@ -362,68 +521,89 @@ __device__ void plan_body(const int32_t* __restrict__ slots, int n, int S, int m
     plan->unit[u].flat = 0;
   }
   if (tid == 0) plan->nu = nu;
-  __syncthreads();
+  lds_sync();
 }
 
 __global__ void __launch_bounds__(kThreads)
 k_ensure(CacheState c, int layer, int32_t* __restrict__ ids, int n, int spec) {
-  __shared__ int32_t scratch[3 * kMaxEntries];
-  ensure_body(c, layer, ids, n, spec, scratch);
+  __shared__ CallLds C;
+  for (int p = threadIdx.x; p < n; p += kThreads) C.id[p] = ids[p];
+  lds_sync();
+  ensure_body(c, layer, n, spec, C);
+  for (int p = threadIdx.x; p < n; p += kThreads) {
+    ids[p] = C.hit[p];
+    if (C.first[p] && C.hit[p] >= 0) c.usage[C.hit[p]] = C.s;  // hit: stamped as used now
+  }
+  if (threadIdx.x == 0) c.clock[0] = C.s;
+  store_pending(c, C);
 }
 
 __global__ void __launch_bounds__(kThreads)
 k_split(CacheState c, int32_t* __restrict__ ids_out, int32_t* __restrict__ cpu_out, int32_t* __restrict__ counts) {
   extern __shared__ uint64_t s_key[];
-  __shared__ SplitLds L;
-  split_body(c, ids_out, cpu_out, nullptr, counts, L, s_key);
+  __shared__ CallLds C;
+  if (!load_pending(c, C)) return;
+  split_body(c, C, s_key);
+  commit_body(c, C, false, ids_out, cpu_out, nullptr, counts);
 }
 
 __global__ void __launch_bounds__(kThreads)
 k_topk(const float* __restrict__ logits, int B, int E, int K, int32_t* __restrict__ ids, float* __restrict__ w) {
-  __shared__ float s_sel[kThreads / 64][kMaxTopK];
   const int wave = threadIdx.x >> 6;
   for (int t = blockIdx.x * (kThreads / 64) + wave; t < B; t += gridDim.x * (kThreads / 64))
-    wave_topk(logits + (int64_t)t * E, E, K, ids + (int64_t)t * K, w + (int64_t)t * K, s_sel[wave]);
+    topk_row(logits + (int64_t)t * E, E, K, ids + (int64_t)t * K, w + (int64_t)t * K, nullptr);
 }
 
 __global__ void __launch_bounds__(kThreads)
 k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, const int32_t* __restrict__ owner,
        DecodePlan* plan) {
+  __shared__ int32_t s_slot[kMaxEntries];
   __shared__ int32_t scratch[2 * kMaxEntries];
-  plan_body(slots, n, S, maxU, maxB, owner, plan, scratch);
+  for (int p = threadIdx.x; p < n; p += kThreads) s_slot[p] = slots[p];
+  lds_sync();
+  plan_body(s_slot, nullptr, 0, owner, n, S, maxU, maxB, plan, scratch);
 }
 
 // One decode layer's control path in one workgroup: top-K of the B logits rows, ensure, split,
-// (speculative ensure + split of the next layer), the decode plan, and the host's inputs
-// (host ids and x) written to host-mapped memory.
+// the decode plan, the commit, (speculative ensure + split + commit for the next layer), and the
+// host's inputs (host ids, fetch lists, x) in host-mapped memory.  Last, wave 0 (the only wave
+// that writes host-mapped memory) fences at system scope and stores `seq` to the host-mapped
+// `ready` word, so the host can poll it.
 __global__ void __launch_bounds__(kThreads)
 k_control(CacheState c, const float* __restrict__ logits, int B, int K, int layer, int32_t* __restrict__ ids,
           float* __restrict__ w, int32_t* __restrict__ slots, int32_t* __restrict__ cpu, int32_t* __restrict__ counts,
           const int32_t* __restrict__ spec_ids, int32_t* __restrict__ spec_slots, int32_t* __restrict__ cpu_host,
           const uint16_t* __restrict__ x, uint16_t* __restrict__ x_host, int H, int maxU, int maxB,
-          DecodePlan* plan) {
-  extern __shared__ uint64_t s_key[];  // victim keys; also scratch for ensure and plan
-  __shared__ SplitLds L;
-  __shared__ float s_sel[kThreads / 64][kMaxTopK];
-  const int tid = threadIdx.x, wave = tid >> 6;
+          DecodePlan* plan, uint64_t* ready, uint64_t seq) {
+  extern __shared__ uint64_t s_key[];  // victim keys, plan scratch
+  __shared__ CallLds C;
+  const int tid = threadIdx.x;
   const int n = B * K;
-  for (int t = wave; t < B; t += kThreads / 64)
-    wave_topk(logits + (int64_t)t * c.E, c.E, K, ids + (int64_t)t * K, w + (int64_t)t * K, s_sel[wave]);
-  __syncthreads();
-  for (int p = tid; p < n; p += kThreads) slots[p] = ids[p];
-  // the host's copy of x travels while the control path runs (16 bytes per thread)
-  for (int i = tid; i < B * H / 8; i += kThreads)
-    reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
-  __syncthreads();
-  ensure_body(c, layer, slots, n, 0, reinterpret_cast<int32_t*>(s_key));
-  split_body(c, slots, cpu, cpu_host, counts, L, s_key);
+  for (int t = tid >> 6; t < B; t += kThreads / 64)
+    topk_row(logits + (int64_t)t * c.E, c.E, K, ids + (int64_t)t * K, w + (int64_t)t * K, C.id + t * K);
+  lds_sync();
+  ensure_body(c, layer, n, 0, C);
+  split_body(c, C, s_key);
+  plan_body(C.slot, C.id, (int64_t)layer * c.E, c.owner, n, c.S, maxU, maxB, plan,
+            reinterpret_cast<int32_t*>(s_key));
+  commit_body(c, C, true, slots, cpu, cpu_host, counts);
   if (spec_ids) {
-    for (int p = tid; p < n; p += kThreads) spec_slots[p] = spec_ids[p];
-    __syncthreads();
-    ensure_body(c, layer + 1, spec_slots, n, 1, reinterpret_cast<int32_t*>(s_key));
-    split_body(c, spec_slots, nullptr, nullptr, counts + 3, L, s_key);
+    __syncthreads();  // the real call's commit is visible to the speculative ensure
+    for (int p = tid; p < n; p += kThreads) C.id[p] = spec_ids[p];
+    lds_sync();
+    ensure_body(c, layer + 1, n, 1, C);
+    split_body(c, C, s_key);
+    commit_body(c, C, true, spec_slots, nullptr, nullptr, counts + 3);
   }
-  plan_body(slots, n, c.S, maxU, maxB, c.owner, plan, reinterpret_cast<int32_t*>(s_key));
+  if (tid < 64) {
+    // the host's copy of x, then the ready word after a system-scope fence
+    for (int i = tid; i < B * H / 8; i += 64)
+      reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
+    if (ready) {
+      __threadfence_system();
+      if (tid == 0) __hip_atomic_store(ready, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
 }
 
 __global__ void k_qstar_batch(const int32_t* __restrict__ m, const uint32_t* __restrict__ f,
@@ -523,10 +703,10 @@ static CacheState state_of(eff_engine* e) {
   return c;
 }
 
-static size_t control_lds(int S) {
-  const size_t keys = (size_t)sort_pow2_of(S) * sizeof(uint64_t);
-  const size_t scratch = (size_t)3 * kMaxEntries * sizeof(int32_t);
-  return keys > scratch ? keys : scratch;
+// dynamic LDS of the control kernel: victim keys and the plan scratch
+static size_t control_lds(int S, int E) {
+  (void)E;
+  return std::max((size_t)sort_pow2_of(S) * sizeof(uint64_t), (size_t)2 * kMaxEntries * sizeof(int32_t));
 }
 
 hipError_t launch_ensure(eff_engine* e, int layer, int32_t* ids, int n, int spec, hipStream_t s) {
@@ -557,21 +737,23 @@ hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s
 }
 
 hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
-                          const int32_t* spec_ids, hipStream_t s) {
+                          const int32_t* spec_ids, uint64_t seq, hipStream_t s) {
   const eff_config& cf = e->cfg;
-  hipLaunchKernelGGL(k_control, dim3(1), dim3(kThreads), control_lds(cf.num_slots), s, state_of(e), logits, B,
+  const size_t lds = control_lds(cf.num_slots, cf.num_experts);
+  hipLaunchKernelGGL(k_control, dim3(1), dim3(kThreads), lds, s, state_of(e), logits, B,
                      cf.top_k, layer, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, spec_ids,
-                     e->d_spec_ids, e->h_cpu_dev, x, e->h_x_dev, cf.hidden, e->maxU, cf.max_tokens, e->d_plan);
+                     e->d_spec_ids, e->h_cpu_dev, x, e->h_x_dev, cf.hidden, e->maxU, cf.max_tokens, e->d_plan,
+                     e->h_ready_dev, seq);
   return hipGetLastError();
 }
 
-hipError_t split_kernel_setup(int S) {
+hipError_t split_kernel_setup(int S, int E) {
   const int P = sort_pow2_of(S);
   hipError_t err = hipFuncSetAttribute((const void*)k_split, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)(P * sizeof(uint64_t)));
   if (err != hipSuccess) return err;
   return hipFuncSetAttribute((const void*)k_control, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)control_lds(S));
+                             (int)control_lds(S, E));
 }
 
 hipError_t launch_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, int n, hipStream_t s) {

@@ -363,18 +363,31 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
 }
 
 // ---------------------------------------------------------------------------- combine
+// out[t, h] = sum over k (ascending) of w[t,k] * y[t,k,h], y from the GPU or the host buffer by the
+// entry's slot (slots == nullptr: all from yg).  All loads of a thread are issued before any use.
+template <int KMAX>
 __global__ void __launch_bounds__(256)
 k_combine(const float* __restrict__ yg, const float* __restrict__ yh, const int32_t* __restrict__ slots,
           const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out) {
   const int t = blockIdx.y;
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
-  float acc = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int p = t * K + k;
-    const float* src = (slots == nullptr || slots[p] >= 0) ? yg : yh;
-    acc = fmaf(w[p], src[(int64_t)p * H + h], acc);
+  float vg[KMAX], vh[KMAX], wk[KMAX];
+  int sk[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (k < K) {
+      const int64_t p = (int64_t)t * K + k;
+      wk[k] = w[p];
+      sk[k] = slots ? slots[p] : 0;
+      vg[k] = yg[p * H + h];
+      vh[k] = yh ? yh[p * H + h] : 0.f;
+    }
   }
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+    if (k < K) acc = fmaf(wk[k], sk[k] >= 0 ? vg[k] : vh[k], acc);
   uint32_t b = __float_as_uint(acc);
   b += 0x7FFFu + ((b >> 16) & 1u);  // round to nearest even
   out[(int64_t)t * H + h] = (uint16_t)(b >> 16);
@@ -442,7 +455,13 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
 hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
                           int B, int K, int H, uint16_t* out, hipStream_t s) {
   dim3 g((H + 255) / 256, B);
-  hipLaunchKernelGGL(k_combine, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out);
+  if (!slots) yhost = nullptr;
+  if (K <= 8)
+    hipLaunchKernelGGL(k_combine<8>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out);
+  else if (K <= 16)
+    hipLaunchKernelGGL(k_combine<16>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out);
+  else
+    hipLaunchKernelGGL(k_combine<kMaxTopK>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out);
   return hipGetLastError();
 }
 

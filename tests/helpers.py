@@ -5,6 +5,8 @@ from __future__ import annotations
 
 import ctypes
 
+import os
+
 import numpy as np
 
 import synth
@@ -47,10 +49,21 @@ def bf16_to_f64(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+# worst rel-L2 / max-abs seen per test, printed at the end of the session (tests/conftest.py)
+OBSERVED = {}
+
+
+def record_error(err, mx):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    e0, m0, n0 = OBSERVED.get(test, (0.0, 0.0, 0))
+    OBSERVED[test] = (max(e0, err), max(m0, mx), n0 + 1)
+
+
 def assert_close_bf16(got_bits, ref_bits, rel=REL_L2, mabs=MAX_ABS, what=""):
     g, r = bf16_to_f64(got_bits), bf16_to_f64(ref_bits)
     err = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
     mx = float(np.max(np.abs(g - r))) if g.size else 0.0
+    record_error(err, mx)
     assert err <= rel and mx <= mabs, "%s rel-L2 %.3e (<= %.1e) max-abs %.3e (<= %.1e)" % (what, err, rel, mx, mabs)
     return err, mx
 
