@@ -22,6 +22,7 @@ INT4_G32_BF16 = 0
 NVFP4_G16_E4M3 = 1
 SPECULATIVE = 1
 CFG_TIMING = 1
+CFG_SYNC_HOST = 2
 T_DECODE_GATEUP, T_DECODE_DOWN, T_PREFILL_GATEUP, T_PREFILL_DOWN = 0, 1, 2, 3
 
 EFF_OK, EFF_EINVAL, EFF_ENOMEM, EFF_EHIP, EFF_ECAPTURE, EFF_ESTATE, EFF_EDEVICE = 0, -1, -2, -3, -4, -5, -6

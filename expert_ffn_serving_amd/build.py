@@ -23,7 +23,8 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]
 # packed fp32 instructions stay disabled in device code
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
-HOST_CPU = ["-mavx2", "-mfma", "-mf16c"]
+# host-only translation units (no kernels): no device pass
+HOST_CPU = ["--offload-arch=" + ARCH, "--cuda-host-only", "-mavx2", "-mfma", "-mf16c"]
 
 
 def _hipcc() -> str:

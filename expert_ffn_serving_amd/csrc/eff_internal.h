@@ -62,7 +62,8 @@ struct DecodeUnit {
   int32_t slot;
   int32_t count;
   int32_t flat;                  // layer * E + expert held by the slot (tensor scales)
-  int32_t pad;
+  int32_t fetch;                 // 1: installed by this call; the FFN kernels read the record
+                                 //    from the host pool and write it into the slot
   int32_t entry[kMaxTokens];     // entry p = t*K + k, ascending
 };
 struct DecodePlan {
@@ -70,6 +71,14 @@ struct DecodePlan {
   int32_t pad[3];
   DecodeUnit unit[kMaxEntries];
 };
+
+// Decode calls publish (seq << 16 | host entries) in a host-mapped ring of words ------------------
+constexpr int kCallRing = 256;
+struct HostJob {
+  uint64_t seq;
+  int32_t layer, B;
+};
+constexpr int kJobRing = 4096;
 
 // Device stats counters (int64) ----------------------------------------------------------------
 enum { ST_CALLS, ST_HITS, ST_FETCHED, ST_HOST, ST_SPEC_FETCHED, ST_HIST0, ST_COUNT = ST_HIST0 + 17 };
@@ -150,10 +159,26 @@ struct eff_engine {
   int32_t* h_cpu = nullptr;       // [maxB*K] host-mapped
   uint16_t* h_x_dev = nullptr;    // device views of the two above
   int32_t* h_cpu_dev = nullptr;
-  uint64_t* h_ready = nullptr;    // host-mapped word the control kernel sets to the call's sequence number
-  uint64_t* h_ready_dev = nullptr;
+  uint64_t* h_call = nullptr;     // host-mapped ring [kCallRing]: seq << 16 | host entries, per call
+  uint64_t* h_call_dev = nullptr;
+  uint64_t* h_done = nullptr;     // host-mapped: the last call whose host share is in h_yhost
+  uint64_t* h_done_dev = nullptr;
   uint64_t ready_seq = 0;
-  float* h_yhost = nullptr;       // [maxB*K*H]
+  float* h_yhost = nullptr;       // [maxB*K*H] host-mapped: the host share's outputs
+  float* h_yhost_dev = nullptr;
+  const uint8_t* pool_dev = nullptr;  // device view of the pinned pool (in-kernel fetches)
+  bool async_host = false;        // host share on the worker thread, the stream waits on h_done
+  bool spec_copy_pending = false; // a speculative copy on the side stream not yet waited for
+  hipEvent_t ev_ctl = nullptr;
+  // host-share worker (async mode)
+  std::thread worker;
+  std::vector<eff::HostJob> jobs;
+  std::atomic<uint64_t> job_head{0}, job_tail{0};
+  std::atomic<bool> worker_stop{false};
+  std::atomic<int> async_err{0};
+  std::mutex async_mu;
+  std::string async_msg;
+  std::atomic<int64_t> host_ns{0}, wait_ns{0}, host_calls_a{0};
 
   // prefill scratch
   int32_t* d_pf_count = nullptr;  // [E+1] per-expert counts / offsets
@@ -176,9 +201,6 @@ struct eff_engine {
   eff::ThreadPool* pool_threads = nullptr;
   // kernel timing (EFF_CFG_TIMING): events (start, end) of each of two kernels per call
   struct TimedCall { int kind; hipEvent_t ev[4]; };
-  double host_ms = 0.0;           // wall time in the host executor
-  double wait_ms = 0.0;           // wall time waiting for the device in the decode path
-  int64_t host_calls = 0;
   std::vector<TimedCall> timed;     // recorded, not yet resolved
   std::vector<hipEvent_t> free_events;
   int64_t t_launches[4] = {0, 0, 0, 0};
@@ -201,6 +223,7 @@ hipError_t launch_fallback_install(eff_engine* e, int layer, const int32_t* expe
                                    hipStream_t s);
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
                              float* y, hipStream_t s, bool plan_ready = false);
+hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s);
 hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s);
 hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
                           const int32_t* spec_ids, uint64_t seq, hipStream_t s);

@@ -45,7 +45,7 @@ static int validate(const eff_config* c, std::string* why) {
   if (c->max_prefill_tokens < 0) return bad("max_prefill_tokens must be >= 0");
   if (c->fetch_frac_q16 > 65536u) return bad("fetch_frac_q16 must be in [0, 65536]");
   if (c->host_threads < 0 || c->host_threads > 256) return bad("host_threads must be in [0, 256]");
-  if (c->flags & ~(uint32_t)EFF_CFG_TIMING) return bad("unknown config flags");
+  if (c->flags & ~(uint32_t)(EFF_CFG_TIMING | EFF_CFG_SYNC_HOST)) return bad("unknown config flags");
   if ((int64_t)c->num_layers * c->num_experts > (int64_t)1 << 30) return bad("L*E too large");
   return EFF_OK;
 }
@@ -59,18 +59,21 @@ static hipError_t dalloc(T** p, size_t count) {
   return hipMalloc((void**)p, std::max<size_t>(1, count) * sizeof(T));
 }
 
+static void stop_worker(eff_engine* e);
+
 static void release(eff_engine* e) {
   if (!e) return;
+  stop_worker(e);
   void* dev[] = {e->d_arena, e->d_table, e->d_owner, e->d_usage, e->d_recency, e->d_clock, e->d_ts,
                  e->d_pending, e->d_fetch, e->d_err, e->d_stats, e->d_plan, e->d_a, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, e->d_spec_ids,
                  e->d_spec_cpu, e->d_logits, e->d_ygpu, e->d_yhost, e->d_pf_count, e->d_pf_rows,
                  e->d_pf_a, e->d_pf_y, e->d_pf_meta, e->d_pf_slot_of, e->d_pf_experts};
   for (void* p : dev)
     if (p) (void)hipFree(p);
-  void* host[] = {e->h_fetch, e->h_x, e->h_cpu, e->h_ready, e->h_yhost, e->h_pf_ids, e->h_pf_meta};
+  void* host[] = {e->h_fetch, e->h_x, e->h_cpu, e->h_call, e->h_done, e->h_yhost, e->h_pf_ids, e->h_pf_meta};
   for (void* p : host)
     if (p) (void)hipHostFree(p);
-  hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0], e->ev_pf_done[1]};
+  hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_ctl, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0], e->ev_pf_done[1]};
   for (hipEvent_t v : evs)
     if (v) (void)hipEventDestroy(v);
   for (auto& tc : e->timed)
@@ -118,12 +121,16 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(dalloc(&e->d_yhost, B * K * H));
   EFF_HIP_TRY(hipHostMalloc((void**)&e->h_x, (size_t)(B * H) * 2, mapped));
   EFF_HIP_TRY(hipHostMalloc((void**)&e->h_cpu, (size_t)(B * K) * 4, mapped));
-  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_ready, 64, mapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_call, kCallRing * sizeof(uint64_t), mapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_done, 64, mapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_yhost, (size_t)(B * K * H) * 4, mapped));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_x_dev, e->h_x, 0));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_cpu_dev, e->h_cpu, 0));
-  EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_ready_dev, e->h_ready, 0));
-  *reinterpret_cast<volatile uint64_t*>(e->h_ready) = 0;
-  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_yhost, (size_t)(B * K * H) * 4, 0));
+  EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_call_dev, e->h_call, 0));
+  EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_done_dev, e->h_done, 0));
+  EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_yhost_dev, e->h_yhost, 0));
+  std::memset(e->h_call, 0, kCallRing * sizeof(uint64_t));
+  std::memset(e->h_done, 0, 64);
   // prefill
   if (T > 0) {
     EFF_HIP_TRY(dalloc(&e->d_pf_count, E + 1));
@@ -136,6 +143,7 @@ static int alloc_all(eff_engine* e) {
     EFF_HIP_TRY(hipHostMalloc((void**)&e->h_pf_meta, (size_t)(2 * E) * 4, 0));
   }
   EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_copy, hipEventDisableTiming));
+  EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_ctl, hipEventDisableTiming));
   EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_spec, hipEventDisableTiming));
   for (int b = 0; b < 2; ++b) {
     EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_pf[b], hipEventDisableTiming));
@@ -222,6 +230,119 @@ static int read_device_error(eff_engine* e) {
   return EFF_OK;
 }
 
+
+// ---------------------------------------------------------------------------- host share
+static int64_t ns_since(std::chrono::steady_clock::time_point t) {
+  return std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t).count();
+}
+
+static void set_async_error(eff_engine* e, const std::string& msg) {
+  std::lock_guard<std::mutex> g(e->async_mu);
+  if (!e->async_err.load()) {
+    e->async_msg = msg;
+    e->async_err.store(1, std::memory_order_release);
+  }
+}
+
+static int check_async_error(eff_engine* e) {
+  if (!e->async_err.load(std::memory_order_acquire)) return EFF_OK;
+  std::lock_guard<std::mutex> g(e->async_mu);
+  return fail(EFF_EHIP, "host share of an earlier decode call: " + e->async_msg);
+}
+
+// Waits for the control kernel's word of call `seq`: the number of entries the host computes,
+// 0 when a later call already overwrote the word (only calls without host entries let the
+// device run ahead), or -1 (error recorded) when the word does not come.  With a stream given,
+// the wait also ends when that stream fails or drains without publishing.
+static int wait_call(eff_engine* e, uint64_t seq, hipStream_t cs = nullptr) {
+  const auto t0 = std::chrono::steady_clock::now();
+  volatile uint64_t* word = e->h_call + seq % kCallRing;
+  int nhost = -1;
+  for (uint64_t spin = 1;; ++spin) {
+    const uint64_t w = *word;
+    const uint64_t ws = w >> 16;
+    if (ws == seq) {
+      nhost = (int)(w & 0xFFFF);
+      break;
+    }
+    if (ws > seq) {
+      nhost = 0;
+      break;
+    }
+    if ((spin & 4095) == 0) {
+      if (cs) {
+        const hipError_t q = hipStreamQuery(cs);
+        if (q == hipSuccess && (*word >> 16) < seq) {
+          set_async_error(e, "control kernel finished without publishing its call");
+          break;
+        }
+        if (q != hipSuccess && q != hipErrorNotReady) {
+          set_async_error(e, std::string("control kernel: ") + hipGetErrorString(q));
+          break;
+        }
+      }
+      if (ns_since(t0) > (int64_t)30 * 1000 * 1000 * 1000) {
+        set_async_error(e, "no control kernel result within 30 s");
+        break;
+      }
+    }
+    _mm_pause();
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  e->wait_ns += ns_since(t0);
+  return nhost;
+}
+
+static void run_job(eff_engine* e, const HostJob& job) {
+  const int nhost = wait_call(e, job.seq);
+  if (nhost > 0) {
+    const auto t1 = std::chrono::steady_clock::now();
+    host_ffn(e, job.layer, e->h_x, e->h_cpu, job.B, e->h_yhost);
+    e->host_ns += ns_since(t1);
+    e->host_calls_a += 1;
+  }
+  if (nhost != 0) {  // release the stream's wait (also after an error, so the stream never hangs)
+    std::atomic_thread_fence(std::memory_order_release);
+    __atomic_store_n(e->h_done, job.seq, __ATOMIC_RELEASE);
+  }
+}
+
+static void worker_loop(eff_engine* e) {
+  uint64_t idle = 0;
+  for (;;) {
+    const uint64_t tail = e->job_tail.load(std::memory_order_relaxed);
+    if (tail == e->job_head.load(std::memory_order_acquire)) {
+      if (e->worker_stop.load(std::memory_order_acquire)) break;
+      if (++idle < 100000) _mm_pause();
+      else std::this_thread::sleep_for(std::chrono::microseconds(20));
+      continue;
+    }
+    idle = 0;
+    run_job(e, e->jobs[tail % kJobRing]);
+    e->job_tail.store(tail + 1, std::memory_order_release);
+  }
+}
+
+static void push_job(eff_engine* e, const HostJob& job) {
+  const uint64_t head = e->job_head.load(std::memory_order_relaxed);
+  while (head - e->job_tail.load(std::memory_order_acquire) >= (uint64_t)kJobRing) _mm_pause();
+  e->jobs[head % kJobRing] = job;
+  e->job_head.store(head + 1, std::memory_order_release);
+}
+
+// Waits until the worker has finished every queued call (each waits for its control kernel).
+static void drain_worker(eff_engine* e) {
+  if (!e->async_host) return;
+  while (e->job_tail.load(std::memory_order_acquire) != e->job_head.load(std::memory_order_acquire))
+    std::this_thread::sleep_for(std::chrono::microseconds(20));
+}
+
+static void stop_worker(eff_engine* e) {
+  if (!e->worker.joinable()) return;
+  e->worker_stop.store(true, std::memory_order_release);
+  e->worker.join();
+}
+
 }  // namespace eff
 
 using namespace eff;
@@ -289,6 +410,13 @@ int eff_create(const eff_config* cfg, const void* host_pool, const float* tensor
     release(e);
     return fail(EFF_EHIP, "copying tensor scales failed");
   }
+  void* pdev = nullptr;
+  if (hipHostGetDevicePointer(&pdev, const_cast<void*>(host_pool), 0) != hipSuccess || !pdev) {
+    (void)hipGetLastError();
+    release(e);
+    return fail(EFF_EINVAL, "host_pool is not mapped into the device address space (use eff_host_alloc)");
+  }
+  e->pool_dev = (const uint8_t*)pdev;
   int nth = cfg->host_threads;
   if (nth == 0) nth = (int)std::max(1u, std::thread::hardware_concurrency());
   e->pool_threads = new (std::nothrow) ThreadPool(nth);
@@ -296,12 +424,25 @@ int eff_create(const eff_config* cfg, const void* host_pool, const float* tensor
     release(e);
     return fail(EFF_ENOMEM, "thread pool");
   }
+  int can_wait = 0;
+  if (hipDeviceGetAttribute(&can_wait, hipDeviceAttributeCanUseStreamWaitValue, dev) != hipSuccess) can_wait = 0;
+  e->async_host = can_wait && !(cfg->flags & EFF_CFG_SYNC_HOST);
+  if (e->async_host) {
+    e->jobs.resize(kJobRing);
+    try {
+      e->worker = std::thread(worker_loop, e);
+    } catch (...) {
+      release(e);
+      return fail(EFF_ENOMEM, "host worker thread");
+    }
+  }
   *out = e;
   return EFF_OK;
 }
 
 int eff_destroy(eff_engine* e) {
   if (!e) return EFF_OK;
+  drain_worker(e);
   (void)hipDeviceSynchronize();
   release(e);
   return EFF_OK;
@@ -433,65 +574,60 @@ int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const in
   return EFF_OK;
 }
 
-// Wait until the control kernel has published call `seq` (host ids, fetch list, x) to host-mapped
-// memory.  Spins on the ready word; checks the stream now and then so that a failed launch or a
-// kernel fault ends the wait with an error instead of a hang.
-static int wait_ready(eff_engine* e, uint64_t seq, hipStream_t cs) {
-  volatile uint64_t* ready = e->h_ready;
-  for (uint64_t spin = 1;; ++spin) {
-    if (*ready == seq) break;
-    if ((spin & 1023) == 0) {
-      const hipError_t q = hipStreamQuery(cs);
-      if (q == hipSuccess) {  // the stream drained: the word must be there now
-        if (*ready == seq) break;
-        return fail(EFF_EHIP, "control kernel finished without publishing its call");
-      }
-      if (q != hipErrorNotReady) return fail(EFF_EHIP, std::string("control kernel: ") + hipGetErrorString(q));
-    }
-    _mm_pause();
-  }
-  std::atomic_thread_fence(std::memory_order_acquire);
-  return EFF_OK;
-}
-
 int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_router, const float* logits, int B,
                      const int32_t* spec_ids, void* out, eff_stream_t compute, eff_stream_t side) {
   if (int rc = check_engine(e)) return rc;
+  if (int rc = check_async_error(e)) return rc;
   const eff_config& c = e->cfg;
   if (!x || !out || (!w_router && !logits) || B < 1 || B > c.max_tokens || layer < 0 || layer >= c.num_layers)
     return fail(EFF_EINVAL, "eff_decode_layer: bad arguments");
   if (e->pending_host) return fail(EFF_ESTATE, "an ensure is pending its split");
   hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
-  if (capturing(cs) || capturing(ss)) return fail(EFF_ECAPTURE, "eff_decode_layer waits on the host");
-  const int K = c.top_k, n = B * K;
+  if (!e->async_host && (capturing(cs) || capturing(ss)))
+    return fail(EFF_ECAPTURE, "eff_decode_layer waits on the host (EFF_CFG_SYNC_HOST)");
+  const int K = c.top_k;
   const float* lg = logits;
   if (w_router) {
     EFF_HIP_TRY(launch_route_logits((const uint16_t*)x, (const uint16_t*)w_router, B, c.num_experts, c.hidden,
                                     e->d_logits, cs));
     lg = e->d_logits;
   }
-  // top-K, ensure, split, the speculative request and the decode plan in one workgroup; the
-  // fetch list, host ids and x land in host-mapped memory
+  // top-K, ensure, split, the speculative request and the decode plan in one workgroup; host ids
+  // and x land in host-mapped memory, then the call word
   const bool spec = spec_ids && layer + 1 < c.num_layers;
   const uint64_t seq = ++e->ready_seq;
   EFF_HIP_TRY(launch_control(e, layer, lg, B, (const uint16_t*)x, spec ? spec_ids : nullptr, seq, cs));
-  e->real_split_pending = true;
-  if (spec) e->spec_split_pending = true;
-  const double t0 = now_ms();
-  if (int rc = wait_ready(e, seq, cs)) return rc;  // the one wait of the layer
-  e->wait_ms += now_ms() - t0;
-  if (int rc = issue_pending_copies(e, cs, ss)) return rc;
-  EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true));
-  bool any_host = false;
-  for (int p = 0; p < n; ++p) any_host |= e->h_cpu[p] >= 0;
-  if (any_host) {
-    const double t1 = now_ms();
-    host_ffn(e, layer, e->h_x, e->h_cpu, B, e->h_yhost);  // overlaps the GPU expert kernels
-    e->host_ms += now_ms() - t1;
-    e->host_calls += 1;
-    EFF_HIP_TRY(hipMemcpyAsync(e->d_yhost, e->h_yhost, (size_t)n * c.hidden * 4, hipMemcpyHostToDevice, cs));
+  // the previous layer's speculative copies land before this layer's expert kernels read or
+  // overwrite any slot
+  if (e->spec_copy_pending) {
+    EFF_HIP_TRY(hipStreamWaitEvent(cs, e->ev_spec, 0));
+    e->spec_copy_pending = false;
   }
-  EFF_HIP_TRY(launch_combine(e->d_ygpu, e->d_yhost, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs));
+  if (spec) {  // this layer's speculative fetches travel on the side stream
+    EFF_HIP_TRY(hipEventRecord(e->ev_ctl, cs));
+    EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_ctl, 0));
+    EFF_HIP_TRY(launch_fetch_copy(e, 1, ss));
+    EFF_HIP_TRY(hipEventRecord(e->ev_spec, ss));
+    e->spec_copy_pending = true;
+  }
+  // GPU experts; a unit installed by this call reads its record from the pool and fills its slot
+  EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true));
+  if (e->async_host) {
+    // the combine waits for the host share (or the control kernel's own release of the call)
+    EFF_HIP_TRY(hipStreamWaitValue64(cs, e->h_done_dev, seq, hipStreamWaitValueGte, ~0ull));
+    EFF_HIP_TRY(launch_combine(e->d_ygpu, e->h_yhost_dev, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs));
+    push_job(e, HostJob{seq, layer, B});
+    return EFF_OK;
+  }
+  const int nhost = wait_call(e, seq, cs);
+  if (nhost < 0) return fail(EFF_EHIP, e->async_msg);
+  if (nhost > 0) {
+    const auto t1 = std::chrono::steady_clock::now();
+    host_ffn(e, layer, e->h_x, e->h_cpu, B, e->h_yhost);  // overlaps the GPU expert kernels
+    e->host_ns += ns_since(t1);
+    e->host_calls_a += 1;
+  }
+  EFF_HIP_TRY(launch_combine(e->d_ygpu, e->h_yhost_dev, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs));
   return EFF_OK;
 }
 
@@ -600,6 +736,7 @@ int eff_get_stats(eff_engine* e, eff_stats* out) {
   if (!out) return fail(EFF_EINVAL, "eff_get_stats: out is NULL");
   int64_t st[ST_COUNT];
   EFF_HIP_TRY(hipDeviceSynchronize());
+  drain_worker(e);
   EFF_HIP_TRY(hipMemcpy(st, e->d_stats, sizeof(st), hipMemcpyDeviceToHost));
   std::memset(out, 0, sizeof(*out));
   out->calls = st[ST_CALLS];
@@ -607,22 +744,23 @@ int eff_get_stats(eff_engine* e, eff_stats* out) {
   out->fetched = st[ST_FETCHED];
   out->host = st[ST_HOST];
   out->spec_fetched = st[ST_SPEC_FETCHED];
-  out->bytes_fetched = e->host_bytes_fetched;
+  out->bytes_fetched = (st[ST_FETCHED] + st[ST_SPEC_FETCHED]) * e->R;
   for (int i = 0; i < 17; ++i) out->qstar_hist[i] = st[ST_HIST0 + i];
   resolve_timing(e);
   for (int i = 0; i < 4; ++i) {
     out->launches[i] = e->t_launches[i];
     out->kernel_ms[i] = e->t_ms[i];
   }
-  out->host_ms = e->host_ms;
-  out->wait_ms = e->wait_ms;
-  out->host_calls = e->host_calls;
+  out->host_ms = e->host_ns.load() * 1e-6;
+  out->wait_ms = e->wait_ns.load() * 1e-6;
+  out->host_calls = e->host_calls_a.load();
   return EFF_OK;
 }
 
 int eff_set_flags(eff_engine* e, uint32_t flags) {
   if (int rc = check_engine(e)) return rc;
-  if (flags & ~(uint32_t)EFF_CFG_TIMING) return fail(EFF_EINVAL, "unknown config flags");
+  if (flags & ~(uint32_t)(EFF_CFG_TIMING | EFF_CFG_SYNC_HOST)) return fail(EFF_EINVAL, "unknown config flags");
+  if ((flags ^ e->cfg.flags) & EFF_CFG_SYNC_HOST) return fail(EFF_EINVAL, "EFF_CFG_SYNC_HOST is fixed at create");
   e->cfg.flags = flags;
   return EFF_OK;
 }
@@ -630,6 +768,7 @@ int eff_set_flags(eff_engine* e, uint32_t flags) {
 int eff_reset_stats(eff_engine* e) {
   if (int rc = check_engine(e)) return rc;
   EFF_HIP_TRY(hipDeviceSynchronize());
+  drain_worker(e);
   resolve_timing(e);
   for (int i = 0; i < 4; ++i) {
     e->t_launches[i] = 0;
@@ -637,8 +776,9 @@ int eff_reset_stats(eff_engine* e) {
   }
   e->host_bytes_fetched = 0;
   e->host_spec_fetched = 0;
-  e->host_ms = e->wait_ms = 0.0;
-  e->host_calls = 0;
+  e->host_ns = 0;
+  e->wait_ns = 0;
+  e->host_calls_a = 0;
   EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
   return EFF_OK;
 }

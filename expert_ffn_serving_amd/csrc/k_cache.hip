@@ -479,9 +479,10 @@ __device__ inline void topk_row(const float* row, int E, int K, int32_t* ids, fl
 }
 
 // Decode plan (distinct GPU slots and their entries) by one workgroup, from the entries' slots
-// in LDS.  flat id of a unit: base + lds_id[p] when ids are known, else owner[slot].
-// scratch: 2*kMaxEntries int32 of LDS.
-__device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, int64_t base,
+// in LDS.  flat id of a unit: base + lds_id[p] when ids are known, else owner[slot].  lds_hit
+// (may be null): the slot the ensure found; a unit whose slot was installed by this call
+// (hit < 0) is marked fetch.  scratch: 2*kMaxEntries int32 of LDS.
+__device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, const int32_t* lds_hit, int64_t base,
                           const int32_t* __restrict__ owner, int n, int S, int maxU, int maxB, DecodePlan* plan,
                           int32_t* scratch) {
   int32_t* s_sl = scratch;
@@ -511,6 +512,7 @@ __device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, int64_
     un.slot = v;
     un.count = cnt;
     un.flat = lds_id ? (int32_t)(base + lds_id[p]) : owner[v];
+    un.fetch = (lds_hit && lds_hit[p] < 0) ? 1 : 0;
     atomicAdd(&s_nu, 1);
   }
   lds_sync();
@@ -519,6 +521,7 @@ __device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, int64_
     plan->unit[u].count = 0;
     plan->unit[u].slot = 0;
     plan->unit[u].flat = 0;
+    plan->unit[u].fetch = 0;
   }
   if (tid == 0) plan->nu = nu;
   lds_sync();
@@ -561,20 +564,21 @@ k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, cons
   __shared__ int32_t scratch[2 * kMaxEntries];
   for (int p = threadIdx.x; p < n; p += kThreads) s_slot[p] = slots[p];
   lds_sync();
-  plan_body(s_slot, nullptr, 0, owner, n, S, maxU, maxB, plan, scratch);
+  plan_body(s_slot, nullptr, nullptr, 0, owner, n, S, maxU, maxB, plan, scratch);
 }
 
 // One decode layer's control path in one workgroup: top-K of the B logits rows, ensure, split,
-// the decode plan, the commit, (speculative ensure + split + commit for the next layer), and the
-// host's inputs (host ids, fetch lists, x) in host-mapped memory.  Last, wave 0 (the only wave
-// that writes host-mapped memory) fences at system scope and stores `seq` to the host-mapped
-// `ready` word, so the host can poll it.
+// the decode plan (units installed by this call are fetched by the FFN kernels), the commit,
+// (speculative ensure + split + commit for the next layer), and the host's inputs (host ids, x)
+// in host-mapped memory.  Last, wave 0 (the only wave that writes host-mapped memory) fences at
+// system scope and publishes call_ring[seq % kCallRing] = seq << 16 | host entries; a call with
+// no host entries also sets *host_done = seq itself (nothing for the host to add).
 __global__ void __launch_bounds__(kThreads)
 k_control(CacheState c, const float* __restrict__ logits, int B, int K, int layer, int32_t* __restrict__ ids,
           float* __restrict__ w, int32_t* __restrict__ slots, int32_t* __restrict__ cpu, int32_t* __restrict__ counts,
           const int32_t* __restrict__ spec_ids, int32_t* __restrict__ spec_slots, int32_t* __restrict__ cpu_host,
           const uint16_t* __restrict__ x, uint16_t* __restrict__ x_host, int H, int maxU, int maxB,
-          DecodePlan* plan, uint64_t* ready, uint64_t seq) {
+          DecodePlan* plan, uint64_t* call_ring, uint64_t* host_done, uint64_t seq) {
   extern __shared__ uint64_t s_key[];  // victim keys, plan scratch
   __shared__ CallLds C;
   const int tid = threadIdx.x;
@@ -584,9 +588,15 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
   lds_sync();
   ensure_body(c, layer, n, 0, C);
   split_body(c, C, s_key);
-  plan_body(C.slot, C.id, (int64_t)layer * c.E, c.owner, n, c.S, maxU, maxB, plan,
+  plan_body(C.slot, C.id, C.hit, (int64_t)layer * c.E, c.owner, n, c.S, maxU, maxB, plan,
             reinterpret_cast<int32_t*>(s_key));
   commit_body(c, C, true, slots, cpu, cpu_host, counts);
+  int nhost = 0;  // wave 0: entries of the real call the host computes
+  if (tid < 64)
+    for (int p0 = 0; p0 < n; p0 += 64) {
+      const int p = p0 + tid;
+      nhost += __popcll(__ballot(p < n && C.slot[p] < 0 && C.id[p] >= 0));
+    }
   if (spec_ids) {
     __syncthreads();  // the real call's commit is visible to the speculative ensure
     for (int p = tid; p < n; p += kThreads) C.id[p] = spec_ids[p];
@@ -596,12 +606,16 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
     commit_body(c, C, true, spec_slots, nullptr, nullptr, counts + 3);
   }
   if (tid < 64) {
-    // the host's copy of x, then the ready word after a system-scope fence
+    // the host's copy of x, then the call word after a system-scope fence
     for (int i = tid; i < B * H / 8; i += 64)
       reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
-    if (ready) {
+    if (call_ring) {
       __threadfence_system();
-      if (tid == 0) __hip_atomic_store(ready, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (tid == 0) {
+        __hip_atomic_store(call_ring + seq % kCallRing, (seq << 16) | (uint64_t)nhost, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+        if (nhost == 0) __hip_atomic_store(host_done, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
     }
   }
 }
@@ -743,7 +757,7 @@ hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, 
   hipLaunchKernelGGL(k_control, dim3(1), dim3(kThreads), lds, s, state_of(e), logits, B,
                      cf.top_k, layer, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, spec_ids,
                      e->d_spec_ids, e->h_cpu_dev, x, e->h_x_dev, cf.hidden, e->maxU, cf.max_tokens, e->d_plan,
-                     e->h_ready_dev, seq);
+                     e->h_call_dev, e->h_done_dev, seq);
   return hipGetLastError();
 }
 

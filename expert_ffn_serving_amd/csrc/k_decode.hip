@@ -65,10 +65,21 @@ template <int FMT>
 __device__ inline uint32_t scale_lane_off(int q, int r) {
   return FMT == EFF_WFMT_INT4_G32_BF16 ? (uint32_t)r * 2u : (uint32_t)((q >> 1) * 16 + r);
 }
+// raw scale bits of one lane (int4: a bf16; NVFP4: an e4m3 byte) and their value
 template <int FMT>
-__device__ inline float load_scale(const uint8_t* p) {
-  if (FMT == EFF_WFMT_INT4_G32_BF16) return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
-  return __builtin_amdgcn_cvt_f32_fp8((uint32_t)*p, 0);
+__device__ inline uint32_t load_scale_raw(const uint8_t* p) {
+  if (FMT == EFF_WFMT_INT4_G32_BF16) return (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+  return (uint32_t)*p;
+}
+template <int FMT>
+__device__ inline void store_scale_raw(uint8_t* p, uint32_t v) {
+  if (FMT == EFF_WFMT_INT4_G32_BF16) *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
+  else *p = (uint8_t)v;
+}
+template <int FMT>
+__device__ inline float scale_value(uint32_t raw) {
+  if (FMT == EFF_WFMT_INT4_G32_BF16) return __uint_as_float(raw << 16);
+  return __builtin_amdgcn_cvt_f32_fp8(raw, 0);
 }
 
 // 8 bf16 activations -> the 4 pairs that meet the weight pairs of one dword
@@ -104,8 +115,9 @@ __device__ inline float dword_dot_bf16(uint32_t d, const uint32_t* xw, float xs)
 }
 
 template <int FMT, int NT>
-__device__ inline void gateup_tile(uint32_t wg, uint32_t wu, float sg, float su, const uint4* xv,
+__device__ inline void gateup_tile(uint32_t wg, uint32_t wu, uint32_t rg, uint32_t ru, const uint4* xv,
                                    float (&acc)[2][NT]) {
+  const float sg = scale_value<FMT>(rg), su = scale_value<FMT>(ru);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     uint32_t xw[4];
@@ -122,11 +134,13 @@ __device__ inline void gateup_tile(uint32_t wg, uint32_t wu, float sg, float su,
 // grid: maxU * (I/16) workgroups of 256 threads, one per (plan unit, 16-row slice of I).  Wave w
 // takes tiles w, w+4, ... of the slice (the 4 waves together sweep 1 KiB runs), gate and up at
 // once; everything reduces inside the workgroup, so no workgroup ever waits for another.
+// A unit installed by this call (fetch) is read from the pinned host pool, and every byte read
+// is also written into its slot: the gate/up and down kernels together copy the whole record.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
-k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
-         const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H, int I, int K,
-         int maxB, float* __restrict__ a_out) {
+k_gateup(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, int64_t R,
+         const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H,
+         int I, int K, int maxB, float* __restrict__ a_out) {
   constexpr int UNR = NT >= 4 ? 2 : (NT == 2 ? 4 : 8);  // tiles in flight per wave
   __shared__ float s_red[4][2][16][NT];
   const int NS = I / 16, KB = H / 32;
@@ -136,15 +150,22 @@ k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__
   if (cnt <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool fetch = un->fetch != 0;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const uint8_t* rec = arena + (int64_t)un->slot * R;
-  const uint8_t* gp = rec + (int64_t)sl * KB * 256 + lane * 4;
+  uint8_t* slot_rec = const_cast<uint8_t*>(arena) + (int64_t)un->slot * R;
+  const uint8_t* rec = fetch ? pool + (int64_t)un->flat * R : slot_rec;
+  const int64_t wofs = (int64_t)sl * KB * 256 + lane * 4;
+  const int64_t sofs = 3 * pay + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
+  const uint8_t* gp = rec + wofs;
   const uint8_t* up = gp + pay;
-  const uint8_t* gs = rec + 3 * pay + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
+  const uint8_t* gs = rec + sofs;
   const uint8_t* us = gs + sca;
+  uint8_t* gpd = slot_rec + wofs;
+  uint8_t* gsd = slot_rec + sofs;
   const uint16_t* xq = x + q * 8;
   for (int c0 = 0; c0 < cnt; c0 += NT) {
     const int nt = min(NT, cnt - c0);
+    const bool copy = fetch && c0 == 0;  // the bytes go to the slot once
     const uint16_t* xt[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) xt[j] = xq + (int64_t)((j < nt) ? un->entry[c0 + j] / K : 0) * H;
@@ -153,29 +174,45 @@ k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__
     for (int j = 0; j < NT; ++j) acc[0][j] = acc[1][j] = 0.f;
     int kb = wave;
     for (; kb + 4 * (UNR - 1) < KB; kb += 4 * UNR) {  // full rounds: every load first
-      uint32_t wg[UNR], wu[UNR];
-      float sg[UNR], su[UNR];
+      uint32_t wg[UNR], wu[UNR], rg[UNR], ru[UNR];
       uint4 xv[UNR][NT];
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
         const int k = kb + 4 * z;
         wg[z] = *reinterpret_cast<const uint32_t*>(gp + k * 256);
         wu[z] = *reinterpret_cast<const uint32_t*>(up + k * 256);
-        sg[z] = load_scale<FMT>(gs + k * 32);
-        su[z] = load_scale<FMT>(us + k * 32);
+        rg[z] = load_scale_raw<FMT>(gs + k * 32);
+        ru[z] = load_scale_raw<FMT>(us + k * 32);
 #pragma unroll
         for (int j = 0; j < NT; ++j) xv[z][j] = *reinterpret_cast<const uint4*>(xt[j] + k * 32);
       }
+      if (copy) {
 #pragma unroll
-      for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], sg[z], su[z], xv[z], acc);
+        for (int z = 0; z < UNR; ++z) {
+          const int k = kb + 4 * z;
+          *reinterpret_cast<uint32_t*>(gpd + k * 256) = wg[z];
+          *reinterpret_cast<uint32_t*>(gpd + pay + k * 256) = wu[z];
+          store_scale_raw<FMT>(gsd + k * 32, rg[z]);
+          store_scale_raw<FMT>(gsd + sca + k * 32, ru[z]);
+        }
+      }
+#pragma unroll
+      for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], acc);
     }
     for (; kb < KB; kb += 4) {  // tail
       uint4 xv[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) xv[j] = *reinterpret_cast<const uint4*>(xt[j] + kb * 32);
-      gateup_tile<FMT, NT>(*reinterpret_cast<const uint32_t*>(gp + kb * 256),
-                           *reinterpret_cast<const uint32_t*>(up + kb * 256), load_scale<FMT>(gs + kb * 32),
-                           load_scale<FMT>(us + kb * 32), xv, acc);
+      const uint32_t wg = *reinterpret_cast<const uint32_t*>(gp + kb * 256);
+      const uint32_t wu = *reinterpret_cast<const uint32_t*>(up + kb * 256);
+      const uint32_t rg = load_scale_raw<FMT>(gs + kb * 32), ru = load_scale_raw<FMT>(us + kb * 32);
+      if (copy) {
+        *reinterpret_cast<uint32_t*>(gpd + kb * 256) = wg;
+        *reinterpret_cast<uint32_t*>(gpd + pay + kb * 256) = wu;
+        store_scale_raw<FMT>(gsd + kb * 32, rg);
+        store_scale_raw<FMT>(gsd + sca + kb * 32, ru);
+      }
+      gateup_tile<FMT, NT>(wg, wu, rg, ru, xv, acc);
     }
     // reduce over q (lanes r, r+16, r+32, r+48), then over the 4 waves in order
 #pragma unroll
@@ -214,8 +251,9 @@ k_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__
 
 // ---------------------------------------------------------------------------- down
 template <int FMT, int NT>
-__device__ inline void down_tile(uint32_t d, float sd, const uint4* s_a4, const float (*s_asum)[512], int kb,
+__device__ inline void down_tile(uint32_t d, uint32_t rd, const uint4* s_a4, const float (*s_asum)[512], int kb,
                                  int q, int nt, int I8, float (&acc)[NT]) {
+  const float sd = scale_value<FMT>(rd);
   uint32_t p0, p1, p2, p3;
   if (FMT == EFF_WFMT_INT4_G32_BF16) {
     p0 = (d & 0x000F000Fu) | 0x64006400u;
@@ -242,9 +280,9 @@ __device__ inline void down_tile(uint32_t d, float sd, const uint4* s_a4, const 
 // two so that its largest value fits.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
-k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
-       const DecodePlan* __restrict__ plan, const float* __restrict__ a_in, int H, int I, int maxB,
-       float* __restrict__ y) {
+k_down(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, int64_t R,
+       const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const float* __restrict__ a_in, int H,
+       int I, int maxB, float* __restrict__ y) {
   extern __shared__ uint4 s_a4[];            // [NT][I/8] groups of 8 fp16 (int4 order permuted)
   __shared__ float s_asum[NT][512];          // int4: sum of each 8-group (I/8 <= 512)
   __shared__ float s_red[4][16][NT];
@@ -259,20 +297,26 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint8_t* rec = arena + (int64_t)un->slot * R;
-  const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 4;
-  const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
+  const bool fetch = un->fetch != 0;
+  uint8_t* slot_rec = const_cast<uint8_t*>(arena) + (int64_t)un->slot * R;
+  const uint8_t* rec = fetch ? pool + (int64_t)un->flat * R : slot_rec;
+  const int64_t wofs = 2 * pay + (int64_t)sl * KB * 256 + lane * 4;
+  const int64_t sofs = 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
+  const uint8_t* dp = rec + wofs;
+  const uint8_t* ds = rec + sofs;
+  uint8_t* dpd = slot_rec + wofs;
+  uint8_t* dsd = slot_rec + sofs;
 
   for (int c0 = 0; c0 < cnt; c0 += NT) {
     const int nt = min(NT, cnt - c0);
+    const bool copy = fetch && c0 == 0;
     // the weights do not depend on the activations: start their loads first
-    uint32_t wd[UNR];
-    float sd[UNR];
+    uint32_t wd[UNR], rd[UNR];
 #pragma unroll
     for (int z = 0; z < UNR; ++z) {
       const int k = wave + 4 * z;
       wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
-      sd[z] = k < KB ? load_scale<FMT>(ds + k * 32) : 0.f;
+      rd[z] = k < KB ? load_scale_raw<FMT>(ds + k * 32) : 0u;
     }
     // per-token power-of-two scale: |a| * 2^-e < 2^15
     for (int j = 0; j < nt; ++j) {
@@ -323,18 +367,34 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = 0.f;
 #pragma unroll
-    for (int z = 0; z < UNR; ++z)
-      if (wave + 4 * z < KB) down_tile<FMT, NT>(wd[z], sd[z], s_a4, s_asum, wave + 4 * z, q, nt, I8, acc);
+    for (int z = 0; z < UNR; ++z) {
+      const int k = wave + 4 * z;
+      if (k < KB) {
+        if (copy) {
+          *reinterpret_cast<uint32_t*>(dpd + k * 256) = wd[z];
+          store_scale_raw<FMT>(dsd + k * 32, rd[z]);
+        }
+        down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_asum, k, q, nt, I8, acc);
+      }
+    }
     for (int kb0 = wave + 4 * UNR; kb0 < KB; kb0 += 4 * UNR) {
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
         const int k = kb0 + 4 * z;
         wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
-        sd[z] = k < KB ? load_scale<FMT>(ds + k * 32) : 0.f;
+        rd[z] = k < KB ? load_scale_raw<FMT>(ds + k * 32) : 0u;
       }
 #pragma unroll
-      for (int z = 0; z < UNR; ++z)
-        if (kb0 + 4 * z < KB) down_tile<FMT, NT>(wd[z], sd[z], s_a4, s_asum, kb0 + 4 * z, q, nt, I8, acc);
+      for (int z = 0; z < UNR; ++z) {
+        const int k = kb0 + 4 * z;
+        if (k < KB) {
+          if (copy) {
+            *reinterpret_cast<uint32_t*>(dpd + k * 256) = wd[z];
+            store_scale_raw<FMT>(dsd + k * 32, rd[z]);
+          }
+          down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_asum, k, q, nt, I8, acc);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -364,7 +424,7 @@ k_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ t
 
 // ---------------------------------------------------------------------------- combine
 // out[t, h] = sum over k (ascending) of w[t,k] * y[t,k,h], y from the GPU or the host buffer by the
-// entry's slot (slots == nullptr: all from yg).  All loads of a thread are issued before any use.
+// entry's slot (slots == nullptr: all from yg; yh may be host-mapped memory).
 template <int KMAX>
 __global__ void __launch_bounds__(256)
 k_combine(const float* __restrict__ yg, const float* __restrict__ yh, const int32_t* __restrict__ slots,
@@ -372,25 +432,43 @@ k_combine(const float* __restrict__ yg, const float* __restrict__ yh, const int3
   const int t = blockIdx.y;
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
-  float vg[KMAX], vh[KMAX], wk[KMAX];
-  int sk[KMAX];
+  float v[KMAX], wk[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     if (k < K) {
       const int64_t p = (int64_t)t * K + k;
       wk[k] = w[p];
-      sk[k] = slots ? slots[p] : 0;
-      vg[k] = yg[p * H + h];
-      vh[k] = yh ? yh[p * H + h] : 0.f;
+      const bool gpu = slots == nullptr || slots[p] >= 0;  // the same for every thread of the token
+      v[k] = (gpu ? yg : yh)[p * H + h];
     }
   }
   float acc = 0.f;
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
-    if (k < K) acc = fmaf(wk[k], sk[k] >= 0 ? vg[k] : vh[k], acc);
+    if (k < K) acc = fmaf(wk[k], v[k], acc);
   uint32_t b = __float_as_uint(acc);
   b += 0x7FFFu + ((b >> 16) & 1u);  // round to nearest even
   out[(int64_t)t * H + h] = (uint16_t)(b >> 16);
+}
+
+// ---------------------------------------------------------------------------- fetch copy
+// Copies the records of a fetch list from the pinned host pool into their slots (16 KiB chunks,
+// 16 bytes per thread); entries outside the pool or the arena are skipped.
+__global__ void __launch_bounds__(256)
+k_fetch_copy(const uint8_t* __restrict__ pool, uint8_t* __restrict__ arena, int64_t R, int64_t n_flat, int S,
+             const FetchList* __restrict__ fl) {
+  constexpr int64_t kChunk = 16384;
+  const int n = min(fl->count, kMaxEntries);
+  const int64_t chunks = (R + kChunk - 1) / kChunk;
+  for (int64_t c = blockIdx.x; c < (int64_t)n * chunks; c += gridDim.x) {
+    const int i = (int)(c / chunks);
+    const int64_t off = (c % chunks) * kChunk, len = min(kChunk, R - off);
+    const int flat = fl->flat[i], slot = fl->slot[i];
+    if (flat < 0 || flat >= n_flat || slot < 0 || slot >= S) continue;
+    const uint4* src = reinterpret_cast<const uint4*>(pool + (int64_t)flat * R + off);
+    uint4* dst = reinterpret_cast<uint4*>(arena + (int64_t)slot * R + off);
+    for (int64_t b = threadIdx.x; b < len / 16; b += 256) dst[b] = src[b];
+  }
 }
 
 template <int FMT, int NT>
@@ -398,15 +476,15 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, hipStream_t 
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   const int ts = timing_begin(e, EFF_T_DECODE_GATEUP, s);
-  hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(e->maxU * (I / 16)), dim3(kWG), 0, s, e->d_arena, e->R, e->d_ts,
-                     e->d_plan, x, H, I, c.top_k, c.max_tokens, e->d_a);
+  hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(e->maxU * (I / 16)), dim3(kWG), 0, s, e->d_arena, e->pool_dev, e->R,
+                     e->d_ts, e->d_plan, x, H, I, c.top_k, c.max_tokens, e->d_a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
   size_t lds = (size_t)NT * (I / 8) * sizeof(uint4);
-  hipLaunchKernelGGL((k_down<FMT, NT>), dim3(e->maxU * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->R, e->d_ts,
-                     e->d_plan, e->d_a, H, I, c.max_tokens, y);
+  hipLaunchKernelGGL((k_down<FMT, NT>), dim3(e->maxU * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
+                     e->d_ts, e->d_plan, e->d_a, H, I, c.max_tokens, y);
   err = hipGetLastError();
   timing_mark(e, ts, 3, s);
   return err;
@@ -450,6 +528,13 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
     default: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 8>(e, x, y, s)
                         : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 8>(e, x, y, s);
   }
+}
+
+hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s) {
+  const eff_config& c = e->cfg;
+  hipLaunchKernelGGL(k_fetch_copy, dim3(256), dim3(256), 0, s, e->pool_dev, e->d_arena, e->R,
+                     (int64_t)c.num_layers * c.num_experts, c.num_slots, e->d_fetch + which);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,

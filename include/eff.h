@@ -62,8 +62,11 @@ enum { EFF_SPECULATIVE = 1u };
 
 /* eff_config.flags */
 enum {
-  EFF_CFG_TIMING = 1u /* bracket the expert kernels with HIP events on their stream; the
-                         durations are summed into eff_stats (adds two event records per call) */
+  EFF_CFG_TIMING = 1u,   /* bracket the expert kernels with HIP events on their stream; the
+                            durations are summed into eff_stats (adds two event records per call) */
+  EFF_CFG_SYNC_HOST = 2u /* eff_decode_layer runs the host share on the calling thread and returns
+                            after enqueuing the combine (default: a worker thread runs it and the
+                            compute stream waits for it on a host-mapped word) */
 };
 
 typedef struct eff_config {
@@ -163,14 +166,21 @@ int eff_host_ffn_decode(eff_engine* e, int layer, const void* x_host, const int3
 int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const int32_t* slots,
                 const float* w, int B, void* out, eff_stream_t stream);
 
-/* One decode MoE layer end to end, eager: route (from x and w_router, or from
- * logits if w_router is NULL) -> ensure -> split -> [speculative ensure/split
- * of layer+1 on spec_ids if not NULL] -> copies on `side` -> GPU expert FFN ->
- * host share -> combine into out (bf16 [B,H]).  top-K, ensure, split and the
- * speculative request run as one single-workgroup kernel with the same
- * semantics as the separate calls.  Waits on the host once (to read the
- * fetch list, the host ids and x from host-mapped memory).  ids/w/slots/cpu_ids/counts of the
- * call can be read back with eff_last_layer_info. */
+/* One decode MoE layer end to end: route (from x and w_router, or from logits if
+ * w_router is NULL) -> ensure -> split -> [speculative ensure/split of layer+1
+ * on spec_ids if not NULL, its copies on `side`] -> GPU expert FFN -> host share
+ * -> combine into out (bf16 [B,H]).  top-K, ensure, split, the speculative
+ * request and the decode plan run as one single-workgroup kernel with the same
+ * semantics as the separate calls ([FT-blog] §六).  Experts installed by the
+ * call are read from the pinned pool by the expert kernels themselves, which
+ * also write them into their slots.  The control kernel publishes the host ids
+ * and x in host-mapped memory; the host share ([FT-deep] §4 ③④) runs on a worker
+ * thread and the compute stream waits for it on a host-mapped word before the
+ * combine (hipStreamWaitValue64), so the call only enqueues work and returns.
+ * With EFF_CFG_SYNC_HOST (or without stream wait-value support) the calling
+ * thread waits for the control kernel and runs the host share itself.  An error
+ * of the host share is reported by the next call.  ids/w/slots/cpu_ids/counts of
+ * the call can be read back with eff_last_layer_info after the stream is done. */
 int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_router,
                      const float* logits, int B, const int32_t* spec_ids, void* out,
                      eff_stream_t compute, eff_stream_t side);
@@ -206,12 +216,12 @@ enum { EFF_T_DECODE_GATEUP = 0, EFF_T_DECODE_DOWN = 1, EFF_T_PREFILL_GATEUP = 2,
 
 typedef struct eff_stats {
   int64_t calls, hits, fetched, host, spec_fetched; /* unique experts, summed over calls */
-  int64_t bytes_fetched;
+  int64_t bytes_fetched;  /* (fetched + spec_fetched) * record bytes */
   int64_t qstar_hist[17]; /* q' counts 0..15, 16+ */
   int64_t launches[4];    /* timed launches per EFF_T_* slot */
   double kernel_ms[4];    /* summed durations per EFF_T_* slot (HIP events) */
   double host_ms;         /* eff_decode_layer: wall time in the host executor */
-  double wait_ms;         /* eff_decode_layer: wall time waiting for the control kernel */
+  double wait_ms;         /* eff_decode_layer: wall time the host share waited for control kernels */
   int64_t host_calls;     /* eff_decode_layer calls with a host share */
 } eff_stats;
 /* Changes eff_config.flags of a live engine (EFF_CFG_* bits); EFF_EINVAL for unknown bits. */

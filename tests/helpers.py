@@ -73,9 +73,9 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
-def make_engine(eff, pool: PinnedPool, K, S, max_tokens, f_q16, max_prefill_tokens=0, host_threads=8):
+def make_engine(eff, pool: PinnedPool, K, S, max_tokens, f_q16, max_prefill_tokens=0, host_threads=8, flags=0):
     cfg = eff.make_config(pool.L, pool.E, K, pool.H, pool.I, pool.fmt, S, max_tokens, max_prefill_tokens,
-                          f_q16, host_threads)
+                          f_q16, host_threads, flags)
     ts = pool.ts if pool.fmt == synth.FMT_NVFP4 else None
     return eff.Engine(cfg, pool.ptr, ts)
 

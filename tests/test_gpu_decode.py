@@ -29,10 +29,10 @@ def dev_bf16(a):
 
 
 def run_decode(eff, pool, K, S, f, B, tokens, router=True, zipf=1.1, spec_keep=-1.0, seed=11,
-               compare_y=True):
+               compare_y=True, flags=0):
     """Decode `tokens` steps through all layers on the GPU (eff_decode_layer) and the oracle."""
     L, E, H = pool.L, pool.E, pool.H
-    eng = make_engine(eff, pool, K, S, B, f)
+    eng = make_engine(eff, pool, K, S, B, f, flags=flags)
     orc = oracle_engine(pool, K, S, f)
     side = torch.cuda.Stream()
     outs = []
@@ -90,6 +90,74 @@ def tiny_pool(eff):
 def test_tiny_decode_every_f(eff, tiny_pool, f):
     outs, st = run_decode(eff, tiny_pool, TINY.K, TINY.S, f, 1, 16, seed=TINY.seed)
     assert outs.shape[0] == 16 * TINY.L
+
+
+@pytest.mark.parametrize("f", [0, 32768, 65536])
+def test_tiny_decode_sync_host(eff, tiny_pool, f):
+    """The host share on the calling thread (EFF_CFG_SYNC_HOST) gives the same results."""
+    a, _ = run_decode(eff, tiny_pool, TINY.K, TINY.S, f, 1, 8, seed=TINY.seed)
+    b, _ = run_decode(eff, tiny_pool, TINY.K, TINY.S, f, 1, 8, seed=TINY.seed, flags=eff.CFG_SYNC_HOST)
+    assert np.array_equal(a, b)
+
+
+def run_ahead(eff, pool, K, S, f, B, tokens, zipf, seed, spec_keep=-1.0, flags=0):
+    """Every layer of every token enqueued before a single synchronize (the host runs ahead of
+    the device; host shares and speculative copies are ordered on the device only); all outputs
+    and the final tables against the oracle."""
+    L, E, H = pool.L, pool.E, pool.H
+    eng = make_engine(eff, pool, K, S, B, f, flags=flags)
+    orc = oracle_engine(pool, K, S, f)
+    side = torch.cuda.Stream()
+    try:
+        xs, lgs, specs, outs = {}, {}, {}, {}
+        for t in range(tokens):
+            for l in range(L):
+                xs[t, l] = synth.activations(seed, l, t * B, B, H)
+                lgs[t, l] = synth.trace_logits(seed, l, E, zipf, t * B, B)
+                specs[t, l] = None
+                if spec_keep >= 0 and l + 1 < L:
+                    nxt = synth.trace_logits(seed, l + 1, E, zipf, t * B, B)
+                    truth = synth.gumbel_topk_sets(nxt, K)
+                    specs[t, l] = np.stack([synth.spec_ids(seed, l + 1, E, zipf, t * B + b, truth[b], spec_keep)
+                                            for b in range(B)])
+        dev = {k: (dev_bf16(xs[k]), torch.from_numpy(lgs[k]).cuda(),
+                   None if specs[k] is None else torch.from_numpy(specs[k].reshape(-1)).cuda()) for k in xs}
+        torch.cuda.synchronize()
+        for t in range(tokens):
+            for l in range(L):
+                xd, lg, sp = dev[t, l]
+                outs[t, l] = torch.empty((B, H), dtype=torch.int16, device="cuda")
+                eng.decode_layer(l, xd, outs[t, l], logits=lg, spec_ids=sp, side=side)
+        torch.cuda.synchronize()
+        for t in range(tokens):
+            for l in range(L):
+                r = orc.decode_layer(l, xs[t, l], logits=lgs[t, l], spec_next=specs[t, l])
+                assert_close_bf16(outs[t, l].cpu().numpy().view(np.uint16), r["out_bits"],
+                                  what="run-ahead t=%d l=%d" % (t, l))
+        snap = eng.snapshot_tables()
+        assert list(snap["table"]) == orc.cache.table
+        assert list(snap["usage"]) == orc.cache.usage
+        return eng.stats()
+    finally:
+        eng.close()
+
+
+@pytest.mark.parametrize("fmt,H,I,E,K,B,S,f,spec", [
+    (synth.FMT_INT4, 2048, 512, 64, 8, 1, 96, 26214, -1.0),
+    (synth.FMT_NVFP4, 2560, 640, 48, 10, 2, 60, 65535, 0.65),
+    (synth.FMT_INT4, 256, 128, 16, 4, 3, 6, 16384, -1.0),
+])
+def test_decode_run_ahead(eff, fmt, H, I, E, K, B, S, f, spec):
+    pool = PinnedPool(eff, 23, 4, E, H, I, fmt)
+    try:
+        st = run_ahead(eff, pool, K, S, f, B, 6, 1.1, 23, spec_keep=spec)
+        assert st["fetched"] > 0
+        if spec >= 0:
+            assert st["spec_fetched"] > 0
+        else:
+            assert st["host"] > 0
+    finally:
+        pool.free()
 
 
 def test_tiny_all_host_and_invariance(eff, tiny_pool):
