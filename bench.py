@@ -253,7 +253,7 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=64)
     ap.add_argument("--prefill-layers", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=4)
-    ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--threads", type=int, default=15)   # host-share pool; one core left for the enqueuing thread
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     args = ap.parse_args()

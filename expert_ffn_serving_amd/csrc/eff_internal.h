@@ -79,6 +79,8 @@ struct HostJob {
   int32_t layer, B;
 };
 constexpr int kJobRing = 4096;
+// polls of the host-share word by the combine kernel before it gives up (about 2 s)
+constexpr uint32_t kCombineSpinLimit = 1u << 20;
 
 // Device stats counters (int64) ----------------------------------------------------------------
 enum { ST_CALLS, ST_HITS, ST_FETCHED, ST_HOST, ST_SPEC_FETCHED, ST_HIST0, ST_COUNT = ST_HIST0 + 17 };
@@ -109,6 +111,15 @@ class ThreadPool {
   std::atomic<int> sleepers_{0};
   std::mutex mu_;
   std::condition_variable cv_;
+};
+
+// Host-share scratch, reused across calls (no allocation per call once grown).
+struct HostScratch {
+  int32_t uexp[kMaxEntries];
+  int32_t ucnt[kMaxEntries];
+  int32_t uent[kMaxEntries][kMaxTokens];
+  std::atomic<int> done[kMaxEntries];
+  std::vector<uint16_t> a;  // per (expert, token): hi row, then lo row of silu(g)*u, bf16
 };
 
 }  // namespace eff
@@ -163,6 +174,8 @@ struct eff_engine {
   uint64_t* h_call_dev = nullptr;
   uint64_t* h_done = nullptr;     // host-mapped: the last call whose host share is in h_yhost
   uint64_t* h_done_dev = nullptr;
+  int32_t* h_err = nullptr;       // host-mapped sticky device error bits (bad id 1, combine wait 4)
+  int32_t* h_err_dev = nullptr;
   uint64_t ready_seq = 0;
   float* h_yhost = nullptr;       // [maxB*K*H] host-mapped: the host share's outputs
   float* h_yhost_dev = nullptr;
@@ -191,7 +204,6 @@ struct eff_engine {
   int pf_layer[2] = {-1, -1};
 
   std::vector<float> h_ts;        // host copy of the tensor scales (host executor)
-  int32_t* h_err = nullptr;       // host-mapped mirror of the device error word
   hipEvent_t ev_pf_done[2] = {nullptr, nullptr};
   bool pf_done_recorded[2] = {false, false};
   int32_t* d_pf_slot_of = nullptr;  // [E] slot per expert (fallback prefill)
@@ -199,6 +211,8 @@ struct eff_engine {
   int32_t* h_pf_ids = nullptr;      // pinned [T*K]
   int32_t* h_pf_meta = nullptr;     // pinned [2E]
   eff::ThreadPool* pool_threads = nullptr;
+  int host_isa = 0;               // host slice kernels: 0 AVX2 + FMA, 1 AVX-512 BF16
+  eff::HostScratch hscratch;
   // kernel timing (EFF_CFG_TIMING): events (start, end) of each of two kernels per call
   struct TimedCall { int kind; hipEvent_t ev[4]; };
   std::vector<TimedCall> timed;     // recorded, not yet resolved
@@ -231,7 +245,8 @@ hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, 
 int timing_begin(eff_engine* e, int kind, hipStream_t s);
 void timing_mark(eff_engine* e, int slot, int i, hipStream_t s);
 hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
-                          int B, int K, int H, uint16_t* out, hipStream_t s);
+                          int B, int K, int H, uint16_t* out, hipStream_t s, const uint64_t* done = nullptr,
+                          uint64_t seq = 0, int32_t* err = nullptr);
 hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int32_t* ids,
                           const float* w, int T, uint16_t* out, const int32_t* slot_of_expert,
                           int slot_base, bool combine, hipStream_t s);
@@ -241,4 +256,5 @@ int decode_nt(int maxB);
 int64_t qstar_host(int64_t m, int64_t f);
 // host executor
 void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_ids, int B, float* y);
+int host_isa_best();
 }  // namespace eff

@@ -128,6 +128,8 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_cpu_dev, e->h_cpu, 0));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_call_dev, e->h_call, 0));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_done_dev, e->h_done, 0));
+  e->h_err = reinterpret_cast<int32_t*>(e->h_done + 1);  // shares the 64-byte block
+  e->h_err_dev = reinterpret_cast<int32_t*>(e->h_done_dev + 1);
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_yhost_dev, e->h_yhost, 0));
   std::memset(e->h_call, 0, kCallRing * sizeof(uint64_t));
   std::memset(e->h_done, 0, 64);
@@ -245,6 +247,11 @@ static void set_async_error(eff_engine* e, const std::string& msg) {
 }
 
 static int check_async_error(eff_engine* e) {
+  const int32_t dev_err = __atomic_exchange_n(e->h_err, 0, __ATOMIC_ACQ_REL);  // sticky device error bits
+  if (dev_err)
+    return fail(EFF_EDEVICE, (dev_err & 1) ? "an expert id was outside [0, E) (entries skipped)"
+                             : (dev_err & 4) ? "a combine gave up waiting for its host share"
+                                             : "device error");
   if (!e->async_err.load(std::memory_order_acquire)) return EFF_OK;
   std::lock_guard<std::mutex> g(e->async_mu);
   return fail(EFF_EHIP, "host share of an earlier decode call: " + e->async_msg);
@@ -424,9 +431,8 @@ int eff_create(const eff_config* cfg, const void* host_pool, const float* tensor
     release(e);
     return fail(EFF_ENOMEM, "thread pool");
   }
-  int can_wait = 0;
-  if (hipDeviceGetAttribute(&can_wait, hipDeviceAttributeCanUseStreamWaitValue, dev) != hipSuccess) can_wait = 0;
-  e->async_host = can_wait && !(cfg->flags & EFF_CFG_SYNC_HOST);
+  e->host_isa = host_isa_best();
+  e->async_host = !(cfg->flags & EFF_CFG_SYNC_HOST);
   if (e->async_host) {
     e->jobs.resize(kJobRing);
     try {
@@ -614,8 +620,8 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true));
   if (e->async_host) {
     // the combine waits for the host share (or the control kernel's own release of the call)
-    EFF_HIP_TRY(hipStreamWaitValue64(cs, e->h_done_dev, seq, hipStreamWaitValueGte, ~0ull));
-    EFF_HIP_TRY(launch_combine(e->d_ygpu, e->h_yhost_dev, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs));
+    EFF_HIP_TRY(launch_combine(e->d_ygpu, e->h_yhost_dev, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs,
+                               e->h_done_dev, seq, e->h_err_dev));
     push_job(e, HostJob{seq, layer, B});
     return EFF_OK;
   }

@@ -40,6 +40,7 @@ struct CacheState {
   FetchList* fl_host;  // host-mapped mirror (device view)
   int64_t* stats;
   int32_t* err;
+  int32_t* host_err;  // host-mapped sticky error bits
   int sort_pow2;
 };
 
@@ -299,6 +300,7 @@ __device__ void commit_body(const CacheState& c, const CallLds& C, bool stamp_hi
       counts[2] = spec ? 0 : m - qq;
     }
     const int err = C.err | atomicExch(c.err, 0);
+    if (err) __hip_atomic_fetch_or(c.host_err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     fl->count = qq;
     flh->count = qq;
     fl->err = err;
@@ -713,6 +715,7 @@ static CacheState state_of(eff_engine* e) {
   c.fl_host = e->h_fetch_dev;
   c.stats = e->d_stats;
   c.err = e->d_err;
+  c.host_err = e->h_err_dev;
   c.sort_pow2 = sort_pow2_of(c.S);
   return c;
 }

@@ -60,6 +60,23 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 // one contiguous run of (Kd/32) tiles of 256 payload bytes (and 32 scale bytes).  Lane
 // (q = lane/16, r = lane%16) reads the dword at byte lane*4 of a tile: row r, inputs 8q..8q+7.
 
+// Copies n bytes (n % 16 == 0, both ends 16-byte aligned) with the whole workgroup, 16 bytes per
+// thread and four loads in flight per thread.
+__device__ inline void wg_copy(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  const int64_t n4 = n / 16;
+  int64_t i = threadIdx.x;
+  for (; i + 3 * kWG < n4; i += 4 * kWG) {
+    const uint4 a = s4[i], b = s4[i + kWG], c = s4[i + 2 * kWG], d = s4[i + 3 * kWG];
+    d4[i] = a;
+    d4[i + kWG] = b;
+    d4[i + 2 * kWG] = c;
+    d4[i + 3 * kWG] = d;
+  }
+  for (; i < n4; i += kWG) d4[i] = s4[i];
+}
+
 // per-lane scale offset inside a tile's 32 scale bytes
 template <int FMT>
 __device__ inline uint32_t scale_lane_off(int q, int r) {
@@ -70,11 +87,6 @@ template <int FMT>
 __device__ inline uint32_t load_scale_raw(const uint8_t* p) {
   if (FMT == EFF_WFMT_INT4_G32_BF16) return (uint32_t)*reinterpret_cast<const uint16_t*>(p);
   return (uint32_t)*p;
-}
-template <int FMT>
-__device__ inline void store_scale_raw(uint8_t* p, uint32_t v) {
-  if (FMT == EFF_WFMT_INT4_G32_BF16) *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
-  else *p = (uint8_t)v;
 }
 template <int FMT>
 __device__ inline float scale_value(uint32_t raw) {
@@ -134,11 +146,11 @@ __device__ inline void gateup_tile(uint32_t wg, uint32_t wu, uint32_t rg, uint32
 // grid: maxU * (I/16) workgroups of 256 threads, one per (plan unit, 16-row slice of I).  Wave w
 // takes tiles w, w+4, ... of the slice (the 4 waves together sweep 1 KiB runs), gate and up at
 // once; everything reduces inside the workgroup, so no workgroup ever waits for another.
-// A unit installed by this call (fetch) is read from the pinned host pool, and every byte read
-// is also written into its slot: the gate/up and down kernels together copy the whole record.
+// A unit installed by this call (fetch) first copies its slices from the pinned host pool into
+// the slot (16-byte loads); the gate/up and down kernels together copy the whole record.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
-k_gateup(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, int64_t R,
+k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
          const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H,
          int I, int K, int maxB, float* __restrict__ a_out) {
   constexpr int UNR = NT >= 4 ? 2 : (NT == 2 ? 4 : 8);  // tiles in flight per wave
@@ -150,22 +162,26 @@ k_gateup(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, in
   if (cnt <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool fetch = un->fetch != 0;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  uint8_t* slot_rec = const_cast<uint8_t*>(arena) + (int64_t)un->slot * R;
-  const uint8_t* rec = fetch ? pool + (int64_t)un->flat * R : slot_rec;
-  const int64_t wofs = (int64_t)sl * KB * 256 + lane * 4;
-  const int64_t sofs = 3 * pay + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
-  const uint8_t* gp = rec + wofs;
+  uint8_t* rec = arena + (int64_t)un->slot * R;
+  if (un->fetch) {
+    // installed by this call: copy this workgroup's gate and up slices (payload and scales) from
+    // the pool into the slot, then read them back like any resident record
+    const uint8_t* src = pool + (int64_t)un->flat * R;
+    const int64_t po = (int64_t)sl * KB * 256, so = 3 * pay + (int64_t)sl * KB * 32;
+    wg_copy(src + po, rec + po, (int64_t)KB * 256);
+    wg_copy(src + pay + po, rec + pay + po, (int64_t)KB * 256);
+    wg_copy(src + so, rec + so, (int64_t)KB * 32);
+    wg_copy(src + sca + so, rec + sca + so, (int64_t)KB * 32);
+    __syncthreads();
+  }
+  const uint8_t* gp = rec + (int64_t)sl * KB * 256 + lane * 4;
   const uint8_t* up = gp + pay;
-  const uint8_t* gs = rec + sofs;
+  const uint8_t* gs = rec + 3 * pay + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
   const uint8_t* us = gs + sca;
-  uint8_t* gpd = slot_rec + wofs;
-  uint8_t* gsd = slot_rec + sofs;
   const uint16_t* xq = x + q * 8;
   for (int c0 = 0; c0 < cnt; c0 += NT) {
     const int nt = min(NT, cnt - c0);
-    const bool copy = fetch && c0 == 0;  // the bytes go to the slot once
     const uint16_t* xt[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) xt[j] = xq + (int64_t)((j < nt) ? un->entry[c0 + j] / K : 0) * H;
@@ -186,16 +202,7 @@ k_gateup(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, in
 #pragma unroll
         for (int j = 0; j < NT; ++j) xv[z][j] = *reinterpret_cast<const uint4*>(xt[j] + k * 32);
       }
-      if (copy) {
-#pragma unroll
-        for (int z = 0; z < UNR; ++z) {
-          const int k = kb + 4 * z;
-          *reinterpret_cast<uint32_t*>(gpd + k * 256) = wg[z];
-          *reinterpret_cast<uint32_t*>(gpd + pay + k * 256) = wu[z];
-          store_scale_raw<FMT>(gsd + k * 32, rg[z]);
-          store_scale_raw<FMT>(gsd + sca + k * 32, ru[z]);
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);  // every load of the round is in flight before any use
 #pragma unroll
       for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], acc);
     }
@@ -203,16 +210,9 @@ k_gateup(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, in
       uint4 xv[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) xv[j] = *reinterpret_cast<const uint4*>(xt[j] + kb * 32);
-      const uint32_t wg = *reinterpret_cast<const uint32_t*>(gp + kb * 256);
-      const uint32_t wu = *reinterpret_cast<const uint32_t*>(up + kb * 256);
-      const uint32_t rg = load_scale_raw<FMT>(gs + kb * 32), ru = load_scale_raw<FMT>(us + kb * 32);
-      if (copy) {
-        *reinterpret_cast<uint32_t*>(gpd + kb * 256) = wg;
-        *reinterpret_cast<uint32_t*>(gpd + pay + kb * 256) = wu;
-        store_scale_raw<FMT>(gsd + kb * 32, rg);
-        store_scale_raw<FMT>(gsd + sca + kb * 32, ru);
-      }
-      gateup_tile<FMT, NT>(wg, wu, rg, ru, xv, acc);
+      gateup_tile<FMT, NT>(*reinterpret_cast<const uint32_t*>(gp + kb * 256),
+                           *reinterpret_cast<const uint32_t*>(up + kb * 256), load_scale_raw<FMT>(gs + kb * 32),
+                           load_scale_raw<FMT>(us + kb * 32), xv, acc);
     }
     // reduce over q (lanes r, r+16, r+32, r+48), then over the 4 waves in order
 #pragma unroll
@@ -280,7 +280,7 @@ __device__ inline void down_tile(uint32_t d, uint32_t rd, const uint4* s_a4, con
 // two so that its largest value fits.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
-k_down(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, int64_t R,
+k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
        const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const float* __restrict__ a_in, int H,
        int I, int maxB, float* __restrict__ y) {
   extern __shared__ uint4 s_a4[];            // [NT][I/8] groups of 8 fp16 (int4 order permuted)
@@ -297,19 +297,19 @@ k_down(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, int6
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool fetch = un->fetch != 0;
-  uint8_t* slot_rec = const_cast<uint8_t*>(arena) + (int64_t)un->slot * R;
-  const uint8_t* rec = fetch ? pool + (int64_t)un->flat * R : slot_rec;
-  const int64_t wofs = 2 * pay + (int64_t)sl * KB * 256 + lane * 4;
-  const int64_t sofs = 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
-  const uint8_t* dp = rec + wofs;
-  const uint8_t* ds = rec + sofs;
-  uint8_t* dpd = slot_rec + wofs;
-  uint8_t* dsd = slot_rec + sofs;
+  uint8_t* rec = arena + (int64_t)un->slot * R;
+  if (un->fetch) {  // installed by this call: this workgroup's down slice from the pool first
+    const uint8_t* src = pool + (int64_t)un->flat * R;
+    const int64_t po = 2 * pay + (int64_t)sl * KB * 256, so = 3 * pay + 2 * sca + (int64_t)sl * KB * 32;
+    wg_copy(src + po, rec + po, (int64_t)KB * 256);
+    wg_copy(src + so, rec + so, (int64_t)KB * 32);
+    __syncthreads();
+  }
+  const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 4;
+  const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
 
   for (int c0 = 0; c0 < cnt; c0 += NT) {
     const int nt = min(NT, cnt - c0);
-    const bool copy = fetch && c0 == 0;
     // the weights do not depend on the activations: start their loads first
     uint32_t wd[UNR], rd[UNR];
 #pragma unroll
@@ -367,16 +367,8 @@ k_down(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, int6
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = 0.f;
 #pragma unroll
-    for (int z = 0; z < UNR; ++z) {
-      const int k = wave + 4 * z;
-      if (k < KB) {
-        if (copy) {
-          *reinterpret_cast<uint32_t*>(dpd + k * 256) = wd[z];
-          store_scale_raw<FMT>(dsd + k * 32, rd[z]);
-        }
-        down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_asum, k, q, nt, I8, acc);
-      }
-    }
+    for (int z = 0; z < UNR; ++z)
+      if (wave + 4 * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_asum, wave + 4 * z, q, nt, I8, acc);
     for (int kb0 = wave + 4 * UNR; kb0 < KB; kb0 += 4 * UNR) {
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
@@ -385,16 +377,8 @@ k_down(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, int6
         rd[z] = k < KB ? load_scale_raw<FMT>(ds + k * 32) : 0u;
       }
 #pragma unroll
-      for (int z = 0; z < UNR; ++z) {
-        const int k = kb0 + 4 * z;
-        if (k < KB) {
-          if (copy) {
-            *reinterpret_cast<uint32_t*>(dpd + k * 256) = wd[z];
-            store_scale_raw<FMT>(dsd + k * 32, rd[z]);
-          }
-          down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_asum, k, q, nt, I8, acc);
-        }
-      }
+      for (int z = 0; z < UNR; ++z)
+        if (kb0 + 4 * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_asum, kb0 + 4 * z, q, nt, I8, acc);
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -425,10 +409,26 @@ k_down(const uint8_t* __restrict__ arena, const uint8_t* __restrict__ pool, int6
 // ---------------------------------------------------------------------------- combine
 // out[t, h] = sum over k (ascending) of w[t,k] * y[t,k,h], y from the GPU or the host buffer by the
 // entry's slot (slots == nullptr: all from yg; yh may be host-mapped memory).
+// With `done` (host-mapped), the kernel first waits until *done >= seq: the host share of the call
+// is in yh (or the call had none).  One thread per workgroup polls with a bounded spin; past the
+// bound it sets bit 4 of *err and combines anyway, so the kernel always ends.
 template <int KMAX>
 __global__ void __launch_bounds__(256)
 k_combine(const float* __restrict__ yg, const float* __restrict__ yh, const int32_t* __restrict__ slots,
-          const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out) {
+          const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out, const uint64_t* done, uint64_t seq,
+          int32_t* err) {
+  if (done) {
+    if (threadIdx.x == 0) {
+      for (uint32_t spin = 0; __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < seq; ++spin) {
+        if (spin >= kCombineSpinLimit) {
+          atomicOr(err, 4);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+    __syncthreads();
+  }
   const int t = blockIdx.y;
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
@@ -538,15 +538,16 @@ hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s) {
 }
 
 hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
-                          int B, int K, int H, uint16_t* out, hipStream_t s) {
+                          int B, int K, int H, uint16_t* out, hipStream_t s, const uint64_t* done, uint64_t seq,
+                          int32_t* err) {
   dim3 g((H + 255) / 256, B);
   if (!slots) yhost = nullptr;
   if (K <= 8)
-    hipLaunchKernelGGL(k_combine<8>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out);
+    hipLaunchKernelGGL(k_combine<8>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out, done, seq, err);
   else if (K <= 16)
-    hipLaunchKernelGGL(k_combine<16>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out);
+    hipLaunchKernelGGL(k_combine<16>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out, done, seq, err);
   else
-    hipLaunchKernelGGL(k_combine<kMaxTopK>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out);
+    hipLaunchKernelGGL(k_combine<kMaxTopK>, g, dim3(256), 0, s, ygpu, yhost, slots, w, K, H, out, done, seq, err);
   return hipGetLastError();
 }
 

@@ -66,7 +66,7 @@ enum {
                             durations are summed into eff_stats (adds two event records per call) */
   EFF_CFG_SYNC_HOST = 2u /* eff_decode_layer runs the host share on the calling thread and returns
                             after enqueuing the combine (default: a worker thread runs it and the
-                            compute stream waits for it on a host-mapped word) */
+                            combine kernel waits for it on a host-mapped word) */
 };
 
 typedef struct eff_config {
@@ -175,10 +175,10 @@ int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const in
  * call are read from the pinned pool by the expert kernels themselves, which
  * also write them into their slots.  The control kernel publishes the host ids
  * and x in host-mapped memory; the host share ([FT-deep] §4 ③④) runs on a worker
- * thread and the compute stream waits for it on a host-mapped word before the
- * combine (hipStreamWaitValue64), so the call only enqueues work and returns.
- * With EFF_CFG_SYNC_HOST (or without stream wait-value support) the calling
- * thread waits for the control kernel and runs the host share itself.  An error
+ * thread, and the combine kernel waits for it on a host-mapped word (a bounded
+ * poll), so the call only enqueues work and returns.  With EFF_CFG_SYNC_HOST
+ * the calling thread waits for the control kernel and runs the host share
+ * itself.  An error
  * of the host share is reported by the next call.  ids/w/slots/cpu_ids/counts of
  * the call can be read back with eff_last_layer_info after the stream is done. */
 int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_router,

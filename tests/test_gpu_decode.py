@@ -221,3 +221,21 @@ def test_expert_ffn_outputs(eff, fmt, H, I):
     finally:
         eng.close()
         pool.free()
+
+
+def test_bad_speculative_id_reported(eff, tiny_pool):
+    """A speculative id outside [0, E) is skipped on the device and reported by the next call."""
+    eng = make_engine(eff, tiny_pool, TINY.K, TINY.S, 1, 65536)
+    side = torch.cuda.Stream()
+    try:
+        x = dev_bf16(synth.activations(5, 0, 0, 1, TINY.H))
+        lg = torch.from_numpy(synth.trace_logits(5, 0, TINY.E, 1.1, 0, 1)).cuda()
+        out = torch.empty((1, TINY.H), dtype=torch.int16, device="cuda")
+        bad = torch.tensor([1, TINY.E], dtype=torch.int32, device="cuda")
+        eng.decode_layer(0, x, out, logits=lg, spec_ids=bad, side=side)
+        torch.cuda.synchronize()
+        with pytest.raises(eff.EffError) as ei:
+            eng.decode_layer(1, x, out, logits=lg, side=side)
+        assert ei.value.code == eff.EFF_EDEVICE
+    finally:
+        eng.close()

@@ -22,16 +22,25 @@ def shim(tmp_path_factory):
     hipcc = "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    subprocess.check_call([hipcc, "-O2", "-std=c++17", "-mavx2", "-mfma", "-fPIC", "-shared", "-o", so] + SRC)
+    subprocess.check_call([hipcc, "-O2", "-std=c++17", "--offload-arch=gfx950", "--cuda-host-only", "-mavx2", "-mfma",
+                           "-mf16c", "-fPIC", "-shared", "-o", so] + SRC)
     lib = ctypes.CDLL(so)
     vp, i = ctypes.c_void_p, ctypes.c_int
-    lib.shim_host_ffn.argtypes = [i, i, i, i, i, i, vp, vp, i, vp, vp, i, vp, i]
+    lib.shim_host_ffn.argtypes = [i, i, i, i, i, i, vp, vp, i, vp, vp, i, vp, i, i]
     return lib
 
 
+def isas(shim):
+    return [0, 1] if shim.shim_host_isa_best() == 1 else [0]
+
+
 @pytest.mark.parametrize("fmt,H,I,E,K,B", [(synth.FMT_INT4, 64, 128, 8, 2, 3), (synth.FMT_INT4, 256, 128, 8, 4, 5),
-                                           (synth.FMT_NVFP4, 128, 192, 8, 3, 4), (synth.FMT_NVFP4, 320, 128, 6, 2, 2)])
-def test_host_executor_matches_oracle(shim, fmt, H, I, E, K, B):
+                                           (synth.FMT_NVFP4, 128, 192, 8, 3, 4), (synth.FMT_NVFP4, 320, 128, 6, 2, 2),
+                                           (synth.FMT_INT4, 2048, 512, 8, 4, 6), (synth.FMT_NVFP4, 2560, 640, 6, 3, 5)])
+@pytest.mark.parametrize("isa", [0, 1])
+def test_host_executor_matches_oracle(shim, fmt, H, I, E, K, B, isa):
+    if isa not in isas(shim):
+        pytest.skip("this CPU has no AVX-512 BF16")
     L, layer = 2, 1
     pool, ts = synth.pool_numpy(41, L, E, H, I, fmt)
     x = synth.activations(41, layer, 0, B, H)
@@ -41,7 +50,7 @@ def test_host_executor_matches_oracle(shim, fmt, H, I, E, K, B):
     cpu[rng.random(cpu.size) < 0.3] = -1            # those entries belong to the GPU
     y = np.full((B, K, H), 7.0, np.float32)
     shim.shim_host_ffn(L, E, K, H, I, fmt, pool.ctypes.data, ts.ctypes.data, layer, x.ctypes.data, cpu.ctypes.data,
-                       B, y.ctypes.data, 4)
+                       B, y.ctypes.data, 4, isa)
     xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     for p, e in enumerate(cpu):
         b, k = divmod(p, K)
