@@ -6,9 +6,9 @@
 // whole prompt through one layer so that experts are not re-read per chunk).
 //
 //   k_pf_sort     one workgroup: count (t,k) pairs per expert, scan, place
-//   k_pf_gateup   per (expert, 256 rows of I): [n_e x H] x [H x 256] for gate and up
+//   k_pf_gemm<2>  per (expert, 256 rows of I): [n_e x H] x [H x 256] for gate and up
 //                 on v_mfma_f32_16x16x32_f16, SwiGLU in the epilogue -> fp16 a
-//   k_pf_down     per (expert, 256 rows of H): [n_e x I] x [I x 256] -> fp32 y per pair
+//   k_pf_gemm<1>  per (expert, 256 rows of H): [n_e x I] x [I x 256] -> fp32 y per pair
 //   k_combine     (shared with decode) out[t] = sum_k w[t,k] y[t,k]
 //
 // Weights stay 4-bit in HBM and are dequantized in registers straight into the
@@ -29,7 +29,8 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMT = 64;       // tokens per M pass (4 subtiles of 16)
+constexpr int kPfPrefetch2 = 4;  // weight prefetch depth (k-tiles) of the gate/up GEMM
+constexpr int kPfPrefetch1 = 4;  // ... and of the down GEMM
 
 __global__ void __launch_bounds__(1024)
 k_pf_sort(const int32_t* __restrict__ ids, int n, int E, int slot_base, const int32_t* __restrict__ slot_of,
@@ -127,183 +128,41 @@ __device__ inline f16x8_t dequant8(uint32_t d, uint32_t s2) {
   return __builtin_bit_cast(f16x8_t, u4);
 }
 
-// 4 scales of one lane for the tiles of 4 consecutive row slices (tiles tstride apart, scale
-// areas tstride/8 apart) as fp16 pairs
-template <int FMT>
-__device__ inline void load_scales(const uint8_t* sp, int64_t sstride, uint32_t* s2) {
-  float f[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (FMT == EFF_WFMT_NVFP4_G16_E4M3)
-      f[t] = __builtin_amdgcn_cvt_f32_fp8((uint32_t)sp[t * sstride], 0);
-    else
-      f[t] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(sp + t * sstride) << 16);
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) s2[t] = pk_f16(f[t], f[t]);
-}
-
-// Stage a 64 x 32 activation tile into LDS as fp16 (row-major, 64 B per row).  src_bf16: rows
-// of a bf16 matrix (x, row index t = entry / K); src_f16: rows of an fp16 matrix indexed by
-// sorted position.  Rows >= mt are zero.  int4 permutes each group of 8 as 0,4,1,5,2,6,3,7.
-template <int FMT, bool BF16_SRC>
-__device__ inline void stage_tile(uint32_t* s_tile, const void* src, int ld, const int32_t* rows, int off,
-                                  int m0, int mt, int K, int k0) {
-  const int tid = threadIdx.x;
-  const int row = tid >> 2, ch = tid & 3;  // 64 rows x 4 chunks of 8
-  uint32_t o[4] = {0u, 0u, 0u, 0u};
-  if (row < mt) {
-    uint4 v;
-    if (BF16_SRC) {
-      const int t = rows[off + m0 + row] / K;
-      v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + (int64_t)t * ld + k0 + ch * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-      if (FMT == EFF_WFMT_INT4_G32_BF16) {
-        o[0] = pk_f16(f[0], f[4]); o[1] = pk_f16(f[1], f[5]); o[2] = pk_f16(f[2], f[6]); o[3] = pk_f16(f[3], f[7]);
-      } else {
-        o[0] = pk_f16(f[0], f[1]); o[1] = pk_f16(f[2], f[3]); o[2] = pk_f16(f[4], f[5]); o[3] = pk_f16(f[6], f[7]);
-      }
-    } else {
-      v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + (int64_t)(off + m0 + row) * ld +
-                                          k0 + ch * 8);
-      if (FMT == EFF_WFMT_INT4_G32_BF16) {
-        // halves h0..h7 in v.x = h0|h1, v.y = h2|h3, v.z = h4|h5, v.w = h6|h7
-        o[0] = (v.x & 0xFFFFu) | (v.z << 16);
-        o[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
-        o[2] = (v.y & 0xFFFFu) | (v.w << 16);
-        o[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
-      } else {
-        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-      }
-    }
-  }
-  *reinterpret_cast<uint4*>(s_tile + row * 16 + ch * 4) = make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// The 4 bytes of this lane in the same k tile of 4 consecutive row slices (tstride bytes apart).
-__device__ inline uint4 load_block(const uint8_t* p, int64_t tstride) {
-  return make_uint4(*reinterpret_cast<const uint32_t*>(p), *reinterpret_cast<const uint32_t*>(p + tstride),
-                    *reinterpret_cast<const uint32_t*>(p + 2 * tstride),
-                    *reinterpret_cast<const uint32_t*>(p + 3 * tstride));
+// fp16 pair of a raw scale (int4: bf16 bits; NVFP4: an e4m3 byte), for packed multiplies
+template <int FMT>
+__device__ inline uint32_t scale_pair(uint32_t raw) {
+  const float f = (FMT == EFF_WFMT_NVFP4_G16_E4M3) ? __builtin_amdgcn_cvt_f32_fp8(raw, 0) : __uint_as_float(raw << 16);
+  return pk_f16(f, f);
 }
 
-// grid: E * (I / 256); 4 waves, wave w owns row block nb = j*4 + w of gate and up
-template <int FMT>
-__global__ void __launch_bounds__(256)
-k_pf_gateup(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
-            const int32_t* __restrict__ owner, int slot_base, const int32_t* __restrict__ slot_of,
-            const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows,
-            const uint16_t* __restrict__ x, int E, int H, int I, int K, uint16_t* __restrict__ a_out) {
-  __shared__ uint32_t s_tile[kMT * 16];  // 64 rows x 32 fp16
-  const int NJ = (I / 64 + 3) / 4;
-  int e, j;
-  map_block(blockIdx.x, E, NJ, &e, &j);
-  if (e >= E) return;
-  const int off = offsets[e], ne = offsets[e + 1] - off;
-  if (ne <= 0) return;
-  const int slot = slot_base >= 0 ? slot_base + e : slot_of[e];
-  const uint8_t* rec = arena + (int64_t)slot * R;
-  const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const int NB = I / 64, KB = H / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
-  const int nb = j * 4 + wave;
-  const bool active = nb < NB;  // waves past the last row block only help stage tiles
-  // this wave's 64 rows are row slices 4nb..4nb+3: tiles KB*256 bytes apart, k tiles 256 apart
-  const int64_t tstride = (int64_t)KB * 256, sstride = (int64_t)KB * 32;
-  const uint8_t* gp = rec + (int64_t)nb * 4 * tstride + lane * 4;
-  const uint8_t* gs = rec + 3 * pay + (int64_t)nb * 4 * sstride +
-                      (FMT == EFF_WFMT_INT4_G32_BF16 ? r * 2 : (q >> 1) * 16 + r);
-  float tsg = 1.f, tsu = 1.f;
-  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
-    const int fl = owner[slot];
-    tsg = ts[(int64_t)fl * 3];
-    tsu = ts[(int64_t)fl * 3 + 1];
-  }
-  for (int m0 = 0; m0 < ne; m0 += kMT) {
-    const int mt = min(kMT, ne - m0), msub = (mt + 15) / 16;
-    f32x4_t acc[2][4][4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[m][t][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 wn[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
-    uint32_t sn[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    if (active) {
-      wn[0] = load_block(gp, tstride);
-      wn[1] = load_block(gp + pay, tstride);
-      load_scales<FMT>(gs, sstride, sn[0]);
-      load_scales<FMT>(gs + sca, sstride, sn[1]);
-    }
-    for (int kb = 0; kb < KB; ++kb) {
-      const uint4 wc[2] = {wn[0], wn[1]};
-      uint32_t sc[2][4];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) sc[m][t] = sn[m][t];
-      if (active && kb + 1 < KB) {  // prefetch the next k tile
-        wn[0] = load_block(gp + (kb + 1) * 256, tstride);
-        wn[1] = load_block(gp + pay + (kb + 1) * 256, tstride);
-        load_scales<FMT>(gs + (kb + 1) * 32, sstride, sn[0]);
-        load_scales<FMT>(gs + sca + (kb + 1) * 32, sstride, sn[1]);
-      }
-      __syncthreads();
-      stage_tile<FMT, true>(s_tile, x, H, rows, off, m0, mt, K, kb * 32);
-      __syncthreads();
-      if (!active) continue;
-      f16x8_t af[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s < msub) af[s] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(s_tile + (s * 16 + r) * 16 + q * 4));
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint32_t dw[4] = {wc[m].x, wc[m].y, wc[m].z, wc[m].w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const f16x8_t bfrag = dequant8<FMT>(dw[t], sc[m][t]);
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            if (s < msub) acc[m][t][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], bfrag, acc[m][t][s], 0, 0, 0);
-        }
-      }
-    }
-    // epilogue: a = silu(g) * u, rows m0 + s*16 + 4*q + i, column nb*64 + t*16 + r
-    if (!active) continue;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = s * 16 + q * 4 + i;
-          if (rr < mt) {
-            const float g = acc[0][t][s][i] * tsg, u = acc[1][t][s][i] * tsu;
-            const _Float16 av = (_Float16)(silu(g) * u);
-            a_out[(int64_t)(off + m0 + rr) * I + nb * 64 + t * 16 + r] = __builtin_bit_cast(uint16_t, av);
-          }
-        }
-  }
-}
+constexpr int kMT = 64;         // tokens per pass (4 MFMA subtiles of 16)
+constexpr int kCT = 8;          // k-tiles (of 32 inputs) per staged activation chunk
+constexpr int kRowU32 = 132;    // LDS row stride in dwords: 256 fp16 + 4 dwords of padding
 
-// grid: E * (H / 256); wave w owns row block nb = j*4 + w of down
-template <int FMT>
-__global__ void __launch_bounds__(256)
-k_pf_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
+// Grouped expert GEMM over the (t,k) pairs sorted by expert.  Workgroup = (expert, 256 output
+// rows) with NMAT * 4 waves: wave w computes 64 rows (4 row slices of 16) of matrix w / 4.  All
+// waves share the activation rows of the expert, staged in LDS as fp16 in chunks of 8 k-tiles
+// (256 inputs), double buffered with one barrier per chunk: the next chunk's global loads are
+// issued before the current chunk's MFMAs.  Weights stream from the slot into registers PF
+// k-tiles ahead and are dequantized into the MFMA B operand.
+//   NMAT 2: gate (waves 0-3) and up (waves 4-7) from x (bf16 rows of the tokens); the gate waves
+//           hand g to the up waves through LDS; a = silu(g) * u -> fp16, one row per sorted pair
+//   NMAT 1: down from a (fp16 sorted rows) -> y (fp32, one row per (t,k) pair)
+template <int FMT, int NMAT, int PF>
+__global__ void __launch_bounds__(256 * NMAT, NMAT == 2 ? 1 : 2)
+k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
           const int32_t* __restrict__ owner, int slot_base, const int32_t* __restrict__ slot_of,
-          const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows,
-          const uint16_t* __restrict__ a_in, int E, int H, int I, float* __restrict__ y) {
-  __shared__ uint32_t s_tile[kMT * 16];
-  const int NJ = (H / 64 + 3) / 4;
+          const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows, const uint16_t* __restrict__ src,
+          int E, int H, int I, int K, uint16_t* __restrict__ a_out, float* __restrict__ y_out) {
+  constexpr int TPB = 256 * NMAT;            // threads
+  constexpr int SEGS = TPB / kMT;            // staging threads per row
+  constexpr int SEGW = 256 / SEGS;           // inputs per staging thread per chunk
+  constexpr int SV = SEGW / 8;               // 16-byte vectors per staging thread
+  __shared__ uint32_t s_a[2][kMT * kRowU32];
+  const int N = (NMAT == 2) ? I : H, Kd = (NMAT == 2) ? H : I;
+  const int NJ = (N / 64 + 3) / 4;
   int e, j;
   map_block(blockIdx.x, E, NJ, &e, &j);
   if (e >= E) return;
@@ -312,66 +171,168 @@ k_pf_down(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   const int slot = slot_base >= 0 ? slot_base + e : slot_of[e];
   const uint8_t* rec = arena + (int64_t)slot * R;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const int NB = H / 64, KB = I / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r = lane & 15;
-  const int nb = j * 4 + wave;
-  const bool active = nb < NB;
+  const int KB = Kd / 32, nchunk = (KB + kCT - 1) / kCT;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mat = wave >> 2, wl = wave & 3;
+  const int nb = j * 4 + wl;
+  const bool active = nb < N / 64;  // waves past the last row block only help stage
+  const int mi = (NMAT == 2) ? mat : 2;  // gate, up | down
+  // this wave's 4 row slices: tiles tstride bytes apart, k tiles 256 bytes apart
   const int64_t tstride = (int64_t)KB * 256, sstride = (int64_t)KB * 32;
-  const uint8_t* dp = rec + 2 * pay + (int64_t)nb * 4 * tstride + lane * 4;
-  const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)nb * 4 * sstride +
+  const uint8_t* wp = rec + mi * pay + (int64_t)(active ? nb : 0) * 4 * tstride + lane * 4;
+  const uint8_t* sp = rec + 3 * pay + mi * sca + (int64_t)(active ? nb : 0) * 4 * sstride +
                       (FMT == EFF_WFMT_INT4_G32_BF16 ? r * 2 : (q >> 1) * 16 + r);
-  float tsd = 1.f;
-  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsd = ts[(int64_t)owner[slot] * 3 + 2];
+  float tsc = 1.f;
+  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsc = ts[(int64_t)owner[slot] * 3 + mi];
+  const int srow = tid / SEGS, sseg = tid % SEGS;  // staging role: row srow, inputs sseg*SEGW ..
+
   for (int m0 = 0; m0 < ne; m0 += kMT) {
     const int mt = min(kMT, ne - m0), msub = (mt + 15) / 16;
+    const uint16_t* srow_ptr = nullptr;
+    if (srow < mt) {
+      if (NMAT == 2) srow_ptr = src + (int64_t)(rows[off + m0 + srow] / K) * H;
+      else srow_ptr = src + (int64_t)(off + m0 + srow) * I;
+    }
     f32x4_t acc[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[t][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 wn = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t sn[4] = {0u, 0u, 0u, 0u};
-    if (active) {
-      wn = load_block(dp, tstride);
-      load_scales<FMT>(ds, sstride, sn);
-    }
-    for (int kb = 0; kb < KB; ++kb) {
-      const uint4 wc = wn;
-      uint32_t sc[4] = {sn[0], sn[1], sn[2], sn[3]};
-      if (active && kb + 1 < KB) {
-        wn = load_block(dp + (kb + 1) * 256, tstride);
-        load_scales<FMT>(ds + (kb + 1) * 32, sstride, sn);
-      }
-      __syncthreads();
-      stage_tile<FMT, false>(s_tile, a_in, I, rows, off, m0, mt, 0, kb * 32);
-      __syncthreads();
-      if (!active) continue;
-      f16x8_t af[4];
+      for (int s2 = 0; s2 < 4; ++s2) acc[t][s2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 stg[SV];
+    auto stage_load = [&](int c) {
+      const int k0 = c * kCT * 32 + sseg * SEGW, kn = min(kCT, KB - c * kCT) * 32;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s < msub) af[s] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(s_tile + (s * 16 + r) * 16 + q * 4));
-      const uint32_t dw[4] = {wc.x, wc.y, wc.z, wc.w};
+      for (int z = 0; z < SV; ++z)
+        stg[z] = (srow_ptr && sseg * SEGW + z * 8 < kn) ? *reinterpret_cast<const uint4*>(srow_ptr + k0 + z * 8)
+                                                        : make_uint4(0u, 0u, 0u, 0u);
+    };
+    auto stage_store = [&](int buf) {
+      uint32_t* dst = s_a[buf] + srow * kRowU32 + sseg * (SEGW / 2);
+#pragma unroll
+      for (int z = 0; z < SV; ++z) {
+        const uint4 v = stg[z];
+        uint32_t o[4];
+        if (NMAT == 2) {  // bf16 -> fp16
+          float f[8];
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(wv[i] << 16);
+            f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+          }
+          if (FMT == EFF_WFMT_INT4_G32_BF16) {  // pairs (0,4), (1,5), (2,6), (3,7)
+            o[0] = pk_f16(f[0], f[4]); o[1] = pk_f16(f[1], f[5]); o[2] = pk_f16(f[2], f[6]); o[3] = pk_f16(f[3], f[7]);
+          } else {
+            o[0] = pk_f16(f[0], f[1]); o[1] = pk_f16(f[2], f[3]); o[2] = pk_f16(f[4], f[5]); o[3] = pk_f16(f[6], f[7]);
+          }
+        } else if (FMT == EFF_WFMT_INT4_G32_BF16) {  // fp16 halves h0..h7 -> pairs (0,4) ...
+          o[0] = (v.x & 0xFFFFu) | (v.z << 16);
+          o[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
+          o[2] = (v.y & 0xFFFFu) | (v.w << 16);
+          o[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+        } else {
+          o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+        }
+        *reinterpret_cast<uint4*>(dst + z * 4) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    };
+    // weight ring: k-tile kb lives in slot kb % PF
+    uint32_t wq[PF][4], sq[PF][4];
+    auto wload = [&](int kb, int ring) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const f16x8_t bfrag = dequant8<FMT>(dw[t], sc[t]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          if (s < msub) acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s], bfrag, acc[t][s], 0, 0, 0);
+        if (active && kb < KB) {
+          wq[ring][t] = *reinterpret_cast<const uint32_t*>(wp + t * tstride + kb * 256);
+          sq[ring][t] = (FMT == EFF_WFMT_INT4_G32_BF16)
+                            ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp + t * sstride + kb * 32)
+                            : (uint32_t)sp[t * sstride + kb * 32];
+        } else {
+          wq[ring][t] = 0u;
+          sq[ring][t] = 0u;
+        }
       }
-    }
-    if (!active) continue;
+    };
+    stage_load(0);
+    stage_store(0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int p = 0; p < PF; ++p) wload(p, p);
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < nchunk) stage_load(c + 1);
+      const uint32_t* abase = s_a[buf] + r * kRowU32 + q * 4;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int kk = 0; kk < kCT; ++kk) {
+        const int kb = c * kCT + kk;
+        if (kb < KB) {  // uniform
+          f16x8_t af[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = s * 16 + q * 4 + i;
-          if (rr < mt) {
-            const int p = rows[off + m0 + rr];
-            y[(int64_t)p * H + nb * 64 + t * 16 + r] = acc[t][s][i] * tsd;
+          for (int s2 = 0; s2 < 4; ++s2)
+            if (s2 < msub)
+              af[s2] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(abase + s2 * 16 * kRowU32 + kk * 16));
+          const int ring = kk % PF;  // kCT % PF == 0: static after unrolling
+          uint32_t w[4], sc[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            w[t] = wq[ring][t];
+            sc[t] = sq[ring][t];
+          }
+          wload(kb + PF, ring);  // prefetch
+          if (active) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const f16x8_t bfrag = dequant8<FMT>(w[t], scale_pair<FMT>(sc[t]));
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2)
+                if (s2 < msub) acc[t][s2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s2], bfrag, acc[t][s2], 0, 0, 0);
+            }
           }
         }
+      }
+      if (c + 1 < nchunk) stage_store(buf ^ 1);
+      __syncthreads();
+    }
+    // epilogue: accumulator (t, s2, i) is row m0 + s2*16 + 4q + i, column nb*64 + t*16 + r
+    if (NMAT == 2) {
+      float* g_lds = reinterpret_cast<float*>(&s_a[0][0]);  // [64 rows][256 columns of the workgroup]
+      if (mat == 0 && active) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g_lds[(s2 * 16 + q * 4 + i) * 256 + wl * 64 + t * 16 + r] = acc[t][s2][i] * tsc;
+      }
+      __syncthreads();
+      if (mat == 1 && active) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int rr = s2 * 16 + q * 4 + i;
+              if (rr < mt) {
+                const float g = g_lds[rr * 256 + wl * 64 + t * 16 + r];
+                const _Float16 av = (_Float16)(silu(g) * (acc[t][s2][i] * tsc));
+                a_out[(int64_t)(off + m0 + rr) * I + nb * 64 + t * 16 + r] = __builtin_bit_cast(uint16_t, av);
+              }
+            }
+      }
+      __syncthreads();  // the LDS is restaged by the next pass
+    } else if (active) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = s2 * 16 + q * 4 + i;
+            if (rr < mt) y_out[(int64_t)rows[off + m0 + rr] * H + nb * 64 + t * 16 + r] = acc[t][s2][i] * tsc;
+          }
+    }
   }
 }
 
@@ -393,24 +354,24 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
   const int nbx2 = ((E + 7) / 8) * 8 * ((H / 64 + 3) / 4);
   const int ts = timing_begin(e, EFF_T_PREFILL_GATEUP, s);
   if (fp4)
-    hipLaunchKernelGGL(k_pf_gateup<EFF_WFMT_NVFP4_G16_E4M3>, dim3(nbx1), dim3(256), 0, s, e->d_arena, e->R,
-                       e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, x, E, H, I,
-                       K, e->d_pf_a);
+    hipLaunchKernelGGL((k_pf_gemm<EFF_WFMT_NVFP4_G16_E4M3, 2, kPfPrefetch2>), dim3(nbx1), dim3(512), 0, s, e->d_arena,
+                       e->R, e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, x, E, H, I,
+                       K, e->d_pf_a, (float*)nullptr);
   else
-    hipLaunchKernelGGL(k_pf_gateup<EFF_WFMT_INT4_G32_BF16>, dim3(nbx1), dim3(256), 0, s, e->d_arena, e->R,
-                       e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, x, E, H, I,
-                       K, e->d_pf_a);
+    hipLaunchKernelGGL((k_pf_gemm<EFF_WFMT_INT4_G32_BF16, 2, kPfPrefetch2>), dim3(nbx1), dim3(512), 0, s, e->d_arena,
+                       e->R, e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, x, E, H, I,
+                       K, e->d_pf_a, (float*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
   if (fp4)
-    hipLaunchKernelGGL(k_pf_down<EFF_WFMT_NVFP4_G16_E4M3>, dim3(nbx2), dim3(256), 0, s, e->d_arena, e->R,
-                       e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, e->d_pf_a,
-                       E, H, I, e->d_pf_y);
+    hipLaunchKernelGGL((k_pf_gemm<EFF_WFMT_NVFP4_G16_E4M3, 1, kPfPrefetch1>), dim3(nbx2), dim3(256), 0, s, e->d_arena,
+                       e->R, e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows,
+                       e->d_pf_a, E, H, I, K, (uint16_t*)nullptr, e->d_pf_y);
   else
-    hipLaunchKernelGGL(k_pf_down<EFF_WFMT_INT4_G32_BF16>, dim3(nbx2), dim3(256), 0, s, e->d_arena, e->R,
-                       e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, e->d_pf_a,
-                       E, H, I, e->d_pf_y);
+    hipLaunchKernelGGL((k_pf_gemm<EFF_WFMT_INT4_G32_BF16, 1, kPfPrefetch1>), dim3(nbx2), dim3(256), 0, s, e->d_arena,
+                       e->R, e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows,
+                       e->d_pf_a, E, H, I, K, (uint16_t*)nullptr, e->d_pf_y);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   timing_mark(e, ts, 3, s);
   if (!combine) return hipSuccess;
