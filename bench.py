@@ -256,6 +256,9 @@ def main():
     ap.add_argument("--threads", type=int, default=15)   # host-share pool; one core left for the enqueuing thread
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="first copy this many GiB device to device with torch (a plain copy kernel of known size, "
+                         "the reference for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
@@ -271,6 +274,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
+    if args.calibrate_copy_gib > 0:
+        n = int(args.calibrate_copy_gib * (1 << 30)) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("  copy calibration: %d bytes device to device" % (n * 4))
+        del a, b
     dec = run_decode(eff, torch, synth, A3B, args.steps, args.warmup, args.profile_steps, args.threads)
     cpu = None
     if not args.skip_cpu:

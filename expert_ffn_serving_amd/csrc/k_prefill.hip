@@ -150,7 +150,10 @@ constexpr int kRowU32 = 132;    // LDS row stride in dwords: 256 fp16 + 4 dwords
 //   NMAT 2: gate (waves 0-3) and up (waves 4-7) from x (bf16 rows of the tokens); the gate waves
 //           hand g to the up waves through LDS; a = silu(g) * u -> fp16, one row per sorted pair
 //   NMAT 1: down from a (fp16 sorted rows) -> y (fp32, one row per (t,k) pair)
-template <int FMT, int NMAT, int PF>
+// FULL: the inner dimension is a multiple of 256 (whole chunks): no per-k-tile checks, and
+// loads past the end re-read the last k-tile instead of being skipped (no branches around memory
+// operations, so the compiler's wait counts stay exact and the prefetch stays in flight).
+template <int FMT, int NMAT, int PF, bool FULL>
 __global__ void __launch_bounds__(256 * NMAT, NMAT == 2 ? 1 : 2)
 k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
           const int32_t* __restrict__ owner, int slot_base, const int32_t* __restrict__ slot_of,
@@ -188,12 +191,10 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   const int srow = tid / SEGS, sseg = tid % SEGS;  // staging role: row srow, inputs sseg*SEGW ..
 
   for (int m0 = 0; m0 < ne; m0 += kMT) {
-    const int mt = min(kMT, ne - m0), msub = (mt + 15) / 16;
-    const uint16_t* srow_ptr = nullptr;
-    if (srow < mt) {
-      if (NMAT == 2) srow_ptr = src + (int64_t)(rows[off + m0 + srow] / K) * H;
-      else srow_ptr = src + (int64_t)(off + m0 + srow) * I;
-    }
+    const int mt = min(kMT, ne - m0);
+    // rows past mt stage the pass's first row again (their results are discarded)
+    const int prow = off + m0 + (srow < mt ? srow : 0);
+    const uint16_t* srow_ptr = (NMAT == 2) ? src + (int64_t)(rows[prow] / K) * H : src + (int64_t)prow * I;
     f32x4_t acc[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -204,9 +205,12 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
     auto stage_load = [&](int c) {
       const int k0 = c * kCT * 32 + sseg * SEGW, kn = min(kCT, KB - c * kCT) * 32;
 #pragma unroll
-      for (int z = 0; z < SV; ++z)
-        stg[z] = (srow_ptr && sseg * SEGW + z * 8 < kn) ? *reinterpret_cast<const uint4*>(srow_ptr + k0 + z * 8)
-                                                        : make_uint4(0u, 0u, 0u, 0u);
+      for (int z = 0; z < SV; ++z) {
+        if (FULL) stg[z] = *reinterpret_cast<const uint4*>(srow_ptr + k0 + z * 8);
+        else
+          stg[z] = (sseg * SEGW + z * 8 < kn) ? *reinterpret_cast<const uint4*>(srow_ptr + k0 + z * 8)
+                                              : make_uint4(0u, 0u, 0u, 0u);
+      }
     };
     auto stage_store = [&](int buf) {
       uint32_t* dst = s_a[buf] + srow * kRowU32 + sseg * (SEGW / 2);
@@ -241,6 +245,17 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
     // weight ring: k-tile kb lives in slot kb % PF
     uint32_t wq[PF][4], sq[PF][4];
     auto wload = [&](int kb, int ring) {
+      if (FULL) {
+        const int k = min(kb, KB - 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          wq[ring][t] = *reinterpret_cast<const uint32_t*>(wp + t * tstride + k * 256);
+          sq[ring][t] = (FMT == EFF_WFMT_INT4_G32_BF16)
+                            ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp + t * sstride + k * 32)
+                            : (uint32_t)sp[t * sstride + k * 32];
+        }
+        return;
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (active && kb < KB) {
@@ -266,12 +281,11 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
 #pragma unroll
       for (int kk = 0; kk < kCT; ++kk) {
         const int kb = c * kCT + kk;
-        if (kb < KB) {  // uniform
+        if (FULL || kb < KB) {  // uniform
           f16x8_t af[4];
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2)
-            if (s2 < msub)
-              af[s2] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(abase + s2 * 16 * kRowU32 + kk * 16));
+          for (int s2 = 0; s2 < 4; ++s2)  // all 4 subtiles (rows past mt are discarded): no branches
+            af[s2] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(abase + s2 * 16 * kRowU32 + kk * 16));
           const int ring = kk % PF;  // kCT % PF == 0: static after unrolling
           uint32_t w[4], sc[4];
 #pragma unroll
@@ -286,7 +300,7 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
               const f16x8_t bfrag = dequant8<FMT>(w[t], scale_pair<FMT>(sc[t]));
 #pragma unroll
               for (int s2 = 0; s2 < 4; ++s2)
-                if (s2 < msub) acc[t][s2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s2], bfrag, acc[t][s2], 0, 0, 0);
+                acc[t][s2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s2], bfrag, acc[t][s2], 0, 0, 0);
             }
           }
         }
@@ -323,6 +337,14 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
       }
       __syncthreads();  // the LDS is restaged by the next pass
     } else if (active) {
+      int prow[4][4];  // output rows of this lane, loaded together before any store
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = s2 * 16 + q * 4 + i;
+          prow[s2][i] = rows[off + m0 + (rr < mt ? rr : 0)];
+        }
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -330,7 +352,7 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = s2 * 16 + q * 4 + i;
-            if (rr < mt) y_out[(int64_t)rows[off + m0 + rr] * H + nb * 64 + t * 16 + r] = acc[t][s2][i] * tsc;
+            if (rr < mt) y_out[(int64_t)prow[s2][i] * H + nb * 64 + t * 16 + r] = acc[t][s2][i] * tsc;
           }
     }
   }
@@ -353,25 +375,27 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
   const int nbx1 = ((E + 7) / 8) * 8 * ((I / 64 + 3) / 4);
   const int nbx2 = ((E + 7) / 8) * 8 * ((H / 64 + 3) / 4);
   const int ts = timing_begin(e, EFF_T_PREFILL_GATEUP, s);
-  if (fp4)
-    hipLaunchKernelGGL((k_pf_gemm<EFF_WFMT_NVFP4_G16_E4M3, 2, kPfPrefetch2>), dim3(nbx1), dim3(512), 0, s, e->d_arena,
-                       e->R, e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, x, E, H, I,
-                       K, e->d_pf_a, (float*)nullptr);
-  else
-    hipLaunchKernelGGL((k_pf_gemm<EFF_WFMT_INT4_G32_BF16, 2, kPfPrefetch2>), dim3(nbx1), dim3(512), 0, s, e->d_arena,
-                       e->R, e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, x, E, H, I,
-                       K, e->d_pf_a, (float*)nullptr);
+  const bool full1 = H % 256 == 0, full2 = I % 256 == 0;
+#define EFF_PF_LAUNCH(F, NM, PFD, FU, GRID, SRC, AO, YO)                                                     \
+  hipLaunchKernelGGL((k_pf_gemm<F, NM, PFD, FU>), dim3(GRID), dim3(256 * NM), 0, s, e->d_arena, e->R, e->d_ts, \
+                     e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, SRC, E, H, I, K, AO, YO)
+#define EFF_PF_PICK(NM, PFD, FU, GRID, SRC, AO, YO)                                           \
+  do {                                                                                        \
+    if (fp4) {                                                                                \
+      if (FU) EFF_PF_LAUNCH(EFF_WFMT_NVFP4_G16_E4M3, NM, PFD, true, GRID, SRC, AO, YO);       \
+      else EFF_PF_LAUNCH(EFF_WFMT_NVFP4_G16_E4M3, NM, PFD, false, GRID, SRC, AO, YO);         \
+    } else {                                                                                  \
+      if (FU) EFF_PF_LAUNCH(EFF_WFMT_INT4_G32_BF16, NM, PFD, true, GRID, SRC, AO, YO);        \
+      else EFF_PF_LAUNCH(EFF_WFMT_INT4_G32_BF16, NM, PFD, false, GRID, SRC, AO, YO);          \
+    }                                                                                         \
+  } while (0)
+  EFF_PF_PICK(2, kPfPrefetch2, full1, nbx1, x, e->d_pf_a, (float*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
-  if (fp4)
-    hipLaunchKernelGGL((k_pf_gemm<EFF_WFMT_NVFP4_G16_E4M3, 1, kPfPrefetch1>), dim3(nbx2), dim3(256), 0, s, e->d_arena,
-                       e->R, e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows,
-                       e->d_pf_a, E, H, I, K, (uint16_t*)nullptr, e->d_pf_y);
-  else
-    hipLaunchKernelGGL((k_pf_gemm<EFF_WFMT_INT4_G32_BF16, 1, kPfPrefetch1>), dim3(nbx2), dim3(256), 0, s, e->d_arena,
-                       e->R, e->d_ts, e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows,
-                       e->d_pf_a, E, H, I, K, (uint16_t*)nullptr, e->d_pf_y);
+  EFF_PF_PICK(1, kPfPrefetch1, full2, nbx2, e->d_pf_a, (uint16_t*)nullptr, e->d_pf_y);
+#undef EFF_PF_PICK
+#undef EFF_PF_LAUNCH
   if ((err = hipGetLastError()) != hipSuccess) return err;
   timing_mark(e, ts, 3, s);
   if (!combine) return hipSuccess;
