@@ -140,6 +140,8 @@ __device__ inline uint32_t scale_pair(uint32_t raw) {
 constexpr int kMT = 64;         // tokens per pass (4 MFMA subtiles of 16)
 constexpr int kCT = 8;          // k-tiles (of 32 inputs) per staged activation chunk
 constexpr int kRowU32 = 132;    // LDS row stride in dwords: 256 fp16 + 4 dwords of padding
+constexpr int kGRow = 260;      // row stride (floats) of the gate results handed to the up waves
+static_assert(kMT * kGRow <= 2 * kMT * kRowU32, "gate results fit the staging buffers");
 
 // Grouped expert GEMM over the (t,k) pairs sorted by expert.  Workgroup = (expert, 256 output
 // rows) with NMAT * 4 waves: wave w computes 64 rows (4 row slices of 16) of matrix w / 4.  All
@@ -188,7 +190,16 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
                       (FMT == EFF_WFMT_INT4_G32_BF16 ? r * 2 : (q >> 1) * 16 + r);
   float tsc = 1.f;
   if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsc = ts[(int64_t)owner[slot] * 3 + mi];
-  const int srow = tid / SEGS, sseg = tid % SEGS;  // staging role: row srow, inputs sseg*SEGW ..
+  // Staging role: row srow; piece z (8 inputs, 16 bytes) of the chunk starts at input pbase + z * pstep.
+  // Every 16 (and every 8) consecutive lanes of a 16-byte LDS store hit distinct bank groups (the
+  // row stride of 132 dwords advances the bank by 4 per row):
+  //   NMAT 2: 8 lanes read one 128-byte line of a row (pieces interleaved); the two 8-lane halves of
+  //           a 16-lane group take rows 8 apart (32 banks apart); wave w stages rows w, w+8, ..
+  //   NMAT 1: each thread stages one contiguous 64-input segment; lane bits 0-2 row, 3-4 segment,
+  //           5 row + 8
+  const int srow = (NMAT == 2) ? wave + (lane >> 3) * 8 : wave * 16 + (lane & 7) + (lane >> 5) * 8;
+  const int pbase = (NMAT == 2) ? (lane & 7) * 8 : ((lane >> 3) & 3) * SEGW;
+  constexpr int pstep = (NMAT == 2) ? 64 : 8;
 
   for (int m0 = 0; m0 < ne; m0 += kMT) {
     const int mt = min(kMT, ne - m0);
@@ -203,17 +214,17 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
 
     uint4 stg[SV];
     auto stage_load = [&](int c) {
-      const int k0 = c * kCT * 32 + sseg * SEGW, kn = min(kCT, KB - c * kCT) * 32;
+      const int k0 = c * kCT * 32 + pbase, kn = min(kCT, KB - c * kCT) * 32;
 #pragma unroll
       for (int z = 0; z < SV; ++z) {
-        if (FULL) stg[z] = *reinterpret_cast<const uint4*>(srow_ptr + k0 + z * 8);
+        if (FULL) stg[z] = *reinterpret_cast<const uint4*>(srow_ptr + k0 + z * pstep);
         else
-          stg[z] = (sseg * SEGW + z * 8 < kn) ? *reinterpret_cast<const uint4*>(srow_ptr + k0 + z * 8)
-                                              : make_uint4(0u, 0u, 0u, 0u);
+          stg[z] = (pbase + z * pstep < kn) ? *reinterpret_cast<const uint4*>(srow_ptr + k0 + z * pstep)
+                                            : make_uint4(0u, 0u, 0u, 0u);
       }
     };
     auto stage_store = [&](int buf) {
-      uint32_t* dst = s_a[buf] + srow * kRowU32 + sseg * (SEGW / 2);
+      uint32_t* dst = s_a[buf] + srow * kRowU32 + pbase / 2;
 #pragma unroll
       for (int z = 0; z < SV; ++z) {
         const uint4 v = stg[z];
@@ -239,7 +250,7 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
         } else {
           o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
         }
-        *reinterpret_cast<uint4*>(dst + z * 4) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(dst + z * (pstep / 2)) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     };
     // weight ring: k-tile kb lives in slot kb % PF
@@ -310,14 +321,14 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
     }
     // epilogue: accumulator (t, s2, i) is row m0 + s2*16 + 4q + i, column nb*64 + t*16 + r
     if (NMAT == 2) {
-      float* g_lds = reinterpret_cast<float*>(&s_a[0][0]);  // [64 rows][256 columns of the workgroup]
+      float* g_lds = reinterpret_cast<float*>(&s_a[0][0]);  // [64 rows][256 columns + 4 padding]
       if (mat == 0 && active) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) g_lds[(s2 * 16 + q * 4 + i) * 256 + wl * 64 + t * 16 + r] = acc[t][s2][i] * tsc;
+            for (int i = 0; i < 4; ++i) g_lds[(s2 * 16 + q * 4 + i) * kGRow + wl * 64 + t * 16 + r] = acc[t][s2][i] * tsc;
       }
       __syncthreads();
       if (mat == 1 && active) {
@@ -329,7 +340,7 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
             for (int i = 0; i < 4; ++i) {
               const int rr = s2 * 16 + q * 4 + i;
               if (rr < mt) {
-                const float g = g_lds[rr * 256 + wl * 64 + t * 16 + r];
+                const float g = g_lds[rr * kGRow + wl * 64 + t * 16 + r];
                 const _Float16 av = (_Float16)(silu(g) * (acc[t][s2][i] * tsc));
                 a_out[(int64_t)(off + m0 + rr) * I + nb * 64 + t * 16 + r] = __builtin_bit_cast(uint16_t, av);
               }
