@@ -93,9 +93,11 @@ __device__ inline void map_block(int b, int E, int NJ, int* e, int* j) {
   }
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> fp16 pair (round to nearest even; one v_cvt_pk_f16_f32)
 __device__ inline uint32_t pk_f16(float a, float b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
 }
 
 __device__ inline uint32_t pk_mul(uint32_t a, uint32_t s2) {
@@ -117,12 +119,14 @@ __device__ inline f16x8_t dequant8(uint32_t d, uint32_t s2) {
     o[2] = pk_mul(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2)), s2);
     o[3] = pk_mul(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3)), s2);
   } else {
-    // pairs (e0,e4), (e1,e5), (e2,e6), (e3,e7); the activation tile uses the same order
-    const uint32_t off = 0xE408E408u;  // fp16(-1032) in both halves
-    o[0] = pk_fma_off((d & 0x000F000Fu) | 0x64006400u, off, s2);
-    o[1] = pk_fma_off(((d >> 4) & 0x000F000Fu) | 0x64006400u, off, s2);
-    o[2] = pk_fma_off(((d >> 8) & 0x000F000Fu) | 0x64006400u, off, s2);
-    o[3] = pk_fma_off(((d >> 12) & 0x000F000Fu) | 0x64006400u, off, s2);
+    // pairs (e0,e4), (e1,e5), (e2,e6), (e3,e7); the activation tile uses the same order.  A nibble
+    // at bits 0-3 of a half, under exponent 2^10, reads 1024 + u; at bits 4-7, under 2^6, 64 + u
+    // (mantissa weight 2^-4 * 2^6 per unit); nibbles 2 and 3 take the same two forms after one shift.
+    const uint32_t d8 = d >> 8;
+    o[0] = pk_fma_off((d & 0x000F000Fu) | 0x64006400u, 0xE408E408u, s2);   // -1032
+    o[1] = pk_fma_off((d & 0x00F000F0u) | 0x54005400u, 0xD480D480u, s2);   // -72
+    o[2] = pk_fma_off((d8 & 0x000F000Fu) | 0x64006400u, 0xE408E408u, s2);  // -1032
+    o[3] = pk_fma_off((d8 & 0x00F000F0u) | 0x54005400u, 0xD480D480u, s2);  // -72
   }
   uint4 u4 = make_uint4(o[0], o[1], o[2], o[3]);
   return __builtin_bit_cast(f16x8_t, u4);
@@ -152,7 +156,7 @@ static_assert(kMT * kGRow <= 2 * kMT * kRowU32, "gate results fit the staging bu
 //   NMAT 2: gate (waves 0-3) and up (waves 4-7) from x (bf16 rows of the tokens); the gate waves
 //           hand g to the up waves through LDS; a = silu(g) * u -> fp16, one row per sorted pair
 //   NMAT 1: down from a (fp16 sorted rows) -> y (fp32, one row per (t,k) pair)
-// FULL: the inner dimension is a multiple of 256 (whole chunks): no per-k-tile checks, and
+// FULL: H and I are multiples of 256 (whole chunks, whole row blocks): no per-k-tile checks, and
 // loads past the end re-read the last k-tile instead of being skipped (no branches around memory
 // operations, so the compiler's wait counts stay exact and the prefetch stays in flight).
 template <int FMT, int NMAT, int PF, bool FULL>
@@ -181,13 +185,22 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mat = wave >> 2, wl = wave & 3;
   const int nb = j * 4 + wl;
-  const bool active = nb < N / 64;  // waves past the last row block only help stage
+  // waves past the last row block only help stage (never with FULL: both dimensions are whole chunks)
+  const bool active = FULL || nb < N / 64;
   const int mi = (NMAT == 2) ? mat : 2;  // gate, up | down
-  // this wave's 4 row slices: tiles tstride bytes apart, k tiles 256 bytes apart
-  const int64_t tstride = (int64_t)KB * 256, sstride = (int64_t)KB * 32;
-  const uint8_t* wp = rec + mi * pay + (int64_t)(active ? nb : 0) * 4 * tstride + lane * 4;
-  const uint8_t* sp = rec + 3 * pay + mi * sca + (int64_t)(active ? nb : 0) * 4 * sstride +
-                      (FMT == EFF_WFMT_INT4_G32_BF16 ? r * 2 : (q >> 1) * 16 + r);
+  // this wave's 4 row slices: tiles tstride bytes apart, k tiles 256 bytes apart.  The record is read
+  // through a buffer resource: the per-lane part of each address is a constant offset register and the
+  // k-tile part a scalar offset, so the weight stream costs no vector address arithmetic (a record is
+  // far below 2 GiB, so 32-bit offsets suffice).
+  const int tstride = KB * 256, sstride = KB * 32;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, (int)R, 0x00020000);
+  int woff[4], soff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    woff[t] = (int)(mi * pay) + ((active ? nb : 0) * 4 + t) * tstride + lane * 4;
+    soff[t] = (int)(3 * pay + mi * sca) + ((active ? nb : 0) * 4 + t) * sstride +
+              (FMT == EFF_WFMT_INT4_G32_BF16 ? r * 2 : (q >> 1) * 16 + r);
+  }
   float tsc = 1.f;
   if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsc = ts[(int64_t)owner[slot] * 3 + mi];
   // Staging role: row srow; piece z (8 inputs, 16 bytes) of the chunk starts at input pbase + z * pstep.
@@ -255,26 +268,23 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
     };
     // weight ring: k-tile kb lives in slot kb % PF
     uint32_t wq[PF][4], sq[PF][4];
-    auto wload = [&](int kb, int ring) {
-      if (FULL) {
-        const int k = min(kb, KB - 1);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          wq[ring][t] = *reinterpret_cast<const uint32_t*>(wp + t * tstride + k * 256);
-          sq[ring][t] = (FMT == EFF_WFMT_INT4_G32_BF16)
-                            ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp + t * sstride + k * 32)
-                            : (uint32_t)sp[t * sstride + k * 32];
-        }
-        return;
-      }
+    auto wtile = [&](int k, int ring) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (active && kb < KB) {
-          wq[ring][t] = *reinterpret_cast<const uint32_t*>(wp + t * tstride + kb * 256);
-          sq[ring][t] = (FMT == EFF_WFMT_INT4_G32_BF16)
-                            ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp + t * sstride + kb * 32)
-                            : (uint32_t)sp[t * sstride + kb * 32];
-        } else {
+        wq[ring][t] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, woff[t], k * 256, 0);
+        sq[ring][t] = (FMT == EFF_WFMT_INT4_G32_BF16)
+                          ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, soff[t], k * 32, 0)
+                          : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsrc, soff[t], k * 32, 0);
+      }
+    };
+    auto wload = [&](int kb, int ring) {
+      if (FULL) {
+        wtile(min(kb, KB - 1), ring);
+      } else if (active && kb < KB) {
+        wtile(kb, ring);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
           wq[ring][t] = 0u;
           sq[ring][t] = 0u;
         }
@@ -289,14 +299,25 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
       const int buf = c & 1;
       if (c + 1 < nchunk) stage_load(c + 1);
       const uint32_t* abase = s_a[buf] + r * kRowU32 + q * 4;
+      // A fragments (all 4 subtiles; rows past mt are discarded: no branches), read one k-tile ahead
+      f16x8_t an[4];
+      auto aread = [&](int kk) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          an[s2] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(abase + s2 * 16 * kRowU32 + kk * 16));
+      };
+      aread(0);
 #pragma unroll
       for (int kk = 0; kk < kCT; ++kk) {
         const int kb = c * kCT + kk;
+        // k-tile boundary: work on ring slots of later k-tiles (their loads may still be in flight) is
+        // not hoisted into this one, which would wait on the whole prefetch
+        __builtin_amdgcn_sched_barrier(0);
         if (FULL || kb < KB) {  // uniform
           f16x8_t af[4];
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2)  // all 4 subtiles (rows past mt are discarded): no branches
-            af[s2] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(abase + s2 * 16 * kRowU32 + kk * 16));
+          for (int s2 = 0; s2 < 4; ++s2) af[s2] = an[s2];
+          if (kk + 1 < kCT) aread(kk + 1);
           const int ring = kk % PF;  // kCT % PF == 0: static after unrolling
           uint32_t w[4], sc[4];
 #pragma unroll
@@ -305,6 +326,7 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
             sc[t] = sq[ring][t];
           }
           wload(kb + PF, ring);  // prefetch
+          __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued ahead of this k-tile's math
           if (active) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -386,7 +408,7 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
   const int nbx1 = ((E + 7) / 8) * 8 * ((I / 64 + 3) / 4);
   const int nbx2 = ((E + 7) / 8) * 8 * ((H / 64 + 3) / 4);
   const int ts = timing_begin(e, EFF_T_PREFILL_GATEUP, s);
-  const bool full1 = H % 256 == 0, full2 = I % 256 == 0;
+  const bool full = H % 256 == 0 && I % 256 == 0;
 #define EFF_PF_LAUNCH(F, NM, PFD, FU, GRID, SRC, AO, YO)                                                     \
   hipLaunchKernelGGL((k_pf_gemm<F, NM, PFD, FU>), dim3(GRID), dim3(256 * NM), 0, s, e->d_arena, e->R, e->d_ts, \
                      e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, SRC, E, H, I, K, AO, YO)
@@ -400,11 +422,11 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
       else EFF_PF_LAUNCH(EFF_WFMT_INT4_G32_BF16, NM, PFD, false, GRID, SRC, AO, YO);          \
     }                                                                                         \
   } while (0)
-  EFF_PF_PICK(2, kPfPrefetch2, full1, nbx1, x, e->d_pf_a, (float*)nullptr);
+  EFF_PF_PICK(2, kPfPrefetch2, full, nbx1, x, e->d_pf_a, (float*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
-  EFF_PF_PICK(1, kPfPrefetch1, full2, nbx2, e->d_pf_a, (uint16_t*)nullptr, e->d_pf_y);
+  EFF_PF_PICK(1, kPfPrefetch1, full, nbx2, e->d_pf_a, (uint16_t*)nullptr, e->d_pf_y);
 #undef EFF_PF_PICK
 #undef EFF_PF_LAUNCH
   if ((err = hipGetLastError()) != hipSuccess) return err;
