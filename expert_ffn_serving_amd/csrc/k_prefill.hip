@@ -30,7 +30,8 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPfPrefetch2 = 4;  // weight prefetch depth (k-tiles) of the gate/up GEMM
-constexpr int kPfPrefetch1 = 4;  // ... and of the down GEMM
+constexpr int kPfPrefetch1 = 4;
+constexpr int kPfLead = 12, kPfPer = 3;  // VALU ops before the first MFMA of a k-tile / after each MFMA  // ... and of the down GEMM
 
 __global__ void __launch_bounds__(1024)
 k_pf_sort(const int32_t* __restrict__ ids, int n, int E, int slot_base, const int32_t* __restrict__ slot_of,
@@ -335,6 +336,16 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
               for (int s2 = 0; s2 < 4; ++s2)
                 acc[t][s2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[s2], bfrag, acc[t][s2], 0, 0, 0);
             }
+            // issue pattern: the first slice's dequant, then each MFMA followed by a few VALU ops of the
+            // next slice's dequant, so one wave keeps the matrix pipe fed while it dequantizes
+            __builtin_amdgcn_sched_group_barrier(0x002, kPfLead, 0);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, kPfPer, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           }
         }
       }
