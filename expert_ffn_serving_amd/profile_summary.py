@@ -1,0 +1,118 @@
+"""Text summaries of rocprofv3 output (kernel statistics and PMC counters).
+
+    python3 -m expert_ffn_serving_amd.profile_summary counters DIR
+        per-kernel totals of every counter in DIR/**/*counter_collection.csv
+    python3 -m expert_ffn_serving_amd.profile_summary traffic --fetch DIR --write DIR \\
+            --kernel k_gateup --copy-bytes 1073741824 --source k_decode.hip --out FILE.json
+        HBM bytes per dispatch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run.  Each
+        counter is scaled by what it reads for the largest plain device-to-device copy in the same
+        run (a copy of --copy-bytes bytes reads and writes exactly that many bytes).
+
+Counters are KiB per dispatch.  On gfx950 FETCH_SIZE reads about half of the bytes a copy
+actually fetches, which is why every figure is calibrated against the copy instead of trusted raw.
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_name(raw):
+    n = raw.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+    return n.replace("eff::", "")
+
+
+def source_sha(*names):
+    """Same hash as the bench's source_sha: sha256 over the named csrc files, 16 hex digits."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "expert_ffn_serving_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters(d):
+    """{(kernel, counter): [value per dispatch]} from a rocprofv3 --pmc csv directory."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    per = collections.defaultdict(float)
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            per[(kernel_name(r["Kernel_Name"]), r["Counter_Name"], r.get("Dispatch_Id", ""))] += float(r["Counter_Value"])
+    out = collections.defaultdict(list)
+    for (k, c, _), v in per.items():
+        out[(k, c)].append(v)
+    return out
+
+
+def cmd_counters(a):
+    data = read_counters(a.dir)
+    print("kernel\tcounter\tdispatches\ttotal\tper_dispatch")
+    for (k, c), v in sorted(data.items()):
+        print("%s\t%s\t%d\t%.6g\t%.6g" % (k, c, len(v), sum(v), sum(v) / len(v)))
+
+
+def per_dispatch(data, counter, kernel):
+    vals = [v for (k, c), vs in data.items() if c == counter and k.startswith(kernel) for v in vs]
+    if not vals:
+        raise SystemExit("no %s dispatches of %s" % (counter, kernel))
+    return sum(vals) / len(vals), len(vals)
+
+
+def copy_factor(data, counter, copy_bytes):
+    vals = [v for (k, c), vs in data.items() if c == counter and k.startswith(COPY_KERNEL) for v in vs]
+    if not vals:
+        raise SystemExit("no %s copy dispatch to calibrate against" % counter)
+    return copy_bytes / (max(vals) * 1024.0)
+
+
+def cmd_traffic(a):
+    fd, wd = read_counters(a.fetch), read_counters(a.write)
+    ff, wf = copy_factor(fd, "FETCH_SIZE", a.copy_bytes), copy_factor(wd, "WRITE_SIZE", a.copy_bytes)
+    fk, nf = per_dispatch(fd, "FETCH_SIZE", a.kernel)
+    wk, nw = per_dispatch(wd, "WRITE_SIZE", a.kernel)
+    res = {
+        "kernel": a.kernel,
+        "hbm_bytes_per_launch": int(round(fk * 1024 * ff + wk * 1024 * wf)),
+        "fetch_kib_per_dispatch": round(fk, 3), "write_kib_per_dispatch": round(wk, 3),
+        "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+        "dispatches": [nf, nw], "copy_bytes": a.copy_bytes,
+        "source_sha": source_sha(*a.source),
+        "sources": a.source,
+    }
+    if a.command:
+        res["command"] = a.command
+    text = json.dumps(res, indent=1)
+    if a.out:
+        with open(a.out, "w") as o:
+            o.write(text + "\n")
+    print(text)
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = p.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=int, default=1 << 30)
+    t.add_argument("--source", nargs="+", default=["k_decode.hip"])
+    t.add_argument("--command", default="")
+    t.add_argument("--out", default="")
+    a = p.parse_args(argv)
+    {"counters": cmd_counters, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
