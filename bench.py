@@ -207,12 +207,15 @@ def run_prefill(eff, torch, synth, W, layers, threads):
         "gemm_ms_per_layer": round((g_ms + d_ms) / max(1, n), 3),
         "gateup_ms_per_layer": round(g_ms / max(1, n), 3), "down_ms_per_layer": round(d_ms / max(1, n), 3),
         "weight_GBps": round(wbytes * n / ((g_ms + d_ms) * 1e-3) / 1e9, 1),
+        "weight_hbm_frac": round(wbytes * n / ((g_ms + d_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "wall_ms_per_layer_with_streaming": round(wall * 1e3 / layers, 2),
         "stream_GBps": round(wbytes * layers / wall / 1e9, 1),
         "source_sha": src_hash("k_prefill.hip"),
     }
-    log("  prefill: %.1f TFLOP/s (%.1f%% of MFMA peak), GEMM %.3f ms/layer, wall %.1f ms/layer" % (
-        tflops, 100 * tflops / MFMA_PEAK_TFLOPS, (g_ms + d_ms) / max(1, n), wall * 1e3 / layers))
+    log("  prefill: %.1f TFLOP/s (%.1f%% of MFMA peak), weights %.0f GB/s (%.1f%% of HBM peak), GEMM %.3f ms/layer, "
+        "wall %.1f ms/layer" % (tflops, 100 * tflops / MFMA_PEAK_TFLOPS, wbytes * n / ((g_ms + d_ms) * 1e-3) / 1e9,
+                                100 * wbytes * n / ((g_ms + d_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                (g_ms + d_ms) / max(1, n), wall * 1e3 / layers))
     eng.close()
     eff.host_free(ptr)
     return res
