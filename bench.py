@@ -251,12 +251,14 @@ def cpu_baseline(synth, W, pool, tokens, threads):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=1024)
     ap.add_argument("--profile-steps", type=int, default=64)
     ap.add_argument("--prefill-layers", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=4)
-    ap.add_argument("--threads", type=int, default=15)   # host-share pool; one core left for the enqueuing thread
+    # host-share pool: 11 workers + the engine's worker thread, which leaves cores of a 16-core host for
+    # the enqueuing thread and the runtime (on 16 cores: 15 threads gave 430-446 tok/s, 12 gave 476-478)
+    ap.add_argument("--threads", type=int, default=12)
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
