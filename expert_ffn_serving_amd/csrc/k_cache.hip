@@ -487,10 +487,50 @@ __device__ inline void topk_row(const float* row, int E, int K, int32_t* ids, fl
 __device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, const int32_t* lds_hit, int64_t base,
                           const int32_t* __restrict__ owner, int n, int S, int maxU, int maxB, DecodePlan* plan,
                           int32_t* scratch) {
+  const int tid = threadIdx.x;
+  if (n <= 64) {
+    // one wave, lane p = entry p: each lane learns which lanes share its slot and which hold a
+    // smaller slot from one uniform readlane sweep (registers only; no LDS round trips)
+    if (tid < 64) {
+      int v = -1;
+      if (tid < n) {
+        const int sl = lds_slot[tid];
+        v = (sl >= 0 && sl < S) ? sl : -1;  // slots outside the arena are never read
+      }
+      uint64_t same = 0, less = 0;
+      for (int q = 0; q < n; ++q) {
+        const int vq = __builtin_amdgcn_readlane(v, q);
+        same |= (uint64_t)(vq == v) << q;
+        less |= (uint64_t)(vq < v) << q;
+      }
+      const bool first = v >= 0 && (same & ((1ull << tid) - 1)) == 0;
+      const uint64_t fm = __ballot(first);
+      const int rank = __popcll(less & fm);  // distinct valid slots below v: units in ascending slot order
+      const int nu = min(__popcll(fm), maxU);
+      if (first && rank < maxU) {  // more distinct slots than a layer has experts: not computed
+        DecodeUnit& un = plan->unit[rank];
+        int cnt = 0;
+        for (uint64_t m = same; m && cnt < maxB; m &= m - 1)  // a slot appears at most once per token
+          un.entry[cnt++] = __builtin_ctzll(m);
+        un.slot = v;
+        un.count = cnt;
+        un.flat = lds_id ? (int32_t)(base + lds_id[tid]) : owner[v];
+        un.fetch = (lds_hit && lds_hit[tid] < 0) ? 1 : 0;
+      }
+      for (int u = nu + tid; u < maxU; u += 64) {
+        plan->unit[u].count = 0;
+        plan->unit[u].slot = 0;
+        plan->unit[u].flat = 0;
+        plan->unit[u].fetch = 0;
+      }
+      if (tid == 0) plan->nu = nu;
+    }
+    lds_sync();
+    return;
+  }
   int32_t* s_sl = scratch;
   int32_t* s_first = scratch + kMaxEntries;
   __shared__ int s_nu;
-  const int tid = threadIdx.x;
   if (tid == 0) s_nu = 0;
   for (int p = tid; p < n; p += blockDim.x) {
     const int v = lds_slot[p];
@@ -585,6 +625,16 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
   __shared__ CallLds C;
   const int tid = threadIdx.x;
   const int n = B * K;
+  if (tid >= 64) {
+    // waves 1.. copy x for the host while wave 0 starts the top-K, and wait until their stores
+    // have completed before they reach the first barrier.  x_host is coherent host memory (not
+    // held in the L2), so a completed store is visible to the host, and the call word that wave 0
+    // publishes after the last barrier is ordered after it.  (A system-scope fence here would
+    // also write back the L2 from every wave, which costs microseconds on the critical path.)
+    for (int i = tid - 64; i < B * H / 8; i += kThreads - 64)
+      reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
+    if (call_ring) __builtin_amdgcn_s_waitcnt(0);
+  }
   for (int t = tid >> 6; t < B; t += kThreads / 64)
     topk_row(logits + (int64_t)t * c.E, c.E, K, ids + (int64_t)t * K, w + (int64_t)t * K, C.id + t * K);
   lds_sync();
@@ -608,15 +658,15 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
     commit_body(c, C, true, spec_slots, nullptr, nullptr, counts + 3);
   }
   if (tid < 64) {
-    // the host's copy of x, then the call word after a system-scope fence
-    for (int i = tid; i < B * H / 8; i += 64)
-      reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
+    // the call word after a system-scope fence (which covers wave 0's host ids; x was fenced by
+    // the waves that copied it, before the first barrier)
     if (call_ring) {
       __threadfence_system();
       if (tid == 0) {
-        __hip_atomic_store(call_ring + seq % kCallRing, (seq << 16) | (uint64_t)nhost, __ATOMIC_RELEASE,
+        // relaxed stores after the release fence (a release store would write back the L2 again)
+        __hip_atomic_store(call_ring + seq % kCallRing, (seq << 16) | (uint64_t)nhost, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
-        if (nhost == 0) __hip_atomic_store(host_done, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (nhost == 0) __hip_atomic_store(host_done, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }
