@@ -99,6 +99,41 @@ __device__ void ensure_body(const CacheState& c, int layer, int n, int spec, Cal
     C.spec = spec;
     C.err = 0;
   }
+  if (n <= 64) {
+    // one wave, lane p = entry p: the table lookup, then one uniform readlane sweep gives each lane
+    // the entries with the same id and with smaller ids (registers only; no LDS round trips).
+    // Wave 0 also holds tid 0, whose initialisation above it follows in program order.
+    if (tid < 64) {
+      int v = tid < n ? C.id[tid] : -1;
+      const bool bad = tid < n && (v < 0 || v >= E);
+      if (bad) v = -1;
+      const int hit = (v >= 0) ? c.table[(int64_t)layer * E + v] : -1;
+      uint64_t same = 0, less = 0;
+      for (int q = 0; q < n; ++q) {
+        const int vq = __builtin_amdgcn_readlane(v, q);
+        same |= (uint64_t)(vq == v) << q;
+        less |= (uint64_t)(vq < v) << q;
+      }
+      const bool first = v >= 0 && (same & ((1ull << tid) - 1)) == 0;
+      const uint64_t fm = __ballot(first), mm = __ballot(first && hit < 0), badm = __ballot(bad);
+      if (tid < n) {
+        C.id[tid] = v;
+        C.hit[tid] = hit;
+        C.first[tid] = first;
+      }
+      if (first) {
+        C.uniq[__popcll(less & fm)] = v;
+        if (hit < 0) C.miss[__popcll(less & mm)] = v;
+      }
+      if (tid == 0) {
+        C.nu = __popcll(fm);
+        C.nm = __popcll(mm);
+        C.err = badm ? 1 : 0;
+      }
+    }
+    lds_sync();
+    return;
+  }
   for (int p = tid; p < n; p += kThreads) {
     int v = C.id[p];
     if (v < 0 || v >= E) {
@@ -473,10 +508,77 @@ __device__ void wave_topk(const float* __restrict__ row, int E, int K, int32_t* 
   }
 }
 
+// The same selection with each lane's keys sorted once, by (key desc, element asc): a lane's
+// candidate is then the head of its list.  A round is one wave max over the heads; when a single
+// lane holds that key (the common case) it is the winner, since a lane's later keys are no larger
+// and its elements are in id order.  Equal keys in several lanes fall back to the lowest id among
+// them.  The winner shifts its list.
+template <int NJ>
+__device__ void wave_topk_sorted(const float* __restrict__ row, int E, int K, int32_t* __restrict__ ids,
+                                 float* __restrict__ w, int32_t* lds_ids) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[NJ];
+  int el[NJ];  // element id lane + 64*j of each key
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? order_key(row[e]) : 0u;
+    el[j] = e;
+  }
+  // insertion sort, descending; a strict comparison keeps equal keys in element order
+#pragma unroll
+  for (int i = 1; i < NJ; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const bool sw = key[j] > key[j - 1];
+      const uint32_t ka = key[j - 1], kb = key[j];
+      const int ea = el[j - 1], eb = el[j];
+      key[j - 1] = sw ? kb : ka;
+      key[j] = sw ? ka : kb;
+      el[j - 1] = sw ? eb : ea;
+      el[j] = sw ? ea : eb;
+    }
+  float mysel = 0.f;  // lane k keeps the k-th selected logit
+  int myid = 0;
+  for (int k = 0; k < K; ++k) {
+    const uint32_t m = wave_reduce_u32<true>(key[0]);
+    const uint64_t hold = __ballot(key[0] == m);
+    int win;
+    if (__popcll(hold) == 1) {
+      win = __builtin_ctzll(hold);
+    } else {
+      const uint32_t cand = key[0] == m ? (uint32_t)el[0] : 0xFFFFFFFFu;
+      win = (int)(wave_reduce_u32<false>(cand) & 63);
+    }
+    const int id = __builtin_amdgcn_readlane(el[0], win);
+    if (lane == win) {
+#pragma unroll
+      for (int j = 0; j + 1 < NJ; ++j) {
+        key[j] = key[j + 1];
+        el[j] = el[j + 1];
+      }
+      key[NJ - 1] = 0u;
+    }
+    if (lane == k) {
+      mysel = key_value(m);
+      myid = id;
+    }
+  }
+  // softmax over the K selected logits, relative to the largest (lane 0's)
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mysel), 0));
+  const float ex = lane < K ? expf(mysel - top) : 0.f;
+  const float sum = wave_sum_f32(ex);
+  if (lane < K) {
+    ids[lane] = myid;
+    w[lane] = ex / sum;
+    if (lds_ids) lds_ids[lane] = myid;
+  }
+}
+
 __device__ inline void topk_row(const float* row, int E, int K, int32_t* ids, float* w, int32_t* lds_ids) {
-  if (E <= 256) wave_topk<4>(row, E, K, ids, w, lds_ids);
-  else if (E <= 512) wave_topk<8>(row, E, K, ids, w, lds_ids);
-  else if (E <= 1024) wave_topk<16>(row, E, K, ids, w, lds_ids);
+  if (E <= 256) wave_topk_sorted<4>(row, E, K, ids, w, lds_ids);
+  else if (E <= 512) wave_topk_sorted<8>(row, E, K, ids, w, lds_ids);
+  else if (E <= 1024) wave_topk_sorted<16>(row, E, K, ids, w, lds_ids);
   else wave_topk<0>(row, E, K, ids, w, lds_ids);
 }
 
@@ -626,20 +728,20 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
   const int tid = threadIdx.x;
   const int n = B * K;
   if (tid >= 64) {
-    // waves 1.. copy x for the host while wave 0 starts the top-K, and wait until their stores
-    // have completed before they reach the first barrier.  x_host is coherent host memory (not
-    // held in the L2), so a completed store is visible to the host, and the call word that wave 0
-    // publishes after the last barrier is ordered after it.  (A system-scope fence here would
-    // also write back the L2 from every wave, which costs microseconds on the critical path.)
+    // waves 1.. copy x for the host while wave 0 starts the top-K.  They wait for these stores
+    // to complete only after the split (below), before the plan's barrier: x_host is coherent host
+    // memory (not held in the L2), so a completed store is visible to the host, and the call word
+    // that wave 0 publishes after the last barrier is ordered after it.  (A system-scope fence
+    // would also write back the L2 from every wave, which costs microseconds.)
     for (int i = tid - 64; i < B * H / 8; i += kThreads - 64)
       reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
-    if (call_ring) __builtin_amdgcn_s_waitcnt(0);
   }
   for (int t = tid >> 6; t < B; t += kThreads / 64)
     topk_row(logits + (int64_t)t * c.E, c.E, K, ids + (int64_t)t * K, w + (int64_t)t * K, C.id + t * K);
   lds_sync();
   ensure_body(c, layer, n, 0, C);
   split_body(c, C, s_key);
+  if (tid >= 64 && call_ring) __builtin_amdgcn_s_waitcnt(0);  // x_host stores complete (see above)
   plan_body(C.slot, C.id, C.hit, (int64_t)layer * c.E, c.owner, n, c.S, maxU, maxB, plan,
             reinterpret_cast<int32_t*>(s_key));
   commit_body(c, C, true, slots, cpu, cpu_host, counts);

@@ -75,15 +75,18 @@ def test_route_ids_bit_exact(eff, H, E, K, B):
         pool.free()
 
 
-def test_route_logits_traces_and_ties(eff):
+@pytest.mark.parametrize("E", [256, 512])
+def test_route_logits_traces_and_ties(eff, E):
     pool = PinnedPool(eff, 5, 1, 1, 64, 64, synth.FMT_INT4)
-    E, K, B = 512, 10, 16
+    K, B = 10, 16
     cfg = eff.make_config(1, E, K, 64, 64, 0, 0, B, 0, 65536, 2)
     eng = eff.Engine(cfg, pool.ptr)
     try:
         lg = synth.trace_logits(3, 0, E, 1.2, 0, B)
         lg[0, :] = 0.0            # all tied: ids 0..K-1
-        lg[1, 7] = lg[1, 9] = lg[1, 300] = 50.0
+        lg[1, 7] = lg[1, 9] = lg[1, 200] = 50.0
+        lg[2, [131, 67, 3, 2]] = 40.0   # equal logits inside one lane (3, 67, 131) and beside it (2)
+        lg[3, [70, 6, 134]] = 30.0      # one lane's equal logits only
         ids = torch.empty((B, K), dtype=torch.int32, device="cuda")
         w = torch.empty((B, K), dtype=torch.float32, device="cuda")
         eng.route_logits(torch.from_numpy(lg).cuda(), ids, w)
@@ -91,7 +94,8 @@ def test_route_logits_traces_and_ties(eff):
         rid, rw = topk_softmax(lg, K)
         got = ids.cpu().numpy()
         assert np.array_equal(got, rid)
-        assert list(got[0]) == list(range(K)) and list(got[1][:3]) == [7, 9, 300]
+        assert list(got[0]) == list(range(K)) and list(got[1][:3]) == [7, 9, 200]
+        assert list(got[2][:4]) == [2, 3, 67, 131] and list(got[3][:3]) == [6, 70, 134]
         assert np.allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
     finally:
         eng.close()
