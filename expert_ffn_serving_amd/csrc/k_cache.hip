@@ -167,11 +167,31 @@ __device__ void ensure_body(const CacheState& c, int layer, int n, int spec, Cal
 }
 
 // Block-wide min of a 64-bit key; every thread gets the result.
-__device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* s_red) {
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o);
-    v = w < v ? w : v;
+// Minimum over the wave of a 64-bit value, with DPP moves of both halves (no LDS round trips);
+// lanes outside a DPP source row see the identity (all ones).
+__device__ inline uint64_t wave_min_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+#define EFF_DPP_MIN64(ctrl, rmask)                                                                      \
+  {                                                                                                     \
+    const uint32_t ol = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)lo, ctrl, rmask, 0xF, false);    \
+    const uint32_t oh = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)hi, ctrl, rmask, 0xF, false);    \
+    const bool lt = oh < hi || (oh == hi && ol < lo);                                                   \
+    lo = lt ? ol : lo;                                                                                  \
+    hi = lt ? oh : hi;                                                                                  \
   }
+  EFF_DPP_MIN64(0xB1, 0xF)   // quad_perm [1,0,3,2]
+  EFF_DPP_MIN64(0x4E, 0xF)   // quad_perm [2,3,0,1]
+  EFF_DPP_MIN64(0x124, 0xF)  // row_ror:4
+  EFF_DPP_MIN64(0x128, 0xF)  // row_ror:8
+  EFF_DPP_MIN64(0x142, 0xA)  // row_bcast:15 into rows 1, 3
+  EFF_DPP_MIN64(0x143, 0xC)  // row_bcast:31 into rows 2, 3
+#undef EFF_DPP_MIN64
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+}
+
+__device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* s_red) {
+  v = wave_min_u64(v);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) s_red[wave] = v;
   lds_sync();
@@ -196,21 +216,27 @@ __device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key) {
   if (q > 0) {
     if (tid == 0) C.nv = 0;
     lds_sync();
-    // the misses' recency and the victim keys, loaded together
-    for (int i = tid; i < m; i += kThreads) C.mrec[i] = c.recency[base + C.miss[i]];
-    int local_nv = 0;
-    for (int v = tid; v < c.sort_pow2; v += kThreads) {
-      uint64_t key = kInfKey;
-      if (v < S) {
-        const int64_t u = c.usage[v];
-        if (u < floor_) {  // slots with usage below the floor, ordered by (usage, slot)
-          key = ((uint64_t)(u + 1) << 14) | (uint64_t)v;
-          ++local_nv;
-        }
-      }
-      s_key[v] = key;
+    // the misses' recency and the victim keys: every load is issued before any is used (a loop that
+    // consumed each load in turn would pay one global round trip per slot a thread owns)
+    static_assert(kMaxEntries <= kThreads && kMaxSlots % kThreads == 0, "one miss per thread, whole rounds");
+    constexpr int kPer = kMaxSlots / kThreads;
+    const int64_t mr = tid < m ? c.recency[base + C.miss[tid]] : 0;
+    int64_t us[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = tid + i * kThreads;
+      us[i] = v < S ? c.usage[v] : 0;
     }
-    if (local_nv) atomicAdd(&C.nv, local_nv);
+    if (tid < m) C.mrec[tid] = mr;
+    int wave_nv = 0;  // counted per wave with ballots: one LDS atomic per wave, not per thread
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int v = tid + i * kThreads;
+      const bool below = v < S && us[i] < floor_;  // slots with usage below the floor, by (usage, slot)
+      if (v < c.sort_pow2) s_key[v] = below ? (((uint64_t)(us[i] + 1) << 14) | (uint64_t)v) : kInfKey;
+      wave_nv += __popcll(__ballot(below));
+    }
+    if ((tid & 63) == 0 && wave_nv) atomicAdd(&C.nv, wave_nv);
     lds_sync();
     for (int p = tid; p < n; p += kThreads) {
       const int v = C.hit[p];
