@@ -66,6 +66,7 @@ struct CallLds {
   int32_t vold[kMaxEntries];    // previous owner of each victim
   int64_t mrec[kMaxEntries];    // recency of each miss
   uint64_t red[kThreads / 64];
+  int nvw[kThreads / 64];       // prebuilt victim keys below the floor, per wave
   int64_t s, floor_;
   int layer, n, spec, nu, nm, nv, qq, err;
 };
@@ -201,11 +202,38 @@ __device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* s_red) {
   return r;
 }
 
+// The victim key of every slot for a real call, from the usage before the call (the split reads it
+// only when it fetches, but the keys cost nothing on the critical path when waves that would
+// otherwise wait build them at the start): ((usage + 1) << 14 | slot) below floor = clock + 1, else
+// kInfKey.  Threads [kKeyT0, kThreads); C.nvw[w] = keys below the floor built by wave w.
+constexpr int kKeyT0 = 320;  // waves 1-4 copy x for the host meanwhile
+__device__ void prebuild_keys(const CacheState& c, CallLds& C, uint64_t* s_key) {
+  constexpr int kNt = kThreads - kKeyT0, kPer = (kMaxSlots + kNt - 1) / kNt;
+  const int t = threadIdx.x - kKeyT0, S = c.S;
+  const int64_t floor_ = c.clock[0] + 1;
+  int64_t us[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int v = t + i * kNt;
+    us[i] = v < S ? c.usage[v] : 0;
+  }
+  int wave_nv = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int v = t + i * kNt;
+    const bool below = v < S && us[i] < floor_;
+    if (v < c.sort_pow2) s_key[v] = below ? (((uint64_t)(us[i] + 1) << 14) | (uint64_t)v) : kInfKey;
+    wave_nv += __popcll(__ballot(below));
+  }
+  if ((threadIdx.x & 63) == 0) C.nvw[threadIdx.x >> 6] = wave_nv;
+}
+
 // split: q*, recency ranking, LRU victims and the -1 partition, computed in LDS (C.victim,
 // C.ranked, C.vold, C.qq, C.slot).  Reads recency, usage and owner; writes nothing to memory.
 // The call's hit slots are never victims (their stamp of this step is committed later).
 // s_key: sort_pow2 uint64 of LDS.
-__device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key) {
+// keys_ready: s_key and C.nvw were prebuilt (prebuild_keys) from the usage this call sees.
+__device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, bool keys_ready = false) {
   const int tid = threadIdx.x;
   const int E = c.E, S = c.S;
   const int n = C.n, m = C.nm;
@@ -214,29 +242,36 @@ __device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key) {
   const int q = (int)qstar_dev(m, c.f);
   int qq = 0;
   if (q > 0) {
-    if (tid == 0) C.nv = 0;
+    if (tid == 0) {
+      int nv = 0;
+      if (keys_ready)
+        for (int w = kKeyT0 / 64; w < kThreads / 64; ++w) nv += C.nvw[w];
+      C.nv = nv;
+    }
     lds_sync();
     // the misses' recency and the victim keys: every load is issued before any is used (a loop that
     // consumed each load in turn would pay one global round trip per slot a thread owns)
     static_assert(kMaxEntries <= kThreads && kMaxSlots % kThreads == 0, "one miss per thread, whole rounds");
     constexpr int kPer = kMaxSlots / kThreads;
     const int64_t mr = tid < m ? c.recency[base + C.miss[tid]] : 0;
-    int64_t us[kPer];
+    if (!keys_ready) {
+      int64_t us[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int v = tid + i * kThreads;
-      us[i] = v < S ? c.usage[v] : 0;
+      for (int i = 0; i < kPer; ++i) {
+        const int v = tid + i * kThreads;
+        us[i] = v < S ? c.usage[v] : 0;
+      }
+      int wave_nv = 0;  // counted per wave with ballots: one LDS atomic per wave, not per thread
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int v = tid + i * kThreads;
+        const bool below = v < S && us[i] < floor_;  // slots with usage below the floor, by (usage, slot)
+        if (v < c.sort_pow2) s_key[v] = below ? (((uint64_t)(us[i] + 1) << 14) | (uint64_t)v) : kInfKey;
+        wave_nv += __popcll(__ballot(below));
+      }
+      if ((tid & 63) == 0 && wave_nv) atomicAdd(&C.nv, wave_nv);
     }
     if (tid < m) C.mrec[tid] = mr;
-    int wave_nv = 0;  // counted per wave with ballots: one LDS atomic per wave, not per thread
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int v = tid + i * kThreads;
-      const bool below = v < S && us[i] < floor_;  // slots with usage below the floor, by (usage, slot)
-      if (v < c.sort_pow2) s_key[v] = below ? (((uint64_t)(us[i] + 1) << 14) | (uint64_t)v) : kInfKey;
-      wave_nv += __popcll(__ballot(below));
-    }
-    if ((tid & 63) == 0 && wave_nv) atomicAdd(&C.nv, wave_nv);
     lds_sync();
     for (int p = tid; p < n; p += kThreads) {
       const int v = C.hit[p];
@@ -753,21 +788,23 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
   __shared__ CallLds C;
   const int tid = threadIdx.x;
   const int n = B * K;
-  if (tid >= 64) {
-    // waves 1.. copy x for the host while wave 0 starts the top-K.  They wait for these stores
+  if (tid >= 64 && tid < kKeyT0) {
+    // waves 1-4 copy x for the host while wave 0 starts the top-K.  They wait for these stores
     // to complete only after the split (below), before the plan's barrier: x_host is coherent host
     // memory (not held in the L2), so a completed store is visible to the host, and the call word
     // that wave 0 publishes after the last barrier is ordered after it.  (A system-scope fence
     // would also write back the L2 from every wave, which costs microseconds.)
-    for (int i = tid - 64; i < B * H / 8; i += kThreads - 64)
+    for (int i = tid - 64; i < B * H / 8; i += kKeyT0 - 64)
       reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
+  } else if (tid >= kKeyT0) {
+    prebuild_keys(c, C, s_key);  // waves 5.. meanwhile
   }
   for (int t = tid >> 6; t < B; t += kThreads / 64)
     topk_row(logits + (int64_t)t * c.E, c.E, K, ids + (int64_t)t * K, w + (int64_t)t * K, C.id + t * K);
   lds_sync();
   ensure_body(c, layer, n, 0, C);
-  split_body(c, C, s_key);
-  if (tid >= 64 && call_ring) __builtin_amdgcn_s_waitcnt(0);  // x_host stores complete (see above)
+  split_body(c, C, s_key, true);
+  if (tid >= 64 && tid < kKeyT0 && call_ring) __builtin_amdgcn_s_waitcnt(0);  // x_host stores complete (above)
   plan_body(C.slot, C.id, C.hit, (int64_t)layer * c.E, c.owner, n, c.S, maxU, maxB, plan,
             reinterpret_cast<int32_t*>(s_key));
   commit_body(c, C, true, slots, cpu, cpu_host, counts);
