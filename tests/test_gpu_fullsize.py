@@ -1,0 +1,109 @@
+"""GPU parity at the full sizes of the timed workloads, in the launch configuration the bench times.
+
+Decode, 35b-a3b (40 layers x 256 int4 experts in pinned host memory, 5120 slots, f = 0.4, B = 1):
+32 tokens x 40 layers of eff_decode_layer with trace logits, issued back to back (no host
+synchronization between calls: asynchronous host share, in-kernel fetches), then
+  * the final table, owner, usage, recency and clock, bit for bit, against the oracle policy
+    replayed over the same routing (plain LRU code, every call in order);
+  * the per-call hit / fetch / host totals against the replay;
+  * sampled outputs (layers and tokens spread over the run, the first and the last call included)
+    against the oracle's routed MoE of the dequantized records (fp64), rel-L2 <= 5e-3 and
+    max-abs <= 2e-2.  The output does not depend on the cache, so the pool record is the reference.
+Prefill, dsv4-flash (256 NVFP4 experts of 4096 x 2048, top-6, 2201 slots, T = 2048 tokens): two
+layers streamed into the double buffer and the grouped GEMMs, sampled tokens against the oracle."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import synth  # noqa: E402
+from oracle import cffn  # noqa: E402
+from oracle.ffn import combine, x_f64  # noqa: E402
+from oracle.formats import f64_to_bf16_bits  # noqa: E402
+from oracle.policy import SlotCache  # noqa: E402
+from oracle.router import topk_softmax  # noqa: E402
+from synth.configs import A3B, DSV4_PREFILL  # noqa: E402
+from tests.helpers import PinnedPool, assert_close_bf16  # noqa: E402
+from tests.test_gpu_prefill import run_prefill  # noqa: E402
+
+TOKENS = 32
+
+
+@pytest.fixture(scope="module")
+def eff():
+    import expert_ffn_serving_amd as e
+    assert torch.cuda.is_available()
+    return e
+
+
+def test_decode_35b_a3b_full_size(eff):
+    W = A3B
+    L, E, K, H, I = W.L, W.E, W.K, W.H, W.I
+    print("full-size decode %s: L=%d E=%d K=%d H=%d I=%d S=%d f=%d tokens=%d" % (
+        W.name, L, E, K, H, I, W.S, W.f_q16, TOKENS), flush=True)
+    pool = PinnedPool(eff, W.seed, L, E, H, I, W.fmt)
+    eng = None
+    try:
+        cfg = eff.make_config(L, E, K, H, I, W.fmt, W.S, 1, 0, W.f_q16, 12)
+        eng = eff.Engine(cfg, pool.ptr, None)
+        X = [synth.activations(W.seed, l, 0, TOKENS, H) for l in range(L)]
+        LG = [synth.trace_logits(W.seed, l, E, W.zipf_s, 0, TOKENS) for l in range(L)]
+        Xd = [torch.from_numpy(x.view(np.int16)).cuda() for x in X]
+        LGd = [torch.from_numpy(lg).cuda() for lg in LG]
+        OUT = torch.empty((TOKENS, L, H), dtype=torch.int16, device="cuda")
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        for t in range(TOKENS):
+            for l in range(L):
+                eng.decode_layer(l, Xd[l][t:t + 1], OUT[t, l:l + 1], logits=LGd[l][t:t + 1], side=side)
+        torch.cuda.synchronize()
+        st = eng.stats()
+        snap = eng.snapshot_tables()
+        out = OUT.cpu().numpy().view(np.uint16)
+
+        # the oracle policy over the same calls, in the same order
+        cache = SlotCache(L, E, W.S, W.f_q16)
+        hits = fetched = host = 0
+        for t in range(TOKENS):
+            for l in range(L):
+                ids, _ = topk_softmax(LG[l][t:t + 1], K)
+                cache.ensure(l, [int(e) for e in ids.reshape(-1)])
+                res = cache.split()
+                hits += len(set(int(e) for e in ids.reshape(-1))) - res.m
+                fetched += res.q
+                host += res.host
+        assert list(snap["table"]) == cache.table
+        assert list(snap["owner"]) == cache.owner
+        assert list(snap["usage"]) == cache.usage
+        assert list(snap["recency"]) == cache.recency
+        assert (st["hits"], st["fetched"], st["host"]) == (hits, fetched, host)
+        assert fetched > 0 and host > 0 and hits > 0   # every branch of the split was taken
+
+        # sampled outputs: the routed MoE of the dequantized records, in fp64
+        samples = [(0, 0), (TOKENS - 1, L - 1)] + [((7 * i) % TOKENS, (13 * i + 5) % L) for i in range(10)]
+        for t, l in samples:
+            ids, w = topk_softmax(LG[l][t:t + 1], K)
+            x = x_f64(X[l][t:t + 1])
+            jobs = [(pool.record(l * E + int(e)), pool.tensor_scales(l * E + int(e)), x) for e in ids[0]]
+            ys = cffn.expert_ffn_batch(jobs, W.fmt, H, I, 16)
+            y = np.stack([yk[0] for yk in ys])[None]          # [1, K, H]
+            ref = f64_to_bf16_bits(combine(y, w))
+            assert_close_bf16(out[t, l:l + 1], ref, what="token %d layer %d" % (t, l))
+    finally:
+        if eng is not None:
+            eng.close()
+        pool.free()
+
+
+def test_prefill_dsv4_full_size(eff):
+    W = DSV4_PREFILL
+    T = W.prefill_T
+    print("full-size prefill %s: E=%d K=%d H=%d I=%d S=%d T=%d, 2 layers" % (W.name, W.E, W.K, W.H, W.I, W.S, T),
+          flush=True)
+    pool = PinnedPool(eff, W.seed, 2, W.E, W.H, W.I, W.fmt)
+    try:
+        toks = [0, 1, 63, 64, 511, 1024, 1500, 2046, T - 1]
+        run_prefill(eff, pool, W.K, W.S, T, [0, 1], W.seed, tokens_checked=toks)
+    finally:
+        pool.free()
