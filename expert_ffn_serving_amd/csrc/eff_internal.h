@@ -72,13 +72,14 @@ struct DecodePlan {
   DecodeUnit unit[kMaxEntries];
 };
 
-// Decode calls publish (seq << 16 | host entries) in a host-mapped ring of words ------------------
+// Decode calls publish one word each in a host-mapped ring, at seq % kCallRing.  seq counts the
+// engine's decode calls from 1 in device memory (the control kernel increments it), so a captured
+// and replayed decode step numbers its calls like eager ones.  Word: seq (low 32 bits) << 32 |
+// layer << 16 | (B - 1) << 10 | host entries.  The host-share worker follows the ring in seq order.
 constexpr int kCallRing = 256;
-struct HostJob {
-  uint64_t seq;
-  int32_t layer, B;
-};
-constexpr int kJobRing = 4096;
+constexpr int kCallLayerShift = 16, kCallBShift = 10;
+constexpr uint64_t kCallHostMask = 0x3FF, kCallBMask = 0x3F, kCallLayerMask = 0xFFFF;
+static_assert(kMaxEntries <= kCallHostMask && kMaxTokens <= kCallBMask + 1, "call word fields");
 // polls of the host-share word by the combine kernel before it gives up (about 2 s)
 constexpr uint32_t kCombineSpinLimit = 1u << 20;
 
@@ -170,13 +171,14 @@ struct eff_engine {
   int32_t* h_cpu = nullptr;       // [maxB*K] host-mapped
   uint16_t* h_x_dev = nullptr;    // device views of the two above
   int32_t* h_cpu_dev = nullptr;
-  uint64_t* h_call = nullptr;     // host-mapped ring [kCallRing]: seq << 16 | host entries, per call
+  uint64_t* h_call = nullptr;     // host-mapped ring [kCallRing] of call words (see kCallRing)
   uint64_t* h_call_dev = nullptr;
   uint64_t* h_done = nullptr;     // host-mapped: the last call whose host share is in h_yhost
   uint64_t* h_done_dev = nullptr;
   int32_t* h_err = nullptr;       // host-mapped sticky device error bits (bad id 1, combine wait 4)
   int32_t* h_err_dev = nullptr;
-  uint64_t ready_seq = 0;
+  uint64_t* d_seq = nullptr;      // device: the last decode call's seq
+  uint64_t sync_seq = 0;          // EFF_CFG_SYNC_HOST: the host's count of decode calls (= *d_seq)
   float* h_yhost = nullptr;       // [maxB*K*H] host-mapped: the host share's outputs
   float* h_yhost_dev = nullptr;
   const uint8_t* pool_dev = nullptr;  // device view of the pinned pool (in-kernel fetches)
@@ -185,8 +187,7 @@ struct eff_engine {
   hipEvent_t ev_ctl = nullptr;
   // host-share worker (async mode)
   std::thread worker;
-  std::vector<eff::HostJob> jobs;
-  std::atomic<uint64_t> job_head{0}, job_tail{0};
+  std::atomic<uint64_t> worker_seq{0};  // every call up to this seq has been handled
   std::atomic<bool> worker_stop{false};
   std::atomic<int> async_err{0};
   std::mutex async_mu;
@@ -240,13 +241,13 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
 hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s);
 hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s);
 hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
-                          const int32_t* spec_ids, uint64_t seq, hipStream_t s);
+                          const int32_t* spec_ids, hipStream_t s);
 // timing hooks: returns the call's event slot (or -1 when timing is off); mark(i) records event i
 int timing_begin(eff_engine* e, int kind, hipStream_t s);
 void timing_mark(eff_engine* e, int slot, int i, hipStream_t s);
 hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
                           int B, int K, int H, uint16_t* out, hipStream_t s, const uint64_t* done = nullptr,
-                          uint64_t seq = 0, int32_t* err = nullptr);
+                          const uint64_t* seq = nullptr, int32_t* err = nullptr);
 hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int32_t* ids,
                           const float* w, int T, uint16_t* out, const int32_t* slot_of_expert,
                           int slot_base, bool combine, hipStream_t s);

@@ -65,7 +65,7 @@ static void release(eff_engine* e) {
   if (!e) return;
   stop_worker(e);
   void* dev[] = {e->d_arena, e->d_table, e->d_owner, e->d_usage, e->d_recency, e->d_clock, e->d_ts,
-                 e->d_pending, e->d_fetch, e->d_err, e->d_stats, e->d_plan, e->d_a, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, e->d_spec_ids,
+                 e->d_pending, e->d_fetch, e->d_err, e->d_seq, e->d_stats, e->d_plan, e->d_a, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, e->d_spec_ids,
                  e->d_spec_cpu, e->d_logits, e->d_ygpu, e->d_yhost, e->d_pf_count, e->d_pf_rows,
                  e->d_pf_a, e->d_pf_y, e->d_pf_meta, e->d_pf_slot_of, e->d_pf_experts};
   for (void* p : dev)
@@ -98,6 +98,7 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(dalloc(&e->d_pending, 1));
   EFF_HIP_TRY(dalloc(&e->d_fetch, 2));
   EFF_HIP_TRY(dalloc(&e->d_err, 1));
+  EFF_HIP_TRY(dalloc(&e->d_seq, 1));
   EFF_HIP_TRY(dalloc(&e->d_stats, ST_COUNT));
   // host-mapped control words are coherent (fine-grained): the host reads them while kernels run
   const unsigned mapped = hipHostMallocMapped | hipHostMallocCoherent;
@@ -159,6 +160,7 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipMemset(e->d_clock, 0, 16));
   EFF_HIP_TRY(hipMemset(e->d_pending, 0, sizeof(Pending)));
   EFF_HIP_TRY(hipMemset(e->d_err, 0, 4));
+  EFF_HIP_TRY(hipMemset(e->d_seq, 0, 8));
   EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
   std::memset(e->h_fetch, 0, 2 * sizeof(FetchList));
   EFF_HIP_TRY(split_kernel_setup((int)S, (int)E));
@@ -261,32 +263,39 @@ static int check_async_error(eff_engine* e) {
 // 0 when a later call already overwrote the word (only calls without host entries let the
 // device run ahead), or -1 (error recorded) when the word does not come.  With a stream given,
 // the wait also ends when that stream fails or drains without publishing.
-static int wait_call(eff_engine* e, uint64_t seq, hipStream_t cs = nullptr) {
+// Fields of a call word (see kCallRing).
+static inline uint32_t word_seq(uint64_t w) { return (uint32_t)(w >> 32); }
+static inline int word_host(uint64_t w) { return (int)(w & kCallHostMask); }
+static inline int word_batch(uint64_t w) { return (int)((w >> kCallBShift) & kCallBMask) + 1; }
+static inline int word_layer(uint64_t w) { return (int)((w >> kCallLayerShift) & kCallLayerMask); }
+// order of two call numbers from their low 32 bits (calls in flight are far fewer than 2^31 apart)
+static inline int32_t seq_order(uint32_t a, uint64_t b) { return (int32_t)(a - (uint32_t)b); }
+
+// EFF_CFG_SYNC_HOST: waits for call `seq`'s word; returns its host entries (-1 on failure).
+static int wait_call(eff_engine* e, uint64_t seq, hipStream_t cs) {
   const auto t0 = std::chrono::steady_clock::now();
   volatile uint64_t* word = e->h_call + seq % kCallRing;
   int nhost = -1;
   for (uint64_t spin = 1;; ++spin) {
     const uint64_t w = *word;
-    const uint64_t ws = w >> 16;
-    if (ws == seq) {
-      nhost = (int)(w & 0xFFFF);
+    const int32_t d = seq_order(word_seq(w), seq);
+    if (d == 0) {
+      nhost = word_host(w);
       break;
     }
-    if (ws > seq) {
+    if (d > 0) {
       nhost = 0;
       break;
     }
     if ((spin & 4095) == 0) {
-      if (cs) {
-        const hipError_t q = hipStreamQuery(cs);
-        if (q == hipSuccess && (*word >> 16) < seq) {
-          set_async_error(e, "control kernel finished without publishing its call");
-          break;
-        }
-        if (q != hipSuccess && q != hipErrorNotReady) {
-          set_async_error(e, std::string("control kernel: ") + hipGetErrorString(q));
-          break;
-        }
+      const hipError_t q = hipStreamQuery(cs);
+      if (q == hipSuccess && seq_order(word_seq(*word), seq) < 0) {
+        set_async_error(e, "control kernel finished without publishing its call");
+        break;
+      }
+      if (q != hipSuccess && q != hipErrorNotReady) {
+        set_async_error(e, std::string("control kernel: ") + hipGetErrorString(q));
+        break;
       }
       if (ns_since(t0) > (int64_t)30 * 1000 * 1000 * 1000) {
         set_async_error(e, "no control kernel result within 30 s");
@@ -300,48 +309,56 @@ static int wait_call(eff_engine* e, uint64_t seq, hipStream_t cs = nullptr) {
   return nhost;
 }
 
-static void run_job(eff_engine* e, const HostJob& job) {
-  const int nhost = wait_call(e, job.seq);
-  if (nhost > 0) {
-    const auto t1 = std::chrono::steady_clock::now();
-    host_ffn(e, job.layer, e->h_x, e->h_cpu, job.B, e->h_yhost);
-    e->host_ns += ns_since(t1);
-    e->host_calls_a += 1;
-  }
-  if (nhost != 0) {  // release the stream's wait (also after an error, so the stream never hangs)
-    std::atomic_thread_fence(std::memory_order_release);
-    __atomic_store_n(e->h_done, job.seq, __ATOMIC_RELEASE);
-  }
-}
-
+// The host-share worker (asynchronous mode) follows the call ring in call order, so it needs no
+// message from the enqueuing thread and a captured decode step drives it like an eager one.  For a
+// call with host entries it runs the host share from the host-mapped x and host ids, then stores
+// h_done = seq, which releases that call's combine kernel.  x and the host ids stay valid meanwhile:
+// the next control kernel runs after that combine.  A ring slot already holding a later call was
+// overwritten while the worker lagged, which only a call without host entries can be (a call with
+// host entries holds its stream until h_done): it is skipped.
 static void worker_loop(eff_engine* e) {
-  uint64_t idle = 0;
+  uint64_t next = e->worker_seq.load(std::memory_order_relaxed) + 1, idle = 0;
+  auto t_wait = std::chrono::steady_clock::now();
   for (;;) {
-    const uint64_t tail = e->job_tail.load(std::memory_order_relaxed);
-    if (tail == e->job_head.load(std::memory_order_acquire)) {
+    const uint64_t w = *(volatile uint64_t*)(e->h_call + next % kCallRing);
+    const int32_t d = seq_order(word_seq(w), next);
+    if (d < 0) {  // not published yet
       if (e->worker_stop.load(std::memory_order_acquire)) break;
       if (++idle < 100000) _mm_pause();
       else std::this_thread::sleep_for(std::chrono::microseconds(20));
       continue;
     }
     idle = 0;
-    run_job(e, e->jobs[tail % kJobRing]);
-    e->job_tail.store(tail + 1, std::memory_order_release);
+    std::atomic_thread_fence(std::memory_order_acquire);
+    if (d == 0 && word_host(w) > 0) {
+      const auto t1 = std::chrono::steady_clock::now();
+      e->wait_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(t1 - t_wait).count();
+      host_ffn(e, word_layer(w), e->h_x, e->h_cpu, word_batch(w), e->h_yhost);
+      e->host_ns += ns_since(t1);
+      e->host_calls_a += 1;
+      std::atomic_thread_fence(std::memory_order_release);
+      __atomic_store_n(e->h_done, next, __ATOMIC_RELEASE);
+      t_wait = std::chrono::steady_clock::now();
+    }
+    e->worker_seq.store(next, std::memory_order_release);
+    ++next;
   }
 }
 
-static void push_job(eff_engine* e, const HostJob& job) {
-  const uint64_t head = e->job_head.load(std::memory_order_relaxed);
-  while (head - e->job_tail.load(std::memory_order_acquire) >= (uint64_t)kJobRing) _mm_pause();
-  e->jobs[head % kJobRing] = job;
-  e->job_head.store(head + 1, std::memory_order_release);
-}
-
-// Waits until the worker has finished every queued call (each waits for its control kernel).
+// Waits until the worker has handled every decode call issued so far (synchronizes the device).
 static void drain_worker(eff_engine* e) {
   if (!e->async_host) return;
-  while (e->job_tail.load(std::memory_order_acquire) != e->job_head.load(std::memory_order_acquire))
+  uint64_t last = 0;
+  if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(&last, e->d_seq, 8, hipMemcpyDeviceToHost) != hipSuccess)
+    return;
+  const auto t0 = std::chrono::steady_clock::now();
+  while (e->worker_seq.load(std::memory_order_acquire) < last) {
+    if (ns_since(t0) > (int64_t)30 * 1000 * 1000 * 1000) {
+      set_async_error(e, "host-share worker did not catch up within 30 s");
+      return;
+    }
     std::this_thread::sleep_for(std::chrono::microseconds(20));
+  }
 }
 
 static void stop_worker(eff_engine* e) {
@@ -434,7 +451,6 @@ int eff_create(const eff_config* cfg, const void* host_pool, const float* tensor
   e->host_isa = host_isa_best();
   e->async_host = !(cfg->flags & EFF_CFG_SYNC_HOST);
   if (e->async_host) {
-    e->jobs.resize(kJobRing);
     try {
       e->worker = std::thread(worker_loop, e);
     } catch (...) {
@@ -591,6 +607,8 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   hipStream_t cs = (hipStream_t)compute, ss = (hipStream_t)side;
   if (!e->async_host && (capturing(cs) || capturing(ss)))
     return fail(EFF_ECAPTURE, "eff_decode_layer waits on the host (EFF_CFG_SYNC_HOST)");
+  if ((c.flags & EFF_CFG_TIMING) && (capturing(cs) || capturing(ss)))
+    return fail(EFF_ECAPTURE, "eff_decode_layer: timing events cannot be captured (EFF_CFG_TIMING)");
   const int K = c.top_k;
   const float* lg = logits;
   if (w_router) {
@@ -601,8 +619,7 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   // top-K, ensure, split, the speculative request and the decode plan in one workgroup; host ids
   // and x land in host-mapped memory, then the call word
   const bool spec = spec_ids && layer + 1 < c.num_layers;
-  const uint64_t seq = ++e->ready_seq;
-  EFF_HIP_TRY(launch_control(e, layer, lg, B, (const uint16_t*)x, spec ? spec_ids : nullptr, seq, cs));
+  EFF_HIP_TRY(launch_control(e, layer, lg, B, (const uint16_t*)x, spec ? spec_ids : nullptr, cs));
   // the previous layer's speculative copies land before this layer's expert kernels read or
   // overwrite any slot
   if (e->spec_copy_pending) {
@@ -621,11 +638,10 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   if (e->async_host) {
     // the combine waits for the host share (or the control kernel's own release of the call)
     EFF_HIP_TRY(launch_combine(e->d_ygpu, e->h_yhost_dev, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs,
-                               e->h_done_dev, seq, e->h_err_dev));
-    push_job(e, HostJob{seq, layer, B});
+                               e->h_done_dev, e->d_seq, e->h_err_dev));
     return EFF_OK;
   }
-  const int nhost = wait_call(e, seq, cs);
+  const int nhost = wait_call(e, ++e->sync_seq, cs);
   if (nhost < 0) return fail(EFF_EHIP, e->async_msg);
   if (nhost > 0) {
     const auto t1 = std::chrono::steady_clock::now();

@@ -775,15 +775,15 @@ k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, cons
 // One decode layer's control path in one workgroup: top-K of the B logits rows, ensure, split,
 // the decode plan (units installed by this call are fetched by the FFN kernels), the commit,
 // (speculative ensure + split + commit for the next layer), and the host's inputs (host ids, x)
-// in host-mapped memory.  Last, wave 0 (the only wave that writes host-mapped memory) fences at
-// system scope and publishes call_ring[seq % kCallRing] = seq << 16 | host entries; a call with
-// no host entries also sets *host_done = seq itself (nothing for the host to add).
+// in host-mapped memory.  Last, wave 0 fences at system scope, numbers the call (seq = ++*seq_ctr,
+// device memory) and publishes its word (seq, layer, B, host entries) at call_ring[seq % kCallRing];
+// a call with no host entries also sets *host_done = seq itself (nothing for the host to add).
 __global__ void __launch_bounds__(kThreads)
 k_control(CacheState c, const float* __restrict__ logits, int B, int K, int layer, int32_t* __restrict__ ids,
           float* __restrict__ w, int32_t* __restrict__ slots, int32_t* __restrict__ cpu, int32_t* __restrict__ counts,
           const int32_t* __restrict__ spec_ids, int32_t* __restrict__ spec_slots, int32_t* __restrict__ cpu_host,
           const uint16_t* __restrict__ x, uint16_t* __restrict__ x_host, int H, int maxU, int maxB,
-          DecodePlan* plan, uint64_t* call_ring, uint64_t* host_done, uint64_t seq) {
+          DecodePlan* plan, uint64_t* call_ring, uint64_t* host_done, uint64_t* seq_ctr) {
   extern __shared__ uint64_t s_key[];  // victim keys, plan scratch
   __shared__ CallLds C;
   const int tid = threadIdx.x;
@@ -828,9 +828,13 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
     if (call_ring) {
       __threadfence_system();
       if (tid == 0) {
-        // relaxed stores after the release fence (a release store would write back the L2 again)
-        __hip_atomic_store(call_ring + seq % kCallRing, (seq << 16) | (uint64_t)nhost, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
+        // this call's number, then the word; relaxed stores after the release fence (a release store
+        // would write back the L2 again)
+        const uint64_t seq = *seq_ctr + 1;
+        *seq_ctr = seq;
+        const uint64_t word = ((seq & 0xFFFFFFFFull) << 32) | ((uint64_t)layer << kCallLayerShift) |
+                              ((uint64_t)(B - 1) << kCallBShift) | (uint64_t)nhost;
+        __hip_atomic_store(call_ring + seq % kCallRing, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         if (nhost == 0) __hip_atomic_store(host_done, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
@@ -969,13 +973,13 @@ hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s
 }
 
 hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
-                          const int32_t* spec_ids, uint64_t seq, hipStream_t s) {
+                          const int32_t* spec_ids, hipStream_t s) {
   const eff_config& cf = e->cfg;
   const size_t lds = control_lds(cf.num_slots, cf.num_experts);
   hipLaunchKernelGGL(k_control, dim3(1), dim3(kThreads), lds, s, state_of(e), logits, B,
                      cf.top_k, layer, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, spec_ids,
                      e->d_spec_ids, e->h_cpu_dev, x, e->h_x_dev, cf.hidden, e->maxU, cf.max_tokens, e->d_plan,
-                     e->h_call_dev, e->h_done_dev, seq);
+                     e->h_call_dev, e->h_done_dev, e->d_seq);
   return hipGetLastError();
 }
 

@@ -409,16 +409,17 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
 // ---------------------------------------------------------------------------- combine
 // out[t, h] = sum over k (ascending) of w[t,k] * y[t,k,h], y from the GPU or the host buffer by the
 // entry's slot (slots == nullptr: all from yg; yh may be host-mapped memory).
-// With `done` (host-mapped), the kernel first waits until *done >= seq: the host share of the call
-// is in yh (or the call had none).  One thread per workgroup polls with a bounded spin; past the
+// With `done` (host-mapped), the kernel first waits until *done >= *seq (the number the control
+// kernel gave this call, in device memory): the host share of the call is in yh (or it had none).  One thread per workgroup polls with a bounded spin; past the
 // bound it sets bit 4 of *err and combines anyway, so the kernel always ends.
 template <int KMAX>
 __global__ void __launch_bounds__(256)
 k_combine(const float* __restrict__ yg, const float* __restrict__ yh, const int32_t* __restrict__ slots,
-          const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out, const uint64_t* done, uint64_t seq,
-          int32_t* err) {
+          const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out, const uint64_t* done,
+          const uint64_t* seq_dev, int32_t* err) {
   if (done) {
     if (threadIdx.x == 0) {
+      const uint64_t seq = *seq_dev;
       for (uint32_t spin = 0; __hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < seq; ++spin) {
         if (spin >= kCombineSpinLimit) {
           atomicOr(err, 4);
@@ -538,7 +539,7 @@ hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s) {
 }
 
 hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
-                          int B, int K, int H, uint16_t* out, hipStream_t s, const uint64_t* done, uint64_t seq,
+                          int B, int K, int H, uint16_t* out, hipStream_t s, const uint64_t* done, const uint64_t* seq,
                           int32_t* err) {
   dim3 g((H + 255) / 256, B);
   if (!slots) yhost = nullptr;

@@ -174,13 +174,20 @@ int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const in
  * semantics as the separate calls ([FT-blog] §六).  Experts installed by the
  * call are read from the pinned pool by the expert kernels themselves, which
  * also write them into their slots.  The control kernel publishes the host ids
- * and x in host-mapped memory; the host share ([FT-deep] §4 ③④) runs on a worker
- * thread, and the combine kernel waits for it on a host-mapped word (a bounded
- * poll), so the call only enqueues work and returns.  With EFF_CFG_SYNC_HOST
+ * and x in host-mapped memory, numbers the call in device memory and publishes
+ * a call word (number, layer, B, host entries) in a host-mapped ring.  The host
+ * share ([FT-deep] §4 ③④) runs on an engine-owned worker thread that follows
+ * that ring, and the combine kernel waits for it on a host-mapped word (a
+ * bounded poll), so the call only enqueues work and returns.  Nothing of a call
+ * passes through the host at enqueue time, so a sequence of calls (for example
+ * all layers of one decode step) may be captured into a HIP graph on `compute`
+ * (with `side` joined through the call's own events) and replayed; the inputs
+ * are then read from the captured addresses at each replay ([FT-deep] §4 ④: the
+ * host branch inside the graph waits on host memory).  With EFF_CFG_SYNC_HOST
  * the calling thread waits for the control kernel and runs the host share
- * itself.  An error
- * of the host share is reported by the next call.  ids/w/slots/cpu_ids/counts of
- * the call can be read back with eff_last_layer_info after the stream is done. */
+ * itself (EFF_ECAPTURE under capture, as with EFF_CFG_TIMING).  An error of the
+ * host share is reported by the next call.  ids/w/slots/cpu_ids/counts of the
+ * call can be read back with eff_last_layer_info after the stream is done. */
 int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_router,
                      const float* logits, int B, const int32_t* spec_ids, void* out,
                      eff_stream_t compute, eff_stream_t side);
