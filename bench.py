@@ -203,11 +203,13 @@ def run_decode(eff, torch, synth, W, steps, warmup, profile_steps, threads, use_
 
 
 # ------------------------------------------------------------------------------------- prefill
-def run_prefill(eff, torch, synth, W, layers, threads):
+def run_prefill(eff, torch, synth, W, layers, threads, cpu_tokens=0, cpu_threads=1, decode_kernels=True):
     import numpy as np
     T = W.prefill_T
     log("prefill %s: T=%d E=%d K=%d H=%d I=%d (%d layers streamed)" % (W.name, T, W.E, W.K, W.H, W.I, layers))
     ptr, ts, R = fill_pool(eff, synth, W.seed, layers, W.E, W.H, W.I, W.fmt, threads)
+    # the decode kernels at this expert shape first, on a fresh engine
+    dk = decode_kernel_rates(eff, torch, synth, W, (ptr, ts, R), layers, threads) if decode_kernels else None
     cfg = eff.make_config(layers, W.E, W.K, W.H, W.I, W.fmt, W.S, 1, T, W.f_q16, threads, eff.CFG_TIMING)
     eng = eff.Engine(cfg, ptr, ts)
     X = [torch.from_numpy(synth.activations(W.seed, l, 0, T, W.H, tag=synth.TAG_PREFILL_X).view(np.int16)).cuda()
@@ -252,13 +254,101 @@ def run_prefill(eff, torch, synth, W, layers, threads):
                                 100 * wbytes * n / ((g_ms + d_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                 (g_ms + d_ms) / max(1, n), wall * 1e3 / layers))
     eng.close()
+    if decode_kernels:
+        res["decode_kernels"] = dk
+    if cpu_tokens > 0:
+        res["cpu_oracle"] = prefill_oracle(synth, W, (ptr, ts, R), cpu_tokens, cpu_threads)
+        log("  prefill cpu oracle: %.1f GFLOP/s (%s)" % (res["cpu_oracle"]["value"], res["cpu_oracle"]["sample"]))
     eff.host_free(ptr)
     return res
 
 
+# ---------------------------------------------------------------------- decode kernels at a large shape
+def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1, 4), tokens=64, zipf=1.0):
+    """HBM rates of the decode expert kernels at the DeepSeek-V4-Flash expert shape (4096 x 2048 NVFP4,
+    top-6), where a layer's experts are tens of MB: layers 0 and 1 of the prefill pool streamed whole into
+    the two slot buffers (S = 2E, every expert resident, no call misses), then `tokens` profiled decode
+    steps per batch size on Zipf(1.0) trace logits, alternating the two layers."""
+    import numpy as np
+    ptr, ts, R = pool
+    E, K, H, I = W.E, W.K, W.H, W.I
+    cfg = eff.make_config(layers, E, K, H, I, W.fmt, 2 * E, max(batches), 0, 65536, threads)
+    eng = eff.Engine(cfg, ptr, ts)
+    comp, side = torch.cuda.Stream(), torch.cuda.Stream()
+    x = torch.from_numpy(synth.activations(W.seed, 0, 0, max(batches), H).view(np.int16)).cuda()
+    out = torch.empty((max(batches), H), dtype=torch.int16, device="cuda")
+    eng.prefill_stream_layer(0, side)
+    eng.prefill_stream_layer(1, side)
+    torch.cuda.synchronize()
+    layers = 2
+    mat_bytes = H * I // 2 + H * I // 16
+    res = {"workload": "dsv4-flash expert shape (H=%d I=%d E=%d K=%d NVFP4), 2 layers, every expert resident" % (
+        H, I, E, K), "tokens": tokens}
+    for B in batches:
+        LG = [torch.from_numpy(synth.trace_logits(W.seed, l, E, zipf, 0, tokens * B)).cuda() for l in range(layers)]
+        eng.reset_stats()
+        eng.set_flags(eff.CFG_TIMING)
+        with torch.cuda.stream(comp):
+            for t in range(tokens):
+                for l in range(layers):
+                    eng.decode_layer(l, x[:B], out[:B], logits=LG[l][t * B:(t + 1) * B], compute=comp, side=side)
+        torch.cuda.synchronize()
+        st = eng.stats()
+        eng.set_flags(0)
+        n = st["launches"][eff.T_DECODE_GATEUP]
+        g_ms, d_ms = st["kernel_ms"][eff.T_DECODE_GATEUP], st["kernel_ms"][eff.T_DECODE_DOWN]
+        U = st["hits"] + st["fetched"]
+        gu = U * 2 * mat_bytes + n * B * H * 2 + U * B * I * 4   # upper bound on the small terms
+        dn = U * mat_bytes + U * B * (I + H) * 4
+        res["B%d" % B] = {
+            "gpu_experts_per_launch": round(U / max(1, n), 2), "fetched": st["fetched"],
+            "gateup_us": round(g_ms * 1e3 / max(1, n), 2), "gateup_GBps": round(gu / (g_ms * 1e-3) / 1e9, 1),
+            "gateup_frac": round(gu / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "down_us": round(d_ms * 1e3 / max(1, n), 2), "down_GBps": round(dn / (d_ms * 1e-3) / 1e9, 1),
+            "down_frac": round(dn / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        log("  decode kernels at the dsv4 shape, B=%d: %.1f experts/launch, gate/up %.1f us (%.0f GB/s), "
+            "down %.1f us (%.0f GB/s), fetched %d" % (B, U / max(1, n), g_ms * 1e3 / max(1, n),
+                                                       gu / (g_ms * 1e-3) / 1e9, d_ms * 1e3 / max(1, n),
+                                                       dn / (d_ms * 1e-3) / 1e9, st["fetched"]))
+    eng.close()
+    return res
+
+
 # ------------------------------------------------------------------------------------- CPU oracle
-def cpu_baseline(synth, W, pool, tokens, threads):
-    """The oracle as it stands, on `tokens` decode steps of the same trace (cold cache)."""
+def host_cpu():
+    """CPU model and the cores this process may run on."""
+    model = "?"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def host_read_gbps(ptr, nbytes, threads, reps=3):
+    """Host memory read bandwidth over `nbytes` of the pinned pool (what the host share streams), with
+    `threads` threads each summing its own contiguous part (NumPy releases the GIL in the reduction)."""
+    import ctypes
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    words = nbytes // 8 // threads * threads
+    a = np.frombuffer((ctypes.c_uint64 * words).from_address(ptr), np.uint64)
+    parts = np.array_split(a, threads)
+    best = 0.0
+    with ThreadPoolExecutor(threads) as ex:
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            list(ex.map(lambda v: int(np.add.reduce(v)), parts))
+            best = max(best, words * 8 / (time.perf_counter() - t0) / 1e9)
+    return round(best, 1)
+
+
+def prefill_oracle(synth, W, pool, tokens, threads):
+    """The oracle's prefill layer (as it stands) on `tokens` tokens of layer 0, in GFLOP/s of expert math."""
     import ctypes
 
     import numpy as np
@@ -269,18 +359,56 @@ def cpu_baseline(synth, W, pool, tokens, threads):
     def rec(flat):
         return np.frombuffer((ctypes.c_uint8 * R).from_address(ptr + flat * R), np.uint8)
 
-    eng = OracleEngine(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, W.f_q16, rec, lambda f: ts[3 * f:3 * f + 3],
+    eng = OracleEngine(2, W.E, W.K, W.H, W.I, W.fmt, W.S, W.f_q16, rec, lambda f: ts[3 * f:3 * f + 3],
                        use_c=True, nthreads=threads)
+    x = synth.activations(W.seed, 0, 0, W.prefill_T, W.H, tag=synth.TAG_PREFILL_X)
+    wr = synth.router_weights(W.seed, 0, W.E, W.H)
+    sample = list(range(0, W.prefill_T, W.prefill_T // tokens))[:tokens]
+    t0 = time.perf_counter()
+    eng.prefill_layer(0, x, wr, tokens=sample)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(sample) * W.K * 3 * W.H * W.I
+    return {"value": round(flops / dt / 1e9, 2), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of the %d tokens of layer 0 (every %dth), including the oracle's copy of the layer's %d "
+                      "records into its buffer; fp64 C evaluator" % (len(sample), W.prefill_T,
+                                                                    W.prefill_T // tokens, W.E)}
+
+def cpu_baseline(synth, W, pool, tokens, threads, tokens_1core=1):
+    """The oracle as it stands, on `tokens` decode steps of the same trace (cold cache), on `threads`
+    threads, and on one thread over the first `tokens_1core` steps."""
+    import ctypes
+
+    import numpy as np
+
+    from oracle.engine import OracleEngine
+    ptr, ts, R = pool
+
+    def rec(flat):
+        return np.frombuffer((ctypes.c_uint8 * R).from_address(ptr + flat * R), np.uint8)
+
     lg = [synth.trace_logits(W.seed, l, W.E, W.zipf_s, 0, tokens) for l in range(W.L)]
     xs = [synth.activations(W.seed, l, 0, tokens, W.H) for l in range(W.L)]
-    t0 = time.perf_counter()
-    for t in range(tokens):
-        for l in range(W.L):
-            eng.decode_layer(l, xs[l][t:t + 1], logits=lg[l][t:t + 1])
-    dt = time.perf_counter() - t0
-    return {"value": round(tokens / dt, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+
+    def timed(n, nthreads):
+        eng = OracleEngine(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, W.f_q16, rec, lambda f: ts[3 * f:3 * f + 3],
+                           use_c=True, nthreads=nthreads)
+        t0 = time.perf_counter()
+        for t in range(n):
+            for l in range(W.L):
+                eng.decode_layer(l, xs[l][t:t + 1], logits=lg[l][t:t + 1])
+        return n / (time.perf_counter() - t0)
+
+    value = timed(tokens, threads)
+    one = timed(tokens_1core, 1)
+    model, avail = host_cpu()
+    return {"value": round(value, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": "%d tokens x %d layers of the %s trace from a cold cache; fp64 C evaluator on %d threads "
-                      "plus single-threaded NumPy routing/policy" % (tokens, W.L, W.name, threads)}
+                      "plus single-threaded NumPy routing/policy" % (tokens, W.L, W.name, threads),
+            "value_1core": round(one, 3),
+            "sample_1core": "the first %d token(s) of the same sample on 1 thread" % tokens_1core,
+            "host_cpu": model, "host_cores_available": avail,
+            "host_read_GBps": host_read_gbps(ptr, 2 << 30, threads),
+            "host_read_probe": "NumPy sums over 2 GiB of the pinned expert pool, %d threads, best of 3" % threads}
 
 
 def main():
@@ -327,14 +455,17 @@ def main():
     dec = run_decode(eff, torch, synth, A3B, args.steps, args.warmup, args.profile_steps, args.threads,
                      not args.no_graph)
     cpu = None
+    ncpu = len(os.sched_getaffinity(0))
     if not args.skip_cpu:
         t0 = time.time()
-        cpu = cpu_baseline(synth, A3B, dec["pool"], args.cpu_tokens, args.threads)
-        log("  cpu oracle: %.3f tok/s (%.1f s)" % (cpu["value"], time.time() - t0))
+        cpu = cpu_baseline(synth, A3B, dec["pool"], args.cpu_tokens, ncpu)
+        log("  cpu oracle: %.3f tok/s on %d threads, %.3f tok/s on 1; host reads %.1f GB/s (%.1f s)" % (
+            cpu["value"], ncpu, cpu["value_1core"], cpu["host_read_GBps"], time.time() - t0))
     eff.host_free(dec["pool"][0])
     pre = None
     if not args.skip_prefill:
-        pre = run_prefill(eff, torch, synth, DSV4_PREFILL, args.prefill_layers, args.threads)
+        pre = run_prefill(eff, torch, synth, DSV4_PREFILL, args.prefill_layers, args.threads,
+                          0 if args.skip_cpu else 16, ncpu)
     line = {
         "metric": METRIC, "value": round(dec["value"], 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(dec["ms"], 4), "higher_is_better": True, "scaling": "weak",

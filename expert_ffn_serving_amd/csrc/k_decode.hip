@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(kWG)
 k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
          const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H,
          int I, int K, int maxB, float* __restrict__ a_out) {
-  constexpr int UNR = NT >= 4 ? 2 : (NT == 2 ? 4 : 8);  // tiles in flight per wave
+  constexpr int UNR = NT >= 8 ? 2 : (NT == 4 ? 4 : 8);  // tiles in flight per wave (x takes 4*NT VGPRs each)
   __shared__ float s_red[4][2][16][NT];
   const int NS = I / 16, KB = H / 32;
   const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
@@ -288,7 +288,7 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   __shared__ float s_red[4][16][NT];
   __shared__ float s_scale[NT];
   __shared__ float s_amax[NT][4];
-  constexpr int UNR = NT >= 4 ? 2 : 4;
+  constexpr int UNR = NT >= 4 ? 4 : 8;  // tiles in flight per wave
   const int NS = H / 16, KB = I / 32, I8 = I / 8;
   const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
   const DecodeUnit* un = &plan->unit[u];
@@ -473,18 +473,18 @@ k_fetch_copy(const uint8_t* __restrict__ pool, uint8_t* __restrict__ arena, int6
 }
 
 template <int FMT, int NT>
-hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, hipStream_t s) {
+hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, hipStream_t s) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   const int ts = timing_begin(e, EFF_T_DECODE_GATEUP, s);
-  hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(e->maxU * (I / 16)), dim3(kWG), 0, s, e->d_arena, e->pool_dev, e->R,
+  hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(units * (I / 16)), dim3(kWG), 0, s, e->d_arena, e->pool_dev, e->R,
                      e->d_ts, e->d_plan, x, H, I, c.top_k, c.max_tokens, e->d_a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
   size_t lds = (size_t)NT * (I / 8) * sizeof(uint4);
-  hipLaunchKernelGGL((k_down<FMT, NT>), dim3(e->maxU * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
+  hipLaunchKernelGGL((k_down<FMT, NT>), dim3(units * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
                      e->d_ts, e->d_plan, e->d_a, H, I, c.max_tokens, y);
   err = hipGetLastError();
   timing_mark(e, ts, 3, s);
@@ -496,13 +496,13 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, hipStream_t 
 int decode_nt(int maxB) { return maxB >= 8 ? 8 : maxB >= 4 ? 4 : maxB >= 2 ? 2 : 1; }
 
 hipError_t decode_kernels_setup(int fmt, int maxB, int I) {
-  // allow up to NT * I * 2 bytes of dynamic LDS for the down kernel
+  // allow N * I * 2 bytes of dynamic LDS for the down kernel of every token width N a call can take
   const int NT = decode_nt(maxB);
-  const int lds = NT * (I / 8) * 16;
   hipError_t err = hipSuccess;
 #define SETUP(F, N)                                                                                    \
-  if (fmt == F && NT == N)                                                                              \
-    err = hipFuncSetAttribute((const void*)k_down<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (fmt == F && N <= NT && err == hipSuccess)                                                         \
+    err = hipFuncSetAttribute((const void*)k_down<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize,    \
+                              N * (I / 8) * 16);
   SETUP(EFF_WFMT_INT4_G32_BF16, 1) SETUP(EFF_WFMT_INT4_G32_BF16, 2) SETUP(EFF_WFMT_INT4_G32_BF16, 4)
   SETUP(EFF_WFMT_INT4_G32_BF16, 8) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 1) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 2)
   SETUP(EFF_WFMT_NVFP4_G16_E4M3, 4) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 8)
@@ -517,17 +517,20 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
     hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s);
     if (err != hipSuccess) return err;
   }
-  const int NT = decode_nt(e->cfg.max_tokens);
+  // the token width follows the call's batch (a unit holds at most one entry per token): a B = 1 call
+  // takes the widest weight prefetch whatever max_tokens is
+  const int NT = decode_nt(B);
+  const int units = std::min(e->maxU, B * e->cfg.top_k);  // plan units a call of B tokens can have
   const bool fp4 = e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3;
   switch (NT) {
-    case 1: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 1>(e, x, y, s)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 1>(e, x, y, s);
-    case 2: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 2>(e, x, y, s)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 2>(e, x, y, s);
-    case 4: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 4>(e, x, y, s)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 4>(e, x, y, s);
-    default: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 8>(e, x, y, s)
-                        : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 8>(e, x, y, s);
+    case 1: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 1>(e, x, y, units, s)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 1>(e, x, y, units, s);
+    case 2: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 2>(e, x, y, units, s)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 2>(e, x, y, units, s);
+    case 4: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 4>(e, x, y, units, s)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 4>(e, x, y, units, s);
+    default: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 8>(e, x, y, units, s)
+                        : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 8>(e, x, y, units, s);
   }
 }
 
