@@ -103,13 +103,15 @@ class ThreadPool {
   void loop();
   void run_tasks(uint64_t g, const std::function<void(int)>* fn, int n);
   std::vector<std::thread> workers_;
-  std::atomic<uint64_t> gen_{0};
-  std::atomic<uint64_t> next_{0};
-  std::atomic<int> done_{0};
+  // idle workers spin on gen_ while tasks are claimed through next_ and counted in done_: each
+  // on a cache line of its own, so that neither write traffic stalls the spinning readers
+  alignas(128) std::atomic<uint64_t> gen_{0};
   std::atomic<const std::function<void(int)>*> fn_{nullptr};
   std::atomic<int> n_{0};
   std::atomic<bool> stop_{false};
-  std::atomic<int> sleepers_{0};
+  alignas(128) std::atomic<uint64_t> next_{0};
+  alignas(128) std::atomic<int> done_{0};
+  alignas(128) std::atomic<int> sleepers_{0};
   std::mutex mu_;
   std::condition_variable cv_;
 };
@@ -119,8 +121,12 @@ struct HostScratch {
   int32_t uexp[kMaxEntries];
   int32_t ucnt[kMaxEntries];
   int32_t uent[kMaxEntries][kMaxTokens];
-  std::atomic<int> done[kMaxEntries];
-  std::vector<uint16_t> a;  // per (expert, token): hi row, then lo row of silu(g)*u, bf16
+  struct alignas(128) Counter {
+    std::atomic<int> v{0};
+  };
+  Counter done[kMaxEntries];  // gate/up slices finished per host expert
+  std::vector<uint16_t> a;   // per (expert, token): hi row, then lo row of silu(g)*u, bf16
+  std::vector<uint16_t> xp;  // the call's token rows in the AVX-512 kernel's paired order
 };
 
 }  // namespace eff

@@ -7,6 +7,7 @@
 // ([FT-blog] §三.2).  fp32 accumulation, fixed order per output row.
 #include <immintrin.h>
 
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstring>
@@ -55,13 +56,10 @@ inline uint16_t f2bf_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// A slice kernel: rows 16*sl .. 16*sl+15 of one matrix (KB tiles of 16 rows x 32 inputs, the
+// The slice kernels: rows 16*sl .. 16*sl+15 of one matrix (KB tiles of 16 rows x 32 inputs, the
 // slice's tiles contiguous at pay + (sl*KB + kb)*256, scales at sca + (sl*KB + kb)*32) against
 // `nrows` bf16 input rows; row i accumulates into token i % nt (so a value can come as a hi + lo
 // pair of rows).  out[r * nt + j] = tscale * sum_k W[16*sl + r][k] * x_j[k], fp32.
-typedef void (*SliceFn)(const uint8_t* pay, const uint8_t* sca, int KB, int sl, int fmt,
-                        const uint16_t* const* xr, int nrows, int nt, float tscale, float* out);
-
 // AVX2 + FMA: per row, 8-wide fp32 FMAs over the row's 32 inputs of each tile, reduced at the end.
 // The 4 bytes of row r, inputs 8q..8q+7 of a tile are its dword (q*16 + r).
 void slice_avx2(const uint8_t* pay, const uint8_t* sca, int KB, int sl, int fmt, const uint16_t* const* xr,
@@ -124,86 +122,120 @@ void slice_avx2(const uint8_t* pay, const uint8_t* sca, int KB, int sl, int fmt,
     }
 }
 
-// AVX-512 BF16: the 16 rows of a tile are the 16 dword lanes of a zmm.  For byte m of a row's
-// dword (nibbles 2m, 2m+1), vpermt2b gathers the two nibbles of every lane into the low byte
-// of each 16-bit half and vpermw maps them to bf16 weights (exact for int4 and e2m1), which
-// vdpbf16ps multiplies with the broadcast bf16 input pair (x[8q+2m], x[8q+2m+1]): products exact,
-// fp32 accumulation.  Scales per (row, group) are applied per tile in fp32.
-__attribute__((target("avx512f,avx512bw,avx512vbmi,avx512bf16"))) void slice_avx512(
-    const uint8_t* pay, const uint8_t* sca, int KB, int sl, int fmt, const uint16_t* const* xr, int nrows, int nt,
-    float tscale, float* out) {
-  alignas(64) uint16_t tab[32];
-  for (int u = 0; u < 32; ++u) {
-    float v = 0.f;
-    if (u < 16) v = (fmt == EFF_WFMT_INT4_G32_BF16) ? (float)(u - 8) : tables().e2m1[u];
-    tab[u] = f2bf_trunc(v);  // exact
-  }
-  const __m512i table = _mm512_load_si512(tab);
-  alignas(64) uint8_t ib[4][64];
-  for (int m = 0; m < 4; ++m)
-    for (int r = 0; r < 16; ++r) {
-      ib[m][4 * r + 0] = (uint8_t)(4 * r + m);
-      ib[m][4 * r + 1] = 0;
-      ib[m][4 * r + 2] = (uint8_t)(64 + 4 * r + m);
-      ib[m][4 * r + 3] = 0;
+// AVX-512 BF16: the 16 rows of a tile are the 16 dword lanes of a zmm.  Shifting a row's dword
+// (inputs 8q..8q+7, input 8q+e in nibble e) right by 4m and masking with 0x000F000F leaves the
+// codes of inputs 8q+m and 8q+m+4 in the two 16-bit halves of each lane; vpermw maps them to
+// bf16 weights (exact for int4 and e2m1), and vdpbf16ps multiplies them with the broadcast bf16
+// pair (x[8q+m], x[8q+m+4]): products exact, fp32 accumulation.  The inputs therefore come in
+// "paired" order (pair_pos), prepared once per call.  Scales per (row, group) are applied per
+// half tile in fp32; the fp32 tensor scale at the end.
+struct MatRef {
+  const uint8_t* pay;  // payload of the matrix (tiles of 16 rows x 32 inputs)
+  const uint8_t* sca;  // its scale bytes
+  float tscale;        // NVFP4 tensor scale, 1 for int4
+  float* out;          // out[r * nt + j] for the slice's 16 rows
+};
+
+// bf16 bit patterns of the 16 codes, indexed by code (entries 16..31 unused)
+struct CodeTables {
+  alignas(64) uint16_t int4[32];
+  alignas(64) uint16_t e2m1[32];
+  CodeTables() {
+    for (int u = 0; u < 32; ++u) {
+      int4[u] = u < 16 ? f2bf_trunc((float)(u - 8)) : 0;  // exact
+      e2m1[u] = u < 16 ? f2bf_trunc(tables().e2m1[u]) : 0;
     }
-  const __m512i idx0 = _mm512_load_si512(ib[0]), idx1 = _mm512_load_si512(ib[1]);
-  const __m512i idx2 = _mm512_load_si512(ib[2]), idx3 = _mm512_load_si512(ib[3]);
-  const __mmask64 keep = 0x5555555555555555ull;
-  const __m512i m0f = _mm512_set1_epi32(0x0F0F0F0F);
-  __m512 tot[kMaxTokens];
-  for (int j = 0; j < nt; ++j) tot[j] = _mm512_setzero_ps();
+  }
+};
+const CodeTables& code_tables() {
+  static CodeTables t;
+  return t;
+}
+
+template <int NM, bool FP4>
+__attribute__((target("avx512f,avx512bw,avx512bf16"))) void slices_avx512(const MatRef* mat, int KB, int sl,
+                                                                          const uint16_t* const* xr, int nrows,
+                                                                          int nt) {
+  const __m512i table = _mm512_load_si512(FP4 ? code_tables().e2m1 : code_tables().int4);
+  const __m512i lo4 = _mm512_set1_epi32(0x000F000F);
+  __m512 tot[NM][kMaxTokens];
+  for (int mi = 0; mi < NM; ++mi)
+    for (int j = 0; j < nt; ++j) tot[mi][j] = _mm512_setzero_ps();
   for (int kb = 0; kb < KB; ++kb) {
     const int64_t tile = (int64_t)sl * KB + kb;
-    const uint8_t* tp = pay + tile * 256;
-    __m512i w[16];
-    for (int q = 0; q < 4; ++q) {
-      const __m512i d = _mm512_loadu_si512(tp + 64 * q);
-      const __m512i v1 = _mm512_and_si512(d, m0f);                        // nibbles 0, 2, 4, 6
-      const __m512i v2 = _mm512_and_si512(_mm512_srli_epi32(d, 4), m0f);  // nibbles 1, 3, 5, 7
-      w[q * 4 + 0] = _mm512_permutexvar_epi16(_mm512_maskz_permutex2var_epi8(keep, v1, idx0, v2), table);
-      w[q * 4 + 1] = _mm512_permutexvar_epi16(_mm512_maskz_permutex2var_epi8(keep, v1, idx1, v2), table);
-      w[q * 4 + 2] = _mm512_permutexvar_epi16(_mm512_maskz_permutex2var_epi8(keep, v1, idx2, v2), table);
-      w[q * 4 + 3] = _mm512_permutexvar_epi16(_mm512_maskz_permutex2var_epi8(keep, v1, idx3, v2), table);
+    __m512 sc[NM][2];
+    for (int mi = 0; mi < NM; ++mi) {
+      const uint8_t* sp = mat[mi].sca + tile * 32;
+      if (!FP4) {
+        const __m256i b = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(sp));
+        sc[mi][0] = sc[mi][1] = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(b), 16));
+      } else {
+        // e4m3 -> fp32: magnitude bits placed under the fp32 exponent/mantissa, times 2^120
+        // (normals and subnormals alike), then the sign
+        const __m512 k120 = _mm512_set1_ps(1.329227995784916e36f);  // 2^120
+        const __m512i x7f = _mm512_set1_epi32(0x7F), x80 = _mm512_set1_epi32(0x80);
+        for (int h = 0; h < 2; ++h) {
+          const __m512i c = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(sp + 16 * h)));
+          const __m512 m = _mm512_mul_ps(_mm512_castsi512_ps(_mm512_slli_epi32(_mm512_and_si512(c, x7f), 20)), k120);
+          sc[mi][h] = _mm512_castsi512_ps(
+              _mm512_or_si512(_mm512_castps_si512(m), _mm512_slli_epi32(_mm512_and_si512(c, x80), 24)));
+        }
+      }
     }
-    const uint8_t* sp = sca + tile * 32;
-    __m512 s0, s1;
-    if (fmt == EFF_WFMT_INT4_G32_BF16) {
-      const __m256i b = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(sp));
-      s0 = s1 = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(b), 16));
-    } else {
-      // e4m3 -> fp32: magnitude bits placed under the fp32 exponent/mantissa, times 2^120
-      // (normals and subnormals alike), then the sign
-      const __m512 k120 = _mm512_set1_ps(1.329227995784916e36f);  // 2^120
-      const __m512i c0 = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(sp)));
-      const __m512i c1 = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(sp + 16)));
-      const __m512i x7f = _mm512_set1_epi32(0x7F), x80 = _mm512_set1_epi32(0x80);
-      s0 = _mm512_mul_ps(_mm512_castsi512_ps(_mm512_slli_epi32(_mm512_and_si512(c0, x7f), 20)), k120);
-      s1 = _mm512_mul_ps(_mm512_castsi512_ps(_mm512_slli_epi32(_mm512_and_si512(c1, x7f), 20)), k120);
-      s0 = _mm512_castsi512_ps(_mm512_or_si512(_mm512_castps_si512(s0), _mm512_slli_epi32(_mm512_and_si512(c0, x80), 24)));
-      s1 = _mm512_castsi512_ps(_mm512_or_si512(_mm512_castps_si512(s1), _mm512_slli_epi32(_mm512_and_si512(c1, x80), 24)));
-    }
-    for (int i = 0; i < nrows; ++i) {
-      const int32_t* xk = reinterpret_cast<const int32_t*>(xr[i] + kb * 32);  // 16 bf16 pairs
-      __m512 a0 = _mm512_setzero_ps(), a1 = _mm512_setzero_ps();
-      for (int z = 0; z < 8; ++z)
-        a0 = _mm512_dpbf16_ps(a0, (__m512bh)w[z], (__m512bh)_mm512_set1_epi32(xk[z]));
-      for (int z = 8; z < 16; ++z)
-        a1 = _mm512_dpbf16_ps(a1, (__m512bh)w[z], (__m512bh)_mm512_set1_epi32(xk[z]));
-      __m512& t = tot[i % nt];
-      t = _mm512_fmadd_ps(s0, a0, t);
-      t = _mm512_fmadd_ps(s1, a1, t);
+    for (int h = 0; h < 2; ++h) {  // inputs 16h .. 16h+15 of the tile (one scale group for NVFP4)
+      __m512i w[NM][8];
+      for (int mi = 0; mi < NM; ++mi)
+        for (int qq = 0; qq < 2; ++qq) {
+          const __m512i d = _mm512_loadu_si512(mat[mi].pay + tile * 256 + 64 * (2 * h + qq));
+          w[mi][4 * qq + 0] = _mm512_permutexvar_epi16(_mm512_and_si512(d, lo4), table);
+          w[mi][4 * qq + 1] = _mm512_permutexvar_epi16(_mm512_and_si512(_mm512_srli_epi32(d, 4), lo4), table);
+          w[mi][4 * qq + 2] = _mm512_permutexvar_epi16(_mm512_and_si512(_mm512_srli_epi32(d, 8), lo4), table);
+          w[mi][4 * qq + 3] = _mm512_permutexvar_epi16(_mm512_and_si512(_mm512_srli_epi32(d, 12), lo4), table);
+        }
+      for (int i = 0; i < nrows; ++i) {
+        const int32_t* xk = reinterpret_cast<const int32_t*>(xr[i] + kb * 32 + 16 * h);  // 8 bf16 pairs
+        __m512 a[NM], b[NM];  // two accumulation chains per matrix (even and odd pairs)
+        for (int mi = 0; mi < NM; ++mi) a[mi] = b[mi] = _mm512_setzero_ps();
+        for (int z = 0; z < 8; z += 2) {
+          const __m512bh bx0 = (__m512bh)_mm512_set1_epi32(xk[z]), bx1 = (__m512bh)_mm512_set1_epi32(xk[z + 1]);
+          for (int mi = 0; mi < NM; ++mi) {
+            a[mi] = _mm512_dpbf16_ps(a[mi], (__m512bh)w[mi][z], bx0);
+            b[mi] = _mm512_dpbf16_ps(b[mi], (__m512bh)w[mi][z + 1], bx1);
+          }
+        }
+        for (int mi = 0; mi < NM; ++mi) a[mi] = _mm512_add_ps(a[mi], b[mi]);
+        const int j = i < nt ? i : i - nt;
+        for (int mi = 0; mi < NM; ++mi) tot[mi][j] = _mm512_fmadd_ps(sc[mi][h], a[mi], tot[mi][j]);
+      }
     }
   }
-  const __m512 ts = _mm512_set1_ps(tscale);
-  for (int j = 0; j < nt; ++j) {
-    alignas(64) float v[16];
-    _mm512_store_ps(v, _mm512_mul_ps(tot[j], ts));
-    for (int r = 0; r < 16; ++r) out[r * nt + j] = v[r];
+  for (int mi = 0; mi < NM; ++mi) {
+    const __m512 ts = _mm512_set1_ps(mat[mi].tscale);
+    for (int j = 0; j < nt; ++j) {
+      alignas(64) float v[16];
+      _mm512_store_ps(v, _mm512_mul_ps(tot[mi][j], ts));
+      for (int r = 0; r < 16; ++r) mat[mi].out[r * nt + j] = v[r];
+    }
   }
 }
 
-SliceFn pick_slice(int isa) { return isa == 1 ? slice_avx512 : slice_avx2; }
+// position of input i in the paired order: inside each group of 8, input e goes to 2*(e%4) + e/4
+inline int pair_pos(int i) { return (i & ~7) | ((i & 3) << 1) | ((i >> 2) & 1); }
+
+// rows 16*sl.. of NM matrices (1 or 2, same shape) against the same input rows: the paired-order
+// AVX-512 kernel (isa 1) or the AVX2 kernel (isa 0, inputs in natural order)
+void run_slices(int isa, int fmt, int nm, const MatRef* m, int KB, int sl, const uint16_t* const* xr, int nrows,
+                int nt) {
+  if (isa == 1) {
+    const bool fp4 = fmt == EFF_WFMT_NVFP4_G16_E4M3;
+    if (nm == 2)
+      fp4 ? slices_avx512<2, true>(m, KB, sl, xr, nrows, nt) : slices_avx512<2, false>(m, KB, sl, xr, nrows, nt);
+    else
+      fp4 ? slices_avx512<1, true>(m, KB, sl, xr, nrows, nt) : slices_avx512<1, false>(m, KB, sl, xr, nrows, nt);
+    return;
+  }
+  for (int mi = 0; mi < nm; ++mi) slice_avx2(m[mi].pay, m[mi].sca, KB, sl, fmt, xr, nrows, nt, m[mi].tscale, m[mi].out);
+}
 
 }  // namespace
 
@@ -216,10 +248,18 @@ int host_isa_best() {
 }
 
 // Host share of one call: entries with cpu_ids[p] >= 0 get y[p] = W_d (silu(W_g x) * (W_u x)) of
-// expert cpu_ids[p] of `layer`, x the entry's token row (bf16).  One parallel pass: the 16-row
-// slices of gate+up of every host expert first, then the slices of down; a down task waits
-// until its expert's gate/up slices are done (tasks are claimed in order, so this cannot
-// deadlock).  The down input a = silu(g)*u goes in as a bf16 hi + lo pair (error ~2^-16).
+// expert cpu_ids[p] of `layer`, x the entry's token row (bf16).
+//
+// The work is 16-row slices: U*SI of gate+up (both matrices in one sweep over the shared inputs,
+// SwiGLU applied) and U*SH of down.  With C pool threads it runs as 2C ordered tasks: task c < C
+// takes a contiguous range of the gate/up slices, task C + c a contiguous range of the down
+// slices, so each thread streams contiguous memory and the claiming costs 2C atomic operations
+// per call instead of one per slice (on the 16-core host this was measured 1.6x faster than one
+// task per slice, and faster than three ranges per thread).  A down range first waits until every gate/up slice of the
+// experts it touches is done; tasks are claimed in order, so every gate/up range has been taken
+// by a running thread by then and the wait always ends.  The down input a = silu(g)*u goes in as
+// a bf16 hi + lo pair (error ~2^-16).  The AVX-512 kernel takes its inputs in paired order: the
+// token rows are permuted once per call and a is written that way.
 void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_ids, int B, float* y) {
   const eff_config& c = e->cfg;
   const int K = c.top_k, H = c.hidden, I = c.inter, E = c.num_experts;
@@ -246,42 +286,49 @@ void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_id
     ++U;
   }
   if (U == 0) return;
+  const int isa = e->host_isa;
+  // the token rows as the slice kernel reads them
+  const uint16_t* xin = x;
+  if (isa == 1) {
+    if (hs.xp.size() < (size_t)B * H) hs.xp.resize((size_t)B * H);
+    for (int t = 0; t < B; ++t)
+      for (int i = 0; i < H; ++i) hs.xp[(size_t)t * H + pair_pos(i)] = x[(size_t)t * H + i];
+    xin = hs.xp.data();
+  }
   // SwiGLU activations (hi and lo bf16 rows) per (expert, token)
   int off[kMaxEntries + 1];
   off[0] = 0;
   for (int u = 0; u < U; ++u) off[u + 1] = off[u] + hs.ucnt[u];
   const size_t need = (size_t)off[U] * I * 2;
   if (hs.a.size() < need) hs.a.resize(need);
-  for (int u = 0; u < U; ++u) hs.done[u].store(0, std::memory_order_relaxed);
-  const SliceFn slice = pick_slice(e->host_isa);
+  for (int u = 0; u < U; ++u) hs.done[u].v.store(0, std::memory_order_relaxed);
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
   const int SI = I / 16, SH = H / 16;
-  const int n1 = U * SI;
-  e->pool_threads->parallel_for(n1 + U * SH, [&](int task) {
-    if (task < n1) {  // gate and up: 16 rows of a
-      const int u = task / SI, sl = task % SI;
-      const int nt = hs.ucnt[u];
-      const int64_t flat = (int64_t)layer * E + hs.uexp[u];
-      const uint8_t* rec = e->pool + flat * e->R;
-      const uint16_t* xr[kMaxTokens];
-      for (int j = 0; j < nt; ++j) xr[j] = x + (size_t)(hs.uent[u][j] / K) * H;
-      float g[16 * kMaxTokens], v[16 * kMaxTokens];
-      slice(rec, rec + 3 * pay, H / 32, sl, c.wformat, xr, nt, nt, e->h_ts[flat * 3 + 0], g);
-      slice(rec + pay, rec + 3 * pay + sca, H / 32, sl, c.wformat, xr, nt, nt, e->h_ts[flat * 3 + 1], v);
-      uint16_t* ahi = hs.a.data() + (size_t)off[u] * I * 2;
-      for (int r = 0; r < 16; ++r)
-        for (int j = 0; j < nt; ++j) {
-          const float gg = g[r * nt + j], uu = v[r * nt + j];
-          const float a = gg / (1.f + std::exp(-gg)) * uu;
-          const uint16_t hi = f2bf_trunc(a);
-          ahi[(size_t)j * I + sl * 16 + r] = hi;                                   // row j
-          ahi[(size_t)(nt + j) * I + sl * 16 + r] = f2bf_rne(a - bf16f(hi));      // row nt + j
-        }
-      hs.done[u].fetch_add(1, std::memory_order_release);
-      return;
+  const int NG = U * SI, ND = U * SH;
+  const int C = e->pool_threads->size();
+  auto gate_up = [&](int u, int sl) {  // 16 rows of a
+    const int nt = hs.ucnt[u];
+    const int64_t flat = (int64_t)layer * E + hs.uexp[u];
+    const uint8_t* rec = e->pool + flat * e->R;
+    const uint16_t* xr[kMaxTokens];
+    for (int j = 0; j < nt; ++j) xr[j] = xin + (size_t)(hs.uent[u][j] / K) * H;
+    float g[16 * kMaxTokens], v[16 * kMaxTokens];
+    const MatRef m[2] = {{rec, rec + 3 * pay, e->h_ts[flat * 3 + 0], g},
+                         {rec + pay, rec + 3 * pay + sca, e->h_ts[flat * 3 + 1], v}};
+    run_slices(isa, c.wformat, 2, m, H / 32, sl, xr, nt, nt);
+    uint16_t* ahi = hs.a.data() + (size_t)off[u] * I * 2;
+    for (int r = 0; r < 16; ++r) {
+      const int col = isa == 1 ? pair_pos(sl * 16 + r) : sl * 16 + r;
+      for (int j = 0; j < nt; ++j) {
+        const float gg = g[r * nt + j], uu = v[r * nt + j];
+        const float a = gg / (1.f + std::exp(-gg)) * uu;
+        const uint16_t hi = f2bf_trunc(a);
+        ahi[(size_t)j * I + col] = hi;                                   // row j
+        ahi[(size_t)(nt + j) * I + col] = f2bf_rne(a - bf16f(hi));      // row nt + j
+      }
     }
-    const int t2 = task - n1, u = t2 / SH, sl = t2 % SH;  // down: 16 rows of y
-    while (hs.done[u].load(std::memory_order_acquire) < SI) _mm_pause();
+  };
+  auto down = [&](int u, int sl) {  // 16 rows of y
     const int nt = hs.ucnt[u];
     const int64_t flat = (int64_t)layer * E + hs.uexp[u];
     const uint8_t* rec = e->pool + flat * e->R;
@@ -289,10 +336,35 @@ void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_id
     const uint16_t* abase = hs.a.data() + (size_t)off[u] * I * 2;
     for (int i = 0; i < 2 * nt; ++i) ar[i] = abase + (size_t)i * I;
     float out[16 * kMaxTokens];
-    slice(rec + 2 * pay, rec + 3 * pay + 2 * sca, I / 32, sl, c.wformat, ar, 2 * nt, nt, e->h_ts[flat * 3 + 2],
-          out);
+    const MatRef m = {rec + 2 * pay, rec + 3 * pay + 2 * sca, e->h_ts[flat * 3 + 2], out};
+    run_slices(isa, c.wformat, 1, &m, I / 32, sl, ar, 2 * nt, nt);
     for (int r = 0; r < 16; ++r)
       for (int j = 0; j < nt; ++j) y[(int64_t)hs.uent[u][j] * H + sl * 16 + r] = out[r * nt + j];
+  };
+  e->pool_threads->parallel_for(2 * C, [&](int task) {
+    if (task < C) {  // gate/up slices [b, f) in (expert, slice) order
+      const int b = (int)((int64_t)NG * task / C), f = (int)((int64_t)NG * (task + 1) / C);
+      int run = 0;
+      for (int i = b; i < f; ++i) {
+        gate_up(i / SI, i % SI);
+        ++run;
+        if (i + 1 == f || (i + 1) % SI == 0) {  // end of this expert's share of the range
+          hs.done[i / SI].v.fetch_add(run, std::memory_order_release);
+          run = 0;
+        }
+      }
+      return;
+    }
+    const int b = (int)((int64_t)ND * (task - C) / C), f = (int)((int64_t)ND * (task - C + 1) / C);
+    int ready = -1;
+    for (int i = b; i < f; ++i) {
+      const int u = i / SH;
+      if (u != ready) {
+        while (hs.done[u].v.load(std::memory_order_acquire) < SI) _mm_pause();
+        ready = u;
+      }
+      down(u, i % SH);
+    }
   });
 }
 
