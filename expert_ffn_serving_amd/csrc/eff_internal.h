@@ -158,7 +158,7 @@ struct eff_engine {
 
   // decode scratch
   eff::DecodePlan* d_plan = nullptr;
-  float* d_a = nullptr;           // [maxU][maxB][I] fp32 SwiGLU activations
+  float* d_a = nullptr;           // SwiGLU activations: [maxU][maxB][I] fp16, then [maxU][maxB][I/8] float2
   int maxU = 0;
 
   // orchestrator buffers (device)

@@ -7,7 +7,10 @@
 //   (plan)      distinct GPU slots of the call and their entries, one record per slot,
 //               made by the control kernels (k_plan or the fused k_control)
 //   k_gateup    gate and up rows of one 16-row slice over all of H, both matrices
-//               at once, reduced inside the workgroup, SwiGLU applied
+//               at once, reduced inside the workgroup, SwiGLU applied; the result is
+//               written as fp16 in the order k_down reads it, scaled per (token, slice)
+//               by a power of two into [2^14, 2^15), with the scale and (int4) the sum
+//               of every 8-group beside it
 //   k_down      one 16-row slice of the down matrix over all of I
 // No workgroup depends on another inside a kernel, so no device-scope fence is
 // needed (on this multi-die part such a fence writes back and invalidates a whole
@@ -152,7 +155,7 @@ template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
 k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
          const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H,
-         int I, int K, int maxB, float* __restrict__ a_out) {
+         int I, int K, int maxB, uint16_t* __restrict__ a16, float2* __restrict__ ag) {
   constexpr int UNR = NT >= 8 ? 2 : (NT == 4 ? 4 : 8);  // tiles in flight per wave (x takes 4*NT VGPRs each)
   __shared__ float s_red[4][2][16][NT];
   const int NS = I / 16, KB = H / 32;
@@ -231,8 +234,8 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
         for (int j = 0; j < NT; ++j) s_red[wave][m][r][j] = acc[m][j];
     }
     __syncthreads();
-    if (tid < 16 * nt) {
-      const int row = tid / nt, j = tid % nt;
+    if (tid < 16 * nt) {  // 16 consecutive lanes per token: j = tid / 16, row = tid % 16
+      const int j = tid >> 4, row = tid & 15;
       float g = s_red[0][0][row][j] + s_red[1][0][row][j];
       g += s_red[2][0][row][j];
       g += s_red[3][0][row][j];
@@ -243,7 +246,29 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
         g *= ts[(int64_t)un->flat * 3 + 0];
         v *= ts[(int64_t)un->flat * 3 + 1];
       }
-      a_out[((int64_t)u * maxB + c0 + j) * I + sl * 16 + row] = silu(g) * v;
+      const float a = silu(g) * v;
+      // the slice's power-of-two scale: max |a| over its 16 rows lands in [2^14, 2^15)
+      float mx = fabsf(a);
+      mx = fmaxf(mx, __shfl_xor(mx, 8));
+      mx = fmaxf(mx, __shfl_xor(mx, 4));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      int sh = 0;
+      if (mx > 0.f) {
+        int ex;
+        frexpf(mx, &ex);  // mx < 2^ex
+        sh = min(15 - ex, 100);
+      }
+      const _Float16 h = (_Float16)ldexpf(a, sh);
+      float gs = (float)h;  // sum of the 8-group (rows 8*(row/8) ..), int4 only
+      gs += __shfl_xor(gs, 4);
+      gs += __shfl_xor(gs, 2);
+      gs += __shfl_xor(gs, 1);
+      // int4: the pairs (a_m, a_m+4) of each 8-group meet the nibble pairs of a weight dword
+      const int pos = FMT == EFF_WFMT_INT4_G32_BF16 ? (row & 8) | ((row & 3) << 1) | ((row >> 2) & 1) : row;
+      const int64_t tok = (int64_t)u * maxB + c0 + j;
+      a16[tok * I + sl * 16 + pos] = __builtin_bit_cast(uint16_t, h);
+      if ((row & 7) == 0) ag[tok * (I / 8) + sl * 2 + (row >> 3)] = make_float2(ldexpf(1.f, -sh), gs);
     }
     __syncthreads();
   }
@@ -251,8 +276,8 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
 
 // ---------------------------------------------------------------------------- down
 template <int FMT, int NT>
-__device__ inline void down_tile(uint32_t d, uint32_t rd, const uint4* s_a4, const float (*s_asum)[512], int kb,
-                                 int q, int nt, int I8, float (&acc)[NT]) {
+__device__ inline void down_tile(uint32_t d, uint32_t rd, const uint4* s_a4, const float2* s_ag, int kb, int q,
+                                 int nt, int I8, float (&acc)[NT]) {
   const float sd = scale_value<FMT>(rd);
   uint32_t p0, p1, p2, p3;
   if (FMT == EFF_WFMT_INT4_G32_BF16) {
@@ -268,26 +293,24 @@ __device__ inline void down_tile(uint32_t d, uint32_t rd, const uint4* s_a4, con
   for (int j = 0; j < NT; ++j) {
     if (j < nt) {
       const uint4 av = s_a4[j * I8 + kb * 4 + q];
+      const float2 sg = s_ag[j * I8 + kb * 4 + q];  // (2^-shift of the slice, sum of the 8-group)
       float raw = dot2_f16(p3, av.w, dot2_f16(p2, av.z, dot2_f16(p1, av.y, dot2_f16(p0, av.x, 0.f))));
-      if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-1032.f, s_asum[j][kb * 4 + q], raw);
-      acc[j] = fmaf(sd, raw, acc[j]);
+      if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-1032.f, sg.y, raw);
+      acc[j] = fmaf(sd, raw * sg.x, acc[j]);
     }
   }
 }
 
-// grid: maxU * (H/16) workgroups, one per (plan unit, 16-row slice of H).  The SwiGLU
-// activations of the unit's tokens are staged in LDS as fp16, each token scaled by a power of
-// two so that its largest value fits.
+// grid: maxU * (H/16) workgroups, one per (plan unit, 16-row slice of H).  The unit's SwiGLU
+// activations, already fp16 from k_gateup, are copied into LDS with their per-group scales and
+// sums before the sweep.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
 k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
-       const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const float* __restrict__ a_in, int H,
-       int I, int maxB, float* __restrict__ y) {
-  extern __shared__ uint4 s_a4[];            // [NT][I/8] groups of 8 fp16 (int4 order permuted)
-  __shared__ float s_asum[NT][512];          // int4: sum of each 8-group (I/8 <= 512)
+       const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ a16,
+       const float2* __restrict__ ag, int H, int I, int maxB, float* __restrict__ y) {
+  extern __shared__ uint4 s_a4[];            // [NT][I/8] groups of 8 fp16, then [NT][I/8] float2
   __shared__ float s_red[4][16][NT];
-  __shared__ float s_scale[NT];
-  __shared__ float s_amax[NT][4];
   constexpr int UNR = NT >= 4 ? 4 : 8;  // tiles in flight per wave
   const int NS = H / 16, KB = I / 32, I8 = I / 8;
   const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
@@ -305,6 +328,7 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
     wg_copy(src + so, rec + so, (int64_t)KB * 32);
     __syncthreads();
   }
+  float2* s_ag = reinterpret_cast<float2*>(s_a4 + NT * I8);
   const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 4;
   const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
 
@@ -318,49 +342,12 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
       wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
       rd[z] = k < KB ? load_scale_raw<FMT>(ds + k * 32) : 0u;
     }
-    // per-token power-of-two scale: |a| * 2^-e < 2^15
-    for (int j = 0; j < nt; ++j) {
-      const float* aj = a_in + ((int64_t)u * maxB + c0 + j) * I;
-      float mx = 0.f;
-      for (int k = tid; k < I; k += kWG) mx = fmaxf(mx, fabsf(aj[k]));
-      for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      if (lane == 0) s_amax[j][wave] = mx;
-    }
-    __syncthreads();
-    if (tid < nt) {
-      float mx = fmaxf(fmaxf(s_amax[tid][0], s_amax[tid][1]), fmaxf(s_amax[tid][2], s_amax[tid][3]));
-      int e = 0;
-      if (mx > 0.f) {
-        frexpf(mx, &e);        // mx = f * 2^e, f in [0.5, 1)
-        e = e > 15 ? e - 15 : 0;
-      }
-      s_scale[tid] = ldexpf(1.f, e);
-    }
-    __syncthreads();
+    // the tokens' activations (16 B per 8-group) and their (scale, sum) pairs into LDS
     for (int i = tid; i < nt * I8; i += kWG) {
       const int j = i / I8, g = i % I8;
-      const float* src = a_in + ((int64_t)u * maxB + c0 + j) * I + g * 8;
-      const float inv = 1.f / s_scale[j];
-      _Float16 h[8];
-      float sum = 0.f;
-#pragma unroll
-      for (int z = 0; z < 8; ++z) {
-        h[z] = (_Float16)(src[z] * inv);
-        sum += (float)h[z];
-      }
-      uint32_t o[4];
-      if (FMT == EFF_WFMT_INT4_G32_BF16) {
-#pragma unroll
-        for (int z = 0; z < 4; ++z)
-          o[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[z]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[z + 4]) << 16);
-        s_asum[j][g] = sum;
-      } else {
-#pragma unroll
-        for (int z = 0; z < 4; ++z)
-          o[z] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * z]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * z + 1]) << 16);
-      }
-      s_a4[j * I8 + g] = make_uint4(o[0], o[1], o[2], o[3]);
+      const int64_t tok = (int64_t)u * maxB + c0 + j;
+      s_a4[j * I8 + g] = *reinterpret_cast<const uint4*>(a16 + tok * I + g * 8);
+      s_ag[j * I8 + g] = ag[tok * I8 + g];
     }
     __syncthreads();
     float acc[NT];
@@ -368,7 +355,7 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
     for (int j = 0; j < NT; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int z = 0; z < UNR; ++z)
-      if (wave + 4 * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_asum, wave + 4 * z, q, nt, I8, acc);
+      if (wave + 4 * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_ag, wave + 4 * z, q, nt, I8, acc);
     for (int kb0 = wave + 4 * UNR; kb0 < KB; kb0 += 4 * UNR) {
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
@@ -378,7 +365,7 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
       }
 #pragma unroll
       for (int z = 0; z < UNR; ++z)
-        if (kb0 + 4 * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_asum, kb0 + 4 * z, q, nt, I8, acc);
+        if (kb0 + 4 * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_ag, kb0 + 4 * z, q, nt, I8, acc);
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -397,7 +384,6 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
       float v = s_red[0][row][j] + s_red[1][row][j];
       v += s_red[2][row][j];
       v += s_red[3][row][j];
-      v = v * s_scale[j];
       if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= ts[(int64_t)un->flat * 3 + 2];
       const int p = un->entry[c0 + j];
       y[(int64_t)p * H + sl * 16 + row] = v;
@@ -477,15 +463,18 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, h
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   const int ts = timing_begin(e, EFF_T_DECODE_GATEUP, s);
+  // d_a holds 4 bytes per activation: the fp16 values, then one (scale, sum) pair per 8 of them
+  uint16_t* a16 = reinterpret_cast<uint16_t*>(e->d_a);
+  float2* ag = reinterpret_cast<float2*>(a16 + (size_t)e->maxU * c.max_tokens * I);
   hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(units * (I / 16)), dim3(kWG), 0, s, e->d_arena, e->pool_dev, e->R,
-                     e->d_ts, e->d_plan, x, H, I, c.top_k, c.max_tokens, e->d_a);
+                     e->d_ts, e->d_plan, x, H, I, c.top_k, c.max_tokens, a16, ag);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
-  size_t lds = (size_t)NT * (I / 8) * sizeof(uint4);
+  size_t lds = (size_t)NT * (I / 8) * (sizeof(uint4) + sizeof(float2));
   hipLaunchKernelGGL((k_down<FMT, NT>), dim3(units * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
-                     e->d_ts, e->d_plan, e->d_a, H, I, c.max_tokens, y);
+                     e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
   err = hipGetLastError();
   timing_mark(e, ts, 3, s);
   return err;
@@ -496,13 +485,13 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, h
 int decode_nt(int maxB) { return maxB >= 8 ? 8 : maxB >= 4 ? 4 : maxB >= 2 ? 2 : 1; }
 
 hipError_t decode_kernels_setup(int fmt, int maxB, int I) {
-  // allow N * I * 2 bytes of dynamic LDS for the down kernel of every token width N a call can take
+  // allow N * I * 3 bytes of dynamic LDS for the down kernel of every token width N a call can take
   const int NT = decode_nt(maxB);
   hipError_t err = hipSuccess;
 #define SETUP(F, N)                                                                                    \
   if (fmt == F && N <= NT && err == hipSuccess)                                                         \
     err = hipFuncSetAttribute((const void*)k_down<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize,    \
-                              N * (I / 8) * 16);
+                              N * (I / 8) * 24);
   SETUP(EFF_WFMT_INT4_G32_BF16, 1) SETUP(EFF_WFMT_INT4_G32_BF16, 2) SETUP(EFF_WFMT_INT4_G32_BF16, 4)
   SETUP(EFF_WFMT_INT4_G32_BF16, 8) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 1) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 2)
   SETUP(EFF_WFMT_NVFP4_G16_E4M3, 4) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 8)
