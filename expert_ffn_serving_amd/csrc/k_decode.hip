@@ -149,8 +149,9 @@ __device__ inline void gateup_tile(uint32_t wg, uint32_t wu, uint32_t rg, uint32
 // grid: maxU * (I/16) workgroups of 256 threads, one per (plan unit, 16-row slice of I).  Wave w
 // takes tiles w, w+4, ... of the slice (the 4 waves together sweep 1 KiB runs), gate and up at
 // once; everything reduces inside the workgroup, so no workgroup ever waits for another.
-// A unit installed by this call (fetch) first copies its slices from the pinned host pool into
-// the slot (16-byte loads); the gate/up and down kernels together copy the whole record.
+// A unit installed by this call (fetch) first copies its gate and up slices from the pinned host
+// pool into the slot (16-byte loads) and, once its rows are done, a 1/(I/16) share of the down
+// matrix: the whole record crosses the link inside this kernel, and k_down finds it resident.
 template <int FMT, int NT>
 __global__ void __launch_bounds__(kWG)
 k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
@@ -272,6 +273,12 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
     }
     __syncthreads();
   }
+  if (un->fetch) {  // this workgroup's share of the down payload and scales
+    const uint8_t* src = pool + (int64_t)un->flat * R;
+    const int64_t dpo = 2 * pay + (int64_t)sl * (pay / NS), dso = 3 * pay + 2 * sca + (int64_t)sl * (sca / NS);
+    wg_copy(src + dpo, rec + dpo, pay / NS);
+    wg_copy(src + dso, rec + dso, sca / NS);
+  }
 }
 
 // ---------------------------------------------------------------------------- down
@@ -320,14 +327,8 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* rec = arena + (int64_t)un->slot * R;
-  if (un->fetch) {  // installed by this call: this workgroup's down slice from the pool first
-    const uint8_t* src = pool + (int64_t)un->flat * R;
-    const int64_t po = 2 * pay + (int64_t)sl * KB * 256, so = 3 * pay + 2 * sca + (int64_t)sl * KB * 32;
-    wg_copy(src + po, rec + po, (int64_t)KB * 256);
-    wg_copy(src + so, rec + so, (int64_t)KB * 32);
-    __syncthreads();
-  }
+  // a record installed by this call was copied whole by k_gateup, the previous kernel on the stream
+  const uint8_t* rec = arena + (int64_t)un->slot * R;
   float2* s_ag = reinterpret_cast<float2*>(s_a4 + NT * I8);
   const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 4;
   const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
