@@ -165,9 +165,15 @@ def run_decode(eff, torch, synth, W, steps, warmup, profile_steps, threads, use_
     gpu_unique = sp["hits"] + sp["fetched"]               # distinct GPU experts over the pass (= entries, B = 1)
     mat_bytes = W.H * W.I // 2 + W.H * W.I // 16           # one matrix: payload + scales
     # algorithmic bytes of k_gateup: gate and up of every GPU expert once, x read, SwiGLU output written
-    gu_bytes = gpu_unique * 2 * mat_bytes + n_launch * B * W.H * 2 + gpu_unique * W.I * 4
-    # k_down: down of every GPU expert once, SwiGLU output read, y written
-    dn_bytes = gpu_unique * mat_bytes + gpu_unique * W.I * 4 + gpu_unique * W.H * 4
+    # (fp16 values plus one 8-byte scale/sum pair per 8 of them: 3 bytes per activation)
+    def gu_alg(units, launches):
+        return units * 2 * mat_bytes + launches * B * W.H * 2 + units * W.I * 3
+
+    # k_down: down of every GPU expert once, SwiGLU output read, y written (fp32)
+    def dn_alg(units):
+        return units * mat_bytes + units * W.I * 3 + units * W.H * 4
+
+    gu_bytes, dn_bytes = gu_alg(gpu_unique, n_launch), dn_alg(gpu_unique)
     gu_gbps = gu_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else 0.0
     dn_gbps = dn_bytes / (d_ms * 1e-3) / 1e9 if d_ms > 0 else 0.0
     src = ("k_decode.hip",)
@@ -184,6 +190,19 @@ def run_decode(eff, torch, synth, W, steps, warmup, profile_steps, threads, use_
                  "algorithmic_bytes_per_launch": int(dn_bytes / max(1, n_launch)),
                  "avg_launch_us": round(d_ms * 1e3 / max(1, n_launch), 2)},
     }
+    # the same kernels on the calls that fetched nothing: HBM reads only, no wait on the host link
+    nf = sp["launches_nofetch"][eff.T_DECODE_GATEUP]
+    if nf > 0:
+        g_nf, d_nf = sp["kernel_ms_nofetch"][eff.T_DECODE_GATEUP], sp["kernel_ms_nofetch"][eff.T_DECODE_DOWN]
+        u_nf = sp["gpu_experts_nofetch"]
+        gnf_gbps = gu_alg(u_nf, nf) / (g_nf * 1e-3) / 1e9
+        dnf_gbps = dn_alg(u_nf) / (d_nf * 1e-3) / 1e9
+        roofline["nofetch_launches"] = {
+            "share_of_launches": round(nf / max(1, n_launch), 3), "gpu_experts_per_launch": round(u_nf / nf, 3),
+            "gateup": {"avg_launch_us": round(g_nf * 1e3 / nf, 2), "achieved": round(gnf_gbps, 1),
+                       "frac": round(gnf_gbps / HBM_PEAK_GBPS, 4)},
+            "down": {"avg_launch_us": round(d_nf * 1e3 / nf, 2), "achieved": round(dnf_gbps, 1),
+                     "frac": round(dnf_gbps / HBM_PEAK_GBPS, 4)}}
     kernel_tok_s = profile_steps * B / ((g_ms + d_ms) * 1e-3) if g_ms + d_ms > 0 else 0.0
     detail = {
         "per_layer_call": {k: round(st[k] / calls, 3) for k in ("hits", "fetched", "host")},
@@ -298,8 +317,8 @@ def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1,
         n = st["launches"][eff.T_DECODE_GATEUP]
         g_ms, d_ms = st["kernel_ms"][eff.T_DECODE_GATEUP], st["kernel_ms"][eff.T_DECODE_DOWN]
         U = st["hits"] + st["fetched"]
-        gu = U * 2 * mat_bytes + n * B * H * 2 + U * B * I * 4   # upper bound on the small terms
-        dn = U * mat_bytes + U * B * (I + H) * 4
+        gu = U * 2 * mat_bytes + n * B * H * 2 + U * B * I * 3   # upper bound on the small terms
+        dn = U * mat_bytes + U * B * (I * 3 + H * 4)
         res["B%d" % B] = {
             "gpu_experts_per_launch": round(U / max(1, n), 2), "fetched": st["fetched"],
             "gateup_us": round(g_ms * 1e3 / max(1, n), 2), "gateup_GBps": round(gu / (g_ms * 1e-3) / 1e9, 1),

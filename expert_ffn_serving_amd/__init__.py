@@ -47,7 +47,8 @@ class Stats(ctypes.Structure):
                 ("host", ctypes.c_int64), ("spec_fetched", ctypes.c_int64), ("bytes_fetched", ctypes.c_int64),
                 ("qstar_hist", ctypes.c_int64 * 17), ("launches", ctypes.c_int64 * 4),
                 ("kernel_ms", ctypes.c_double * 4), ("host_ms", ctypes.c_double), ("wait_ms", ctypes.c_double),
-                ("host_calls", ctypes.c_int64)]
+                ("host_calls", ctypes.c_int64), ("launches_nofetch", ctypes.c_int64 * 4),
+                ("kernel_ms_nofetch", ctypes.c_double * 4), ("gpu_experts_nofetch", ctypes.c_int64)]
 
 
 _lib = None
@@ -267,7 +268,9 @@ class Engine:
         return dict(calls=st.calls, hits=st.hits, fetched=st.fetched, host=st.host,
                     spec_fetched=st.spec_fetched, bytes_fetched=st.bytes_fetched,
                     qstar_hist=list(st.qstar_hist), launches=list(st.launches), kernel_ms=list(st.kernel_ms),
-                    host_ms=st.host_ms, wait_ms=st.wait_ms, host_calls=st.host_calls)
+                    host_ms=st.host_ms, wait_ms=st.wait_ms, host_calls=st.host_calls,
+                    launches_nofetch=list(st.launches_nofetch), kernel_ms_nofetch=list(st.kernel_ms_nofetch),
+                    gpu_experts_nofetch=st.gpu_experts_nofetch)
 
     def reset_stats(self):
         _check(lib().eff_reset_stats(self.h))

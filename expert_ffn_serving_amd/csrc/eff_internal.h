@@ -16,7 +16,8 @@
 
 namespace eff {
 
-constexpr int kMaxTokens = 32;        // decode batch bound
+constexpr int kMaxTokens = 32;
+constexpr int kTimedMax = 4096;       // timed launches held before their events are resolved        // decode batch bound
 constexpr int kMaxTopK = 32;
 constexpr int kMaxEntries = 512;     // entries (B*K) of one decode call
 constexpr int kMaxSlots = 16384;      // single-workgroup victim sort (keys in LDS)
@@ -221,11 +222,16 @@ struct eff_engine {
   int host_isa = 0;               // host slice kernels: 0 AVX2 + FMA, 1 AVX-512 BF16
   eff::HostScratch hscratch;
   // kernel timing (EFF_CFG_TIMING): events (start, end) of each of two kernels per call
-  struct TimedCall { int kind; hipEvent_t ev[4]; };
-  std::vector<TimedCall> timed;     // recorded, not yet resolved
+  struct TimedCall { int kind; hipEvent_t ev[4]; bool has_q; };
+  std::vector<TimedCall> timed;     // recorded, not yet resolved (at most kTimedMax)
   std::vector<hipEvent_t> free_events;
   int64_t t_launches[4] = {0, 0, 0, 0};
   double t_ms[4] = {0, 0, 0, 0};
+  int64_t t_launches_nf[4] = {0, 0, 0, 0};  // calls that fetched nothing
+  double t_ms_nf[4] = {0, 0, 0, 0};
+  int64_t t_units_nf = 0;                   // their distinct GPU experts
+  int32_t* h_tq = nullptr;                  // pinned [kTimedMax][2]: fetch count, GPU experts per timed call
+  const int32_t* timing_q_src = nullptr;    // device fetch count of the call being launched, if any
   int64_t host_bytes_fetched = 0;
   int64_t host_spec_fetched = 0;
 };

@@ -70,7 +70,8 @@ static void release(eff_engine* e) {
                  e->d_pf_a, e->d_pf_y, e->d_pf_meta, e->d_pf_slot_of, e->d_pf_experts};
   for (void* p : dev)
     if (p) (void)hipFree(p);
-  void* host[] = {e->h_fetch, e->h_x, e->h_cpu, e->h_call, e->h_done, e->h_yhost, e->h_pf_ids, e->h_pf_meta};
+  void* host[] = {e->h_fetch, e->h_x, e->h_cpu, e->h_call, e->h_done, e->h_yhost, e->h_pf_ids, e->h_pf_meta,
+                  e->h_tq};
   for (void* p : host)
     if (p) (void)hipHostFree(p);
   hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_ctl, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0], e->ev_pf_done[1]};
@@ -125,6 +126,7 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipHostMalloc((void**)&e->h_call, kCallRing * sizeof(uint64_t), mapped));
   EFF_HIP_TRY(hipHostMalloc((void**)&e->h_done, 64, mapped));
   EFF_HIP_TRY(hipHostMalloc((void**)&e->h_yhost, (size_t)(B * K * H) * 4, mapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_tq, kTimedMax * 2 * sizeof(int32_t), 0));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_x_dev, e->h_x, 0));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_cpu_dev, e->h_cpu, 0));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_call_dev, e->h_call, 0));
@@ -192,6 +194,14 @@ static void resolve_timing(eff_engine* e) {
       e->t_ms[tc.kind + 1] += b;
       e->t_launches[tc.kind] += 1;
       e->t_launches[tc.kind + 1] += 1;
+      const int32_t* tq = e->h_tq + 2 * (&tc - e->timed.data());
+      if (tc.has_q && tq[0] == 0) {
+        e->t_units_nf += tq[1];
+        e->t_ms_nf[tc.kind] += a;
+        e->t_ms_nf[tc.kind + 1] += b;
+        e->t_launches_nf[tc.kind] += 1;
+        e->t_launches_nf[tc.kind + 1] += 1;
+      }
     }
     for (hipEvent_t ev : tc.ev)
       if (ev) e->free_events.push_back(ev);
@@ -201,12 +211,18 @@ static void resolve_timing(eff_engine* e) {
 
 int timing_begin(eff_engine* e, int kind, hipStream_t s) {
   if (!(e->cfg.flags & EFF_CFG_TIMING)) return -1;
-  if (e->timed.size() >= 4096) resolve_timing(e);  // bounded number of live events
+  if (e->timed.size() >= (size_t)kTimedMax) resolve_timing(e);  // bounded number of live events
   eff_engine::TimedCall tc;
   tc.kind = kind;
   for (int i = 0; i < 4; ++i) tc.ev[i] = take_event(e);
+  const int slot = (int)e->timed.size();
+  // the call's fetch count and GPU expert count, copied before the launch's first event (stream order)
+  tc.has_q = e->timing_q_src &&
+             hipMemcpyAsync(e->h_tq + 2 * slot, e->timing_q_src, sizeof(int32_t), hipMemcpyDeviceToHost, s) ==
+                 hipSuccess &&
+             hipMemcpyAsync(e->h_tq + 2 * slot + 1, &e->d_plan->nu, sizeof(int32_t), hipMemcpyDeviceToHost, s) ==
+                 hipSuccess;
   e->timed.push_back(tc);
-  const int slot = (int)e->timed.size() - 1;
   timing_mark(e, slot, 0, s);
   return slot;
 }
@@ -634,7 +650,10 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
     e->spec_copy_pending = true;
   }
   // GPU experts; a unit installed by this call reads its record from the pool and fills its slot
-  EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true));
+  e->timing_q_src = e->d_counts + 1;  // this call's fetch count (real split)
+  const hipError_t ffn_err = launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true);
+  e->timing_q_src = nullptr;
+  EFF_HIP_TRY(ffn_err);
   if (e->async_host) {
     // the combine waits for the host share (or the control kernel's own release of the call)
     EFF_HIP_TRY(launch_combine(e->d_ygpu, e->h_yhost_dev, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs,
@@ -772,7 +791,10 @@ int eff_get_stats(eff_engine* e, eff_stats* out) {
   for (int i = 0; i < 4; ++i) {
     out->launches[i] = e->t_launches[i];
     out->kernel_ms[i] = e->t_ms[i];
+    out->launches_nofetch[i] = e->t_launches_nf[i];
+    out->kernel_ms_nofetch[i] = e->t_ms_nf[i];
   }
+  out->gpu_experts_nofetch = e->t_units_nf;
   out->host_ms = e->host_ns.load() * 1e-6;
   out->wait_ms = e->wait_ns.load() * 1e-6;
   out->host_calls = e->host_calls_a.load();
@@ -793,9 +815,10 @@ int eff_reset_stats(eff_engine* e) {
   drain_worker(e);
   resolve_timing(e);
   for (int i = 0; i < 4; ++i) {
-    e->t_launches[i] = 0;
-    e->t_ms[i] = 0.0;
+    e->t_launches[i] = e->t_launches_nf[i] = 0;
+    e->t_ms[i] = e->t_ms_nf[i] = 0.0;
   }
+  e->t_units_nf = 0;
   e->host_bytes_fetched = 0;
   e->host_spec_fetched = 0;
   e->host_ns = 0;

@@ -790,10 +790,12 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
   const int n = B * K;
   if (tid >= 64 && tid < kKeyT0) {
     // waves 1-4 copy x for the host while wave 0 starts the top-K.  They wait for these stores
-    // to complete only after the split (below), before the plan's barrier: x_host is coherent host
-    // memory (not held in the L2), so a completed store is visible to the host, and the call word
-    // that wave 0 publishes after the last barrier is ordered after it.  (A system-scope fence
-    // would also write back the L2 from every wave, which costs microseconds.)
+    // to complete only after the split (below), before the plan's barrier; wave 0's system-scope
+    // fence before the call word then publishes them together with its own stores.  A completed
+    // store to coherent host memory is not yet visible to the host without that fence (measured:
+    // host ids published with completed system-scope stores and no fence were read stale), and
+    // one fence for the workgroup is enough: a fence per wave would write back the L2 once per
+    // wave, which costs microseconds.
     for (int i = tid - 64; i < B * H / 8; i += kKeyT0 - 64)
       reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
   } else if (tid >= kKeyT0) {
@@ -823,8 +825,8 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
     commit_body(c, C, true, spec_slots, nullptr, nullptr, counts + 3);
   }
   if (tid < 64) {
-    // the call word after a system-scope fence (which covers wave 0's host ids; x was fenced by
-    // the waves that copied it, before the first barrier)
+    // the call word after a system-scope fence (which covers wave 0's host ids and x, whose
+    // stores waves 1-4 completed before the plan's barrier)
     if (call_ring) {
       __threadfence_system();
       if (tid == 0) {

@@ -7,6 +7,9 @@
         HBM bytes per dispatch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run.  Each
         counter is scaled by what it reads for the largest plain device-to-device copy in the same
         run (a copy of --copy-bytes bytes reads and writes exactly that many bytes).
+    python3 -m expert_ffn_serving_amd.profile_summary trace DIR --kernel 'k_gateup<0, 1>' --last 2560
+        average duration of a kernel's dispatches in DIR/**/*kernel_trace.csv, over all of them and
+        over the last N by start time (the window a bench times last, e.g. its profiled pass).
 
 Counters are KiB per dispatch.  On gfx950 FETCH_SIZE reads about half of the bytes a copy
 actually fetches, which is why every figure is calibrated against the copy instead of trusted raw.
@@ -97,6 +100,37 @@ def cmd_traffic(a):
     print(text)
 
 
+def read_trace(d):
+    """{kernel: [(start_ns, duration_ns)]} from a rocprofv3 --kernel-trace csv directory."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_trace.csv under %s" % d)
+    out = collections.defaultdict(list)
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            out[kernel_name(r["Kernel_Name"])].append((s, e - s))
+    for v in out.values():
+        v.sort()
+    return out
+
+
+def cmd_trace(a):
+    data = read_trace(a.dir)
+    names = [k for k in data if k.startswith(a.kernel)]
+    if not names:
+        raise SystemExit("no dispatches of %s" % a.kernel)
+    res = {}
+    for k in sorted(names):
+        d = [x[1] for x in data[k]]
+        tail = d[-a.last:] if a.last > 0 else d
+        res[k] = {"dispatches": len(d), "avg_us": round(sum(d) / len(d) / 1e3, 3),
+                  "last": len(tail), "last_avg_us": round(sum(tail) / len(tail) / 1e3, 3),
+                  "last_min_us": round(min(tail) / 1e3, 3), "last_max_us": round(max(tail) / 1e3, 3)}
+    print(json.dumps(res, indent=1))
+    return res
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -110,8 +144,12 @@ def main(argv=None):
     t.add_argument("--source", nargs="+", default=["k_decode.hip"])
     t.add_argument("--command", default="")
     t.add_argument("--out", default="")
+    r = sub.add_parser("trace")
+    r.add_argument("dir")
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--last", type=int, default=0)
     a = p.parse_args(argv)
-    {"counters": cmd_counters, "traffic": cmd_traffic}[a.cmd](a)
+    {"counters": cmd_counters, "traffic": cmd_traffic, "trace": cmd_trace}[a.cmd](a)
 
 
 if __name__ == "__main__":

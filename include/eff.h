@@ -230,6 +230,11 @@ typedef struct eff_stats {
   double host_ms;         /* eff_decode_layer: wall time in the host executor */
   double wait_ms;         /* eff_decode_layer: wall time the host share waited for control kernels */
   int64_t host_calls;     /* eff_decode_layer calls with a host share */
+  /* the EFF_T_DECODE_* slots again, counting only eff_decode_layer calls that fetched no record
+   * (their kernels read HBM only; a fetch makes the gate/up kernel wait on the host link) */
+  int64_t launches_nofetch[4];
+  double kernel_ms_nofetch[4];
+  int64_t gpu_experts_nofetch; /* distinct GPU experts summed over those calls */
 } eff_stats;
 /* Changes eff_config.flags of a live engine (EFF_CFG_* bits); EFF_EINVAL for unknown bits. */
 int eff_set_flags(eff_engine* e, uint32_t flags);

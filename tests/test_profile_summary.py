@@ -49,3 +49,21 @@ def test_missing_counters_are_an_error(tmp_path):
     write_csv(f, "FETCH_SIZE", [("void eff::k_gateup<0, 1>(args)", 1.0)])
     with pytest.raises(SystemExit):
         ps.main(["traffic", "--fetch", f, "--write", f, "--kernel", "k_gateup"])  # no copy to calibrate
+
+
+def test_trace_window_averages(tmp_path, capsys):
+    d = tmp_path / "t"
+    os.makedirs(d / "host")
+    with open(d / "host" / "x_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        # five dispatches of one kernel, out of order in the file; one of another kernel
+        for start, dur in [(500, 9000), (100, 1000), (300, 3000), (400, 5000), (200, 2000)]:
+            w.writerow({"Kernel_Name": "void eff::(anonymous namespace)::k_down<0, 1>(args)",
+                        "Start_Timestamp": start, "End_Timestamp": start + dur})
+        w.writerow({"Kernel_Name": "eff::(anonymous namespace)::k_control(args)", "Start_Timestamp": 50,
+                    "End_Timestamp": 60})
+    res = ps.main(["trace", str(d), "--kernel", "k_down", "--last", "2"]) or json.loads(capsys.readouterr().out)
+    r = res["k_down<0, 1>"]
+    assert r["dispatches"] == 5 and r["avg_us"] == pytest.approx(4.0)
+    assert r["last"] == 2 and r["last_avg_us"] == pytest.approx(7.0)   # the two latest starts: 5000, 9000 ns
