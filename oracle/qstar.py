@@ -43,3 +43,25 @@ def qstar_bruteforce(m: int, f: int) -> int:
         if best_c is None or c < best_c:
             best_F, best_c = F, c
     return best_F
+
+
+def frac_q16(pcie_bytes_per_s: float, host_bytes_per_s: float) -> int:
+    """f from the two measured rates, as [FT-deep] §4 design pattern ② defines it: B_P / B_H
+    times 65536, an integer.  Readings (the pages give no rounding or range rule): the integer
+    part (floor), which also turns the configs' 0.4 and 0.7 into their 26214 and 45875; capped
+    at 65536, the value that fetches every miss, which is where B_P >= B_H leaves the method
+    ([FT-blog] §六: q* -> m as B_H approaches B_P); a host rate of zero with a nonzero link rate
+    also gives 65536, and no link (B_P = 0) gives 0.  Negative or NaN rates are rejected.
+    Exact rational arithmetic on the two floats, so the floor is taken of the true quotient."""
+    from fractions import Fraction
+    import math
+    bp, bh = pcie_bytes_per_s, host_bytes_per_s
+    if math.isnan(bp) or math.isnan(bh) or bp < 0 or bh < 0:
+        raise ValueError("rates must be non-negative numbers")
+    if bp == 0:
+        return 0
+    if bh == 0 or math.isinf(bp):
+        return Q16
+    if math.isinf(bh):
+        return 0
+    return min(Q16, math.floor(Fraction(bp) * Q16 / Fraction(bh)))

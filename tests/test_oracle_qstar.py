@@ -112,3 +112,39 @@ def test_invalid_inputs():
         qstar_rule(3, Q16 + 1)
     with pytest.raises(ValueError):
         qstar_rule(-1, 5)
+
+
+# f from measured rates ([FT-deep] §4 design pattern ②: B_P / B_H times 65536, an integer)
+def test_frac_q16_matches_the_configs_values():
+    from oracle.qstar import frac_q16
+    # the 35b-a3b and dsv4 decode configs quote f = 0.4 and 0.7 as 26214 and 45875
+    assert frac_q16(0.4, 1.0) == 26214 and frac_q16(0.7, 1.0) == 45875
+    assert frac_q16(4e9, 10e9) == 26214 and frac_q16(7.0, 10.0) == 45875
+
+
+def test_frac_q16_ends_and_edges():
+    from oracle.qstar import frac_q16
+    assert frac_q16(1.0, 1.0) == 65536          # link as fast as host memory: fetch every miss
+    assert frac_q16(3.0, 1.0) == 65536          # faster link: capped
+    assert frac_q16(0.0, 5.0) == 0              # no link: everything on the host
+    assert frac_q16(5.0, 0.0) == 65536          # no host bandwidth: everything fetched
+    assert frac_q16(1.0, 65536.0) == 1 and frac_q16(1.0, 65537.0) == 0   # the integer part, not rounding
+    assert frac_q16(65535.0, 65536.0) == 65535
+    for bad in ((-1.0, 1.0), (1.0, -1.0), (float("nan"), 1.0)):
+        with pytest.raises(ValueError):
+            frac_q16(*bad)
+
+
+def test_frac_q16_monotone_and_consistent_with_qstar():
+    import random
+    from oracle.qstar import frac_q16, qstar_rule
+    rnd = random.Random(7)
+    for _ in range(2000):
+        bh = rnd.uniform(1e9, 500e9)
+        bp, bp2 = sorted(rnd.uniform(0, 1.2 * bh) for _ in range(2))
+        f, f2 = frac_q16(bp, bh), frac_q16(bp2, bh)
+        assert 0 <= f <= f2 <= 65536                   # more link bandwidth never fetches less
+        r = min(1.0, bp / bh)
+        assert abs(f - 65536 * r) < 1.0 + 1e-9          # within one unit of the exact ratio
+        for m in (1, 7, 16, 160):
+            assert abs(qstar_rule(m, f) - m * r) <= 1.0 + m / 65536   # q* ~ m B_P / B_H ([FT-blog] §六)
