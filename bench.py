@@ -215,6 +215,18 @@ def run_decode(eff, torch, synth, W, steps, warmup, profile_steps, threads, use_
         "timed_as": "eager calls on one stream (no host synchronization)",
         "graph_replay_tok_s": round(steps * B / dt_graph, 2) if dt_graph else None,
     }
+    # the fetch fraction this machine would give ([FT-deep] §4 ②): link and host expert rates, run
+    # at the same time; the timed run keeps the workload's f
+    bw = eng.profile_bandwidth(512)
+    detail["bandwidth_profile"] = {
+        "records": bw["records"], "record_bytes": bw["record_bytes"],
+        "pcie_GBps_concurrent": round(bw["pcie_concurrent"] / 1e9, 2),
+        "host_GBps_concurrent": round(bw["host_concurrent"] / 1e9, 2),
+        "pcie_GBps_alone": round(bw["pcie_alone"] / 1e9, 2), "host_GBps_alone": round(bw["host_alone"] / 1e9, 2),
+        "frac_q16": bw["frac_q16"], "frac_q16_alone": bw["frac_q16_alone"], "frac_q16_workload": W.f_q16}
+    log("  bandwidth profile: link %.1f GB/s, host %.1f GB/s at once (alone %.1f / %.1f) -> f = %d (workload: %d)" % (
+        bw["pcie_concurrent"] / 1e9, bw["host_concurrent"] / 1e9, bw["pcie_alone"] / 1e9, bw["host_alone"] / 1e9,
+        bw["frac_q16"], W.f_q16))
     eng.close()
     del X, LG
     return dict(value=steps * B / dt, ms=dt * 1e3 / steps, roofline=roofline, detail=detail,

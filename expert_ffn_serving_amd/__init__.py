@@ -75,6 +75,9 @@ def lib():
             "eff_split_misses": (I32, [VP, VP, VP, VP, VP]),
             "eff_qstar": (I64, [I64, U32]),
             "eff_qstar_batch": (I32, [VP, VP, VP, I32, VP]),
+            "eff_frac_q16": (U32, [ctypes.c_double, ctypes.c_double]),
+            "eff_profile_bandwidth": (I32, [VP, I32, VP]),
+            "eff_set_fetch_frac": (I32, [VP, U32]),
             "eff_copy_missing": (I32, [VP, VP, VP]),
             "eff_expert_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP, VP]),
             "eff_host_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP]),
@@ -141,6 +144,18 @@ def _memcpy_d2h(dst: int, src: int, nbytes: int):
 
 def qstar(m: int, f: int) -> int:
     return int(lib().eff_qstar(m, f))
+
+
+def frac_q16(pcie_bytes_per_s: float, host_bytes_per_s: float) -> int:
+    """eff_frac_q16: 65536 * B_P / B_H as an integer, capped at 65536 (0xFFFFFFFF: bad input)."""
+    return int(lib().eff_frac_q16(pcie_bytes_per_s, host_bytes_per_s))
+
+
+class BwProfile(ctypes.Structure):
+    _fields_ = [("pcie_alone", ctypes.c_double), ("host_alone", ctypes.c_double),
+                ("pcie_concurrent", ctypes.c_double), ("host_concurrent", ctypes.c_double),
+                ("frac_q16", ctypes.c_uint32), ("frac_q16_alone", ctypes.c_uint32),
+                ("record_bytes", ctypes.c_int64), ("records", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 def qstar_batch(m, f, q, stream=None):
@@ -278,6 +293,16 @@ class Engine:
     def set_flags(self, flags: int):
         _check(lib().eff_set_flags(self.h, flags))
         self.cfg.flags = flags
+
+    def profile_bandwidth(self, records: int) -> dict:
+        """eff_profile_bandwidth: link and host expert rates (bytes/s), alone and concurrent, and f."""
+        out = BwProfile()
+        _check(lib().eff_profile_bandwidth(self.h, records, ctypes.byref(out)))
+        return {k: getattr(out, k) for k, _ in BwProfile._fields_ if k != "pad"}
+
+    def set_fetch_frac(self, frac_q16: int):
+        _check(lib().eff_set_fetch_frac(self.h, frac_q16))
+        self.cfg.fetch_frac_q16 = frac_q16
 
     def slot_ptr(self, slot: int) -> int:
         out = ctypes.c_void_p()

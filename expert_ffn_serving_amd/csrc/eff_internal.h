@@ -251,6 +251,8 @@ hipError_t launch_fallback_install(eff_engine* e, int layer, const int32_t* expe
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
                              float* y, hipStream_t s, bool plan_ready = false);
 hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s);
+// n records from the pool (flat ids first + i*stride modulo L*E) into dst[2][R] (bandwidth profile)
+hipError_t launch_bw_copy(eff_engine* e, int64_t first, int64_t stride, int n, uint8_t* dst, hipStream_t s);
 hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s);
 hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
                           const int32_t* spec_ids, hipStream_t s);

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -539,6 +540,130 @@ int eff_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, int n, eff_
   if (n < 0) return fail(EFF_EINVAL, "eff_qstar_batch: n < 0");
   EFF_HIP_TRY(launch_qstar_batch(m, f, q, n, (hipStream_t)stream));
   return EFF_OK;
+}
+
+uint32_t eff_frac_q16(double bp, double bh) {
+  if (std::isnan(bp) || std::isnan(bh) || bp < 0 || bh < 0) return 0xFFFFFFFFu;
+  if (bp == 0) return 0;
+  if (bh == 0 || std::isinf(bp)) return 65536u;
+  if (std::isinf(bh)) return 0;
+  // the integer part of bp * 65536 / bh, exactly: the quotient's floor, then corrected by the
+  // sign of q*bh - bp*65536 (one rounding in the fma keeps the sign; bp*65536 is exact)
+  const double num = bp * 65536.0;
+  double q = std::floor(num / bh);
+  if (q >= 65536.0) return 65536u;
+  if (std::fma(q, bh, -num) > 0) q -= 1;
+  else if (std::fma(q + 1, bh, -num) <= 0) q += 1;
+  return q >= 65536.0 ? 65536u : (uint32_t)q;
+}
+
+int eff_set_fetch_frac(eff_engine* e, uint32_t frac_q16) {
+  if (int rc = check_engine(e)) return rc;
+  if (frac_q16 > 65536u) return fail(EFF_EINVAL, "fetch_frac_q16 must be in [0, 65536]");
+  e->cfg.fetch_frac_q16 = frac_q16;
+  return EFF_OK;
+}
+
+// The host side of the profile: `calls` host shares of one token with K experts each (a layer's
+// experts in turn, layers cycling first, so consecutive calls read distinct records).
+static double host_profile_pass(eff_engine* e, int calls, const uint16_t* x, float* y) {
+  const eff_config& c = e->cfg;
+  std::vector<int32_t> cpu(c.top_k);
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0; i < calls; ++i) {
+    const int layer = i % c.num_layers, base = (i / c.num_layers) * c.top_k;
+    for (int k = 0; k < c.top_k; ++k) cpu[k] = (base + k) % c.num_experts;
+    host_ffn(e, layer, x, cpu.data(), 1, y);
+  }
+  return std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+}
+
+int eff_profile_bandwidth(eff_engine* e, int records, eff_bw_profile* out) {
+  if (int rc = check_engine(e)) return rc;
+  if (!out) return fail(EFF_EINVAL, "eff_profile_bandwidth: out is NULL");
+  const eff_config& c = e->cfg;
+  const int64_t n_flat = (int64_t)c.num_layers * c.num_experts;
+  if (records < 1 || records > n_flat) return fail(EFF_EINVAL, "records must be in [1, L*E]");
+  if (capturing(nullptr)) return fail(EFF_ECAPTURE, "eff_profile_bandwidth waits on the host");
+  drain_worker(e);
+  if (int rc = check_async_error(e)) return rc;
+  hipStream_t s = nullptr;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  uint8_t* dst = nullptr;
+  int rc = EFF_OK;
+  const int64_t stride = std::max<int64_t>(1, n_flat / records);
+  const int K = c.top_k, calls = (records + K - 1) / K;
+  const double host_bytes = (double)calls * K * e->R;
+  std::vector<uint16_t> x(c.hidden);
+  std::vector<float> y((size_t)K * c.hidden);
+  uint32_t lcg = 12345u;  // a fixed token: bf16 values in about [-2, 2)
+  for (auto& v : x) {
+    lcg = lcg * 1664525u + 1013904223u;
+    const float f = ((lcg >> 8) * (1.0f / 16777216.0f)) * 4.0f - 2.0f;
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    v = (uint16_t)(u >> 16);
+  }
+  auto gpu_pass = [&](int n, float* ms) -> hipError_t {
+    hipError_t err = hipEventRecord(ev[0], s);
+    if (err == hipSuccess) err = launch_bw_copy(e, 0, stride, n, dst, s);
+    if (err == hipSuccess) err = hipEventRecord(ev[1], s);
+    return err;
+  };
+  auto gpu_done = [&](float* ms) -> hipError_t {
+    hipError_t err = hipEventSynchronize(ev[1]);
+    if (err == hipSuccess) err = hipEventElapsedTime(ms, ev[0], ev[1]);
+    return err;
+  };
+  do {
+    if (hipStreamCreate(&s) != hipSuccess || hipEventCreate(&ev[0]) != hipSuccess ||
+        hipEventCreate(&ev[1]) != hipSuccess) {
+      rc = fail(EFF_EHIP, "eff_profile_bandwidth: stream or events");
+      break;
+    }
+    if (hipMalloc((void**)&dst, 2 * (size_t)e->R) != hipSuccess) {
+      rc = fail(EFF_ENOMEM, "eff_profile_bandwidth: scratch");
+      break;
+    }
+    float ms = 0.f;
+    // warm-up, then the link alone
+    if (gpu_pass(std::min(records, 4), &ms) != hipSuccess || gpu_done(&ms) != hipSuccess ||
+        gpu_pass(records, &ms) != hipSuccess || gpu_done(&ms) != hipSuccess) {
+      rc = fail(EFF_EHIP, "eff_profile_bandwidth: copy kernel");
+      break;
+    }
+    const double t_p = std::max(1e-9, ms * 1e-3);
+    // the host alone (one warm-up call)
+    host_profile_pass(e, 1, x.data(), y.data());
+    const double t_h = std::max(1e-9, host_profile_pass(e, calls, x.data(), y.data()));
+    // both at once: enough records on the link to cover the host pass
+    const int n2 = (int)std::min<double>(n_flat, std::max(1.0, std::round(records * t_h / t_p)));
+    if (gpu_pass(n2, &ms) != hipSuccess) {
+      rc = fail(EFF_EHIP, "eff_profile_bandwidth: copy kernel");
+      break;
+    }
+    const double t_h2 = std::max(1e-9, host_profile_pass(e, calls, x.data(), y.data()));
+    if (gpu_done(&ms) != hipSuccess) {
+      rc = fail(EFF_EHIP, "eff_profile_bandwidth: copy kernel");
+      break;
+    }
+    const double t_p2 = std::max(1e-9, ms * 1e-3);
+    out->pcie_alone = (double)records * e->R / t_p;
+    out->host_alone = host_bytes / t_h;
+    out->pcie_concurrent = (double)n2 * e->R / t_p2;
+    out->host_concurrent = host_bytes / t_h2;
+    out->frac_q16 = eff_frac_q16(out->pcie_concurrent, out->host_concurrent);
+    out->frac_q16_alone = eff_frac_q16(out->pcie_alone, out->host_alone);
+    out->record_bytes = e->R;
+    out->records = records;
+    out->pad = 0;
+  } while (false);
+  if (s) (void)hipStreamSynchronize(s);
+  if (dst) (void)hipFree(dst);
+  for (hipEvent_t v : ev)
+    if (v) (void)hipEventDestroy(v);
+  if (s) (void)hipStreamDestroy(s);
+  return rc;
 }
 
 static int issue_copies(eff_engine* e, int which, hipStream_t side) {

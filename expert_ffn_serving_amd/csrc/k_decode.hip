@@ -459,6 +459,20 @@ k_fetch_copy(const uint8_t* __restrict__ pool, uint8_t* __restrict__ arena, int6
   }
 }
 
+// The link rate of the in-kernel fetch path, for the bandwidth profile: n records (flat ids first,
+// first + stride, ... modulo the pool) copied from the pinned host pool with 16-byte loads, like
+// the fetch units of k_gateup, into two record-sized device buffers used in turn.
+__global__ void __launch_bounds__(256)
+k_bw_copy(const uint8_t* __restrict__ pool, int64_t R, int64_t n_flat, int64_t first, int64_t stride, int n,
+          uint8_t* __restrict__ dst) {
+  const int64_t per = R / 16, total = per * n;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per, c = i % per;
+    const int64_t flat = (first + r * stride) % n_flat;
+    reinterpret_cast<uint4*>(dst + (r & 1) * R)[c] = reinterpret_cast<const uint4*>(pool + flat * R)[c];
+  }
+}
+
 template <int FMT, int NT>
 hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, hipStream_t s) {
   const eff_config& c = e->cfg;
@@ -522,6 +536,13 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
     default: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 8>(e, x, y, units, s)
                         : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 8>(e, x, y, units, s);
   }
+}
+
+hipError_t launch_bw_copy(eff_engine* e, int64_t first, int64_t stride, int n, uint8_t* dst, hipStream_t s) {
+  const eff_config& c = e->cfg;
+  hipLaunchKernelGGL(k_bw_copy, dim3(1024), dim3(256), 0, s, e->pool_dev, e->R,
+                     (int64_t)c.num_layers * c.num_experts, first, stride, n, dst);
+  return hipGetLastError();
 }
 
 hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s) {

@@ -139,6 +139,42 @@ int eff_split_misses(eff_engine* e, int32_t* ids_inout, int32_t* cpu_ids, int32_
 int64_t eff_qstar(int64_t m, uint32_t f);
 int eff_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, int n, eff_stream_t stream);
 
+/* The fetch fraction from two measured rates ([FT-deep] §4 design pattern ②):
+ * f = B_P / B_H * 65536 as an integer, B_P the link's expert transfer rate and
+ * B_H the host's expert processing rate, in bytes/s.  The integer part, capped at
+ * 65536 (B_P >= B_H fetches every miss, [FT-blog] §六); B_P = 0 gives 0, B_H = 0
+ * (with B_P > 0) 65536.  Host only.  Returns 0xFFFFFFFF for a negative or NaN rate. */
+uint32_t eff_frac_q16(double pcie_bytes_per_s, double host_bytes_per_s);
+
+/* Bandwidth profile ([FT-deep] §4 ②: f comes from a profile of both paths, and
+ * preferably from running them at the same time, because the link transfer and the
+ * host computation compete for the host memory controller; [FT-blog] §六: measured
+ * on the target machine with the real tensor shapes).  Rates are bytes of expert
+ * records per second. */
+typedef struct eff_bw_profile {
+  double pcie_alone;       /* in-kernel record copy from the pinned pool into HBM, alone */
+  double host_alone;       /* the host executor over whole experts (1 token, K per call), alone */
+  double pcie_concurrent;  /* the same two, run at the same time */
+  double host_concurrent;
+  uint32_t frac_q16;       /* eff_frac_q16 of the concurrent rates (the one to use) */
+  uint32_t frac_q16_alone; /* eff_frac_q16 of the rates measured alone */
+  int64_t record_bytes;
+  int32_t records;         /* records moved by each path in each measurement */
+  int32_t pad;
+} eff_bw_profile;
+
+/* Measures the profile on this engine's pool, records spread over the whole pool
+ * (1 <= records <= L*E).  Synchronous: waits for the device and for the host-share
+ * worker first, uses the engine's host threads and a private stream and scratch
+ * buffer; the slot cache, its tables and the statistics are not touched.  Not
+ * during graph capture (EFF_ECAPTURE) and not while another call into the engine
+ * runs.  It does not change f: pass out->frac_q16 to eff_set_fetch_frac. */
+int eff_profile_bandwidth(eff_engine* e, int records, eff_bw_profile* out);
+
+/* Sets the engine's fetch fraction (0..65536, else EFF_EINVAL) for the calls
+ * enqueued after it.  A graph captured earlier keeps the value it was captured with. */
+int eff_set_fetch_frac(eff_engine* e, uint32_t frac_q16);
+
 /* copy ([FT-deep] §4 ③ copy_missing): waits on the host for `compute` to reach
  * the last split, then enqueues one hipMemcpyAsync per fetched record (host
  * pool -> slot) on `side` and makes `compute` wait for them.  Also issues the

@@ -39,6 +39,21 @@ def test_binding_argument_counts_match_header(eff):
         assert len(getattr(L, name).argtypes) == n, (name, n, len(getattr(L, name).argtypes))
 
 
+def test_frac_q16_matches_the_oracle(eff):
+    import random
+    from oracle.qstar import frac_q16
+    rnd = random.Random(3)
+    cases = [(0.4, 1.0), (0.7, 1.0), (1.0, 1.0), (2.0, 1.0), (0.0, 3.0), (3.0, 0.0), (1.0, 65536.0),
+             (1.0, 65537.0), (65535.0, 65536.0), (55e9, 330e9), (float("inf"), 1.0), (1.0, float("inf"))]
+    cases += [(rnd.uniform(0, 2e11), rnd.uniform(1, 4e11)) for _ in range(3000)]
+    # quotients just below and at integers, where a rounded division would land on the wrong side
+    cases += [(k * 3.0 - 1e-12, 3.0 * 65536) for k in range(1, 200)] + [(k * 7.0, 7.0 * 65536) for k in range(200)]
+    for bp, bh in cases:
+        assert eff.frac_q16(bp, bh) == frac_q16(bp, bh), (bp, bh)
+    for bad in ((-1.0, 1.0), (1.0, -2.0), (float("nan"), 1.0)):
+        assert eff.frac_q16(*bad) == 0xFFFFFFFF
+
+
 def test_host_only_entry_points(eff):
     assert eff.qstar(3, 32768) == 1 and eff.qstar(16, 45875) == 11 and eff.qstar(5, 0) == 0
     assert eff.qstar(-1, 5) == -1 and eff.qstar(4, 65537) == -1
