@@ -37,6 +37,12 @@ class OracleEngine:
         self.use_c = (H * I > 64 * 1024) if use_c is None else use_c
         self.nthreads = nthreads
 
+    def rebuild(self, S_new: int) -> None:
+        """Runtime cache rebuild ([FT-blog] §七 item 1): the slot contents go with the old cache."""
+        self.cache.rebuild(S_new)
+        self.S = S_new
+        self.arena = {}
+
     # ------------------------------------------------------------------ helpers
     def _copy(self, fetch) -> None:
         for flat, v in fetch:

@@ -30,6 +30,11 @@ Readings where the pages are silent (each listed in the design doc):
   the layer whose expert compute may still be running keeps its slots).
 * q' = min(q*, number of victims); the i-th ranked miss takes the i-th victim.
 * A speculative call fetches only (no host share) and leaves recency alone.
+* A runtime rebuild to S' slots ([FT-blog] §七 item 1: the GPU expert cache is
+  repartitioned for a new budget at a safe point, without touching the host pool;
+  since the pool is the source of truth, losing the cache only costs speed) starts
+  from an empty cache of S' slots.  The step counter, last_real and the expert
+  recency are statistics of the routing, not of the cache, and carry over.
 """
 from __future__ import annotations
 
@@ -173,6 +178,19 @@ class SlotCache:
         return copies
 
     # ------------------------------------------------------------------ checks
+    # ------------------------------------------------------------------ rebuild
+    def rebuild(self, S_new: int) -> None:
+        """The cache rebuilt with S_new slots: every slot empty, nothing resident; step,
+        last_real and recency kept.  Only at a safe point: no ensure waiting for its split."""
+        if S_new < 0:
+            raise ValueError("S_new >= 0 required")
+        if self.pending is not None:
+            raise RuntimeError("rebuild with an ensure pending its split")
+        self.S = S_new
+        self.table = [-1] * (self.L * self.E)
+        self.owner = [-1] * S_new
+        self.usage = [-1] * S_new
+
     def check_bijection(self) -> None:
         for v, o in enumerate(self.owner):
             if o >= 0 and self.table[o] != v:

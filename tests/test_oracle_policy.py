@@ -174,3 +174,53 @@ def test_prefill_moves_expert_out_of_other_slot():
     if old != E + 2:
         assert c.owner[old] == -1 and c.usage[old] == -1
     c.check_bijection()
+
+
+# ---------------------------------------------------------------------- runtime rebuild
+@pytest.mark.parametrize("S,S2", [(3, 5), (5, 2), (4, 0), (0, 3), (2, 9)])
+def test_rebuild_then_textbook_lru(S, S2):
+    """After a rebuild to S2 slots ([FT-blog] §七 item 1) the cache starts empty: with f = 65536 and
+    one id per call the misses from there on are an independent move-to-front list of capacity S2
+    started empty, whatever the cache held before."""
+    rng = random.Random(10 * S + S2)
+    L, E = 2, 8
+    c = SlotCache(L, E, S, 65536)
+    before = []
+    for _ in range(150):
+        l, e = rng.randrange(L), rng.randrange(E)
+        c.ensure_split(l, [e])
+        before.append(l * E + e)
+    c.rebuild(S2)
+    assert c.table == [-1] * (L * E) and c.owner == [-1] * S2 and c.usage == [-1] * S2
+    stream, got = [], []
+    for _ in range(300):
+        l, e = rng.randrange(L), rng.randrange(E)
+        r = c.ensure_split(l, [e])
+        stream.append(l * E + e)
+        got.append(r.m == 1)
+        c.check_bijection()
+        assert all(0 <= v < S2 for _, v in r.fetch)
+    assert got == mtf_lru_misses(stream, S2)
+
+
+def test_rebuild_keeps_clock_and_recency_and_refuses_a_pending_ensure():
+    rng = random.Random(5)
+    L, E, K = 2, 8, 3
+    c = SlotCache(L, E, 6, 26214)
+    for _ in range(40):
+        c.ensure_split(rng.randrange(L), rng.sample(range(E), K))
+    step, last, rec = c.step, c.last_real, list(c.recency)
+    c.rebuild(4)
+    assert (c.step, c.last_real, c.recency) == (step, last, rec)
+    # the first call after the rebuild: every unique id misses, and the q* misses ranked by the
+    # recency carried over are the ones fetched
+    ids = [1, 4, 6]
+    r = c.ensure_split(0, ids)
+    assert r.m == 3 and r.q == qstar_rule(3, 26214)
+    order = sorted(ids, key=lambda e: (-rec[e], e))
+    assert [f for f, _ in r.fetch] == order[:r.q]
+    c.ensure(1, [2])
+    with pytest.raises(RuntimeError):
+        c.rebuild(8)
+    with pytest.raises(ValueError):
+        SlotCache(L, E, 2, 65536).rebuild(-1)
