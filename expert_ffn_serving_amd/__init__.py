@@ -26,6 +26,7 @@ CFG_SYNC_HOST = 2
 T_DECODE_GATEUP, T_DECODE_DOWN, T_PREFILL_GATEUP, T_PREFILL_DOWN = 0, 1, 2, 3
 
 EFF_OK, EFF_EINVAL, EFF_ENOMEM, EFF_EHIP, EFF_ECAPTURE, EFF_ESTATE, EFF_EDEVICE = 0, -1, -2, -3, -4, -5, -6
+EFF_EREJECTED = -7
 
 
 class EffError(RuntimeError):
@@ -78,6 +79,7 @@ def lib():
             "eff_frac_q16": (U32, [ctypes.c_double, ctypes.c_double]),
             "eff_profile_bandwidth": (I32, [VP, I32, VP]),
             "eff_set_fetch_frac": (I32, [VP, U32]),
+            "eff_rebuild_cache": (I32, [VP, I32, ctypes.c_uint64]),
             "eff_copy_missing": (I32, [VP, VP, VP]),
             "eff_expert_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP, VP]),
             "eff_host_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP]),
@@ -303,6 +305,12 @@ class Engine:
     def set_fetch_frac(self, frac_q16: int):
         _check(lib().eff_set_fetch_frac(self.h, frac_q16))
         self.cfg.fetch_frac_q16 = frac_q16
+
+    def rebuild_cache(self, num_slots: int, max_arena_bytes: int = 0):
+        """eff_rebuild_cache: the slot cache rebuilt with num_slots slots (EffError with code
+        EFF_EREJECTED, and the engine unchanged, when the request does not fit)."""
+        _check(lib().eff_rebuild_cache(self.h, num_slots, max_arena_bytes))
+        self.cfg.num_slots = num_slots
 
     def slot_ptr(self, slot: int) -> int:
         out = ctypes.c_void_p()

@@ -666,6 +666,62 @@ int eff_profile_bandwidth(eff_engine* e, int records, eff_bw_profile* out) {
   return rc;
 }
 
+int eff_rebuild_cache(eff_engine* e, int num_slots, uint64_t max_arena_bytes) {
+  if (int rc = check_engine(e)) return rc;
+  if (capturing(nullptr)) return fail(EFF_ECAPTURE, "eff_rebuild_cache waits on the host");
+  const eff_config& c = e->cfg;
+  const int64_t L = c.num_layers, E = c.num_experts;
+  // geometry and budget, before anything else
+  if (num_slots < 0 || num_slots > kMaxSlots) return fail(EFF_EREJECTED, "num_slots must be in [0, 16384]");
+  const uint64_t arena = (uint64_t)num_slots * (uint64_t)e->R;
+  if (max_arena_bytes > 0 && arena > max_arena_bytes)
+    return fail(EFF_EREJECTED, "the slot arena does not fit the byte budget");
+  // a safe point: no call half done
+  if (e->pending_host) return fail(EFF_EREJECTED, "an ensure is waiting for its split");
+  if (e->real_split_pending || e->spec_split_pending)
+    return fail(EFF_EREJECTED, "a split's copies have not been issued (eff_copy_missing)");
+  if (e->pf_streamed[0] || e->pf_streamed[1])
+    return fail(EFF_EREJECTED, "a streamed prefill layer has not been computed");
+  drain_worker(e);
+  if (int rc = check_async_error(e)) return rc;
+  // the new buffers first; on any failure only they are released
+  uint8_t* arena_new = nullptr;
+  int32_t* owner_new = nullptr;
+  int64_t* usage_new = nullptr;
+  auto reject = [&](const std::string& why) {
+    (void)hipGetLastError();
+    if (arena_new) (void)hipFree(arena_new);
+    if (owner_new) (void)hipFree(owner_new);
+    if (usage_new) (void)hipFree(usage_new);
+    return fail(EFF_EREJECTED, why);
+  };
+  const size_t S1 = (size_t)std::max(1, num_slots);
+  if (arena > 0 && hipMalloc((void**)&arena_new, arena) != hipSuccess)
+    return reject("the slot arena cannot be allocated");
+  if (hipMalloc((void**)&owner_new, S1 * sizeof(int32_t)) != hipSuccess ||
+      hipMalloc((void**)&usage_new, S1 * sizeof(int64_t)) != hipSuccess)
+    return reject("the slot tables cannot be allocated");
+  if (hipMemset(owner_new, 0xFF, S1 * sizeof(int32_t)) != hipSuccess ||
+      hipMemset(usage_new, 0xFF, S1 * sizeof(int64_t)) != hipSuccess)
+    return reject("clearing the new slot tables failed");
+  if (num_slots > c.num_slots && split_kernel_setup(num_slots, (int)E) != hipSuccess)
+    return reject("the victim sort cannot take that many slots");
+  // commit: nothing resident, the old cache released, the clock and recency kept
+  if (hipMemset(e->d_table, 0xFF, (size_t)(L * E) * sizeof(int32_t)) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess)
+    return reject("clearing the table failed");
+  if (e->d_arena) (void)hipFree(e->d_arena);
+  (void)hipFree(e->d_owner);
+  (void)hipFree(e->d_usage);
+  e->d_arena = arena_new;
+  e->d_owner = owner_new;
+  e->d_usage = usage_new;
+  e->cfg.num_slots = num_slots;
+  std::memset(e->h_fetch, 0, 2 * sizeof(FetchList));
+  EFF_HIP_TRY(hipMemset(e->d_fetch, 0, 2 * sizeof(FetchList)));  // no list names an old slot
+  return EFF_OK;
+}
+
 static int issue_copies(eff_engine* e, int which, hipStream_t side) {
   const FetchList& fl = e->h_fetch[which];
   for (int i = 0; i < fl.count; ++i) {

@@ -52,7 +52,8 @@ enum {
   EFF_EHIP = -3,     /* a HIP runtime call failed (message has hipGetErrorString) */
   EFF_ECAPTURE = -4, /* the call must wait on the host and the stream is being captured */
   EFF_ESTATE = -5,   /* call out of order (e.g. split without a pending ensure) */
-  EFF_EDEVICE = -6   /* a kernel reported bad input (e.g. an expert id >= E); see message */
+  EFF_EDEVICE = -6,  /* a kernel reported bad input (e.g. an expert id >= E); see message */
+  EFF_EREJECTED = -7 /* a rebuild was validated and refused; the engine is unchanged and usable */
 };
 
 enum { EFF_WFMT_INT4_G32_BF16 = 0, EFF_WFMT_NVFP4_G16_E4M3 = 1 };
@@ -174,6 +175,23 @@ int eff_profile_bandwidth(eff_engine* e, int records, eff_bw_profile* out);
 /* Sets the engine's fetch fraction (0..65536, else EFF_EINVAL) for the calls
  * enqueued after it.  A graph captured earlier keeps the value it was captured with. */
 int eff_set_fetch_frac(eff_engine* e, uint32_t frac_q16);
+
+/* Runtime cache rebuild ([FT-blog] §七 item 1; [FT-deep] §4 design pattern ⑦): the
+ * slot cache is rebuilt with num_slots slots for a new HBM budget, without touching
+ * the host pool.  Everything is checked, and the new slot arena, owner and usage
+ * arrays are allocated, before anything is freed; a request that does not fit returns
+ * EFF_EREJECTED and leaves the engine exactly as it was:
+ *   - num_slots outside [0, 16384];
+ *   - max_arena_bytes > 0 and num_slots * record bytes > max_arena_bytes;
+ *   - not at a safe point: an ensure waiting for its split, a split whose copies
+ *     eff_copy_missing has not issued, or a prefill layer streamed but not computed;
+ *   - the new buffers cannot be allocated (the old cache is still held then).
+ * On success the rebuilt cache is empty (every expert misses until fetched again);
+ * the step clock, last_real and the expert recency carry over, and results are
+ * unchanged because the pool is the source of truth.  Synchronous: waits for the
+ * device and the host-share worker.  Not during capture (EFF_ECAPTURE).  Graphs
+ * captured before a rebuild address the old arena and must not be replayed after it. */
+int eff_rebuild_cache(eff_engine* e, int num_slots, uint64_t max_arena_bytes);
 
 /* copy ([FT-deep] §4 ③ copy_missing): waits on the host for `compute` to reach
  * the last split, then enqueues one hipMemcpyAsync per fetched record (host
