@@ -266,7 +266,7 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
                           const float* w, int T, uint16_t* out, const int32_t* slot_of_expert,
                           int slot_base, bool combine, hipStream_t s);
 hipError_t split_kernel_setup(int S, int E);
-hipError_t decode_kernels_setup(int fmt, int maxB, int I);
+hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I);
 int decode_nt(int maxB);
 int64_t qstar_host(int64_t m, int64_t f);
 // host executor

@@ -167,7 +167,7 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
   std::memset(e->h_fetch, 0, 2 * sizeof(FetchList));
   EFF_HIP_TRY(split_kernel_setup((int)S, (int)E));
-  EFF_HIP_TRY(decode_kernels_setup(c.wformat, (int)B, (int)I));
+  EFF_HIP_TRY(decode_kernels_setup(c.wformat, (int)B, (int)H, (int)I));
   EFF_HIP_TRY(hipDeviceSynchronize());
   return EFF_OK;
 }

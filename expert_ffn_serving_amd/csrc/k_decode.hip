@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(kWG)
 k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
          const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H,
          int I, int K, int maxB, uint16_t* __restrict__ a16, float2* __restrict__ ag) {
-  constexpr int UNR = NT >= 8 ? 2 : (NT == 4 ? 4 : 8);  // tiles in flight per wave (x takes 4*NT VGPRs each)
+  extern __shared__ uint4 s_x[];  // NT > 1: [NT][H/8], the token rows of the current chunk
   __shared__ float s_red[4][2][16][NT];
   const int NS = I / 16, KB = H / 32;
   const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
@@ -183,40 +183,83 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   const uint8_t* up = gp + pay;
   const uint8_t* gs = rec + 3 * pay + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
   const uint8_t* us = gs + sca;
-  const uint16_t* xq = x + q * 8;
+  const int H8 = H / 8;
   for (int c0 = 0; c0 < cnt; c0 += NT) {
     const int nt = min(NT, cnt - c0);
-    const uint16_t* xt[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) xt[j] = xq + (int64_t)((j < nt) ? un->entry[c0 + j] / K : 0) * H;
     float acc[2][NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[0][j] = acc[1][j] = 0.f;
-    int kb = wave;
-    for (; kb + 4 * (UNR - 1) < KB; kb += 4 * UNR) {  // full rounds: every load first
+    if constexpr (NT == 1) {
+      // one token: its activations ride with the weight loads, straight from global memory (an
+      // LDS stage and its barrier cost more than they free at this width)
+      constexpr int UNR = 8;  // tiles in flight per wave
+      const uint16_t* xt = x + q * 8 + (int64_t)(un->entry[c0] / K) * H;
+      int kb = wave;
+      for (; kb + 4 * (UNR - 1) < KB; kb += 4 * UNR) {  // full rounds: every load first
+        uint32_t wg[UNR], wu[UNR], rg[UNR], ru[UNR];
+        uint4 xv[UNR][1];
+#pragma unroll
+        for (int z = 0; z < UNR; ++z) {
+          const int k = kb + 4 * z;
+          wg[z] = *reinterpret_cast<const uint32_t*>(gp + k * 256);
+          wu[z] = *reinterpret_cast<const uint32_t*>(up + k * 256);
+          rg[z] = load_scale_raw<FMT>(gs + k * 32);
+          ru[z] = load_scale_raw<FMT>(us + k * 32);
+          xv[z][0] = *reinterpret_cast<const uint4*>(xt + k * 32);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the round is in flight before any use
+#pragma unroll
+        for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], acc);
+      }
+      for (; kb < KB; kb += 4) {  // tail
+        const uint4 xv[1] = {*reinterpret_cast<const uint4*>(xt + kb * 32)};
+        gateup_tile<FMT, NT>(*reinterpret_cast<const uint32_t*>(gp + kb * 256),
+                             *reinterpret_cast<const uint32_t*>(up + kb * 256), load_scale_raw<FMT>(gs + kb * 32),
+                             load_scale_raw<FMT>(us + kb * 32), xv, acc);
+      }
+    } else {
+      // several tokens: the first round of weight loads, then the chunk's token rows into LDS (the
+      // weights do not wait for them); the registers then hold weights only
+      constexpr int UNR = NT >= 4 ? 4 : 8;  // tiles in flight per wave
       uint32_t wg[UNR], wu[UNR], rg[UNR], ru[UNR];
-      uint4 xv[UNR][NT];
+      int kb = wave;
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
         const int k = kb + 4 * z;
-        wg[z] = *reinterpret_cast<const uint32_t*>(gp + k * 256);
-        wu[z] = *reinterpret_cast<const uint32_t*>(up + k * 256);
-        rg[z] = load_scale_raw<FMT>(gs + k * 32);
-        ru[z] = load_scale_raw<FMT>(us + k * 32);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) xv[z][j] = *reinterpret_cast<const uint4*>(xt[j] + k * 32);
+        const bool in = k < KB;
+        wg[z] = in ? *reinterpret_cast<const uint32_t*>(gp + k * 256) : 0u;
+        wu[z] = in ? *reinterpret_cast<const uint32_t*>(up + k * 256) : 0u;
+        rg[z] = in ? load_scale_raw<FMT>(gs + k * 32) : 0u;
+        ru[z] = in ? load_scale_raw<FMT>(us + k * 32) : 0u;
       }
-      __builtin_amdgcn_sched_barrier(0);  // every load of the round is in flight before any use
+      for (int i = tid; i < nt * H8; i += kWG) {
+        const int j = i / H8, g = i % H8;
+        s_x[i] = *reinterpret_cast<const uint4*>(x + (int64_t)(un->entry[c0 + j] / K) * H + g * 8);
+      }
+      __syncthreads();
+      for (;;) {
 #pragma unroll
-      for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], acc);
-    }
-    for (; kb < KB; kb += 4) {  // tail
-      uint4 xv[NT];
+        for (int z = 0; z < UNR; ++z) {
+          const int k = kb + 4 * z;
+          if (k < KB) {  // uniform per wave
+            uint4 xv[NT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) xv[j] = *reinterpret_cast<const uint4*>(xt[j] + kb * 32);
-      gateup_tile<FMT, NT>(*reinterpret_cast<const uint32_t*>(gp + kb * 256),
-                           *reinterpret_cast<const uint32_t*>(up + kb * 256), load_scale_raw<FMT>(gs + kb * 32),
-                           load_scale_raw<FMT>(us + kb * 32), xv, acc);
+            for (int j = 0; j < NT; ++j) xv[j] = j < nt ? s_x[j * H8 + k * 4 + q] : make_uint4(0, 0, 0, 0);
+            gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv, acc);
+          }
+        }
+        kb += 4 * UNR;
+        if (kb >= KB) break;
+#pragma unroll
+        for (int z = 0; z < UNR; ++z) {  // the next round
+          const int k = kb + 4 * z;
+          const bool in = k < KB;
+          wg[z] = in ? *reinterpret_cast<const uint32_t*>(gp + k * 256) : 0u;
+          wu[z] = in ? *reinterpret_cast<const uint32_t*>(up + k * 256) : 0u;
+          rg[z] = in ? load_scale_raw<FMT>(gs + k * 32) : 0u;
+          ru[z] = in ? load_scale_raw<FMT>(us + k * 32) : 0u;
+        }
+      }
     }
     // reduce over q (lanes r, r+16, r+32, r+48), then over the 4 waves in order
 #pragma unroll
@@ -481,7 +524,8 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, h
   // d_a holds 4 bytes per activation: the fp16 values, then one (scale, sum) pair per 8 of them
   uint16_t* a16 = reinterpret_cast<uint16_t*>(e->d_a);
   float2* ag = reinterpret_cast<float2*>(a16 + (size_t)e->maxU * c.max_tokens * I);
-  hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(units * (I / 16)), dim3(kWG), 0, s, e->d_arena, e->pool_dev, e->R,
+  hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(units * (I / 16)), dim3(kWG), (size_t)(NT > 1 ? NT * H * 2 : 0), s, e->d_arena,
+                     e->pool_dev, e->R,
                      e->d_ts, e->d_plan, x, H, I, c.top_k, c.max_tokens, a16, ag);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -499,14 +543,18 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, h
 
 int decode_nt(int maxB) { return maxB >= 8 ? 8 : maxB >= 4 ? 4 : maxB >= 2 ? 2 : 1; }
 
-hipError_t decode_kernels_setup(int fmt, int maxB, int I) {
-  // allow N * I * 3 bytes of dynamic LDS for the down kernel of every token width N a call can take
+hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
+  // allow N * H * 2 bytes of dynamic LDS for the gate/up kernel and N * I * 3 for the down kernel,
+  // for every token width N a call can take
   const int NT = decode_nt(maxB);
   hipError_t err = hipSuccess;
 #define SETUP(F, N)                                                                                    \
   if (fmt == F && N <= NT && err == hipSuccess)                                                         \
     err = hipFuncSetAttribute((const void*)k_down<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize,    \
-                              N * (I / 8) * 24);
+                              N * (I / 8) * 24);                                                        \
+  if (fmt == F && N <= NT && err == hipSuccess)                                                         \
+    err = hipFuncSetAttribute((const void*)k_gateup<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize,  \
+                              N * H * 2);
   SETUP(EFF_WFMT_INT4_G32_BF16, 1) SETUP(EFF_WFMT_INT4_G32_BF16, 2) SETUP(EFF_WFMT_INT4_G32_BF16, 4)
   SETUP(EFF_WFMT_INT4_G32_BF16, 8) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 1) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 2)
   SETUP(EFF_WFMT_NVFP4_G16_E4M3, 4) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 8)
