@@ -351,10 +351,11 @@ __device__ inline void down_tile(uint32_t d, uint32_t rd, const uint4* s_a4, con
   }
 }
 
-// grid: maxU * (H/16) workgroups, one per (plan unit, 16-row slice of H).  The unit's SwiGLU
-// activations, already fp16 from k_gateup, are copied into LDS with their per-group scales and
-// sums before the sweep.
-template <int FMT, int NT>
+// grid: maxU * (H/(16*RS)) workgroups, one per (plan unit, RS 16-row slices of H); 4/RS waves
+// share a slice.  The unit's SwiGLU activations, already fp16 from k_gateup, are copied into LDS
+// with their per-group scales and sums before the sweep, once for the RS slices.
+constexpr int kDownRS = 2;  // measured: 2 beats 1 and 4 at H = 4096, I = 2048
+template <int FMT, int NT, int RS>
 __global__ void __launch_bounds__(kWG)
 k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
        const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ a16,
@@ -362,14 +363,17 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   extern __shared__ uint4 s_a4[];            // [NT][I/8] groups of 8 fp16, then [NT][I/8] float2
   __shared__ float s_red[4][16][NT];
   constexpr int UNR = NT >= 4 ? 4 : 8;  // tiles in flight per wave
-  const int NS = H / 16, KB = I / 32, I8 = I / 8;
-  const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
+  constexpr int NW = 4 / RS;            // waves per slice
+  static_assert(RS == 1 || RS == 2 || RS == 4, "1, 2 or 4 slices per workgroup");
+  const int NG = H / (16 * RS), KB = I / 32, I8 = I / 8;
+  const int u = blockIdx.x / NG, sg = blockIdx.x % NG;
   const DecodeUnit* un = &plan->unit[u];
   const int cnt = un->count;
   if (cnt <= 0) return;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ss = wave % RS, sw = wave / RS, sl = sg * RS + ss;  // this wave's slice, its place in it
   // a record installed by this call was copied whole by k_gateup, the previous kernel on the stream
   const uint8_t* rec = arena + (int64_t)un->slot * R;
   float2* s_ag = reinterpret_cast<float2*>(s_a4 + NT * I8);
@@ -382,7 +386,7 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
     uint32_t wd[UNR], rd[UNR];
 #pragma unroll
     for (int z = 0; z < UNR; ++z) {
-      const int k = wave + 4 * z;
+      const int k = sw + NW * z;
       wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
       rd[z] = k < KB ? load_scale_raw<FMT>(ds + k * 32) : 0u;
     }
@@ -399,17 +403,17 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
     for (int j = 0; j < NT; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int z = 0; z < UNR; ++z)
-      if (wave + 4 * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_ag, wave + 4 * z, q, nt, I8, acc);
-    for (int kb0 = wave + 4 * UNR; kb0 < KB; kb0 += 4 * UNR) {
+      if (sw + NW * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_ag, sw + NW * z, q, nt, I8, acc);
+    for (int kb0 = sw + NW * UNR; kb0 < KB; kb0 += NW * UNR) {
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
-        const int k = kb0 + 4 * z;
+        const int k = kb0 + NW * z;
         wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
         rd[z] = k < KB ? load_scale_raw<FMT>(ds + k * 32) : 0u;
       }
 #pragma unroll
       for (int z = 0; z < UNR; ++z)
-        if (kb0 + 4 * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_ag, kb0 + 4 * z, q, nt, I8, acc);
+        if (kb0 + NW * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_ag, kb0 + NW * z, q, nt, I8, acc);
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -423,14 +427,15 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
       for (int j = 0; j < NT; ++j) s_red[wave][r][j] = acc[j];
     }
     __syncthreads();
-    if (tid < 16 * nt) {
-      const int row = tid / nt, j = tid % nt;
-      float v = s_red[0][row][j] + s_red[1][row][j];
-      v += s_red[2][row][j];
-      v += s_red[3][row][j];
+    for (int idx = tid; idx < 16 * RS * nt; idx += kWG) {
+      const int j = idx % nt, rr = idx / nt, s2 = rr / 16, row = rr % 16;
+      // the slice's waves in order (RS = 1: waves 0, 1, 2, 3)
+      float v = s_red[s2][row][j];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) v += s_red[w2 * RS + s2][row][j];
       if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= ts[(int64_t)un->flat * 3 + 2];
       const int p = un->entry[c0 + j];
-      y[(int64_t)p * H + sl * 16 + row] = v;
+      y[(int64_t)p * H + (sg * RS + s2) * 16 + row] = v;
     }
     __syncthreads();
   }
@@ -532,7 +537,13 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, h
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
   size_t lds = (size_t)NT * (I / 8) * (sizeof(uint4) + sizeof(float2));
-  hipLaunchKernelGGL((k_down<FMT, NT>), dim3(units * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
+  // kDownRS slices per workgroup for long down rows (I >= 1024: the activation stage is then shared
+  // by enough tiles per wave); short rows keep one slice and four waves per slice
+  if (I >= 1024 && H % (16 * kDownRS) == 0)
+    hipLaunchKernelGGL((k_down<FMT, NT, kDownRS>), dim3(units * (H / (16 * kDownRS))), dim3(kWG), lds, s, e->d_arena,
+                       e->pool_dev, e->R, e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
+  else
+    hipLaunchKernelGGL((k_down<FMT, NT, 1>), dim3(units * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
                      e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
   err = hipGetLastError();
   timing_mark(e, ts, 3, s);
@@ -550,8 +561,11 @@ hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
   hipError_t err = hipSuccess;
 #define SETUP(F, N)                                                                                    \
   if (fmt == F && N <= NT && err == hipSuccess)                                                         \
-    err = hipFuncSetAttribute((const void*)k_down<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize,    \
+    err = hipFuncSetAttribute((const void*)k_down<F, N, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, \
                               N * (I / 8) * 24);                                                        \
+  if (fmt == F && N <= NT && err == hipSuccess)                                                         \
+    err = hipFuncSetAttribute((const void*)k_down<F, N, kDownRS>,                                       \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, N * (I / 8) * 24);            \
   if (fmt == F && N <= NT && err == hipSuccess)                                                         \
     err = hipFuncSetAttribute((const void*)k_gateup<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize,  \
                               N * H * 2);
