@@ -647,47 +647,52 @@ __device__ inline void topk_row(const float* row, int E, int K, int32_t* ids, fl
 // in LDS.  flat id of a unit: base + lds_id[p] when ids are known, else owner[slot].  lds_hit
 // (may be null): the slot the ensure found; a unit whose slot was installed by this call
 // (hit < 0) is marked fetch.  scratch: 2*kMaxEntries int32 of LDS.
+// The decode plan of a call of at most 64 entries, by wave 0 alone (no barrier): each lane
+// learns which lanes share its slot and which hold a smaller slot from one uniform readlane sweep
+// (registers only; no LDS round trips).  Call with tid < 64.
+__device__ void plan_wave0(const int32_t* lds_slot, const int32_t* lds_id, const int32_t* lds_hit, int64_t base,
+                           const int32_t* __restrict__ owner, int n, int S, int maxU, int maxB, DecodePlan* plan) {
+  const int tid = threadIdx.x;
+  int v = -1;
+  if (tid < n) {
+    const int sl = lds_slot[tid];
+    v = (sl >= 0 && sl < S) ? sl : -1;  // slots outside the arena are never read
+  }
+  uint64_t same = 0, less = 0;
+  for (int q = 0; q < n; ++q) {
+    const int vq = __builtin_amdgcn_readlane(v, q);
+    same |= (uint64_t)(vq == v) << q;
+    less |= (uint64_t)(vq < v) << q;
+  }
+  const bool first = v >= 0 && (same & ((1ull << tid) - 1)) == 0;
+  const uint64_t fm = __ballot(first);
+  const int rank = __popcll(less & fm);  // distinct valid slots below v: units in ascending slot order
+  const int nu = min(__popcll(fm), maxU);
+  if (first && rank < maxU) {  // more distinct slots than a layer has experts: not computed
+    DecodeUnit& un = plan->unit[rank];
+    int cnt = 0;
+    for (uint64_t m = same; m && cnt < maxB; m &= m - 1)  // a slot appears at most once per token
+      un.entry[cnt++] = __builtin_ctzll(m);
+    un.slot = v;
+    un.count = cnt;
+    un.flat = lds_id ? (int32_t)(base + lds_id[tid]) : owner[v];
+    un.fetch = (lds_hit && lds_hit[tid] < 0) ? 1 : 0;
+  }
+  for (int u = nu + tid; u < maxU; u += 64) {
+    plan->unit[u].count = 0;
+    plan->unit[u].slot = 0;
+    plan->unit[u].flat = 0;
+    plan->unit[u].fetch = 0;
+  }
+  if (tid == 0) plan->nu = nu;
+}
+
 __device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, const int32_t* lds_hit, int64_t base,
                           const int32_t* __restrict__ owner, int n, int S, int maxU, int maxB, DecodePlan* plan,
                           int32_t* scratch) {
   const int tid = threadIdx.x;
   if (n <= 64) {
-    // one wave, lane p = entry p: each lane learns which lanes share its slot and which hold a
-    // smaller slot from one uniform readlane sweep (registers only; no LDS round trips)
-    if (tid < 64) {
-      int v = -1;
-      if (tid < n) {
-        const int sl = lds_slot[tid];
-        v = (sl >= 0 && sl < S) ? sl : -1;  // slots outside the arena are never read
-      }
-      uint64_t same = 0, less = 0;
-      for (int q = 0; q < n; ++q) {
-        const int vq = __builtin_amdgcn_readlane(v, q);
-        same |= (uint64_t)(vq == v) << q;
-        less |= (uint64_t)(vq < v) << q;
-      }
-      const bool first = v >= 0 && (same & ((1ull << tid) - 1)) == 0;
-      const uint64_t fm = __ballot(first);
-      const int rank = __popcll(less & fm);  // distinct valid slots below v: units in ascending slot order
-      const int nu = min(__popcll(fm), maxU);
-      if (first && rank < maxU) {  // more distinct slots than a layer has experts: not computed
-        DecodeUnit& un = plan->unit[rank];
-        int cnt = 0;
-        for (uint64_t m = same; m && cnt < maxB; m &= m - 1)  // a slot appears at most once per token
-          un.entry[cnt++] = __builtin_ctzll(m);
-        un.slot = v;
-        un.count = cnt;
-        un.flat = lds_id ? (int32_t)(base + lds_id[tid]) : owner[v];
-        un.fetch = (lds_hit && lds_hit[tid] < 0) ? 1 : 0;
-      }
-      for (int u = nu + tid; u < maxU; u += 64) {
-        plan->unit[u].count = 0;
-        plan->unit[u].slot = 0;
-        plan->unit[u].flat = 0;
-        plan->unit[u].fetch = 0;
-      }
-      if (tid == 0) plan->nu = nu;
-    }
+    if (tid < 64) plan_wave0(lds_slot, lds_id, lds_hit, base, owner, n, S, maxU, maxB, plan);
     lds_sync();
     return;
   }
@@ -778,6 +783,24 @@ k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, cons
 // in host-mapped memory.  Last, wave 0 fences at system scope, numbers the call (seq = ++*seq_ctr,
 // device memory) and publishes its word (seq, layer, B, host entries) at call_ring[seq % kCallRing];
 // a call with no host entries also sets *host_done = seq itself (nothing for the host to add).
+// Wave 0, last: the call word after a system-scope fence (which covers wave 0's host ids and x,
+// whose stores waves 1-4 completed before a barrier that wave 0 passed since).
+__device__ inline void publish_call(uint64_t* call_ring, uint64_t* host_done, uint64_t* seq_ctr, int layer, int B,
+                                    int nhost) {
+  if (!call_ring) return;
+  __threadfence_system();
+  if (threadIdx.x == 0) {
+    // this call's number, then the word; relaxed stores after the release fence (a release store
+    // would write back the L2 again)
+    const uint64_t seq = *seq_ctr + 1;
+    *seq_ctr = seq;
+    const uint64_t word = ((seq & 0xFFFFFFFFull) << 32) | ((uint64_t)layer << kCallLayerShift) |
+                          ((uint64_t)(B - 1) << kCallBShift) | (uint64_t)nhost;
+    __hip_atomic_store(call_ring + seq % kCallRing, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (nhost == 0) __hip_atomic_store(host_done, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 __global__ void __launch_bounds__(kThreads)
 k_control(CacheState c, const float* __restrict__ logits, int B, int K, int layer, int32_t* __restrict__ ids,
           float* __restrict__ w, int32_t* __restrict__ slots, int32_t* __restrict__ cpu, int32_t* __restrict__ counts,
@@ -805,6 +828,23 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
     topk_row(logits + (int64_t)t * c.E, c.E, K, ids + (int64_t)t * K, w + (int64_t)t * K, C.id + t * K);
   lds_sync();
   ensure_body(c, layer, n, 0, C);
+  if (n <= 64 && !spec_ids && qstar_dev(C.nm, c.f) == 0) {
+    // nothing to fetch (q* = 0, uniform): no victims are needed, so wave 0 finishes the call alone,
+    // without a block barrier per phase.  One barrier orders the x copies before wave 0's fence.
+    if (tid >= 64 && tid < kKeyT0 && call_ring) __builtin_amdgcn_s_waitcnt(0);  // x_host stores complete
+    lds_sync();
+    if (tid >= 64) return;
+    if (tid < n) C.slot[tid] = C.hit[tid];  // the -1 partition: hits keep their slot
+    if (tid == 0) C.qq = 0;
+    // the lanes of this wave read each other's entries from LDS next (in order within a wave)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    plan_wave0(C.slot, C.id, C.hit, (int64_t)layer * c.E, c.owner, n, c.S, maxU, maxB, plan);
+    commit_body(c, C, true, slots, cpu, cpu_host, counts);
+    int nhost = __popcll(__ballot(tid < n && C.slot[tid] < 0 && C.id[tid] >= 0));
+    publish_call(call_ring, host_done, seq_ctr, layer, B, nhost);
+    return;
+  }
   split_body(c, C, s_key, true);
   if (tid >= 64 && tid < kKeyT0 && call_ring) __builtin_amdgcn_s_waitcnt(0);  // x_host stores complete (above)
   plan_body(C.slot, C.id, C.hit, (int64_t)layer * c.E, c.owner, n, c.S, maxU, maxB, plan,
@@ -824,23 +864,7 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
     split_body(c, C, s_key);
     commit_body(c, C, true, spec_slots, nullptr, nullptr, counts + 3);
   }
-  if (tid < 64) {
-    // the call word after a system-scope fence (which covers wave 0's host ids and x, whose
-    // stores waves 1-4 completed before the plan's barrier)
-    if (call_ring) {
-      __threadfence_system();
-      if (tid == 0) {
-        // this call's number, then the word; relaxed stores after the release fence (a release store
-        // would write back the L2 again)
-        const uint64_t seq = *seq_ctr + 1;
-        *seq_ctr = seq;
-        const uint64_t word = ((seq & 0xFFFFFFFFull) << 32) | ((uint64_t)layer << kCallLayerShift) |
-                              ((uint64_t)(B - 1) << kCallBShift) | (uint64_t)nhost;
-        __hip_atomic_store(call_ring + seq % kCallRing, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        if (nhost == 0) __hip_atomic_store(host_done, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      }
-    }
-  }
+  if (tid < 64) publish_call(call_ring, host_done, seq_ctr, layer, B, nhost);
 }
 
 __global__ void k_qstar_batch(const int32_t* __restrict__ m, const uint32_t* __restrict__ f,
