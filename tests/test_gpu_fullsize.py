@@ -9,6 +9,12 @@ synchronization between calls: asynchronous host share, in-kernel fetches), then
   * sampled outputs (layers and tokens spread over the run, the first and the last call included)
     against the oracle's routed MoE of the dequantized records (fp64), rel-L2 <= 5e-3 and
     max-abs <= 2e-2.  The output does not depend on the cache, so the pool record is the reference.
+Decode, qwen3.8-flash-next (48 layers x 512 NVFP4 experts of 2560 x 640 in pinned host memory,
+top-10, 2457 slots, f = 65535, B = 16, speculative next-layer requests keeping 65 % of the true
+top-10): 4 steps x 48 layers issued back to back, 160 entries per call (the control kernel's
+paths for more than 64 entries, the 8-token decode kernels with two token chunks per unit); the
+final tables and the hit / fetch / host / speculative totals bit for bit against the oracle policy,
+and sampled outputs against the oracle.
 Prefill, dsv4-flash (256 NVFP4 experts of 4096 x 2048, top-6, 2201 slots, T = 2048 tokens): two
 layers streamed into the double buffer and the grouped GEMMs, sampled tokens against the oracle."""
 import numpy as np
@@ -23,7 +29,7 @@ from oracle.ffn import combine, x_f64  # noqa: E402
 from oracle.formats import f64_to_bf16_bits  # noqa: E402
 from oracle.policy import SlotCache  # noqa: E402
 from oracle.router import topk_softmax  # noqa: E402
-from synth.configs import A3B, DSV4_PREFILL  # noqa: E402
+from synth.configs import A3B, DSV4_PREFILL, QWEN_NEXT  # noqa: E402
 from tests.helpers import PinnedPool, assert_close_bf16  # noqa: E402
 from tests.test_gpu_prefill import run_prefill  # noqa: E402
 
@@ -90,6 +96,81 @@ def test_decode_35b_a3b_full_size(eff):
             y = np.stack([yk[0] for yk in ys])[None]          # [1, K, H]
             ref = f64_to_bf16_bits(combine(y, w))
             assert_close_bf16(out[t, l:l + 1], ref, what="token %d layer %d" % (t, l))
+    finally:
+        if eng is not None:
+            eng.close()
+        pool.free()
+
+
+def test_decode_qwen_next_full_size_batch16(eff):
+    W, B, steps = QWEN_NEXT, 16, 4
+    L, E, K, H, I = W.L, W.E, W.K, W.H, W.I
+    print("full-size decode %s: L=%d E=%d K=%d H=%d I=%d S=%d f=%d B=%d steps=%d spec=%.2f" % (
+        W.name, L, E, K, H, I, W.S, W.f_q16, B, steps, W.spec_keep), flush=True)
+    pool = PinnedPool(eff, W.seed, L, E, H, I, W.fmt)
+    eng = None
+    try:
+        cfg = eff.make_config(L, E, K, H, I, W.fmt, W.S, B, 0, W.f_q16, 12)
+        eng = eff.Engine(cfg, pool.ptr, pool.ts)
+        n_rows = steps * B
+        X = [synth.activations(W.seed, l, 0, n_rows, H) for l in range(L)]
+        LG = [synth.trace_logits(W.seed, l, E, W.zipf_s, 0, n_rows) for l in range(L)]
+        SP = []  # SP[l]: the speculative ids for layer l + 1 issued with layer l's call
+        for l in range(L - 1):
+            truth = synth.gumbel_topk_sets(LG[l + 1], K)
+            SP.append(np.stack([synth.spec_ids(W.seed, l + 1, E, W.zipf_s, r, truth[r], W.spec_keep)
+                                for r in range(n_rows)]).astype(np.int32))
+        Xd = [torch.from_numpy(x.view(np.int16)).cuda() for x in X]
+        LGd = [torch.from_numpy(lg).cuda() for lg in LG]
+        SPd = [torch.from_numpy(sp.reshape(-1)).cuda() for sp in SP]
+        OUT = torch.empty((steps, L, B, H), dtype=torch.int16, device="cuda")
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        for t in range(steps):
+            rows = slice(t * B, (t + 1) * B)
+            for l in range(L):
+                spec = SPd[l][t * B * K:(t + 1) * B * K] if l + 1 < L else None
+                eng.decode_layer(l, Xd[l][rows], OUT[t, l], logits=LGd[l][rows], spec_ids=spec, side=side)
+        torch.cuda.synchronize()
+        st = eng.stats()
+        snap = eng.snapshot_tables()
+        out = OUT.cpu().numpy().view(np.uint16)
+
+        # the oracle policy over the same calls, in the same order (real, then the speculative one)
+        cache = SlotCache(L, E, W.S, W.f_q16)
+        hits = fetched = host = spec_fetched = 0
+        for t in range(steps):
+            rows = slice(t * B, (t + 1) * B)
+            for l in range(L):
+                ids, _ = topk_softmax(LG[l][rows], K)
+                flat = [int(e) for e in ids.reshape(-1)]
+                cache.ensure(l, flat)
+                res = cache.split()
+                hits += len(set(flat)) - res.m
+                fetched += res.q
+                host += res.host
+                if l + 1 < L:
+                    cache.ensure(l + 1, [int(e) for e in SP[l][rows].reshape(-1)], speculative=True)
+                    spec_fetched += cache.split().q
+        assert list(snap["table"]) == cache.table
+        assert list(snap["owner"]) == cache.owner
+        assert list(snap["usage"]) == cache.usage
+        assert list(snap["recency"]) == cache.recency
+        assert (snap["step"], snap["last_real"]) == (cache.step, cache.last_real)
+        assert (st["hits"], st["fetched"], st["host"], st["spec_fetched"]) == (hits, fetched, host, spec_fetched)
+        assert fetched > 0 and spec_fetched > 0 and hits > 0
+
+        # sampled outputs (tokens 0, 5, 10, 15 of a few calls): the routed MoE of the pool records, fp64
+        for t, l in [(0, 0), (steps - 1, L - 1), (1, 17), (2, 30)]:
+            rows = slice(t * B, (t + 1) * B)
+            ids, w = topk_softmax(LG[l][rows], K)
+            for b in (0, 5, 10, 15):
+                x = x_f64(X[l][t * B + b:t * B + b + 1])
+                jobs = [(pool.record(l * E + int(e)), pool.tensor_scales(l * E + int(e)), x) for e in ids[b]]
+                ys = cffn.expert_ffn_batch(jobs, W.fmt, H, I, 16)
+                y = np.stack([yk[0] for yk in ys])[None]
+                ref = f64_to_bf16_bits(combine(y, w[b:b + 1]))
+                assert_close_bf16(out[t, l, b:b + 1], ref, what="step %d layer %d token %d" % (t, l, b))
     finally:
         if eng is not None:
             eng.close()
