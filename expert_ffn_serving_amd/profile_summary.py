@@ -3,7 +3,7 @@
     python3 -m expert_ffn_serving_amd.profile_summary counters DIR
         per-kernel totals of every counter in DIR/**/*counter_collection.csv
     python3 -m expert_ffn_serving_amd.profile_summary traffic --fetch DIR --write DIR \\
-            --kernel k_gateup --copy-bytes 1073741824 --source k_decode.hip --out FILE.json
+            --kernel k_gateup --copy-bytes 1073741824 --source k_decode.hip [--last N] --out FILE.json
         HBM bytes per dispatch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run.  Each
         counter is scaled by what it reads for the largest plain device-to-device copy in the same
         run (a copy of --copy-bytes bytes reads and writes exactly that many bytes).
@@ -51,27 +51,31 @@ def read_counters(d):
         for r in csv.DictReader(open(f)):
             per[(kernel_name(r["Kernel_Name"]), r["Counter_Name"], r.get("Dispatch_Id", ""))] += float(r["Counter_Value"])
     out = collections.defaultdict(list)
-    for (k, c, _), v in per.items():
-        out[(k, c)].append(v)
+    for (k, c, d), v in per.items():
+        out[(k, c)].append((int(d) if str(d).isdigit() else 0, v))
     return out
 
 
 def cmd_counters(a):
     data = read_counters(a.dir)
     print("kernel\tcounter\tdispatches\ttotal\tper_dispatch")
-    for (k, c), v in sorted(data.items()):
+    for (k, c), dv in sorted(data.items()):
+        v = [x for _, x in dv]
         print("%s\t%s\t%d\t%.6g\t%.6g" % (k, c, len(v), sum(v), sum(v) / len(v)))
 
 
-def per_dispatch(data, counter, kernel):
-    vals = [v for (k, c), vs in data.items() if c == counter and k.startswith(kernel) for v in vs]
+def per_dispatch(data, counter, kernel, last=0):
+    """Average of the kernel's dispatches (the last `last` of them by dispatch id, if > 0)."""
+    vals = sorted((d, v) for (k, c), dv in data.items() if c == counter and k.startswith(kernel) for d, v in dv)
     if not vals:
         raise SystemExit("no %s dispatches of %s" % (counter, kernel))
-    return sum(vals) / len(vals), len(vals)
+    if last > 0:
+        vals = vals[-last:]
+    return sum(v for _, v in vals) / len(vals), len(vals)
 
 
 def copy_factor(data, counter, copy_bytes):
-    vals = [v for (k, c), vs in data.items() if c == counter and k.startswith(COPY_KERNEL) for v in vs]
+    vals = [v for (k, c), dv in data.items() if c == counter and k.startswith(COPY_KERNEL) for _, v in dv]
     if not vals:
         raise SystemExit("no %s copy dispatch to calibrate against" % counter)
     return copy_bytes / (max(vals) * 1024.0)
@@ -80,8 +84,8 @@ def copy_factor(data, counter, copy_bytes):
 def cmd_traffic(a):
     fd, wd = read_counters(a.fetch), read_counters(a.write)
     ff, wf = copy_factor(fd, "FETCH_SIZE", a.copy_bytes), copy_factor(wd, "WRITE_SIZE", a.copy_bytes)
-    fk, nf = per_dispatch(fd, "FETCH_SIZE", a.kernel)
-    wk, nw = per_dispatch(wd, "WRITE_SIZE", a.kernel)
+    fk, nf = per_dispatch(fd, "FETCH_SIZE", a.kernel, a.last)
+    wk, nw = per_dispatch(wd, "WRITE_SIZE", a.kernel, a.last)
     res = {
         "kernel": a.kernel,
         "hbm_bytes_per_launch": int(round(fk * 1024 * ff + wk * 1024 * wf)),
@@ -93,6 +97,8 @@ def cmd_traffic(a):
     }
     if a.command:
         res["command"] = a.command
+    if a.note:
+        res["note"] = a.note
     text = json.dumps(res, indent=1)
     if a.out:
         with open(a.out, "w") as o:
@@ -143,6 +149,8 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, default=1 << 30)
     t.add_argument("--source", nargs="+", default=["k_decode.hip"])
     t.add_argument("--command", default="")
+    t.add_argument("--note", default="")
+    t.add_argument("--last", type=int, default=0, help="only the last N dispatches of the kernel")
     t.add_argument("--out", default="")
     r = sub.add_parser("trace")
     r.add_argument("dir")

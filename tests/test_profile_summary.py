@@ -67,3 +67,15 @@ def test_trace_window_averages(tmp_path, capsys):
     r = res["k_down<0, 1>"]
     assert r["dispatches"] == 5 and r["avg_us"] == pytest.approx(4.0)
     assert r["last"] == 2 and r["last_avg_us"] == pytest.approx(7.0)   # the two latest starts: 5000, 9000 ns
+
+
+def test_traffic_last_window(tmp_path):
+    f, w = str(tmp_path / "f"), str(tmp_path / "w")
+    rows = [("__amd_rocclr_copyBuffer", 2048.0)] + [("void eff::k_gateup<0, 1>(a)", float(v)) for v in (1, 2, 3, 10, 20)]
+    write_csv(f, "FETCH_SIZE", rows)
+    write_csv(w, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 4096.0)] + [("void eff::k_gateup<0, 1>(a)", 1.0)] * 5)
+    out = str(tmp_path / "t.json")
+    ps.main(["traffic", "--fetch", f, "--write", w, "--kernel", "k_gateup", "--copy-bytes", str(1 << 22),
+             "--last", "2", "--out", out])
+    d = json.load(open(out))
+    assert d["fetch_kib_per_dispatch"] == pytest.approx(15.0) and d["dispatches"] == [2, 2]   # the last two ids
