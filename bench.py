@@ -295,11 +295,12 @@ def run_prefill(eff, torch, synth, W, layers, threads, cpu_tokens=0, cpu_threads
 
 
 # ---------------------------------------------------------------------- decode kernels at a large shape
-def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1, 4), tokens=64, zipf=1.0):
-    """HBM rates of the decode expert kernels at the DeepSeek-V4-Flash expert shape (4096 x 2048 NVFP4,
-    top-6), where a layer's experts are tens of MB: layers 0 and 1 of the prefill pool streamed whole into
-    the two slot buffers (S = 2E, every expert resident, no call misses), then `tokens` profiled decode
-    steps per batch size on Zipf(1.0) trace logits, alternating the two layers."""
+def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1, 4), tokens=64, zipf=1.0,
+                        label="dsv4"):
+    """HBM rates of the decode expert kernels at a workload's expert shape (e.g. the DeepSeek-V4-Flash
+    4096 x 2048 NVFP4 experts, tens of MB per layer): layers 0 and 1 of the pool streamed whole into the
+    two slot buffers (S = 2E, every expert resident, no call misses), then `tokens` profiled decode steps
+    per batch size on Zipf trace logits, alternating the two layers."""
     import numpy as np
     ptr, ts, R = pool
     E, K, H, I = W.E, W.K, W.H, W.I
@@ -313,8 +314,8 @@ def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1,
     torch.cuda.synchronize()
     layers = 2
     mat_bytes = H * I // 2 + H * I // 16
-    res = {"workload": "dsv4-flash expert shape (H=%d I=%d E=%d K=%d NVFP4), 2 layers, every expert resident" % (
-        H, I, E, K), "tokens": tokens}
+    res = {"workload": "%s expert shape (H=%d I=%d E=%d K=%d NVFP4), 2 layers, every expert resident" % (
+        W.name, H, I, E, K), "tokens": tokens, "zipf": zipf}
     for B in batches:
         LG = [torch.from_numpy(synth.trace_logits(W.seed, l, E, zipf, 0, tokens * B)).cuda() for l in range(layers)]
         eng.reset_stats()
@@ -337,8 +338,8 @@ def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1,
             "gateup_frac": round(gu / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "down_us": round(d_ms * 1e3 / max(1, n), 2), "down_GBps": round(dn / (d_ms * 1e-3) / 1e9, 1),
             "down_frac": round(dn / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-        log("  decode kernels at the dsv4 shape, B=%d: %.1f experts/launch, gate/up %.1f us (%.0f GB/s), "
-            "down %.1f us (%.0f GB/s), fetched %d" % (B, U / max(1, n), g_ms * 1e3 / max(1, n),
+        log("  decode kernels at the %s shape, B=%d: %.1f experts/launch, gate/up %.1f us (%.0f GB/s), "
+            "down %.1f us (%.0f GB/s), fetched %d" % (label, B, U / max(1, n), g_ms * 1e3 / max(1, n),
                                                        gu / (g_ms * 1e-3) / 1e9, d_ms * 1e3 / max(1, n),
                                                        dn / (d_ms * 1e-3) / 1e9, st["fetched"]))
     eng.close()
@@ -454,6 +455,8 @@ def main():
     # the enqueuing thread and the runtime (on 16 cores: 15 threads gave 430-446 tok/s, 12 gave 476-478)
     ap.add_argument("--threads", type=int, default=12)
     ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-qwen-next-kernels", action="store_true",
+                    help="skip the decode kernels at the qwen3.8-flash-next expert shape (B = 1, 8, 16)")
     ap.add_argument("--no-graph", action="store_true", help="time eager decode calls only (no HIP graph)")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -468,7 +471,7 @@ def main():
 
     import expert_ffn_serving_amd as eff
     import synth
-    from synth.configs import A3B, DSV4_PREFILL
+    from synth.configs import A3B, DSV4_PREFILL, QWEN_NEXT
 
     eff.lib()   # fails loudly if the HIP library is missing
     if not torch.cuda.is_available():
@@ -497,6 +500,14 @@ def main():
     if not args.skip_prefill:
         pre = run_prefill(eff, torch, synth, DSV4_PREFILL, args.prefill_layers, args.threads,
                           0 if args.skip_cpu else 16, ncpu)
+    qn = None
+    if not args.skip_qwen_next_kernels:   # the decode kernels at the third decode workload's expert shape
+        W = QWEN_NEXT
+        log("decode kernels %s: E=%d K=%d H=%d I=%d (2 layers resident)" % (W.name, W.E, W.K, W.H, W.I))
+        pool = fill_pool(eff, synth, W.seed, 2, W.E, W.H, W.I, W.fmt, args.threads)
+        qn = decode_kernel_rates(eff, torch, synth, W, pool, 2, args.threads, batches=W.batches, zipf=W.zipf_s,
+                                 label="qwen3.8-flash-next")
+        eff.host_free(pool[0])
     line = {
         "metric": METRIC, "value": round(dec["value"], 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(dec["ms"], 4), "higher_is_better": True, "scaling": "weak",
@@ -508,6 +519,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_detail": dec["detail"],
         "prefill": pre,
+        "decode_kernels_qwen_next": qn,
     }
     print(json.dumps(line), flush=True)
 

@@ -129,12 +129,14 @@ __device__ inline float dword_dot_bf16(uint32_t d, const uint32_t* xw, float xs)
   return raw;
 }
 
+// tokens j >= nt (a unit's last chunk holds fewer than NT) are skipped: nt is uniform per workgroup
 template <int FMT, int NT>
-__device__ inline void gateup_tile(uint32_t wg, uint32_t wu, uint32_t rg, uint32_t ru, const uint4* xv,
+__device__ inline void gateup_tile(uint32_t wg, uint32_t wu, uint32_t rg, uint32_t ru, const uint4* xv, int nt,
                                    float (&acc)[2][NT]) {
   const float sg = scale_value<FMT>(rg), su = scale_value<FMT>(ru);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
+    if (NT > 1 && j >= nt) break;
     uint32_t xw[4];
     x_pairs<FMT>(xv[j], xw);
     float xs = 0.f;
@@ -209,13 +211,13 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
         }
         __builtin_amdgcn_sched_barrier(0);  // every load of the round is in flight before any use
 #pragma unroll
-        for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], acc);
+        for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], 1, acc);
       }
       for (; kb < KB; kb += 4) {  // tail
         const uint4 xv[1] = {*reinterpret_cast<const uint4*>(xt + kb * 32)};
         gateup_tile<FMT, NT>(*reinterpret_cast<const uint32_t*>(gp + kb * 256),
                              *reinterpret_cast<const uint32_t*>(up + kb * 256), load_scale_raw<FMT>(gs + kb * 32),
-                             load_scale_raw<FMT>(us + kb * 32), xv, acc);
+                             load_scale_raw<FMT>(us + kb * 32), xv, 1, acc);
       }
     } else {
       // several tokens: the first round of weight loads, then the chunk's token rows into LDS (the
@@ -244,8 +246,8 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
           if (k < KB) {  // uniform per wave
             uint4 xv[NT];
 #pragma unroll
-            for (int j = 0; j < NT; ++j) xv[j] = j < nt ? s_x[j * H8 + k * 4 + q] : make_uint4(0, 0, 0, 0);
-            gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv, acc);
+            for (int j = 0; j < NT; ++j) xv[j] = j < nt ? s_x[j * H8 + k * 4 + q] : make_uint4(0, 0, 0, 0);  // read only below nt
+            gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv, nt, acc);
           }
         }
         kb += 4 * UNR;
