@@ -356,7 +356,6 @@ __device__ inline void down_tile(uint32_t d, uint32_t rd, const uint4* s_a4, con
 // grid: maxU * (H/(16*RS)) workgroups, one per (plan unit, RS 16-row slices of H); 4/RS waves
 // share a slice.  The unit's SwiGLU activations, already fp16 from k_gateup, are copied into LDS
 // with their per-group scales and sums before the sweep, once for the RS slices.
-constexpr int kDownRS = 2;  // measured: 2 beats 1 and 4 at H = 4096, I = 2048
 template <int FMT, int NT, int RS>
 __global__ void __launch_bounds__(kWG)
 k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
@@ -523,6 +522,16 @@ k_bw_copy(const uint8_t* __restrict__ pool, int64_t R, int64_t n_flat, int64_t f
   }
 }
 
+// 16-row slices per down workgroup (measured): 4 when a launch would otherwise have 8192 or more
+// small workgroups (qwen3.8-flash-next shape, B = 8 and 16: 47 -> 34 us and 80 -> 58 us); 2 for
+// long rows (I >= 1024: the activation stage is shared by enough tiles per wave); else 1 (the
+// 35b-a3b shape at B = 1, where fewer, longer workgroups are slower)
+int down_slices(int units, int H, int I) {
+  if (units * (H / 16) >= 8192 && H % 64 == 0) return 4;
+  if (I >= 1024 && H % 32 == 0) return 2;
+  return 1;
+}
+
 template <int FMT, int NT>
 hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, hipStream_t s) {
   const eff_config& c = e->cfg;
@@ -539,14 +548,16 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, h
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
   size_t lds = (size_t)NT * (I / 8) * (sizeof(uint4) + sizeof(float2));
-  // kDownRS slices per workgroup for long down rows (I >= 1024: the activation stage is then shared
-  // by enough tiles per wave); short rows keep one slice and four waves per slice
-  if (I >= 1024 && H % (16 * kDownRS) == 0)
-    hipLaunchKernelGGL((k_down<FMT, NT, kDownRS>), dim3(units * (H / (16 * kDownRS))), dim3(kWG), lds, s, e->d_arena,
-                       e->pool_dev, e->R, e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
+  const int rs = down_slices(units, H, I);
+  if (rs == 4)
+    hipLaunchKernelGGL((k_down<FMT, NT, 4>), dim3(units * (H / 64)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
+                       e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
+  else if (rs == 2)
+    hipLaunchKernelGGL((k_down<FMT, NT, 2>), dim3(units * (H / 32)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
+                       e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
   else
     hipLaunchKernelGGL((k_down<FMT, NT, 1>), dim3(units * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
-                     e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
+                       e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
   err = hipGetLastError();
   timing_mark(e, ts, 3, s);
   return err;
@@ -566,8 +577,11 @@ hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
     err = hipFuncSetAttribute((const void*)k_down<F, N, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, \
                               N * (I / 8) * 24);                                                        \
   if (fmt == F && N <= NT && err == hipSuccess)                                                         \
-    err = hipFuncSetAttribute((const void*)k_down<F, N, kDownRS>,                                       \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, N * (I / 8) * 24);            \
+    err = hipFuncSetAttribute((const void*)k_down<F, N, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                              N * (I / 8) * 24);                                                        \
+  if (fmt == F && N <= NT && err == hipSuccess)                                                         \
+    err = hipFuncSetAttribute((const void*)k_down<F, N, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                              N * (I / 8) * 24);                                                        \
   if (fmt == F && N <= NT && err == hipSuccess)                                                         \
     err = hipFuncSetAttribute((const void*)k_gateup<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize,  \
                               N * H * 2);
