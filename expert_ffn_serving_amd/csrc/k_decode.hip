@@ -213,11 +213,23 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
 #pragma unroll
         for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], 1, acc);
       }
-      for (; kb < KB; kb += 4) {  // tail
-        const uint4 xv[1] = {*reinterpret_cast<const uint4*>(xt + kb * 32)};
-        gateup_tile<FMT, NT>(*reinterpret_cast<const uint32_t*>(gp + kb * 256),
-                             *reinterpret_cast<const uint32_t*>(up + kb * 256), load_scale_raw<FMT>(gs + kb * 32),
-                             load_scale_raw<FMT>(us + kb * 32), xv, 1, acc);
+      if (kb < KB) {  // the last, partial round (H / 32 not a multiple of 4 * UNR): its loads together too
+        uint32_t wg[UNR], wu[UNR], rg[UNR], ru[UNR];
+        uint4 xv[UNR][1];
+#pragma unroll
+        for (int z = 0; z < UNR; ++z) {
+          const int k = kb + 4 * z;
+          const bool in = k < KB;  // uniform per wave
+          wg[z] = in ? *reinterpret_cast<const uint32_t*>(gp + k * 256) : 0u;
+          wu[z] = in ? *reinterpret_cast<const uint32_t*>(up + k * 256) : 0u;
+          rg[z] = in ? load_scale_raw<FMT>(gs + k * 32) : 0u;
+          ru[z] = in ? load_scale_raw<FMT>(us + k * 32) : 0u;
+          xv[z][0] = in ? *reinterpret_cast<const uint4*>(xt + k * 32) : make_uint4(0, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int z = 0; z < UNR; ++z)
+          if (kb + 4 * z < KB) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], 1, acc);
       }
     } else {
       // several tokens: the first round of weight loads, then the chunk's token rows into LDS (the
