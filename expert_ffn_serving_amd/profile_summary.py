@@ -129,9 +129,12 @@ def cmd_trace(a):
     res = {}
     for k in sorted(names):
         d = [x[1] for x in data[k]]
-        tail = d[-a.last:] if a.last > 0 else d
+        head = d[:len(d) - a.skip] if a.skip > 0 else d
+        tail = head[-a.last:] if a.last > 0 else head
+        if not tail:
+            raise SystemExit("no dispatches of %s left after skipping %d" % (k, a.skip))
         res[k] = {"dispatches": len(d), "avg_us": round(sum(d) / len(d) / 1e3, 3),
-                  "last": len(tail), "last_avg_us": round(sum(tail) / len(tail) / 1e3, 3),
+                  "skipped": a.skip, "last": len(tail), "last_avg_us": round(sum(tail) / len(tail) / 1e3, 3),
                   "last_min_us": round(min(tail) / 1e3, 3), "last_max_us": round(max(tail) / 1e3, 3)}
     print(json.dumps(res, indent=1))
     return res
@@ -156,6 +159,7 @@ def main(argv=None):
     r.add_argument("dir")
     r.add_argument("--kernel", required=True)
     r.add_argument("--last", type=int, default=0)
+    r.add_argument("--skip", type=int, default=0, help="leave out the last N dispatches before taking the window")
     a = p.parse_args(argv)
     {"counters": cmd_counters, "traffic": cmd_traffic, "trace": cmd_trace}[a.cmd](a)
 

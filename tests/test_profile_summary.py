@@ -67,6 +67,10 @@ def test_trace_window_averages(tmp_path, capsys):
     r = res["k_down<0, 1>"]
     assert r["dispatches"] == 5 and r["avg_us"] == pytest.approx(4.0)
     assert r["last"] == 2 and r["last_avg_us"] == pytest.approx(7.0)   # the two latest starts: 5000, 9000 ns
+    res = ps.main(["trace", str(d), "--kernel", "k_down", "--skip", "2", "--last", "2"]) or json.loads(
+        capsys.readouterr().out)
+    r = res["k_down<0, 1>"]
+    assert r["last"] == 2 and r["last_avg_us"] == pytest.approx(2.5)   # the two before those: 2000, 3000 ns
 
 
 def test_traffic_last_window(tmp_path):
