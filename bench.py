@@ -346,6 +346,71 @@ def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1,
     return res
 
 
+def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16):
+    """End-to-end decode over a workload's whole pool (every layer, its slot count) with speculative
+    next-layer requests, for each batch size in W.batches: `warm` untimed then `timed` timed steps of all
+    W.L layers, each from an empty cache.  Run twice: at the workload's fetch fraction, and at the one the
+    bandwidth profile gives on this machine ([FT-deep] §4 ②), which sends part of the misses to the host
+    executor and fetches fewer of the speculative ones.  Reports tok/s and the per-layer-call policy counts;
+    the link bytes are the demand and speculative fetches times the record size."""
+    import numpy as np
+    ptr, ts, R = fill_pool(eff, synth, W.seed, W.L, W.E, W.H, W.I, W.fmt, 16)
+    res = {"workload": "%s (L=%d E=%d K=%d H=%d I=%d NVFP4, S=%d, speculative keep %.2f)" % (
+        W.name, W.L, W.E, W.K, W.H, W.I, W.S, W.spec_keep), "warmup": warm, "steps": timed, "record_bytes": R}
+    side = torch.cuda.Stream()
+    cfg = eff.make_config(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, max(W.batches), 0, W.f_q16, threads)
+    eng = eff.Engine(cfg, ptr, ts)
+    bw = eng.profile_bandwidth(256)
+    eng.close()
+    res["profiled_f"] = {"frac_q16": bw["frac_q16"], "pcie_GBps_concurrent": round(bw["pcie_concurrent"] / 1e9, 2),
+                         "host_GBps_concurrent": round(bw["host_concurrent"] / 1e9, 2)}
+    log("  bandwidth profile at this record size: link %.1f GB/s, host %.1f GB/s -> f = %d" % (
+        bw["pcie_concurrent"] / 1e9, bw["host_concurrent"] / 1e9, bw["frac_q16"]))
+    for B in W.batches:
+        n_rows = (warm + timed) * B
+        X = [torch.from_numpy(synth.activations(W.seed, l, 0, n_rows, W.H).view(np.int16)).cuda() for l in range(W.L)]
+        lg_host = [synth.trace_logits(W.seed, l, W.E, W.zipf_s, 0, n_rows) for l in range(W.L)]
+        LG = [torch.from_numpy(a).cuda() for a in lg_host]
+        SP = []
+        for l in range(W.L - 1):   # predictions of layer l+1's sets, made at layer l
+            truth = synth.gumbel_topk_sets(lg_host[l + 1], W.K)
+            SP.append(torch.from_numpy(np.stack([synth.spec_ids(W.seed, l + 1, W.E, W.zipf_s, r, truth[r], W.spec_keep)
+                                                 for r in range(n_rows)]).astype(np.int32).reshape(-1)).cuda())
+        out = torch.empty((B, W.H), dtype=torch.int16, device="cuda")
+        for tag, f in (("workload_f", W.f_q16), ("profiled_f", bw["frac_q16"])):
+            cfg = eff.make_config(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, B, 0, f, threads)
+            eng = eff.Engine(cfg, ptr, ts)
+
+            def run(t0, t1):
+                for t in range(t0, t1):
+                    r = slice(t * B, (t + 1) * B)
+                    for l in range(W.L):
+                        eng.decode_layer(l, X[l][r], out, logits=LG[l][r], side=side,
+                                         spec_ids=SP[l][t * B * W.K:(t + 1) * B * W.K] if l + 1 < W.L else None)
+            run(0, warm)
+            torch.cuda.synchronize()
+            s0 = eng.stats()
+            t0 = time.perf_counter()
+            run(warm, warm + timed)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            s1 = eng.stats()
+            eng.close()
+            n = timed * W.L
+            per = {k: round((s1[k] - s0[k]) / n, 2) for k in ("hits", "fetched", "host", "spec_fetched")}
+            link = (per["fetched"] + per["spec_fetched"]) * R
+            res.setdefault("B%d" % B, {})[tag] = {
+                "frac_q16": f, "tok_s": round(timed * B / dt, 2), "ms_per_step": round(dt * 1e3 / timed, 3),
+                "us_per_layer": round(dt * 1e6 / n, 1), "per_layer_call": per,
+                "link_MB_per_layer": round(link / 1e6, 1), "link_GBps": round(link / (dt / n) / 1e9, 1)}
+            log("  %s end to end, B=%d, f=%d: %.1f tok/s (%.1f us per layer), per layer call %s, %.0f MB over "
+                "the link per layer (%.1f GB/s)" % (W.name, B, f, timed * B / dt, dt * 1e6 / n, per, link / 1e6,
+                                                   link / (dt / n) / 1e9))
+        del X, LG, SP
+    eff.host_free(ptr)
+    return res
+
+
 # ------------------------------------------------------------------------------------- CPU oracle
 def host_cpu():
     """CPU model and the cores this process may run on."""
@@ -457,6 +522,9 @@ def main():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-qwen-next-kernels", action="store_true",
                     help="skip the decode kernels at the qwen3.8-flash-next expert shape (B = 1, 8, 16)")
+    ap.add_argument("--qwen-next-e2e", action="store_true",
+                    help="also run the qwen3.8-flash-next decode end to end over its whole pool (about 70 GB of "
+                         "pinned host memory, B = 1, 8, 16)")
     ap.add_argument("--no-graph", action="store_true", help="time eager decode calls only (no HIP graph)")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -508,6 +576,10 @@ def main():
         qn = decode_kernel_rates(eff, torch, synth, W, pool, 2, args.threads, batches=W.batches, zipf=W.zipf_s,
                                  label="qwen3.8-flash-next")
         eff.host_free(pool[0])
+    qe = None
+    if args.qwen_next_e2e:
+        log("decode end to end %s" % QWEN_NEXT.name)
+        qe = decode_e2e(eff, torch, synth, QWEN_NEXT, args.threads)
     line = {
         "metric": METRIC, "value": round(dec["value"], 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(dec["ms"], 4), "higher_is_better": True, "scaling": "weak",
@@ -520,6 +592,7 @@ def main():
         "decode_detail": dec["detail"],
         "prefill": pre,
         "decode_kernels_qwen_next": qn,
+        "decode_e2e_qwen_next": qe,
     }
     print(json.dumps(line), flush=True)
 
