@@ -30,6 +30,10 @@ Readings where the pages are silent (each listed in the design doc):
   the layer whose expert compute may still be running keeps its slots).
 * q' = min(q*, number of victims); the i-th ranked miss takes the i-th victim.
 * A speculative call fetches only (no host share) and leaves recency alone.
+* Optional speculative budget ([NVMe-8GB] "엔진" item 3: guesses for the next
+  layer are few, two of them there, and read in the gap left by the real reads):
+  a speculative call fetches at most `spec_budget` records, the first of its
+  ranked misses; None leaves q' as above.  Real calls ignore the budget.
 * A runtime rebuild to S' slots ([FT-blog] §七 item 1: the GPU expert cache is
   repartitioned for a new budget at a safe point, without touching the host pool;
   since the pool is the source of truth, losing the cache only costs speed) starts
@@ -66,8 +70,9 @@ class _Pending:
 
 
 class SlotCache:
-    def __init__(self, L: int, E: int, S: int, f_q16: int):
+    def __init__(self, L: int, E: int, S: int, f_q16: int, spec_budget: int | None = None):
         self.L, self.E, self.S, self.f = L, E, S, f_q16
+        self.spec_budget = spec_budget
         self.table = [-1] * (L * E)
         self.owner = [-1] * S
         self.usage = [-1] * S
@@ -107,6 +112,8 @@ class SlotCache:
         victims = sorted((v for v in range(self.S) if self.usage[v] < p.floor),
                          key=lambda v: (self.usage[v], v))
         qq = min(q, len(victims))
+        if p.speculative and self.spec_budget is not None:
+            qq = min(qq, self.spec_budget)
         fetch = []
         for i in range(qq):
             v, e = victims[i], ranked[i]

@@ -145,6 +145,54 @@ def test_speculative_then_real_hits():
     assert r.m == 1 and r.slots[0] == spec.slots[0]
 
 
+def test_speculative_budget_takes_the_ranked_prefix():
+    """A speculative call under a budget fetches exactly the first `budget` (miss, victim) pairs of what the
+    same call without one would, from the same state; hits are stamped alike, every entry maps to a slot
+    holding its expert or to -1, and a real call from that state is unaffected by the budget."""
+    import copy
+    import random
+    rng = random.Random(5)
+    L, E, S = 3, 16, 10
+    checked = 0
+    for _ in range(300):
+        base = SlotCache(L, E, S, 65535)
+        for _ in range(rng.randint(0, 6)):   # a random history of real and speculative calls
+            base.ensure_split(rng.randrange(L), rng.sample(range(E), rng.randint(1, 5)),
+                              speculative=rng.random() < 0.3)
+        layer, ids = rng.randrange(L), rng.sample(range(E), rng.randint(1, 8))
+        ref_cache = copy.deepcopy(base)
+        ref = ref_cache.ensure_split(layer, ids, speculative=True)
+        for budget in (0, 1, 2, 5):
+            c = copy.deepcopy(base)
+            c.spec_budget = budget
+            r = c.ensure_split(layer, ids, speculative=True)
+            assert r.q == min(ref.q, budget) and r.m == ref.m
+            assert r.fetch == ref.fetch[:budget]
+            assert r.cpu_ids == [-1] * len(ids)
+            for e, v in zip(ids, r.slots):
+                assert v == -1 or c.owner[v] == layer * E + e
+                if v >= 0:
+                    assert c.usage[v] == c.step          # hit or installed: stamped with this call
+            assert c.recency == base.recency             # speculation leaves recency alone
+            c.check_bijection()
+            real_a, real_b = copy.deepcopy(base), copy.deepcopy(base)
+            real_b.spec_budget = budget
+            assert real_a.ensure_split(layer, ids) == real_b.ensure_split(layer, ids)
+            checked += ref.q > budget
+    assert checked > 50   # the budget bound often
+
+
+def test_speculative_budget_zero_only_protects_hits():
+    L, E, S = 2, 8, 4
+    c = SlotCache(L, E, S, 65536, spec_budget=0)
+    c.ensure_split(0, [0, 1])
+    c.ensure_split(1, [2])
+    spec = c.ensure_split(0, [1, 5, 6], speculative=True)
+    assert spec.q == 0 and spec.fetch == [] and spec.m == 2
+    assert spec.slots[1:] == [-1, -1]
+    assert c.usage[spec.slots[0]] == c.step            # the predicted resident is protected
+
+
 def test_prefill_install_leaves_last_two_layers():
     L, E = 5, 8
     c = SlotCache(L, E, 2 * E + 3, 65536)
