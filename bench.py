@@ -349,9 +349,11 @@ def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1,
 def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16):
     """End-to-end decode over a workload's whole pool (every layer, its slot count) with speculative
     next-layer requests, for each batch size in W.batches: `warm` untimed then `timed` timed steps of all
-    W.L layers, each from an empty cache.  Run twice: at the workload's fetch fraction, and at the one the
+    W.L layers, each from an empty cache.  Run at the workload's fetch fraction and at the one the
     bandwidth profile gives on this machine ([FT-deep] §4 ②), which sends part of the misses to the host
-    executor and fetches fewer of the speculative ones.  Reports tok/s and the per-layer-call policy counts;
+    executor and fetches fewer of the speculative ones; each with speculative copies as requested, with at
+    most two per request copied after the gate/up kernel ([NVMe-8GB] "엔진" item 3), and (workload f) with
+    none.  Reports tok/s and the per-layer-call policy counts;
     the link bytes are the demand and speculative fetches times the record size."""
     import numpy as np
     ptr, ts, R = fill_pool(eff, synth, W.seed, W.L, W.E, W.H, W.I, W.fmt, 16)
@@ -377,9 +379,13 @@ def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16):
             SP.append(torch.from_numpy(np.stack([synth.spec_ids(W.seed, l + 1, W.E, W.zipf_s, r, truth[r], W.spec_keep)
                                                  for r in range(n_rows)]).astype(np.int32).reshape(-1)).cuda())
         out = torch.empty((B, W.H), dtype=torch.int16, device="cuda")
-        for tag, f in (("workload_f", W.f_q16), ("profiled_f", bw["frac_q16"])):
+        fp = bw["frac_q16"]
+        for tag, f, budget, gap in (("workload_f", W.f_q16, -1, False), ("workload_f_gap2", W.f_q16, 2, True),
+                                    ("workload_f_nospec", W.f_q16, 0, False), ("profiled_f", fp, -1, False),
+                                    ("profiled_f_gap2", fp, 2, True)):
             cfg = eff.make_config(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, B, 0, f, threads)
             eng = eff.Engine(cfg, ptr, ts)
+            eng.set_speculation(budget, gap)
 
             def run(t0, t1):
                 for t in range(t0, t1):
@@ -400,12 +406,12 @@ def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16):
             per = {k: round((s1[k] - s0[k]) / n, 2) for k in ("hits", "fetched", "host", "spec_fetched")}
             link = (per["fetched"] + per["spec_fetched"]) * R
             res.setdefault("B%d" % B, {})[tag] = {
-                "frac_q16": f, "tok_s": round(timed * B / dt, 2), "ms_per_step": round(dt * 1e3 / timed, 3),
+                "frac_q16": f, "spec_budget": budget, "spec_in_gap": gap, "tok_s": round(timed * B / dt, 2), "ms_per_step": round(dt * 1e3 / timed, 3),
                 "us_per_layer": round(dt * 1e6 / n, 1), "per_layer_call": per,
                 "link_MB_per_layer": round(link / 1e6, 1), "link_GBps": round(link / (dt / n) / 1e9, 1)}
-            log("  %s end to end, B=%d, f=%d: %.1f tok/s (%.1f us per layer), per layer call %s, %.0f MB over "
-                "the link per layer (%.1f GB/s)" % (W.name, B, f, timed * B / dt, dt * 1e6 / n, per, link / 1e6,
-                                                   link / (dt / n) / 1e9))
+            log("  %s end to end, B=%d, %s (f=%d): %.1f tok/s (%.1f us per layer), per layer call %s, %.0f MB "
+                "over the link per layer (%.1f GB/s)" % (W.name, B, tag, f, timed * B / dt, dt * 1e6 / n, per,
+                                                        link / 1e6, link / (dt / n) / 1e9))
         del X, LG, SP
     eff.host_free(ptr)
     return res

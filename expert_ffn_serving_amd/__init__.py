@@ -79,6 +79,7 @@ def lib():
             "eff_frac_q16": (U32, [ctypes.c_double, ctypes.c_double]),
             "eff_profile_bandwidth": (I32, [VP, I32, VP]),
             "eff_set_fetch_frac": (I32, [VP, U32]),
+            "eff_set_speculation": (I32, [VP, I32, I32]),
             "eff_rebuild_cache": (I32, [VP, I32, ctypes.c_uint64]),
             "eff_copy_missing": (I32, [VP, VP, VP]),
             "eff_expert_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP, VP]),
@@ -301,6 +302,11 @@ class Engine:
         out = BwProfile()
         _check(lib().eff_profile_bandwidth(self.h, records, ctypes.byref(out)))
         return {k: getattr(out, k) for k, _ in BwProfile._fields_ if k != "pad"}
+
+    def set_speculation(self, max_fetch: int = -1, in_gap: bool = False):
+        """eff_set_speculation: at most max_fetch records per speculative request (-1: no budget), copied
+        right after the control kernel or, with in_gap, after the layer's gate/up kernel."""
+        _check(lib().eff_set_speculation(self.h, max_fetch, 1 if in_gap else 0))
 
     def set_fetch_frac(self, frac_q16: int):
         _check(lib().eff_set_fetch_frac(self.h, frac_q16))

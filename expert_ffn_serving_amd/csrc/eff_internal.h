@@ -191,6 +191,9 @@ struct eff_engine {
   const uint8_t* pool_dev = nullptr;  // device view of the pinned pool (in-kernel fetches)
   bool async_host = false;        // host share on the worker thread, the stream waits on h_done
   bool spec_copy_pending = false; // a speculative copy on the side stream not yet waited for
+  int spec_budget = -1;           // eff_set_speculation: records per speculative request (-1: any)
+  bool spec_in_gap = false;       // eff_set_speculation: speculative copies start after gate/up
+  hipEvent_t ev_gateup = nullptr; // end of the layer's gate/up kernel (speculative copies in the gap)
   hipEvent_t ev_ctl = nullptr;
   // host-share worker (async mode)
   std::thread worker;
@@ -248,8 +251,9 @@ hipError_t launch_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, i
 hipError_t launch_prefill_install(eff_engine* e, int layer, hipStream_t s);
 hipError_t launch_fallback_install(eff_engine* e, int layer, const int32_t* experts, int n,
                                    hipStream_t s);
+// after_gateup: recorded on s between the gate/up and the down kernel (nullptr: none)
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
-                             float* y, hipStream_t s, bool plan_ready = false);
+                             float* y, hipStream_t s, bool plan_ready = false, hipEvent_t after_gateup = nullptr);
 hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s);
 // n records from the pool (flat ids first + i*stride modulo L*E) into dst[2][R] (bandwidth profile)
 hipError_t launch_bw_copy(eff_engine* e, int64_t first, int64_t stride, int n, uint8_t* dst, hipStream_t s);

@@ -75,7 +75,8 @@ static void release(eff_engine* e) {
                   e->h_tq};
   for (void* p : host)
     if (p) (void)hipHostFree(p);
-  hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_ctl, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0], e->ev_pf_done[1]};
+  hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_ctl, e->ev_gateup, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0],
+                      e->ev_pf_done[1]};
   for (hipEvent_t v : evs)
     if (v) (void)hipEventDestroy(v);
   for (auto& tc : e->timed)
@@ -151,6 +152,7 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_copy, hipEventDisableTiming));
   EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_ctl, hipEventDisableTiming));
   EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_spec, hipEventDisableTiming));
+  EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_gateup, hipEventDisableTiming));
   for (int b = 0; b < 2; ++b) {
     EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_pf[b], hipEventDisableTiming));
     EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_pf_done[b], hipEventDisableTiming));
@@ -557,6 +559,15 @@ uint32_t eff_frac_q16(double bp, double bh) {
   return q >= 65536.0 ? 65536u : (uint32_t)q;
 }
 
+int eff_set_speculation(eff_engine* e, int max_fetch, int in_gap) {
+  if (int rc = check_engine(e)) return rc;
+  if (max_fetch < -1 || (in_gap != 0 && in_gap != 1))
+    return fail(EFF_EINVAL, "eff_set_speculation: max_fetch >= -1 and in_gap 0 or 1");
+  e->spec_budget = max_fetch;
+  e->spec_in_gap = in_gap != 0;
+  return EFF_OK;
+}
+
 int eff_set_fetch_frac(eff_engine* e, uint32_t frac_q16) {
   if (int rc = check_engine(e)) return rc;
   if (frac_q16 > 65536u) return fail(EFF_EINVAL, "fetch_frac_q16 must be in [0, 65536]");
@@ -823,7 +834,10 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
     EFF_HIP_TRY(hipStreamWaitEvent(cs, e->ev_spec, 0));
     e->spec_copy_pending = false;
   }
-  if (spec) {  // this layer's speculative fetches travel on the side stream
+  // this layer's speculative fetches travel on the side stream: right after the control kernel, or
+  // in the gap after the gate/up kernel, which copies the layer's own fetched records
+  const bool gap = spec && e->spec_in_gap;
+  if (spec && !gap) {
     EFF_HIP_TRY(hipEventRecord(e->ev_ctl, cs));
     EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_ctl, 0));
     EFF_HIP_TRY(launch_fetch_copy(e, 1, ss));
@@ -832,9 +846,16 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   }
   // GPU experts; a unit installed by this call reads its record from the pool and fills its slot
   e->timing_q_src = e->d_counts + 1;  // this call's fetch count (real split)
-  const hipError_t ffn_err = launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true);
+  const hipError_t ffn_err = launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true,
+                                               gap ? e->ev_gateup : nullptr);
   e->timing_q_src = nullptr;
   EFF_HIP_TRY(ffn_err);
+  if (gap) {  // the victims are slots this call does not use, so the copy may overlap its down kernel
+    EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_gateup, 0));
+    EFF_HIP_TRY(launch_fetch_copy(e, 1, ss));
+    EFF_HIP_TRY(hipEventRecord(e->ev_spec, ss));
+    e->spec_copy_pending = true;
+  }
   if (e->async_host) {
     // the combine waits for the host share (or the control kernel's own release of the call)
     EFF_HIP_TRY(launch_combine(e->d_ygpu, e->h_yhost_dev, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs,

@@ -42,6 +42,7 @@ struct CacheState {
   int32_t* err;
   int32_t* host_err;  // host-mapped sticky error bits
   int sort_pow2;
+  int spec_budget;  // most records a speculative call fetches (-1: no budget)
 };
 
 // Barrier for data exchanged through LDS only: waits for this wave's LDS accesses, not for its
@@ -239,7 +240,8 @@ __device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, boo
   const int n = C.n, m = C.nm;
   const int64_t floor_ = C.floor_;
   const int64_t base = (int64_t)C.layer * E;
-  const int q = (int)qstar_dev(m, c.f);
+  int q = (int)qstar_dev(m, c.f);
+  if (C.spec && c.spec_budget >= 0) q = min(q, c.spec_budget);  // q' = min(q*, victims, budget)
   int qq = 0;
   if (q > 0) {
     if (tid == 0) {
@@ -962,6 +964,7 @@ static CacheState state_of(eff_engine* e) {
   c.err = e->d_err;
   c.host_err = e->h_err_dev;
   c.sort_pow2 = sort_pow2_of(c.S);
+  c.spec_budget = e->spec_budget;
   return c;
 }
 

@@ -545,7 +545,7 @@ int down_slices(int units, int H, int I) {
 }
 
 template <int FMT, int NT>
-hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, hipStream_t s) {
+hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, hipStream_t s, hipEvent_t after_gateup) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   const int ts = timing_begin(e, EFF_T_DECODE_GATEUP, s);
@@ -557,6 +557,7 @@ hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, h
                      e->d_ts, e->d_plan, x, H, I, c.top_k, c.max_tokens, a16, ag);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (after_gateup && (err = hipEventRecord(after_gateup, s)) != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
   size_t lds = (size_t)NT * (I / 8) * (sizeof(uint4) + sizeof(float2));
@@ -605,7 +606,7 @@ hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
 }
 
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
-                             float* y, hipStream_t s, bool plan_ready) {
+                             float* y, hipStream_t s, bool plan_ready, hipEvent_t after_gateup) {
   (void)layer;
   if (!plan_ready) {
     hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s);
@@ -617,14 +618,14 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
   const int units = std::min(e->maxU, B * e->cfg.top_k);  // plan units a call of B tokens can have
   const bool fp4 = e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3;
   switch (NT) {
-    case 1: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 1>(e, x, y, units, s)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 1>(e, x, y, units, s);
-    case 2: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 2>(e, x, y, units, s)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 2>(e, x, y, units, s);
-    case 4: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 4>(e, x, y, units, s)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 4>(e, x, y, units, s);
-    default: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 8>(e, x, y, units, s)
-                        : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 8>(e, x, y, units, s);
+    case 1: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 1>(e, x, y, units, s, after_gateup)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 1>(e, x, y, units, s, after_gateup);
+    case 2: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 2>(e, x, y, units, s, after_gateup)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 2>(e, x, y, units, s, after_gateup);
+    case 4: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 4>(e, x, y, units, s, after_gateup)
+                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 4>(e, x, y, units, s, after_gateup);
+    default: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 8>(e, x, y, units, s, after_gateup)
+                        : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 8>(e, x, y, units, s, after_gateup);
   }
 }
 

@@ -176,6 +176,21 @@ int eff_profile_bandwidth(eff_engine* e, int records, eff_bw_profile* out);
  * enqueued after it.  A graph captured earlier keeps the value it was captured with. */
 int eff_set_fetch_frac(eff_engine* e, uint32_t frac_q16);
 
+/* Speculative fetch scheduling ([NVMe-8GB] "엔진" item 3, prefetch into the gap: a
+ * few guesses of the next layer's experts, read after the layer's real reads so
+ * that they do not share the link with them).
+ *   max_fetch  records one speculative request may fetch at most: its q' becomes
+ *              min(q', max_fetch), the first ranked misses; -1 = no budget (the
+ *              default), 0 = fetch none (predicted residents are still protected).
+ *   in_gap     0: eff_decode_layer starts a speculative copy right after the
+ *              control kernel, beside the layer's own fetches (the default);
+ *              1: after the layer's gate/up kernel, which performs those fetches.
+ * Either way the next layer's expert kernels wait for the copy.  Applies to the
+ * calls enqueued after it (a graph captured earlier keeps its values); the policy
+ * and every result other than timing are the same for both values of in_gap.
+ * EFF_EINVAL for max_fetch < -1 or in_gap not 0 or 1. */
+int eff_set_speculation(eff_engine* e, int max_fetch, int in_gap);
+
 /* Runtime cache rebuild ([FT-blog] §七 item 1; [FT-deep] §4 design pattern ⑦): the
  * slot cache is rebuilt with num_slots slots for a new HBM budget, without touching
  * the host pool.  Everything is checked, and the new slot arena, owner and usage

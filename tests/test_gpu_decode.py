@@ -29,11 +29,14 @@ def dev_bf16(a):
 
 
 def run_decode(eff, pool, K, S, f, B, tokens, router=True, zipf=1.1, spec_keep=-1.0, seed=11,
-               compare_y=True, flags=0):
+               compare_y=True, flags=0, spec_budget=None, spec_gap=False):
     """Decode `tokens` steps through all layers on the GPU (eff_decode_layer) and the oracle."""
     L, E, H = pool.L, pool.E, pool.H
     eng = make_engine(eff, pool, K, S, B, f, flags=flags)
     orc = oracle_engine(pool, K, S, f)
+    if spec_budget is not None or spec_gap:
+        eng.set_speculation(-1 if spec_budget is None else spec_budget, spec_gap)
+        orc.cache.spec_budget = spec_budget
     side = torch.cuda.Stream()
     outs = []
     try:
@@ -191,6 +194,37 @@ def test_decode_speculative(eff):
         assert st["spec_fetched"] > 0
     finally:
         pool.free()
+
+
+@pytest.mark.parametrize("budget,gap", [(2, True), (0, False), (None, True), (3, False)])
+def test_decode_speculative_budget_and_gap(eff, budget, gap):
+    """A budget on speculative fetches and copies started after the gate/up kernel: ids, slots, split and
+    speculative counts, outputs and the final tables match the oracle's policy with the same budget; the
+    outputs equal those of the unbudgeted run (the pool is the source of truth)."""
+    pool = PinnedPool(eff, 22, 3, 32, 2560, 640, synth.FMT_NVFP4)
+    try:
+        ref, st0 = run_decode(eff, pool, 10, 40, 65535, 2, 4, router=False, zipf=1.2, spec_keep=0.65, seed=22)
+        outs, st = run_decode(eff, pool, 10, 40, 65535, 2, 4, router=False, zipf=1.2, spec_keep=0.65, seed=22,
+                              spec_budget=budget, spec_gap=gap)
+        assert np.array_equal(outs, ref)
+        if budget is None:
+            assert st["spec_fetched"] == st0["spec_fetched"]
+        else:
+            assert st["spec_fetched"] <= budget * 4 * 2   # at most `budget` per speculative request
+            assert st["spec_fetched"] < st0["spec_fetched"]
+    finally:
+        pool.free()
+
+
+def test_set_speculation_rejects_bad_values(eff, tiny_pool):
+    eng = make_engine(eff, tiny_pool, TINY.K, TINY.S, 1, 32768)
+    try:
+        for a, b in ((-2, 0), (1, 2), (0, -1)):
+            assert eff.lib().eff_set_speculation(eng.h, a, b) == eff.EFF_EINVAL
+        assert eff.lib().eff_set_speculation(eng.h, -1, 0) == 0
+        eng.set_speculation(2, True)
+    finally:
+        eng.close()
 
 
 @pytest.mark.parametrize("fmt,H,I", [(synth.FMT_INT4, 2048, 512), (synth.FMT_NVFP4, 4096, 2048),
