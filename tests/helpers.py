@@ -18,13 +18,26 @@ MAX_ABS = 2e-2
 class PinnedPool:
     """L*E records in pinned host memory (eff_host_alloc), filled by synth."""
 
-    def __init__(self, eff, seed, L, E, H, I, fmt, nthreads=16, layers=None):
+    def __init__(self, eff, seed, L, E, H, I, fmt, nthreads=16, layers=None, flats=None):
         self.eff = eff
         self.L, self.E, self.H, self.I, self.fmt = L, E, H, I, fmt
         self.R = synth.record_bytes(H, I)
         self.nbytes = L * E * self.R
         self.ptr = eff.host_alloc(self.nbytes)
         self.ts = np.ones(L * E * 3, np.float32)
+        if flats is not None:   # only these records (the generator keys each record by its flat id)
+            fl = sorted(set(int(f) for f in flats))
+            i = 0
+            while i < len(fl):
+                j = i
+                while j + 1 < len(fl) and fl[j + 1] == fl[j] + 1:
+                    j += 1
+                n = j - i + 1
+                ts = np.empty(n * 3, np.float32)
+                synth.fill_records(seed, E, H, I, fmt, fl[i], n, self.ptr + fl[i] * self.R, ts, nthreads)
+                self.ts[fl[i] * 3:(fl[i] + n) * 3] = ts
+                i = j + 1
+            return
         layers = range(L) if layers is None else layers
         for l in layers:   # layers not listed stay unfilled (never routed to in that test)
             ts = np.empty(E * 3, np.float32)

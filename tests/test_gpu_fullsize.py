@@ -15,6 +15,12 @@ top-10): 4 steps x 48 layers issued back to back, 160 entries per call (the cont
 paths for more than 64 entries, the 8-token decode kernels with two token chunks per unit); the
 final tables and the hit / fetch / host / speculative totals bit for bit against the oracle policy,
 and sampled outputs against the oracle.
+Decode, dsv4-flash (256 NVFP4 experts of 4096 x 2048 per layer, top-6, 2201 slots, f = 45875,
+Zipf(1.0), B = 4): the whole 43-layer pool (155.8 GB) cannot be pinned on a machine whose pinned
+allocations stop near 70 GB, so 16 of its layers are (58 GB, past 32-bit record offsets); 3 steps x
+16 layers issued back to back; only the records the routing trace reaches are generated (the
+generator keys each record by its flat id, so they are the full pool's), the rest is allocated but
+never read.  Final tables and totals against the oracle policy, sampled outputs against the oracle.
 Prefill, dsv4-flash (256 NVFP4 experts of 4096 x 2048, top-6, 2201 slots, T = 2048 tokens): two
 layers streamed into the double buffer and the grouped GEMMs, sampled tokens against the oracle."""
 import numpy as np
@@ -29,7 +35,7 @@ from oracle.ffn import combine, x_f64  # noqa: E402
 from oracle.formats import f64_to_bf16_bits  # noqa: E402
 from oracle.policy import SlotCache  # noqa: E402
 from oracle.router import topk_softmax  # noqa: E402
-from synth.configs import A3B, DSV4_PREFILL, QWEN_NEXT  # noqa: E402
+from synth.configs import A3B, DSV4_DECODE, DSV4_PREFILL, QWEN_NEXT  # noqa: E402
 from tests.helpers import PinnedPool, assert_close_bf16  # noqa: E402
 from tests.test_gpu_prefill import run_prefill  # noqa: E402
 
@@ -165,6 +171,70 @@ def test_decode_qwen_next_full_size_batch16(eff):
             rows = slice(t * B, (t + 1) * B)
             ids, w = topk_softmax(LG[l][rows], K)
             for b in (0, 5, 10, 15):
+                x = x_f64(X[l][t * B + b:t * B + b + 1])
+                jobs = [(pool.record(l * E + int(e)), pool.tensor_scales(l * E + int(e)), x) for e in ids[b]]
+                ys = cffn.expert_ffn_batch(jobs, W.fmt, H, I, 16)
+                y = np.stack([yk[0] for yk in ys])[None]
+                ref = f64_to_bf16_bits(combine(y, w[b:b + 1]))
+                assert_close_bf16(out[t, l, b:b + 1], ref, what="step %d layer %d token %d" % (t, l, b))
+    finally:
+        if eng is not None:
+            eng.close()
+        pool.free()
+
+
+def test_decode_dsv4_full_size_batch4(eff):
+    W, B, steps = DSV4_DECODE, 4, 3
+    L, E, K, H, I = 16, W.E, W.K, W.H, W.I   # 16 of the 43 layers: the pinned pool must fit
+    print("full-size decode %s: L=%d E=%d K=%d H=%d I=%d S=%d f=%d B=%d steps=%d" % (
+        W.name, L, E, K, H, I, W.S, W.f_q16, B, steps), flush=True)
+    n_rows = steps * B
+    LG = [synth.trace_logits(W.seed, l, E, W.zipf_s, 0, n_rows) for l in range(L)]
+    IDS = [topk_softmax(lg, K) for lg in LG]
+    touched = {l * E + int(e) for l in range(L) for e in IDS[l][0].reshape(-1)}
+    pool = PinnedPool(eff, W.seed, L, E, H, I, W.fmt, flats=touched)
+    eng = None
+    try:
+        cfg = eff.make_config(L, E, K, H, I, W.fmt, W.S, B, 0, W.f_q16, 12)
+        eng = eff.Engine(cfg, pool.ptr, pool.ts)
+        X = [synth.activations(W.seed, l, 0, n_rows, H) for l in range(L)]
+        Xd = [torch.from_numpy(x.view(np.int16)).cuda() for x in X]
+        LGd = [torch.from_numpy(lg).cuda() for lg in LG]
+        OUT = torch.empty((steps, L, B, H), dtype=torch.int16, device="cuda")
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        for t in range(steps):
+            rows = slice(t * B, (t + 1) * B)
+            for l in range(L):
+                eng.decode_layer(l, Xd[l][rows], OUT[t, l], logits=LGd[l][rows], side=side)
+        torch.cuda.synchronize()
+        st = eng.stats()
+        snap = eng.snapshot_tables()
+        out = OUT.cpu().numpy().view(np.uint16)
+
+        cache = SlotCache(L, E, W.S, W.f_q16)
+        hits = fetched = host = 0
+        for t in range(steps):
+            rows = slice(t * B, (t + 1) * B)
+            for l in range(L):
+                flat = [int(e) for e in IDS[l][0][rows].reshape(-1)]
+                cache.ensure(l, flat)
+                res = cache.split()
+                hits += len(set(flat)) - res.m
+                fetched += res.q
+                host += res.host
+        assert list(snap["table"]) == cache.table
+        assert list(snap["owner"]) == cache.owner
+        assert list(snap["usage"]) == cache.usage
+        assert list(snap["recency"]) == cache.recency
+        assert (snap["step"], snap["last_real"]) == (cache.step, cache.last_real)
+        assert (st["hits"], st["fetched"], st["host"]) == (hits, fetched, host)
+        assert fetched > 0 and host > 0 and hits > 0
+
+        for t, l in [(0, 0), (steps - 1, L - 1), (1, 9)]:
+            rows = slice(t * B, (t + 1) * B)
+            ids, w = IDS[l][0][rows], IDS[l][1][rows]
+            for b in (0, 3):
                 x = x_f64(X[l][t * B + b:t * B + b + 1])
                 jobs = [(pool.record(l * E + int(e)), pool.tensor_scales(l * E + int(e)), x) for e in ids[b]]
                 ys = cffn.expert_ffn_batch(jobs, W.fmt, H, I, 16)
