@@ -346,7 +346,7 @@ def decode_kernel_rates(eff, torch, synth, W, pool, layers, threads, batches=(1,
     return res
 
 
-def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16):
+def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16, layers=None, slots=None):
     """End-to-end decode over a workload's whole pool (every layer, its slot count) with speculative
     next-layer requests, for each batch size in W.batches: `warm` untimed then `timed` timed steps of all
     W.L layers, each from an empty cache.  Run at the workload's fetch fraction and at the one the
@@ -354,13 +354,18 @@ def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16):
     executor and fetches fewer of the speculative ones; each with speculative copies as requested, with at
     most two per request copied after the gate/up kernel ([NVMe-8GB] "엔진" item 3), and (workload f) with
     none.  Reports tok/s and the per-layer-call policy counts;
-    the link bytes are the demand and speculative fetches times the record size."""
+    the link bytes are the demand and speculative fetches times the record size.  `layers` and `slots`
+    run the first `layers` layers of the pool with `slots` slots instead (a pool too large to pin)."""
     import numpy as np
-    ptr, ts, R = fill_pool(eff, synth, W.seed, W.L, W.E, W.H, W.I, W.fmt, 16)
-    res = {"workload": "%s (L=%d E=%d K=%d H=%d I=%d NVFP4, S=%d, speculative keep %.2f)" % (
-        W.name, W.L, W.E, W.K, W.H, W.I, W.S, W.spec_keep), "warmup": warm, "steps": timed, "record_bytes": R}
+    L = layers or W.L
+    S = slots or W.S
+    spec_on = W.spec_keep >= 0
+    ptr, ts, R = fill_pool(eff, synth, W.seed, L, W.E, W.H, W.I, W.fmt, 16)
+    res = {"workload": "%s (L=%d E=%d K=%d H=%d I=%d NVFP4, S=%d%s)" % (
+        W.name, L, W.E, W.K, W.H, W.I, S, ", speculative keep %.2f" % W.spec_keep if spec_on else ""),
+        "warmup": warm, "steps": timed, "record_bytes": R}
     side = torch.cuda.Stream()
-    cfg = eff.make_config(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, max(W.batches), 0, W.f_q16, threads)
+    cfg = eff.make_config(L, W.E, W.K, W.H, W.I, W.fmt, S, max(W.batches), 0, W.f_q16, threads)
     eng = eff.Engine(cfg, ptr, ts)
     bw = eng.profile_bandwidth(256)
     eng.close()
@@ -370,29 +375,32 @@ def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16):
         bw["pcie_concurrent"] / 1e9, bw["host_concurrent"] / 1e9, bw["frac_q16"]))
     for B in W.batches:
         n_rows = (warm + timed) * B
-        X = [torch.from_numpy(synth.activations(W.seed, l, 0, n_rows, W.H).view(np.int16)).cuda() for l in range(W.L)]
-        lg_host = [synth.trace_logits(W.seed, l, W.E, W.zipf_s, 0, n_rows) for l in range(W.L)]
+        X = [torch.from_numpy(synth.activations(W.seed, l, 0, n_rows, W.H).view(np.int16)).cuda() for l in range(L)]
+        lg_host = [synth.trace_logits(W.seed, l, W.E, W.zipf_s, 0, n_rows) for l in range(L)]
         LG = [torch.from_numpy(a).cuda() for a in lg_host]
         SP = []
-        for l in range(W.L - 1):   # predictions of layer l+1's sets, made at layer l
+        for l in range(L - 1 if spec_on else 0):   # predictions of layer l+1's sets, made at layer l
             truth = synth.gumbel_topk_sets(lg_host[l + 1], W.K)
             SP.append(torch.from_numpy(np.stack([synth.spec_ids(W.seed, l + 1, W.E, W.zipf_s, r, truth[r], W.spec_keep)
                                                  for r in range(n_rows)]).astype(np.int32).reshape(-1)).cuda())
         out = torch.empty((B, W.H), dtype=torch.int16, device="cuda")
         fp = bw["frac_q16"]
-        for tag, f, budget, gap in (("workload_f", W.f_q16, -1, False), ("workload_f_gap2", W.f_q16, 2, True),
-                                    ("workload_f_nospec", W.f_q16, 0, False), ("profiled_f", fp, -1, False),
-                                    ("profiled_f_gap2", fp, 2, True)):
-            cfg = eff.make_config(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, B, 0, f, threads)
+        variants = ((("workload_f", W.f_q16, -1, False), ("workload_f_gap2", W.f_q16, 2, True),
+                     ("workload_f_nospec", W.f_q16, 0, False), ("profiled_f", fp, -1, False),
+                     ("profiled_f_gap2", fp, 2, True)) if spec_on else
+                    (("workload_f", W.f_q16, -1, False), ("profiled_f", fp, -1, False)))
+        for tag, f, budget, gap in variants:
+            cfg = eff.make_config(L, W.E, W.K, W.H, W.I, W.fmt, S, B, 0, f, threads)
             eng = eff.Engine(cfg, ptr, ts)
             eng.set_speculation(budget, gap)
 
             def run(t0, t1):
                 for t in range(t0, t1):
                     r = slice(t * B, (t + 1) * B)
-                    for l in range(W.L):
+                    for l in range(L):
                         eng.decode_layer(l, X[l][r], out, logits=LG[l][r], side=side,
-                                         spec_ids=SP[l][t * B * W.K:(t + 1) * B * W.K] if l + 1 < W.L else None)
+                                         spec_ids=SP[l][t * B * W.K:(t + 1) * B * W.K] if spec_on and l + 1 < L
+                                         else None)
             run(0, warm)
             torch.cuda.synchronize()
             s0 = eng.stats()
@@ -402,7 +410,7 @@ def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16):
             dt = time.perf_counter() - t0
             s1 = eng.stats()
             eng.close()
-            n = timed * W.L
+            n = timed * L
             per = {k: round((s1[k] - s0[k]) / n, 2) for k in ("hits", "fetched", "host", "spec_fetched")}
             link = (per["fetched"] + per["spec_fetched"]) * R
             res.setdefault("B%d" % B, {})[tag] = {
@@ -531,6 +539,9 @@ def main():
     ap.add_argument("--qwen-next-e2e", action="store_true",
                     help="also run the qwen3.8-flash-next decode end to end over its whole pool (about 70 GB of "
                          "pinned host memory, B = 1, 8, 16)")
+    ap.add_argument("--dsv4-e2e", action="store_true",
+                    help="also run the dsv4-flash decode end to end on 16 of its 43 layers (58 GB pinned; the whole "
+                         "pool does not pin) with the slots scaled to its 20 %%, B = 1 and 4")
     ap.add_argument("--no-graph", action="store_true", help="time eager decode calls only (no HIP graph)")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -545,7 +556,7 @@ def main():
 
     import expert_ffn_serving_amd as eff
     import synth
-    from synth.configs import A3B, DSV4_PREFILL, QWEN_NEXT
+    from synth.configs import A3B, DSV4_DECODE, DSV4_PREFILL, QWEN_NEXT
 
     eff.lib()   # fails loudly if the HIP library is missing
     if not torch.cuda.is_available():
@@ -586,6 +597,11 @@ def main():
     if args.qwen_next_e2e:
         log("decode end to end %s" % QWEN_NEXT.name)
         qe = decode_e2e(eff, torch, synth, QWEN_NEXT, args.threads)
+    de = None
+    if args.dsv4_e2e:
+        log("decode end to end %s (16 layers)" % DSV4_DECODE.name)
+        de = decode_e2e(eff, torch, synth, DSV4_DECODE, args.threads, layers=16,
+                        slots=int(DSV4_DECODE.S * 16 / DSV4_DECODE.L))
     line = {
         "metric": METRIC, "value": round(dec["value"], 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(dec["ms"], 4), "higher_is_better": True, "scaling": "weak",
@@ -599,6 +615,7 @@ def main():
         "prefill": pre,
         "decode_kernels_qwen_next": qn,
         "decode_e2e_qwen_next": qe,
+        "decode_e2e_dsv4_16_layers": de,
     }
     print(json.dumps(line), flush=True)
 
