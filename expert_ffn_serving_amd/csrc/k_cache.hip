@@ -668,7 +668,18 @@ __device__ void plan_wave0(const int32_t* lds_slot, const int32_t* lds_id, const
   }
   const bool first = v >= 0 && (same & ((1ull << tid) - 1)) == 0;
   const uint64_t fm = __ballot(first);
-  const int rank = __popcll(less & fm);  // distinct valid slots below v: units in ascending slot order
+  // units by descending token count, then ascending slot: the workgroups of the busiest experts
+  // start first and the short ones fill in behind them (one entry each: ascending slot)
+  const int c = min(__popcll(same), maxB);
+  uint64_t before = less;
+  if (__ballot(first && c > 1)) {
+    before = 0;
+    for (int q = 0; q < n; ++q) {
+      const int vq = __builtin_amdgcn_readlane(v, q), cq = __builtin_amdgcn_readlane(c, q);
+      before |= (uint64_t)(cq > c || (cq == c && vq < v)) << q;
+    }
+  }
+  const int rank = __popcll(before & fm);
   const int nu = min(__popcll(fm), maxU);
   if (first && rank < maxU) {  // more distinct slots than a layer has experts: not computed
     DecodeUnit& un = plan->unit[rank];
@@ -707,16 +718,24 @@ __device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, const 
     s_sl[p] = (v >= 0 && v < S) ? v : -1;  // slots outside the arena are never read
   }
   lds_sync();
-  for (int p = tid; p < n; p += blockDim.x) {
+  for (int p = tid; p < n; p += blockDim.x) {  // s_first: the slot's entry count at its first entry, else 0
     int v = s_sl[p], first = v >= 0;
     for (int q = 0; q < p && first; ++q) first = s_sl[q] != v;
-    s_first[p] = first;
+    int c = 0;
+    if (first)
+      for (int q = p; q < n; ++q) c += s_sl[q] == v;
+    s_first[p] = first ? min(c, maxB) : 0;
   }
   lds_sync();
   for (int p = tid; p < n; p += blockDim.x) {
     if (!s_first[p]) continue;
-    int v = s_sl[p], rank = 0, cnt = 0;
-    for (int q = 0; q < n; ++q) rank += s_first[q] && s_sl[q] < v;
+    // units by descending token count, then ascending slot (as in plan_wave0)
+    const int v = s_sl[p], c = s_first[p];
+    int rank = 0, cnt = 0;
+    for (int q = 0; q < n; ++q) {
+      const int cq = s_first[q];
+      rank += cq > c || (cq == c && cq > 0 && s_sl[q] < v);
+    }
     if (rank >= maxU) continue;  // more distinct slots than a layer has experts: not computed
     DecodeUnit& un = plan->unit[rank];
     for (int q = 0; q < n && cnt < maxB; ++q)  // a slot appears at most once per token
