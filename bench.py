@@ -352,8 +352,7 @@ def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16, layers=None, sl
     W.L layers, each from an empty cache.  Run at the workload's fetch fraction and at the one the
     bandwidth profile gives on this machine ([FT-deep] §4 ②), which sends part of the misses to the host
     executor and fetches fewer of the speculative ones; each with speculative copies as requested, with at
-    most two per request copied after the gate/up kernel ([NVMe-8GB] "엔진" item 3), and (workload f) with
-    none.  Reports tok/s and the per-layer-call policy counts;
+    most two per request copied after the gate/up kernel ([NVMe-8GB] "엔진" item 3), and with none.  Reports tok/s and the per-layer-call policy counts;
     the link bytes are the demand and speculative fetches times the record size.  `layers` and `slots`
     run the first `layers` layers of the pool with `slots` slots instead (a pool too large to pin)."""
     import numpy as np
@@ -387,7 +386,7 @@ def decode_e2e(eff, torch, synth, W, threads, warm=48, timed=16, layers=None, sl
         fp = bw["frac_q16"]
         variants = ((("workload_f", W.f_q16, -1, False), ("workload_f_gap2", W.f_q16, 2, True),
                      ("workload_f_nospec", W.f_q16, 0, False), ("profiled_f", fp, -1, False),
-                     ("profiled_f_gap2", fp, 2, True)) if spec_on else
+                     ("profiled_f_gap2", fp, 2, True), ("profiled_f_nospec", fp, 0, False)) if spec_on else
                     (("workload_f", W.f_q16, -1, False), ("profiled_f", fp, -1, False)))
         for tag, f, budget, gap in variants:
             cfg = eff.make_config(L, W.E, W.K, W.H, W.I, W.fmt, S, B, 0, f, threads)
