@@ -548,7 +548,7 @@ def main():
                          "the reference for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
