@@ -228,6 +228,24 @@ def run_decode(eff, torch, synth, W, steps, warmup, profile_steps, threads, use_
         bw["pcie_concurrent"] / 1e9, bw["host_concurrent"] / 1e9, bw["pcie_alone"] / 1e9, bw["host_alone"] / 1e9,
         bw["frac_q16"], W.f_q16))
     eng.close()
+    # context only: the same timed steps at the profiled f, from an empty cache after the same warm-up
+    cfg2 = eff.make_config(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, B, 0, bw["frac_q16"], threads)
+    eng2 = eff.Engine(cfg2, ptr, ts if W.fmt == synth.FMT_NVFP4 else None)
+    h = eng2.h   # step() calls through h
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warmup, warmup + steps):
+        step(t)
+    torch.cuda.synchronize()
+    dt2 = time.perf_counter() - t0
+    st2 = eng2.stats()
+    eng2.close()
+    detail["bandwidth_profile"]["tok_s_at_profiled_f"] = round(steps * B / dt2, 2)
+    detail["bandwidth_profile"]["host_share_of_misses_at_profiled_f"] = round(
+        st2["host"] / max(1, st2["host"] + st2["fetched"]), 3)
+    log("  at the profiled f: %.1f tok/s (workload f: %.1f)" % (steps * B / dt2, steps * B / dt))
     del X, LG
     return dict(value=steps * B / dt, ms=dt * 1e3 / steps, roofline=roofline, detail=detail,
                 pool=(ptr, ts, R), B=B)
