@@ -24,6 +24,8 @@ SPECULATIVE = 1
 CFG_TIMING = 1
 CFG_SYNC_HOST = 2
 T_DECODE_GATEUP, T_DECODE_DOWN, T_PREFILL_GATEUP, T_PREFILL_DOWN = 0, 1, 2, 3
+HOST_ISA_SCALAR, HOST_ISA_AVX2, HOST_ISA_AVX512F, HOST_ISA_AVX512_BF16 = 0, 1, 2, 3
+HOST_ISA_NAMES = {0: "scalar", 1: "avx2+fma", 2: "avx512f", 3: "avx512-bf16"}
 
 EFF_OK, EFF_EINVAL, EFF_ENOMEM, EFF_EHIP, EFF_ECAPTURE, EFF_ESTATE, EFF_EDEVICE = 0, -1, -2, -3, -4, -5, -6
 EFF_EREJECTED = -7
@@ -72,6 +74,7 @@ def lib():
             "eff_host_free": (I32, [VP]),
             "eff_route": (I32, [VP, VP, VP, I32, VP, VP, VP]),
             "eff_route_logits": (I32, [VP, VP, I32, VP, VP, VP]),
+            "eff_last_logits": (I32, [VP, VP]),
             "eff_ensure_experts": (I32, [VP, I32, VP, I32, U32, VP]),
             "eff_split_misses": (I32, [VP, VP, VP, VP, VP]),
             "eff_qstar": (I64, [I64, U32]),
@@ -93,6 +96,8 @@ def lib():
             "eff_get_stats": (I32, [VP, VP]),
             "eff_reset_stats": (I32, [VP]),
             "eff_set_flags": (I32, [VP, U32]),
+            "eff_get_host_info": (I32, [VP, VP]),
+            "eff_set_host_isa": (I32, [VP, I32]),
             "eff_slot_ptr": (I32, [VP, I32, VP]),
         }
         for name, (res, args) in sig.items():
@@ -154,6 +159,11 @@ def frac_q16(pcie_bytes_per_s: float, host_bytes_per_s: float) -> int:
     return int(lib().eff_frac_q16(pcie_bytes_per_s, host_bytes_per_s))
 
 
+class HostInfo(ctypes.Structure):
+    _fields_ = [("isa", ctypes.c_int32), ("isa_best", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("pinned", ctypes.c_int32), ("physical_cores", ctypes.c_int32), ("pad", ctypes.c_int32)]
+
+
 class BwProfile(ctypes.Structure):
     _fields_ = [("pcie_alone", ctypes.c_double), ("host_alone", ctypes.c_double),
                 ("pcie_concurrent", ctypes.c_double), ("host_concurrent", ctypes.c_double),
@@ -210,6 +220,16 @@ class Engine:
     # -- decode primitives
     def route(self, x, w_router, ids, w, stream=None):
         _check(lib().eff_route(self.h, _p(x), _p(w_router), x.shape[0], _p(ids), _p(w), _s(stream)))
+
+    def last_logits(self, B: int):
+        """Host copy (float32 [B, E]) of the logits the last eff_route computed."""
+        import numpy as np
+        ptr = ctypes.c_void_p()
+        _check(lib().eff_last_logits(self.h, ctypes.byref(ptr)))
+        torch.cuda.synchronize()
+        out = np.empty((B, self.cfg.num_experts), np.float32)
+        _memcpy_d2h(out.ctypes.data, ptr.value, out.nbytes)
+        return out
 
     def route_logits(self, logits, ids, w, stream=None):
         _check(lib().eff_route_logits(self.h, _p(logits), logits.shape[0], _p(ids), _p(w), _s(stream)))
@@ -307,6 +327,15 @@ class Engine:
         """eff_set_speculation: at most max_fetch records per speculative request (-1: no budget), copied
         right after the control kernel or, with in_gap, after the layer's gate/up kernel."""
         _check(lib().eff_set_speculation(self.h, max_fetch, 1 if in_gap else 0))
+
+    def host_info(self) -> dict:
+        """eff_get_host_info: the host executor's instruction set, threads and pinning."""
+        out = HostInfo()
+        _check(lib().eff_get_host_info(self.h, ctypes.byref(out)))
+        return {k: getattr(out, k) for k, _ in HostInfo._fields_ if k != "pad"}
+
+    def set_host_isa(self, isa: int):
+        _check(lib().eff_set_host_isa(self.h, isa))
 
     def set_fetch_frac(self, frac_q16: int):
         _check(lib().eff_set_fetch_frac(self.h, frac_q16))

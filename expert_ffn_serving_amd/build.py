@@ -23,8 +23,10 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]
 # packed fp32 instructions stay disabled in device code
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
-# host-only translation units (no kernels): no device pass
-HOST_CPU = ["--offload-arch=" + ARCH, "--cuda-host-only", "-mavx2", "-mfma", "-mf16c"]
+# host-only translation units (no kernels): no device pass.  Built for baseline x86-64: the host
+# executor's AVX2 and AVX-512 kernels carry their own target attributes and are chosen at run time,
+# so the library also loads (and runs its scalar kernels) on a CPU without them.
+HOST_CPU = ["--offload-arch=" + ARCH, "--cuda-host-only"]
 
 
 def _hipcc() -> str:

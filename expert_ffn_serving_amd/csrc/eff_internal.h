@@ -16,8 +16,8 @@
 
 namespace eff {
 
-constexpr int kMaxTokens = 32;
-constexpr int kTimedMax = 4096;       // timed launches held before their events are resolved        // decode batch bound
+constexpr int kMaxTokens = 32;       // decode batch bound
+constexpr int kTimedMax = 4096;      // timed launches held before their events are resolved
 constexpr int kMaxTopK = 32;
 constexpr int kMaxEntries = 512;     // entries (B*K) of one decode call
 constexpr int kMaxSlots = 16384;      // single-workgroup victim sort (keys in LDS)
@@ -48,7 +48,13 @@ struct Pending {
   int32_t miss[kMaxEntries];   // unique missing ids ascending
 };
 
-// Fetch list written by the split kernel (device memory and a host-mapped mirror) ----------------
+// Fetch lists written by the split kernel (device memory and a host-mapped mirror): list 0 for real
+// calls, lists 1 and 2 for speculative requests of even and odd layers.  A speculative request made
+// during layer l (for layer l+1) is copied on a side stream that the next layer's expert kernels wait
+// for; the request that reuses its list is made two layers later, after that wait.
+constexpr int kFetchLists = 3;
+__host__ __device__ inline int spec_fetch_list(int layer) { return 1 + (layer & 1); }
+// ------------------------------------------------------------------------------------------------
 struct FetchList {
   int32_t count;
   int32_t err;         // device error word of the ensure/split pair (bit 1: bad id, bit 2: no pending)
@@ -94,7 +100,10 @@ enum { ST_CALLS, ST_HITS, ST_FETCHED, ST_HOST, ST_SPEC_FETCHED, ST_HIST0, ST_COU
 // never run a task of a finished or newer job.
 class ThreadPool {
  public:
-  explicit ThreadPool(int n);
+  // n threads in all: n - 1 workers plus the thread that calls parallel_for.  With `pin`, worker i
+  // is pinned to logical CPU pin[i + 1] (pin[0] is left for the calling thread).
+  explicit ThreadPool(int n, const std::vector<int>* pin = nullptr);
+  int pinned_workers() const { return pinned_.load(); }
   ~ThreadPool();
   // run fn(i) for i in [0, n) on the pool and the calling thread; returns when all are done
   void parallel_for(int n, const std::function<void(int)>& fn);
@@ -113,9 +122,16 @@ class ThreadPool {
   alignas(128) std::atomic<uint64_t> next_{0};
   alignas(128) std::atomic<int> done_{0};
   alignas(128) std::atomic<int> sleepers_{0};
+  std::atomic<int> pinned_{0};
   std::mutex mu_;
   std::condition_variable cv_;
 };
+
+// One logical CPU per physical core the process may use: the affinity mask, SMT siblings
+// dropped (first sibling kept), at most as many as the cgroup's CPU quota allows.
+std::vector<int> physical_core_cpus();
+// Pins the calling thread to one logical CPU; true on success.
+bool pin_this_thread(int cpu);
 
 // Host-share scratch, reused across calls (no allocation per call once grown).
 struct HostScratch {
@@ -147,14 +163,15 @@ struct eff_engine {
   int64_t* d_clock = nullptr;     // {step, last_real}
   float* d_ts = nullptr;          // [L*E*3]
   eff::Pending* d_pending = nullptr;
-  eff::FetchList* d_fetch = nullptr;   // [2]: real, speculative
-  eff::FetchList* h_fetch = nullptr;   // host-mapped mirror [2] (host view)
+  eff::FetchList* d_fetch = nullptr;   // [kFetchLists]: real, speculative (even layer), speculative (odd layer)
+  eff::FetchList* h_fetch = nullptr;   // host-mapped mirror [kFetchLists] (host view)
   eff::FetchList* h_fetch_dev = nullptr;  // the same memory as seen by kernels
   int32_t* d_err = nullptr;            // device error word
   int64_t* d_stats = nullptr;
   bool pending_host = false;           // host-side mirror of Pending::valid
   bool spec_pending_call = false;      // the pending ensure is speculative
   bool spec_split_pending = false;     // a speculative split's fetches not yet copied
+  int spec_list = 1;                   // fetch list of the pending speculative ensure/split
   bool real_split_pending = false;
 
   // decode scratch
@@ -222,7 +239,12 @@ struct eff_engine {
   int32_t* h_pf_ids = nullptr;      // pinned [T*K]
   int32_t* h_pf_meta = nullptr;     // pinned [2E]
   eff::ThreadPool* pool_threads = nullptr;
-  int host_isa = 0;               // host slice kernels: 0 AVX2 + FMA, 1 AVX-512 BF16
+  int host_isa = 0;               // host slice kernels: EFF_HOST_ISA_*
+  int host_isa_max = 0;           // the best the CPU supports
+  std::vector<int> host_cpus;     // pinned: cpus[0] for the engine's worker, cpus[i] for pool worker i - 1
+  bool host_pin = false;
+  std::atomic<bool> worker_pinned{false};
+  int host_physical = 0;
   eff::HostScratch hscratch;
   // kernel timing (EFF_CFG_TIMING): events (start, end) of each of two kernels per call
   struct TimedCall { int kind; hipEvent_t ev[4]; bool has_q; };

@@ -99,13 +99,13 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(dalloc(&e->d_clock, 2));
   EFF_HIP_TRY(dalloc(&e->d_ts, L * E * 3));
   EFF_HIP_TRY(dalloc(&e->d_pending, 1));
-  EFF_HIP_TRY(dalloc(&e->d_fetch, 2));
+  EFF_HIP_TRY(dalloc(&e->d_fetch, kFetchLists));
   EFF_HIP_TRY(dalloc(&e->d_err, 1));
   EFF_HIP_TRY(dalloc(&e->d_seq, 1));
   EFF_HIP_TRY(dalloc(&e->d_stats, ST_COUNT));
   // host-mapped control words are coherent (fine-grained): the host reads them while kernels run
   const unsigned mapped = hipHostMallocMapped | hipHostMallocCoherent;
-  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_fetch, 2 * sizeof(FetchList), mapped));
+  EFF_HIP_TRY(hipHostMalloc((void**)&e->h_fetch, kFetchLists * sizeof(FetchList), mapped));
   EFF_HIP_TRY(hipHostGetDevicePointer((void**)&e->h_fetch_dev, e->h_fetch, 0));
   // decode scratch
   e->maxU = (int)std::min<int64_t>(B * K, E);
@@ -167,7 +167,7 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipMemset(e->d_err, 0, 4));
   EFF_HIP_TRY(hipMemset(e->d_seq, 0, 8));
   EFF_HIP_TRY(hipMemset(e->d_stats, 0, ST_COUNT * 8));
-  std::memset(e->h_fetch, 0, 2 * sizeof(FetchList));
+  std::memset(e->h_fetch, 0, kFetchLists * sizeof(FetchList));
   EFF_HIP_TRY(split_kernel_setup((int)S, (int)E));
   EFF_HIP_TRY(decode_kernels_setup(c.wformat, (int)B, (int)H, (int)I));
   EFF_HIP_TRY(hipDeviceSynchronize());
@@ -242,7 +242,7 @@ static int check_engine(eff_engine* e) {
 }
 
 static int read_device_error(eff_engine* e) {
-  for (int w = 0; w < 2; ++w) {
+  for (int w = 0; w < kFetchLists; ++w) {
     const int err = e->h_fetch[w].err;
     if (err) {
       e->h_fetch[w].err = 0;
@@ -336,6 +336,7 @@ static int wait_call(eff_engine* e, uint64_t seq, hipStream_t cs) {
 // overwritten while the worker lagged, which only a call without host entries can be (a call with
 // host entries holds its stream until h_done): it is skipped.
 static void worker_loop(eff_engine* e) {
+  if (e->host_pin && !e->host_cpus.empty() && pin_this_thread(e->host_cpus[0])) e->worker_pinned.store(true);
   uint64_t next = e->worker_seq.load(std::memory_order_relaxed) + 1, idle = 0;
   auto t_wait = std::chrono::steady_clock::now();
   for (;;) {
@@ -460,15 +461,22 @@ int eff_create(const eff_config* cfg, const void* host_pool, const float* tensor
     return fail(EFF_EINVAL, "host_pool is not mapped into the device address space (use eff_host_alloc)");
   }
   e->pool_dev = (const uint8_t*)pdev;
+  // the host executor: one thread per physical core ([FT-deep] §7), SMT siblings excluded, one core
+  // left to the thread that enqueues the GPU work; each pinned to its core.  An explicit thread count
+  // is pinned the same way when there are enough cores for it.
+  e->host_cpus = physical_core_cpus();
+  e->host_physical = (int)e->host_cpus.size();
   int nth = cfg->host_threads;
-  if (nth == 0) nth = (int)std::max(1u, std::thread::hardware_concurrency());
-  e->pool_threads = new (std::nothrow) ThreadPool(nth);
+  if (nth == 0) nth = std::max(1, e->host_physical - (e->host_physical > 1 ? 1 : 0));
+  e->host_pin = e->host_physical > 0 && nth <= e->host_physical;
+  e->async_host = !(cfg->flags & EFF_CFG_SYNC_HOST);
+  // in the synchronous mode the caller's thread runs its share unpinned; the pool keeps cpus[1..]
+  e->pool_threads = new (std::nothrow) ThreadPool(nth, e->host_pin ? &e->host_cpus : nullptr);
   if (!e->pool_threads) {
     release(e);
     return fail(EFF_ENOMEM, "thread pool");
   }
-  e->host_isa = host_isa_best();
-  e->async_host = !(cfg->flags & EFF_CFG_SYNC_HOST);
+  e->host_isa = e->host_isa_max = host_isa_best();
   if (e->async_host) {
     try {
       e->worker = std::thread(worker_loop, e);
@@ -501,6 +509,13 @@ int eff_route(eff_engine* e, const void* x, const void* w_router, int B, int32_t
   return EFF_OK;
 }
 
+int eff_last_logits(eff_engine* e, const float** logits) {
+  if (int rc = check_engine(e)) return rc;
+  if (!logits) return fail(EFF_EINVAL, "eff_last_logits: logits is NULL");
+  *logits = e->d_logits;
+  return EFF_OK;
+}
+
 int eff_route_logits(eff_engine* e, const float* logits, int B, int32_t* ids, float* w, eff_stream_t stream) {
   if (int rc = check_engine(e)) return rc;
   const int maxB = std::max(e->cfg.max_tokens, e->cfg.max_prefill_tokens);
@@ -515,9 +530,13 @@ int eff_ensure_experts(eff_engine* e, int layer, int32_t* ids_inout, int n, uint
     return fail(EFF_EINVAL, "eff_ensure_experts: bad arguments");
   if (flags & ~(uint32_t)EFF_SPECULATIVE) return fail(EFF_EINVAL, "eff_ensure_experts: unknown flags");
   if (e->pending_host) return fail(EFF_ESTATE, "an ensure is already pending its split");
+  // the fetch list of an earlier split of the same kind is read by eff_copy_missing
+  if ((flags & EFF_SPECULATIVE) ? e->spec_split_pending : e->real_split_pending)
+    return fail(EFF_ESTATE, "the copies of the previous split of this kind have not been issued (eff_copy_missing)");
   EFF_HIP_TRY(launch_ensure(e, layer, ids_inout, n, (flags & EFF_SPECULATIVE) ? 1 : 0, (hipStream_t)stream));
   e->pending_host = true;
   e->spec_pending_call = (flags & EFF_SPECULATIVE) != 0;
+  if (e->spec_pending_call) e->spec_list = spec_fetch_list(layer);
   return EFF_OK;
 }
 
@@ -728,8 +747,8 @@ int eff_rebuild_cache(eff_engine* e, int num_slots, uint64_t max_arena_bytes) {
   e->d_owner = owner_new;
   e->d_usage = usage_new;
   e->cfg.num_slots = num_slots;
-  std::memset(e->h_fetch, 0, 2 * sizeof(FetchList));
-  EFF_HIP_TRY(hipMemset(e->d_fetch, 0, 2 * sizeof(FetchList)));  // no list names an old slot
+  std::memset(e->h_fetch, 0, kFetchLists * sizeof(FetchList));
+  EFF_HIP_TRY(hipMemset(e->d_fetch, 0, kFetchLists * sizeof(FetchList)));  // no list names an old slot
   return EFF_OK;
 }
 
@@ -755,7 +774,7 @@ static int issue_pending_copies(eff_engine* e, hipStream_t cs, hipStream_t ss) {
     e->real_split_pending = false;
   }
   if (e->spec_split_pending) {
-    if (int rc = issue_copies(e, 1, ss)) return rc;
+    if (int rc = issue_copies(e, e->spec_list, ss)) return rc;
     e->spec_split_pending = false;
   }
   EFF_HIP_TRY(hipEventRecord(e->ev_copy, ss));
@@ -840,7 +859,7 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   if (spec && !gap) {
     EFF_HIP_TRY(hipEventRecord(e->ev_ctl, cs));
     EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_ctl, 0));
-    EFF_HIP_TRY(launch_fetch_copy(e, 1, ss));
+    EFF_HIP_TRY(launch_fetch_copy(e, spec_fetch_list(layer + 1), ss));
     EFF_HIP_TRY(hipEventRecord(e->ev_spec, ss));
     e->spec_copy_pending = true;
   }
@@ -852,7 +871,7 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   EFF_HIP_TRY(ffn_err);
   if (gap) {  // the victims are slots this call does not use, so the copy may overlap its down kernel
     EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_gateup, 0));
-    EFF_HIP_TRY(launch_fetch_copy(e, 1, ss));
+    EFF_HIP_TRY(launch_fetch_copy(e, spec_fetch_list(layer + 1), ss));
     EFF_HIP_TRY(hipEventRecord(e->ev_spec, ss));
     e->spec_copy_pending = true;
   }
@@ -1000,6 +1019,31 @@ int eff_get_stats(eff_engine* e, eff_stats* out) {
   out->host_ms = e->host_ns.load() * 1e-6;
   out->wait_ms = e->wait_ns.load() * 1e-6;
   out->host_calls = e->host_calls_a.load();
+  return EFF_OK;
+}
+
+int eff_get_host_info(eff_engine* e, eff_host_info* out) {
+  if (int rc = check_engine(e)) return rc;
+  if (!out) return fail(EFF_EINVAL, "eff_get_host_info: out is NULL");
+  const int threads = e->pool_threads->size();
+  const int pinned = e->pool_threads->pinned_workers() + (e->worker_pinned.load() ? 1 : 0);
+  out->isa = e->host_isa;
+  out->isa_best = e->host_isa_max;
+  out->threads = threads;
+  out->pinned = (e->host_pin && e->async_host && pinned == threads) ? 1 : 0;
+  out->physical_cores = e->host_physical;
+  out->pad = 0;
+  return EFF_OK;
+}
+
+int eff_set_host_isa(eff_engine* e, int isa) {
+  if (int rc = check_engine(e)) return rc;
+  if (isa < EFF_HOST_ISA_SCALAR || isa > e->host_isa_max)
+    return fail(EFF_EINVAL, "eff_set_host_isa: unknown level or one this CPU does not support");
+  if (capturing(nullptr)) return fail(EFF_ECAPTURE, "eff_set_host_isa waits for the host-share worker");
+  drain_worker(e);
+  if (int rc = check_async_error(e)) return rc;
+  e->host_isa = isa;
   return EFF_OK;
 }
 

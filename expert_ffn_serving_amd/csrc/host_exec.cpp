@@ -6,11 +6,16 @@
 // physical core because decode on the host is bound by memory bandwidth
 // ([FT-blog] §三.2).  fp32 accumulation, fixed order per output row.
 #include <immintrin.h>
+#include <pthread.h>
+#include <sched.h>
 
 #include <algorithm>
 #include <chrono>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
+#include <set>
+#include <utility>
 #include <vector>
 
 #include "eff_internal.h"
@@ -62,8 +67,9 @@ inline uint16_t f2bf_rne(float f) {
 // pair of rows).  out[r * nt + j] = tscale * sum_k W[16*sl + r][k] * x_j[k], fp32.
 // AVX2 + FMA: per row, 8-wide fp32 FMAs over the row's 32 inputs of each tile, reduced at the end.
 // The 4 bytes of row r, inputs 8q..8q+7 of a tile are its dword (q*16 + r).
-void slice_avx2(const uint8_t* pay, const uint8_t* sca, int KB, int sl, int fmt, const uint16_t* const* xr,
-                int nrows, int nt, float tscale, float* out) {
+__attribute__((target("avx2,fma"))) void slice_avx2(const uint8_t* pay, const uint8_t* sca, int KB, int sl, int fmt,
+                                                   const uint16_t* const* xr, int nrows, int nt, float tscale,
+                                                   float* out) {
   const __m256i shifts = _mm256_setr_epi32(0, 4, 8, 12, 16, 20, 24, 28);
   const __m256i m15 = _mm256_set1_epi32(15), m7 = _mm256_set1_epi32(7), m8 = _mm256_set1_epi32(8);
   const __m256 eight = _mm256_set1_ps(8.f);
@@ -219,32 +225,162 @@ __attribute__((target("avx512f,avx512bw,avx512bf16"))) void slices_avx512(const 
   }
 }
 
+// AVX-512F (no BF16 dot product): the 16 rows of a tile are the 16 dword lanes of a zmm as above;
+// shifting a row dword right by 4m and masking leaves the code of input 8q+m in each lane, and one
+// vpermps maps the 16 codes to fp32 weights (exact).  Each weight vector meets the broadcast fp32
+// input of its column; the half-tile sums get the (row, group) scales, the tensor scale comes last.
+// Inputs in natural order.
+template <int NM, bool FP4>
+__attribute__((target("avx512f"))) void slices_avx512f(const MatRef* mat, int KB, int sl, const uint16_t* const* xr,
+                                                      int nrows, int nt) {
+  alignas(64) float tab[16];
+  for (int c = 0; c < 16; ++c) tab[c] = FP4 ? tables().e2m1[c] : (float)(c - 8);
+  const __m512 table = _mm512_load_ps(tab);
+  const __m512i m15 = _mm512_set1_epi32(15);
+  __m512 tot[NM][kMaxTokens];
+  for (int mi = 0; mi < NM; ++mi)
+    for (int j = 0; j < nt; ++j) tot[mi][j] = _mm512_setzero_ps();
+  alignas(64) float xf[2 * kMaxTokens][32];
+  for (int kb = 0; kb < KB; ++kb) {
+    const int64_t tile = (int64_t)sl * KB + kb;
+    for (int i = 0; i < nrows; ++i)
+      for (int h = 0; h < 2; ++h) {
+        const __m256i b = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(xr[i] + kb * 32 + 16 * h));
+        _mm512_store_ps(&xf[i][16 * h], _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(b), 16)));
+      }
+    __m512 sc[NM][2];
+    for (int mi = 0; mi < NM; ++mi) {
+      const uint8_t* sp = mat[mi].sca + tile * 32;
+      if (!FP4) {
+        const __m256i b = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(sp));
+        sc[mi][0] = sc[mi][1] = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(b), 16));
+      } else {
+        const __m512 k120 = _mm512_set1_ps(1.329227995784916e36f);  // 2^120, as in the BF16 kernel
+        const __m512i x7f = _mm512_set1_epi32(0x7F), x80 = _mm512_set1_epi32(0x80);
+        for (int h = 0; h < 2; ++h) {
+          const __m512i c = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(sp + 16 * h)));
+          const __m512 m = _mm512_mul_ps(_mm512_castsi512_ps(_mm512_slli_epi32(_mm512_and_si512(c, x7f), 20)), k120);
+          sc[mi][h] = _mm512_castsi512_ps(
+              _mm512_or_si512(_mm512_castps_si512(m), _mm512_slli_epi32(_mm512_and_si512(c, x80), 24)));
+        }
+      }
+    }
+    for (int h = 0; h < 2; ++h) {  // inputs 16h .. 16h+15: dwords q = 2h, 2h+1 of every row
+      __m512 w[NM][16];
+      for (int mi = 0; mi < NM; ++mi)
+        for (int qq = 0; qq < 2; ++qq) {
+          const __m512i d = _mm512_loadu_si512(mat[mi].pay + tile * 256 + 64 * (2 * h + qq));
+          for (int m = 0; m < 8; ++m)
+            w[mi][8 * qq + m] = _mm512_permutexvar_ps(_mm512_and_si512(_mm512_srli_epi32(d, 4 * m), m15), table);
+        }
+      for (int i = 0; i < nrows; ++i) {
+        const int j = i < nt ? i : i - nt;
+        for (int mi = 0; mi < NM; ++mi) {
+          __m512 a = _mm512_mul_ps(w[mi][0], _mm512_set1_ps(xf[i][16 * h]));
+          for (int z = 1; z < 16; ++z) a = _mm512_fmadd_ps(w[mi][z], _mm512_set1_ps(xf[i][16 * h + z]), a);
+          tot[mi][j] = _mm512_fmadd_ps(sc[mi][h], a, tot[mi][j]);
+        }
+      }
+    }
+  }
+  for (int mi = 0; mi < NM; ++mi) {
+    const __m512 ts = _mm512_set1_ps(mat[mi].tscale);
+    for (int j = 0; j < nt; ++j) {
+      alignas(64) float v[16];
+      _mm512_store_ps(v, _mm512_mul_ps(tot[mi][j], ts));
+      for (int r = 0; r < 16; ++r) mat[mi].out[r * nt + j] = v[r];
+    }
+  }
+}
+
+// Scalar: the same sums one row and one input at a time (any x86-64 host).  Per row and token, the
+// half-tile sums get the (row, group) scale, the tensor scale comes last.  Inputs in natural order.
+void slices_scalar(const MatRef* mat, int nm, int fmt, int KB, int sl, const uint16_t* const* xr, int nrows,
+                   int nt) {
+  const Tables& T = tables();
+  const bool fp4 = fmt == EFF_WFMT_NVFP4_G16_E4M3;
+  for (int mi = 0; mi < nm; ++mi)
+    for (int r = 0; r < 16; ++r) {
+      float tot[kMaxTokens];
+      for (int j = 0; j < nt; ++j) tot[j] = 0.f;
+      for (int kb = 0; kb < KB; ++kb) {
+        const int64_t tile = (int64_t)sl * KB + kb;
+        const uint8_t* pay = mat[mi].pay + tile * 256;
+        const uint8_t* sp = mat[mi].sca + tile * 32;
+        for (int h = 0; h < 2; ++h) {
+          float s;
+          if (fp4) {
+            s = T.e4m3[sp[16 * h + r]];
+          } else {
+            uint16_t sb;
+            std::memcpy(&sb, sp + 2 * r, 2);
+            s = bf16f(sb);
+          }
+          float w[16];
+          for (int qq = 0; qq < 2; ++qq) {
+            uint32_t d;
+            std::memcpy(&d, pay + 4 * ((2 * h + qq) * 16 + r), 4);
+            for (int m = 0; m < 8; ++m) {
+              const uint32_t c = (d >> (4 * m)) & 15u;
+              w[8 * qq + m] = fp4 ? T.e2m1[c] : (float)((int)c - 8);
+            }
+          }
+          for (int i = 0; i < nrows; ++i) {
+            const uint16_t* x = xr[i] + kb * 32 + 16 * h;
+            float a = 0.f;
+            for (int z = 0; z < 16; ++z) a = std::fma(w[z], bf16f(x[z]), a);
+            float& t = tot[i < nt ? i : i - nt];
+            t = std::fma(s, a, t);
+          }
+        }
+      }
+      for (int j = 0; j < nt; ++j) mat[mi].out[r * nt + j] = tot[j] * mat[mi].tscale;
+    }
+}
+
 // position of input i in the paired order: inside each group of 8, input e goes to 2*(e%4) + e/4
 inline int pair_pos(int i) { return (i & ~7) | ((i & 3) << 1) | ((i >> 2) & 1); }
 
-// rows 16*sl.. of NM matrices (1 or 2, same shape) against the same input rows: the paired-order
-// AVX-512 kernel (isa 1) or the AVX2 kernel (isa 0, inputs in natural order)
+// rows 16*sl.. of NM matrices (1 or 2, same shape) against the same input rows, with the kernel of
+// the engine's instruction set (only the AVX-512 BF16 kernel takes its inputs in paired order)
 void run_slices(int isa, int fmt, int nm, const MatRef* m, int KB, int sl, const uint16_t* const* xr, int nrows,
                 int nt) {
-  if (isa == 1) {
-    const bool fp4 = fmt == EFF_WFMT_NVFP4_G16_E4M3;
-    if (nm == 2)
-      fp4 ? slices_avx512<2, true>(m, KB, sl, xr, nrows, nt) : slices_avx512<2, false>(m, KB, sl, xr, nrows, nt);
-    else
-      fp4 ? slices_avx512<1, true>(m, KB, sl, xr, nrows, nt) : slices_avx512<1, false>(m, KB, sl, xr, nrows, nt);
-    return;
+  const bool fp4 = fmt == EFF_WFMT_NVFP4_G16_E4M3;
+  switch (isa) {
+    case EFF_HOST_ISA_AVX512_BF16:
+      if (nm == 2)
+        fp4 ? slices_avx512<2, true>(m, KB, sl, xr, nrows, nt) : slices_avx512<2, false>(m, KB, sl, xr, nrows, nt);
+      else
+        fp4 ? slices_avx512<1, true>(m, KB, sl, xr, nrows, nt) : slices_avx512<1, false>(m, KB, sl, xr, nrows, nt);
+      return;
+    case EFF_HOST_ISA_AVX512F:
+      if (nm == 2)
+        fp4 ? slices_avx512f<2, true>(m, KB, sl, xr, nrows, nt) : slices_avx512f<2, false>(m, KB, sl, xr, nrows, nt);
+      else
+        fp4 ? slices_avx512f<1, true>(m, KB, sl, xr, nrows, nt) : slices_avx512f<1, false>(m, KB, sl, xr, nrows, nt);
+      return;
+    case EFF_HOST_ISA_AVX2:
+      for (int mi = 0; mi < nm; ++mi)
+        slice_avx2(m[mi].pay, m[mi].sca, KB, sl, fmt, xr, nrows, nt, m[mi].tscale, m[mi].out);
+      return;
+    default:
+      slices_scalar(m, nm, fmt, KB, sl, xr, nrows, nt);
   }
-  for (int mi = 0; mi < nm; ++mi) slice_avx2(m[mi].pay, m[mi].sca, KB, sl, fmt, xr, nrows, nt, m[mi].tscale, m[mi].out);
 }
 
 }  // namespace
 
+// The best host instruction set of the running CPU: AVX-512 BF16 (with BW and VBMI) ->
+// AVX-512F -> AVX2 + FMA -> scalar ([FT-deep] §7: the host executor picks the best of these at
+// run time).
 int host_isa_best() {
   __builtin_cpu_init();
-  return (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
-          __builtin_cpu_supports("avx512vbmi") && __builtin_cpu_supports("avx512bf16"))
-             ? 1
-             : 0;
+  if (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+      __builtin_cpu_supports("avx512vbmi") && __builtin_cpu_supports("avx512bf16"))
+    return EFF_HOST_ISA_AVX512_BF16;
+  if (__builtin_cpu_supports("avx512f")) return EFF_HOST_ISA_AVX512F;
+  if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma")) return EFF_HOST_ISA_AVX2;
+  return EFF_HOST_ISA_SCALAR;
 }
 
 // Host share of one call: entries with cpu_ids[p] >= 0 get y[p] = W_d (silu(W_g x) * (W_u x)) of
@@ -289,7 +425,7 @@ void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_id
   const int isa = e->host_isa;
   // the token rows as the slice kernel reads them
   const uint16_t* xin = x;
-  if (isa == 1) {
+  if (isa == EFF_HOST_ISA_AVX512_BF16) {
     if (hs.xp.size() < (size_t)B * H) hs.xp.resize((size_t)B * H);
     for (int t = 0; t < B; ++t)
       for (int i = 0; i < H; ++i) hs.xp[(size_t)t * H + pair_pos(i)] = x[(size_t)t * H + i];
@@ -318,7 +454,7 @@ void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_id
     run_slices(isa, c.wformat, 2, m, H / 32, sl, xr, nt, nt);
     uint16_t* ahi = hs.a.data() + (size_t)off[u] * I * 2;
     for (int r = 0; r < 16; ++r) {
-      const int col = isa == 1 ? pair_pos(sl * 16 + r) : sl * 16 + r;
+      const int col = isa == EFF_HOST_ISA_AVX512_BF16 ? pair_pos(sl * 16 + r) : sl * 16 + r;
       for (int j = 0; j < nt; ++j) {
         const float gg = g[r * nt + j], uu = v[r * nt + j];
         const float a = gg / (1.f + std::exp(-gg)) * uu;
@@ -368,9 +504,74 @@ void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_id
   });
 }
 
+// ------------------------------------------------------------------------------- topology
+namespace {
+int read_int(const char* path, int fallback) {
+  FILE* f = std::fopen(path, "r");
+  if (!f) return fallback;
+  int v = fallback;
+  if (std::fscanf(f, "%d", &v) != 1) v = fallback;
+  std::fclose(f);
+  return v;
+}
+
+// CPUs the cgroup's quota allows (cgroup v2 cpu.max, else v1 cfs quota / period); 0 = no limit
+int cgroup_cpu_limit() {
+  if (FILE* f = std::fopen("/sys/fs/cgroup/cpu.max", "r")) {
+    char q[32] = {0};
+    long long period = 0;
+    const int n = std::fscanf(f, "%31s %lld", q, &period);
+    std::fclose(f);
+    if (n == 2 && std::strcmp(q, "max") != 0 && period > 0) {
+      const long long quota = std::atoll(q);
+      if (quota > 0) return (int)std::max(1LL, (quota + period - 1) / period);
+    }
+    return 0;
+  }
+  const int quota = read_int("/sys/fs/cgroup/cpu/cpu.cfs_quota_us", -1);
+  const int period = read_int("/sys/fs/cgroup/cpu/cpu.cfs_period_us", -1);
+  if (quota > 0 && period > 0) return std::max(1, (quota + period - 1) / period);
+  return 0;
+}
+}  // namespace
+
+std::vector<int> physical_core_cpus() {
+  std::vector<int> out;
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  if (sched_getaffinity(0, sizeof(set), &set) != 0) return out;
+  std::set<std::pair<int, int>> seen;  // (package, core)
+  for (int cpu = 0; cpu < CPU_SETSIZE; ++cpu) {
+    if (!CPU_ISSET(cpu, &set)) continue;
+    char path[128];
+    std::snprintf(path, sizeof(path), "/sys/devices/system/cpu/cpu%d/topology/core_id", cpu);
+    const int core = read_int(path, -1 - cpu);  // unknown topology: every CPU its own core
+    std::snprintf(path, sizeof(path), "/sys/devices/system/cpu/cpu%d/topology/physical_package_id", cpu);
+    const int pkg = read_int(path, 0);
+    if (seen.insert({pkg, core}).second) out.push_back(cpu);
+  }
+  const int lim = cgroup_cpu_limit();
+  if (lim > 0 && (int)out.size() > lim) out.resize(lim);
+  return out;
+}
+
+bool pin_this_thread(int cpu) {
+  if (cpu < 0 || cpu >= CPU_SETSIZE) return false;
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  CPU_SET(cpu, &set);
+  return pthread_setaffinity_np(pthread_self(), sizeof(set), &set) == 0;
+}
+
 // ----------------------------------------------------------------------------------- pool
-ThreadPool::ThreadPool(int n) {
-  for (int i = 0; i < n - 1; ++i) workers_.emplace_back([this] { loop(); });
+ThreadPool::ThreadPool(int n, const std::vector<int>* pin) {
+  for (int i = 0; i < n - 1; ++i) {
+    const int cpu = (pin && i + 1 < (int)pin->size()) ? (*pin)[i + 1] : -1;
+    workers_.emplace_back([this, cpu] {
+      if (cpu >= 0 && pin_this_thread(cpu)) pinned_.fetch_add(1);
+      loop();
+    });
+  }
 }
 
 ThreadPool::~ThreadPool() {

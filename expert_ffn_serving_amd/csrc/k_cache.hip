@@ -357,8 +357,11 @@ __device__ void commit_body(const CacheState& c, const CallLds& C, bool stamp_hi
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = C.n, spec = C.spec, m = C.nm, nu = C.nu, qq = C.qq;
   const int64_t s = C.s, base = (int64_t)C.layer * c.E;
-  FetchList* fl = c.fl_dev + (spec ? 1 : 0);
-  FetchList* flh = c.fl_host + (spec ? 1 : 0);
+  // a speculative request for layer l fills list 1 + l % 2, so the copy of the previous request (on
+  // another stream, ordered before the next layer's expert kernels) never reads a list being rewritten
+  const int li = spec ? spec_fetch_list(C.layer) : 0;
+  FetchList* fl = c.fl_dev + li;
+  FetchList* flh = c.fl_host + li;
   if (stamp_hits)
     for (int p = tid; p < n; p += kThreads)
       if (C.first[p] && C.hit[p] >= 0) c.usage[C.hit[p]] = s;  // hit: stamped as used now

@@ -70,6 +70,15 @@ enum {
                             combine kernel waits for it on a host-mapped word) */
 };
 
+/* Instruction sets of the host executor, best first as eff_create picks them ([FT-deep] §7:
+ * AVX-512 BF16 -> AVX-512F -> AVX2 + FMA -> scalar, chosen at run time). */
+enum {
+  EFF_HOST_ISA_SCALAR = 0,
+  EFF_HOST_ISA_AVX2 = 1,       /* AVX2 + FMA */
+  EFF_HOST_ISA_AVX512F = 2,
+  EFF_HOST_ISA_AVX512_BF16 = 3 /* AVX-512 F, BW, VBMI and BF16 */
+};
+
 typedef struct eff_config {
   int32_t num_layers;         /* L */
   int32_t num_experts;        /* E, <= 4096 */
@@ -81,7 +90,9 @@ typedef struct eff_config {
   int32_t max_tokens;         /* decode batch bound B, 1..32 */
   int32_t max_prefill_tokens; /* prefill chunk bound T (0: no prefill) */
   uint32_t fetch_frac_q16;    /* f = B_P/B_H * 65536, 0..65536 */
-  int32_t host_threads;       /* threads of the host executor (0: hardware concurrency) */
+  int32_t host_threads;       /* threads of the host executor; 0: one per physical core the process
+                                 may use, SMT siblings excluded, less one core left to the thread
+                                 that enqueues GPU work, each pinned to its core */
   uint32_t flags;             /* EFF_CFG_* bits */
 } eff_config;
 
@@ -111,6 +122,11 @@ int eff_host_free(void* p);
  * 32,16,...,1.  B <= max_tokens (decode) or <= max_prefill_tokens. */
 int eff_route(eff_engine* e, const void* x, const void* w_router, int B, int32_t* ids, float* w,
               eff_stream_t stream);
+/* Device pointer of the engine-owned fp32 logits [B,E] (row-major) that the last
+ * eff_route, or eff_decode_layer given w_router, computed; the next such call
+ * overwrites them.  Diagnostics: lets a caller compare the fixed summation order
+ * bit for bit.  The pointer stays valid until eff_destroy. */
+int eff_last_logits(eff_engine* e, const float** logits);
 /* Same top-k/softmax from precomputed fp32 logits [B,E] (routing traces). */
 int eff_route_logits(eff_engine* e, const float* logits, int B, int32_t* ids, float* w,
                      eff_stream_t stream);
@@ -120,7 +136,9 @@ int eff_route_logits(eff_engine* e, const float* logits, int B, int32_t* ids, fl
  * the resident slot or -1.  Stamps hits as used at this step; keeps the call
  * pending for eff_split_misses.  flags: EFF_SPECULATIVE for a fetch-only
  * request made one layer early ([NVMe-8GB] "시간이 실제로 소요되는 부분").
- * An id outside [0,E) is reported as EFF_EDEVICE by the next host-waiting call. */
+ * An id outside [0,E) is reported as EFF_EDEVICE by the next host-waiting call.
+ * EFF_ESTATE while an ensure waits for its split, or while the copies of an earlier
+ * split of the same kind (real or speculative) have not been issued by eff_copy_missing. */
 int eff_ensure_experts(eff_engine* e, int layer, int32_t* ids_inout, int n, uint32_t flags,
                        eff_stream_t stream);
 
@@ -286,6 +304,22 @@ int eff_expert_ffn_prefill_layer(eff_engine* e, int layer, const void* x, const 
  * [L*E], clock int64 [2] = {step, last_real}. */
 int eff_snapshot_tables(eff_engine* e, int32_t* table, int32_t* owner, int64_t* usage,
                         int64_t* recency, int64_t* clock);
+
+/* The host executor as eff_create set it up ([FT-deep] §7 hardware requirements: one thread per
+ * physical core, SMT siblings left idle because they only compete for the same load ports). */
+typedef struct eff_host_info {
+  int32_t isa;            /* EFF_HOST_ISA_* in use */
+  int32_t isa_best;       /* the best the CPU supports */
+  int32_t threads;        /* threads that run a host share (pool workers + the engine's worker) */
+  int32_t pinned;         /* 1: each of them is pinned to a physical core of its own */
+  int32_t physical_cores; /* physical cores the process may use (affinity mask, cgroup CPU quota) */
+  int32_t pad;
+} eff_host_info;
+int eff_get_host_info(eff_engine* e, eff_host_info* out);
+/* Selects the host executor's instruction set (EFF_HOST_ISA_*), for example a lower level than the
+ * CPU's best to compare them.  Waits for the host-share worker first; not during graph capture.
+ * EFF_EINVAL for an unknown level or one the CPU does not support. */
+int eff_set_host_isa(eff_engine* e, int isa);
 
 /* Kernel timing slots of eff_stats (filled with EFF_CFG_TIMING). */
 enum { EFF_T_DECODE_GATEUP = 0, EFF_T_DECODE_DOWN = 1, EFF_T_PREFILL_GATEUP = 2, EFF_T_PREFILL_DOWN = 3 };

@@ -1,13 +1,13 @@
 """Text summaries of rocprofv3 output (kernel statistics and PMC counters).
 
-    python3 -m expert_ffn_serving_amd.profile_summary counters DIR
+    python3 profile_summary.py counters DIR
         per-kernel totals of every counter in DIR/**/*counter_collection.csv
-    python3 -m expert_ffn_serving_amd.profile_summary traffic --fetch DIR --write DIR \\
+    python3 profile_summary.py traffic --fetch DIR --write DIR \\
             --kernel k_gateup --copy-bytes 1073741824 --source k_decode.hip [--last N] --out FILE.json
         HBM bytes per dispatch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run.  Each
         counter is scaled by what it reads for the largest plain device-to-device copy in the same
         run (a copy of --copy-bytes bytes reads and writes exactly that many bytes).
-    python3 -m expert_ffn_serving_amd.profile_summary trace DIR --kernel 'k_gateup<0, 1>' --last 2560
+    python3 profile_summary.py trace DIR --kernel 'k_gateup<0, 1>' --last 2560
         average duration of a kernel's dispatches in DIR/**/*kernel_trace.csv, over all of them and
         over the last N by start time (the window a bench times last, e.g. its profiled pass).
 
@@ -23,7 +23,7 @@ import json
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 

@@ -75,6 +75,58 @@ def test_route_ids_bit_exact(eff, H, E, K, B):
         pool.free()
 
 
+@pytest.mark.parametrize("H,E,B", [(2048, 256, 4), (2560, 512, 3), (4096, 256, 5), (512, 64, 2)])
+def test_route_logits_bit_exact(eff, H, E, B):
+    """The fp32 router logits themselves (not only the ids) equal the oracle's fixed-order sums bit for
+    bit at the real hidden sizes, where each lane adds blocks of V = 8 consecutive inputs."""
+    pool = PinnedPool(eff, 5, 1, 1, 64, 64, synth.FMT_INT4)
+    cfg = eff.make_config(1, E, 6, H, 64, 0, 0, B, B, 65536, 2)
+    eng = eff.Engine(cfg, pool.ptr)
+    try:
+        x = synth.activations(17, 0, 0, B, H)
+        wr = synth.router_weights(17, 0, E, H)
+        ids = torch.empty((B, 6), dtype=torch.int32, device="cuda")
+        w = torch.empty((B, 6), dtype=torch.float32, device="cuda")
+        eng.route(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(wr.view(np.int16)).cuda(), ids, w)
+        got = eng.last_logits(B)
+        ref = logits_fixed_order(x, wr)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    finally:
+        eng.close()
+        pool.free()
+
+
+def test_route_logits_order_cases(eff):
+    """The hand-derived order cases of the oracle's router pins, on the GPU: each case is one router
+    row against x = 1, so its logit must equal the case's value exactly."""
+    from tests.test_oracle_router import ORDER_CASES, order_case_inputs
+    pool = PinnedPool(eff, 5, 1, 1, 64, 64, synth.FMT_INT4)
+    try:
+        for H in sorted({c[0] for c in ORDER_CASES}):
+            cases = [c for c in ORDER_CASES if c[0] == H]
+            E = 8
+            wr = np.zeros((E, H), np.uint16)
+            x = None
+            for e, (_, prods, _) in enumerate(cases):
+                x, w1 = order_case_inputs(H, prods)
+                wr[e] = w1[0]
+            cfg = eff.make_config(1, E, 2, H, 64, 0, 0, 1, 1, 65536, 2)
+            eng = eff.Engine(cfg, pool.ptr)
+            try:
+                ids = torch.empty((1, 2), dtype=torch.int32, device="cuda")
+                w = torch.empty((1, 2), dtype=torch.float32, device="cuda")
+                eng.route(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(wr.view(np.int16)).cuda(),
+                          ids, w)
+                got = eng.last_logits(1)[0]
+                for e, (_, _, want) in enumerate(cases):
+                    assert float(got[e]) == want, (H, e, float(got[e]), want)
+                assert np.all(got[len(cases):] == 0)
+            finally:
+                eng.close()
+    finally:
+        pool.free()
+
+
 @pytest.mark.parametrize("E", [256, 512])
 def test_route_logits_traces_and_ties(eff, E):
     pool = PinnedPool(eff, 5, 1, 1, 64, 64, synth.FMT_INT4)

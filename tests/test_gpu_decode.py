@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 import synth  # noqa: E402
 from synth.configs import TINY  # noqa: E402
-from tests.helpers import PinnedPool, assert_close_bf16, make_engine, oracle_engine, rel_l2  # noqa: E402
+from tests.helpers import MAX_ABS, PinnedPool, assert_close_bf16, make_engine, oracle_engine, rel_l2  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -103,13 +103,17 @@ def test_tiny_decode_sync_host(eff, tiny_pool, f):
     assert np.array_equal(a, b)
 
 
-def run_ahead(eff, pool, K, S, f, B, tokens, zipf, seed, spec_keep=-1.0, flags=0):
+def run_ahead(eff, pool, K, S, f, B, tokens, zipf, seed, spec_keep=-1.0, flags=0, spec_budget=None,
+              spec_gap=False):
     """Every layer of every token enqueued before a single synchronize (the host runs ahead of
     the device; host shares and speculative copies are ordered on the device only); all outputs
-    and the final tables against the oracle."""
+    and the final tables against the oracle (with the same speculative budget, if any)."""
     L, E, H = pool.L, pool.E, pool.H
     eng = make_engine(eff, pool, K, S, B, f, flags=flags)
     orc = oracle_engine(pool, K, S, f)
+    if spec_budget is not None or spec_gap:
+        eng.set_speculation(-1 if spec_budget is None else spec_budget, spec_gap)
+        orc.cache.spec_budget = spec_budget
     side = torch.cuda.Stream()
     try:
         xs, lgs, specs, outs = {}, {}, {}, {}
@@ -132,17 +136,43 @@ def run_ahead(eff, pool, K, S, f, B, tokens, zipf, seed, spec_keep=-1.0, flags=0
                 outs[t, l] = torch.empty((B, H), dtype=torch.int16, device="cuda")
                 eng.decode_layer(l, xd, outs[t, l], logits=lg, spec_ids=sp, side=side)
         torch.cuda.synchronize()
+        tot = dict(fetched=0, host=0, spec_fetched=0)
         for t in range(tokens):
             for l in range(L):
                 r = orc.decode_layer(l, xs[t, l], logits=lgs[t, l], spec_next=specs[t, l])
                 assert_close_bf16(outs[t, l].cpu().numpy().view(np.uint16), r["out_bits"],
                                   what="run-ahead t=%d l=%d" % (t, l))
+                tot["fetched"] += r["q"]
+                tot["host"] += r["host"]
+                tot["spec_fetched"] += r["spec"].q if r["spec"] is not None else 0
         snap = eng.snapshot_tables()
         assert list(snap["table"]) == orc.cache.table
+        assert list(snap["owner"]) == orc.cache.owner
         assert list(snap["usage"]) == orc.cache.usage
-        return eng.stats()
+        assert list(snap["recency"]) == orc.cache.recency
+        st = eng.stats()
+        assert {k: st[k] for k in tot} == tot
+        return st
     finally:
         eng.close()
+
+
+@pytest.mark.parametrize("B,budget,gap", [(8, 2, True), (8, 2, False), (16, 2, True), (16, None, True),
+                                          (16, 3, False)])
+def test_decode_run_ahead_speculative_budget_gap(eff, B, budget, gap):
+    """Speculative requests with a budget, copied right after the control kernel or in the gap after
+    the gate/up kernel, every layer enqueued without a host synchronization, so that a layer's
+    speculative copy overlaps the next layer's control kernel: at the qwen3.8-flash-next expert shape
+    (2560 x 640 NVFP4, top-10) with several records per request.  Every output and the final tables
+    against the oracle policy with the same budget."""
+    print("run-ahead speculative: B=%d budget=%s gap=%s" % (B, budget, gap), flush=True)
+    pool = PinnedPool(eff, 31, 4, 64, 2560, 640, synth.FMT_NVFP4)
+    try:
+        st = run_ahead(eff, pool, 10, 3 * B * 10 // 2, 65535, B, 4, 1.2, 31, spec_keep=0.65, spec_budget=budget,
+                       spec_gap=gap)
+        assert st["spec_fetched"] > 0 and st["fetched"] > 0
+    finally:
+        pool.free()
 
 
 @pytest.mark.parametrize("fmt,H,I,E,K,B,S,f,spec", [
@@ -178,6 +208,8 @@ def test_tiny_all_host_and_invariance(eff, tiny_pool):
     (synth.FMT_NVFP4, 4096, 2048, 12, 6, 1, 8, 45875),
     (synth.FMT_NVFP4, 4096, 2048, 12, 6, 4, 20, 65535),
     (synth.FMT_NVFP4, 2560, 640, 24, 10, 16, 60, 65535),
+    (synth.FMT_NVFP4, 2560, 640, 64, 10, 1, 40, 65535),
+    (synth.FMT_NVFP4, 2560, 640, 64, 10, 8, 120, 65535),
 ])
 def test_decode_shapes(eff, fmt, H, I, E, K, B, S, f):
     pool = PinnedPool(eff, 21, 2, E, H, I, fmt)
@@ -252,6 +284,7 @@ def test_expert_ffn_outputs(eff, fmt, H, I):
         refs = expert_ffn_batch(jobs, fmt, H, I, nthreads=16)
         for j, (b, k) in enumerate([(b, k) for b in range(B) for k in range(K)]):
             assert rel_l2(yg[b, k], refs[j][0]) < 2e-3, (b, k)
+            assert float(np.max(np.abs(yg[b, k] - refs[j][0]))) <= MAX_ABS, (b, k)
     finally:
         eng.close()
         pool.free()

@@ -22,7 +22,7 @@ allocations stop near 70 GB, so 16 of its layers are (58 GB, past 32-bit record 
 generator keys each record by its flat id, so they are the full pool's), the rest is allocated but
 never read.  Final tables and totals against the oracle policy, sampled outputs against the oracle.
 Prefill, dsv4-flash (256 NVFP4 experts of 4096 x 2048, top-6, 2201 slots, T = 2048 tokens): two
-layers streamed into the double buffer and the grouped GEMMs, sampled tokens against the oracle."""
+layers streamed into the double buffer and the grouped GEMMs, 64 sampled tokens per layer against the oracle."""
 import numpy as np
 import pytest
 
@@ -254,7 +254,10 @@ def test_prefill_dsv4_full_size(eff):
           flush=True)
     pool = PinnedPool(eff, W.seed, 2, W.E, W.H, W.I, W.fmt)
     try:
-        toks = [0, 1, 63, 64, 511, 1024, 1500, 2046, T - 1]
+        # 64 sampled tokens per layer: the ends, tile edges, and a stride over the chunk
+        fixed = [0, 1, 63, 64, 511, 1024, 1500, 2046, T - 1]
+        toks = sorted(fixed + [t for t in range(5, T, 37) if t not in fixed][:64 - len(fixed)])
+        assert len(toks) == 64
         run_prefill(eff, pool, W.K, W.S, T, [0, 1], W.seed, tokens_checked=toks)
     finally:
         pool.free()

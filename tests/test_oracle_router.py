@@ -51,6 +51,87 @@ def test_order_is_the_documented_one():
     assert float(seq) == 1.0
 
 
+# Order-sensitive products for V > 1.  Each case lists (input index j, product x_j * w_j) with every
+# other product zero; the expected fp32 logit is derived by hand from the documented order (lane l
+# adds j = 64*V*c + V*l + i, blocks c outer, i inner, then the pairwise fold (l, l+o) for o = 32..1)
+# and fp32 round-to-nearest-even.  The alternative orders a plausible mistake would use give the other
+# value named in each comment.  All products are exact: x_j = 1 and w_j is a power of two or 1.
+ORDER_CASES = [
+    # H = 512: V = 8, one block.  Lane 0 adds j = 0..7 in turn: 2^25 + 1 rounds back to 2^25 (spacing 4),
+    # then - 2^25 gives 0.  One input per lane (V = 1) would leave the 1 alone in lane 1: result 1.
+    (512, [(0, 2.0 ** 25), (1, 1.0), (2, -2.0 ** 25)], 0.0),
+    # H = 2048: V = 8, four blocks of 512.  c outer, i inner: lane 0 adds j = 0 (2^24), 1 (+1: the tie
+    # rounds to even, 2^24), then j = 512 (-2^24): 0.  With i outer the cancellation comes first: 1.
+    (2048, [(0, 2.0 ** 24), (1, 1.0), (512, -2.0 ** 24)], 0.0),
+    # H = 2048: the lanes fold (l, l+32) first.  Lane 0 holds 2^25 (j = 0), lane 32 holds -2^25
+    # (j = 256) and lane 1 holds 1 (j = 8): (2^25 - 2^25) + 1 = 1.  Folding (l, l+1) first gives
+    # 2^25 + 1 = 2^25 and then 0; a left-to-right sum of the lanes also gives 0.
+    (2048, [(0, 2.0 ** 25), (256, -2.0 ** 25), (8, 1.0)], 1.0),
+    # H = 2560: V = 8 (2560 = 64 * 8 * 5).  Lane 0 adds j = 0 (2^24), 4 (+1, rounds to 2^24), 7 (-2^24):
+    # 0.  With V = 4 the 1 would sit in lane 1 with -2^24 (exact -16777215): 2^24 - 16777215 = 1.
+    (2560, [(0, 2.0 ** 24), (4, 1.0), (7, -2.0 ** 24)], 0.0),
+    # H = 2560: the last of five blocks (j = 2048) comes after the whole first block: 0 as above; with
+    # the blocks inner the 1 comes after the cancellation: 1.
+    (2560, [(0, 2.0 ** 24), (1, 1.0), (2048, -2.0 ** 24)], 0.0),
+    # H = 4096: V = 8, eight blocks; lanes 16 and 48 cancel at the first fold, lane 0's 1 survives:
+    # lane 0 (j = 0) 1, lane 16 (j = 128) 2^25, lane 48 (j = 384) -2^25, lane 32 (j = 256) 2^-20.
+    # Fold o=32: s0 = 1 + 2^-20, s16 = 0.  o=16: s0 += s16.  Result 1 + 2^-20 (exact).  Folding o=16
+    # first adds 2^25 to 1 (lost), then 2^-20 is lost against 2^25 too: 0 after the cancellation.
+    (4096, [(0, 1.0), (128, 2.0 ** 25), (384, -2.0 ** 25), (256, 2.0 ** -20)], 1.0 + 2.0 ** -20),
+]
+
+
+def order_case_inputs(H, prods):
+    """bf16 bit arrays x [1, H] (ones) and w [1, H] (the products) for one order case."""
+    w = np.zeros(H, np.float64)
+    for j, v in prods:
+        w[j] = v
+    x = F.f64_to_bf16_bits(np.ones(H))[None, :]
+    return x, F.f64_to_bf16_bits(w)[None, :]
+
+
+@pytest.mark.parametrize("case", range(len(ORDER_CASES)))
+def test_order_v_gt_1(case):
+    """The documented order for V > 1 (blocks of V consecutive inputs per lane, blocks outer), against
+    values derived by hand; each case fails under the nearest alternative order."""
+    H, prods, want = ORDER_CASES[case]
+    assert lane_width(H) == 8
+    x, w = order_case_inputs(H, prods)
+    assert float(logits_fixed_order(x, w)[0, 0]) == want
+
+
+def _alt_order_sum(H, prods, V, blocks_outer=True, fold_down=True):
+    """A deliberately different summation order (negative control): V inputs per lane block, blocks
+    outer or inner, lanes folded from o = 32 down or from o = 1 up."""
+    p = np.zeros(H, np.float32)
+    for j, v in prods:
+        p[j] = v
+    R = H // (64 * V)
+    acc = np.zeros(64, np.float32)
+    order = [(c, i) for c in range(R) for i in range(V)] if blocks_outer else \
+        [(c, i) for i in range(V) for c in range(R)]
+    for c, i in order:
+        acc = (acc + p[64 * V * c + V * np.arange(64) + i]).astype(np.float32)
+    offs = [32, 16, 8, 4, 2, 1] if fold_down else [1, 2, 4, 8, 16, 32]
+    for o in offs:
+        if fold_down:
+            acc[:o] = (acc[:o] + acc[o:2 * o]).astype(np.float32)
+        else:   # pairs (2m, 2m+1) first: s[l] += s[l + o] for l a multiple of 2o
+            idx = np.arange(0, 64, 2 * o)
+            acc[idx] = (acc[idx] + acc[idx + o]).astype(np.float32)
+    return float(acc[0])
+
+
+def test_order_cases_fail_under_other_orders():
+    """Negative control: each plausible wrong order (one input per lane, a smaller V, blocks inner,
+    lanes folded from o = 1 up) misses the hand-derived value of at least one case, and the documented
+    order, written this second way, meets all of them."""
+    for H, prods, want in ORDER_CASES:
+        assert _alt_order_sum(H, prods, 8) == want
+    for kw in (dict(V=1), dict(V=4), dict(V=8, blocks_outer=False), dict(V=8, fold_down=False)):
+        assert any(_alt_order_sum(H, prods, **kw) != want for H, prods, want in ORDER_CASES), kw
+
+
 def brute_topk(row, K):
     best = None
     for comb in itertools.combinations(range(len(row)), K):

@@ -5,7 +5,7 @@ import os
 
 import pytest
 
-from expert_ffn_serving_amd import profile_summary as ps
+import profile_summary as ps
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 
