@@ -293,7 +293,6 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
                           int slot_base, bool combine, hipStream_t s);
 hipError_t split_kernel_setup(int S, int E);
 hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I);
-int decode_nt(int maxB);
 int64_t qstar_host(int64_t m, int64_t f);
 // host executor
 void host_ffn(eff_engine* e, int layer, const uint16_t* x, const int32_t* cpu_ids, int B, float* y);

@@ -60,8 +60,15 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------------------- gate / up
 // A matrix is stored as 16-row x 32-input tiles, row slices outer: the 16 rows of slice sl are
-// one contiguous run of (Kd/32) tiles of 256 payload bytes (and 32 scale bytes).  Lane
-// (q = lane/16, r = lane%16) reads the dword at byte lane*4 of a tile: row r, inputs 8q..8q+7.
+// one contiguous run of (Kd/32) tiles of 256 payload bytes (and 32 scale bytes).  Inside a tile,
+// the dword at byte 4*(q*16 + r) holds row r, inputs 8q..8q+7.
+//
+// A wave reads a slice in 1 KiB runs of 4 consecutive tiles, one 16-byte load per lane.  Lane l
+// gets bytes 16l..16l+15 of the run: tile t = l/16 of the run, rows 4g..4g+3 (g = l%4), inputs
+// 8q..8q+7 of the tile (q = (l/4)%4), one dword per row.  Its scales are one aligned word of the
+// tile's scale bytes (NVFP4: the 4 e4m3 bytes of its rows in group q/2; int4: the 4 bf16 of its
+// rows), and the 8 inputs it needs, x[128*run + 8*(l/4) ...], are shared by its 4 rows.  The partial
+// sums of row 4g+j end in the 16 lanes with l%4 = g and are added by a fixed butterfly.
 
 // Copies n bytes (n % 16 == 0, both ends 16-byte aligned) with the whole workgroup, 16 bytes per
 // thread and four loads in flight per thread.
@@ -80,21 +87,40 @@ __device__ inline void wg_copy(const uint8_t* __restrict__ src, uint8_t* __restr
   for (; i < n4; i += kWG) d4[i] = s4[i];
 }
 
-// per-lane scale offset inside a tile's 32 scale bytes
+// the lane's scale word inside a tile's 32 scale bytes (NVFP4: 4 bytes; int4: 8 bytes)
 template <int FMT>
-__device__ inline uint32_t scale_lane_off(int q, int r) {
-  return FMT == EFF_WFMT_INT4_G32_BF16 ? (uint32_t)r * 2u : (uint32_t)((q >> 1) * 16 + r);
+__device__ inline int lane_scale_off(int q, int g) {
+  return FMT == EFF_WFMT_INT4_G32_BF16 ? 8 * g : 16 * (q >> 1) + 4 * g;
 }
-// raw scale bits of one lane (int4: a bf16; NVFP4: an e4m3 byte) and their value
+struct Scales4 {
+  uint32_t a, b;  // NVFP4: a = e4m3 of rows 4g..4g+3 (byte j = row 4g+j); int4: a, b = bf16 pairs
+};
 template <int FMT>
-__device__ inline uint32_t load_scale_raw(const uint8_t* p) {
-  if (FMT == EFF_WFMT_INT4_G32_BF16) return (uint32_t)*reinterpret_cast<const uint16_t*>(p);
-  return (uint32_t)*p;
+__device__ inline Scales4 load_scales4(const uint8_t* p) {
+  Scales4 s;
+  if (FMT == EFF_WFMT_INT4_G32_BF16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    s.a = v.x;
+    s.b = v.y;
+  } else {
+    s.a = *reinterpret_cast<const uint32_t*>(p);
+    s.b = 0;
+  }
+  return s;
 }
 template <int FMT>
-__device__ inline float scale_value(uint32_t raw) {
-  if (FMT == EFF_WFMT_INT4_G32_BF16) return __uint_as_float(raw << 16);
-  return __builtin_amdgcn_cvt_f32_fp8(raw, 0);
+__device__ inline void scale_values(const Scales4& s, float (&v)[4]) {
+  if (FMT == EFF_WFMT_INT4_G32_BF16) {
+    v[0] = bf16_lo(s.a);
+    v[1] = bf16_hi(s.a);
+    v[2] = bf16_lo(s.b);
+    v[3] = bf16_hi(s.b);
+  } else {
+    v[0] = __builtin_amdgcn_cvt_f32_fp8(s.a, 0);
+    v[1] = __builtin_amdgcn_cvt_f32_fp8(s.a, 1);
+    v[2] = __builtin_amdgcn_cvt_f32_fp8(s.a, 2);
+    v[3] = __builtin_amdgcn_cvt_f32_fp8(s.a, 3);
+  }
 }
 
 // 8 bf16 activations -> the 4 pairs that meet the weight pairs of one dword
@@ -111,200 +137,238 @@ __device__ inline void x_pairs(const uint4 v, uint32_t* xw) {
   }
 }
 
-// sum over the 8 inputs of one dword of weights against the paired activations (unscaled)
+// one weight dword (8 inputs of one row) as 4 bf16 pairs that meet the paired activations: int4
+// nibble u becomes bf16(128 + u) (OR-ed under 0x4300), e2m1 is converted exactly
 template <int FMT>
-__device__ inline float dword_dot_bf16(uint32_t d, const uint32_t* xw, float xs) {
-  uint32_t p0, p1, p2, p3;
+__device__ inline void dequant_bf16(uint32_t d, uint32_t (&p)[4]) {
   if (FMT == EFF_WFMT_INT4_G32_BF16) {
-    p0 = (d & 0x000F000Fu) | 0x43004300u;
-    p1 = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
-    p2 = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
-    p3 = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
+    p[0] = (d & 0x000F000Fu) | 0x43004300u;
+    p[1] = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
+    p[2] = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
+    p[3] = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
   } else {
-    p0 = fp4_to_bf16x2<0>(d); p1 = fp4_to_bf16x2<1>(d);
-    p2 = fp4_to_bf16x2<2>(d); p3 = fp4_to_bf16x2<3>(d);
+    p[0] = fp4_to_bf16x2<0>(d); p[1] = fp4_to_bf16x2<1>(d);
+    p[2] = fp4_to_bf16x2<2>(d); p[3] = fp4_to_bf16x2<3>(d);
   }
-  float raw = dot2_bf16(p3, xw[3], dot2_bf16(p2, xw[2], dot2_bf16(p1, xw[1], dot2_bf16(p0, xw[0], 0.f))));
-  if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-136.f, xs, raw);
-  return raw;
 }
 
-// tokens j >= nt (a unit's last chunk holds fewer than NT) are skipped: nt is uniform per workgroup
+// The lane's 4 rows of one matrix in one run against `nt` tokens (paired activations xw, and for
+// int4 the sum of each token's 8 inputs, which takes off the 128 + u encoding and the -8 offset:
+// sum (u - 8) x = sum (128 + u) x - 136 sum x).  Each row's dword is dequantized once for all tokens.
 template <int FMT, int NT>
-__device__ inline void gateup_tile(uint32_t wg, uint32_t wu, uint32_t rg, uint32_t ru, const uint4* xv, int nt,
-                                   float (&acc)[2][NT]) {
-  const float sg = scale_value<FMT>(rg), su = scale_value<FMT>(ru);
+__device__ inline void matrix_run(const uint4 w, const Scales4& rs, const uint32_t (&xw)[NT][4], const float (&xs)[NT],
+                                  int nt, float (&acc)[4][NT]) {
+  float s[4];
+  scale_values<FMT>(rs, s);
+  const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t p[4];
+    dequant_bf16<FMT>(d4[r], p);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (NT > 1 && j >= nt) break;
+      float raw = dot2_bf16(p[3], xw[j][3], dot2_bf16(p[2], xw[j][2], dot2_bf16(p[1], xw[j][1],
+                  dot2_bf16(p[0], xw[j][0], 0.f))));
+      if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-136.f, xs[j], raw);
+      acc[r][j] = fmaf(s[r], raw, acc[r][j]);
+    }
+  }
+}
+
+// the lane's share of one run of one matrix against `nt` tokens (nt uniform per wave, NT > 1 stops there)
+template <int FMT, int NT>
+__device__ inline void run_tokens(const uint4 w, const Scales4& rs, const uint4* xv, int nt, float (&acc)[4][NT]) {
+  uint32_t xw[NT][4];
+  float xs[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     if (NT > 1 && j >= nt) break;
-    uint32_t xw[4];
-    x_pairs<FMT>(xv[j], xw);
-    float xs = 0.f;
+    x_pairs<FMT>(xv[j], xw[j]);
+    xs[j] = 0.f;
     if (FMT == EFF_WFMT_INT4_G32_BF16)
-      xs = dot2_bf16(xw[3], 0x3F803F80u, dot2_bf16(xw[2], 0x3F803F80u,
-                     dot2_bf16(xw[1], 0x3F803F80u, dot2_bf16(xw[0], 0x3F803F80u, 0.f))));
-    acc[0][j] = fmaf(sg, dword_dot_bf16<FMT>(wg, xw, xs), acc[0][j]);
-    acc[1][j] = fmaf(su, dword_dot_bf16<FMT>(wu, xw, xs), acc[1][j]);
+      xs[j] = dot2_bf16(xw[j][3], 0x3F803F80u, dot2_bf16(xw[j][2], 0x3F803F80u,
+                        dot2_bf16(xw[j][1], 0x3F803F80u, dot2_bf16(xw[j][0], 0x3F803F80u, 0.f))));
   }
+  matrix_run<FMT, NT>(w, rs, xw, xs, nt, acc);
 }
 
-// grid: maxU * (I/16) workgroups of 256 threads, one per (plan unit, 16-row slice of I).  Wave w
-// takes tiles w, w+4, ... of the slice (the 4 waves together sweep 1 KiB runs), gate and up at
-// once; everything reduces inside the workgroup, so no workgroup ever waits for another.
-// A unit installed by this call (fetch) first copies its gate and up slices from the pinned host
-// pool into the slot (16-byte loads) and, once its rows are done, a 1/(I/16) share of the down
-// matrix: the whole record crosses the link inside this kernel, and k_down finds it resident.
-template <int FMT, int NT>
-__global__ void __launch_bounds__(kWG)
+// adds v over the 16 lanes with the same l % 4 (bits 2..5 of the lane id) in a fixed order
+__device__ inline float sum16(float v) {
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// grid: maxU * (I/16) * P / 2 workgroups of 256 threads, one per (plan unit, group of 2/P consecutive
+// 16-row slices of I).  A slice takes 2P waves: P for its gate rows and P for its up rows, each wave
+// every P-th run of its matrix; everything reduces inside the workgroup (the SwiGLU meets gate and
+// up in LDS), so no workgroup ever waits for another.  A unit installed by this call (fetch) first
+// copies its workgroup's gate and up slices from the pinned host pool into the slot (16-byte loads)
+// and, once its rows are done, the same share of the down matrix: the whole record crosses the link
+// inside this kernel, and k_down finds it resident.
+template <int FMT, int NT, int P>
+__global__ void __launch_bounds__(kWG, (FMT == EFF_WFMT_NVFP4_G16_E4M3 || NT < 8) ? 3 : 2)
 k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
          const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H,
-         int I, int K, int maxB, uint16_t* __restrict__ a16, float2* __restrict__ ag) {
-  extern __shared__ uint4 s_x[];  // NT > 1: [NT][H/8], the token rows of the current chunk
-  __shared__ float s_red[4][2][16][NT];
-  const int NS = I / 16, KB = H / 32;
-  const int u = blockIdx.x / NS, sl = blockIdx.x % NS;
+         int I, int K, int maxB, int nch, uint16_t* __restrict__ a16, float2* __restrict__ ag) {
+  static_assert(P == 1 || P == 2, "1 or 2 waves per matrix of a slice");
+  constexpr int SPW = 2 / P;                      // slices per workgroup
+  constexpr int UNR = NT == 1 ? 4 : NT == 2 ? 8 : NT == 4 ? 6 : 4;  // runs in flight per wave
+  extern __shared__ uint4 s_x[];                  // NT > 1: [NT][H/8], the token rows of the current chunk
+  __shared__ float s_red[4][16][NT];
+  const int NS = I / 16, NG = NS / SPW, KB = H / 32, NRF = KB / 4;
+  const int u = blockIdx.x / (NG * nch), ch = (blockIdx.x / NG) % nch, sgp = blockIdx.x % NG;
   const DecodeUnit* un = &plan->unit[u];
   const int cnt = un->count;
-  if (cnt <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  // A resident unit's token chunks run in workgroups of their own (chunk ch: tokens ch*NT ..), so the
+  // busiest experts do not run their chunks one after the other.  A unit installed by this call is
+  // copied by its chunk-0 workgroups, which then take every chunk themselves.
+  const int c_begin = un->fetch ? 0 : ch * NT;
+  const int c_end = (un->fetch || ch == nch - 1) ? cnt : min(cnt, (ch + 1) * NT);
+  if (c_begin >= c_end || (un->fetch && ch > 0)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ss = wave / (2 * P), mat = (wave / P) & 1, wp = wave % P, sl = sgp * SPW + ss;
+  const int t4 = lane >> 4, g = lane & 3, q = (lane >> 2) & 3;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
   uint8_t* rec = arena + (int64_t)un->slot * R;
   if (un->fetch) {
     // installed by this call: copy this workgroup's gate and up slices (payload and scales) from
     // the pool into the slot, then read them back like any resident record
     const uint8_t* src = pool + (int64_t)un->flat * R;
-    const int64_t po = (int64_t)sl * KB * 256, so = 3 * pay + (int64_t)sl * KB * 32;
-    wg_copy(src + po, rec + po, (int64_t)KB * 256);
-    wg_copy(src + pay + po, rec + pay + po, (int64_t)KB * 256);
-    wg_copy(src + so, rec + so, (int64_t)KB * 32);
-    wg_copy(src + sca + so, rec + sca + so, (int64_t)KB * 32);
+    const int64_t po = (int64_t)sgp * SPW * KB * 256, so = 3 * pay + (int64_t)sgp * SPW * KB * 32;
+    wg_copy(src + po, rec + po, (int64_t)SPW * KB * 256);
+    wg_copy(src + pay + po, rec + pay + po, (int64_t)SPW * KB * 256);
+    wg_copy(src + so, rec + so, (int64_t)SPW * KB * 32);
+    wg_copy(src + sca + so, rec + sca + so, (int64_t)SPW * KB * 32);
     __syncthreads();
   }
-  const uint8_t* gp = rec + (int64_t)sl * KB * 256 + lane * 4;
-  const uint8_t* up = gp + pay;
-  const uint8_t* gs = rec + 3 * pay + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
-  const uint8_t* us = gs + sca;
+  // run r of the wave's matrix slice: payload at +r*1024 (+16 lane), the lane's scale word at +(4r + t4)*32 + off
+  const uint8_t* wp8 = rec + mat * pay + (int64_t)sl * KB * 256 + lane * 16;
+  const uint8_t* sp8 = rec + 3 * pay + mat * sca + (int64_t)sl * KB * 32 + t4 * 32 + lane_scale_off<FMT>(q, g);
+  const int xo = 8 * (lane >> 2);           // the lane's inputs in a run: 128 r + xo .. +7
+  const bool tail = (KB & 3) != 0;          // a last run of 1..3 tiles (H % 128 != 0)
+  const bool tail_lane = 4 * NRF + t4 < KB; // the lane's tile exists in that run
   const int H8 = H / 8;
-  for (int c0 = 0; c0 < cnt; c0 += NT) {
-    const int nt = min(NT, cnt - c0);
-    float acc[2][NT];
+  for (int c0 = c_begin; c0 < c_end; c0 += NT) {
+    const int nt = min(NT, c_end - c0);
+    float acc[4][NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[0][j] = acc[1][j] = 0.f;
-    if constexpr (NT == 1) {
-      // one token: its activations ride with the weight loads, straight from global memory (an
-      // LDS stage and its barrier cost more than they free at this width)
-      constexpr int UNR = 8;  // tiles in flight per wave
-      const uint16_t* xt = x + q * 8 + (int64_t)(un->entry[c0] / K) * H;
-      int kb = wave;
-      for (; kb + 4 * (UNR - 1) < KB; kb += 4 * UNR) {  // full rounds: every load first
-        uint32_t wg[UNR], wu[UNR], rg[UNR], ru[UNR];
-        uint4 xv[UNR][1];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int z = 0; z < UNR; ++z) {
-          const int k = kb + 4 * z;
-          wg[z] = *reinterpret_cast<const uint32_t*>(gp + k * 256);
-          wu[z] = *reinterpret_cast<const uint32_t*>(up + k * 256);
-          rg[z] = load_scale_raw<FMT>(gs + k * 32);
-          ru[z] = load_scale_raw<FMT>(us + k * 32);
-          xv[z][0] = *reinterpret_cast<const uint4*>(xt + k * 32);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // every load of the round is in flight before any use
-#pragma unroll
-        for (int z = 0; z < UNR; ++z) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], 1, acc);
-      }
-      if (kb < KB) {  // the last, partial round (H / 32 not a multiple of 4 * UNR): its loads together too
-        uint32_t wg[UNR], wu[UNR], rg[UNR], ru[UNR];
-        uint4 xv[UNR][1];
-#pragma unroll
-        for (int z = 0; z < UNR; ++z) {
-          const int k = kb + 4 * z;
-          const bool in = k < KB;  // uniform per wave
-          wg[z] = in ? *reinterpret_cast<const uint32_t*>(gp + k * 256) : 0u;
-          wu[z] = in ? *reinterpret_cast<const uint32_t*>(up + k * 256) : 0u;
-          rg[z] = in ? load_scale_raw<FMT>(gs + k * 32) : 0u;
-          ru[z] = in ? load_scale_raw<FMT>(us + k * 32) : 0u;
-          xv[z][0] = in ? *reinterpret_cast<const uint4*>(xt + k * 32) : make_uint4(0, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int z = 0; z < UNR; ++z)
-          if (kb + 4 * z < KB) gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv[z], 1, acc);
-      }
-    } else {
-      // several tokens: the first round of weight loads, then the chunk's token rows into LDS (the
-      // weights do not wait for them); the registers then hold weights only
-      constexpr int UNR = NT >= 4 ? 4 : 8;  // tiles in flight per wave
-      uint32_t wg[UNR], wu[UNR], rg[UNR], ru[UNR];
-      int kb = wave;
-#pragma unroll
-      for (int z = 0; z < UNR; ++z) {
-        const int k = kb + 4 * z;
-        const bool in = k < KB;
-        wg[z] = in ? *reinterpret_cast<const uint32_t*>(gp + k * 256) : 0u;
-        wu[z] = in ? *reinterpret_cast<const uint32_t*>(up + k * 256) : 0u;
-        rg[z] = in ? load_scale_raw<FMT>(gs + k * 32) : 0u;
-        ru[z] = in ? load_scale_raw<FMT>(us + k * 32) : 0u;
-      }
-      for (int i = tid; i < nt * H8; i += kWG) {
-        const int j = i / H8, g = i % H8;
-        s_x[i] = *reinterpret_cast<const uint4*>(x + (int64_t)(un->entry[c0 + j] / K) * H + g * 8);
-      }
-      __syncthreads();
-      for (;;) {
-#pragma unroll
-        for (int z = 0; z < UNR; ++z) {
-          const int k = kb + 4 * z;
-          if (k < KB) {  // uniform per wave
-            uint4 xv[NT];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) xv[j] = j < nt ? s_x[j * H8 + k * 4 + q] : make_uint4(0, 0, 0, 0);  // read only below nt
-            gateup_tile<FMT, NT>(wg[z], wu[z], rg[z], ru[z], xv, nt, acc);
-          }
-        }
-        kb += 4 * UNR;
-        if (kb >= KB) break;
-#pragma unroll
-        for (int z = 0; z < UNR; ++z) {  // the next round
-          const int k = kb + 4 * z;
-          const bool in = k < KB;
-          wg[z] = in ? *reinterpret_cast<const uint32_t*>(gp + k * 256) : 0u;
-          wu[z] = in ? *reinterpret_cast<const uint32_t*>(up + k * 256) : 0u;
-          rg[z] = in ? load_scale_raw<FMT>(gs + k * 32) : 0u;
-          ru[z] = in ? load_scale_raw<FMT>(us + k * 32) : 0u;
-        }
-      }
-    }
-    // reduce over q (lanes r, r+16, r+32, r+48), then over the 4 waves in order
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int j = 0; j < NT; ++j) acc[r][j] = 0.f;
+    // A rolling pipeline over the wave's runs (every P-th run of its matrix slice): UNR register slots,
+    // each refilled with the run UNR ahead as soon as it has been used, so UNR runs stay in flight.
+    uint4 wv[UNR], xg[NT == 1 ? UNR : 1];
+    Scales4 rs[UNR];
+    const uint16_t* xt = x + (int64_t)(un->entry[c0] / K) * H + xo;  // NT == 1: the token's row
+    // NT > 1: the chunk's token rows go to LDS.  Their loads are issued first and the weights' after
+    // them, so the stores below wait for the rows only while the first weights are still in flight.
+    uint4 xs[NT > 1 ? NT : 1][2];
+    if constexpr (NT > 1) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        float v = acc[m][j];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[m][j] = v;
+        if (j < nt) {
+          const uint16_t* row = x + (int64_t)(__builtin_amdgcn_readfirstlane(un->entry[c0 + j]) / K) * H;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = tid + h * kWG;
+            if (c < H8) xs[j][h] = *reinterpret_cast<const uint4*>(row + c * 8);
+          }
+        }
       }
-    if (lane < 16) {
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+    for (int z = 0; z < UNR; ++z) {
+      const int r = wp + P * z;
+      if (r < NRF) {  // uniform
+        wv[z] = *reinterpret_cast<const uint4*>(wp8 + (int64_t)r * 1024);
+        rs[z] = load_scales4<FMT>(sp8 + r * 128);
+        if constexpr (NT == 1) xg[z] = *reinterpret_cast<const uint4*>(xt + r * 128);
+      }
+    }
+    if constexpr (NT > 1) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) s_red[wave][m][r][j] = acc[m][j];
+      for (int j = 0; j < NT; ++j) {
+        if (j < nt) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = tid + h * kWG;
+            if (c < H8) s_x[j * H8 + c] = xs[j][h];
+          }
+        }
+      }
+      __syncthreads();
+    }
+    for (int r0 = wp; r0 < NRF; r0 += P * UNR) {
+#pragma unroll
+      for (int z = 0; z < UNR; ++z) {
+        const int r = r0 + P * z;
+        if (r < NRF) {  // uniform
+          if constexpr (NT == 1) {
+            run_tokens<FMT, NT>(wv[z], rs[z], &xg[z], 1, acc);
+          } else {
+            uint4 xv[NT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) xv[j] = j < nt ? s_x[j * H8 + r * 16 + (lane >> 2)] : make_uint4(0, 0, 0, 0);
+            run_tokens<FMT, NT>(wv[z], rs[z], xv, nt, acc);
+          }
+          const int rn = r + P * UNR;
+          if (rn < NRF) {
+            wv[z] = *reinterpret_cast<const uint4*>(wp8 + (int64_t)rn * 1024);
+            rs[z] = load_scales4<FMT>(sp8 + rn * 128);
+            if constexpr (NT == 1) xg[z] = *reinterpret_cast<const uint4*>(xt + rn * 128);
+          }
+        }
+      }
+    }
+    if (tail && wp == NRF % P && tail_lane) {  // the last, partial run
+      const int r = NRF;
+      const uint4 w1 = *reinterpret_cast<const uint4*>(wp8 + (int64_t)r * 1024);
+      const Scales4 s1 = load_scales4<FMT>(sp8 + r * 128);
+      uint4 xv[NT];
+      if constexpr (NT == 1) {
+        xv[0] = *reinterpret_cast<const uint4*>(xt + r * 128);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) xv[j] = j < nt ? s_x[j * H8 + r * 16 + (lane >> 2)] : make_uint4(0, 0, 0, 0);
+      }
+      run_tokens<FMT, NT>(w1, s1, xv, NT == 1 ? 1 : nt, acc);
+    }
+    // rows 4g+r: the 16 lanes with the same g, then the matrix's waves in order (through LDS)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        if (NT == 1 || j < nt) acc[r][j] = sum16(acc[r][j]);
+    if (lane < 4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) s_red[wave][4 * lane + r][j] = acc[r][j];
     }
     __syncthreads();
-    if (tid < 16 * nt) {  // 16 consecutive lanes per token: j = tid / 16, row = tid % 16
-      const int j = tid >> 4, row = tid & 15;
-      float g = s_red[0][0][row][j] + s_red[1][0][row][j];
-      g += s_red[2][0][row][j];
-      g += s_red[3][0][row][j];
-      float v = s_red[0][1][row][j] + s_red[1][1][row][j];
-      v += s_red[2][1][row][j];
-      v += s_red[3][1][row][j];
-      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
-        g *= ts[(int64_t)un->flat * 3 + 0];
-        v *= ts[(int64_t)un->flat * 3 + 1];
+    // 16 consecutive lanes per (slice, token), row = idx % 16; a whole 16-lane group is in or out of
+    // each pass (kWG and the total are multiples of 16), so the group reductions below see all its rows
+    for (int idx = tid; idx < SPW * 16 * nt; idx += kWG) {
+      const int s2 = idx / (16 * nt), j = (idx / 16) % nt, row = idx & 15;
+      const int wg0 = s2 * 2 * P, wu0 = wg0 + P;   // the slice's gate waves, then its up waves
+      float gv = s_red[wg0][row][j], uv = s_red[wu0][row][j];
+#pragma unroll
+      for (int w2 = 1; w2 < P; ++w2) {
+        gv += s_red[wg0 + w2][row][j];
+        uv += s_red[wu0 + w2][row][j];
       }
-      const float a = silu(g) * v;
+      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
+        gv *= ts[(int64_t)un->flat * 3 + 0];
+        uv *= ts[(int64_t)un->flat * 3 + 1];
+      }
+      const float a = silu(gv) * uv;
       // the slice's power-of-two scale: max |a| over its 16 rows lands in [2^14, 2^15)
       float mx = fabsf(a);
       mx = fmaxf(mx, __shfl_xor(mx, 8));
@@ -318,137 +382,187 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
         sh = min(15 - ex, 100);
       }
       const _Float16 h = (_Float16)ldexpf(a, sh);
-      float gs = (float)h;  // sum of the 8-group (rows 8*(row/8) ..), int4 only
-      gs += __shfl_xor(gs, 4);
-      gs += __shfl_xor(gs, 2);
-      gs += __shfl_xor(gs, 1);
+      float gsum = (float)h;  // sum of the 8-group (rows 8*(row/8) ..), int4 only
+      gsum += __shfl_xor(gsum, 4);
+      gsum += __shfl_xor(gsum, 2);
+      gsum += __shfl_xor(gsum, 1);
       // int4: the pairs (a_m, a_m+4) of each 8-group meet the nibble pairs of a weight dword
       const int pos = FMT == EFF_WFMT_INT4_G32_BF16 ? (row & 8) | ((row & 3) << 1) | ((row >> 2) & 1) : row;
+      const int slice = sgp * SPW + s2;
       const int64_t tok = (int64_t)u * maxB + c0 + j;
-      a16[tok * I + sl * 16 + pos] = __builtin_bit_cast(uint16_t, h);
-      if ((row & 7) == 0) ag[tok * (I / 8) + sl * 2 + (row >> 3)] = make_float2(ldexpf(1.f, -sh), gs);
+      a16[tok * I + slice * 16 + pos] = __builtin_bit_cast(uint16_t, h);
+      if ((row & 7) == 0) ag[tok * (I / 8) + slice * 2 + (row >> 3)] = make_float2(ldexpf(1.f, -sh), gsum);
     }
     __syncthreads();
   }
   if (un->fetch) {  // this workgroup's share of the down payload and scales
     const uint8_t* src = pool + (int64_t)un->flat * R;
-    const int64_t dpo = 2 * pay + (int64_t)sl * (pay / NS), dso = 3 * pay + 2 * sca + (int64_t)sl * (sca / NS);
-    wg_copy(src + dpo, rec + dpo, pay / NS);
-    wg_copy(src + dso, rec + dso, sca / NS);
+    const int64_t dpo = 2 * pay + (int64_t)sgp * (pay / NG), dso = 3 * pay + 2 * sca + (int64_t)sgp * (sca / NG);
+    wg_copy(src + dpo, rec + dpo, pay / NG);
+    wg_copy(src + dso, rec + dso, sca / NG);
   }
 }
 
 // ---------------------------------------------------------------------------- down
+// The lane's share of one run of the down matrix against `nt` tokens: its 8 inputs of the SwiGLU
+// output are fp16 (already scaled per (token, 16-row slice of I) by k_gateup; int4 pairs them like
+// the nibbles), with that 8-group's (2^-shift, sum) pair.
 template <int FMT, int NT>
-__device__ inline void down_tile(uint32_t d, uint32_t rd, const uint4* s_a4, const float2* s_ag, int kb, int q,
-                                 int nt, int I8, float (&acc)[NT]) {
-  const float sd = scale_value<FMT>(rd);
-  uint32_t p0, p1, p2, p3;
-  if (FMT == EFF_WFMT_INT4_G32_BF16) {
-    p0 = (d & 0x000F000Fu) | 0x64006400u;
-    p1 = ((d >> 4) & 0x000F000Fu) | 0x64006400u;
-    p2 = ((d >> 8) & 0x000F000Fu) | 0x64006400u;
-    p3 = ((d >> 12) & 0x000F000Fu) | 0x64006400u;
-  } else {
-    p0 = fp4_to_f16x2<0>(d); p1 = fp4_to_f16x2<1>(d);
-    p2 = fp4_to_f16x2<2>(d); p3 = fp4_to_f16x2<3>(d);
+__device__ inline void down_run(const uint4 wd, const Scales4& rd, const uint4* s_a4, const float2* s_ag, int idx,
+                                int nt, int I8, float (&acc)[4][NT]) {
+  float sd[4];
+  scale_values<FMT>(rd, sd);
+  const uint32_t d4[4] = {wd.x, wd.y, wd.z, wd.w};
+  uint32_t p[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t d = d4[r];
+    if (FMT == EFF_WFMT_INT4_G32_BF16) {
+      p[r][0] = (d & 0x000F000Fu) | 0x64006400u;
+      p[r][1] = ((d >> 4) & 0x000F000Fu) | 0x64006400u;
+      p[r][2] = ((d >> 8) & 0x000F000Fu) | 0x64006400u;
+      p[r][3] = ((d >> 12) & 0x000F000Fu) | 0x64006400u;
+    } else {
+      p[r][0] = fp4_to_f16x2<0>(d); p[r][1] = fp4_to_f16x2<1>(d);
+      p[r][2] = fp4_to_f16x2<2>(d); p[r][3] = fp4_to_f16x2<3>(d);
+    }
   }
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    if (j < nt) {
-      const uint4 av = s_a4[j * I8 + kb * 4 + q];
-      const float2 sg = s_ag[j * I8 + kb * 4 + q];  // (2^-shift of the slice, sum of the 8-group)
-      float raw = dot2_f16(p3, av.w, dot2_f16(p2, av.z, dot2_f16(p1, av.y, dot2_f16(p0, av.x, 0.f))));
+    if (NT > 1 && j >= nt) break;
+    const uint4 av = s_a4[j * I8 + idx];
+    const float2 sg = s_ag[j * I8 + idx];  // (2^-shift of the slice, sum of the 8-group)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float raw = dot2_f16(p[r][3], av.w, dot2_f16(p[r][2], av.z, dot2_f16(p[r][1], av.y, dot2_f16(p[r][0], av.x, 0.f))));
       if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-1032.f, sg.y, raw);
-      acc[j] = fmaf(sd, raw * sg.x, acc[j]);
+      acc[r][j] = fmaf(sd[r], raw * sg.x, acc[r][j]);
     }
   }
 }
 
-// grid: maxU * (H/(16*RS)) workgroups, one per (plan unit, RS 16-row slices of H); 4/RS waves
-// share a slice.  The unit's SwiGLU activations, already fp16 from k_gateup, are copied into LDS
-// with their per-group scales and sums before the sweep, once for the RS slices.
-template <int FMT, int NT, int RS>
+// grid: maxU * (H/16) / (4/WPS) workgroups, one per (plan unit, group of 4/WPS consecutive 16-row
+// slices of H); WPS waves share a slice.  The unit's SwiGLU activations, already fp16 from k_gateup,
+// are copied into LDS with their per-group scales and sums once for the workgroup's slices.
+template <int FMT, int NT, int WPS>
 __global__ void __launch_bounds__(kWG)
 k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
        const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ a16,
-       const float2* __restrict__ ag, int H, int I, int maxB, float* __restrict__ y) {
-  extern __shared__ uint4 s_a4[];            // [NT][I/8] groups of 8 fp16, then [NT][I/8] float2
+       const float2* __restrict__ ag, int H, int I, int maxB, int nch, float* __restrict__ y) {
+  static_assert(WPS == 1 || WPS == 2 || WPS == 4, "1, 2 or 4 waves per slice");
+  constexpr int SPW = 4 / WPS;
+  constexpr int UNR = NT <= 2 ? 8 : 6;            // runs in flight per wave
+  extern __shared__ uint4 s_a4[];               // [NT][I/8] groups of 8 fp16, then [NT][I/8] float2
   __shared__ float s_red[4][16][NT];
-  constexpr int UNR = NT >= 4 ? 4 : 8;  // tiles in flight per wave
-  constexpr int NW = 4 / RS;            // waves per slice
-  static_assert(RS == 1 || RS == 2 || RS == 4, "1, 2 or 4 slices per workgroup");
-  const int NG = H / (16 * RS), KB = I / 32, I8 = I / 8;
-  const int u = blockIdx.x / NG, sg = blockIdx.x % NG;
+  const int NSH = H / 16, NG = NSH / SPW, KB = I / 32, NRF = KB / 4, I8 = I / 8;
+  const int u = blockIdx.x / (NG * nch), ch = (blockIdx.x / NG) % nch, sgp = blockIdx.x % NG;
   const DecodeUnit* un = &plan->unit[u];
   const int cnt = un->count;
-  if (cnt <= 0) return;
+  // with nch > 1 each token chunk of a unit in workgroups of its own (every record is resident by now),
+  // the last taking what is left
+  const int c_begin = ch * NT, c_end = ch == nch - 1 ? cnt : min(cnt, (ch + 1) * NT);
+  if (c_begin >= c_end) return;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
-  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ss = wave % RS, sw = wave / RS, sl = sg * RS + ss;  // this wave's slice, its place in it
+  const int ss = wave / WPS, wp = wave % WPS, sl = sgp * SPW + ss;
+  const int t4 = lane >> 4, g = lane & 3, q = (lane >> 2) & 3;
   // a record installed by this call was copied whole by k_gateup, the previous kernel on the stream
   const uint8_t* rec = arena + (int64_t)un->slot * R;
   float2* s_ag = reinterpret_cast<float2*>(s_a4 + NT * I8);
-  const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 4;
-  const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + scale_lane_off<FMT>(q, r);
+  const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 16;
+  const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + t4 * 32 + lane_scale_off<FMT>(q, g);
+  const int ai = lane >> 2;                     // the lane's 8-group in a run: 16 r + ai
+  const bool tail = (KB & 3) != 0;
+  const bool tail_lane = 4 * NRF + t4 < KB;
 
-  for (int c0 = 0; c0 < cnt; c0 += NT) {
-    const int nt = min(NT, cnt - c0);
-    // the weights do not depend on the activations: start their loads first
-    uint32_t wd[UNR], rd[UNR];
+  for (int c0 = c_begin; c0 < c_end; c0 += NT) {
+    const int nt = min(NT, c_end - c0);
+    // the weights do not depend on the activations: start their loads first (a rolling pipeline of
+    // UNR slots, each refilled with the run UNR ahead as soon as it has been used)
+    uint4 wd[UNR];
+    Scales4 rd[UNR];
 #pragma unroll
     for (int z = 0; z < UNR; ++z) {
-      const int k = sw + NW * z;
-      wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
-      rd[z] = k < KB ? load_scale_raw<FMT>(ds + k * 32) : 0u;
+      const int r = wp + WPS * z;
+      if (r < NRF) {
+        wd[z] = *reinterpret_cast<const uint4*>(dp + (int64_t)r * 1024);
+        rd[z] = load_scales4<FMT>(ds + r * 128);
+      }
     }
-    // the tokens' activations (16 B per 8-group) and their (scale, sum) pairs into LDS
-    for (int i = tid; i < nt * I8; i += kWG) {
-      const int j = i / I8, g = i % I8;
-      const int64_t tok = (int64_t)u * maxB + c0 + j;
-      s_a4[j * I8 + g] = *reinterpret_cast<const uint4*>(a16 + tok * I + g * 8);
-      s_ag[j * I8 + g] = ag[tok * I8 + g];
+    // the tokens' activations (16 B per 8-group) and their (scale, sum) pairs into LDS, every load of
+    // a thread issued before its stores
+    {
+      constexpr int LPT = 4;
+      const int n = nt * I8;
+      for (int i0 = tid; i0 < n; i0 += LPT * kWG) {
+        uint4 va[LPT];
+        float2 vg[LPT];
+#pragma unroll
+        for (int k = 0; k < LPT; ++k) {
+          const int i = i0 + k * kWG;
+          if (i < n) {
+            const int64_t tok = (int64_t)u * maxB + c0 + i / I8;
+            va[k] = *reinterpret_cast<const uint4*>(a16 + tok * I + (i % I8) * 8);
+            vg[k] = ag[tok * I8 + i % I8];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < LPT; ++k) {
+          const int i = i0 + k * kWG;
+          if (i < n) {
+            s_a4[i] = va[k];
+            s_ag[i] = vg[k];
+          }
+        }
+      }
     }
     __syncthreads();
-    float acc[NT];
+    float acc[4][NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = 0.f;
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int z = 0; z < UNR; ++z)
-      if (sw + NW * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_ag, sw + NW * z, q, nt, I8, acc);
-    for (int kb0 = sw + NW * UNR; kb0 < KB; kb0 += NW * UNR) {
+      for (int j = 0; j < NT; ++j) acc[r][j] = 0.f;
+    for (int r0 = wp; r0 < NRF; r0 += WPS * UNR) {
 #pragma unroll
       for (int z = 0; z < UNR; ++z) {
-        const int k = kb0 + NW * z;
-        wd[z] = k < KB ? *reinterpret_cast<const uint32_t*>(dp + k * 256) : 0u;
-        rd[z] = k < KB ? load_scale_raw<FMT>(ds + k * 32) : 0u;
+        const int r = r0 + WPS * z;
+        if (r < NRF) {
+          down_run<FMT, NT>(wd[z], rd[z], s_a4, s_ag, r * 16 + ai, nt, I8, acc);
+          const int rn = r + WPS * UNR;
+          if (rn < NRF) {
+            wd[z] = *reinterpret_cast<const uint4*>(dp + (int64_t)rn * 1024);
+            rd[z] = load_scales4<FMT>(ds + rn * 128);
+          }
+        }
       }
-#pragma unroll
-      for (int z = 0; z < UNR; ++z)
-        if (kb0 + NW * z < KB) down_tile<FMT, NT>(wd[z], rd[z], s_a4, s_ag, kb0 + NW * z, q, nt, I8, acc);
+    }
+    if (tail && wp == NRF % WPS && tail_lane) {
+      const int r = NRF;
+      const uint4 w1 = *reinterpret_cast<const uint4*>(dp + (int64_t)r * 1024);
+      const Scales4 s1 = load_scales4<FMT>(ds + r * 128);
+      down_run<FMT, NT>(w1, s1, s_a4, s_ag, r * 16 + ai, nt, I8, acc);
     }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      float v = acc[j];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[j] = v;
-    }
-    if (lane < 16) {
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int j = 0; j < NT; ++j) s_red[wave][r][j] = acc[j];
+      for (int j = 0; j < NT; ++j)
+        if (NT == 1 || j < nt) acc[r][j] = sum16(acc[r][j]);
+    if (lane < 4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) s_red[wave][4 * lane + r][j] = acc[r][j];
     }
     __syncthreads();
-    for (int idx = tid; idx < 16 * RS * nt; idx += kWG) {
+    for (int idx = tid; idx < 16 * SPW * nt; idx += kWG) {
       const int j = idx % nt, rr = idx / nt, s2 = rr / 16, row = rr % 16;
-      // the slice's waves in order (RS = 1: waves 0, 1, 2, 3)
-      float v = s_red[s2][row][j];
+      float v = s_red[s2 * WPS][row][j];  // the slice's waves in order
 #pragma unroll
-      for (int w2 = 1; w2 < NW; ++w2) v += s_red[w2 * RS + s2][row][j];
+      for (int w2 = 1; w2 < WPS; ++w2) v += s_red[s2 * WPS + w2][row][j];
       if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= ts[(int64_t)un->flat * 3 + 2];
       const int p = un->entry[c0 + j];
-      y[(int64_t)p * H + (sg * RS + s2) * 16 + row] = v;
+      y[(int64_t)p * H + (sgp * SPW + s2) * 16 + row] = v;
     }
     __syncthreads();
   }
@@ -534,74 +648,123 @@ k_bw_copy(const uint8_t* __restrict__ pool, int64_t R, int64_t n_flat, int64_t f
   }
 }
 
-// 16-row slices per down workgroup (measured): 4 when a launch would otherwise have 8192 or more
-// small workgroups (qwen3.8-flash-next shape, B = 8 and 16: 47 -> 34 us and 80 -> 58 us); 2 for
-// long rows (I >= 1024: the activation stage is shared by enough tiles per wave); else 1 (the
-// 35b-a3b shape at B = 1, where fewer, longer workgroups are slower)
-int down_slices(int units, int H, int I) {
-  if (units * (H / 16) >= 8192 && H % 64 == 0) return 4;
-  if (I >= 1024 && H % 32 == 0) return 2;
-  return 1;
+// Waves per 16-row slice of a matrix (the rest of a 4-wave workgroup takes further slices).  A
+// launch wants a few thousand waves to keep every CU streaming, and a wave enough 1 KiB runs to make
+// its reduction worth it: with many slices each wave takes a whole slice of one matrix, with few the
+// slice's runs are split over more waves.
+int gateup_waves_per_matrix(int slices) { return slices >= 1024 ? 1 : 2; }
+int down_wps(int slices, int runs) {
+  if (slices >= 2048 || runs <= 8) return 1;
+  return slices >= 1024 ? 2 : 4;
+}
+
+template <int FMT, int NT, int P>
+hipError_t launch_gateup_t(eff_engine* e, const uint16_t* x, int units, int nch, hipStream_t s, uint16_t* a16,
+                           float2* ag) {
+  const eff_config& c = e->cfg;
+  const int H = c.hidden, I = c.inter;
+  hipLaunchKernelGGL((k_gateup<FMT, NT, P>), dim3(units * nch * (I / 16) * P / 2), dim3(kWG),
+                     (size_t)(NT > 1 ? NT * H * 2 : 0), s, e->d_arena, e->pool_dev, e->R, e->d_ts, e->d_plan, x, H, I,
+                     c.top_k, c.max_tokens, nch, a16, ag);
+  return hipGetLastError();
+}
+
+template <int FMT, int NT, int WPS>
+hipError_t launch_down_t(eff_engine* e, int units, int nch, hipStream_t s, const uint16_t* a16, const float2* ag,
+                         float* y) {
+  const eff_config& c = e->cfg;
+  const int H = c.hidden, I = c.inter;
+  const size_t lds = (size_t)NT * (I / 8) * (sizeof(uint4) + sizeof(float2));
+  hipLaunchKernelGGL((k_down<FMT, NT, WPS>), dim3(units * nch * (H / 16) * WPS / 4), dim3(kWG), lds, s, e->d_arena,
+                     e->pool_dev, e->R, e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, nch, y);
+  return hipGetLastError();
+}
+
+// Token chunk widths (tokens a workgroup takes at once) by the call's batch, measured at the
+// qwen3.8-flash-next expert shape: gate/up is the longer sweep, where 8-token chunks pay at B = 16
+// (61.6 against 67.8 us with 4) and 4-token chunks at B = 8 (36.0 against 48.0 us with 8); the down
+// rows are short, and 4-token chunks are faster there at both (B = 16: 35.7 against 45.5 us).
+int gateup_nt(int B) { return B >= 16 ? 8 : B >= 4 ? 4 : B >= 2 ? 2 : 1; }
+int down_nt(int B) { return B >= 4 ? 4 : B >= 2 ? 2 : 1; }
+
+template <int FMT, int NT>
+hipError_t launch_gateup_p(eff_engine* e, const uint16_t* x, int units, int B, hipStream_t s, uint16_t* a16,
+                           float2* ag) {
+  const int nch = (B + NT - 1) / NT;  // token chunks a unit can have (a unit holds at most one entry per token)
+  if (gateup_waves_per_matrix(units * (e->cfg.inter / 16)) == 1)
+    return launch_gateup_t<FMT, NT, 1>(e, x, units, nch, s, a16, ag);
+  return launch_gateup_t<FMT, NT, 2>(e, x, units, nch, s, a16, ag);
 }
 
 template <int FMT, int NT>
-hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, hipStream_t s, hipEvent_t after_gateup) {
+hipError_t launch_down_w(eff_engine* e, int units, hipStream_t s, const uint16_t* a16, const float2* ag, float* y) {
+  // the down kernel takes a unit's chunks in turn: its rows are short (I inputs), so a second wave of
+  // workgroups per unit costs more than the chunks' arithmetic it would spread
+  switch (down_wps(units * (e->cfg.hidden / 16), e->cfg.inter / 128)) {
+    case 1: return launch_down_t<FMT, NT, 1>(e, units, 1, s, a16, ag, y);
+    case 2: return launch_down_t<FMT, NT, 2>(e, units, 1, s, a16, ag, y);
+    default: return launch_down_t<FMT, NT, 4>(e, units, 1, s, a16, ag, y);
+  }
+}
+
+template <int FMT>
+hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, int B, hipStream_t s,
+                        hipEvent_t after_gateup) {
   const eff_config& c = e->cfg;
-  const int H = c.hidden, I = c.inter;
+  const int I = c.inter;
   const int ts = timing_begin(e, EFF_T_DECODE_GATEUP, s);
-  // d_a holds 4 bytes per activation: the fp16 values, then one (scale, sum) pair per 8 of them
+  // d_a holds 4 bytes per activation: the fp16 values, then one (scale, sum) pair per 8 of them; a
+  // unit's token j is row u * max_tokens + j whatever the chunk widths
   uint16_t* a16 = reinterpret_cast<uint16_t*>(e->d_a);
   float2* ag = reinterpret_cast<float2*>(a16 + (size_t)e->maxU * c.max_tokens * I);
-  hipLaunchKernelGGL((k_gateup<FMT, NT>), dim3(units * (I / 16)), dim3(kWG), (size_t)(NT > 1 ? NT * H * 2 : 0), s, e->d_arena,
-                     e->pool_dev, e->R,
-                     e->d_ts, e->d_plan, x, H, I, c.top_k, c.max_tokens, a16, ag);
-  hipError_t err = hipGetLastError();
+  hipError_t err;
+  switch (gateup_nt(B)) {
+    case 1: err = launch_gateup_p<FMT, 1>(e, x, units, B, s, a16, ag); break;
+    case 2: err = launch_gateup_p<FMT, 2>(e, x, units, B, s, a16, ag); break;
+    case 4: err = launch_gateup_p<FMT, 4>(e, x, units, B, s, a16, ag); break;
+    default: err = launch_gateup_p<FMT, 8>(e, x, units, B, s, a16, ag); break;
+  }
   if (err != hipSuccess) return err;
   if (after_gateup && (err = hipEventRecord(after_gateup, s)) != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
-  size_t lds = (size_t)NT * (I / 8) * (sizeof(uint4) + sizeof(float2));
-  const int rs = down_slices(units, H, I);
-  if (rs == 4)
-    hipLaunchKernelGGL((k_down<FMT, NT, 4>), dim3(units * (H / 64)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
-                       e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
-  else if (rs == 2)
-    hipLaunchKernelGGL((k_down<FMT, NT, 2>), dim3(units * (H / 32)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
-                       e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
-  else
-    hipLaunchKernelGGL((k_down<FMT, NT, 1>), dim3(units * (H / 16)), dim3(kWG), lds, s, e->d_arena, e->pool_dev, e->R,
-                       e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, y);
-  err = hipGetLastError();
+  switch (down_nt(B)) {
+    case 1: err = launch_down_w<FMT, 1>(e, units, s, a16, ag, y); break;
+    case 2: err = launch_down_w<FMT, 2>(e, units, s, a16, ag, y); break;
+    default: err = launch_down_w<FMT, 4>(e, units, s, a16, ag, y); break;
+  }
   timing_mark(e, ts, 3, s);
   return err;
 }
 
 }  // namespace
 
-int decode_nt(int maxB) { return maxB >= 8 ? 8 : maxB >= 4 ? 4 : maxB >= 2 ? 2 : 1; }
-
 hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
   // allow N * H * 2 bytes of dynamic LDS for the gate/up kernel and N * I * 3 for the down kernel,
   // for every token width N a call can take
-  const int NT = decode_nt(maxB);
+  const int NG = gateup_nt(maxB), ND = down_nt(maxB);
   hipError_t err = hipSuccess;
-#define SETUP(F, N)                                                                                    \
-  if (fmt == F && N <= NT && err == hipSuccess)                                                         \
-    err = hipFuncSetAttribute((const void*)k_down<F, N, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                              N * (I / 8) * 24);                                                        \
-  if (fmt == F && N <= NT && err == hipSuccess)                                                         \
-    err = hipFuncSetAttribute((const void*)k_down<F, N, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                              N * (I / 8) * 24);                                                        \
-  if (fmt == F && N <= NT && err == hipSuccess)                                                         \
-    err = hipFuncSetAttribute((const void*)k_down<F, N, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                              N * (I / 8) * 24);                                                        \
-  if (fmt == F && N <= NT && err == hipSuccess)                                                         \
-    err = hipFuncSetAttribute((const void*)k_gateup<F, N>, hipFuncAttributeMaxDynamicSharedMemorySize,  \
-                              N * H * 2);
-  SETUP(EFF_WFMT_INT4_G32_BF16, 1) SETUP(EFF_WFMT_INT4_G32_BF16, 2) SETUP(EFF_WFMT_INT4_G32_BF16, 4)
-  SETUP(EFF_WFMT_INT4_G32_BF16, 8) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 1) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 2)
-  SETUP(EFF_WFMT_NVFP4_G16_E4M3, 4) SETUP(EFF_WFMT_NVFP4_G16_E4M3, 8)
-#undef SETUP
+  auto set = [&](const void* fn, int bytes) {
+    if (err == hipSuccess) err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  };
+#define SETUP_G(F, N)                                                       \
+  if (fmt == F && N <= NG) {                                                \
+    set((const void*)k_gateup<F, N, 1>, N * H * 2);                         \
+    set((const void*)k_gateup<F, N, 2>, N * H * 2);                         \
+  }
+#define SETUP_D(F, N)                                                       \
+  if (fmt == F && N <= ND) {                                                \
+    set((const void*)k_down<F, N, 1>, N * (I / 8) * 24);                    \
+    set((const void*)k_down<F, N, 2>, N * (I / 8) * 24);                    \
+    set((const void*)k_down<F, N, 4>, N * (I / 8) * 24);                    \
+  }
+  SETUP_G(EFF_WFMT_INT4_G32_BF16, 1) SETUP_G(EFF_WFMT_INT4_G32_BF16, 2) SETUP_G(EFF_WFMT_INT4_G32_BF16, 4)
+  SETUP_G(EFF_WFMT_INT4_G32_BF16, 8) SETUP_G(EFF_WFMT_NVFP4_G16_E4M3, 1) SETUP_G(EFF_WFMT_NVFP4_G16_E4M3, 2)
+  SETUP_G(EFF_WFMT_NVFP4_G16_E4M3, 4) SETUP_G(EFF_WFMT_NVFP4_G16_E4M3, 8)
+  SETUP_D(EFF_WFMT_INT4_G32_BF16, 1) SETUP_D(EFF_WFMT_INT4_G32_BF16, 2) SETUP_D(EFF_WFMT_INT4_G32_BF16, 4)
+  SETUP_D(EFF_WFMT_NVFP4_G16_E4M3, 1) SETUP_D(EFF_WFMT_NVFP4_G16_E4M3, 2) SETUP_D(EFF_WFMT_NVFP4_G16_E4M3, 4)
+#undef SETUP_G
+#undef SETUP_D
   return err;
 }
 
@@ -612,21 +775,12 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
     hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s);
     if (err != hipSuccess) return err;
   }
-  // the token width follows the call's batch (a unit holds at most one entry per token): a B = 1 call
-  // takes the widest weight prefetch whatever max_tokens is
-  const int NT = decode_nt(B);
+  // the token widths follow the call's batch (a unit holds at most one entry per token): a B = 1 call
+  // takes the one-token kernels whatever max_tokens is
   const int units = std::min(e->maxU, B * e->cfg.top_k);  // plan units a call of B tokens can have
-  const bool fp4 = e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3;
-  switch (NT) {
-    case 1: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 1>(e, x, y, units, s, after_gateup)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 1>(e, x, y, units, s, after_gateup);
-    case 2: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 2>(e, x, y, units, s, after_gateup)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 2>(e, x, y, units, s, after_gateup);
-    case 4: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 4>(e, x, y, units, s, after_gateup)
-                       : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 4>(e, x, y, units, s, after_gateup);
-    default: return fp4 ? launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3, 8>(e, x, y, units, s, after_gateup)
-                        : launch_ffn_t<EFF_WFMT_INT4_G32_BF16, 8>(e, x, y, units, s, after_gateup);
-  }
+  if (e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3)
+    return launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3>(e, x, y, units, B, s, after_gateup);
+  return launch_ffn_t<EFF_WFMT_INT4_G32_BF16>(e, x, y, units, B, s, after_gateup);
 }
 
 hipError_t launch_bw_copy(eff_engine* e, int64_t first, int64_t stride, int n, uint8_t* dst, hipStream_t s) {
