@@ -86,6 +86,7 @@ def lib():
             "eff_rebuild_cache": (I32, [VP, I32, ctypes.c_uint64]),
             "eff_copy_missing": (I32, [VP, VP, VP]),
             "eff_expert_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP, VP]),
+            "eff_expert_ffn_decode_noalloc": (I32, [VP, I32, VP, VP, I32, VP, VP]),
             "eff_host_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP]),
             "eff_combine": (I32, [VP, VP, VP, VP, VP, I32, VP, VP]),
             "eff_decode_layer": (I32, [VP, I32, VP, VP, VP, I32, VP, VP, VP, VP]),
@@ -245,6 +246,9 @@ class Engine:
 
     def expert_ffn_decode(self, layer, x, slots, y, stream=None):
         _check(lib().eff_expert_ffn_decode(self.h, layer, _p(x), _p(slots), x.shape[0], _p(y), _s(stream)))
+
+    def expert_ffn_decode_noalloc(self, layer, x, slots, y, stream=None):
+        _check(lib().eff_expert_ffn_decode_noalloc(self.h, layer, _p(x), _p(slots), x.shape[0], _p(y), _s(stream)))
 
     def host_ffn_decode(self, layer, x_host, cpu_ids_host, y_host):
         """numpy arrays: x uint16 [B,H], cpu_ids int32 [B*K], y float32 [B,K,H]."""

@@ -279,7 +279,17 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
 hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s);
 // n records from the pool (flat ids first + i*stride modulo L*E) into dst[2][R] (bandwidth profile)
 hipError_t launch_bw_copy(eff_engine* e, int64_t first, int64_t stride, int n, uint8_t* dst, hipStream_t s);
-hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s);
+// the decode plan of n entries into `plan`, units [0, maxU) written (count 0 past the last)
+hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s, DecodePlan* plan, int maxU);
+// The no-allocation decode: plan and SwiGLU staging in a file-scope device array (per device, its
+// address taken once at engine creation).  noalloc_setup: for the current device; noalloc_need:
+// scratch bytes a call of B tokens needs; launch_ffn_decode_noalloc: as launch_ffn_decode without
+// events or engine scratch.
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+hipError_t noalloc_setup(int device);
+size_t noalloc_need(const eff_engine* e, int B);
+hipError_t launch_ffn_decode_noalloc(eff_engine* e, const uint16_t* x, const int32_t* slots, int B, float* y,
+                                     hipStream_t s);
 hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
                           const int32_t* spec_ids, hipStream_t s);
 // timing hooks: returns the call's event slot (or -1 when timing is off); mark(i) records event i

@@ -461,6 +461,12 @@ int eff_create(const eff_config* cfg, const void* host_pool, const float* tensor
     return fail(EFF_EINVAL, "host_pool is not mapped into the device address space (use eff_host_alloc)");
   }
   e->pool_dev = (const uint8_t*)pdev;
+  // the address of this device's copy of the no-allocation scratch (eff_expert_ffn_decode_noalloc)
+  if (hipError_t err = noalloc_setup(dev); err != hipSuccess) {
+    release(e);
+    return fail(EFF_EHIP, std::string("noalloc_setup (hipGetSymbolAddress of the static scratch): ") +
+                              hipGetErrorString(err));
+  }
   // the host executor: one thread per physical core ([FT-deep] §7), SMT siblings excluded, one core
   // left to the thread that enqueues the GPU work; each pinned to its core.  An explicit thread count
   // is pinned the same way when there are enough cores for it.
@@ -800,6 +806,26 @@ int eff_expert_ffn_decode(eff_engine* e, int layer, const void* x, const int32_t
   if (!x || !slots || !y || B < 1 || B > e->cfg.max_tokens || layer < 0 || layer >= e->cfg.num_layers)
     return fail(EFF_EINVAL, "eff_expert_ffn_decode: bad arguments");
   EFF_HIP_TRY(launch_ffn_decode(e, layer, (const uint16_t*)x, slots, B, y, (hipStream_t)stream));
+  return EFF_OK;
+}
+
+int eff_expert_ffn_decode_noalloc(eff_engine* e, int layer, const void* x, const int32_t* slots, int B, float* y,
+                                  eff_stream_t stream) {
+  if (int rc = check_engine(e)) return rc;
+  if (!x || !slots || !y || B < 1 || B > e->cfg.max_tokens || layer < 0 || layer >= e->cfg.num_layers)
+    return fail(EFF_EINVAL, "eff_expert_ffn_decode_noalloc: bad arguments");
+  const size_t need = noalloc_need(e, B);
+  if (need > kNoAllocScratchBytes)
+    return fail(EFF_EINVAL, "eff_expert_ffn_decode_noalloc: this call needs " + std::to_string(need) +
+                                " bytes of scratch (plan + 3 * min(B*K, units) * max_tokens * inter), more than the " +
+                                std::to_string(kNoAllocScratchBytes) + " of the static scratch");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != e->device)
+    return fail(EFF_EINVAL, "eff_expert_ffn_decode_noalloc: the current device is not the engine's");
+  const hipError_t err = launch_ffn_decode_noalloc(e, (const uint16_t*)x, slots, B, y, (hipStream_t)stream);
+  if (err == hipErrorNotInitialized)
+    return fail(EFF_ESTATE, "eff_expert_ffn_decode_noalloc: no scratch address for this device");
+  EFF_HIP_TRY(err);
   return EFF_OK;
 }
 

@@ -1017,9 +1017,9 @@ hipError_t launch_topk(const float* logits, int B, int E, int K, int32_t* ids, f
   return hipGetLastError();
 }
 
-hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kThreads), 0, s, slots, n, e->cfg.num_slots, e->maxU,
-                     e->cfg.max_tokens, e->d_owner, e->d_plan);
+hipError_t launch_plan(eff_engine* e, const int32_t* slots, int n, hipStream_t s, DecodePlan* plan, int maxU) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kThreads), 0, s, slots, n, e->cfg.num_slots, maxU,
+                     e->cfg.max_tokens, e->d_owner, plan);
   return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@
 //   e2m1   v_cvt_scalef32_pk_{bf16,f16}_fp4 with scale 1.0 (the instruction uses
 //          only the exponent of its scale operand, so the e4m3 block scale is
 //          applied afterwards in fp32); e4m3 via v_cvt_f32_fp8 (OCP E4M3FN).
+#include <mutex>
+
 #include "eff_internal.h"
 
 namespace eff {
@@ -659,24 +661,24 @@ int down_wps(int slices, int runs) {
 }
 
 template <int FMT, int NT, int P>
-hipError_t launch_gateup_t(eff_engine* e, const uint16_t* x, int units, int nch, hipStream_t s, uint16_t* a16,
-                           float2* ag) {
+hipError_t launch_gateup_t(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int nch, hipStream_t s,
+                           uint16_t* a16, float2* ag) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   hipLaunchKernelGGL((k_gateup<FMT, NT, P>), dim3(units * nch * (I / 16) * P / 2), dim3(kWG),
-                     (size_t)(NT > 1 ? NT * H * 2 : 0), s, e->d_arena, e->pool_dev, e->R, e->d_ts, e->d_plan, x, H, I,
+                     (size_t)(NT > 1 ? NT * H * 2 : 0), s, e->d_arena, e->pool_dev, e->R, e->d_ts, plan, x, H, I,
                      c.top_k, c.max_tokens, nch, a16, ag);
   return hipGetLastError();
 }
 
 template <int FMT, int NT, int WPS>
-hipError_t launch_down_t(eff_engine* e, int units, int nch, hipStream_t s, const uint16_t* a16, const float2* ag,
-                         float* y) {
+hipError_t launch_down_t(eff_engine* e, const DecodePlan* plan, int units, int nch, hipStream_t s, const uint16_t* a16,
+                         const float2* ag, float* y) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   const size_t lds = (size_t)NT * (I / 8) * (sizeof(uint4) + sizeof(float2));
   hipLaunchKernelGGL((k_down<FMT, NT, WPS>), dim3(units * nch * (H / 16) * WPS / 4), dim3(kWG), lds, s, e->d_arena,
-                     e->pool_dev, e->R, e->d_ts, e->d_plan, a16, ag, H, I, c.max_tokens, nch, y);
+                     e->pool_dev, e->R, e->d_ts, plan, a16, ag, H, I, c.max_tokens, nch, y);
   return hipGetLastError();
 }
 
@@ -688,50 +690,48 @@ int gateup_nt(int B) { return B >= 16 ? 8 : B >= 4 ? 4 : B >= 2 ? 2 : 1; }
 int down_nt(int B) { return B >= 4 ? 4 : B >= 2 ? 2 : 1; }
 
 template <int FMT, int NT>
-hipError_t launch_gateup_p(eff_engine* e, const uint16_t* x, int units, int B, hipStream_t s, uint16_t* a16,
-                           float2* ag) {
+hipError_t launch_gateup_p(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int B, hipStream_t s,
+                           uint16_t* a16, float2* ag) {
   const int nch = (B + NT - 1) / NT;  // token chunks a unit can have (a unit holds at most one entry per token)
   if (gateup_waves_per_matrix(units * (e->cfg.inter / 16)) == 1)
-    return launch_gateup_t<FMT, NT, 1>(e, x, units, nch, s, a16, ag);
-  return launch_gateup_t<FMT, NT, 2>(e, x, units, nch, s, a16, ag);
+    return launch_gateup_t<FMT, NT, 1>(e, plan, x, units, nch, s, a16, ag);
+  return launch_gateup_t<FMT, NT, 2>(e, plan, x, units, nch, s, a16, ag);
 }
 
 template <int FMT, int NT>
-hipError_t launch_down_w(eff_engine* e, int units, hipStream_t s, const uint16_t* a16, const float2* ag, float* y) {
+hipError_t launch_down_w(eff_engine* e, const DecodePlan* plan, int units, hipStream_t s, const uint16_t* a16,
+                         const float2* ag, float* y) {
   // the down kernel takes a unit's chunks in turn: its rows are short (I inputs), so a second wave of
   // workgroups per unit costs more than the chunks' arithmetic it would spread
   switch (down_wps(units * (e->cfg.hidden / 16), e->cfg.inter / 128)) {
-    case 1: return launch_down_t<FMT, NT, 1>(e, units, 1, s, a16, ag, y);
-    case 2: return launch_down_t<FMT, NT, 2>(e, units, 1, s, a16, ag, y);
-    default: return launch_down_t<FMT, NT, 4>(e, units, 1, s, a16, ag, y);
+    case 1: return launch_down_t<FMT, NT, 1>(e, plan, units, 1, s, a16, ag, y);
+    case 2: return launch_down_t<FMT, NT, 2>(e, plan, units, 1, s, a16, ag, y);
+    default: return launch_down_t<FMT, NT, 4>(e, plan, units, 1, s, a16, ag, y);
   }
 }
 
+// The two expert kernels of one call on the plan `plan`; a16 holds units * max_tokens * I fp16
+// activations (a unit's token j is row u * max_tokens + j whatever the chunk widths) and ag one
+// (scale, sum) pair per 8 of them.  `timed`: bracket the kernels with the engine's timing events.
 template <int FMT>
-hipError_t launch_ffn_t(eff_engine* e, const uint16_t* x, float* y, int units, int B, hipStream_t s,
-                        hipEvent_t after_gateup) {
-  const eff_config& c = e->cfg;
-  const int I = c.inter;
-  const int ts = timing_begin(e, EFF_T_DECODE_GATEUP, s);
-  // d_a holds 4 bytes per activation: the fp16 values, then one (scale, sum) pair per 8 of them; a
-  // unit's token j is row u * max_tokens + j whatever the chunk widths
-  uint16_t* a16 = reinterpret_cast<uint16_t*>(e->d_a);
-  float2* ag = reinterpret_cast<float2*>(a16 + (size_t)e->maxU * c.max_tokens * I);
+hipError_t launch_ffn_t(eff_engine* e, const DecodePlan* plan, uint16_t* a16, float2* ag, const uint16_t* x, float* y,
+                        int units, int B, hipStream_t s, hipEvent_t after_gateup, bool timed) {
+  const int ts = timed ? timing_begin(e, EFF_T_DECODE_GATEUP, s) : -1;
   hipError_t err;
   switch (gateup_nt(B)) {
-    case 1: err = launch_gateup_p<FMT, 1>(e, x, units, B, s, a16, ag); break;
-    case 2: err = launch_gateup_p<FMT, 2>(e, x, units, B, s, a16, ag); break;
-    case 4: err = launch_gateup_p<FMT, 4>(e, x, units, B, s, a16, ag); break;
-    default: err = launch_gateup_p<FMT, 8>(e, x, units, B, s, a16, ag); break;
+    case 1: err = launch_gateup_p<FMT, 1>(e, plan, x, units, B, s, a16, ag); break;
+    case 2: err = launch_gateup_p<FMT, 2>(e, plan, x, units, B, s, a16, ag); break;
+    case 4: err = launch_gateup_p<FMT, 4>(e, plan, x, units, B, s, a16, ag); break;
+    default: err = launch_gateup_p<FMT, 8>(e, plan, x, units, B, s, a16, ag); break;
   }
   if (err != hipSuccess) return err;
   if (after_gateup && (err = hipEventRecord(after_gateup, s)) != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
   switch (down_nt(B)) {
-    case 1: err = launch_down_w<FMT, 1>(e, units, s, a16, ag, y); break;
-    case 2: err = launch_down_w<FMT, 2>(e, units, s, a16, ag, y); break;
-    default: err = launch_down_w<FMT, 4>(e, units, s, a16, ag, y); break;
+    case 1: err = launch_down_w<FMT, 1>(e, plan, units, s, a16, ag, y); break;
+    case 2: err = launch_down_w<FMT, 2>(e, plan, units, s, a16, ag, y); break;
+    default: err = launch_down_w<FMT, 4>(e, plan, units, s, a16, ag, y); break;
   }
   timing_mark(e, ts, 3, s);
   return err;
@@ -772,15 +772,72 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
                              float* y, hipStream_t s, bool plan_ready, hipEvent_t after_gateup) {
   (void)layer;
   if (!plan_ready) {
-    hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s);
+    hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s, e->d_plan, e->maxU);
     if (err != hipSuccess) return err;
   }
   // the token widths follow the call's batch (a unit holds at most one entry per token): a B = 1 call
   // takes the one-token kernels whatever max_tokens is
   const int units = std::min(e->maxU, B * e->cfg.top_k);  // plan units a call of B tokens can have
+  uint16_t* a16 = reinterpret_cast<uint16_t*>(e->d_a);
+  float2* ag = reinterpret_cast<float2*>(a16 + (size_t)e->maxU * e->cfg.max_tokens * e->cfg.inter);
   if (e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3)
-    return launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3>(e, x, y, units, B, s, after_gateup);
-  return launch_ffn_t<EFF_WFMT_INT4_G32_BF16>(e, x, y, units, B, s, after_gateup);
+    return launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3>(e, e->d_plan, a16, ag, x, y, units, B, s, after_gateup, true);
+  return launch_ffn_t<EFF_WFMT_INT4_G32_BF16>(e, e->d_plan, a16, ag, x, y, units, B, s, after_gateup, true);
+}
+
+// ---------------------------------------------------------------------------- static scratch
+// The scratch of eff_expert_ffn_decode_noalloc, for callers that cannot allocate (graph capture,
+// tight serving loops): the decode plan, then the SwiGLU activations (fp16) and their (scale, sum)
+// pairs, in one file-scope device array.  Each GPU holds its own copy until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it is only a stand-in): the address of
+// each device's copy comes from hipGetSymbolAddress, taken once per device with that device current,
+// and kernels get that address.  Every call on a GPU shares its copy, so calls that overlap on one
+// GPU race; nothing in it needs to start at zero (the plan kernel writes every unit the expert
+// kernels read, and they write the activations before reading them).
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+constexpr size_t kPlanBytes = (sizeof(DecodePlan) + 255) / 256 * 256;
+}  // namespace
+
+hipError_t noalloc_setup(int device) {
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (err != hipSuccess) return err;
+  if (!p) return hipErrorInvalidSymbol;
+  g_scratch_ptr[device] = p;
+  return hipSuccess;
+}
+
+size_t noalloc_need(const eff_engine* e, int B) {
+  const size_t units = (size_t)std::min(e->maxU, B * e->cfg.top_k);
+  // fp16 activations (2 bytes) and one 8-byte pair per 8 of them: 3 bytes per activation
+  return kPlanBytes + units * (size_t)e->cfg.max_tokens * (size_t)e->cfg.inter * 3;
+}
+
+hipError_t launch_ffn_decode_noalloc(eff_engine* e, const uint16_t* x, const int32_t* slots, int B, float* y,
+                                     hipStream_t s) {
+  void* base = nullptr;
+  {
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (e->device >= 0 && e->device < kMaxDevices) base = g_scratch_ptr[e->device];
+  }
+  if (!base) return hipErrorNotInitialized;
+  const int units = std::min(e->maxU, B * e->cfg.top_k);
+  DecodePlan* plan = reinterpret_cast<DecodePlan*>(base);
+  uint16_t* a16 = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(base) + kPlanBytes);
+  float2* ag = reinterpret_cast<float2*>(a16 + (size_t)units * e->cfg.max_tokens * e->cfg.inter);
+  hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s, plan, units);
+  if (err != hipSuccess) return err;
+  if (e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3)
+    return launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3>(e, plan, a16, ag, x, y, units, B, s, nullptr, false);
+  return launch_ffn_t<EFF_WFMT_INT4_G32_BF16>(e, plan, a16, ag, x, y, units, B, s, nullptr, false);
 }
 
 hipError_t launch_bw_copy(eff_engine* e, int64_t first, int64_t stride, int n, uint8_t* dst, hipStream_t s) {

@@ -240,6 +240,18 @@ int eff_copy_missing(eff_engine* e, eff_stream_t compute, eff_stream_t side);
 int eff_expert_ffn_decode(eff_engine* e, int layer, const void* x, const int32_t* slots, int B,
                           float* y, eff_stream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): eff_expert_ffn_decode with the same arguments and results, whose decode
+ * plan and SwiGLU staging live in a file-scope device array of 8 MiB (its address on each device is
+ * taken once, by eff_create) instead of engine buffers; it calls no hipMalloc, hipFree or other
+ * allocating routine (an error message may allocate host memory).  Every call on a GPU shares that
+ * array: calls that overlap on one GPU race, whatever engine they come from.  A call needs
+ * 73,984 + 3 * min(B*K, units) * max_tokens * inter bytes (units = min(max_tokens*K, E));
+ * beyond 8 MiB it returns EFF_EINVAL and launches nothing.  The current device must be the
+ * engine's (EFF_EINVAL otherwise).  No kernel timing. */
+int eff_expert_ffn_decode_noalloc(eff_engine* e, int layer, const void* x, const int32_t* slots, int B,
+                                  float* y, eff_stream_t stream);
+
 /* Host share ([FT-deep] §4 ③ decode_submit/decode_sync; [FT-blog] §三.2): the
  * same expert FFN on the host, from the pinned pool, for entries with
  * cpu_ids[p] >= 0.  Synchronous; all pointers are host memory.  y_host fp32
