@@ -34,6 +34,11 @@ Readings where the pages are silent (each listed in the design doc):
   layer are few, two of them there, and read in the gap left by the real reads):
   a speculative call fetches at most `spec_budget` records, the first of its
   ranked misses; None leaves q' as above.  Real calls ignore the budget.
+* Optional link gap (the same passage: guesses use only the transfer time the
+  real reads leave): with `spec_link` = G records the link can carry in one
+  layer's time, a speculative call fetches at most max(0, G - q_real), q_real the
+  q' of the latest real split (the layer's own fetches), again the first of its
+  ranked misses.  Both caps may apply at once (the smaller wins).
 * A runtime rebuild to S' slots ([FT-blog] §七 item 1: the GPU expert cache is
   repartitioned for a new budget at a safe point, without touching the host pool;
   since the pool is the source of truth, losing the cache only costs speed) starts
@@ -70,9 +75,12 @@ class _Pending:
 
 
 class SlotCache:
-    def __init__(self, L: int, E: int, S: int, f_q16: int, spec_budget: int | None = None):
+    def __init__(self, L: int, E: int, S: int, f_q16: int, spec_budget: int | None = None,
+                 spec_link: int | None = None):
         self.L, self.E, self.S, self.f = L, E, S, f_q16
         self.spec_budget = spec_budget
+        self.spec_link = spec_link
+        self.last_real_q = 0      # q' of the latest real split
         self.table = [-1] * (L * E)
         self.owner = [-1] * S
         self.usage = [-1] * S
@@ -114,6 +122,8 @@ class SlotCache:
         qq = min(q, len(victims))
         if p.speculative and self.spec_budget is not None:
             qq = min(qq, self.spec_budget)
+        if p.speculative and self.spec_link is not None:
+            qq = min(qq, max(0, self.spec_link - self.last_real_q))
         fetch = []
         for i in range(qq):
             v, e = victims[i], ranked[i]
@@ -133,6 +143,7 @@ class SlotCache:
             for e in p.uniq:
                 self.recency[l * E + e] = p.s
             self.last_real = p.s
+            self.last_real_q = qq
         return SplitResult(slots, cpu_ids, fetch, m, qq, host)
 
     def ensure_split(self, layer: int, ids: List[int], speculative: bool = False) -> SplitResult:

@@ -182,6 +182,54 @@ def test_speculative_budget_takes_the_ranked_prefix():
     assert checked > 50   # the budget bound often
 
 
+def test_speculative_gap_is_capacity_left_by_the_real_fetches():
+    """With a link gap of G records per layer, a speculative call fetches exactly the first
+    max(0, G - q) pairs the unbudgeted call would, q the fetch count of the latest real call of the
+    history (tracked here from the returned results, not read from the cache); real calls are
+    unaffected; with a budget too, the smaller cap wins."""
+    import copy
+    import random
+    rng = random.Random(9)
+    L, E, S = 3, 16, 10
+    checked = 0
+    for _ in range(300):
+        base = SlotCache(L, E, S, 65535)
+        q_real = 0
+        for _ in range(rng.randint(0, 6)):
+            spec = rng.random() < 0.3
+            r = base.ensure_split(rng.randrange(L), rng.sample(range(E), rng.randint(1, 5)), speculative=spec)
+            if not spec:
+                q_real = r.q
+        layer, ids = rng.randrange(L), rng.sample(range(E), rng.randint(1, 8))
+        ref = copy.deepcopy(base).ensure_split(layer, ids, speculative=True)
+        for G in (0, 1, 3, 6):
+            for budget in (None, 1):
+                c = copy.deepcopy(base)
+                c.spec_link, c.spec_budget = G, budget
+                r = c.ensure_split(layer, ids, speculative=True)
+                cap = max(0, G - q_real) if budget is None else min(budget, max(0, G - q_real))
+                assert r.q == min(ref.q, cap) and r.fetch == ref.fetch[:cap]
+                checked += ref.q > cap
+            real_a, real_b = copy.deepcopy(base), copy.deepcopy(base)
+            real_b.spec_link = G
+            assert real_a.ensure_split(layer, ids) == real_b.ensure_split(layer, ids)
+    assert checked > 100
+
+
+def test_speculative_gap_follows_the_latest_real_call():
+    """Worked case: the cap is G minus the fetches of the real call just before the speculative one."""
+    L, E, S = 2, 8, 8
+    c = SlotCache(L, E, S, 65536, spec_link=3)
+    r = c.ensure_split(0, [0, 1])                  # two misses, both fetched
+    assert r.q == 2
+    spec = c.ensure_split(1, [4, 5, 6], speculative=True)
+    assert spec.q == 1 and spec.m == 3             # 3 - 2 = 1 guess
+    r = c.ensure_split(0, [0, 1])                  # both hit: nothing fetched
+    assert r.q == 0
+    spec = c.ensure_split(1, [4, 5, 6, 7], speculative=True)
+    assert spec.q == 3                             # 3 - 0 = 3 guesses (4 was fetched before)
+
+
 def test_speculative_budget_zero_only_protects_hits():
     L, E, S = 2, 8, 4
     c = SlotCache(L, E, S, 65536, spec_budget=0)
