@@ -83,6 +83,7 @@ def lib():
             "eff_profile_bandwidth": (I32, [VP, I32, VP]),
             "eff_set_fetch_frac": (I32, [VP, U32]),
             "eff_set_speculation": (I32, [VP, I32, I32]),
+            "eff_set_speculation_link": (I32, [VP, I32]),
             "eff_rebuild_cache": (I32, [VP, I32, ctypes.c_uint64]),
             "eff_copy_missing": (I32, [VP, VP, VP]),
             "eff_expert_ffn_decode": (I32, [VP, I32, VP, VP, I32, VP, VP]),
@@ -340,6 +341,10 @@ class Engine:
 
     def set_host_isa(self, isa: int):
         _check(lib().eff_set_host_isa(self.h, isa))
+
+    def set_speculation_link(self, link_records: int):
+        """eff_set_speculation_link: speculative fetches limited to the link records a layer leaves (-1: off)."""
+        _check(lib().eff_set_speculation_link(self.h, link_records))
 
     def set_fetch_frac(self, frac_q16: int):
         _check(lib().eff_set_fetch_frac(self.h, frac_q16))

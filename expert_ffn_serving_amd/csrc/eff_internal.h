@@ -53,6 +53,10 @@ struct Pending {
 // during layer l (for layer l+1) is copied on a side stream that the next layer's expert kernels wait
 // for; the request that reuses its list is made two layers later, after that wait.
 constexpr int kFetchLists = 3;
+// Bytes allocated after the last slot of the arena: a decode wave loads a whole 1 KiB run (and its
+// 128 scale bytes) even where a slice ends inside it, and past its last run it loads that run again
+// so that no load sits behind a branch; such bytes are never used.
+constexpr int64_t kArenaTail = 4096;
 __host__ __device__ inline int spec_fetch_list(int layer) { return 1 + (layer & 1); }
 // ------------------------------------------------------------------------------------------------
 struct FetchList {
@@ -160,7 +164,7 @@ struct eff_engine {
   int32_t* d_owner = nullptr;
   int64_t* d_usage = nullptr;
   int64_t* d_recency = nullptr;
-  int64_t* d_clock = nullptr;     // {step, last_real}
+  int64_t* d_clock = nullptr;     // {step, last_real, fetches of the last real call}
   float* d_ts = nullptr;          // [L*E*3]
   eff::Pending* d_pending = nullptr;
   eff::FetchList* d_fetch = nullptr;   // [kFetchLists]: real, speculative (even layer), speculative (odd layer)
@@ -199,7 +203,7 @@ struct eff_engine {
   uint64_t* h_call_dev = nullptr;
   uint64_t* h_done = nullptr;     // host-mapped: the last call whose host share is in h_yhost
   uint64_t* h_done_dev = nullptr;
-  int32_t* h_err = nullptr;       // host-mapped sticky device error bits (bad id 1, combine wait 4)
+  int32_t* h_err = nullptr;       // host-mapped sticky device error bits (bad id 1, combine wait 4, prefill fp16 range 8)
   int32_t* h_err_dev = nullptr;
   uint64_t* d_seq = nullptr;      // device: the last decode call's seq
   uint64_t sync_seq = 0;          // EFF_CFG_SYNC_HOST: the host's count of decode calls (= *d_seq)
@@ -209,6 +213,7 @@ struct eff_engine {
   bool async_host = false;        // host share on the worker thread, the stream waits on h_done
   bool spec_copy_pending = false; // a speculative copy on the side stream not yet waited for
   int spec_budget = -1;           // eff_set_speculation: records per speculative request (-1: any)
+  int spec_link = -1;              // eff_set_speculation_link: link records per layer (-1: no cap)
   bool spec_in_gap = false;       // eff_set_speculation: speculative copies start after gate/up
   hipEvent_t ev_gateup = nullptr; // end of the layer's gate/up kernel (speculative copies in the gap)
   hipEvent_t ev_ctl = nullptr;

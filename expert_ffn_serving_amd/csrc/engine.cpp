@@ -91,12 +91,12 @@ static int alloc_all(eff_engine* e) {
   const eff_config& c = e->cfg;
   const int64_t L = c.num_layers, E = c.num_experts, S = c.num_slots, H = c.hidden, I = c.inter;
   const int64_t K = c.top_k, B = c.max_tokens, T = c.max_prefill_tokens;
-  EFF_HIP_TRY(dalloc(&e->d_arena, (size_t)(S * e->R)));
+  EFF_HIP_TRY(dalloc(&e->d_arena, S > 0 ? (size_t)(S * e->R + kArenaTail) : 0));
   EFF_HIP_TRY(dalloc(&e->d_table, L * E));
   EFF_HIP_TRY(dalloc(&e->d_owner, S));
   EFF_HIP_TRY(dalloc(&e->d_usage, S));
   EFF_HIP_TRY(dalloc(&e->d_recency, L * E));
-  EFF_HIP_TRY(dalloc(&e->d_clock, 2));
+  EFF_HIP_TRY(dalloc(&e->d_clock, 3));
   EFF_HIP_TRY(dalloc(&e->d_ts, L * E * 3));
   EFF_HIP_TRY(dalloc(&e->d_pending, 1));
   EFF_HIP_TRY(dalloc(&e->d_fetch, kFetchLists));
@@ -162,7 +162,7 @@ static int alloc_all(eff_engine* e) {
   EFF_HIP_TRY(hipMemset(e->d_owner, 0xFF, (size_t)std::max<int64_t>(1, S) * 4));
   EFF_HIP_TRY(hipMemset(e->d_usage, 0xFF, (size_t)std::max<int64_t>(1, S) * 8));
   EFF_HIP_TRY(hipMemset(e->d_recency, 0xFF, (size_t)(L * E) * 8));
-  EFF_HIP_TRY(hipMemset(e->d_clock, 0, 16));
+  EFF_HIP_TRY(hipMemset(e->d_clock, 0, 24));
   EFF_HIP_TRY(hipMemset(e->d_pending, 0, sizeof(Pending)));
   EFF_HIP_TRY(hipMemset(e->d_err, 0, 4));
   EFF_HIP_TRY(hipMemset(e->d_seq, 0, 8));
@@ -272,6 +272,7 @@ static int check_async_error(eff_engine* e) {
   if (dev_err)
     return fail(EFF_EDEVICE, (dev_err & 1) ? "an expert id was outside [0, E) (entries skipped)"
                              : (dev_err & 4) ? "a combine gave up waiting for its host share"
+                             : (dev_err & 8) ? "a prefill activation or SwiGLU output exceeded the fp16 range (65504)"
                                              : "device error");
   if (!e->async_err.load(std::memory_order_acquire)) return EFF_OK;
   std::lock_guard<std::mutex> g(e->async_mu);
@@ -593,6 +594,13 @@ int eff_set_speculation(eff_engine* e, int max_fetch, int in_gap) {
   return EFF_OK;
 }
 
+int eff_set_speculation_link(eff_engine* e, int link_records) {
+  if (int rc = check_engine(e)) return rc;
+  if (link_records < -1) return fail(EFF_EINVAL, "eff_set_speculation_link: link_records >= -1");
+  e->spec_link = link_records;
+  return EFF_OK;
+}
+
 int eff_set_fetch_frac(eff_engine* e, uint32_t frac_q16) {
   if (int rc = check_engine(e)) return rc;
   if (frac_q16 > 65536u) return fail(EFF_EINVAL, "fetch_frac_q16 must be in [0, 65536]");
@@ -709,7 +717,7 @@ int eff_rebuild_cache(eff_engine* e, int num_slots, uint64_t max_arena_bytes) {
   const int64_t L = c.num_layers, E = c.num_experts;
   // geometry and budget, before anything else
   if (num_slots < 0 || num_slots > kMaxSlots) return fail(EFF_EREJECTED, "num_slots must be in [0, 16384]");
-  const uint64_t arena = (uint64_t)num_slots * (uint64_t)e->R;
+  const uint64_t arena = num_slots > 0 ? (uint64_t)num_slots * (uint64_t)e->R + kArenaTail : 0;
   if (max_arena_bytes > 0 && arena > max_arena_bytes)
     return fail(EFF_EREJECTED, "the slot arena does not fit the byte budget");
   // a safe point: no call half done
@@ -952,6 +960,7 @@ int eff_prefill_stream_layer(eff_engine* e, int layer, eff_stream_t side) {
 int eff_expert_ffn_prefill_layer(eff_engine* e, int layer, const void* x, const int32_t* ids, const float* w,
                                  int T, void* out, eff_stream_t stream) {
   if (int rc = check_engine(e)) return rc;
+  if (int rc = check_async_error(e)) return rc;
   const eff_config& c = e->cfg;
   if (!x || !ids || !w || !out || T < 1 || T > c.max_prefill_tokens || layer < 0 || layer >= c.num_layers)
     return fail(EFF_EINVAL, "eff_expert_ffn_prefill_layer: bad arguments");
@@ -1016,6 +1025,7 @@ int eff_snapshot_tables(eff_engine* e, int32_t* table, int32_t* owner, int64_t* 
   if (usage && S) EFF_HIP_TRY(hipMemcpy(usage, e->d_usage, S * 8, hipMemcpyDeviceToHost));
   if (recency) EFF_HIP_TRY(hipMemcpy(recency, e->d_recency, LE * 8, hipMemcpyDeviceToHost));
   if (clock) EFF_HIP_TRY(hipMemcpy(clock, e->d_clock, 16, hipMemcpyDeviceToHost));
+  if (int rc = check_async_error(e)) return rc;
   return read_device_error(e);
 }
 

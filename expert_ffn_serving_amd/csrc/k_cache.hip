@@ -43,6 +43,8 @@ struct CacheState {
   int32_t* host_err;  // host-mapped sticky error bits
   int sort_pow2;
   int spec_budget;  // most records a speculative call fetches (-1: no budget)
+  int spec_link;     // records the link carries per layer; a speculative call fetches at most this minus
+                    // the latest real call's fetches (-1: no such cap)
 };
 
 // Barrier for data exchanged through LDS only: waits for this wave's LDS accesses, not for its
@@ -234,14 +236,18 @@ __device__ void prebuild_keys(const CacheState& c, CallLds& C, uint64_t* s_key) 
 // The call's hit slots are never victims (their stamp of this step is committed later).
 // s_key: sort_pow2 uint64 of LDS.
 // keys_ready: s_key and C.nvw were prebuilt (prebuild_keys) from the usage this call sees.
-__device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, bool keys_ready = false) {
+// real_q: the latest real call's fetch count when the caller has it (the fused control kernel, whose
+// real split precedes its speculative one), else -1: read from clock[2].
+__device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, bool keys_ready = false,
+                           int real_q = -1) {
   const int tid = threadIdx.x;
   const int E = c.E, S = c.S;
   const int n = C.n, m = C.nm;
   const int64_t floor_ = C.floor_;
   const int64_t base = (int64_t)C.layer * E;
   int q = (int)qstar_dev(m, c.f);
-  if (C.spec && c.spec_budget >= 0) q = min(q, c.spec_budget);  // q' = min(q*, victims, budget)
+  if (C.spec && c.spec_budget >= 0) q = min(q, c.spec_budget);  // q' = min(q*, victims, budget, gap)
+  if (C.spec && c.spec_link >= 0) q = min(q, max(0, c.spec_link - (real_q >= 0 ? real_q : (int)c.clock[2])));
   int qq = 0;
   if (q > 0) {
     if (tid == 0) {
@@ -394,7 +400,10 @@ __device__ void commit_body(const CacheState& c, const CallLds& C, bool stamp_hi
   }
   if (tid == 0) {
     c.clock[0] = s;
-    if (!spec) c.clock[1] = s;
+    if (!spec) {
+      c.clock[1] = s;
+      c.clock[2] = qq;  // the real call's fetches (speculative link cap)
+    }
     if (counts) {
       counts[0] = m;
       counts[1] = qq;
@@ -881,11 +890,12 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
       nhost += __popcll(__ballot(p < n && C.slot[p] < 0 && C.id[p] >= 0));
     }
   if (spec_ids) {
+    const int real_q = C.qq;  // the real call's fetches, before the speculative call reuses C
     __syncthreads();  // the real call's commit is visible to the speculative ensure
     for (int p = tid; p < n; p += kThreads) C.id[p] = spec_ids[p];
     lds_sync();
     ensure_body(c, layer + 1, n, 1, C);
-    split_body(c, C, s_key);
+    split_body(c, C, s_key, false, real_q);
     commit_body(c, C, true, spec_slots, nullptr, nullptr, counts + 3);
   }
   if (tid < 64) publish_call(call_ring, host_done, seq_ctr, layer, B, nhost);
@@ -987,6 +997,7 @@ static CacheState state_of(eff_engine* e) {
   c.host_err = e->h_err_dev;
   c.sort_pow2 = sort_pow2_of(c.S);
   c.spec_budget = e->spec_budget;
+  c.spec_link = e->spec_link;
   return c;
 }
 

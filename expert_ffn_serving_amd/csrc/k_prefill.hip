@@ -19,7 +19,9 @@
 // in [2^-10, 2688], so it is exact in fp16); the fp32 tensor scale is applied
 // after accumulation.  int4: fp16(1024+u) - 1032 = u - 8 exactly, then times
 // the scale (exact in fp16 for scales >= 2^-14).  Activations enter the MFMA
-// as fp16 (bf16 inputs convert exactly inside fp16's normal range).
+// as fp16 (bf16 inputs convert exactly inside fp16's normal range); an input or
+// SwiGLU output beyond the fp16 range sets bit 8 of the engine's device error
+// word, which the next host-waiting call reports, instead of passing an inf on.
 #include "eff_internal.h"
 
 namespace eff {
@@ -142,6 +144,7 @@ __device__ inline uint32_t scale_pair(uint32_t raw) {
   return pk_f16(f, f);
 }
 
+constexpr float kF16Max = 65504.f;  // activations enter the MFMA as fp16: larger ones are reported
 constexpr int kMT = 64;         // tokens per pass (4 MFMA subtiles of 16)
 constexpr int kCT = 8;          // k-tiles (of 32 inputs) per staged activation chunk
 constexpr int kRowU32 = 132;    // LDS row stride in dwords: 256 fp16 + 4 dwords of padding
@@ -165,7 +168,7 @@ __global__ void __launch_bounds__(256 * NMAT, NMAT == 2 ? 1 : 2)
 k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
           const int32_t* __restrict__ owner, int slot_base, const int32_t* __restrict__ slot_of,
           const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows, const uint16_t* __restrict__ src,
-          int E, int H, int I, int K, uint16_t* __restrict__ a_out, float* __restrict__ y_out) {
+          int E, int H, int I, int K, uint16_t* __restrict__ a_out, float* __restrict__ y_out, int32_t* err) {
   constexpr int TPB = 256 * NMAT;            // threads
   constexpr int SEGS = TPB / kMT;            // staging threads per row
   constexpr int SEGW = 256 / SEGS;           // inputs per staging thread per chunk
@@ -215,6 +218,7 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   const int pbase = (NMAT == 2) ? (lane & 7) * 8 : ((lane >> 3) & 3) * SEGW;
   constexpr int pstep = (NMAT == 2) ? 64 : 8;
 
+  bool range_bad = false;  // an activation or SwiGLU output beyond the fp16 range (becomes inf)
   for (int m0 = 0; m0 < ne; m0 += kMT) {
     const int mt = min(kMT, ne - m0);
     // rows past mt stage the pass's first row again (their results are discarded)
@@ -251,6 +255,10 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
             f[2 * i] = __uint_as_float(wv[i] << 16);
             f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
           }
+          float mx = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(f[i]));
+          if (mx > kF16Max) range_bad = true;
           if (FMT == EFF_WFMT_INT4_G32_BF16) {  // pairs (0,4), (1,5), (2,6), (3,7)
             o[0] = pk_f16(f[0], f[4]); o[1] = pk_f16(f[1], f[5]); o[2] = pk_f16(f[2], f[6]); o[3] = pk_f16(f[3], f[7]);
           } else {
@@ -374,7 +382,9 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
               const int rr = s2 * 16 + q * 4 + i;
               if (rr < mt) {
                 const float g = g_lds[rr * kGRow + wl * 64 + t * 16 + r];
-                const _Float16 av = (_Float16)(silu(g) * (acc[t][s2][i] * tsc));
+                const float a = silu(g) * (acc[t][s2][i] * tsc);
+                if (!(fabsf(a) <= kF16Max)) range_bad = true;
+                const _Float16 av = (_Float16)a;
                 a_out[(int64_t)(off + m0 + rr) * I + nb * 64 + t * 16 + r] = __builtin_bit_cast(uint16_t, av);
               }
             }
@@ -400,6 +410,7 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
           }
     }
   }
+  if (err && __ballot(range_bad) && lane == 0) __hip_atomic_fetch_or(err, 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace
@@ -422,7 +433,8 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
   const bool full = H % 256 == 0 && I % 256 == 0;
 #define EFF_PF_LAUNCH(F, NM, PFD, FU, GRID, SRC, AO, YO)                                                     \
   hipLaunchKernelGGL((k_pf_gemm<F, NM, PFD, FU>), dim3(GRID), dim3(256 * NM), 0, s, e->d_arena, e->R, e->d_ts, \
-                     e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, SRC, E, H, I, K, AO, YO)
+                     e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, SRC, E, H, I, K, AO, YO,    \
+                     e->h_err_dev)
 #define EFF_PF_PICK(NM, PFD, FU, GRID, SRC, AO, YO)                                           \
   do {                                                                                        \
     if (fp4) {                                                                                \

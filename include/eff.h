@@ -209,6 +209,14 @@ int eff_set_fetch_frac(eff_engine* e, uint32_t frac_q16);
  * EFF_EINVAL for max_fetch < -1 or in_gap not 0 or 1. */
 int eff_set_speculation(eff_engine* e, int max_fetch, int in_gap);
 
+/* The link's gap for speculative fetches ([NVMe-8GB] "엔진" item 3: guesses are read in the transfer
+ * time the layer's real reads leave): link_records = the records the link can carry in one layer's
+ * time; a speculative request then fetches at most max(0, link_records - q'), q' the records the
+ * latest real split fetched (the layer's own), the first of its ranked misses.  Applies with the
+ * max_fetch of eff_set_speculation (the smaller cap wins) to the calls enqueued after it; -1 (the
+ * default) turns the cap off.  EFF_EINVAL below -1. */
+int eff_set_speculation_link(eff_engine* e, int link_records);
+
 /* Runtime cache rebuild ([FT-blog] §七 item 1; [FT-deep] §4 design pattern ⑦): the
  * slot cache is rebuilt with num_slots slots for a new HBM budget, without touching
  * the host pool.  Everything is checked, and the new slot arena, owner and usage
@@ -307,7 +315,10 @@ int eff_prefill_stream_layer(eff_engine* e, int layer, eff_stream_t side);
  * ids int32 [T,K] (expert ids from eff_route), w fp32 [T,K] -> out bf16 [T,H].
  * Groups the (t,k) pairs by expert and runs a grouped GEMM per expert on the
  * slot buffer of layer%2, then the weighted combine.  With S < 2E it loads the
- * routed experts on demand in groups of min(S,E) (waits on the host). */
+ * routed experts on demand in groups of min(S,E) (waits on the host).  The GEMMs
+ * take activations and the SwiGLU output as fp16: a value beyond 65504 is
+ * reported as EFF_EDEVICE by the next host-waiting call (this one included, for
+ * an earlier layer). */
 int eff_expert_ffn_prefill_layer(eff_engine* e, int layer, const void* x, const int32_t* ids,
                                  const float* w, int T, void* out, eff_stream_t stream);
 

@@ -4,7 +4,7 @@ Per call: routing ids, slots, host ids and counts bit for bit; expert outputs y
 and the combined bf16 output within rel-L2 <= 5e-3 and max-abs <= 2e-2.  Covers
 both weight formats, batch 1 and ragged batches (tokens per expert up to 16,
 more than one token chunk), every f of the tiny sweep, all-host (S = 0) and
-all-GPU partitions, speculative requests, and cache-size invariance on the GPU
+all-GPU partitions, speculative requests (with budget and link caps), and cache-size invariance on the GPU
 (bit-identical outputs for every S >= B*K when f = 65536)."""
 import numpy as np
 import pytest
@@ -29,14 +29,12 @@ def dev_bf16(a):
 
 
 def run_decode(eff, pool, K, S, f, B, tokens, router=True, zipf=1.1, spec_keep=-1.0, seed=11,
-               compare_y=True, flags=0, spec_budget=None, spec_gap=False):
+               compare_y=True, flags=0, spec_budget=None, spec_gap=False, spec_link=None):
     """Decode `tokens` steps through all layers on the GPU (eff_decode_layer) and the oracle."""
     L, E, H = pool.L, pool.E, pool.H
     eng = make_engine(eff, pool, K, S, B, f, flags=flags)
     orc = oracle_engine(pool, K, S, f)
-    if spec_budget is not None or spec_gap:
-        eng.set_speculation(-1 if spec_budget is None else spec_budget, spec_gap)
-        orc.cache.spec_budget = spec_budget
+    set_spec(eng, orc, spec_budget, spec_gap, spec_link)
     side = torch.cuda.Stream()
     outs = []
     try:
@@ -103,17 +101,25 @@ def test_tiny_decode_sync_host(eff, tiny_pool, f):
     assert np.array_equal(a, b)
 
 
-def run_ahead(eff, pool, K, S, f, B, tokens, zipf, seed, spec_keep=-1.0, flags=0, spec_budget=None,
-              spec_gap=False):
-    """Every layer of every token enqueued before a single synchronize (the host runs ahead of
-    the device; host shares and speculative copies are ordered on the device only); all outputs
-    and the final tables against the oracle (with the same speculative budget, if any)."""
-    L, E, H = pool.L, pool.E, pool.H
-    eng = make_engine(eff, pool, K, S, B, f, flags=flags)
-    orc = oracle_engine(pool, K, S, f)
+def set_spec(eng, orc, spec_budget, spec_gap, spec_link):
+    """The same speculative caps on the engine and the oracle policy (None: the defaults)."""
     if spec_budget is not None or spec_gap:
         eng.set_speculation(-1 if spec_budget is None else spec_budget, spec_gap)
         orc.cache.spec_budget = spec_budget
+    if spec_link is not None:
+        eng.set_speculation_link(spec_link)
+        orc.cache.spec_link = spec_link
+
+
+def run_ahead(eff, pool, K, S, f, B, tokens, zipf, seed, spec_keep=-1.0, flags=0, spec_budget=None,
+              spec_gap=False, spec_link=None):
+    """Every layer of every token enqueued before a single synchronize (the host runs ahead of
+    the device; host shares and speculative copies are ordered on the device only); all outputs
+    and the final tables against the oracle (with the same speculative caps, if any)."""
+    L, E, H = pool.L, pool.E, pool.H
+    eng = make_engine(eff, pool, K, S, B, f, flags=flags)
+    orc = oracle_engine(pool, K, S, f)
+    set_spec(eng, orc, spec_budget, spec_gap, spec_link)
     side = torch.cuda.Stream()
     try:
         xs, lgs, specs, outs = {}, {}, {}, {}
@@ -173,6 +179,51 @@ def test_decode_run_ahead_speculative_budget_gap(eff, B, budget, gap):
         assert st["spec_fetched"] > 0 and st["fetched"] > 0
     finally:
         pool.free()
+
+
+@pytest.mark.parametrize("B,link,budget,gap", [(16, 24, None, False), (16, 12, 3, True), (8, 0, None, True),
+                                               (8, 40, None, False)])
+def test_decode_run_ahead_speculative_link_cap(eff, B, link, budget, gap):
+    """The link cap on speculative fetches (the records one layer's link time carries, less the layer's
+    own real fetches), alone and with a budget, copied in either place, every layer enqueued before one
+    synchronize: outputs, counts and the final tables against the oracle policy with the same caps."""
+    print("run-ahead speculative link cap: B=%d link=%d budget=%s gap=%s" % (B, link, budget, gap), flush=True)
+    pool = PinnedPool(eff, 33, 4, 64, 2560, 640, synth.FMT_NVFP4)
+    try:
+        st = run_ahead(eff, pool, 10, 3 * B * 10 // 2, 65535, B, 4, 1.2, 33, spec_keep=0.65, spec_budget=budget,
+                       spec_gap=gap, spec_link=link)
+        assert st["fetched"] > 0
+        if link == 0:
+            assert st["spec_fetched"] == 0, st
+    finally:
+        pool.free()
+
+
+def test_speculation_link_cap_limits_guesses(eff):
+    """A link cap no smaller than any layer's real plus speculative fetches changes nothing; a small one
+    fetches fewer guesses; the outputs are the same every time (the pool is the source of truth)."""
+    pool = PinnedPool(eff, 22, 3, 32, 2560, 640, synth.FMT_NVFP4)
+    try:
+        kw = dict(router=False, zipf=1.2, spec_keep=0.65, seed=22)
+        ref, st0 = run_decode(eff, pool, 10, 40, 65535, 2, 4, **kw)
+        big, st1 = run_decode(eff, pool, 10, 40, 65535, 2, 4, spec_link=1000, **kw)
+        small, st2 = run_decode(eff, pool, 10, 40, 65535, 2, 4, spec_link=6, **kw)
+        assert np.array_equal(big, ref) and np.array_equal(small, ref)
+        keys = ("calls", "hits", "fetched", "host", "spec_fetched", "bytes_fetched")
+        assert {k: st1[k] for k in keys} == {k: st0[k] for k in keys}
+        assert st2["spec_fetched"] < st0["spec_fetched"]
+    finally:
+        pool.free()
+
+
+def test_set_speculation_link_rejects_bad_values(eff, tiny_pool):
+    eng = make_engine(eff, tiny_pool, TINY.K, TINY.S, 1, 32768)
+    try:
+        assert eff.lib().eff_set_speculation_link(eng.h, -2) == eff.EFF_EINVAL
+        assert eff.lib().eff_set_speculation_link(eng.h, -1) == 0
+        eng.set_speculation_link(5)
+    finally:
+        eng.close()
 
 
 @pytest.mark.parametrize("fmt,H,I,E,K,B,S,f,spec", [

@@ -98,3 +98,36 @@ def test_prefill_shapes(eff, fmt, H, I, E, K, T):
         run_prefill(eff, pool, K, 2 * E + 5, T, range(L), 31)
     finally:
         pool.free()
+
+
+def test_prefill_fp16_range_reported(eff):
+    """An activation beyond the fp16 range (the GEMMs take fp16 inputs) is reported as EFF_EDEVICE by
+    the next host-waiting call instead of flowing on as inf; a normal layer after it reports nothing."""
+    pool = PinnedPool(eff, TINY.seed, TINY.L, TINY.E, TINY.H, TINY.I, TINY.fmt)
+    T, E, K = 24, TINY.E, TINY.K
+    eng = make_engine(eff, pool, K, 2 * E, 1, 65536, max_prefill_tokens=T)
+    side = torch.cuda.Stream()
+    try:
+        X = synth.activations(TINY.seed, 0, 0, T, TINY.H, tag=synth.TAG_PREFILL_X).copy()
+        wr = synth.router_weights(TINY.seed, 0, E, TINY.H)
+        ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        out = torch.empty((T, TINY.H), dtype=torch.int16, device="cuda")
+        big = X.copy()
+        big[5, 7] = 0x47C3  # bf16 of 99840, above the fp16 maximum 65504
+        eng.prefill_stream_layer(0, side)
+        eng.route(dev_bf16(X), dev_bf16(wr), ids, w)   # routing from the in-range rows
+        eng.expert_ffn_prefill_layer(0, dev_bf16(big), ids, w, out)
+        torch.cuda.synchronize()
+        with pytest.raises(eff.EffError) as ei:
+            eng.snapshot_tables()
+        assert ei.value.code == eff.EFF_EDEVICE and "fp16" in str(ei.value)
+        # reported once; an in-range layer afterwards is clean
+        eng.prefill_stream_layer(1, side)
+        eng.route(dev_bf16(X), dev_bf16(wr), ids, w)
+        eng.expert_ffn_prefill_layer(1, dev_bf16(X), ids, w, out)
+        torch.cuda.synchronize()
+        eng.snapshot_tables()
+    finally:
+        eng.close()
+        pool.free()
