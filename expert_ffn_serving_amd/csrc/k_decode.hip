@@ -195,6 +195,37 @@ __device__ inline void run_tokens(const uint4 w, const Scales4& rs, const uint4*
   matrix_run<FMT, NT>(w, rs, xw, xs, nt, acc);
 }
 
+// The same for NT > 1 tokens whose 8 inputs are read from LDS (token j at sx[j * stride]): the 4 rows
+// are dequantized first and each token's activations read only when they meet them, so the
+// registers hold one token's activations at a time (same operations, same order as run_tokens).
+template <int FMT, int NT>
+__device__ inline void run_tokens_lds(const uint4 w, const Scales4& rs, const uint4* sx, int stride, int nt,
+                                      float (&acc)[4][NT]) {
+  float s[4];
+  scale_values<FMT>(rs, s);
+  const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
+  uint32_t p[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dequant_bf16<FMT>(d4[r], p[r]);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if (j >= nt) break;
+    uint32_t xw[4];
+    x_pairs<FMT>(sx[j * stride], xw);
+    float xs = 0.f;
+    if (FMT == EFF_WFMT_INT4_G32_BF16)
+      xs = dot2_bf16(xw[3], 0x3F803F80u, dot2_bf16(xw[2], 0x3F803F80u,
+                     dot2_bf16(xw[1], 0x3F803F80u, dot2_bf16(xw[0], 0x3F803F80u, 0.f))));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float raw = dot2_bf16(p[r][3], xw[3], dot2_bf16(p[r][2], xw[2], dot2_bf16(p[r][1], xw[1],
+                  dot2_bf16(p[r][0], xw[0], 0.f))));
+      if (FMT == EFF_WFMT_INT4_G32_BF16) raw = fmaf(-136.f, xs, raw);
+      acc[r][j] = fmaf(s[r], raw, acc[r][j]);
+    }
+  }
+}
+
 // adds v over the 16 lanes with the same l % 4 (bits 2..5 of the lane id) in a fixed order
 __device__ inline float sum16(float v) {
   v += __shfl_xor(v, 4);
@@ -255,6 +286,11 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   const bool tail = (KB & 3) != 0;          // a last run of 1..3 tiles (H % 128 != 0)
   const bool tail_lane = 4 * NRF + t4 < KB; // the lane's tile exists in that run
   const int H8 = H / 8;
+  // the wave's runs are wp, wp + P, ...: nr of them; past the last one (and where there is none) a
+  // load takes the last (or first) run again, so every load below is unconditional and the compiler
+  // keeps UNR of them in flight (a load behind a branch makes it wait for all of them at the join)
+  const int nr = NRF > wp ? (NRF - wp + P - 1) / P : 0;
+  const int rlast = wp + P * max(nr - 1, 0);
   for (int c0 = c_begin; c0 < c_end; c0 += NT) {
     const int nt = min(NT, c_end - c0);
     float acc[4][NT];
@@ -262,85 +298,67 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[r][j] = 0.f;
-    // A rolling pipeline over the wave's runs (every P-th run of its matrix slice): UNR register slots,
-    // each refilled with the run UNR ahead as soon as it has been used, so UNR runs stay in flight.
     uint4 wv[UNR], xg[NT == 1 ? UNR : 1];
     Scales4 rs[UNR];
-    const uint16_t* xt = x + (int64_t)(un->entry[c0] / K) * H + xo;  // NT == 1: the token's row
-    // NT > 1: the chunk's token rows go to LDS.  Their loads are issued first and the weights' after
-    // them, so the stores below wait for the rows only while the first weights are still in flight.
+    const uint16_t* xr = x + (int64_t)(un->entry[c0] / K) * H;  // NT == 1: the token's row
+    const uint16_t* xt = xr + xo;
+    // NT > 1: the chunk's token rows go to LDS.  Their loads are issued first (past the chunk's last
+    // token and past the row's end they repeat the last ones) and the weights' after them, so the
+    // stores below wait for the rows only while the first weights are still in flight.
     uint4 xs[NT > 1 ? NT : 1][2];
     if constexpr (NT > 1) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        if (j < nt) {
-          const uint16_t* row = x + (int64_t)(__builtin_amdgcn_readfirstlane(un->entry[c0 + j]) / K) * H;
+        const uint16_t* row = x + (int64_t)(__builtin_amdgcn_readfirstlane(un->entry[c0 + min(j, nt - 1)]) / K) * H;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int c = tid + h * kWG;
-            if (c < H8) xs[j][h] = *reinterpret_cast<const uint4*>(row + c * 8);
-          }
-        }
+        for (int h = 0; h < 2; ++h) xs[j][h] = *reinterpret_cast<const uint4*>(row + min(tid + h * kWG, H8 - 1) * 8);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    auto load_run = [&](int z, int r) {
+      wv[z] = *reinterpret_cast<const uint4*>(wp8 + (int64_t)r * 1024);
+      rs[z] = load_scales4<FMT>(sp8 + r * 128);
+      if constexpr (NT == 1) xg[z] = *reinterpret_cast<const uint4*>(xr + min(r * 128 + xo, H - 8));  // in the row
+    };
 #pragma unroll
-    for (int z = 0; z < UNR; ++z) {
-      const int r = wp + P * z;
-      if (r < NRF) {  // uniform
-        wv[z] = *reinterpret_cast<const uint4*>(wp8 + (int64_t)r * 1024);
-        rs[z] = load_scales4<FMT>(sp8 + r * 128);
-        if constexpr (NT == 1) xg[z] = *reinterpret_cast<const uint4*>(xt + r * 128);
-      }
-    }
+    for (int z = 0; z < UNR; ++z) load_run(z, min(wp + P * z, rlast));
     if constexpr (NT > 1) {
       __builtin_amdgcn_sched_barrier(0);
+      // unconditional stores too (rows past nt hold copies of the last one and are never read; a
+      // clamped column writes the value its own lane holds), so no load is sunk behind a branch
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        if (j < nt) {
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int c = tid + h * kWG;
-            if (c < H8) s_x[j * H8 + c] = xs[j][h];
-          }
-        }
-      }
+        for (int h = 0; h < 2; ++h) s_x[j * H8 + min(tid + h * kWG, H8 - 1)] = xs[j][h];
       __syncthreads();
     }
-    for (int r0 = wp; r0 < NRF; r0 += P * UNR) {
+    // a rolling pipeline: UNR register slots, each refilled with the run UNR ahead once it is used.
+    // Blocks of RB runs are unrolled whole (a loop back-edge makes the compiler wait for every load
+    // in flight at the loop head), so a wave with at most RB runs sees no back-edge at all.
+    constexpr int RB = 4 * UNR;
+    for (int i0 = 0; i0 < nr; i0 += RB) {
 #pragma unroll
-      for (int z = 0; z < UNR; ++z) {
-        const int r = r0 + P * z;
-        if (r < NRF) {  // uniform
-          if constexpr (NT == 1) {
-            run_tokens<FMT, NT>(wv[z], rs[z], &xg[z], 1, acc);
-          } else {
-            uint4 xv[NT];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) xv[j] = j < nt ? s_x[j * H8 + r * 16 + (lane >> 2)] : make_uint4(0, 0, 0, 0);
-            run_tokens<FMT, NT>(wv[z], rs[z], xv, nt, acc);
-          }
-          const int rn = r + P * UNR;
-          if (rn < NRF) {
-            wv[z] = *reinterpret_cast<const uint4*>(wp8 + (int64_t)rn * 1024);
-            rs[z] = load_scales4<FMT>(sp8 + rn * 128);
-            if constexpr (NT == 1) xg[z] = *reinterpret_cast<const uint4*>(xt + rn * 128);
-          }
+      for (int k = 0; k < RB; ++k) {
+        const int i = i0 + k, z = k % UNR, r = wp + P * i;
+        if (i >= nr) break;  // uniform
+        if constexpr (NT == 1) {
+          run_tokens<FMT, NT>(wv[z], rs[z], &xg[z], 1, acc);
+        } else {
+          run_tokens_lds<FMT, NT>(wv[z], rs[z], s_x + r * 16 + (lane >> 2), H8, nt, acc);
         }
+        load_run(z, min(r + P * UNR, rlast));
       }
     }
     if (tail && wp == NRF % P && tail_lane) {  // the last, partial run
       const int r = NRF;
       const uint4 w1 = *reinterpret_cast<const uint4*>(wp8 + (int64_t)r * 1024);
       const Scales4 s1 = load_scales4<FMT>(sp8 + r * 128);
-      uint4 xv[NT];
       if constexpr (NT == 1) {
-        xv[0] = *reinterpret_cast<const uint4*>(xt + r * 128);
+        const uint4 xv = *reinterpret_cast<const uint4*>(xt + r * 128);
+        run_tokens<FMT, NT>(w1, s1, &xv, 1, acc);
       } else {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) xv[j] = j < nt ? s_x[j * H8 + r * 16 + (lane >> 2)] : make_uint4(0, 0, 0, 0);
+        run_tokens_lds<FMT, NT>(w1, s1, s_x + r * 16 + (lane >> 2), H8, nt, acc);
       }
-      run_tokens<FMT, NT>(w1, s1, xv, NT == 1 ? 1 : nt, acc);
     }
     // rows 4g+r: the 16 lanes with the same g, then the matrix's waves in order (through LDS)
 #pragma unroll
@@ -478,46 +496,42 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   const bool tail = (KB & 3) != 0;
   const bool tail_lane = 4 * NRF + t4 < KB;
 
+  // the wave's runs are wp, wp + WPS, ...: nr of them; as in k_gateup every load below is unconditional
+  // (past the last run a load takes it again) so that the compiler keeps them in flight
+  const int nr = NRF > wp ? (NRF - wp + WPS - 1) / WPS : 0;
+  const int rlast = wp + WPS * max(nr - 1, 0);
   for (int c0 = c_begin; c0 < c_end; c0 += NT) {
     const int nt = min(NT, c_end - c0);
-    // the weights do not depend on the activations: start their loads first (a rolling pipeline of
-    // UNR slots, each refilled with the run UNR ahead as soon as it has been used)
+    // the tokens' activations (16 B per 8-group) and their (scale, sum) pairs: LPT loads per thread
+    // (the launcher keeps NT * I / 8 within LPT * kWG), issued before the weights' so that their LDS
+    // stores wait for them alone; past the chunk's last one a thread loads and stores that one again
+    constexpr int LPT = 4;
+    const int n = nt * I8;
+    uint4 va[LPT];
+    float2 vg[LPT];
+#pragma unroll
+    for (int k = 0; k < LPT; ++k) {
+      const int i = min(tid + k * kWG, n - 1);
+      const int64_t tok = (int64_t)u * maxB + c0 + i / I8;
+      va[k] = *reinterpret_cast<const uint4*>(a16 + tok * I + (i % I8) * 8);
+      vg[k] = ag[tok * I8 + i % I8];
+    }
+    asm volatile("" ::: "memory");  // keeps these loads ahead of the weights' (no code)
+    // the weights: a rolling pipeline of UNR slots, each refilled with the run UNR ahead once used
     uint4 wd[UNR];
     Scales4 rd[UNR];
+    auto load_run = [&](int z, int r) {
+      wd[z] = *reinterpret_cast<const uint4*>(dp + (int64_t)r * 1024);
+      rd[z] = load_scales4<FMT>(ds + r * 128);
+    };
 #pragma unroll
-    for (int z = 0; z < UNR; ++z) {
-      const int r = wp + WPS * z;
-      if (r < NRF) {
-        wd[z] = *reinterpret_cast<const uint4*>(dp + (int64_t)r * 1024);
-        rd[z] = load_scales4<FMT>(ds + r * 128);
-      }
-    }
-    // the tokens' activations (16 B per 8-group) and their (scale, sum) pairs into LDS, every load of
-    // a thread issued before its stores
-    {
-      constexpr int LPT = 4;
-      const int n = nt * I8;
-      for (int i0 = tid; i0 < n; i0 += LPT * kWG) {
-        uint4 va[LPT];
-        float2 vg[LPT];
+    for (int z = 0; z < UNR; ++z) load_run(z, min(wp + WPS * z, rlast));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k = 0; k < LPT; ++k) {
-          const int i = i0 + k * kWG;
-          if (i < n) {
-            const int64_t tok = (int64_t)u * maxB + c0 + i / I8;
-            va[k] = *reinterpret_cast<const uint4*>(a16 + tok * I + (i % I8) * 8);
-            vg[k] = ag[tok * I8 + i % I8];
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < LPT; ++k) {
-          const int i = i0 + k * kWG;
-          if (i < n) {
-            s_a4[i] = va[k];
-            s_ag[i] = vg[k];
-          }
-        }
-      }
+    for (int k = 0; k < LPT; ++k) {
+      const int i = min(tid + k * kWG, n - 1);
+      s_a4[i] = va[k];
+      s_ag[i] = vg[k];
     }
     __syncthreads();
     float acc[4][NT];
@@ -525,18 +539,14 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[r][j] = 0.f;
-    for (int r0 = wp; r0 < NRF; r0 += WPS * UNR) {
+    constexpr int RB = 2 * UNR;  // runs unrolled whole per block (no loop back-edge inside)
+    for (int i0 = 0; i0 < nr; i0 += RB) {
 #pragma unroll
-      for (int z = 0; z < UNR; ++z) {
-        const int r = r0 + WPS * z;
-        if (r < NRF) {
-          down_run<FMT, NT>(wd[z], rd[z], s_a4, s_ag, r * 16 + ai, nt, I8, acc);
-          const int rn = r + WPS * UNR;
-          if (rn < NRF) {
-            wd[z] = *reinterpret_cast<const uint4*>(dp + (int64_t)rn * 1024);
-            rd[z] = load_scales4<FMT>(ds + rn * 128);
-          }
-        }
+      for (int k = 0; k < RB; ++k) {
+        const int i = i0 + k, z = k % UNR, r = wp + WPS * i;
+        if (i >= nr) break;  // uniform
+        down_run<FMT, NT>(wd[z], rd[z], s_a4, s_ag, r * 16 + ai, nt, I8, acc);
+        load_run(z, min(r + WPS * UNR, rlast));
       }
     }
     if (tail && wp == NRF % WPS && tail_lane) {
@@ -687,7 +697,12 @@ hipError_t launch_down_t(eff_engine* e, const DecodePlan* plan, int units, int n
 // (61.6 against 67.8 us with 4) and 4-token chunks at B = 8 (36.0 against 48.0 us with 8); the down
 // rows are short, and 4-token chunks are faster there at both (B = 16: 35.7 against 45.5 us).
 int gateup_nt(int B) { return B >= 16 ? 8 : B >= 4 ? 4 : B >= 2 ? 2 : 1; }
-int down_nt(int B) { return B >= 4 ? 4 : B >= 2 ? 2 : 1; }
+// (the down kernel stages a chunk's activations with 4 loads per thread: N * I / 8 <= 1024)
+int down_nt(int B, int I) {
+  int n = B >= 4 ? 4 : B >= 2 ? 2 : 1;
+  while (n > 1 && n * I > 8192) n /= 2;
+  return n;
+}
 
 template <int FMT, int NT>
 hipError_t launch_gateup_p(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int B, hipStream_t s,
@@ -728,7 +743,7 @@ hipError_t launch_ffn_t(eff_engine* e, const DecodePlan* plan, uint16_t* a16, fl
   if (after_gateup && (err = hipEventRecord(after_gateup, s)) != hipSuccess) return err;
   timing_mark(e, ts, 1, s);
   timing_mark(e, ts, 2, s);
-  switch (down_nt(B)) {
+  switch (down_nt(B, e->cfg.inter)) {
     case 1: err = launch_down_w<FMT, 1>(e, plan, units, s, a16, ag, y); break;
     case 2: err = launch_down_w<FMT, 2>(e, plan, units, s, a16, ag, y); break;
     default: err = launch_down_w<FMT, 4>(e, plan, units, s, a16, ag, y); break;
@@ -742,7 +757,7 @@ hipError_t launch_ffn_t(eff_engine* e, const DecodePlan* plan, uint16_t* a16, fl
 hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
   // allow N * H * 2 bytes of dynamic LDS for the gate/up kernel and N * I * 3 for the down kernel,
   // for every token width N a call can take
-  const int NG = gateup_nt(maxB), ND = down_nt(maxB);
+  const int NG = gateup_nt(maxB), ND = down_nt(maxB, I);
   hipError_t err = hipSuccess;
   auto set = [&](const void* fn, int bytes) {
     if (err == hipSuccess) err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
