@@ -717,9 +717,10 @@ int eff_rebuild_cache(eff_engine* e, int num_slots, uint64_t max_arena_bytes) {
   const int64_t L = c.num_layers, E = c.num_experts;
   // geometry and budget, before anything else
   if (num_slots < 0 || num_slots > kMaxSlots) return fail(EFF_EREJECTED, "num_slots must be in [0, 16384]");
-  const uint64_t arena = num_slots > 0 ? (uint64_t)num_slots * (uint64_t)e->R + kArenaTail : 0;
-  if (max_arena_bytes > 0 && arena > max_arena_bytes)
+  const uint64_t slot_bytes = (uint64_t)num_slots * (uint64_t)e->R;
+  if (max_arena_bytes > 0 && slot_bytes > max_arena_bytes)
     return fail(EFF_EREJECTED, "the slot arena does not fit the byte budget");
+  const uint64_t arena = num_slots > 0 ? slot_bytes + kArenaTail : 0;
   // a safe point: no call half done
   if (e->pending_host) return fail(EFF_EREJECTED, "an ensure is waiting for its split");
   if (e->real_split_pending || e->spec_split_pending)
