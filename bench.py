@@ -10,12 +10,17 @@ value: the qwen3.8-flash-next decode end to end over its whole pool, the largest
   layers: control (top-K, ensure, split, speculative request, plan), in-kernel record fetches over
   PCIe, GPU expert FFN, host share, combine.  The slot cache is first warmed by the workload's 512
   trace tokens, then W untimed and K timed steps.  Inputs (x, trace logits, predictions) are resident
-  in HBM before timing.  B = 1 and 8 run beside it with the same settings.
+  in HBM before timing.  Speculative fetches are capped by the link: a request fetches at most G
+  records less the layer's own fetches, G the records the link (its rate alone, from the engine's
+  bandwidth profile) carries while the layer's expert kernels run with nothing to fetch (their
+  all-resident time at the same batch, below), i.e. the link time a layer leaves idle.  B = 1 and 8
+  run beside it with the same settings, and each batch also without speculation.
 
 Beside it (context, not `value`):
   roofline       the dominant kernel, the decode gate/up GEMV (k_gateup, NVFP4, 8-token chunks) at
                  the same expert shape and B = 16 with every expert resident (two layers streamed
-                 whole into the slots), timed with HIP events on its stream; algorithmic bytes per
+                 whole into the slots), timed with HIP events that the launch sets at the kernel's own
+                 start and end (on its stream); algorithmic bytes per
                  launch over its average duration.  In the end-to-end run a fetched record crosses
                  PCIe inside this kernel, which makes those launches link-bound: `link` reports them.
   decode_kernels the same for B = 1, 8, 16 and for the dsv4-flash expert shape (B = 1, 4).
@@ -116,7 +121,7 @@ def decode_inputs(torch, synth, W, L, B, n_steps):
 
 
 def e2e_run(eff, torch, W, pool, inputs, B, f, steps, warmup, warm_tokens, L=None, S=None, spec_budget=-1,
-            spec_gap=False, spec=True, threads=0, timing=False):
+            spec_gap=False, spec=True, threads=0, timing=False, spec_link=-1):
     """One end-to-end decode run on a fresh engine: the cache warmed by `warm_tokens` trace tokens,
     `warmup` untimed steps, then `steps` timed steps (bracketed by device synchronizations)."""
     ptr, ts, R = pool
@@ -126,6 +131,7 @@ def e2e_run(eff, torch, W, pool, inputs, B, f, steps, warmup, warm_tokens, L=Non
     cfg = eff.make_config(L, W.E, W.K, W.H, W.I, W.fmt, S, B, 0, f, threads)
     eng = eff.Engine(cfg, ptr, ts if W.fmt == 1 else None)
     eng.set_speculation(spec_budget, spec_gap)
+    eng.set_speculation_link(spec_link)
     comp, side = torch.cuda.Stream(), torch.cuda.Stream()
     L_, h = eff.lib(), eng.h
     cs, ss = comp.cuda_stream, side.cuda_stream
@@ -164,6 +170,7 @@ def e2e_run(eff, torch, W, pool, inputs, B, f, steps, warmup, warm_tokens, L=Non
     per = {k: round((s1[k] - s0[k]) / n, 3) for k in ("hits", "fetched", "host", "spec_fetched")}
     link = (per["fetched"] + per["spec_fetched"]) * R
     res = {"B": B, "frac_q16": f, "spec": use_spec, "spec_budget": spec_budget, "spec_in_gap": spec_gap,
+           "spec_link_records": spec_link if use_spec else None,
            "cache_warmup_tokens": n_warm * B, "warmup_steps": warmup, "steps": steps,
            "tok_s": round(steps * B / dt, 2), "ms_per_step": round(dt * 1e3 / steps, 3),
            "us_per_layer": round(dt * 1e6 / n, 1), "per_layer_call": per,
@@ -180,7 +187,7 @@ def e2e_run(eff, torch, W, pool, inputs, B, f, steps, warmup, warm_tokens, L=Non
     return res, dt
 
 
-def run_headline(eff, torch, synth, W, steps, warmup, threads, skip_variants=False):
+def run_headline(eff, torch, synth, W, steps, warmup, threads, compute_us, skip_variants=False):
     """The workload's end-to-end decode at B = 16 (value) and B = 1, 8, plus context variants."""
     log("decode end to end %s: L=%d E=%d K=%d H=%d I=%d S=%d f=%d spec keep %.2f" % (
         W.name, W.L, W.E, W.K, W.H, W.I, W.S, W.f_q16, W.spec_keep))
@@ -200,26 +207,46 @@ def run_headline(eff, torch, synth, W, steps, warmup, threads, skip_variants=Fal
     log("  bandwidth profile: link %.1f GB/s, host %.1f GB/s at once -> f = %d (workload: %d)" % (
         bw["pcie_concurrent"] / 1e9, bw["host_concurrent"] / 1e9, bw["frac_q16"], W.f_q16))
     head = None
+    link_Bps = bw["pcie_alone"]
+
+    def link_cap(B):
+        """Records the link (its rate alone) carries while the layer's expert kernels run with every
+        expert resident (gate/up + down at this batch, measured by decode_kernel_rates): the link
+        time a layer leaves when its own reads take none."""
+        return int(link_Bps * compute_us[B] * 1e-6 / R)
+
+    def show(tag, r):
+        log("  B=%d, %s (f=%d, link cap %s): %.2f tok/s (%.1f us per layer), per layer call %s, %.1f MB/layer over "
+            "the link (%.1f GB/s)" % (r["B"], tag, r["frac_q16"], r["spec_link_records"], r["tok_s"], r["us_per_layer"],
+                                      r["per_layer_call"], r["link_MB_per_layer"], r["link_GBps"]))
+
     for B in sorted(W.batches, reverse=True):
         n_steps = (W.warmup_tokens + B - 1) // B + warmup + steps
         inputs = decode_inputs(torch, synth, W, W.L, B, n_steps)
-        r, dt = e2e_run(eff, torch, W, pool, inputs, B, W.f_q16, steps, warmup, W.warmup_tokens, threads=threads)
+
+        def run(f, **kw):
+            return e2e_run(eff, torch, W, pool, inputs, B, f, steps, warmup, W.warmup_tokens, threads=threads, **kw)
+
+        # speculation reads guesses only in the link time the layer's real reads leave ([NVMe-8GB] "엔진"
+        # item 3): the cap is the link's records per layer of the same step without speculation
+        nospec, _ = run(W.f_q16, spec=False)
+        res["B%d_nospec" % B] = nospec
+        show("no speculation", nospec)
+        r, dt = run(W.f_q16, spec_link=link_cap(B))
         res["B%d" % B] = r
-        log("  B=%d, workload settings: %.2f tok/s (%.1f us per layer), per layer call %s, %.1f MB/layer over "
-            "the link (%.1f GB/s)" % (B, r["tok_s"], r["us_per_layer"], r["per_layer_call"], r["link_MB_per_layer"],
-                                      r["link_GBps"]))
+        show("workload settings", r)
         if B == 16:
             head = (r, dt)
             if not skip_variants:
-                for tag, f, budget, gap, sp in (("nospec", W.f_q16, -1, False, False),
-                                                ("gap2", W.f_q16, 2, True, True),
-                                                ("profiled_f", bw["frac_q16"], -1, False, True),
-                                                ("profiled_f_nospec", bw["frac_q16"], -1, False, False)):
-                    rv, _ = e2e_run(eff, torch, W, pool, inputs, B, f, steps, warmup, W.warmup_tokens,
-                                    spec_budget=budget, spec_gap=gap, spec=sp, threads=threads)
-                    res["B16_" + tag] = rv
-                    log("  B=16, %s (f=%d): %.2f tok/s, per layer call %s" % (tag, f, rv["tok_s"],
-                                                                             rv["per_layer_call"]))
+                rv, _ = run(W.f_q16)
+                res["B16_spec_uncapped"] = rv
+                show("speculation without the link cap", rv)
+                pn, _ = run(bw["frac_q16"], spec=False)
+                res["B16_profiled_f_nospec"] = pn
+                show("profiled f, no speculation", pn)
+                pc, _ = run(bw["frac_q16"], spec_link=link_cap(B))
+                res["B16_profiled_f"] = pc
+                show("profiled f", pc)
         del inputs
         torch.cuda.empty_cache()
     eff.host_free(ptr)
@@ -231,7 +258,7 @@ def decode_kernel_rates(eff, torch, synth, W, batches, tokens=64, threads=0, lab
     """HBM rates of the decode expert kernels at a workload's expert shape: layers 0 and 1 streamed
     whole into the two slot buffers (S = 2E, every expert resident, no call misses), then `tokens`
     decode steps per batch size on the workload's Zipf trace, alternating the two layers, with the
-    expert kernels bracketed by HIP events on their stream (EFF_CFG_TIMING)."""
+    expert kernels timed by HIP events that each launch sets at its kernel's start and end (EFF_CFG_TIMING)."""
     import numpy as np
     pool = fill_pool(eff, synth, W.seed, 2, W.E, W.H, W.I, W.fmt)
     ptr, ts, R = pool
@@ -537,12 +564,14 @@ def prefill_oracle(synth, W, pool, tokens, threads):
                                                                     W.prefill_T // tokens, W.E)}
 
 
-def cpu_baseline(eff, synth, W, tokens, threads, tokens_1core=1):
+def cpu_baseline(eff, synth, W, tokens, threads, layers_1core=6):
     """The oracle as it stands on the headline workload's decode: `tokens` tokens (B = 1) through every
-    layer of the same trace from a cold cache, on `threads` threads, and the first `tokens_1core` on
-    one thread; its tok/s is per token of that sample.  Only the records the sample routes to are
-    generated (the generator keys a record by its flat id, so they are the pool's)."""
+    layer of the same trace from a cold cache, on `threads` threads, and the first token's first
+    `layers_1core` layers on one thread (scaled to a whole token); tok/s per token of that sample.  Only
+    the records the sample routes to are generated (the generator keys a record by its flat id, so they
+    are the pool's); their generation is not timed."""
     import ctypes
+    from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
 
@@ -552,24 +581,26 @@ def cpu_baseline(eff, synth, W, tokens, threads, tokens_1core=1):
     xs = [synth.activations(W.seed, l, 0, tokens, W.H) for l in range(W.L)]
     flats = sorted({l * W.E + int(e) for l in range(W.L) for row in synth.gumbel_topk_sets(lg[l], W.K) for e in row})
     buf = np.empty((len(flats), R), np.uint8)
-    tsb = np.empty(len(flats) * 3, np.float32)
-    for i, fl in enumerate(flats):
-        t3 = np.empty(3, np.float32)
-        synth.fill_records(W.seed, W.E, W.H, W.I, W.fmt, fl, 1, buf[i].ctypes.data, t3, 1)
-        tsb[3 * i:3 * i + 3] = t3
+    tsb = np.empty((len(flats), 3), np.float32)
+
+    def gen(i):
+        synth.fill_records(W.seed, W.E, W.H, W.I, W.fmt, flats[i], 1, buf[i].ctypes.data, tsb[i], 1)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(gen, range(len(flats))))
     where = {fl: i for i, fl in enumerate(flats)}
 
-    def timed(n, nthreads):
+    def timed(n, nthreads, layers):
         eng = OracleEngine(W.L, W.E, W.K, W.H, W.I, W.fmt, W.S, W.f_q16, lambda f: buf[where[f]],
-                           lambda f: tsb[3 * where[f]:3 * where[f] + 3], use_c=True, nthreads=nthreads)
+                           lambda f: tsb[where[f]], use_c=True, nthreads=nthreads)
         t0 = time.perf_counter()
         for t in range(n):
-            for l in range(W.L):
+            for l in range(layers):
                 eng.decode_layer(l, xs[l][t:t + 1], logits=lg[l][t:t + 1])
-        return n / (time.perf_counter() - t0)
+        return n * layers / W.L / (time.perf_counter() - t0)
 
-    value = timed(tokens, threads)
-    one = timed(tokens_1core, 1)
+    value = timed(tokens, threads, W.L)
+    one = timed(1, 1, layers_1core)
     info = host_cpu()
     ptr = eff.host_alloc(2 << 30)
     try:
@@ -577,12 +608,13 @@ def cpu_baseline(eff, synth, W, tokens, threads, tokens_1core=1):
         rd = host_read_gbps(ptr, 2 << 30, threads)
     finally:
         eff.host_free(ptr)
-    return {"value": round(value, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": "%d tokens (B = 1) x %d layers of the %s trace from a cold cache (all records the sample "
-                      "routes to); fp64 C evaluator on %d threads plus single-threaded NumPy routing and policy" % (
-                          tokens, W.L, W.name, threads),
-            "value_1core": round(one, 3),
-            "sample_1core": "the first %d token(s) of the same sample on 1 thread" % tokens_1core,
+    return {"value": round(value, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": "%d token(s) (B = 1) x %d layers of the %s trace from a cold cache (all records the sample "
+                      "routes to, generated beforehand); fp64 C evaluator on %d threads plus single-threaded "
+                      "NumPy routing and policy" % (tokens, W.L, W.name, threads),
+            "value_1core": round(one, 4),
+            "sample_1core": "the first %d of the first token's %d layers on 1 thread, scaled to a whole token" % (
+                layers_1core, W.L),
             "host_cpu": info, "host_read_GBps": rd,
             "host_read_probe": "NumPy sums over 2 GiB of pinned host memory, %d threads, best of 3" % threads}
 
@@ -595,7 +627,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5, help="untimed steps after the cache warm-up")
     ap.add_argument("--kernel-tokens", type=int, default=64, help="decode steps per batch in the kernel passes")
     ap.add_argument("--prefill-layers", type=int, default=6)
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=1)
     ap.add_argument("--threads", type=int, default=0,
                     help="host executor threads (0: one per physical core, one core left for the enqueuing thread)")
     ap.add_argument("--skip-prefill", action="store_true")
@@ -623,24 +655,28 @@ def main():
         counters_pass(eff, torch, synth, QWEN_NEXT, B=16, tokens=args.kernel_tokens, threads=args.threads)
         return
     W = QWEN_NEXT
-    head_res, (head, dt) = run_headline(eff, torch, synth, W, args.steps, args.warmup, args.threads,
-                                        skip_variants=args.skip_context)
-    # the dominant kernel at the same shape and batch, every expert resident
+    # the dominant kernel at the headline's shape and batches, every expert resident (first: the
+    # headline's speculative link cap takes the expert kernels' time from it)
     log("decode kernels %s (2 layers resident)" % W.name)
     kq = decode_kernel_rates(eff, torch, synth, W, W.batches, args.kernel_tokens, args.threads)
     k16 = kq["B16"]
+    compute_us = {B: kq["B%d" % B]["gateup_us"] + kq["B%d" % B]["down_us"] for B in W.batches}
+    head_res, (head, dt) = run_headline(eff, torch, synth, W, args.steps, args.warmup, args.threads, compute_us,
+                                        skip_variants=args.skip_context)
     srcs = ("k_decode.hip",)
     roofline = {
         "bound": "hbm", "achieved": k16["gateup_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": k16["gateup_frac"], "traffic": traffic_from_profile(TRAFFIC_FILE, srcs),
-        "kernel": "k_gateup<NVFP4, 8> (decode gate+up GEMV with SwiGLU, B = 16, one launch per layer call)",
+        "kernel": "k_gateup<NVFP4, 8, 1> (decode gate+up GEMV with SwiGLU, B = 16, one launch per layer call)",
         "workload": "%s expert shape, B = 16, every expert resident (2 layers streamed whole into the slots), "
                     "%d steps x 2 layers of the workload's Zipf(%.1f) trace" % (W.name, args.kernel_tokens, W.zipf_s),
         "algorithmic_bytes_per_launch": k16["gateup_alg_bytes_per_launch"],
         "gpu_experts_per_launch": k16["gpu_experts_per_launch"], "avg_launch_us": k16["gateup_us"],
-        "launches": k16["launches"], "timed_as": "HIP events on the kernel's stream around each launch",
+        "launches": k16["launches"],
+        "timed_as": "HIP events that each launch sets at its kernel's start and end (hipExtLaunchKernelGGL), "
+                    "on the kernel's stream",
         "source_sha": src_hash(*srcs),
-        "down": {"kernel": "k_down<NVFP4, 8, 4>", "achieved": k16["down_GBps"], "frac": k16["down_frac"],
+        "down": {"kernel": "k_down<NVFP4, 4, 1>", "achieved": k16["down_GBps"], "frac": k16["down_frac"],
                  "algorithmic_bytes_per_launch": k16["down_alg_bytes_per_launch"], "avg_launch_us": k16["down_us"]},
     }
     link = {"bound": "pcie", "achieved_GBps": head["link_GBps"],
@@ -694,7 +730,8 @@ def main():
         "config": {"workload": W.name, "layers": W.L, "experts": W.E, "top_k": W.K, "hidden": W.H, "inter": W.I,
                    "weights": "nvfp4 (e2m1, e4m3 per 16, fp32 per matrix)", "record_bytes": head_res["record_bytes"],
                    "slots": W.S, "fetch_frac_q16": W.f_q16, "batch": B, "routing": "zipf(%.1f) trace" % W.zipf_s,
-                   "speculative_keep": W.spec_keep, "cache_warmup_tokens": head["cache_warmup_tokens"],
+                   "speculative_keep": W.spec_keep, "speculative_link_cap_records": head["spec_link_records"],
+                   "cache_warmup_tokens": head["cache_warmup_tokens"],
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "link": link,

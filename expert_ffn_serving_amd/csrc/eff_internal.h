@@ -298,8 +298,13 @@ hipError_t launch_ffn_decode_noalloc(eff_engine* e, const uint16_t* x, const int
 hipError_t launch_control(eff_engine* e, int layer, const float* logits, int B, const uint16_t* x,
                           const int32_t* spec_ids, hipStream_t s);
 // timing hooks: returns the call's event slot (or -1 when timing is off); mark(i) records event i
-int timing_begin(eff_engine* e, int kind, hipStream_t s);
+// (record_first = false: event 0 is left for the launch itself to set)
+int timing_begin(eff_engine* e, int kind, hipStream_t s, bool record_first = true);
 void timing_mark(eff_engine* e, int slot, int i, hipStream_t s);
+// event i of a timed call (nullptr when the slot is -1): a launcher can hand events 0/1 and 2/3 to
+// hipExtLaunchKernelGGL, which sets them at its kernel's start and end (the kernel's own duration)
+hipEvent_t timing_event(eff_engine* e, int slot, int i);
+bool stream_capturing(hipStream_t s);
 hipError_t launch_combine(const float* ygpu, const float* yhost, const int32_t* slots, const float* w,
                           int B, int K, int H, uint16_t* out, hipStream_t s, const uint64_t* done = nullptr,
                           const uint64_t* seq = nullptr, int32_t* err = nullptr);

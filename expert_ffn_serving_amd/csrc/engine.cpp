@@ -212,7 +212,7 @@ static void resolve_timing(eff_engine* e) {
   e->timed.clear();
 }
 
-int timing_begin(eff_engine* e, int kind, hipStream_t s) {
+int timing_begin(eff_engine* e, int kind, hipStream_t s, bool record_first) {
   if (!(e->cfg.flags & EFF_CFG_TIMING)) return -1;
   if (e->timed.size() >= (size_t)kTimedMax) resolve_timing(e);  // bounded number of live events
   eff_engine::TimedCall tc;
@@ -226,8 +226,18 @@ int timing_begin(eff_engine* e, int kind, hipStream_t s) {
              hipMemcpyAsync(e->h_tq + 2 * slot + 1, &e->d_plan->nu, sizeof(int32_t), hipMemcpyDeviceToHost, s) ==
                  hipSuccess;
   e->timed.push_back(tc);
-  timing_mark(e, slot, 0, s);
+  if (record_first) timing_mark(e, slot, 0, s);
   return slot;
+}
+
+hipEvent_t timing_event(eff_engine* e, int slot, int i) {
+  if (slot < 0 || slot >= (int)e->timed.size()) return nullptr;
+  return e->timed[slot].ev[i];
+}
+
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
 }
 
 void timing_mark(eff_engine* e, int slot, int i, hipStream_t s) {

@@ -26,6 +26,8 @@
 //   e2m1   v_cvt_scalef32_pk_{bf16,f16}_fp4 with scale 1.0 (the instruction uses
 //          only the exponent of its scale operand, so the e4m3 block scale is
 //          applied afterwards in fp32); e4m3 via v_cvt_f32_fp8 (OCP E4M3FN).
+#include <hip/hip_ext.h>
+
 #include <mutex>
 
 #include "eff_internal.h"
@@ -670,25 +672,37 @@ int down_wps(int slices, int runs) {
   return slices >= 1024 ? 2 : 4;
 }
 
+// With events (t0, t1) the launch sets them at the kernel's own start and end (hipExtLaunchKernelGGL):
+// the timing then covers the kernel alone, as a profiler's kernel trace does.
 template <int FMT, int NT, int P>
 hipError_t launch_gateup_t(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int nch, hipStream_t s,
-                           uint16_t* a16, float2* ag) {
+                           uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
-  hipLaunchKernelGGL((k_gateup<FMT, NT, P>), dim3(units * nch * (I / 16) * P / 2), dim3(kWG),
-                     (size_t)(NT > 1 ? NT * H * 2 : 0), s, e->d_arena, e->pool_dev, e->R, e->d_ts, plan, x, H, I,
-                     c.top_k, c.max_tokens, nch, a16, ag);
+  const dim3 grid(units * nch * (I / 16) * P / 2), block(kWG);
+  const uint32_t lds = NT > 1 ? NT * H * 2 : 0;
+  if (t0)
+    hipExtLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R,
+                          e->d_ts, plan, x, H, I, c.top_k, c.max_tokens, nch, a16, ag);
+  else
+    hipLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, e->d_ts, plan, x,
+                       H, I, c.top_k, c.max_tokens, nch, a16, ag);
   return hipGetLastError();
 }
 
 template <int FMT, int NT, int WPS>
 hipError_t launch_down_t(eff_engine* e, const DecodePlan* plan, int units, int nch, hipStream_t s, const uint16_t* a16,
-                         const float2* ag, float* y) {
+                         const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
-  const size_t lds = (size_t)NT * (I / 8) * (sizeof(uint4) + sizeof(float2));
-  hipLaunchKernelGGL((k_down<FMT, NT, WPS>), dim3(units * nch * (H / 16) * WPS / 4), dim3(kWG), lds, s, e->d_arena,
-                     e->pool_dev, e->R, e->d_ts, plan, a16, ag, H, I, c.max_tokens, nch, y);
+  const uint32_t lds = (uint32_t)(NT * (I / 8) * (sizeof(uint4) + sizeof(float2)));
+  const dim3 grid(units * nch * (H / 16) * WPS / 4), block(kWG);
+  if (t0)
+    hipExtLaunchKernelGGL((k_down<FMT, NT, WPS>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R,
+                          e->d_ts, plan, a16, ag, H, I, c.max_tokens, nch, y);
+  else
+    hipLaunchKernelGGL((k_down<FMT, NT, WPS>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, e->d_ts, plan, a16,
+                       ag, H, I, c.max_tokens, nch, y);
   return hipGetLastError();
 }
 
@@ -706,22 +720,22 @@ int down_nt(int B, int I) {
 
 template <int FMT, int NT>
 hipError_t launch_gateup_p(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int B, hipStream_t s,
-                           uint16_t* a16, float2* ag) {
+                           uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1) {
   const int nch = (B + NT - 1) / NT;  // token chunks a unit can have (a unit holds at most one entry per token)
   if (gateup_waves_per_matrix(units * (e->cfg.inter / 16)) == 1)
-    return launch_gateup_t<FMT, NT, 1>(e, plan, x, units, nch, s, a16, ag);
-  return launch_gateup_t<FMT, NT, 2>(e, plan, x, units, nch, s, a16, ag);
+    return launch_gateup_t<FMT, NT, 1>(e, plan, x, units, nch, s, a16, ag, t0, t1);
+  return launch_gateup_t<FMT, NT, 2>(e, plan, x, units, nch, s, a16, ag, t0, t1);
 }
 
 template <int FMT, int NT>
 hipError_t launch_down_w(eff_engine* e, const DecodePlan* plan, int units, hipStream_t s, const uint16_t* a16,
-                         const float2* ag, float* y) {
+                         const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1) {
   // the down kernel takes a unit's chunks in turn: its rows are short (I inputs), so a second wave of
   // workgroups per unit costs more than the chunks' arithmetic it would spread
   switch (down_wps(units * (e->cfg.hidden / 16), e->cfg.inter / 128)) {
-    case 1: return launch_down_t<FMT, NT, 1>(e, plan, units, 1, s, a16, ag, y);
-    case 2: return launch_down_t<FMT, NT, 2>(e, plan, units, 1, s, a16, ag, y);
-    default: return launch_down_t<FMT, NT, 4>(e, plan, units, 1, s, a16, ag, y);
+    case 1: return launch_down_t<FMT, NT, 1>(e, plan, units, 1, s, a16, ag, y, t0, t1);
+    case 2: return launch_down_t<FMT, NT, 2>(e, plan, units, 1, s, a16, ag, y, t0, t1);
+    default: return launch_down_t<FMT, NT, 4>(e, plan, units, 1, s, a16, ag, y, t0, t1);
   }
 }
 
@@ -731,24 +745,31 @@ hipError_t launch_down_w(eff_engine* e, const DecodePlan* plan, int units, hipSt
 template <int FMT>
 hipError_t launch_ffn_t(eff_engine* e, const DecodePlan* plan, uint16_t* a16, float2* ag, const uint16_t* x, float* y,
                         int units, int B, hipStream_t s, hipEvent_t after_gateup, bool timed) {
-  const int ts = timed ? timing_begin(e, EFF_T_DECODE_GATEUP, s) : -1;
+  // timed outside a capture: each kernel sets its own start and end events; inside a capture the
+  // events are recorded on the stream around the launches
+  const bool own = timed && !stream_capturing(s);
+  const int ts = timed ? timing_begin(e, EFF_T_DECODE_GATEUP, s, !own) : -1;
+  hipEvent_t g0 = own ? timing_event(e, ts, 0) : nullptr, g1 = own ? timing_event(e, ts, 1) : nullptr;
+  hipEvent_t d0 = own ? timing_event(e, ts, 2) : nullptr, d1 = own ? timing_event(e, ts, 3) : nullptr;
   hipError_t err;
   switch (gateup_nt(B)) {
-    case 1: err = launch_gateup_p<FMT, 1>(e, plan, x, units, B, s, a16, ag); break;
-    case 2: err = launch_gateup_p<FMT, 2>(e, plan, x, units, B, s, a16, ag); break;
-    case 4: err = launch_gateup_p<FMT, 4>(e, plan, x, units, B, s, a16, ag); break;
-    default: err = launch_gateup_p<FMT, 8>(e, plan, x, units, B, s, a16, ag); break;
+    case 1: err = launch_gateup_p<FMT, 1>(e, plan, x, units, B, s, a16, ag, g0, g1); break;
+    case 2: err = launch_gateup_p<FMT, 2>(e, plan, x, units, B, s, a16, ag, g0, g1); break;
+    case 4: err = launch_gateup_p<FMT, 4>(e, plan, x, units, B, s, a16, ag, g0, g1); break;
+    default: err = launch_gateup_p<FMT, 8>(e, plan, x, units, B, s, a16, ag, g0, g1); break;
   }
   if (err != hipSuccess) return err;
   if (after_gateup && (err = hipEventRecord(after_gateup, s)) != hipSuccess) return err;
-  timing_mark(e, ts, 1, s);
-  timing_mark(e, ts, 2, s);
-  switch (down_nt(B, e->cfg.inter)) {
-    case 1: err = launch_down_w<FMT, 1>(e, plan, units, s, a16, ag, y); break;
-    case 2: err = launch_down_w<FMT, 2>(e, plan, units, s, a16, ag, y); break;
-    default: err = launch_down_w<FMT, 4>(e, plan, units, s, a16, ag, y); break;
+  if (!own) {
+    timing_mark(e, ts, 1, s);
+    timing_mark(e, ts, 2, s);
   }
-  timing_mark(e, ts, 3, s);
+  switch (down_nt(B, e->cfg.inter)) {
+    case 1: err = launch_down_w<FMT, 1>(e, plan, units, s, a16, ag, y, d0, d1); break;
+    case 2: err = launch_down_w<FMT, 2>(e, plan, units, s, a16, ag, y, d0, d1); break;
+    default: err = launch_down_w<FMT, 4>(e, plan, units, s, a16, ag, y, d0, d1); break;
+  }
+  if (!own) timing_mark(e, ts, 3, s);
   return err;
 }
 

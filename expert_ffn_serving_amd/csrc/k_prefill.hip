@@ -22,6 +22,8 @@
 // as fp16 (bf16 inputs convert exactly inside fp16's normal range); an input or
 // SwiGLU output beyond the fp16 range sets bit 8 of the engine's device error
 // word, which the next host-waiting call reports, instead of passing an inf on.
+#include <hip/hip_ext.h>
+
 #include "eff_internal.h"
 
 namespace eff {
@@ -429,12 +431,15 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
   const bool fp4 = c.wformat == EFF_WFMT_NVFP4_G16_E4M3;
   const int nbx1 = ((E + 7) / 8) * 8 * ((I / 64 + 3) / 4);
   const int nbx2 = ((E + 7) / 8) * 8 * ((H / 64 + 3) / 4);
-  const int ts = timing_begin(e, EFF_T_PREFILL_GATEUP, s);
+  // timed outside a capture: each GEMM sets its own start and end events (its own duration)
+  const bool own = (c.flags & EFF_CFG_TIMING) && !stream_capturing(s);
+  const int ts = timing_begin(e, EFF_T_PREFILL_GATEUP, s, !own);
+  hipEvent_t t0 = own ? timing_event(e, ts, 0) : nullptr, t1 = own ? timing_event(e, ts, 1) : nullptr;
   const bool full = H % 256 == 0 && I % 256 == 0;
-#define EFF_PF_LAUNCH(F, NM, PFD, FU, GRID, SRC, AO, YO)                                                     \
-  hipLaunchKernelGGL((k_pf_gemm<F, NM, PFD, FU>), dim3(GRID), dim3(256 * NM), 0, s, e->d_arena, e->R, e->d_ts, \
-                     e->d_owner, slot_base, slot_of_expert, e->d_pf_count, e->d_pf_rows, SRC, E, H, I, K, AO, YO,    \
-                     e->h_err_dev)
+#define EFF_PF_LAUNCH(F, NM, PFD, FU, GRID, SRC, AO, YO)                                                        \
+  hipExtLaunchKernelGGL((k_pf_gemm<F, NM, PFD, FU>), dim3(GRID), dim3(256 * NM), 0, s, t0, t1, 0, e->d_arena, e->R, \
+                        e->d_ts, e->d_owner, slot_base, slot_of_expert, (const int32_t*)e->d_pf_count,          \
+                        (const int32_t*)e->d_pf_rows, (const uint16_t*)(SRC), E, H, I, K, AO, YO, e->h_err_dev)
 #define EFF_PF_PICK(NM, PFD, FU, GRID, SRC, AO, YO)                                           \
   do {                                                                                        \
     if (fp4) {                                                                                \
@@ -447,13 +452,17 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
   } while (0)
   EFF_PF_PICK(2, kPfPrefetch2, full, nbx1, x, e->d_pf_a, (float*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  timing_mark(e, ts, 1, s);
-  timing_mark(e, ts, 2, s);
+  if (!own) {
+    timing_mark(e, ts, 1, s);
+    timing_mark(e, ts, 2, s);
+  }
+  t0 = own ? timing_event(e, ts, 2) : nullptr;
+  t1 = own ? timing_event(e, ts, 3) : nullptr;
   EFF_PF_PICK(1, kPfPrefetch1, full, nbx2, e->d_pf_a, (uint16_t*)nullptr, e->d_pf_y);
 #undef EFF_PF_PICK
 #undef EFF_PF_LAUNCH
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  timing_mark(e, ts, 3, s);
+  if (!own) timing_mark(e, ts, 3, s);
   if (!combine) return hipSuccess;
   return launch_combine(e->d_pf_y, nullptr, nullptr, w, T, K, H, out, s);
 }

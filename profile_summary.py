@@ -8,8 +8,10 @@
         counter is scaled by what it reads for the largest plain device-to-device copy in the same
         run (a copy of --copy-bytes bytes reads and writes exactly that many bytes).
     python3 profile_summary.py trace DIR --kernel 'k_gateup<0, 1>' --last 2560
+    python3 profile_summary.py trace DIR --kernel 'k_gateup<1, 8, 1>' --skip-first 2 --first 128
         average duration of a kernel's dispatches in DIR/**/*kernel_trace.csv, over all of them and
-        over the last N by start time (the window a bench times last, e.g. its profiled pass).
+        over a window by start time: the last N, or the first N after skipping some (the pass a
+        bench times, e.g. its first one).
 
 Counters are KiB per dispatch.  On gfx950 FETCH_SIZE reads about half of the bytes a copy
 actually fetches, which is why every figure is calibrated against the copy instead of trusted raw.
@@ -130,11 +132,15 @@ def cmd_trace(a):
     for k in sorted(names):
         d = [x[1] for x in data[k]]
         head = d[:len(d) - a.skip] if a.skip > 0 else d
-        tail = head[-a.last:] if a.last > 0 else head
+        if a.first > 0:   # a window from the start instead: skip_first dispatches, then `first` of them
+            tail = head[a.skip_first:a.skip_first + a.first]
+        else:
+            tail = head[-a.last:] if a.last > 0 else head
         if not tail:
             raise SystemExit("no dispatches of %s left after skipping %d" % (k, a.skip))
         res[k] = {"dispatches": len(d), "avg_us": round(sum(d) / len(d) / 1e3, 3),
-                  "skipped": a.skip, "last": len(tail), "last_avg_us": round(sum(tail) / len(tail) / 1e3, 3),
+                  "skipped": a.skip, "skipped_first": a.skip_first, "window": len(tail),
+                  "last": len(tail), "last_avg_us": round(sum(tail) / len(tail) / 1e3, 3),
                   "last_min_us": round(min(tail) / 1e3, 3), "last_max_us": round(max(tail) / 1e3, 3)}
     print(json.dumps(res, indent=1))
     return res
@@ -160,6 +166,8 @@ def main(argv=None):
     r.add_argument("--kernel", required=True)
     r.add_argument("--last", type=int, default=0)
     r.add_argument("--skip", type=int, default=0, help="leave out the last N dispatches before taking the window")
+    r.add_argument("--first", type=int, default=0, help="window: the first N dispatches (after --skip-first)")
+    r.add_argument("--skip-first", type=int, default=0)
     a = p.parse_args(argv)
     {"counters": cmd_counters, "traffic": cmd_traffic, "trace": cmd_trace}[a.cmd](a)
 
