@@ -91,6 +91,28 @@ __device__ inline void wg_copy(const uint8_t* __restrict__ src, uint8_t* __restr
   for (; i < n4; i += kWG) d4[i] = s4[i];
 }
 
+// LDS byte address of a shared array (uniform)
+template <typename T>
+__device__ inline uint32_t lds_address(T* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)p));
+}
+
+// 16 bytes per lane from src (the lane's own address) straight into LDS at lds + 16 * lane (lds
+// uniform), without a register: global_load_lds_dwordx4.  The compiler does not see this write, so the
+// caller waits for it with vm_wait before anything reads the bytes.  It sets M0, which no other code
+// in these kernels uses (M0 is on the clobber list).
+__device__ inline void lds_copy16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// waits until at most N vector memory operations of this wave are outstanding.  Loads complete in the
+// order they were issued, so once N is the number of loads issued after a given LDS copy, that copy
+// is complete (stores issued meanwhile only make the wait stricter).
+template <int N>
+__device__ inline void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // the lane's scale word inside a tile's 32 scale bytes (NVFP4: 4 bytes; int4: 8 bytes)
 template <int FMT>
 __device__ inline int lane_scale_off(int q, int g) {
@@ -252,7 +274,7 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   static_assert(P == 1 || P == 2, "1 or 2 waves per matrix of a slice");
   constexpr int SPW = 2 / P;                      // slices per workgroup
   constexpr int UNR = NT == 1 ? 4 : NT == 2 ? 8 : NT == 4 ? 6 : 4;  // runs in flight per wave
-  extern __shared__ uint4 s_x[];                  // NT > 1: [NT][H/8], the token rows of the current chunk
+  extern __shared__ uint4 s_x[];                  // NT > 1: [NT][H/8] token rows of the chunk, 1 KiB slack
   __shared__ float s_red[4][16][NT];
   const int NS = I / 16, NG = NS / SPW, KB = H / 32, NRF = KB / 4;
   const int u = blockIdx.x / (NG * nch), ch = (blockIdx.x / NG) % nch, sgp = blockIdx.x % NG;
@@ -304,18 +326,18 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
     Scales4 rs[UNR];
     const uint16_t* xr = x + (int64_t)(un->entry[c0] / K) * H;  // NT == 1: the token's row
     const uint16_t* xt = xr + xo;
-    // NT > 1: the chunk's token rows go to LDS.  Their loads are issued first (past the chunk's last
-    // token and past the row's end they repeat the last ones) and the weights' after them, so the
-    // stores below wait for the rows only while the first weights are still in flight.
-    uint4 xs[NT > 1 ? NT : 1][2];
+    // NT > 1: the chunk's token rows go to LDS straight from memory (no registers), 1 KiB per copy over
+    // the rows laid end to end: lane l of copy c fills place 64 c + l of row (64 c + l) / (H/8); past the
+    // last row it loads the last row's end into the slack behind s_x.  Every place is written by one
+    // lane.  Issued before the weights' loads, and waited for below while those are still in flight.
     if constexpr (NT > 1) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const uint16_t* row = x + (int64_t)(__builtin_amdgcn_readfirstlane(un->entry[c0 + min(j, nt - 1)]) / K) * H;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) xs[j][h] = *reinterpret_cast<const uint4*>(row + min(tid + h * kWG, H8 - 1) * 8);
+      const uint32_t lds0 = lds_address(s_x);
+      const int n = nt * H8;
+      for (int c = wave; c < (n + 63) / 64; c += kWG / 64) {
+        const int pl = min(c * 64 + lane, n - 1), j = pl / H8;
+        const uint16_t* row = x + (int64_t)(un->entry[c0 + j] / K) * H;
+        lds_copy16(row + (pl - j * H8) * 8, lds0 + c * 1024);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     auto load_run = [&](int z, int r) {
       wv[z] = *reinterpret_cast<const uint4*>(wp8 + (int64_t)r * 1024);
@@ -325,13 +347,8 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
 #pragma unroll
     for (int z = 0; z < UNR; ++z) load_run(z, min(wp + P * z, rlast));
     if constexpr (NT > 1) {
-      __builtin_amdgcn_sched_barrier(0);
-      // unconditional stores too (rows past nt hold copies of the last one and are never read; a
-      // clamped column writes the value its own lane holds), so no load is sunk behind a branch
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) s_x[j * H8 + min(tid + h * kWG, H8 - 1)] = xs[j][h];
+      // the row copies are complete once at most the weights' 2 * UNR loads (issued after them) remain
+      vm_wait<2 * UNR>();
       __syncthreads();
     }
     // a rolling pipeline: UNR register slots, each refilled with the run UNR ahead once it is used.
@@ -473,7 +490,7 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
        const float2* __restrict__ ag, int H, int I, int maxB, int nch, float* __restrict__ y) {
   static_assert(WPS == 1 || WPS == 2 || WPS == 4, "1, 2 or 4 waves per slice");
   constexpr int SPW = 4 / WPS;
-  constexpr int UNR = NT <= 2 ? 8 : 6;            // runs in flight per wave
+  constexpr int UNR = NT <= 2 ? 4 : 6;            // runs in flight per wave (4: fewer VGPRs, more waves)
   extern __shared__ uint4 s_a4[];               // [NT][I/8] groups of 8 fp16, then [NT][I/8] float2
   __shared__ float s_red[4][16][NT];
   const int NSH = H / 16, NG = NSH / SPW, KB = I / 32, NRF = KB / 4, I8 = I / 8;
@@ -680,7 +697,7 @@ hipError_t launch_gateup_t(eff_engine* e, const DecodePlan* plan, const uint16_t
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   const dim3 grid(units * nch * (I / 16) * P / 2), block(kWG);
-  const uint32_t lds = NT > 1 ? NT * H * 2 : 0;
+  const uint32_t lds = NT > 1 ? NT * H * 2 + 1024 : 0;  // token rows and the copies' slack
   if (t0)
     hipExtLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R,
                           e->d_ts, plan, x, H, I, c.top_k, c.max_tokens, nch, a16, ag);
@@ -785,8 +802,8 @@ hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
   };
 #define SETUP_G(F, N)                                                       \
   if (fmt == F && N <= NG) {                                                \
-    set((const void*)k_gateup<F, N, 1>, N * H * 2);                         \
-    set((const void*)k_gateup<F, N, 2>, N * H * 2);                         \
+    set((const void*)k_gateup<F, N, 1>, N * H * 2 + 1024);                  \
+    set((const void*)k_gateup<F, N, 2>, N * H * 2 + 1024);                  \
   }
 #define SETUP_D(F, N)                                                       \
   if (fmt == F && N <= ND) {                                                \
