@@ -61,7 +61,8 @@ __host__ __device__ inline int spec_fetch_list(int layer) { return 1 + (layer & 
 // ------------------------------------------------------------------------------------------------
 struct FetchList {
   int32_t count;
-  int32_t err;         // device error word of the ensure/split pair (bit 1: bad id, bit 2: no pending)
+  int32_t err;         // device error word of the ensure/split pair (bit 1: bad id, bit 2: no pending,
+                       // bit 16: victim count)
   int32_t flat[kMaxEntries];
   int32_t slot[kMaxEntries];
 };
@@ -203,7 +204,8 @@ struct eff_engine {
   uint64_t* h_call_dev = nullptr;
   uint64_t* h_done = nullptr;     // host-mapped: the last call whose host share is in h_yhost
   uint64_t* h_done_dev = nullptr;
-  int32_t* h_err = nullptr;       // host-mapped sticky device error bits (bad id 1, combine wait 4, prefill fp16 range 8)
+  int32_t* h_err = nullptr;       // host-mapped sticky device error bits (bad id 1, combine wait 4, prefill fp16 range 8,
+                                  // victim count 16)
   int32_t* h_err_dev = nullptr;
   uint64_t* d_seq = nullptr;      // device: the last decode call's seq
   uint64_t sync_seq = 0;          // EFF_CFG_SYNC_HOST: the host's count of decode calls (= *d_seq)

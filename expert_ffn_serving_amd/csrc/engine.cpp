@@ -256,8 +256,9 @@ static int read_device_error(eff_engine* e) {
     const int err = e->h_fetch[w].err;
     if (err) {
       e->h_fetch[w].err = 0;
-      return fail(EFF_EDEVICE, (err & 1) ? "an expert id was outside [0, E) (entries skipped)"
-                                         : "split ran without a pending ensure");
+      return fail(EFF_EDEVICE, (err & 1)    ? "an expert id was outside [0, E) (entries skipped)"
+                               : (err & 16) ? "victim selection found fewer candidates than it counted"
+                                            : "split ran without a pending ensure");
     }
   }
   return EFF_OK;
@@ -283,6 +284,7 @@ static int check_async_error(eff_engine* e) {
     return fail(EFF_EDEVICE, (dev_err & 1) ? "an expert id was outside [0, E) (entries skipped)"
                              : (dev_err & 4) ? "a combine gave up waiting for its host share"
                              : (dev_err & 8) ? "a prefill activation or SwiGLU output exceeded the fp16 range (65504)"
+                             : (dev_err & 16) ? "victim selection found fewer candidates than it counted"
                                              : "device error");
   if (!e->async_err.load(std::memory_order_acquire)) return EFF_OK;
   std::lock_guard<std::mutex> g(e->async_mu);
@@ -899,9 +901,11 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
     e->spec_copy_pending = false;
   }
   // this layer's speculative fetches travel on the side stream: right after the control kernel, or
-  // in the gap after the gate/up kernel, which copies the layer's own fetched records
-  const bool gap = spec && e->spec_in_gap;
-  if (spec && !gap) {
+  // in the gap after the gate/up kernel, which copies the layer's own fetched records.  A budget or
+  // link cap of 0 lets the request fetch nothing (it still stamps its hits), so there is no copy.
+  const bool copy = spec && e->spec_budget != 0 && e->spec_link != 0;
+  const bool gap = copy && e->spec_in_gap;
+  if (copy && !gap) {
     EFF_HIP_TRY(hipEventRecord(e->ev_ctl, cs));
     EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_ctl, 0));
     EFF_HIP_TRY(launch_fetch_copy(e, spec_fetch_list(layer + 1), ss));

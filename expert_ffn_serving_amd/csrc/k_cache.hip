@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr uint64_t kInfKey = ~0ull;
+constexpr int kArgminMax = 4;  // victims chosen by block-wide argmin rounds; more by radix select
 
 // q*(m, f): floor of the balance point m*f/65536 or the next integer, whichever
 // has the smaller max(F*(65536-f), (m-F)*f) (the lower one on a tie), capped at m
@@ -57,7 +58,7 @@ __device__ inline void lds_sync() {
 
 // One ensure + split call, kept in LDS.  The call reads the slot state from device memory and
 // writes every change in one commit at the end.
-struct CallLds {
+struct alignas(16) CallLds {
   int32_t id[kMaxEntries];      // expert id of each entry (-1: invalid)
   int32_t hit[kMaxEntries];     // slot the ensure found (resident), else -1
   int32_t slot[kMaxEntries];    // the partition after the split
@@ -67,30 +68,137 @@ struct CallLds {
   int32_t ranked[kMaxEntries];  // misses by (recency desc, id asc)
   int32_t victim[kMaxEntries];  // victims by (usage, slot)
   int32_t vold[kMaxEntries];    // previous owner of each victim
-  int64_t mrec[kMaxEntries];    // recency of each miss
+  int32_t mrank[kMaxEntries];   // rank of each miss (index into miss)
+  int32_t hist[256];            // radix select: one digit's histogram
+  int64_t mrec[kMaxEntries];    // recency of each miss (then the selected victim keys)
   uint64_t red[kThreads / 64];
   int nvw[kThreads / 64];       // prebuilt victim keys below the floor, per wave
   int64_t s, floor_;
+  uint64_t rs_and, rs_or;       // radix select: AND and OR of the candidate keys
   int layer, n, spec, nu, nm, nv, qq, err;
+  int rs_bin, rs_rem, rs_n;     // radix select: the chosen digit, the rank left, keys selected
 };
 
 __device__ inline void stat_add(int64_t* p, int64_t v) {
   atomicAdd(reinterpret_cast<unsigned long long*>(p), (unsigned long long)v);
 }
 
-// first[p]: entry p is the first one with its (valid) id.
+// first[p]: entry p is the first one with its (valid) id.  Entry p = thread p; each sweeps all
+// n entries in order, a loop of the same length on every lane whose loads read one LDS word for
+// the whole wave (a broadcast) and do not wait for each other.
+static_assert(kMaxEntries <= kThreads && kMaxEntries % 32 == 0, "one entry per thread; whole batches");
+
+// f(q, a[q]) (and b[q] for the two-array forms) for q = 0 .. n-1, the same sequence on every lane:
+// batches of 16 values read with 4 (8) LDS vector loads issued together, which every lane reads
+// at one address (a broadcast), so the loop waits for the LDS once per batch.  a, b: 16-byte
+// aligned LDS arrays of kMaxEntries (read past n up to the batch's end, never past the array).
+constexpr int kSweepB = 16;
+static_assert(kMaxEntries % kSweepB == 0, "whole batches");
+template <typename F>
+__device__ inline void sweep(const int32_t* a, int n_, F f) {
+  const int n = __builtin_amdgcn_readfirstlane(n_);  // uniform: scalar loop bounds
+  for (int q0 = 0; q0 < n; q0 += kSweepB) {
+    int4 x[kSweepB / 4];
+#pragma unroll
+    for (int i = 0; i < kSweepB / 4; ++i) x[i] = reinterpret_cast<const int4*>(a + q0)[i];
+    if (q0 + kSweepB <= n) {  // a whole batch: no check per value
+#pragma unroll
+      for (int i = 0; i < kSweepB / 4; ++i) {
+        const int q = q0 + 4 * i;
+        f(q, x[i].x);
+        f(q + 1, x[i].y);
+        f(q + 2, x[i].z);
+        f(q + 3, x[i].w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSweepB / 4; ++i) {
+        const int q = q0 + 4 * i;
+        if (q < n) f(q, x[i].x);
+        if (q + 1 < n) f(q + 1, x[i].y);
+        if (q + 2 < n) f(q + 2, x[i].z);
+        if (q + 3 < n) f(q + 3, x[i].w);
+      }
+    }
+  }
+}
+template <typename F>
+__device__ inline void sweep2(const int32_t* a, const int32_t* b, int n_, F f) {
+  const int n = __builtin_amdgcn_readfirstlane(n_);
+  for (int q0 = 0; q0 < n; q0 += kSweepB) {
+    int4 x[kSweepB / 4], y[kSweepB / 4];
+#pragma unroll
+    for (int i = 0; i < kSweepB / 4; ++i) {
+      x[i] = reinterpret_cast<const int4*>(a + q0)[i];
+      y[i] = reinterpret_cast<const int4*>(b + q0)[i];
+    }
+    if (q0 + kSweepB <= n) {
+#pragma unroll
+      for (int i = 0; i < kSweepB / 4; ++i) {
+        const int q = q0 + 4 * i;
+        f(q, x[i].x, y[i].x);
+        f(q + 1, x[i].y, y[i].y);
+        f(q + 2, x[i].z, y[i].z);
+        f(q + 3, x[i].w, y[i].w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSweepB / 4; ++i) {
+        const int q = q0 + 4 * i;
+        if (q < n) f(q, x[i].x, y[i].x);
+        if (q + 1 < n) f(q + 1, x[i].y, y[i].y);
+        if (q + 2 < n) f(q + 2, x[i].z, y[i].z);
+        if (q + 3 < n) f(q + 3, x[i].w, y[i].w);
+      }
+    }
+  }
+}
+// f(q, a[q], b[q]) with b 64-bit (a may be null: 0 is passed)
+template <typename F>
+__device__ inline void sweep_i64(const int32_t* a, const uint64_t* b, int n_, F f) {
+  const int n = __builtin_amdgcn_readfirstlane(n_);
+  for (int q0 = 0; q0 < n; q0 += kSweepB) {
+    int4 x[kSweepB / 4];
+    ulonglong2 y[kSweepB / 2];
+#pragma unroll
+    for (int i = 0; i < kSweepB / 4; ++i) x[i] = a ? reinterpret_cast<const int4*>(a + q0)[i] : make_int4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kSweepB / 2; ++i) y[i] = reinterpret_cast<const ulonglong2*>(b + q0)[i];
+    if (q0 + kSweepB <= n) {
+#pragma unroll
+      for (int i = 0; i < kSweepB / 4; ++i) {
+        const int q = q0 + 4 * i;
+        f(q, x[i].x, (uint64_t)y[2 * i].x);
+        f(q + 1, x[i].y, (uint64_t)y[2 * i].y);
+        f(q + 2, x[i].z, (uint64_t)y[2 * i + 1].x);
+        f(q + 3, x[i].w, (uint64_t)y[2 * i + 1].y);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSweepB / 4; ++i) {
+        const int q = q0 + 4 * i;
+        if (q < n) f(q, x[i].x, (uint64_t)y[2 * i].x);
+        if (q + 1 < n) f(q + 1, x[i].y, (uint64_t)y[2 * i].y);
+        if (q + 2 < n) f(q + 2, x[i].z, (uint64_t)y[2 * i + 1].x);
+        if (q + 3 < n) f(q + 3, x[i].w, (uint64_t)y[2 * i + 1].y);
+      }
+    }
+  }
+}
+
 __device__ inline void mark_first(CallLds& C, int n) {
-  for (int p = threadIdx.x; p < n; p += kThreads) {
-    const int id = C.id[p];
-    int f = id >= 0;
-    for (int q = 0; q < p && f; ++q) f = C.id[q] != id;
-    C.first[p] = f;
+  const int p = threadIdx.x;
+  if ((p & ~63) < n) {  // waves holding entries
+    const int id = p < n ? C.id[p] : -1;
+    bool dup = false;
+    sweep(C.id, n, [&](int q, int o) { dup |= q < p && o == id; });
+    if (p < n) C.first[p] = id >= 0 && !dup;
   }
 }
 
 // ensure: dedup and residency ([FT-deep] §4 ⑤; [FT-blog] §六).  In: C.id[0..n).  Out, in LDS:
 // C.hit, C.first, C.uniq, C.miss, step and floor.  Reads the table; writes nothing to memory.
-__device__ void ensure_body(const CacheState& c, int layer, int n, int spec, CallLds& C) {
+__device__ __attribute__((always_inline)) void ensure_body(const CacheState& c, int layer, int n, int spec, CallLds& C) {
   const int tid = threadIdx.x, E = c.E;
   if (tid == 0) {
     const int64_t s = c.clock[0] + 1;
@@ -138,34 +246,49 @@ __device__ void ensure_body(const CacheState& c, int layer, int n, int spec, Cal
     lds_sync();
     return;
   }
-  for (int p = tid; p < n; p += kThreads) {
-    int v = C.id[p];
+  // more entries: entry p = thread p.  The table lookups, then two sweeps over all entries (as in
+  // mark_first): is the entry the first with its id, and how many distinct (missing) ids are
+  // smaller.  C.slot holds each first entry's (id, missing) packed until the split overwrites it.
+  int v = -1, hit = -1;
+  if (tid < n) {
+    v = C.id[tid];
     if (v < 0 || v >= E) {
       atomicOr(&C.err, 1);
       v = -1;
-      C.id[p] = -1;
     }
-    C.hit[p] = (v >= 0) ? c.table[(int64_t)layer * E + v] : -1;
+    hit = (v >= 0) ? c.table[(int64_t)layer * E + v] : -1;
+    C.id[tid] = v;
+    C.hit[tid] = hit;
   }
   lds_sync();
-  mark_first(C, n);
+  const bool wv = (tid & ~63) < n;  // waves holding entries
+  bool first = false;
+  if (wv) {
+    bool dup = false;
+    sweep(C.id, n, [&](int q, int o) { dup |= q < tid && o == v; });
+    first = tid < n && v >= 0 && !dup;
+    if (tid < n) {
+      C.first[tid] = first;
+      C.slot[tid] = first ? (v << 1 | (hit < 0 ? 1 : 0)) : -1;
+    }
+  }
   lds_sync();
-  for (int p = tid; p < n; p += kThreads) {
-    if (!C.first[p]) continue;
-    const int id = C.id[p];
+  if (wv) {
     int ru = 0, rm = 0;
-    for (int q = 0; q < n; ++q) {
-      if (!C.first[q]) continue;
-      const int o = C.id[q];
-      ru += o < id;
-      rm += (o < id) && (C.hit[q] < 0);
+    sweep(C.slot, n, [&](int, int pk) {
+      const bool lt = pk >= 0 && (pk >> 1) < v;
+      ru += lt;
+      rm += lt && (pk & 1);
+    });
+    if (first) {
+      C.uniq[ru] = v;
+      if (hit < 0) C.miss[rm] = v;
     }
-    C.uniq[ru] = id;
-    if (C.hit[p] < 0) {
-      C.miss[rm] = id;
-      atomicAdd(&C.nm, 1);
-    }
-    atomicAdd(&C.nu, 1);
+  }
+  const uint64_t fm = __ballot(first), mm = __ballot(first && hit < 0);
+  if ((tid & 63) == 0 && fm) {
+    atomicAdd(&C.nu, __popcll(fm));
+    if (mm) atomicAdd(&C.nm, __popcll(mm));
   }
   lds_sync();
 }
@@ -238,7 +361,7 @@ __device__ void prebuild_keys(const CacheState& c, CallLds& C, uint64_t* s_key) 
 // keys_ready: s_key and C.nvw were prebuilt (prebuild_keys) from the usage this call sees.
 // real_q: the latest real call's fetch count when the caller has it (the fused control kernel, whose
 // real split precedes its speculative one), else -1: read from clock[2].
-__device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, bool keys_ready = false,
+__device__ __attribute__((always_inline)) void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, bool keys_ready = false,
                            int real_q = -1) {
   const int tid = threadIdx.x;
   const int E = c.E, S = c.S;
@@ -255,6 +378,11 @@ __device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, boo
       if (keys_ready)
         for (int w = kKeyT0 / 64; w < kThreads / 64; ++w) nv += C.nvw[w];
       C.nv = nv;
+      C.rs_and = ~0ull;
+      C.rs_or = 0;
+      C.rs_n = 0;
+      C.rs_bin = 0;
+      C.rs_rem = 1;
     }
     lds_sync();
     // the misses' recency and the victim keys: every load is issued before any is used (a loop that
@@ -289,20 +417,22 @@ __device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, boo
       }
     }
     // Misses ranked by (recency desc, id asc) ([FT-deep] §4 ⑤: prefer recently active experts).
-    for (int i = tid; i < m; i += kThreads) {
-      const int e = C.miss[i];
-      const int64_t r = C.mrec[i];
+    if ((tid & ~63) < m) {  // waves holding misses (one per thread)
+      const int e = tid < m ? C.miss[tid] : 0;
+      const int64_t r = tid < m ? C.mrec[tid] : 0;
       int rank = 0;
-      for (int j = 0; j < m; ++j) {
-        const int o = C.miss[j];
-        const int64_t ro = C.mrec[j];
+      sweep_i64(C.miss, reinterpret_cast<const uint64_t*>(C.mrec), m, [&](int, int o, uint64_t u) {
+        const int64_t ro = (int64_t)u;
         rank += (ro > r) || (ro == r && o < e);
+      });
+      if (tid < m) {
+        C.ranked[rank] = e;
+        C.mrank[tid] = rank;
       }
-      C.ranked[rank] = e;
     }
     lds_sync();
     qq = min(q, C.nv);
-    if (qq > 0 && qq <= 16) {
+    if (qq > 0 && qq <= kArgminMax) {
       // few fetches: qq rounds of block-wide argmin
       for (int i = 0; i < qq; ++i) {
         uint64_t lm = kInfKey;
@@ -315,39 +445,111 @@ __device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, boo
         }
         lds_sync();
       }
-    } else if (qq > 16) {
-      // many fetches: bitonic sort of all keys (ascending)
-      for (int k = 2; k <= c.sort_pow2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-          for (int i = tid; i < c.sort_pow2; i += kThreads) {
-            const int ixj = i ^ j;
-            if (ixj > i) {
-              const uint64_t a = s_key[i], b = s_key[ixj];
-              const bool up = (i & k) == 0;
-              if ((a > b) == up) {
-                s_key[i] = b;
-                s_key[ixj] = a;
-              }
-            }
-          }
-          lds_sync();
+    } else if (qq > kArgminMax) {
+      // more fetches: radix select of the qq smallest keys (distinct: the slot is in the low bits),
+      // 8 bits a pass from the highest bit in which the candidates differ, then their ranks
+      uint64_t kand = ~0ull, kor = 0;
+      for (int v = tid; v < S; v += kThreads) {
+        const uint64_t k = s_key[v];
+        if (k != kInfKey) {
+          kand &= k;
+          kor |= k;
         }
       }
-      for (int i = tid; i < qq; i += kThreads) C.victim[i] = (int)(s_key[i] & 0x3FFF);
+      for (int d = 32; d >= 1; d >>= 1) {
+        kand &= __shfl_xor(kand, d);
+        kor |= __shfl_xor(kor, d);
+      }
+      if ((tid & 63) == 0) {
+        atomicAnd(&C.rs_and, kand);
+        atomicOr(&C.rs_or, kor);
+      }
+      lds_sync();
+      const uint64_t diff = C.rs_and ^ C.rs_or;
+      int shift = diff ? ((63 - __builtin_clzll(diff)) & ~7) : 0;
+      uint64_t prefix = C.rs_and & (shift >= 56 ? 0ull : ~0ull << (shift + 8));  // bits every candidate shares
+      int rem = qq;  // the rem-th smallest key among those that match prefix above the digit
+      for (;;) {
+        const uint64_t hm = shift >= 56 ? 0ull : ~0ull << (shift + 8);
+        if (tid < 256) C.hist[tid] = 0;
+        lds_sync();
+        for (int v = tid; v < S; v += kThreads) {
+          const uint64_t k = s_key[v];
+          if (k != kInfKey && (k & hm) == prefix) atomicAdd(&C.hist[(k >> shift) & 255], 1);
+        }
+        lds_sync();
+        if (tid < 64) {  // lane l: bins 4l..4l+3; the bin where the running count reaches rem
+          const int h0 = C.hist[4 * tid], h1 = C.hist[4 * tid + 1], h2 = C.hist[4 * tid + 2], h3 = C.hist[4 * tid + 3];
+          const int sum = h0 + h1 + h2 + h3;
+          int incl = sum;
+          for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            if (tid >= d) incl += o;
+          }
+          int acc = incl - sum;
+          if (acc < rem && rem <= incl) {
+            int b = 0;
+            if (rem > acc + h0) {
+              acc += h0;
+              b = 1;
+              if (rem > acc + h1) {
+                acc += h1;
+                b = 2;
+                if (rem > acc + h2) {
+                  acc += h2;
+                  b = 3;
+                }
+              }
+            }
+            C.rs_bin = 4 * tid + b;
+            C.rs_rem = rem - acc;
+          }
+        }
+        lds_sync();
+        prefix |= (uint64_t)C.rs_bin << shift;
+        rem = C.rs_rem;
+        if (shift == 0) break;
+        shift -= 8;
+      }
+      // prefix is now the qq-th smallest key: the keys up to it, unordered, then each one's rank
+      uint64_t* sel = reinterpret_cast<uint64_t*>(C.mrec);  // the misses' recency is used up
+      for (int v = tid; v < S; v += kThreads) {
+        const uint64_t k = s_key[v];
+        if (k <= prefix) {
+          const int i = atomicAdd(&C.rs_n, 1);
+          if (i < kMaxEntries) sel[i] = k;
+        }
+      }
+      lds_sync();
+      if (C.rs_n != qq) {  // the keys disagree with the count of candidates: never seen; fetch fewer
+        if (tid == 0) atomicOr(&C.err, 16);
+        qq = min(qq, C.rs_n);
+      }
+      if ((tid & ~63) < qq) {
+        const uint64_t k = tid < qq ? sel[tid] : 0;
+        int r = 0;
+        sweep_i64(nullptr, sel, qq, [&](int, int, uint64_t o) { r += o < k; });
+        if (tid < qq) C.victim[r] = (int)(k & 0x3FFF);
+      }
       lds_sync();
     }
     for (int i = tid; i < qq; i += kThreads) C.vold[i] = c.owner[C.victim[i]];
   }
-  // The -1 partition ([FT-deep] §4 ③): i-th ranked miss -> i-th victim; hits keep their slot.
+  // The -1 partition ([FT-deep] §4 ③): i-th ranked miss -> i-th victim; hits keep their slot.  A
+  // missing entry finds its id in the ascending miss list, then that miss's rank.
   for (int p = tid; p < n; p += kThreads) {
     const int id = C.id[p];
     int slot = C.hit[p];
-    if (slot < 0 && id >= 0)
-      for (int i = 0; i < qq; ++i)
-        if (C.ranked[i] == id) {
-          slot = C.victim[i];
-          break;
-        }
+    if (slot < 0 && id >= 0 && qq > 0) {
+      int lo = 0, hi = m - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (C.miss[mid] < id) lo = mid + 1;
+        else hi = mid;
+      }
+      const int r = C.mrank[lo];
+      if (r < qq) slot = C.victim[r];
+    }
     C.slot[p] = slot;
   }
   if (tid == 0) C.qq = qq;
@@ -357,7 +559,7 @@ __device__ void split_body(const CacheState& c, CallLds& C, uint64_t* s_key, boo
 // Commit a call: hit stamps (when stamp_hits), installs, the fetch list, outputs, recency,
 // clocks, counts and stats.  Host-mapped outputs (cpu_host, the fetch list mirror) are written
 // by wave 0 only, so that one wave's system fence publishes them.  All arrays may be null.
-__device__ void commit_body(const CacheState& c, const CallLds& C, bool stamp_hits, int32_t* __restrict__ slots_out,
+__device__ __attribute__((always_inline)) void commit_body(const CacheState& c, const CallLds& C, bool stamp_hits, int32_t* __restrict__ slots_out,
                             int32_t* __restrict__ cpu_out, int32_t* __restrict__ cpu_host,
                             int32_t* __restrict__ counts) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -660,11 +862,11 @@ __device__ inline void topk_row(const float* row, int E, int K, int32_t* ids, fl
 // Decode plan (distinct GPU slots and their entries) by one workgroup, from the entries' slots
 // in LDS.  flat id of a unit: base + lds_id[p] when ids are known, else owner[slot].  lds_hit
 // (may be null): the slot the ensure found; a unit whose slot was installed by this call
-// (hit < 0) is marked fetch.  scratch: 2*kMaxEntries int32 of LDS.
+// (hit < 0) is marked fetch.  scratch: 3*kMaxEntries int32 of LDS (16-byte aligned).
 // The decode plan of a call of at most 64 entries, by wave 0 alone (no barrier): each lane
 // learns which lanes share its slot and which hold a smaller slot from one uniform readlane sweep
 // (registers only; no LDS round trips).  Call with tid < 64.
-__device__ void plan_wave0(const int32_t* lds_slot, const int32_t* lds_id, const int32_t* lds_hit, int64_t base,
+__device__ __attribute__((always_inline)) void plan_wave0(const int32_t* lds_slot, const int32_t* lds_id, const int32_t* lds_hit, int64_t base,
                            const int32_t* __restrict__ owner, int n, int S, int maxU, int maxB, DecodePlan* plan) {
   const int tid = threadIdx.x;
   int v = -1;
@@ -712,7 +914,7 @@ __device__ void plan_wave0(const int32_t* lds_slot, const int32_t* lds_id, const
   if (tid == 0) plan->nu = nu;
 }
 
-__device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, const int32_t* lds_hit, int64_t base,
+__device__ __attribute__((always_inline)) void plan_body(const int32_t* lds_slot, const int32_t* lds_id, const int32_t* lds_hit, int64_t base,
                           const int32_t* __restrict__ owner, int n, int S, int maxU, int maxB, DecodePlan* plan,
                           int32_t* scratch) {
   const int tid = threadIdx.x;
@@ -721,43 +923,58 @@ __device__ void plan_body(const int32_t* lds_slot, const int32_t* lds_id, const 
     lds_sync();
     return;
   }
+  // more entries: entry p = thread p.  One sweep over all entries (as in mark_first) gives each
+  // entry its slot's first entry, its place among the slot's entries and the slot's entry count; a
+  // second ranks the units; then every entry writes itself into its unit.
   int32_t* s_sl = scratch;
-  int32_t* s_first = scratch + kMaxEntries;
+  int32_t* s_first = scratch + kMaxEntries;     // at a slot's first entry: its count (<= maxB), else 0
+  int32_t* s_rank = scratch + 2 * kMaxEntries;  // at a slot's first entry: its unit, or maxU
   __shared__ int s_nu;
   if (tid == 0) s_nu = 0;
-  for (int p = tid; p < n; p += blockDim.x) {
-    const int v = lds_slot[p];
-    s_sl[p] = (v >= 0 && v < S) ? v : -1;  // slots outside the arena are never read
+  int v = -1;
+  if (tid < n) {
+    const int sl = lds_slot[tid];
+    v = (sl >= 0 && sl < S) ? sl : -1;  // slots outside the arena are never read
+    s_sl[tid] = v;
   }
   lds_sync();
-  for (int p = tid; p < n; p += blockDim.x) {  // s_first: the slot's entry count at its first entry, else 0
-    int v = s_sl[p], first = v >= 0;
-    for (int q = 0; q < p && first; ++q) first = s_sl[q] != v;
-    int c = 0;
-    if (first)
-      for (int q = p; q < n; ++q) c += s_sl[q] == v;
-    s_first[p] = first ? min(c, maxB) : 0;
+  const bool wv = (tid & ~63) < n;  // waves holding entries
+  int c = 0, pos = 0, fq = 0;
+  if (wv) {
+    int cnt = 0;
+    fq = kMaxEntries;
+    sweep(s_sl, n, [&](int q, int o) {
+      const bool same = o == v;
+      cnt += same;
+      pos += same && q < tid;
+      fq = same && fq == kMaxEntries ? q : fq;
+    });
+    if (tid < n && v >= 0 && pos == 0) c = min(cnt, maxB);
   }
+  if (tid < n) s_first[tid] = c;
   lds_sync();
-  for (int p = tid; p < n; p += blockDim.x) {
-    if (!s_first[p]) continue;
+  int rank = maxU;
+  if (wv) {
     // units by descending token count, then ascending slot (as in plan_wave0)
-    const int v = s_sl[p], c = s_first[p];
-    int rank = 0, cnt = 0;
-    for (int q = 0; q < n; ++q) {
-      const int cq = s_first[q];
-      rank += cq > c || (cq == c && cq > 0 && s_sl[q] < v);
-    }
-    if (rank >= maxU) continue;  // more distinct slots than a layer has experts: not computed
-    DecodeUnit& un = plan->unit[rank];
-    for (int q = 0; q < n && cnt < maxB; ++q)  // a slot appears at most once per token
-      if (s_sl[q] == v) un.entry[cnt++] = q;
-    un.slot = v;
-    un.count = cnt;
-    un.flat = lds_id ? (int32_t)(base + lds_id[p]) : owner[v];
-    un.fetch = (lds_hit && lds_hit[p] < 0) ? 1 : 0;
-    atomicAdd(&s_nu, 1);
+    int rk = 0;
+    sweep2(s_first, s_sl, n, [&](int, int cq, int sq) { rk += cq > c || (cq == c && sq < v); });
+    if (c > 0) rank = min(rk, maxU);  // more distinct slots than a layer has experts: not computed
   }
+  if (tid < n) s_rank[tid] = rank;
+  lds_sync();
+  if (tid < n && v >= 0 && pos < maxB) {  // a slot appears at most once per token
+    const int r = s_rank[fq];
+    if (r < maxU) plan->unit[r].entry[pos] = tid;
+  }
+  if (rank < maxU) {
+    DecodeUnit& un = plan->unit[rank];
+    un.slot = v;
+    un.count = c;
+    un.flat = lds_id ? (int32_t)(base + lds_id[tid]) : owner[v];
+    un.fetch = (lds_hit && lds_hit[tid] < 0) ? 1 : 0;
+  }
+  const uint64_t um = __ballot(rank < maxU);
+  if ((tid & 63) == 0 && um) atomicAdd(&s_nu, __popcll(um));
   lds_sync();
   const int nu = min(s_nu, maxU);
   for (int u = nu + tid; u < maxU; u += blockDim.x) {
@@ -786,7 +1003,7 @@ k_ensure(CacheState c, int layer, int32_t* __restrict__ ids, int n, int spec) {
 
 __global__ void __launch_bounds__(kThreads)
 k_split(CacheState c, int32_t* __restrict__ ids_out, int32_t* __restrict__ cpu_out, int32_t* __restrict__ counts) {
-  extern __shared__ uint64_t s_key[];
+  extern __shared__ __attribute__((aligned(16))) uint64_t s_key[];
   __shared__ CallLds C;
   if (!load_pending(c, C)) return;
   split_body(c, C, s_key);
@@ -804,7 +1021,7 @@ __global__ void __launch_bounds__(kThreads)
 k_plan(const int32_t* __restrict__ slots, int n, int S, int maxU, int maxB, const int32_t* __restrict__ owner,
        DecodePlan* plan) {
   __shared__ int32_t s_slot[kMaxEntries];
-  __shared__ int32_t scratch[2 * kMaxEntries];
+  __shared__ __attribute__((aligned(16))) int32_t scratch[3 * kMaxEntries];
   for (int p = threadIdx.x; p < n; p += kThreads) s_slot[p] = slots[p];
   lds_sync();
   plan_body(s_slot, nullptr, nullptr, 0, owner, n, S, maxU, maxB, plan, scratch);
@@ -840,25 +1057,24 @@ k_control(CacheState c, const float* __restrict__ logits, int B, int K, int laye
           const int32_t* __restrict__ spec_ids, int32_t* __restrict__ spec_slots, int32_t* __restrict__ cpu_host,
           const uint16_t* __restrict__ x, uint16_t* __restrict__ x_host, int H, int maxU, int maxB,
           DecodePlan* plan, uint64_t* call_ring, uint64_t* host_done, uint64_t* seq_ctr) {
-  extern __shared__ uint64_t s_key[];  // victim keys, plan scratch
+  extern __shared__ __attribute__((aligned(16))) uint64_t s_key[];  // victim keys, plan scratch (16-byte aligned)
   __shared__ CallLds C;
   const int tid = threadIdx.x;
   const int n = B * K;
-  if (tid >= 64 && tid < kKeyT0) {
-    // waves 1-4 copy x for the host while wave 0 starts the top-K.  They wait for these stores
-    // to complete only after the split (below), before the plan's barrier; wave 0's system-scope
-    // fence before the call word then publishes them together with its own stores.  A completed
-    // store to coherent host memory is not yet visible to the host without that fence (measured:
-    // host ids published with completed system-scope stores and no fence were read stale), and
-    // one fence for the workgroup is enough: a fence per wave would write back the L2 once per
-    // wave, which costs microseconds.
-    for (int i = tid - 64; i < B * H / 8; i += kKeyT0 - 64)
-      reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
-  } else if (tid >= kKeyT0) {
-    prebuild_keys(c, C, s_key);  // waves 5.. meanwhile
-  }
+  if (tid >= kKeyT0) prebuild_keys(c, C, s_key);  // waves 5.., before their top-K rows
   for (int t = tid >> 6; t < B; t += kThreads / 64)
     topk_row(logits + (int64_t)t * c.E, c.E, K, ids + (int64_t)t * K, w + (int64_t)t * K, C.id + t * K);
+  if (tid >= 64 && tid < kKeyT0) {
+    // waves 1-4 copy x for the host after their top-K rows (whose loads would otherwise wait for
+    // these stores).  They wait for the stores to complete only after the split (below), before
+    // the plan's barrier; wave 0's system-scope fence before the call word then publishes them
+    // together with its own stores.  A completed store to coherent host memory is not yet visible
+    // to the host without that fence (measured: host ids published with completed system-scope
+    // stores and no fence were read stale), and one fence for the workgroup is enough: a fence per
+    // wave would write back the L2 once per wave, which costs microseconds.
+    for (int i = tid - 64; i < B * H / 8; i += kKeyT0 - 64)
+      reinterpret_cast<uint4*>(x_host)[i] = reinterpret_cast<const uint4*>(x)[i];
+  }
   lds_sync();
   ensure_body(c, layer, n, 0, C);
   if (n <= 64 && !spec_ids && qstar_dev(C.nm, c.f) == 0) {
@@ -1004,7 +1220,7 @@ static CacheState state_of(eff_engine* e) {
 // dynamic LDS of the control kernel: victim keys and the plan scratch
 static size_t control_lds(int S, int E) {
   (void)E;
-  return std::max((size_t)sort_pow2_of(S) * sizeof(uint64_t), (size_t)2 * kMaxEntries * sizeof(int32_t));
+  return std::max((size_t)sort_pow2_of(S) * sizeof(uint64_t), (size_t)3 * kMaxEntries * sizeof(int32_t));
 }
 
 hipError_t launch_ensure(eff_engine* e, int layer, int32_t* ids, int n, int spec, hipStream_t s) {
