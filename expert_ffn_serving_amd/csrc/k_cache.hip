@@ -6,6 +6,7 @@
 // [FT-deep] §4 design pattern ② explains why: the miss count exists only on the
 // device while the decode step is captured).
 #include <algorithm>
+#include <cstddef>
 
 #include "eff_internal.h"
 
@@ -78,6 +79,12 @@ struct alignas(16) CallLds {
   int layer, n, spec, nu, nm, nv, qq, err;
   int rs_bin, rs_rem, rs_n;     // radix select: the chosen digit, the rank left, keys selected
 };
+// ranked, victim, vold and mrank are written by the split only: until then the ensure uses them
+// as one table of up to kEnsureTab experts
+constexpr int kEnsureTab = 4 * kMaxEntries;
+static_assert(offsetof(CallLds, mrank) == offsetof(CallLds, ranked) + 3 * kMaxEntries * sizeof(int32_t),
+              "one contiguous table");
+static_assert(kEnsureTab % kThreads == 0, "whole ids per thread");
 
 __device__ inline void stat_add(int64_t* p, int64_t v) {
   atomicAdd(reinterpret_cast<unsigned long long*>(p), (unsigned long long)v);
@@ -242,6 +249,62 @@ __device__ __attribute__((always_inline)) void ensure_body(const CacheState& c, 
         C.nm = __popcll(mm);
         C.err = badm ? 1 : 0;
       }
+    }
+    lds_sync();
+    return;
+  }
+  if (E <= kEnsureTab) {
+    // more entries, few experts: entry p = thread p, and a table over the experts.  Each entry's
+    // id takes the largest (n - p) of its entries (its first entry) with the missing bit; then
+    // one exclusive scan over the experts numbers the distinct and the distinct missing ids.
+    int32_t* tab = C.ranked;
+    for (int e = tid; e < E; e += kThreads) tab[e] = 0;
+    int v = -1, hit = -1;
+    if (tid < n) {
+      v = C.id[tid];
+      if (v < 0 || v >= E) {
+        atomicOr(&C.err, 1);
+        v = -1;
+      }
+      hit = (v >= 0) ? c.table[(int64_t)layer * E + v] : -1;
+      C.id[tid] = v;
+      C.hit[tid] = hit;
+    }
+    lds_sync();
+    if (v >= 0) atomicMax(&tab[v], (n - tid) << 1 | (hit < 0 ? 1 : 0));
+    lds_sync();
+    if (tid < n) C.first[tid] = v >= 0 && (tab[v] >> 1) == n - tid;
+    constexpr int kPer = kEnsureTab / kThreads;  // experts tid*kPer .. +kPer-1 of this thread
+    int cnt[kPer], local = 0;  // per expert: present + (missing << 16)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid * kPer + i;
+      const int t = e < E ? tab[e] : 0;
+      cnt[i] = t ? 1 + ((t & 1) << 16) : 0;
+      local += cnt[i];
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+    int incl = local;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) C.hist[wave] = incl;  // the histogram is free until the split
+    lds_sync();
+    int before = incl - local;
+    for (int w = 0; w < wave; ++w) before += C.hist[w];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (cnt[i]) {
+        const int e = tid * kPer + i;
+        C.uniq[before & 0xFFFF] = e;
+        if (cnt[i] >> 16) C.miss[before >> 16] = e;
+      }
+      before += cnt[i];
+    }
+    if (tid == kThreads - 1) {
+      C.nu = before & 0xFFFF;
+      C.nm = before >> 16;
     }
     lds_sync();
     return;
