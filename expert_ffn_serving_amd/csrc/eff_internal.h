@@ -213,12 +213,9 @@ struct eff_engine {
   float* h_yhost_dev = nullptr;
   const uint8_t* pool_dev = nullptr;  // device view of the pinned pool (in-kernel fetches)
   bool async_host = false;        // host share on the worker thread, the stream waits on h_done
-  bool spec_copy_pending = false; // a speculative copy on the side stream not yet waited for
   int spec_budget = -1;           // eff_set_speculation: records per speculative request (-1: any)
   int spec_link = -1;              // eff_set_speculation_link: link records per layer (-1: no cap)
-  bool spec_in_gap = false;       // eff_set_speculation: speculative copies start after gate/up
-  hipEvent_t ev_gateup = nullptr; // end of the layer's gate/up kernel (speculative copies in the gap)
-  hipEvent_t ev_ctl = nullptr;
+  bool spec_in_gap = false;       // eff_set_speculation: speculative copies ride in the down kernel
   // host-share worker (async mode)
   std::thread worker;
   std::atomic<uint64_t> worker_seq{0};  // every call up to this seq has been handled
@@ -234,7 +231,7 @@ struct eff_engine {
   uint16_t* d_pf_a = nullptr;     // [T*K][I] fp16 SwiGLU activations
   float* d_pf_y = nullptr;        // [T*K][H] fp32 expert outputs
   int32_t* d_pf_meta = nullptr;   // misc
-  hipEvent_t ev_copy = nullptr, ev_spec = nullptr, ev_pf[2] = {nullptr, nullptr};
+  hipEvent_t ev_copy = nullptr, ev_pf[2] = {nullptr, nullptr};
   bool pf_streamed[2] = {false, false};
   int pf_layer[2] = {-1, -1};
 
@@ -280,10 +277,20 @@ hipError_t launch_qstar_batch(const int32_t* m, const uint32_t* f, int32_t* q, i
 hipError_t launch_prefill_install(eff_engine* e, int layer, hipStream_t s);
 hipError_t launch_fallback_install(eff_engine* e, int layer, const int32_t* experts, int n,
                                    hipStream_t s);
-// after_gateup: recorded on s between the gate/up and the down kernel (nullptr: none)
+// A speculative fetch list copied by extra workgroups at the front of an expert kernel's grid
+// (fl null: none), so that the copy needs no launch or event of its own and the next layer's
+// kernels follow it in stream order.  n_flat = L*E, S: the bounds every entry is checked against.
+struct SpecCopy {
+  const FetchList* fl = nullptr;
+  int nwg = 0;
+  int S = 0;
+  int64_t n_flat = 0;
+};
+constexpr int kSpecCopyWGs = 64;  // workgroups that carry a speculative copy (the link is the bound)
+// spec: a speculative copy carried by the gate/up kernel (in_down false) or by the down kernel
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
-                             float* y, hipStream_t s, bool plan_ready = false, hipEvent_t after_gateup = nullptr);
-hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s);
+                             float* y, hipStream_t s, bool plan_ready = false, SpecCopy spec = SpecCopy(),
+                             bool in_down = false);
 // n records from the pool (flat ids first + i*stride modulo L*E) into dst[2][R] (bandwidth profile)
 hipError_t launch_bw_copy(eff_engine* e, int64_t first, int64_t stride, int n, uint8_t* dst, hipStream_t s);
 // the decode plan of n entries into `plan`, units [0, maxU) written (count 0 past the last)

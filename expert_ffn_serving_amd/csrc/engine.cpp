@@ -75,8 +75,7 @@ static void release(eff_engine* e) {
                   e->h_tq};
   for (void* p : host)
     if (p) (void)hipHostFree(p);
-  hipEvent_t evs[] = {e->ev_copy, e->ev_spec, e->ev_ctl, e->ev_gateup, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0],
-                      e->ev_pf_done[1]};
+  hipEvent_t evs[] = {e->ev_copy, e->ev_pf[0], e->ev_pf[1], e->ev_pf_done[0], e->ev_pf_done[1]};
   for (hipEvent_t v : evs)
     if (v) (void)hipEventDestroy(v);
   for (auto& tc : e->timed)
@@ -150,9 +149,6 @@ static int alloc_all(eff_engine* e) {
     EFF_HIP_TRY(hipHostMalloc((void**)&e->h_pf_meta, (size_t)(2 * E) * 4, 0));
   }
   EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_copy, hipEventDisableTiming));
-  EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_ctl, hipEventDisableTiming));
-  EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_spec, hipEventDisableTiming));
-  EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_gateup, hipEventDisableTiming));
   for (int b = 0; b < 2; ++b) {
     EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_pf[b], hipEventDisableTiming));
     EFF_HIP_TRY(hipEventCreateWithFlags(&e->ev_pf_done[b], hipEventDisableTiming));
@@ -894,36 +890,24 @@ int eff_decode_layer(eff_engine* e, int layer, const void* x, const void* w_rout
   // and x land in host-mapped memory, then the call word
   const bool spec = spec_ids && layer + 1 < c.num_layers;
   EFF_HIP_TRY(launch_control(e, layer, lg, B, (const uint16_t*)x, spec ? spec_ids : nullptr, cs));
-  // the previous layer's speculative copies land before this layer's expert kernels read or
-  // overwrite any slot
-  if (e->spec_copy_pending) {
-    EFF_HIP_TRY(hipStreamWaitEvent(cs, e->ev_spec, 0));
-    e->spec_copy_pending = false;
+  // GPU experts; a unit installed by this call reads its record from the pool and fills its slot.
+  // This layer's speculative fetches ride along as extra workgroups of its gate/up kernel (beside
+  // the layer's own fetches) or, in the gap, of its down kernel: their victims are slots this call
+  // does not use, and the next layer's kernels follow them in stream order, with no launch or event
+  // of their own.  A budget or link cap of 0 lets the request fetch nothing (it still stamps its
+  // hits), so nothing rides along then.
+  SpecCopy sc;
+  if (spec && e->spec_budget != 0 && e->spec_link != 0) {
+    sc.fl = e->d_fetch + spec_fetch_list(layer + 1);
+    sc.nwg = kSpecCopyWGs;
+    sc.S = c.num_slots;
+    sc.n_flat = (int64_t)c.num_layers * c.num_experts;
   }
-  // this layer's speculative fetches travel on the side stream: right after the control kernel, or
-  // in the gap after the gate/up kernel, which copies the layer's own fetched records.  A budget or
-  // link cap of 0 lets the request fetch nothing (it still stamps its hits), so there is no copy.
-  const bool copy = spec && e->spec_budget != 0 && e->spec_link != 0;
-  const bool gap = copy && e->spec_in_gap;
-  if (copy && !gap) {
-    EFF_HIP_TRY(hipEventRecord(e->ev_ctl, cs));
-    EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_ctl, 0));
-    EFF_HIP_TRY(launch_fetch_copy(e, spec_fetch_list(layer + 1), ss));
-    EFF_HIP_TRY(hipEventRecord(e->ev_spec, ss));
-    e->spec_copy_pending = true;
-  }
-  // GPU experts; a unit installed by this call reads its record from the pool and fills its slot
   e->timing_q_src = e->d_counts + 1;  // this call's fetch count (real split)
-  const hipError_t ffn_err = launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true,
-                                               gap ? e->ev_gateup : nullptr);
+  const hipError_t ffn_err = launch_ffn_decode(e, layer, (const uint16_t*)x, e->d_slots, B, e->d_ygpu, cs, true, sc,
+                                               e->spec_in_gap);
   e->timing_q_src = nullptr;
   EFF_HIP_TRY(ffn_err);
-  if (gap) {  // the victims are slots this call does not use, so the copy may overlap its down kernel
-    EFF_HIP_TRY(hipStreamWaitEvent(ss, e->ev_gateup, 0));
-    EFF_HIP_TRY(launch_fetch_copy(e, spec_fetch_list(layer + 1), ss));
-    EFF_HIP_TRY(hipEventRecord(e->ev_spec, ss));
-    e->spec_copy_pending = true;
-  }
   if (e->async_host) {
     // the combine waits for the host share (or the control kernel's own release of the call)
     EFF_HIP_TRY(launch_combine(e->d_ygpu, e->h_yhost_dev, e->d_slots, e->d_w, B, K, c.hidden, (uint16_t*)out, cs,

@@ -40,6 +40,25 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWG = 256;  // 4 waves
 
+// Workgroup wg of nwg (kWG threads) copies its share of a fetch list's records from the pinned host
+// pool into their slots: 16 KiB chunks in turn, 16 bytes per thread; entries outside the pool or the
+// arena are skipped.
+__device__ void copy_fetch_list(const uint8_t* __restrict__ pool, uint8_t* __restrict__ arena, int64_t R,
+                                int64_t n_flat, int S, const FetchList* __restrict__ fl, int wg, int nwg) {
+  constexpr int64_t kChunk = 16384;
+  const int n = min(fl->count, kMaxEntries);
+  const int64_t chunks = (R + kChunk - 1) / kChunk;
+  for (int64_t c = wg; c < (int64_t)n * chunks; c += nwg) {
+    const int i = (int)(c / chunks);
+    const int64_t off = (c % chunks) * kChunk, len = min(kChunk, R - off);
+    const int flat = fl->flat[i], slot = fl->slot[i];
+    if (flat < 0 || flat >= n_flat || slot < 0 || slot >= S) continue;
+    const uint4* src = reinterpret_cast<const uint4*>(pool + (int64_t)flat * R + off);
+    uint4* dst = reinterpret_cast<uint4*>(arena + (int64_t)slot * R + off);
+    for (int64_t b = threadIdx.x; b < len / 16; b += kWG) dst[b] = src[b];
+  }
+}
+
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -268,7 +287,7 @@ __device__ inline float sum16(float v) {
 // inside this kernel, and k_down finds it resident.
 template <int FMT, int NT, int P>
 __global__ void __launch_bounds__(kWG, (FMT == EFF_WFMT_NVFP4_G16_E4M3 || NT < 8) ? 3 : 2)
-k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
+k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
          const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H,
          int I, int K, int maxB, int nch, uint16_t* __restrict__ a16, float2* __restrict__ ag) {
   static_assert(P == 1 || P == 2, "1 or 2 waves per matrix of a slice");
@@ -276,8 +295,13 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   constexpr int UNR = NT == 1 ? 4 : NT == 2 ? 8 : NT == 4 ? 6 : 4;  // runs in flight per wave
   extern __shared__ uint4 s_x[];                  // NT > 1: [NT][H/8] token rows of the chunk, 1 KiB slack
   __shared__ float s_red[4][16][NT];
+  if ((int)blockIdx.x < sc.nwg) {  // the front of the grid carries a speculative copy
+    copy_fetch_list(pool, arena, R, sc.n_flat, sc.S, sc.fl, blockIdx.x, sc.nwg);
+    return;
+  }
+  const int bid = blockIdx.x - sc.nwg;
   const int NS = I / 16, NG = NS / SPW, KB = H / 32, NRF = KB / 4;
-  const int u = blockIdx.x / (NG * nch), ch = (blockIdx.x / NG) % nch, sgp = blockIdx.x % NG;
+  const int u = bid / (NG * nch), ch = (bid / NG) % nch, sgp = bid % NG;
   const DecodeUnit* un = &plan->unit[u];
   const int cnt = un->count;
   // A resident unit's token chunks run in workgroups of their own (chunk ch: tokens ch*NT ..), so the
@@ -485,7 +509,7 @@ __device__ inline void down_run(const uint4 wd, const Scales4& rd, const uint4* 
 // are copied into LDS with their per-group scales and sums once for the workgroup's slices.
 template <int FMT, int NT, int WPS>
 __global__ void __launch_bounds__(kWG)
-k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
+k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
        const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ a16,
        const float2* __restrict__ ag, int H, int I, int maxB, int nch, float* __restrict__ y) {
   static_assert(WPS == 1 || WPS == 2 || WPS == 4, "1, 2 or 4 waves per slice");
@@ -493,8 +517,13 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R,
   constexpr int UNR = NT <= 2 ? 4 : 6;            // runs in flight per wave (4: fewer VGPRs, more waves)
   extern __shared__ uint4 s_a4[];               // [NT][I/8] groups of 8 fp16, then [NT][I/8] float2
   __shared__ float s_red[4][16][NT];
+  if ((int)blockIdx.x < sc.nwg) {  // the front of the grid carries a speculative copy
+    copy_fetch_list(pool, arena, R, sc.n_flat, sc.S, sc.fl, blockIdx.x, sc.nwg);
+    return;
+  }
+  const int bid = blockIdx.x - sc.nwg;
   const int NSH = H / 16, NG = NSH / SPW, KB = I / 32, NRF = KB / 4, I8 = I / 8;
-  const int u = blockIdx.x / (NG * nch), ch = (blockIdx.x / NG) % nch, sgp = blockIdx.x % NG;
+  const int u = bid / (NG * nch), ch = (bid / NG) % nch, sgp = bid % NG;
   const DecodeUnit* un = &plan->unit[u];
   const int cnt = un->count;
   // with nch > 1 each token chunk of a unit in workgroups of its own (every record is resident by now),
@@ -645,26 +674,6 @@ k_combine(const float* __restrict__ yg, const float* __restrict__ yh, const int3
   out[(int64_t)t * H + h] = (uint16_t)(b >> 16);
 }
 
-// ---------------------------------------------------------------------------- fetch copy
-// Copies the records of a fetch list from the pinned host pool into their slots (16 KiB chunks,
-// 16 bytes per thread); entries outside the pool or the arena are skipped.
-__global__ void __launch_bounds__(256)
-k_fetch_copy(const uint8_t* __restrict__ pool, uint8_t* __restrict__ arena, int64_t R, int64_t n_flat, int S,
-             const FetchList* __restrict__ fl) {
-  constexpr int64_t kChunk = 16384;
-  const int n = min(fl->count, kMaxEntries);
-  const int64_t chunks = (R + kChunk - 1) / kChunk;
-  for (int64_t c = blockIdx.x; c < (int64_t)n * chunks; c += gridDim.x) {
-    const int i = (int)(c / chunks);
-    const int64_t off = (c % chunks) * kChunk, len = min(kChunk, R - off);
-    const int flat = fl->flat[i], slot = fl->slot[i];
-    if (flat < 0 || flat >= n_flat || slot < 0 || slot >= S) continue;
-    const uint4* src = reinterpret_cast<const uint4*>(pool + (int64_t)flat * R + off);
-    uint4* dst = reinterpret_cast<uint4*>(arena + (int64_t)slot * R + off);
-    for (int64_t b = threadIdx.x; b < len / 16; b += 256) dst[b] = src[b];
-  }
-}
-
 // The link rate of the in-kernel fetch path, for the bandwidth profile: n records (flat ids first,
 // first + stride, ... modulo the pool) copied from the pinned host pool with 16-byte loads, like
 // the fetch units of k_gateup, into two record-sized device buffers used in turn.
@@ -693,33 +702,35 @@ int down_wps(int slices, int runs) {
 // the timing then covers the kernel alone, as a profiler's kernel trace does.
 template <int FMT, int NT, int P>
 hipError_t launch_gateup_t(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int nch, hipStream_t s,
-                           uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1) {
+                           uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
-  const dim3 grid(units * nch * (I / 16) * P / 2), block(kWG);
+  if (!sc.fl) sc.nwg = 0;
+  const dim3 grid(sc.nwg + units * nch * (I / 16) * P / 2), block(kWG);
   const uint32_t lds = NT > 1 ? NT * H * 2 + 1024 : 0;  // token rows and the copies' slack
   if (t0)
-    hipExtLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R,
+    hipExtLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R, sc,
                           e->d_ts, plan, x, H, I, c.top_k, c.max_tokens, nch, a16, ag);
   else
-    hipLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, e->d_ts, plan, x,
-                       H, I, c.top_k, c.max_tokens, nch, a16, ag);
+    hipLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, sc, e->d_ts, plan,
+                       x, H, I, c.top_k, c.max_tokens, nch, a16, ag);
   return hipGetLastError();
 }
 
 template <int FMT, int NT, int WPS>
 hipError_t launch_down_t(eff_engine* e, const DecodePlan* plan, int units, int nch, hipStream_t s, const uint16_t* a16,
-                         const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1) {
+                         const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
+  if (!sc.fl) sc.nwg = 0;
   const uint32_t lds = (uint32_t)(NT * (I / 8) * (sizeof(uint4) + sizeof(float2)));
-  const dim3 grid(units * nch * (H / 16) * WPS / 4), block(kWG);
+  const dim3 grid(sc.nwg + units * nch * (H / 16) * WPS / 4), block(kWG);
   if (t0)
-    hipExtLaunchKernelGGL((k_down<FMT, NT, WPS>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R,
+    hipExtLaunchKernelGGL((k_down<FMT, NT, WPS>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R, sc,
                           e->d_ts, plan, a16, ag, H, I, c.max_tokens, nch, y);
   else
-    hipLaunchKernelGGL((k_down<FMT, NT, WPS>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, e->d_ts, plan, a16,
-                       ag, H, I, c.max_tokens, nch, y);
+    hipLaunchKernelGGL((k_down<FMT, NT, WPS>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, sc, e->d_ts, plan,
+                       a16, ag, H, I, c.max_tokens, nch, y);
   return hipGetLastError();
 }
 
@@ -737,31 +748,33 @@ int down_nt(int B, int I) {
 
 template <int FMT, int NT>
 hipError_t launch_gateup_p(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int B, hipStream_t s,
-                           uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1) {
+                           uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
   const int nch = (B + NT - 1) / NT;  // token chunks a unit can have (a unit holds at most one entry per token)
   if (gateup_waves_per_matrix(units * (e->cfg.inter / 16)) == 1)
-    return launch_gateup_t<FMT, NT, 1>(e, plan, x, units, nch, s, a16, ag, t0, t1);
-  return launch_gateup_t<FMT, NT, 2>(e, plan, x, units, nch, s, a16, ag, t0, t1);
+    return launch_gateup_t<FMT, NT, 1>(e, plan, x, units, nch, s, a16, ag, t0, t1, sc);
+  return launch_gateup_t<FMT, NT, 2>(e, plan, x, units, nch, s, a16, ag, t0, t1, sc);
 }
 
 template <int FMT, int NT>
 hipError_t launch_down_w(eff_engine* e, const DecodePlan* plan, int units, hipStream_t s, const uint16_t* a16,
-                         const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1) {
+                         const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
   // the down kernel takes a unit's chunks in turn: its rows are short (I inputs), so a second wave of
   // workgroups per unit costs more than the chunks' arithmetic it would spread
   switch (down_wps(units * (e->cfg.hidden / 16), e->cfg.inter / 128)) {
-    case 1: return launch_down_t<FMT, NT, 1>(e, plan, units, 1, s, a16, ag, y, t0, t1);
-    case 2: return launch_down_t<FMT, NT, 2>(e, plan, units, 1, s, a16, ag, y, t0, t1);
-    default: return launch_down_t<FMT, NT, 4>(e, plan, units, 1, s, a16, ag, y, t0, t1);
+    case 1: return launch_down_t<FMT, NT, 1>(e, plan, units, 1, s, a16, ag, y, t0, t1, sc);
+    case 2: return launch_down_t<FMT, NT, 2>(e, plan, units, 1, s, a16, ag, y, t0, t1, sc);
+    default: return launch_down_t<FMT, NT, 4>(e, plan, units, 1, s, a16, ag, y, t0, t1, sc);
   }
 }
 
 // The two expert kernels of one call on the plan `plan`; a16 holds units * max_tokens * I fp16
 // activations (a unit's token j is row u * max_tokens + j whatever the chunk widths) and ag one
 // (scale, sum) pair per 8 of them.  `timed`: bracket the kernels with the engine's timing events.
+// `spec`: a speculative copy carried by the gate/up kernel, or by the down kernel when in_down.
 template <int FMT>
 hipError_t launch_ffn_t(eff_engine* e, const DecodePlan* plan, uint16_t* a16, float2* ag, const uint16_t* x, float* y,
-                        int units, int B, hipStream_t s, hipEvent_t after_gateup, bool timed) {
+                        int units, int B, hipStream_t s, SpecCopy spec, bool in_down, bool timed) {
+  const SpecCopy none, sg = in_down ? none : spec, sd = in_down ? spec : none;
   // timed outside a capture: each kernel sets its own start and end events; inside a capture the
   // events are recorded on the stream around the launches
   const bool own = timed && !stream_capturing(s);
@@ -770,21 +783,20 @@ hipError_t launch_ffn_t(eff_engine* e, const DecodePlan* plan, uint16_t* a16, fl
   hipEvent_t d0 = own ? timing_event(e, ts, 2) : nullptr, d1 = own ? timing_event(e, ts, 3) : nullptr;
   hipError_t err;
   switch (gateup_nt(B)) {
-    case 1: err = launch_gateup_p<FMT, 1>(e, plan, x, units, B, s, a16, ag, g0, g1); break;
-    case 2: err = launch_gateup_p<FMT, 2>(e, plan, x, units, B, s, a16, ag, g0, g1); break;
-    case 4: err = launch_gateup_p<FMT, 4>(e, plan, x, units, B, s, a16, ag, g0, g1); break;
-    default: err = launch_gateup_p<FMT, 8>(e, plan, x, units, B, s, a16, ag, g0, g1); break;
+    case 1: err = launch_gateup_p<FMT, 1>(e, plan, x, units, B, s, a16, ag, g0, g1, sg); break;
+    case 2: err = launch_gateup_p<FMT, 2>(e, plan, x, units, B, s, a16, ag, g0, g1, sg); break;
+    case 4: err = launch_gateup_p<FMT, 4>(e, plan, x, units, B, s, a16, ag, g0, g1, sg); break;
+    default: err = launch_gateup_p<FMT, 8>(e, plan, x, units, B, s, a16, ag, g0, g1, sg); break;
   }
   if (err != hipSuccess) return err;
-  if (after_gateup && (err = hipEventRecord(after_gateup, s)) != hipSuccess) return err;
   if (!own) {
     timing_mark(e, ts, 1, s);
     timing_mark(e, ts, 2, s);
   }
   switch (down_nt(B, e->cfg.inter)) {
-    case 1: err = launch_down_w<FMT, 1>(e, plan, units, s, a16, ag, y, d0, d1); break;
-    case 2: err = launch_down_w<FMT, 2>(e, plan, units, s, a16, ag, y, d0, d1); break;
-    default: err = launch_down_w<FMT, 4>(e, plan, units, s, a16, ag, y, d0, d1); break;
+    case 1: err = launch_down_w<FMT, 1>(e, plan, units, s, a16, ag, y, d0, d1, sd); break;
+    case 2: err = launch_down_w<FMT, 2>(e, plan, units, s, a16, ag, y, d0, d1, sd); break;
+    default: err = launch_down_w<FMT, 4>(e, plan, units, s, a16, ag, y, d0, d1, sd); break;
   }
   if (!own) timing_mark(e, ts, 3, s);
   return err;
@@ -822,7 +834,7 @@ hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
 }
 
 hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const int32_t* slots, int B,
-                             float* y, hipStream_t s, bool plan_ready, hipEvent_t after_gateup) {
+                             float* y, hipStream_t s, bool plan_ready, SpecCopy spec, bool in_down) {
   (void)layer;
   if (!plan_ready) {
     hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s, e->d_plan, e->maxU);
@@ -834,8 +846,8 @@ hipError_t launch_ffn_decode(eff_engine* e, int layer, const uint16_t* x, const 
   uint16_t* a16 = reinterpret_cast<uint16_t*>(e->d_a);
   float2* ag = reinterpret_cast<float2*>(a16 + (size_t)e->maxU * e->cfg.max_tokens * e->cfg.inter);
   if (e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3)
-    return launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3>(e, e->d_plan, a16, ag, x, y, units, B, s, after_gateup, true);
-  return launch_ffn_t<EFF_WFMT_INT4_G32_BF16>(e, e->d_plan, a16, ag, x, y, units, B, s, after_gateup, true);
+    return launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3>(e, e->d_plan, a16, ag, x, y, units, B, s, spec, in_down, true);
+  return launch_ffn_t<EFF_WFMT_INT4_G32_BF16>(e, e->d_plan, a16, ag, x, y, units, B, s, spec, in_down, true);
 }
 
 // ---------------------------------------------------------------------------- static scratch
@@ -889,21 +901,14 @@ hipError_t launch_ffn_decode_noalloc(eff_engine* e, const uint16_t* x, const int
   hipError_t err = launch_plan(e, slots, B * e->cfg.top_k, s, plan, units);
   if (err != hipSuccess) return err;
   if (e->cfg.wformat == EFF_WFMT_NVFP4_G16_E4M3)
-    return launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3>(e, plan, a16, ag, x, y, units, B, s, nullptr, false);
-  return launch_ffn_t<EFF_WFMT_INT4_G32_BF16>(e, plan, a16, ag, x, y, units, B, s, nullptr, false);
+    return launch_ffn_t<EFF_WFMT_NVFP4_G16_E4M3>(e, plan, a16, ag, x, y, units, B, s, SpecCopy(), false, false);
+  return launch_ffn_t<EFF_WFMT_INT4_G32_BF16>(e, plan, a16, ag, x, y, units, B, s, SpecCopy(), false, false);
 }
 
 hipError_t launch_bw_copy(eff_engine* e, int64_t first, int64_t stride, int n, uint8_t* dst, hipStream_t s) {
   const eff_config& c = e->cfg;
   hipLaunchKernelGGL(k_bw_copy, dim3(1024), dim3(256), 0, s, e->pool_dev, e->R,
                      (int64_t)c.num_layers * c.num_experts, first, stride, n, dst);
-  return hipGetLastError();
-}
-
-hipError_t launch_fetch_copy(eff_engine* e, int which, hipStream_t s) {
-  const eff_config& c = e->cfg;
-  hipLaunchKernelGGL(k_fetch_copy, dim3(256), dim3(256), 0, s, e->pool_dev, e->d_arena, e->R,
-                     (int64_t)c.num_layers * c.num_experts, c.num_slots, e->d_fetch + which);
   return hipGetLastError();
 }
 

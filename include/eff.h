@@ -200,12 +200,15 @@ int eff_set_fetch_frac(eff_engine* e, uint32_t frac_q16);
  *   max_fetch  records one speculative request may fetch at most: its q' becomes
  *              min(q', max_fetch), the first ranked misses; -1 = no budget (the
  *              default), 0 = fetch none (predicted residents are still protected).
- *   in_gap     0: eff_decode_layer starts a speculative copy right after the
- *              control kernel, beside the layer's own fetches (the default);
- *              1: after the layer's gate/up kernel, which performs those fetches.
- * Either way the next layer's expert kernels wait for the copy.  Applies to the
- * calls enqueued after it (a graph captured earlier keeps its values); the policy
- * and every result other than timing are the same for both values of in_gap.
+ *   in_gap     0: eff_decode_layer's speculative copy is carried by extra
+ *              workgroups of the layer's gate/up kernel, beside the layer's own
+ *              fetches (the default); 1: by the layer's down kernel, after the
+ *              gate/up kernel has performed those fetches.
+ * Either way the next layer's kernels follow the copy in stream order, and a
+ * request that can fetch nothing (max_fetch 0, or a link cap of 0) carries no
+ * copy.  Applies to the calls enqueued after it (a graph captured earlier keeps
+ * its values); the policy and every result other than timing are the same for
+ * both values of in_gap.
  * EFF_EINVAL for max_fetch < -1 or in_gap not 0 or 1. */
 int eff_set_speculation(eff_engine* e, int max_fetch, int in_gap);
 
@@ -275,7 +278,7 @@ int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const in
 
 /* One decode MoE layer end to end: route (from x and w_router, or from logits if
  * w_router is NULL) -> ensure -> split -> [speculative ensure/split of layer+1
- * on spec_ids if not NULL, its copies on `side`] -> GPU expert FFN -> host share
+ * on spec_ids if not NULL, its copies inside this layer's expert kernels] -> GPU expert FFN -> host share
  * -> combine into out (bf16 [B,H]).  top-K, ensure, split, the speculative
  * request and the decode plan run as one single-workgroup kernel with the same
  * semantics as the separate calls ([FT-blog] §六).  Experts installed by the
@@ -288,7 +291,7 @@ int eff_combine(eff_engine* e, const float* y_gpu, const float* y_host, const in
  * bounded poll), so the call only enqueues work and returns.  Nothing of a call
  * passes through the host at enqueue time, so a sequence of calls (for example
  * all layers of one decode step) may be captured into a HIP graph on `compute`
- * (with `side` joined through the call's own events) and replayed; the inputs
+ * and replayed (`side` is only checked for capture; nothing is enqueued on it); the inputs
  * are then read from the captured addresses at each replay ([FT-deep] §4 ④: the
  * host branch inside the graph waits on host memory).  With EFF_CFG_SYNC_HOST
  * the calling thread waits for the control kernel and runs the host share
