@@ -685,8 +685,8 @@ def main():
                                       3),
             "MB_per_layer": head["link_MB_per_layer"],
             "note": "the headline step at f = 65535: every miss and every speculative guess crosses PCIe inside "
-                    "the gate/up kernel or the speculative copy kernel; its rate against the link rate the "
-                    "bandwidth profile measured on this machine"}
+                    "the layer's expert kernels (speculative records in extra workgroups of the same kernels); "
+                    "its rate against the link rate the bandwidth profile measured on this machine"}
     dk = None
     if not args.skip_prefill:
         log("decode kernels %s (2 layers resident)" % DSV4_DECODE.name)

@@ -50,8 +50,8 @@ struct Pending {
 
 // Fetch lists written by the split kernel (device memory and a host-mapped mirror): list 0 for real
 // calls, lists 1 and 2 for speculative requests of even and odd layers.  A speculative request made
-// during layer l (for layer l+1) is copied on a side stream that the next layer's expert kernels wait
-// for; the request that reuses its list is made two layers later, after that wait.
+// during layer l (for layer l+1) is copied by extra workgroups of layer l's own expert kernels; the
+// request that reuses its list is made two layers later, after those kernels in stream order.
 constexpr int kFetchLists = 3;
 // Bytes allocated after the last slot of the arena: a decode wave loads a whole 1 KiB run (and its
 // 128 scale bytes) even where a slice ends inside it, and past its last run it loads that run again

@@ -628,8 +628,8 @@ __device__ __attribute__((always_inline)) void commit_body(const CacheState& c, 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = C.n, spec = C.spec, m = C.nm, nu = C.nu, qq = C.qq;
   const int64_t s = C.s, base = (int64_t)C.layer * c.E;
-  // a speculative request for layer l fills list 1 + l % 2, so the copy of the previous request (on
-  // another stream, ordered before the next layer's expert kernels) never reads a list being rewritten
+  // a speculative request for layer l fills list 1 + l % 2: consecutive requests never share a list,
+  // whichever kernel carries their copies
   const int li = spec ? spec_fetch_list(C.layer) : 0;
   FetchList* fl = c.fl_dev + li;
   FetchList* flh = c.fl_host + li;
