@@ -1,7 +1,9 @@
 """GPU parity of the integer control path against the oracle, bit for bit:
 q* (every f for m <= 64), router ids, and whole ensure/split call sequences
 (slots, host ids, counts, fetch lists, final tables), including speculative
-calls, S = 0, tiny caches and calls large enough for the sorted victim path."""
+calls, S = 0, tiny caches, calls with more than 4 victims (the radix select,
+up to four 8-bit passes) and calls with more than 64 entries (the expert-table
+ensure at most 2048 experts, the sweep ensure above)."""
 import random
 
 import numpy as np
@@ -213,12 +215,43 @@ def test_sequences_batched_speculative(eff):
 
 
 def test_sequences_many_fetches_sorted_path(eff):
-    # > 16 fetches per call exercise the sorted victim selection
+    # many fetches per call (256 entries): the radix victim selection and the expert-table ensure
     rng = random.Random(4)
     L, E, K, B = 3, 256, 8, 32
     calls = [(s % L, [e for _ in range(B) for e in rng.sample(range(E), K)], False) for s in range(18)]
     run_sequence(eff, L, E, K, 700, 65536, calls, B)
     run_sequence(eff, L, E, K, 5000, 65536, calls, B)
+
+
+def test_sequences_many_experts_sweep_path(eff):
+    # more than 64 entries and more than 2048 experts: the ensure takes its sweeps over the entries
+    # (the expert-table path covers at most 2048); half of the tokens draw from a small hot set so
+    # that ids repeat across tokens, the rest from the whole range (ids above 2048 included)
+    rng = random.Random(5)
+    L, E, K, B = 2, 3000, 8, 16
+    hot = rng.sample(range(E), 24)
+
+    def draw():
+        return [e for _ in range(B) for e in rng.sample(hot if rng.random() < 0.5 else range(E), K)]
+
+    calls = []
+    for step in range(24):
+        layer = step % L
+        calls.append((layer, draw(), False))
+        if layer + 1 < L:
+            calls.append((layer + 1, draw(), True))
+    for S, f in [(200, 65535), (300, 45875)]:
+        run_sequence(eff, L, E, K, S, f, calls, B)
+
+
+def test_sequences_long_run_radix_passes(eff):
+    # the largest cache (16384 slots) filling up over 1400 calls of about 8 misses each (8 layers of
+    # 4096 experts): past step 1024 the empty slots' victim keys (below 2^14) sit beside used ones
+    # above 2^24, so the radix select runs four 8-bit passes (every other case here needs at most three)
+    rng = random.Random(6)
+    L, E, K, B = 8, 4096, 8, 1
+    calls = [(s % L, rng.sample(range(E), K), False) for s in range(1400)]
+    run_sequence(eff, L, E, K, 16384, 65535, calls, B)
 
 
 def test_bad_id_reported(eff):
