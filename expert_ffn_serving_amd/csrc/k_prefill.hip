@@ -25,6 +25,7 @@
 #include <hip/hip_ext.h>
 
 #include "eff_internal.h"
+#include "lds_dma.h"
 
 namespace eff {
 namespace {
@@ -176,6 +177,8 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   constexpr int SEGW = 256 / SEGS;           // inputs per staging thread per chunk
   constexpr int SV = SEGW / 8;               // 16-byte vectors per staging thread
   __shared__ uint32_t s_a[2][kMT * kRowU32];
+  // FULL: each wave's scale bytes of a chunk (4 slices x 8 k-tiles x 32 bytes), double buffered
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][NMAT * 4][FULL ? 4 * kCT * 32 : 16];
   const int N = (NMAT == 2) ? I : H, Kd = (NMAT == 2) ? H : I;
   const int NJ = (N / 64 + 3) / 4;
   int e, j;
@@ -209,6 +212,18 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   }
   float tsc = 1.f;
   if (FMT == EFF_WFMT_NVFP4_G16_E4M3) tsc = ts[(int64_t)owner[slot] * 3 + mi];
+  // FULL: the scales of a slice's 8 k-tiles of a chunk are 256 contiguous bytes, so one LDS-direct
+  // copy per chunk brings the wave's 4 slices (lane l: slice l/16, bytes 16(l%16)..+15) into
+  // s_sc[buf][wave] = [slice][k-tile of the chunk][32 bytes], with no register held while in flight;
+  // each k-tile then reads its lane's byte (int4: bf16) back.  Without FULL the scales stream
+  // beside the weights in registers.
+  const uint8_t* scb = rec + 3 * pay + mi * sca + (int64_t)((active ? nb : 0) * 4 + (lane >> 4)) * sstride +
+                       (lane & 15) * 16;
+  const uint32_t sc_lds0 = lds_address(&s_sc[0][wave][0]), sc_lds1 = lds_address(&s_sc[1][wave][0]);
+  const int sc_lane = (FMT == EFF_WFMT_INT4_G32_BF16) ? r * 2 : (q >> 1) * 16 + r;
+  auto sc_copy = [&](int c, int buf) {
+    if constexpr (FULL) lds_copy16(scb + (int64_t)c * kCT * 32, buf ? sc_lds1 : sc_lds0);
+  };
   // Staging role: row srow; piece z (8 inputs, 16 bytes) of the chunk starts at input pbase + z * pstep.
   // Every 16 (and every 8) consecutive lanes of a 16-byte LDS store hit distinct bank groups (the
   // row stride of 132 dwords advances the bank by 4 per row):
@@ -278,14 +293,15 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
       }
     };
     // weight ring: k-tile kb lives in slot kb % PF
-    uint32_t wq[PF][4], sq[PF][4];
+    uint32_t wq[PF][4], sq[FULL ? 1 : PF][4];
     auto wtile = [&](int k, int ring) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         wq[ring][t] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, woff[t], k * 256, 0);
-        sq[ring][t] = (FMT == EFF_WFMT_INT4_G32_BF16)
-                          ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, soff[t], k * 32, 0)
-                          : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsrc, soff[t], k * 32, 0);
+        if constexpr (!FULL)
+          sq[ring][t] = (FMT == EFF_WFMT_INT4_G32_BF16)
+                            ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, soff[t], k * 32, 0)
+                            : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsrc, soff[t], k * 32, 0);
       }
     };
     auto wload = [&](int kb, int ring) {
@@ -297,25 +313,40 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           wq[ring][t] = 0u;
-          sq[ring][t] = 0u;
+          if constexpr (!FULL) sq[ring][t] = 0u;
         }
       }
     };
     stage_load(0);
+    sc_copy(0, 0);
+    if constexpr (FULL) vm_wait<0>();  // chunk 0's scales are in LDS (with the stage loads)
     stage_store(0);
 #pragma unroll
     for (int p = 0; p < PF; ++p) wload(p, p);
     __syncthreads();
     for (int c = 0; c < nchunk; ++c) {
       const int buf = c & 1;
-      if (c + 1 < nchunk) stage_load(c + 1);
+      if (c + 1 < nchunk) {
+        stage_load(c + 1);
+        sc_copy(c + 1, buf ^ 1);
+      }
       const uint32_t* abase = s_a[buf] + r * kRowU32 + q * 4;
-      // A fragments (all 4 subtiles; rows past mt are discarded: no branches), read one k-tile ahead
+      const uint8_t* sbase = &s_sc[buf][wave][0] + sc_lane;
+      // A fragments (all 4 subtiles; rows past mt are discarded: no branches) and, with FULL, the
+      // lane's scales of the 4 slices, read one k-tile ahead
       f16x8_t an[4];
+      uint32_t sn[4];
       auto aread = [&](int kk) {
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2)
           an[s2] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(abase + s2 * 16 * kRowU32 + kk * 16));
+        if constexpr (FULL) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            sn[t] = (FMT == EFF_WFMT_INT4_G32_BF16)
+                        ? (uint32_t)*reinterpret_cast<const uint16_t*>(sbase + t * kCT * 32 + kk * 32)
+                        : (uint32_t)sbase[t * kCT * 32 + kk * 32];
+        }
       };
       aread(0);
 #pragma unroll
@@ -326,16 +357,16 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
         __builtin_amdgcn_sched_barrier(0);
         if (FULL || kb < KB) {  // uniform
           f16x8_t af[4];
+          uint32_t sc[4];
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) af[s2] = an[s2];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) sc[t] = FULL ? sn[t] : sq[FULL ? 0 : kk % PF][t];
           if (kk + 1 < kCT) aread(kk + 1);
           const int ring = kk % PF;  // kCT % PF == 0: static after unrolling
-          uint32_t w[4], sc[4];
+          uint32_t w[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            w[t] = wq[ring][t];
-            sc[t] = sq[ring][t];
-          }
+          for (int t = 0; t < 4; ++t) w[t] = wq[ring][t];
           wload(kb + PF, ring);  // prefetch
           __builtin_amdgcn_sched_barrier(0);  // keep the prefetch issued ahead of this k-tile's math
           if (active) {
@@ -359,6 +390,8 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
           }
         }
       }
+      // the next chunk's scales: their copy was issued before this chunk's 4 * kCT weight loads
+      if constexpr (FULL) vm_wait<4 * kCT>();
       if (c + 1 < nchunk) stage_store(buf ^ 1);
       __syncthreads();
     }
