@@ -229,6 +229,7 @@ struct eff_engine {
   int32_t* d_pf_count = nullptr;  // [E+1] per-expert counts / offsets
   int32_t* d_pf_rows = nullptr;   // [T*K] sorted entries (t*K+k)
   uint16_t* d_pf_a = nullptr;     // [T*K][I] fp16 SwiGLU activations
+  uint16_t* d_pf_x = nullptr;     // [T][H] fp16 copy of the tokens' bf16 inputs
   float* d_pf_y = nullptr;        // [T*K][H] fp32 expert outputs
   int32_t* d_pf_meta = nullptr;   // misc
   hipEvent_t ev_copy = nullptr, ev_pf[2] = {nullptr, nullptr};

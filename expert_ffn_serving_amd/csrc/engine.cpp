@@ -68,7 +68,7 @@ static void release(eff_engine* e) {
   void* dev[] = {e->d_arena, e->d_table, e->d_owner, e->d_usage, e->d_recency, e->d_clock, e->d_ts,
                  e->d_pending, e->d_fetch, e->d_err, e->d_seq, e->d_stats, e->d_plan, e->d_a, e->d_ids, e->d_w, e->d_slots, e->d_cpu, e->d_counts, e->d_spec_ids,
                  e->d_spec_cpu, e->d_logits, e->d_ygpu, e->d_yhost, e->d_pf_count, e->d_pf_rows,
-                 e->d_pf_a, e->d_pf_y, e->d_pf_meta, e->d_pf_slot_of, e->d_pf_experts};
+                 e->d_pf_a, e->d_pf_x, e->d_pf_y, e->d_pf_meta, e->d_pf_slot_of, e->d_pf_experts};
   for (void* p : dev)
     if (p) (void)hipFree(p);
   void* host[] = {e->h_fetch, e->h_x, e->h_cpu, e->h_call, e->h_done, e->h_yhost, e->h_pf_ids, e->h_pf_meta,
@@ -142,6 +142,7 @@ static int alloc_all(eff_engine* e) {
     EFF_HIP_TRY(dalloc(&e->d_pf_count, E + 1));
     EFF_HIP_TRY(dalloc(&e->d_pf_rows, T * K));
     EFF_HIP_TRY(dalloc(&e->d_pf_a, (size_t)(T * K * I)));
+    EFF_HIP_TRY(dalloc(&e->d_pf_x, (size_t)(T * H)));
     EFF_HIP_TRY(dalloc(&e->d_pf_y, (size_t)(T * K * H)));
     EFF_HIP_TRY(dalloc(&e->d_pf_slot_of, E));
     EFF_HIP_TRY(dalloc(&e->d_pf_experts, E));

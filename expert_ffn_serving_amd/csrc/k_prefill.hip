@@ -6,6 +6,7 @@
 // whole prompt through one layer so that experts are not re-read per chunk).
 //
 //   k_pf_sort     one workgroup: count (t,k) pairs per expert, scan, place
+//   k_pf_x16      the tokens' bf16 rows to fp16 once (range-checked), for every expert that reads them
 //   k_pf_gemm<2>  per (expert, 256 rows of I): [n_e x H] x [H x 256] for gate and up
 //                 on v_mfma_f32_16x16x32_f16, SwiGLU in the epilogue -> fp16 a
 //   k_pf_gemm<1>  per (expert, 256 rows of H): [n_e x I] x [I x 256] -> fp32 y per pair
@@ -23,6 +24,8 @@
 // SwiGLU output beyond the fp16 range sets bit 8 of the engine's device error
 // word, which the next host-waiting call reports, instead of passing an inf on.
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 
 #include "eff_internal.h"
 #include "lds_dma.h"
@@ -101,6 +104,29 @@ __device__ inline void map_block(int b, int E, int NJ, int* e, int* j) {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+constexpr float kF16Max = 65504.f;  // activations enter the MFMA as fp16: larger ones are reported
+
+// The tokens' bf16 rows to fp16, 8 values a thread, once per layer: each row is staged by every
+// workgroup of the K experts it is routed to, which then copy it as it is.  A value beyond the fp16
+// range sets bit 8 of the engine's device error word (it would become an infinity).
+__global__ void __launch_bounds__(256)
+k_pf_x16(const uint16_t* __restrict__ x, int64_t n8, uint16_t* __restrict__ x16, int32_t* err) {
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float lo = __uint_as_float(wv[k] << 16), hi = __uint_as_float(wv[k] & 0xFFFF0000u);
+      bad |= !(fabsf(lo) <= kF16Max) || !(fabsf(hi) <= kF16Max);
+      o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), f16x2_t));
+    }
+    reinterpret_cast<uint4*>(x16)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (err && __ballot(bad) && (threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // two floats -> fp16 pair (round to nearest even; one v_cvt_pk_f16_f32)
 __device__ inline uint32_t pk_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
@@ -147,7 +173,6 @@ __device__ inline uint32_t scale_pair(uint32_t raw) {
   return pk_f16(f, f);
 }
 
-constexpr float kF16Max = 65504.f;  // activations enter the MFMA as fp16: larger ones are reported
 constexpr int kMT = 64;         // tokens per pass (4 MFMA subtiles of 16)
 constexpr int kCT = 8;          // k-tiles (of 32 inputs) per staged activation chunk
 constexpr int kRowU32 = 132;    // LDS row stride in dwords: 256 fp16 + 4 dwords of padding
@@ -160,7 +185,7 @@ static_assert(kMT * kGRow <= 2 * kMT * kRowU32, "gate results fit the staging bu
 // (256 inputs), double buffered with one barrier per chunk: the next chunk's global loads are
 // issued before the current chunk's MFMAs.  Weights stream from the slot into registers PF
 // k-tiles ahead and are dequantized into the MFMA B operand.
-//   NMAT 2: gate (waves 0-3) and up (waves 4-7) from x (bf16 rows of the tokens); the gate waves
+//   NMAT 2: gate (waves 0-3) and up (waves 4-7) from x (fp16 rows of the tokens); the gate waves
 //           hand g to the up waves through LDS; a = silu(g) * u -> fp16, one row per sorted pair
 //   NMAT 1: down from a (fp16 sorted rows) -> y (fp32, one row per (t,k) pair)
 // FULL: H and I are multiples of 256 (whole chunks, whole row blocks): no per-k-tile checks, and
@@ -264,24 +289,8 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
       for (int z = 0; z < SV; ++z) {
         const uint4 v = stg[z];
         uint32_t o[4];
-        if (NMAT == 2) {  // bf16 -> fp16
-          float f[8];
-          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(wv[i] << 16);
-            f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
-          }
-          float mx = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(f[i]));
-          if (mx > kF16Max) range_bad = true;
-          if (FMT == EFF_WFMT_INT4_G32_BF16) {  // pairs (0,4), (1,5), (2,6), (3,7)
-            o[0] = pk_f16(f[0], f[4]); o[1] = pk_f16(f[1], f[5]); o[2] = pk_f16(f[2], f[6]); o[3] = pk_f16(f[3], f[7]);
-          } else {
-            o[0] = pk_f16(f[0], f[1]); o[1] = pk_f16(f[2], f[3]); o[2] = pk_f16(f[4], f[5]); o[3] = pk_f16(f[6], f[7]);
-          }
-        } else if (FMT == EFF_WFMT_INT4_G32_BF16) {  // fp16 halves h0..h7 -> pairs (0,4) ...
+        // fp16 rows (x converted once by k_pf_x16, or a): int4 pairs (0,4), (1,5), (2,6), (3,7)
+        if (FMT == EFF_WFMT_INT4_G32_BF16) {  // fp16 halves h0..h7 -> pairs (0,4) ...
           o[0] = (v.x & 0xFFFFu) | (v.z << 16);
           o[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
           o[2] = (v.y & 0xFFFFu) | (v.w << 16);
@@ -483,7 +492,16 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
       else EFF_PF_LAUNCH(EFF_WFMT_INT4_G32_BF16, NM, PFD, false, GRID, SRC, AO, YO);          \
     }                                                                                         \
   } while (0)
-  EFF_PF_PICK(2, kPfPrefetch2, full, nbx1, x, e->d_pf_a, (float*)nullptr);
+  // the tokens' rows to fp16 once; timed, the gate/up interval starts at this kernel
+  const int64_t n8 = (int64_t)T * H / 8;
+  const int xg = (int)std::min<int64_t>((n8 + 255) / 256, 2048);
+  if (own)
+    hipExtLaunchKernelGGL(k_pf_x16, dim3(xg), dim3(256), 0, s, t0, nullptr, 0, x, n8, e->d_pf_x, e->h_err_dev);
+  else
+    hipLaunchKernelGGL(k_pf_x16, dim3(xg), dim3(256), 0, s, x, n8, e->d_pf_x, e->h_err_dev);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  t0 = nullptr;
+  EFF_PF_PICK(2, kPfPrefetch2, full, nbx1, e->d_pf_x, e->d_pf_a, (float*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (!own) {
     timing_mark(e, ts, 1, s);
