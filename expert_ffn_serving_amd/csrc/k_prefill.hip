@@ -39,6 +39,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPfPrefetch2 = 4;  // weight prefetch depth (k-tiles) of the gate/up GEMM
 constexpr int kPfPrefetch1 = 4;
+constexpr int kPfGateupWPM = 4;  // gate/up: waves per matrix (64 rows each; 2, two workgroups per CU, was slower)
 constexpr int kPfLead = 12, kPfPer = 3;  // VALU ops before the first MFMA of a k-tile / after each MFMA  // ... and of the down GEMM
 
 __global__ void __launch_bounds__(1024)
@@ -179,33 +180,39 @@ constexpr int kRowU32 = 132;    // LDS row stride in dwords: 256 fp16 + 4 dwords
 constexpr int kGRow = 260;      // row stride (floats) of the gate results handed to the up waves
 static_assert(kMT * kGRow <= 2 * kMT * kRowU32, "gate results fit the staging buffers");
 
-// Grouped expert GEMM over the (t,k) pairs sorted by expert.  Workgroup = (expert, 256 output
-// rows) with NMAT * 4 waves: wave w computes 64 rows (4 row slices of 16) of matrix w / 4.  All
+// Grouped expert GEMM over the (t,k) pairs sorted by expert.  Workgroup = (expert, WPM * 64 output
+// rows) with NMAT * WPM waves: wave w computes 64 rows (4 row slices of 16) of matrix w / WPM.  All
 // waves share the activation rows of the expert, staged in LDS as fp16 in chunks of 8 k-tiles
 // (256 inputs), double buffered with one barrier per chunk: the next chunk's global loads are
 // issued before the current chunk's MFMAs.  Weights stream from the slot into registers PF
 // k-tiles ahead and are dequantized into the MFMA B operand.
-//   NMAT 2: gate (waves 0-3) and up (waves 4-7) from x (fp16 rows of the tokens); the gate waves
+//   NMAT 2: gate (waves 0..WPM-1) and up (the next WPM) from x (fp16 rows of the tokens); the gate waves
 //           hand g to the up waves through LDS; a = silu(g) * u -> fp16, one row per sorted pair
 //   NMAT 1: down from a (fp16 sorted rows) -> y (fp32, one row per (t,k) pair)
 // FULL: H and I are multiples of 256 (whole chunks, whole row blocks): no per-k-tile checks, and
 // loads past the end re-read the last k-tile instead of being skipped (no branches around memory
 // operations, so the compiler's wait counts stay exact and the prefetch stays in flight).
+template <int NMAT>
+constexpr int pf_wpm() { return NMAT == 2 ? kPfGateupWPM : 4; }
+template <int NMAT>
+constexpr int pf_threads() { return 64 * NMAT * pf_wpm<NMAT>(); }
+
 template <int FMT, int NMAT, int PF, bool FULL>
-__global__ void __launch_bounds__(256 * NMAT, NMAT == 2 ? 1 : 2)
+__global__ void __launch_bounds__(pf_threads<NMAT>(), pf_threads<NMAT>() > 256 ? 1 : 2)
 k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict__ ts,
           const int32_t* __restrict__ owner, int slot_base, const int32_t* __restrict__ slot_of,
           const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows, const uint16_t* __restrict__ src,
           int E, int H, int I, int K, uint16_t* __restrict__ a_out, float* __restrict__ y_out, int32_t* err) {
-  constexpr int TPB = 256 * NMAT;            // threads
+  constexpr int WPM = pf_wpm<NMAT>();        // waves per matrix
+  constexpr int TPB = pf_threads<NMAT>();    // threads
   constexpr int SEGS = TPB / kMT;            // staging threads per row
   constexpr int SEGW = 256 / SEGS;           // inputs per staging thread per chunk
   constexpr int SV = SEGW / 8;               // 16-byte vectors per staging thread
   __shared__ uint32_t s_a[2][kMT * kRowU32];
   // FULL: each wave's scale bytes of a chunk (4 slices x 8 k-tiles x 32 bytes), double buffered
-  __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][NMAT * 4][FULL ? 4 * kCT * 32 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][NMAT * WPM][FULL ? 4 * kCT * 32 : 16];
   const int N = (NMAT == 2) ? I : H, Kd = (NMAT == 2) ? H : I;
-  const int NJ = (N / 64 + 3) / 4;
+  const int NJ = (N / 64 + WPM - 1) / WPM;
   int e, j;
   map_block(blockIdx.x, E, NJ, &e, &j);
   if (e >= E) return;
@@ -217,8 +224,8 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   const int KB = Kd / 32, nchunk = (KB + kCT - 1) / kCT;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int mat = wave >> 2, wl = wave & 3;
-  const int nb = j * 4 + wl;
+  const int mat = wave / WPM, wl = wave % WPM;
+  const int nb = j * WPM + wl;
   // waves past the last row block only help stage (never with FULL: both dimensions are whole chunks)
   const bool active = FULL || nb < N / 64;
   const int mi = (NMAT == 2) ? mat : 2;  // gate, up | down
@@ -256,9 +263,10 @@ k_pf_gemm(const uint8_t* __restrict__ arena, int64_t R, const float* __restrict_
   //           a 16-lane group take rows 8 apart (32 banks apart); wave w stages rows w, w+8, ..
   //   NMAT 1: each thread stages one contiguous 64-input segment; lane bits 0-2 row, 3-4 segment,
   //           5 row + 8
-  const int srow = (NMAT == 2) ? wave + (lane >> 3) * 8 : wave * 16 + (lane & 7) + (lane >> 5) * 8;
-  const int pbase = (NMAT == 2) ? (lane & 7) * 8 : ((lane >> 3) & 3) * SEGW;
-  constexpr int pstep = (NMAT == 2) ? 64 : 8;
+  const int srow = (TPB == 512) ? wave + (lane >> 3) * 8 : wave * 16 + (lane & 7) + (lane >> 5) * 8;
+  const int pbase = (TPB == 512) ? (lane & 7) * 8 : ((lane >> 3) & 3) * SEGW;
+  constexpr int pstep = (TPB == 512) ? 64 : 8;
+  static_assert(TPB == 512 || TPB == 256, "the two staging maps");
 
   bool range_bad = false;  // an activation or SwiGLU output beyond the fp16 range (becomes inf)
   for (int m0 = 0; m0 < ne; m0 += kMT) {
@@ -471,15 +479,16 @@ hipError_t launch_prefill(eff_engine* e, int layer, const uint16_t* x, const int
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const bool fp4 = c.wformat == EFF_WFMT_NVFP4_G16_E4M3;
-  const int nbx1 = ((E + 7) / 8) * 8 * ((I / 64 + 3) / 4);
-  const int nbx2 = ((E + 7) / 8) * 8 * ((H / 64 + 3) / 4);
+  constexpr int wg = pf_wpm<2>(), wd = pf_wpm<1>();
+  const int nbx1 = ((E + 7) / 8) * 8 * ((I / 64 + wg - 1) / wg);
+  const int nbx2 = ((E + 7) / 8) * 8 * ((H / 64 + wd - 1) / wd);
   // timed outside a capture: each GEMM sets its own start and end events (its own duration)
   const bool own = (c.flags & EFF_CFG_TIMING) && !stream_capturing(s);
   const int ts = timing_begin(e, EFF_T_PREFILL_GATEUP, s, !own);
   hipEvent_t t0 = own ? timing_event(e, ts, 0) : nullptr, t1 = own ? timing_event(e, ts, 1) : nullptr;
   const bool full = H % 256 == 0 && I % 256 == 0;
 #define EFF_PF_LAUNCH(F, NM, PFD, FU, GRID, SRC, AO, YO)                                                        \
-  hipExtLaunchKernelGGL((k_pf_gemm<F, NM, PFD, FU>), dim3(GRID), dim3(256 * NM), 0, s, t0, t1, 0, e->d_arena, e->R, \
+  hipExtLaunchKernelGGL((k_pf_gemm<F, NM, PFD, FU>), dim3(GRID), dim3(pf_threads<NM>()), 0, s, t0, t1, 0, e->d_arena, e->R, \
                         e->d_ts, e->d_owner, slot_base, slot_of_expert, (const int32_t*)e->d_pf_count,          \
                         (const int32_t*)e->d_pf_rows, (const uint16_t*)(SRC), E, H, I, K, AO, YO, e->h_err_dev)
 #define EFF_PF_PICK(NM, PFD, FU, GRID, SRC, AO, YO)                                           \
