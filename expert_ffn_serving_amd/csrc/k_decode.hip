@@ -248,12 +248,23 @@ __device__ inline void run_tokens_lds(const uint4 w, const Scales4& rs, const ui
   }
 }
 
-// adds v over the 16 lanes with the same l % 4 (bits 2..5 of the lane id) in a fixed order
+// Lane moves without LDS round trips: DPP inside rows of 16 lanes (CTRL: 0x120 + n rotates a row by n,
+// 0x104 reads the lane 4 above in the row, 0xB1 / 0x4E swap neighbours / pairs in each quad).
+template <int CTRL>
+__device__ inline float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Adds v over the 16 lanes with the same l % 4 (l the lane id) in a fixed order: rotations by 4 and 8
+// inside each row of 16 lanes, then gfx950's row swaps bring row 1 onto row 0 (and 3 onto 2) and rows
+// 2-3 onto rows 0-1.  The sum is complete in lanes 0..15 only.
 __device__ inline float sum16(float v) {
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x128>(v);
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  v += __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_permlane16_swap(b, b, false, false)[1]);
+  const uint32_t c = __builtin_bit_cast(uint32_t, v);
+  v += __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_permlane32_swap(c, c, false, false)[1]);
   return v;
 }
 
@@ -271,7 +282,7 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
          int I, int K, int maxB, int nch, uint16_t* __restrict__ a16, float2* __restrict__ ag) {
   static_assert(P == 1 || P == 2, "1 or 2 waves per matrix of a slice");
   constexpr int SPW = 2 / P;                      // slices per workgroup
-  constexpr int UNR = NT == 1 ? 4 : NT == 2 ? 8 : NT == 4 ? 6 : 4;  // runs in flight per wave
+  constexpr int UNR = NT == 1 ? 4 : NT == 2 ? 8 : NT == 4 ? 5 : 4;  // runs in flight per wave (NT = 4: 4 waves per SIMD)
   extern __shared__ uint4 s_x[];                  // NT > 1: [NT][H/8] token rows of the chunk, 1 KiB slack
   __shared__ float s_red[4][16][NT];
   if ((int)blockIdx.x < sc.nwg) {  // the front of the grid carries a speculative copy
@@ -295,6 +306,12 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
   const int t4 = lane >> 4, g = lane & 3, q = (lane >> 2) & 3;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
   uint8_t* rec = arena + (int64_t)un->slot * R;
+  // NVFP4 tensor scales, read now: in the epilogue their load would be one more round trip to wait for
+  float tsg = 1.f, tsu = 1.f;
+  if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
+    tsg = ts[(int64_t)un->flat * 3 + 0];
+    tsu = ts[(int64_t)un->flat * 3 + 1];
+  }
   if (un->fetch) {
     // installed by this call: copy this workgroup's gate and up slices (payload and scales) from
     // the pool into the slot, then read them back like any resident record
@@ -333,12 +350,15 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
     // the rows laid end to end: lane l of copy c fills place 64 c + l of row (64 c + l) / (H/8); past the
     // last row it loads the last row's end into the slack behind s_x.  Every place is written by one
     // lane.  Issued before the weights' loads, and waited for below while those are still in flight.
+    // The chunk's row numbers are read once (lane j holds token c0 + j's, lanes past nt repeat the
+    // last): a load inside the copy loop would make every pass wait for all copies issued before it.
     if constexpr (NT > 1) {
+      const int rowj = un->entry[c0 + min(lane % NT, nt - 1)] / K;
       const uint32_t lds0 = lds_address(s_x);
       const int n = nt * H8;
       for (int c = wave; c < (n + 63) / 64; c += kWG / 64) {
         const int pl = min(c * 64 + lane, n - 1), j = pl / H8;
-        const uint16_t* row = x + (int64_t)(un->entry[c0 + j] / K) * H;
+        const uint16_t* row = x + (int64_t)__shfl(rowj, j) * H;
         lds_copy16(row + (pl - j * H8) * 8, lds0 + c * 1024);
       }
     }
@@ -355,18 +375,20 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
       __syncthreads();
     }
     // a rolling pipeline: UNR register slots, each refilled with the run UNR ahead once it is used.
-    // Blocks of RB runs are unrolled whole (a loop back-edge makes the compiler wait for every load
-    // in flight at the loop head), so a wave with at most RB runs sees no back-edge at all.
-    constexpr int RB = 4 * UNR;
-    for (int i0 = 0; i0 < nr; i0 += RB) {
+    // An iteration takes UNR runs, one per slot, and every path through it issues the same refills
+    // (past the wave's last run only the arithmetic is skipped), so the loop head is reached with the
+    // same loads in flight from before the loop and from its end, and the compiler's wait there
+    // covers just the next run (a loop left from inside made it wait for every load in flight).
+    for (int i0 = 0; i0 < nr; i0 += UNR) {
 #pragma unroll
-      for (int k = 0; k < RB; ++k) {
-        const int i = i0 + k, z = k % UNR, r = wp + P * i;
-        if (i >= nr) break;  // uniform
-        if constexpr (NT == 1) {
-          run_tokens<FMT, NT>(wv[z], rs[z], &xg[z], 1, acc);
-        } else {
-          run_tokens_lds<FMT, NT>(wv[z], rs[z], s_x + r * 16 + (lane >> 2), H8, nt, acc);
+      for (int z = 0; z < UNR; ++z) {
+        const int r = wp + P * (i0 + z);
+        if (i0 + z < nr) {  // uniform
+          if constexpr (NT == 1) {
+            run_tokens<FMT, NT>(wv[z], rs[z], &xg[z], 1, acc);
+          } else {
+            run_tokens_lds<FMT, NT>(wv[z], rs[z], s_x + r * 16 + (lane >> 2), H8, nt, acc);
+          }
         }
         load_run(z, min(r + P * UNR, rlast));
       }
@@ -407,16 +429,16 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
         uv += s_red[wu0 + w2][row][j];
       }
       if (FMT == EFF_WFMT_NVFP4_G16_E4M3) {
-        gv *= ts[(int64_t)un->flat * 3 + 0];
-        uv *= ts[(int64_t)un->flat * 3 + 1];
+        gv *= tsg;
+        uv *= tsu;
       }
       const float a = silu(gv) * uv;
       // the slice's power-of-two scale: max |a| over its 16 rows lands in [2^14, 2^15)
-      float mx = fabsf(a);
-      mx = fmaxf(mx, __shfl_xor(mx, 8));
-      mx = fmaxf(mx, __shfl_xor(mx, 4));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      float mx = fabsf(a);  // over the group's 16 lanes, one DPP row
+      mx = fmaxf(mx, dpp_f32<0x128>(mx));
+      mx = fmaxf(mx, dpp_f32<0x124>(mx));
+      mx = fmaxf(mx, dpp_f32<0x122>(mx));
+      mx = fmaxf(mx, dpp_f32<0x121>(mx));
       int sh = 0;
       if (mx > 0.f) {
         int ex;
@@ -424,10 +446,10 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
         sh = min(15 - ex, 100);
       }
       const _Float16 h = (_Float16)ldexpf(a, sh);
-      float gsum = (float)h;  // sum of the 8-group (rows 8*(row/8) ..), int4 only
-      gsum += __shfl_xor(gsum, 4);
-      gsum += __shfl_xor(gsum, 2);
-      gsum += __shfl_xor(gsum, 1);
+      float gsum = (float)h;  // sum of the 8-group (rows 8*(row/8) ..), complete in its first lane; int4 only
+      gsum += dpp_f32<0xB1>(gsum);
+      gsum += dpp_f32<0x4E>(gsum);
+      gsum += dpp_f32<0x104>(gsum);
       // int4: the pairs (a_m, a_m+4) of each 8-group meet the nibble pairs of a weight dword
       const int pos = FMT == EFF_WFMT_INT4_G32_BF16 ? (row & 8) | ((row & 3) << 1) | ((row >> 2) & 1) : row;
       const int slice = sgp * SPW + s2;
@@ -493,9 +515,10 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
        const float2* __restrict__ ag, int H, int I, int maxB, int nch, float* __restrict__ y) {
   static_assert(WPS == 1 || WPS == 2 || WPS == 4, "1, 2 or 4 waves per slice");
   constexpr int SPW = 4 / WPS;
-  constexpr int UNR = NT <= 2 ? 4 : 6;            // runs in flight per wave (4: fewer VGPRs, more waves)
+  constexpr int UNR = NT <= 2 ? 4 : 5;            // runs in flight per wave (NVFP4 NT = 4 fits 128 VGPRs: 4 waves per SIMD)
   extern __shared__ uint4 s_a4[];               // [NT][I/8] groups of 8 fp16, then [NT][I/8] float2
   __shared__ float s_red[4][16][NT];
+  __shared__ int s_p[NT];                       // the chunk's entries (rows of y)
   if ((int)blockIdx.x < sc.nwg) {  // the front of the grid carries a speculative copy
     copy_fetch_list(pool, arena, R, sc.n_flat, sc.S, sc.fl, blockIdx.x, sc.nwg);
     return;
@@ -516,6 +539,9 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
   const int t4 = lane >> 4, g = lane & 3, q = (lane >> 2) & 3;
   // a record installed by this call was copied whole by k_gateup, the previous kernel on the stream
   const uint8_t* rec = arena + (int64_t)un->slot * R;
+  // the NVFP4 tensor scale and (below) the chunk's entries are read before the weights, not in the
+  // epilogue, where each load would be one more round trip to wait for
+  const float tsd = FMT == EFF_WFMT_NVFP4_G16_E4M3 ? ts[(int64_t)un->flat * 3 + 2] : 1.f;
   float2* s_ag = reinterpret_cast<float2*>(s_a4 + NT * I8);
   const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 16;
   const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + t4 * 32 + lane_scale_off<FMT>(q, g);
@@ -543,6 +569,7 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
       va[k] = *reinterpret_cast<const uint4*>(a16 + tok * I + (i % I8) * 8);
       vg[k] = ag[tok * I8 + i % I8];
     }
+    const int pe = tid < NT ? un->entry[c0 + min(tid, nt - 1)] : 0;
     asm volatile("" ::: "memory");  // keeps these loads ahead of the weights' (no code)
     // the weights: a rolling pipeline of UNR slots, each refilled with the run UNR ahead once used
     uint4 wd[UNR];
@@ -560,6 +587,7 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
       s_a4[i] = va[k];
       s_ag[i] = vg[k];
     }
+    if (tid < NT) s_p[tid] = pe;
     __syncthreads();
     float acc[4][NT];
 #pragma unroll
@@ -599,8 +627,8 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
       float v = s_red[s2 * WPS][row][j];  // the slice's waves in order
 #pragma unroll
       for (int w2 = 1; w2 < WPS; ++w2) v += s_red[s2 * WPS + w2][row][j];
-      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= ts[(int64_t)un->flat * 3 + 2];
-      const int p = un->entry[c0 + j];
+      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= tsd;
+      const int p = s_p[j];
       y[(int64_t)p * H + (sgp * SPW + s2) * 16 + row] = v;
     }
     __syncthreads();
