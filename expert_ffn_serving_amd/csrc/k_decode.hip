@@ -293,6 +293,13 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
   const int NS = I / 16, NG = NS / SPW, KB = H / 32, NRF = KB / 4;
   const int u = bid / (NG * nch), ch = (bid / NG) % nch, sgp = bid % NG;
   const DecodeUnit* un = &plan->unit[u];
+  // The entries of chunk ch (lane l: entry ch*NT + l % NT), read at once rather than after the unit's
+  // fields: they are the workgroup's first chunk unless a fetched unit takes all its chunks.  A
+  // relaxed atomic load, which the compiler issues here instead of moving it behind the branch that
+  // waits for those fields.  Lanes past the chunk's tokens read entries that are not used.
+  const int e_first = __hip_atomic_load(const_cast<int32_t*>(&un->entry[min(ch * NT + (int)(threadIdx.x & 63) % NT,
+                                                                               kMaxTokens - 1)]),
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   const int cnt = un->count;
   // A resident unit's token chunks run in workgroups of their own (chunk ch: tokens ch*NT ..), so the
   // busiest experts do not run their chunks one after the other.  A unit installed by this call is
@@ -344,7 +351,8 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
       for (int j = 0; j < NT; ++j) acc[r][j] = 0.f;
     uint4 wv[UNR], xg[NT == 1 ? UNR : 1];
     Scales4 rs[UNR];
-    const uint16_t* xr = x + (int64_t)(un->entry[c0] / K) * H;  // NT == 1: the token's row
+    // NT == 1: the token's row
+    const uint16_t* xr = x + (int64_t)(__builtin_amdgcn_readfirstlane(c0 == ch * NT ? e_first : un->entry[c0]) / K) * H;
     const uint16_t* xt = xr + xo;
     // NT > 1: the chunk's token rows go to LDS straight from memory (no registers), 1 KiB per copy over
     // the rows laid end to end: lane l of copy c fills place 64 c + l of row (64 c + l) / (H/8); past the
@@ -353,7 +361,7 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
     // The chunk's row numbers are read once (lane j holds token c0 + j's, lanes past nt repeat the
     // last): a load inside the copy loop would make every pass wait for all copies issued before it.
     if constexpr (NT > 1) {
-      const int rowj = un->entry[c0 + min(lane % NT, nt - 1)] / K;
+      const int rowj = (c0 == ch * NT ? e_first : un->entry[c0 + min(lane % NT, nt - 1)]) / K;
       const uint32_t lds0 = lds_address(s_x);
       const int n = nt * H8;
       for (int c = wave; c < (n + 63) / 64; c += kWG / 64) {
