@@ -291,7 +291,11 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
   }
   const int bid = blockIdx.x - sc.nwg;
   const int NS = I / 16, NG = NS / SPW, KB = H / 32, NRF = KB / 4;
-  const int u = bid / (NG * nch), ch = (bid / NG) % nch, sgp = bid % NG;
+  // Workgroups go to the 8 dies (XCDs) in turn by block number, and each die has its own L2.  The
+  // slice groups of a unit's later chunks are rotated by their block's offset mod 8, so that most
+  // of them run on the die that reads the same slices for chunk 0 (about the same time: the chunks
+  // are adjacent in the grid) and find them in its L2 instead of reading the weights again.
+  const int u = bid / (NG * nch), ch = (bid / NG) % nch, sgp = (bid % NG + (ch * NG) % 8) % NG;
   const DecodeUnit* un = &plan->unit[u];
   // The entries of chunk ch (lane l: entry ch*NT + l % NT), read at once rather than after the unit's
   // fields: they are the workgroup's first chunk unless a fetched unit takes all its chunks.  A
