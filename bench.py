@@ -33,6 +33,7 @@ Beside it (context, not `value`):
 
 `--counters-pass` runs only a program for rocprofv3 counter passes: the roofline kernel's workload
 through the standalone entry points (no fused control kernel), after a 1 GiB calibration copy.
+`--counters-prefill` does the same for the prefill grouped GEMMs (two dsv4-flash layers streamed).
 """
 from __future__ import annotations
 
@@ -310,6 +311,25 @@ def decode_kernel_rates(eff, torch, synth, W, batches, tokens=64, threads=0, lab
     return res
 
 
+def calibration_copy(torch):
+    """A 1 GiB device-to-device copy: what a counter reads for it scales the counter to bytes."""
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def counters_prefill(eff, torch, synth, W, layers=2, threads=0):
+    """A program for rocprofv3 counter passes over the prefill grouped GEMMs: the calibration copy,
+    then run_prefill on `layers` layers of the prefill workload (route, sort, fp16 rows, gate/up and
+    down GEMMs, combine; no decode kernels)."""
+    calibration_copy(torch)
+    run_prefill(eff, torch, synth, W, layers, threads)
+
+
 def counters_pass(eff, torch, synth, W, B=16, tokens=64, warm=8, threads=0):
     """A program for rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE): a 1 GiB device-to-device copy
     (the calibration), then the roofline kernel's workload (the same expert shape, B, trace and
@@ -318,13 +338,7 @@ def counters_pass(eff, torch, synth, W, B=16, tokens=64, warm=8, threads=0):
     expert_ffn_decode.  The fused control kernel is not launched.  The last tokens * 2 k_gateup
     dispatches are the measured window."""
     import numpy as np
-    n = (1 << 30) // 4
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
-    b = torch.empty_like(a)
-    torch.cuda.synchronize()
-    b.copy_(a)
-    torch.cuda.synchronize()
-    del a, b
+    calibration_copy(torch)
     ptr, ts, R = fill_pool(eff, synth, W.seed, 2, W.E, W.H, W.I, W.fmt)
     E, K, H = W.E, W.K, W.H
     cfg = eff.make_config(2, E, K, H, W.I, W.fmt, 2 * E, B, 0, 65536, threads)
@@ -636,6 +650,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--counters-pass", action="store_true",
                     help="only run the roofline kernel's workload for rocprofv3 counter passes (no JSON line)")
+    ap.add_argument("--counters-prefill", action="store_true",
+                    help="only run two prefill layers for rocprofv3 counter passes (no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path, and this machine runs one "
@@ -653,6 +669,9 @@ def main():
         sys.exit(3)
     if args.counters_pass:
         counters_pass(eff, torch, synth, QWEN_NEXT, B=16, tokens=args.kernel_tokens, threads=args.threads)
+        return
+    if args.counters_prefill:
+        counters_prefill(eff, torch, synth, DSV4_PREFILL, layers=2, threads=args.threads)
         return
     W = QWEN_NEXT
     # the dominant kernel at the headline's shape and batches, every expert resident (first: the
