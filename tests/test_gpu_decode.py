@@ -261,6 +261,9 @@ def test_tiny_all_host_and_invariance(eff, tiny_pool):
     (synth.FMT_NVFP4, 2560, 640, 24, 10, 16, 60, 65535),
     (synth.FMT_NVFP4, 2560, 640, 64, 10, 1, 40, 65535),
     (synth.FMT_NVFP4, 2560, 640, 64, 10, 8, 120, 65535),
+    (synth.FMT_NVFP4, 2560, 640, 64, 10, 12, 100, 65535),   # 4-token chunks, three per unit
+    (synth.FMT_INT4, 2048, 512, 64, 8, 8, 100, 45875),      # int4, 4-token chunks
+    (synth.FMT_INT4, 2048, 512, 64, 8, 16, 100, 65535),     # int4, 8-token chunks
 ])
 def test_decode_shapes(eff, fmt, H, I, E, K, B, S, f):
     pool = PinnedPool(eff, 21, 2, E, H, I, fmt)
