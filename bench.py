@@ -33,7 +33,8 @@ Beside it (context, not `value`):
 
 `--counters-pass` runs only a program for rocprofv3 counter passes: the roofline kernel's workload
 through the standalone entry points (no fused control kernel), after a 1 GiB calibration copy.
-`--counters-prefill` does the same for the prefill grouped GEMMs (two dsv4-flash layers streamed).
+`--counters-prefill` does the same for the prefill grouped GEMMs (two dsv4-flash layers streamed);
+`--counters-shape dsv4` runs the counters pass at the dsv4-flash expert shape (B = 4) instead.
 """
 from __future__ import annotations
 
@@ -652,6 +653,8 @@ def main():
                     help="only run the roofline kernel's workload for rocprofv3 counter passes (no JSON line)")
     ap.add_argument("--counters-prefill", action="store_true",
                     help="only run two prefill layers for rocprofv3 counter passes (no JSON line)")
+    ap.add_argument("--counters-shape", choices=("qwen", "dsv4"), default="qwen",
+                    help="--counters-pass at the qwen3.8-flash-next shape (B = 16) or the dsv4-flash one (B = 4)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path, and this machine runs one "
@@ -668,7 +671,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
     if args.counters_pass:
-        counters_pass(eff, torch, synth, QWEN_NEXT, B=16, tokens=args.kernel_tokens, threads=args.threads)
+        if args.counters_shape == "dsv4":
+            counters_pass(eff, torch, synth, DSV4_DECODE, B=4, tokens=args.kernel_tokens, threads=args.threads)
+        else:
+            counters_pass(eff, torch, synth, QWEN_NEXT, B=16, tokens=args.kernel_tokens, threads=args.threads)
         return
     if args.counters_prefill:
         counters_prefill(eff, torch, synth, DSV4_PREFILL, layers=2, threads=args.threads)
