@@ -268,8 +268,8 @@ __device__ inline float sum16(float v) {
   return v;
 }
 
-// grid: maxU * (I/16) * P / 2 workgroups of 256 threads, one per (plan unit, group of 2/P consecutive
-// 16-row slices of I).  A slice takes 2P waves: P for its gate rows and P for its up rows, each wave
+// grid: (u2 * nch + maxU - u2) * (I/16) * P / 2 workgroups of 256 threads, one per (plan unit, token
+// chunk, group of 2/P consecutive 16-row slices of I).  A slice takes 2P waves: P for its gate rows and P for its up rows, each wave
 // every P-th run of its matrix; everything reduces inside the workgroup (the SwiGLU meets gate and
 // up in LDS), so no workgroup ever waits for another.  A unit installed by this call (fetch) first
 // copies its workgroup's gate and up slices from the pinned host pool into the slot (16-byte loads)
@@ -279,7 +279,7 @@ template <int FMT, int NT, int P>
 __global__ void __launch_bounds__(kWG, (FMT == EFF_WFMT_NVFP4_G16_E4M3 || NT < 8) ? 3 : 2)
 k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
          const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ x, int H,
-         int I, int K, int maxB, int nch, uint16_t* __restrict__ a16, float2* __restrict__ ag) {
+         int I, int K, int maxB, int nch, int u2, uint16_t* __restrict__ a16, float2* __restrict__ ag) {
   static_assert(P == 1 || P == 2, "1 or 2 waves per matrix of a slice");
   constexpr int SPW = 2 / P;                      // slices per workgroup
   constexpr int UNR = NT == 1 ? 4 : NT == 2 ? 8 : NT == 4 ? 5 : 4;  // runs in flight per wave (NT = 4: 4 waves per SIMD)
@@ -291,11 +291,17 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
   }
   const int bid = blockIdx.x - sc.nwg;
   const int NS = I / 16, NG = NS / SPW, KB = H / 32, NRF = KB / 4;
+  // Only the first u2 units (busiest first; no later unit can hold more than NT tokens) have nch
+  // chunk blocks; the others one, which takes all their tokens.
   // Workgroups go to the 8 dies (XCDs) in turn by block number, and each die has its own L2.  The
   // slice groups of a unit's later chunks are rotated by their block's offset mod 8, so that most
   // of them run on the die that reads the same slices for chunk 0 (about the same time: the chunks
   // are adjacent in the grid) and find them in its L2 instead of reading the weights again.
-  const int u = bid / (NG * nch), ch = (bid / NG) % nch, sgp = (bid % NG + (ch * NG) % 8) % NG;
+  const int nA = u2 * nch * NG;
+  const int nchu = bid < nA ? nch : 1;
+  const int u = bid < nA ? bid / (NG * nch) : u2 + (bid - nA) / NG;
+  const int ch = bid < nA ? (bid / NG) % nch : 0;
+  const int sgp = ((bid < nA ? bid : bid - nA) % NG + (ch * NG) % 8) % NG;
   const DecodeUnit* un = &plan->unit[u];
   // The entries of chunk ch (lane l: entry ch*NT + l % NT), read at once rather than after the unit's
   // fields: they are the workgroup's first chunk unless a fetched unit takes all its chunks.  A
@@ -309,7 +315,7 @@ k_gateup(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy s
   // busiest experts do not run their chunks one after the other.  A unit installed by this call is
   // copied by its chunk-0 workgroups, which then take every chunk themselves.
   const int c_begin = un->fetch ? 0 : ch * NT;
-  const int c_end = (un->fetch || ch == nch - 1) ? cnt : min(cnt, (ch + 1) * NT);
+  const int c_end = (un->fetch || ch == nchu - 1) ? cnt : min(cnt, (ch + 1) * NT);
   if (c_begin >= c_end || (un->fetch && ch > 0)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -720,19 +726,19 @@ int down_wps(int slices, int runs) {
 // With events (t0, t1) the launch sets them at the kernel's own start and end (hipExtLaunchKernelGGL):
 // the timing then covers the kernel alone, as a profiler's kernel trace does.
 template <int FMT, int NT, int P>
-hipError_t launch_gateup_t(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int nch, hipStream_t s,
-                           uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
+hipError_t launch_gateup_t(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int nch, int u2,
+                           hipStream_t s, uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   if (!sc.fl) sc.nwg = 0;
-  const dim3 grid(sc.nwg + units * nch * (I / 16) * P / 2), block(kWG);
+  const dim3 grid(sc.nwg + (u2 * nch + (units - u2)) * (I / 16) * P / 2), block(kWG);
   const uint32_t lds = NT > 1 ? NT * H * 2 + 1024 : 0;  // token rows and the copies' slack
   if (t0)
     hipExtLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R, sc,
-                          e->d_ts, plan, x, H, I, c.top_k, c.max_tokens, nch, a16, ag);
+                          e->d_ts, plan, x, H, I, c.top_k, c.max_tokens, nch, u2, a16, ag);
   else
     hipLaunchKernelGGL((k_gateup<FMT, NT, P>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, sc, e->d_ts, plan,
-                       x, H, I, c.top_k, c.max_tokens, nch, a16, ag);
+                       x, H, I, c.top_k, c.max_tokens, nch, u2, a16, ag);
   return hipGetLastError();
 }
 
@@ -769,9 +775,12 @@ template <int FMT, int NT>
 hipError_t launch_gateup_p(eff_engine* e, const DecodePlan* plan, const uint16_t* x, int units, int B, hipStream_t s,
                            uint16_t* a16, float2* ag, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
   const int nch = (B + NT - 1) / NT;  // token chunks a unit can have (a unit holds at most one entry per token)
+  // units that can hold more than NT tokens: each has NT + 1 of the call's B * K entries or more, and
+  // the plan lists them first (busiest first); the grid gives only those nch chunk blocks
+  const int u2 = nch > 1 ? std::min(units, B * e->cfg.top_k / (NT + 1)) : units;
   if (gateup_waves_per_matrix(units * (e->cfg.inter / 16)) == 1)
-    return launch_gateup_t<FMT, NT, 1>(e, plan, x, units, nch, s, a16, ag, t0, t1, sc);
-  return launch_gateup_t<FMT, NT, 2>(e, plan, x, units, nch, s, a16, ag, t0, t1, sc);
+    return launch_gateup_t<FMT, NT, 1>(e, plan, x, units, nch, u2, s, a16, ag, t0, t1, sc);
+  return launch_gateup_t<FMT, NT, 2>(e, plan, x, units, nch, u2, s, a16, ag, t0, t1, sc);
 }
 
 template <int FMT, int NT>
