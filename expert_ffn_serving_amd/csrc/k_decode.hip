@@ -523,33 +523,44 @@ __device__ inline void down_run(const uint4 wd, const Scales4& rd, const uint4* 
   }
 }
 
+// Tokens of a unit whose activations the down kernel stages into LDS at once (a multiple of NT): as
+// many of the call's maxB as fit kDownLds bytes beside the 1 KiB slacks, never fewer than NT.
+constexpr int kDownLds = 38 * 1024;  // 4 workgroups per CU (the kernel's register bound) within 160 KiB
+inline int down_span(int NT, int maxB, int I) {
+  const int fit = (kDownLds - 2048) / ((I / 8) * 24) / NT * NT;
+  return std::max(NT, std::min(maxB, fit));
+}
+inline int down_lds_bytes(int NT, int maxB, int I) { return down_span(NT, maxB, I) * (I / 8) * 24 + 2048; }
+
 // grid: maxU * (H/16) / (4/WPS) workgroups, one per (plan unit, group of 4/WPS consecutive 16-row
-// slices of H); WPS waves share a slice.  The unit's SwiGLU activations, already fp16 from k_gateup,
-// are copied into LDS with their per-group scales and sums once for the workgroup's slices.
-template <int FMT, int NT, int WPS>
+// slices of H); WPS waves share a slice.  The workgroup takes all of its unit's tokens, NT at a time.
+// Their SwiGLU activations (already fp16 from k_gateup) and per-group (scale, sum) pairs are rows
+// u * maxB + j of a16 and ag, contiguous for a unit: they go to LDS by direct copies, `span` tokens
+// per pass (all of them unless the unit has more), with one barrier per pass.  When a wave's runs all
+// fit its UNR register slots (KEEP) the weights are loaded once and stay in registers for every chunk.
+template <int NT>
+constexpr int down_unr() { return NT <= 2 ? 4 : 5; }  // runs in flight per wave (NVFP4 NT = 4 fits 128 VGPRs: 4 waves per SIMD)
+template <int FMT, int NT, int WPS, bool KEEP>
 __global__ void __launch_bounds__(kWG)
 k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
        const float* __restrict__ ts, const DecodePlan* __restrict__ plan, const uint16_t* __restrict__ a16,
-       const float2* __restrict__ ag, int H, int I, int maxB, int nch, float* __restrict__ y) {
+       const float2* __restrict__ ag, int H, int I, int maxB, int span, float* __restrict__ y) {
   static_assert(WPS == 1 || WPS == 2 || WPS == 4, "1, 2 or 4 waves per slice");
   constexpr int SPW = 4 / WPS;
-  constexpr int UNR = NT <= 2 ? 4 : 5;            // runs in flight per wave (NVFP4 NT = 4 fits 128 VGPRs: 4 waves per SIMD)
-  extern __shared__ uint4 s_a4[];               // [NT][I/8] groups of 8 fp16, then [NT][I/8] float2
+  constexpr int UNR = down_unr<NT>();
+  extern __shared__ uint4 s_a4[];               // [span][I/8] groups of 8 fp16, 1 KiB slack, [span][I/8] float2, 1 KiB slack
   __shared__ float s_red[4][16][NT];
-  __shared__ int s_p[NT];                       // the chunk's entries (rows of y)
+  __shared__ int s_p[kMaxTokens];               // the pass's entries (rows of y)
   if ((int)blockIdx.x < sc.nwg) {  // the front of the grid carries a speculative copy
     copy_fetch_list(pool, arena, R, sc.n_flat, sc.S, sc.fl, blockIdx.x, sc.nwg);
     return;
   }
   const int bid = blockIdx.x - sc.nwg;
   const int NSH = H / 16, NG = NSH / SPW, KB = I / 32, NRF = KB / 4, I8 = I / 8;
-  const int u = bid / (NG * nch), ch = (bid / NG) % nch, sgp = bid % NG;
+  const int u = bid / NG, sgp = bid % NG;
   const DecodeUnit* un = &plan->unit[u];
   const int cnt = un->count;
-  // with nch > 1 each token chunk of a unit in workgroups of its own (every record is resident by now),
-  // the last taking what is left
-  const int c_begin = ch * NT, c_end = ch == nch - 1 ? cnt : min(cnt, (ch + 1) * NT);
-  if (c_begin >= c_end) return;
+  if (cnt <= 0) return;
   const int64_t pay = (int64_t)H * I / 2, sca = (int64_t)H * I / 16;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -557,10 +568,12 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
   const int t4 = lane >> 4, g = lane & 3, q = (lane >> 2) & 3;
   // a record installed by this call was copied whole by k_gateup, the previous kernel on the stream
   const uint8_t* rec = arena + (int64_t)un->slot * R;
-  // the NVFP4 tensor scale and (below) the chunk's entries are read before the weights, not in the
-  // epilogue, where each load would be one more round trip to wait for
+  // the NVFP4 tensor scale is read before the weights, not in the epilogue, where the load would be
+  // one more round trip to wait for
   const float tsd = FMT == EFF_WFMT_NVFP4_G16_E4M3 ? ts[(int64_t)un->flat * 3 + 2] : 1.f;
-  float2* s_ag = reinterpret_cast<float2*>(s_a4 + NT * I8);
+  const int SL = span * I8;                     // 16-byte places of a pass's activations
+  float2* s_ag = reinterpret_cast<float2*>(s_a4 + SL + 64);
+  const uint32_t ldsA = lds_address(s_a4), ldsG = ldsA + (uint32_t)(SL + 64) * 16;
   const uint8_t* dp = rec + 2 * pay + (int64_t)sl * KB * 256 + lane * 16;
   const uint8_t* ds = rec + 3 * pay + 2 * sca + (int64_t)sl * KB * 32 + t4 * 32 + lane_scale_off<FMT>(q, g);
   const int ai = lane >> 2;                     // the lane's 8-group in a run: 16 r + ai
@@ -571,85 +584,118 @@ k_down(uint8_t* arena, const uint8_t* __restrict__ pool, int64_t R, SpecCopy sc,
   // (past the last run a load takes it again) so that the compiler keeps them in flight
   const int nr = NRF > wp ? (NRF - wp + WPS - 1) / WPS : 0;
   const int rlast = wp + WPS * max(nr - 1, 0);
-  for (int c0 = c_begin; c0 < c_end; c0 += NT) {
-    const int nt = min(NT, c_end - c0);
-    // the tokens' activations (16 B per 8-group) and their (scale, sum) pairs: LPT loads per thread
-    // (the launcher keeps NT * I / 8 within LPT * kWG), issued before the weights' so that their LDS
-    // stores wait for them alone; past the chunk's last one a thread loads and stores that one again
-    constexpr int LPT = 4;
-    const int n = nt * I8;
-    uint4 va[LPT];
-    float2 vg[LPT];
-#pragma unroll
-    for (int k = 0; k < LPT; ++k) {
-      const int i = min(tid + k * kWG, n - 1);
-      const int64_t tok = (int64_t)u * maxB + c0 + i / I8;
-      va[k] = *reinterpret_cast<const uint4*>(a16 + tok * I + (i % I8) * 8);
-      vg[k] = ag[tok * I8 + i % I8];
-    }
-    const int pe = tid < NT ? un->entry[c0 + min(tid, nt - 1)] : 0;
-    asm volatile("" ::: "memory");  // keeps these loads ahead of the weights' (no code)
-    // the weights: a rolling pipeline of UNR slots, each refilled with the run UNR ahead once used
-    uint4 wd[UNR];
-    Scales4 rd[UNR];
-    auto load_run = [&](int z, int r) {
-      wd[z] = *reinterpret_cast<const uint4*>(dp + (int64_t)r * 1024);
-      rd[z] = load_scales4<FMT>(ds + r * 128);
-    };
+  uint4 wd[UNR];
+  Scales4 rd[UNR];
+  auto load_run = [&](int z, int r) {
+    wd[z] = *reinterpret_cast<const uint4*>(dp + (int64_t)r * 1024);
+    rd[z] = load_scales4<FMT>(ds + r * 128);
+  };
+  // a pass's rows, 1 KiB per copy laid end to end: lane l of copy c fills place 64 c + l; past the
+  // last place it loads the last one again into the slack.  Every place is written by one lane.  (I
+  // is a multiple of 32, so a pass's float2 pairs fill whole 16-byte places.)  Returns the entry of
+  // the pass's token tid (rows of y).
+  auto stage = [&](int p0, int np) {
+    const uint16_t* asrc = a16 + ((int64_t)u * maxB + p0) * I;
+    const float2* gsrc = ag + ((int64_t)u * maxB + p0) * I8;
+    const int na = np * I8, ng = np * I8 / 2;
+    for (int c = wave; c < (na + 63) / 64; c += kWG / 64) lds_copy16(asrc + (int64_t)min(c * 64 + lane, na - 1) * 8, ldsA + c * 1024);
+    for (int c = wave; c < (ng + 63) / 64; c += kWG / 64) lds_copy16(gsrc + 2 * min(c * 64 + lane, ng - 1), ldsG + c * 1024);
+    return tid < np ? un->entry[p0 + tid] : 0;
+  };
+  // the first pass's copies go out first, then (KEEP) the wave's runs, once for all passes
+  int pe = stage(0, min(span, cnt));
+  if constexpr (KEEP) {
 #pragma unroll
     for (int z = 0; z < UNR; ++z) load_run(z, min(wp + WPS * z, rlast));
-    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma nounroll
+  for (int p0 = 0; p0 < cnt; p0 += span) {
+    const int np = min(span, cnt - p0);
+    if (p0 > 0) pe = stage(p0, np);
+    if constexpr (KEEP) {
+      // the copies are complete once at most the runs' 2 * UNR loads, issued after them, remain
+      if (p0 == 0) vm_wait<2 * UNR>(); else vm_wait<0>();
+    } else {
+      // the pass's first runs, issued after the copies: the copies are complete once at most these
+      // 2 * UNR loads remain
 #pragma unroll
-    for (int k = 0; k < LPT; ++k) {
-      const int i = min(tid + k * kWG, n - 1);
-      s_a4[i] = va[k];
-      s_ag[i] = vg[k];
+      for (int z = 0; z < UNR; ++z) load_run(z, min(wp + WPS * z, rlast));
+      vm_wait<2 * UNR>();
     }
-    if (tid < NT) s_p[tid] = pe;
+    if (tid < np) s_p[tid] = pe;
     __syncthreads();
-    float acc[4][NT];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[r][j] = 0.f;
-    constexpr int RB = 2 * UNR;  // runs unrolled whole per block (no loop back-edge inside)
-    for (int i0 = 0; i0 < nr; i0 += RB) {
-#pragma unroll
-      for (int k = 0; k < RB; ++k) {
-        const int i = i0 + k, z = k % UNR, r = wp + WPS * i;
-        if (i >= nr) break;  // uniform
-        down_run<FMT, NT>(wd[z], rd[z], s_a4, s_ag, r * 16 + ai, nt, I8, acc);
-        load_run(z, min(r + WPS * UNR, rlast));
-      }
-    }
-    if (tail && wp == NRF % WPS && tail_lane) {
-      const int r = NRF;
-      const uint4 w1 = *reinterpret_cast<const uint4*>(dp + (int64_t)r * 1024);
-      const Scales4 s1 = load_scales4<FMT>(ds + r * 128);
-      down_run<FMT, NT>(w1, s1, s_a4, s_ag, r * 16 + ai, nt, I8, acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-        if (NT == 1 || j < nt) acc[r][j] = sum16(acc[r][j]);
-    if (lane < 4) {
+#pragma nounroll
+    for (int c0 = p0; c0 < p0 + np; c0 += NT) {
+      const int nt = min(NT, p0 + np - c0);
+      const uint4* sa = s_a4 + (c0 - p0) * I8;
+      const float2* sg = s_ag + (c0 - p0) * I8;
+      float acc[4][NT];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) s_red[wave][4 * lane + r][j] = acc[r][j];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < 16 * SPW * nt; idx += kWG) {
-      const int j = idx % nt, rr = idx / nt, s2 = rr / 16, row = rr % 16;
-      float v = s_red[s2 * WPS][row][j];  // the slice's waves in order
+        for (int j = 0; j < NT; ++j) acc[r][j] = 0.f;
+      if constexpr (KEEP) {  // nr <= UNR
 #pragma unroll
-      for (int w2 = 1; w2 < WPS; ++w2) v += s_red[s2 * WPS + w2][row][j];
-      if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= tsd;
-      const int p = s_p[j];
-      y[(int64_t)p * H + (sgp * SPW + s2) * 16 + row] = v;
+        for (int z = 0; z < UNR; ++z) {
+          if (z >= nr) break;  // uniform
+          down_run<FMT, NT>(wd[z], rd[z], sa, sg, (wp + WPS * z) * 16 + ai, nt, I8, acc);
+        }
+      } else {
+        // a rolling pipeline of UNR slots, each refilled with the run UNR ahead once used; a later
+        // chunk of the pass loads its first runs again (from L2)
+        if (c0 > p0) {
+#pragma unroll
+          for (int z = 0; z < UNR; ++z) load_run(z, min(wp + WPS * z, rlast));
+        }
+        constexpr int RB = 2 * UNR;  // runs unrolled whole per block (no loop back-edge inside)
+        for (int i0 = 0; i0 < nr; i0 += RB) {
+#pragma unroll
+          for (int k = 0; k < RB; ++k) {
+            const int i = i0 + k, z = k % UNR, r = wp + WPS * i;
+            if (i >= nr) break;  // uniform
+            down_run<FMT, NT>(wd[z], rd[z], sa, sg, r * 16 + ai, nt, I8, acc);
+            load_run(z, min(r + WPS * UNR, rlast));
+          }
+        }
+      }
+      if (tail && wp == NRF % WPS && tail_lane) {
+        const int r = NRF;
+        const uint4 w1 = *reinterpret_cast<const uint4*>(dp + (int64_t)r * 1024);
+        const Scales4 s1 = load_scales4<FMT>(ds + r * 128);
+        down_run<FMT, NT>(w1, s1, sa, sg, r * 16 + ai, nt, I8, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          if (NT == 1 || j < nt) acc[r][j] = sum16(acc[r][j]);
+      if (lane < 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) s_red[wave][4 * lane + r][j] = acc[r][j];
+      }
+      __syncthreads();
+      for (int idx = tid; idx < 16 * SPW * nt; idx += kWG) {
+        const int j = idx % nt, rr = idx / nt, s2 = rr / 16, row = rr % 16;
+        float v = s_red[s2 * WPS][row][j];  // the slice's waves in order
+#pragma unroll
+        for (int w2 = 1; w2 < WPS; ++w2) v += s_red[s2 * WPS + w2][row][j];
+        if (FMT == EFF_WFMT_NVFP4_G16_E4M3) v *= tsd;
+        const int p = s_p[c0 - p0 + j];
+        y[(int64_t)p * H + (sgp * SPW + s2) * 16 + row] = v;
+      }
+      __syncthreads();
+      if constexpr (KEEP) {
+        // the kept runs count as rewritten here (no code): otherwise the compiler would keep every
+        // run's dequantized values live across the chunks instead of the packed weights
+#pragma unroll
+        for (int z = 0; z < UNR; ++z) {
+          asm volatile("" : "+v"(wd[z].x), "+v"(wd[z].y), "+v"(wd[z].z), "+v"(wd[z].w), "+v"(rd[z].a));
+          if constexpr (FMT == EFF_WFMT_INT4_G32_BF16) asm volatile("" : "+v"(rd[z].b));
+        }
+      }
     }
-    __syncthreads();
   }
 }
 
@@ -742,20 +788,21 @@ hipError_t launch_gateup_t(eff_engine* e, const DecodePlan* plan, const uint16_t
   return hipGetLastError();
 }
 
-template <int FMT, int NT, int WPS>
-hipError_t launch_down_t(eff_engine* e, const DecodePlan* plan, int units, int nch, hipStream_t s, const uint16_t* a16,
+template <int FMT, int NT, int WPS, bool KEEP>
+hipError_t launch_down_t(eff_engine* e, const DecodePlan* plan, int units, hipStream_t s, const uint16_t* a16,
                          const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
   const eff_config& c = e->cfg;
   const int H = c.hidden, I = c.inter;
   if (!sc.fl) sc.nwg = 0;
-  const uint32_t lds = (uint32_t)(NT * (I / 8) * (sizeof(uint4) + sizeof(float2)));
-  const dim3 grid(sc.nwg + units * nch * (H / 16) * WPS / 4), block(kWG);
+  const int span = down_span(NT, c.max_tokens, I);
+  const uint32_t lds = (uint32_t)down_lds_bytes(NT, c.max_tokens, I);
+  const dim3 grid(sc.nwg + units * (H / 16) * WPS / 4), block(kWG);
   if (t0)
-    hipExtLaunchKernelGGL((k_down<FMT, NT, WPS>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R, sc,
-                          e->d_ts, plan, a16, ag, H, I, c.max_tokens, nch, y);
+    hipExtLaunchKernelGGL((k_down<FMT, NT, WPS, KEEP>), grid, block, lds, s, t0, t1, 0, e->d_arena, e->pool_dev, e->R, sc,
+                          e->d_ts, plan, a16, ag, H, I, c.max_tokens, span, y);
   else
-    hipLaunchKernelGGL((k_down<FMT, NT, WPS>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, sc, e->d_ts, plan,
-                       a16, ag, H, I, c.max_tokens, nch, y);
+    hipLaunchKernelGGL((k_down<FMT, NT, WPS, KEEP>), grid, block, lds, s, e->d_arena, e->pool_dev, e->R, sc, e->d_ts, plan,
+                       a16, ag, H, I, c.max_tokens, span, y);
   return hipGetLastError();
 }
 
@@ -764,7 +811,7 @@ hipError_t launch_down_t(eff_engine* e, const DecodePlan* plan, int units, int n
 // (61.6 against 67.8 us with 4) and 4-token chunks at B = 8 (36.0 against 48.0 us with 8); the down
 // rows are short, and 4-token chunks are faster there at both (B = 16: 35.7 against 45.5 us).
 int gateup_nt(int B) { return B >= 16 ? 8 : B >= 4 ? 4 : B >= 2 ? 2 : 1; }
-// (the down kernel stages a chunk's activations with 4 loads per thread: N * I / 8 <= 1024)
+// (N * I <= 8192 keeps a pass of N tokens within 26 KiB of LDS whatever I)
 int down_nt(int B, int I) {
   int n = B >= 4 ? 4 : B >= 2 ? 2 : 1;
   while (n > 1 && n * I > 8192) n /= 2;
@@ -783,15 +830,25 @@ hipError_t launch_gateup_p(eff_engine* e, const DecodePlan* plan, const uint16_t
   return launch_gateup_t<FMT, NT, 2>(e, plan, x, units, nch, u2, s, a16, ag, t0, t1, sc);
 }
 
+// the weights stay in registers when every wave's runs, (I/128 + WPS - 1) / WPS at most, fit its slots
+inline bool down_keep(int I, int WPS, int unr) { return (I / 128 + WPS - 1) / WPS <= unr; }
+template <int FMT, int NT, int WPS>
+hipError_t launch_down_k(eff_engine* e, const DecodePlan* plan, int units, hipStream_t s, const uint16_t* a16,
+                         const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
+  if (down_keep(e->cfg.inter, WPS, down_unr<NT>()))
+    return launch_down_t<FMT, NT, WPS, true>(e, plan, units, s, a16, ag, y, t0, t1, sc);
+  return launch_down_t<FMT, NT, WPS, false>(e, plan, units, s, a16, ag, y, t0, t1, sc);
+}
+
 template <int FMT, int NT>
 hipError_t launch_down_w(eff_engine* e, const DecodePlan* plan, int units, hipStream_t s, const uint16_t* a16,
                          const float2* ag, float* y, hipEvent_t t0, hipEvent_t t1, SpecCopy sc) {
   // the down kernel takes a unit's chunks in turn: its rows are short (I inputs), so a second wave of
   // workgroups per unit costs more than the chunks' arithmetic it would spread
   switch (down_wps(units * (e->cfg.hidden / 16), e->cfg.inter / 128)) {
-    case 1: return launch_down_t<FMT, NT, 1>(e, plan, units, 1, s, a16, ag, y, t0, t1, sc);
-    case 2: return launch_down_t<FMT, NT, 2>(e, plan, units, 1, s, a16, ag, y, t0, t1, sc);
-    default: return launch_down_t<FMT, NT, 4>(e, plan, units, 1, s, a16, ag, y, t0, t1, sc);
+    case 1: return launch_down_k<FMT, NT, 1>(e, plan, units, s, a16, ag, y, t0, t1, sc);
+    case 2: return launch_down_k<FMT, NT, 2>(e, plan, units, s, a16, ag, y, t0, t1, sc);
+    default: return launch_down_k<FMT, NT, 4>(e, plan, units, s, a16, ag, y, t0, t1, sc);
   }
 }
 
@@ -847,9 +904,12 @@ hipError_t decode_kernels_setup(int fmt, int maxB, int H, int I) {
   }
 #define SETUP_D(F, N)                                                       \
   if (fmt == F && N <= ND) {                                                \
-    set((const void*)k_down<F, N, 1>, N * (I / 8) * 24);                    \
-    set((const void*)k_down<F, N, 2>, N * (I / 8) * 24);                    \
-    set((const void*)k_down<F, N, 4>, N * (I / 8) * 24);                    \
+    set((const void*)k_down<F, N, 1, true>, down_lds_bytes(N, maxB, I));    \
+    set((const void*)k_down<F, N, 1, false>, down_lds_bytes(N, maxB, I));   \
+    set((const void*)k_down<F, N, 2, true>, down_lds_bytes(N, maxB, I));    \
+    set((const void*)k_down<F, N, 2, false>, down_lds_bytes(N, maxB, I));   \
+    set((const void*)k_down<F, N, 4, true>, down_lds_bytes(N, maxB, I));    \
+    set((const void*)k_down<F, N, 4, false>, down_lds_bytes(N, maxB, I));   \
   }
   SETUP_G(EFF_WFMT_INT4_G32_BF16, 1) SETUP_G(EFF_WFMT_INT4_G32_BF16, 2) SETUP_G(EFF_WFMT_INT4_G32_BF16, 4)
   SETUP_G(EFF_WFMT_INT4_G32_BF16, 8) SETUP_G(EFF_WFMT_NVFP4_G16_E4M3, 1) SETUP_G(EFF_WFMT_NVFP4_G16_E4M3, 2)
