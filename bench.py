@@ -701,7 +701,7 @@ def main():
         "timed_as": "HIP events that each launch sets at its kernel's start and end (hipExtLaunchKernelGGL), "
                     "on the kernel's stream",
         "source_sha": src_hash(*srcs),
-        "down": {"kernel": "k_down<NVFP4, 4, 1>", "achieved": k16["down_GBps"], "frac": k16["down_frac"],
+        "down": {"kernel": "k_down<NVFP4, 4, 1, true> (weights kept in registers across token chunks)", "achieved": k16["down_GBps"], "frac": k16["down_frac"],
                  "algorithmic_bytes_per_launch": k16["down_alg_bytes_per_launch"], "avg_launch_us": k16["down_us"]},
     }
     link = {"bound": "pcie", "achieved_GBps": head["link_GBps"],
