@@ -264,6 +264,10 @@ def test_tiny_all_host_and_invariance(eff, tiny_pool):
     (synth.FMT_NVFP4, 2560, 640, 64, 10, 12, 100, 65535),   # 4-token chunks, three per unit
     (synth.FMT_INT4, 2048, 512, 64, 8, 8, 100, 45875),      # int4, 4-token chunks
     (synth.FMT_INT4, 2048, 512, 64, 8, 16, 100, 65535),     # int4, 8-token chunks
+    # units with more tokens than the down kernel stages in one pass (38 KiB of LDS): a second pass
+    (synth.FMT_NVFP4, 2560, 640, 16, 10, 32, 16, 65535),   # 16 of 32 tokens per pass, weights kept
+    (synth.FMT_INT4, 2048, 512, 16, 8, 32, 16, 65535),     # 24 of 32 per pass, weights kept
+    (synth.FMT_NVFP4, 4096, 2048, 8, 6, 8, 8, 65535),      # 4 of 8 per pass, runs streamed again
 ])
 def test_decode_shapes(eff, fmt, H, I, E, K, B, S, f):
     pool = PinnedPool(eff, 21, 2, E, H, I, fmt)
